@@ -1,0 +1,340 @@
+/*
+ * Deformable-sampling CPU oracle — TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, fp64 loop nests that define what the GPU library must compute.
+ * Only tests/, the smoke check and the bench's cpu_baseline leg may load this.
+ * It shares no source, header, table or helper with the HIP library.
+ *
+ * Sources (page title, section):
+ *  [P-DCNv1]  "用PyTorch实战DCNv1：从零构建可变形卷积与ROI池化模块"
+ *             (Hands-on DCNv1 in PyTorch), section 1 (the deformable sum
+ *             y(p0) = sum_n w(p_n) x(p0 + p_n + dp_n)) and section 2 (the
+ *             bilinear kernel G(q,p) = g(qx,px) g(qy,py), g(a,b) = max(0,1-|a-b|);
+ *             offsets laid out as interleaved (x, y) pairs per point).
+ *  [P-DCNv2]  "DCNv2实战：在YOLOv5中替换普通卷积…" (DCNv2 in YOLOv5), section 1:
+ *             each sampled value is additionally scaled by a modulation scalar.
+ *  [P-DCNv3]  "DCNV3技术深度解析与高性能AI开发环境构建" (DCNv3 deep dive), the
+ *             forward-kernel section: kernel points indexed row-major
+ *             (k = ki*kernel_w + kj).
+ *  [P-DCNv4]  lpnh.cn news 2795861 (DCNv4 in YOLOv11), section 1.1: channels
+ *             split into groups with their own offsets and modulation; DCNv3
+ *             normalises the modulation with a softmax over the points, DCNv4
+ *             does not; section 3.2: channels-last input, offset_scale.
+ *  [P-AGG]    mlqm.cn news 106099 (Sparse4D deformable_aggregation), sections
+ *             2.1-2.2 (inputs: multi-camera multi-scale features flattened to
+ *             [B, N*H*W, C], spatial shapes, scale start index, sampling
+ *             locations, weights) and section 7 (softmax-normalised weights).
+ *
+ * Readings where the pages are silent (each listed in the design doc):
+ *  - zero outside the image, per corner;
+ *  - grid base = out*stride - pad + tap*dilation;
+ *  - offset pairs are (dx, dy), x first;
+ *  - the scaled core offset is one fp32 quantity: fl32(offset_scale*delta);
+ *  - aggregation pixel coordinate: x = fl32(u*W) - 0.5 (pixel centres at
+ *    (i+1/2)/W), y likewise with v and H.
+ *
+ * Every function also returns, per output element, the sum of the absolute
+ * values of all product terms ("absum"), used by the tests' error bound.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+/* ---------------------------------------------------------------------- */
+/* Bilinear sample, [P-DCNv1] section 2.                                   */
+/* X(h, w) is X[(h*W + w) * cstride]; positions outside [0,H)x[0,W) give 0. */
+/* The 4-corner form below equals the lattice sum over all q of G(q,p)X(q): */
+/* g(q,p) is non-zero only for the two integers q bracketing p, with        */
+/* weights 1-f and f.                                                       */
+/* ---------------------------------------------------------------------- */
+double oracle_bilinear(const double *X, int64_t H, int64_t W, int64_t cstride,
+                       double y, double x, double *absum)
+{
+    double y0 = floor(y), x0 = floor(x);
+    double fy = y - y0, fx = x - x0;
+    double wy[2] = {1.0 - fy, fy};
+    double wx[2] = {1.0 - fx, fx};
+    double s = 0.0, a = 0.0;
+    for (int dy = 0; dy < 2; ++dy) {
+        for (int dx = 0; dx < 2; ++dx) {
+            double qy = y0 + dy, qx = x0 + dx;
+            double wq = wy[dy] * wx[dx];
+            if (wq == 0.0) continue;
+            if (qy < 0.0 || qy >= (double)H || qx < 0.0 || qx >= (double)W) continue;
+            double v = X[((int64_t)qy * W + (int64_t)qx) * cstride];
+            s += wq * v;
+            a += fabs(wq * v);
+        }
+    }
+    if (absum) *absum += a;
+    return s;
+}
+
+/* fl32(s * d): the exact product of two fp32 values fits in a double, so one
+ * conversion performs the single round-to-nearest-even. */
+static double fl32_mul(float s, double d)
+{
+    return (double)(float)((double)s * d);
+}
+
+/* Softmax of n values in fp64, max-subtracted ([P-DCNv4] section 1.1 for
+ * DCNv3's per-group normalisation; [P-AGG] section 7 for aggregation). */
+static void softmax_d(const double *l, int64_t n, int64_t lstride, double *m)
+{
+    double mx = -INFINITY;
+    for (int64_t i = 0; i < n; ++i)
+        if (l[i * lstride] > mx) mx = l[i * lstride];
+    double den = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        m[i] = exp(l[i * lstride] - mx);
+        den += m[i];
+    }
+    for (int64_t i = 0; i < n; ++i) m[i] /= den;
+}
+
+void oracle_softmax(const double *l, int64_t n, double *m) { softmax_d(l, n, 1, m); }
+
+static int64_t out_size(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d)
+{
+    return (in + 2 * p - d * (k - 1) - 1) / s + 1;
+}
+
+/* ---------------------------------------------------------------------- */
+/* DCNv3/v4 core, channels-last.                                            */
+/*  x      [N, H, W, G*C]                                                   */
+/*  offset [N, Ho, Wo, G, K, 2]  (dx, dy), K = kh*kw, k = i*kw + j         */
+/*  mask   [N, Ho, Wo, G, K] or NULL (then every modulation is 1)           */
+/*  out    [npix, G*C]  for the listed output pixels (pix = (n*Ho+ho)*Wo+wo)*/
+/*         or [N*Ho*Wo, G*C] when pix == NULL.                              */
+/* out[.., g*C+c] = sum_k m_k * bilinear(x[n,:,:,g*C+c], y_k, x_k) with     */
+/* y_k = ho*sh - ph + i*dh + dy_k and x_k = wo*sw - pw + j*dw + dx_k         */
+/* ([P-DCNv1] s1, [P-DCNv2] s1, [P-DCNv4] s1.1). With softmax != 0, m_k is  */
+/* the softmax over k of the mask values of (n, ho, wo, g).                 */
+/* ---------------------------------------------------------------------- */
+int oracle_dcn_core(const double *x, const double *offset, const double *mask,
+                    double *out, double *absum,
+                    int64_t N, int64_t H, int64_t W, int64_t G, int64_t C,
+                    int64_t kh, int64_t kw, int64_t sh, int64_t sw,
+                    int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                    float offset_scale, int softmax,
+                    const int64_t *pix, int64_t npix)
+{
+    int64_t Ho = out_size(H, kh, sh, ph, dh), Wo = out_size(W, kw, sw, pw, dw);
+    int64_t K = kh * kw, GC = G * C;
+    if (Ho <= 0 || Wo <= 0) return 1;
+    if (!pix) npix = N * Ho * Wo;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = 0; t < npix; ++t) {
+        int64_t p = pix ? pix[t] : t;
+        if (p < 0 || p >= N * Ho * Wo) { bad = 1; continue; }
+        int64_t n = p / (Ho * Wo), ho = (p / Wo) % Ho, wo = p % Wo;
+        double *m = (double *)malloc(sizeof(double) * (size_t)K);
+        for (int64_t g = 0; g < G; ++g) {
+            const double *om = offset + (p * G + g) * K * 2;
+            const double *mm = mask ? mask + (p * G + g) * K : NULL;
+            for (int64_t k = 0; k < K; ++k) m[k] = mm ? mm[k] : 1.0;
+            if (softmax) softmax_d(mm ? mm : m, K, 1, m);
+            for (int64_t c = 0; c < C; ++c) {
+                const double *X = x + n * H * W * GC + g * C + c;
+                double s = 0.0, a = 0.0;
+                for (int64_t i = 0; i < kh; ++i) {
+                    for (int64_t j = 0; j < kw; ++j) {
+                        int64_t k = i * kw + j;
+                        double yy = (double)(ho * sh - ph + i * dh) + fl32_mul(offset_scale, om[2 * k + 1]);
+                        double xx = (double)(wo * sw - pw + j * dw) + fl32_mul(offset_scale, om[2 * k + 0]);
+                        double ab = 0.0;
+                        double b = oracle_bilinear(X, H, W, GC, yy, xx, &ab);
+                        s += m[k] * b;
+                        a += fabs(m[k]) * ab;
+                    }
+                }
+                out[t * GC + g * C + c] = s;
+                if (absum) absum[t * GC + g * C + c] = a;
+            }
+        }
+        free(m);
+    }
+    return bad ? 2 : 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* DCNv2 deform-im2col column for one output pixel, NCHW.                   */
+/*  x      [N, Cin, H, W]                                                   */
+/*  offset [N, dg*K*2, Ho, Wo]: channel (g*K + k)*2 + 0 is dx, +1 is dy      */
+/*  mask   [N, dg*K, Ho, Wo] or NULL                                        */
+/*  col    [Cin*K] for pixel p: col[ci*K + k] = m * bilinear(x[n,ci], pos)  */
+/* Channel ci belongs to deformable group ci / (Cin/dg). With softmax != 0  */
+/* the K modulation values of each deformable group are softmax-normalised. */
+/* ---------------------------------------------------------------------- */
+static void v2_column(const double *x, const double *offset, const double *mask,
+                      double *col, double *colabs, int64_t p,
+                      int64_t Cin, int64_t H, int64_t W, int64_t Ho, int64_t Wo,
+                      int64_t kh, int64_t kw, int64_t sh, int64_t sw,
+                      int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                      int64_t dg, int softmax, double *m)
+{
+    int64_t K = kh * kw, HWo = Ho * Wo;
+    int64_t n = p / HWo, r = p % HWo, ho = r / Wo, wo = r % Wo;
+    int64_t cpg = Cin / dg;
+    for (int64_t g = 0; g < dg; ++g) {
+        for (int64_t k = 0; k < K; ++k)
+            m[k] = mask ? mask[(n * dg * K + g * K + k) * HWo + r] : 1.0;
+        if (softmax && mask)
+            softmax_d(mask + (n * dg * K + g * K) * HWo + r, K, HWo, m);
+        else if (softmax)
+            for (int64_t k = 0; k < K; ++k) m[k] = 1.0 / (double)K;
+        for (int64_t ci = g * cpg; ci < (g + 1) * cpg; ++ci) {
+            const double *X = x + (n * Cin + ci) * H * W;
+            for (int64_t i = 0; i < kh; ++i) {
+                for (int64_t j = 0; j < kw; ++j) {
+                    int64_t k = i * kw + j;
+                    int64_t oc = (n * dg * K + g * K + k) * 2;
+                    double dx = offset[(oc + 0) * HWo + r];
+                    double dy = offset[(oc + 1) * HWo + r];
+                    double yy = (double)(ho * sh - ph + i * dh) + dy;
+                    double xx = (double)(wo * sw - pw + j * dw) + dx;
+                    double ab = 0.0;
+                    double b = oracle_bilinear(X, H, W, 1, yy, xx, &ab);
+                    col[ci * K + k] = m[k] * b;
+                    if (colabs) colabs[ci * K + k] = fabs(m[k]) * ab;
+                }
+            }
+        }
+    }
+}
+
+/* Deform-im2col of the listed pixels: cols [npix, Cin*K] (row t = column of
+ * pixel pix[t], element ci*K + k). */
+int oracle_dcn_v2_columns(const double *x, const double *offset, const double *mask,
+                          double *cols,
+                          int64_t N, int64_t Cin, int64_t H, int64_t W,
+                          int64_t kh, int64_t kw, int64_t sh, int64_t sw,
+                          int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                          int64_t dg, int softmax, const int64_t *pix, int64_t npix)
+{
+    int64_t Ho = out_size(H, kh, sh, ph, dh), Wo = out_size(W, kw, sw, pw, dw);
+    int64_t K = kh * kw;
+    if (Ho <= 0 || Wo <= 0 || dg <= 0 || Cin % dg) return 1;
+    if (!pix) npix = N * Ho * Wo;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = 0; t < npix; ++t) {
+        int64_t p = pix ? pix[t] : t;
+        if (p < 0 || p >= N * Ho * Wo) { bad = 1; continue; }
+        double *m = (double *)malloc(sizeof(double) * (size_t)K);
+        v2_column(x, offset, mask, cols + t * Cin * K, NULL, p, Cin, H, W, Ho, Wo,
+                  kh, kw, sh, sw, ph, pw, dh, dw, dg, softmax, m);
+        free(m);
+    }
+    return bad ? 2 : 0;
+}
+
+/* DCNv2 modulated deformable convolution ([P-DCNv2] s1), NCHW:
+ *  weight [Cout, Cin, kh, kw]; out [npix, Cout] for the listed pixels, or
+ *  [N*Ho*Wo, Cout] (pixel-major) when pix == NULL.
+ *  out[p, co] = sum_{ci,k} weight[co, ci, k] * col_p[ci*K + k]. */
+int oracle_dcn_v2(const double *x, const double *offset, const double *mask,
+                  const double *weight, double *out, double *absum,
+                  int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
+                  int64_t kh, int64_t kw, int64_t sh, int64_t sw,
+                  int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                  int64_t dg, int softmax, const int64_t *pix, int64_t npix)
+{
+    int64_t Ho = out_size(H, kh, sh, ph, dh), Wo = out_size(W, kw, sw, pw, dw);
+    int64_t K = kh * kw, R = Cin * K;
+    if (Ho <= 0 || Wo <= 0 || dg <= 0 || Cin % dg) return 1;
+    if (!pix) npix = N * Ho * Wo;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = 0; t < npix; ++t) {
+        int64_t p = pix ? pix[t] : t;
+        if (p < 0 || p >= N * Ho * Wo) { bad = 1; continue; }
+        double *m = (double *)malloc(sizeof(double) * (size_t)K);
+        double *col = (double *)malloc(sizeof(double) * (size_t)R);
+        double *cab = (double *)malloc(sizeof(double) * (size_t)R);
+        v2_column(x, offset, mask, col, cab, p, Cin, H, W, Ho, Wo,
+                  kh, kw, sh, sw, ph, pw, dh, dw, dg, softmax, m);
+        for (int64_t co = 0; co < Cout; ++co) {
+            const double *wr = weight + co * R;
+            double s = 0.0, a = 0.0;
+            for (int64_t rr = 0; rr < R; ++rr) {
+                s += wr[rr] * col[rr];
+                a += fabs(wr[rr]) * cab[rr];
+            }
+            out[t * Cout + co] = s;
+            if (absum) absum[t * Cout + co] = a;
+        }
+        free(cab);
+        free(col);
+        free(m);
+    }
+    return bad ? 2 : 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Multi-camera multi-scale deformable aggregation ([P-AGG] s2.1-2.2, s7).  */
+/*  feat   [B, P_total, G*Cg]; map (cam, s) occupies rows                    */
+/*         scale_start[cam, s] + h*W_s + w, with (H_s, W_s) = spatial_shape  */
+/*  loc    [B, A, pts, cams, 2] (u, v) normalised to the camera image        */
+/*  weights[B, A, pts, cams, scales, G] (logits when softmax != 0)           */
+/*  out    [nanch, G*Cg] for the listed (b*A + a) anchors, or [B*A, G*Cg].   */
+/* Pixel coordinate: x = fl32(u*W_s) - 0.5, y = fl32(v*H_s) - 0.5.           */
+/* ---------------------------------------------------------------------- */
+int oracle_deform_agg(const double *feat, const int32_t *spatial_shape,
+                      const int32_t *scale_start, const double *loc,
+                      const double *weights, double *out, double *absum,
+                      int64_t B, int64_t P_total, int64_t A, int64_t pts,
+                      int64_t cams, int64_t scales, int64_t G, int64_t Cg,
+                      int softmax, const int64_t *anch, int64_t nanch)
+{
+    int64_t GC = G * Cg, T = pts * cams * scales;
+    for (int64_t cs = 0; cs < cams * scales; ++cs) {
+        int64_t Hs = spatial_shape[2 * cs], Ws = spatial_shape[2 * cs + 1];
+        if (Hs <= 0 || Ws <= 0 || scale_start[cs] < 0 || scale_start[cs] + Hs * Ws > P_total)
+            return 1;
+    }
+    if (!anch) nanch = B * A;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = 0; t < nanch; ++t) {
+        int64_t ba = anch ? anch[t] : t;
+        if (ba < 0 || ba >= B * A) { bad = 1; continue; }
+        int64_t b = ba / A;
+        double *w = (double *)malloc(sizeof(double) * (size_t)T);
+        for (int64_t g = 0; g < G; ++g) {
+            /* weights of (b, a, g) over (p, cam, s) */
+            const double *wl = weights + ba * T * G + g;
+            if (softmax) {
+                softmax_d(wl, T, G, w);
+            } else {
+                for (int64_t i = 0; i < T; ++i) w[i] = wl[i * G];
+            }
+            for (int64_t c = 0; c < Cg; ++c) {
+                double s = 0.0, a = 0.0;
+                for (int64_t p = 0; p < pts; ++p) {
+                    for (int64_t cam = 0; cam < cams; ++cam) {
+                        const double *uv = loc + ((ba * pts + p) * cams + cam) * 2;
+                        for (int64_t sc = 0; sc < scales; ++sc) {
+                            int64_t cs = cam * scales + sc;
+                            int64_t Hs = spatial_shape[2 * cs], Ws = spatial_shape[2 * cs + 1];
+                            double xx = (double)(float)(uv[0] * (double)Ws) - 0.5;
+                            double yy = (double)(float)(uv[1] * (double)Hs) - 0.5;
+                            const double *X = feat + (b * P_total + scale_start[cs]) * GC + g * Cg + c;
+                            double ab = 0.0;
+                            double v = oracle_bilinear(X, Hs, Ws, GC, yy, xx, &ab);
+                            double wi = w[(p * cams + cam) * scales + sc];
+                            s += wi * v;
+                            a += fabs(wi) * ab;
+                        }
+                    }
+                }
+                out[t * GC + g * Cg + c] = s;
+                if (absum) absum[t * GC + g * Cg + c] = a;
+            }
+        }
+        free(w);
+    }
+    return bad ? 2 : 0;
+}

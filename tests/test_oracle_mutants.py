@@ -1,0 +1,78 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a copy of oracle.c (a swapped pair, a wrong sign
+or index, a dropped term, a transposed operand), builds it with gcc into a
+temporary library, and runs the pin suite against it in a subprocess. The pins
+must fail for every mutant; the unmodified source must pass.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+# (name, text in oracle.c, replacement, occurrence to replace: 1-based)
+MUTANTS = [
+    ("core_swap_dx_dy", "fl32_mul(offset_scale, om[2 * k + 1])", "fl32_mul(offset_scale, om[2 * k + 0])", 1),
+    ("core_pad_sign", "(double)(ho * sh - ph + i * dh)", "(double)(ho * sh + ph + i * dh)", 1),
+    ("core_no_dilation", "(double)(wo * sw - pw + j * dw)", "(double)(wo * sw - pw + j)", 1),
+    ("core_point_order_col_major", "int64_t k = i * kw + j;", "int64_t k = j * kh + i;", 1),
+    ("core_group_channel_base", "x + n * H * W * GC + g * C + c", "x + n * H * W * GC + c", 1),
+    ("core_mask_group_stride", "mask + (p * G + g) * K", "mask + p * K", 1),
+    ("bilinear_weights_transposed", "double wx[2] = {1.0 - fx, fx};", "double wx[2] = {fx, 1.0 - fx};", 1),
+    ("bilinear_drop_corner", "for (int dx = 0; dx < 2; ++dx)", "for (int dx = 0; dx < 1; ++dx)", 1),
+    ("bilinear_edge_off_by_one", "qy >= (double)H", "qy > (double)H", 1),
+    ("softmax_no_max_shift", "m[i] = exp(l[i * lstride] - mx);", "m[i] = exp(l[i * lstride]);", 1),
+    ("softmax_no_normalise", "for (int64_t i = 0; i < n; ++i) m[i] /= den;", "", 1),
+    ("v2_swap_dx_dy", "double dx = offset[(oc + 0) * HWo + r];", "double dx = offset[(oc + 1) * HWo + r];", 1),
+    ("v2_mask_ignores_group", "mask[(n * dg * K + g * K + k) * HWo + r]", "mask[(n * dg * K + k) * HWo + r]", 1),
+    ("v2_weight_transposed", "s += wr[rr] * col[rr];", "s += weight[(rr % Cout) * R + rr / Cout] * col[rr];", 1),
+    ("v2_point_order_col_major", "int64_t k = i * kw + j;", "int64_t k = j * kh + i;", 2),
+    ("agg_no_half_pixel", "(double)(float)(uv[0] * (double)Ws) - 0.5", "(double)(float)(uv[0] * (double)Ws)", 1),
+    ("agg_uv_swapped", "double yy = (double)(float)(uv[1] * (double)Hs) - 0.5;",
+     "double yy = (double)(float)(uv[0] * (double)Hs) - 0.5;", 1),
+    ("agg_weight_order", "w[(p * cams + cam) * scales + sc]", "w[(sc * cams + cam) * pts + p]", 1),
+    ("agg_ignores_scale_start", "(b * P_total + scale_start[cs]) * GC", "(b * P_total) * GC", 1),
+    ("agg_weight_group_stride", "weights + ba * T * G + g;", "weights + ba * T * G;", 1),
+]
+
+
+def _replace_nth(text, old, new, n):
+    idx = -1
+    for _ in range(n):
+        idx = text.find(old, idx + 1)
+        assert idx >= 0, "mutation anchor not found: %r (occurrence %d)" % (old, n)
+    return text[:idx] + new + text[idx + len(old):]
+
+
+def _build(src_text, tmp_path, name):
+    c = tmp_path / (name + ".c")
+    so = tmp_path / ("lib" + name + ".so")
+    c.write_text(src_text)
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
+                    "-o", str(so), str(c), "-lm"], check=True)
+    return str(so)
+
+
+def _run_pins(lib):
+    env = dict(os.environ, DS_ORACLE_LIB=lib, OMP_NUM_THREADS="2")
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                           os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+
+
+def test_unmodified_oracle_passes_pins(tmp_path):
+    lib = _build(open(SRC).read(), tmp_path, "orig")
+    res = _run_pins(lib)
+    assert res.returncode == 0, res.stdout[-3000:]
+
+
+@pytest.mark.parametrize("name,old,new,nth", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new, nth):
+    text = _replace_nth(open(SRC).read(), old, new, nth)
+    lib = _build(text, tmp_path, name)
+    res = _run_pins(lib)
+    assert res.returncode != 0, "mutant %s survived the pins" % name

@@ -1,0 +1,219 @@
+"""Seeded synthetic inputs for the deformable-sampling ops.
+
+This module is shared by the tests, the smoke check and the bench. It only draws
+random numbers and lays them out; it holds none of the sampling arithmetic
+(no bilinear weights, no positions, no softmax of the op), so neither the oracle
+nor the GPU path can lean on it for a result.
+
+Draws come from NumPy ``Generator(PCG64(seed))`` in float64, in a fixed order
+(features, offsets/locations, masks/logits, out-of-bounds selection, weights),
+and are then rounded once (round-to-nearest-even) to the tensor's dtype by torch.
+Everything returned is a CPU torch tensor.
+
+Named workloads (see ``WORKLOADS``) mirror the shapes and value distributions of
+the ops' typical uses: a DCNv4 block on a 32x32 map, a DCNv3 stage on 56x56
+maps, a DCNv4 layer at the stride-8 (80x80) level of a 640-pixel detector, a
+DCNv2 layer on 40x40 maps and a six-camera, four-scale aggregation with 900
+anchors. Real datasets (COCO, VisDrone, nuScenes, KITTI) are not used; these
+inputs stand in for them with the same tensor shapes.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _t(a: np.ndarray, dtype: str) -> torch.Tensor:
+    """float64 numpy -> torch tensor of the named dtype (one RNE rounding)."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).to(DTYPES[dtype]).contiguous()
+
+
+def out_size(n, k, s, p, d):
+    """Output extent of a strided, padded, dilated window (shape bookkeeping only)."""
+    return (n + 2 * p - d * (k - 1) - 1) // s + 1
+
+
+def _force_oob(r, offset, frac, H, W, pad_h, pad_w, ax_x=0, ax_y=1):
+    """Push a Bernoulli(frac) subset of taps fully outside the image.
+
+    A chosen tap gets, on a random side, an offset component of magnitude
+    (extent + pad + U(1, 8)) pixels: whatever the tap's grid base is (it lies in
+    [-pad, extent + pad - 1]), the sample then lands at least one pixel beyond
+    the image on that side, so all four bilinear corners are outside. The other
+    component keeps its normal draw. offset[..., 0] is dx, offset[..., 1] is dy.
+    """
+    shape = offset.shape[:-1]
+    pick = r.random(shape) < frac
+    side = r.integers(0, 4, size=shape)
+    dist = r.uniform(1.0, 8.0, size=shape)
+    top = pick & (side == 0)
+    bot = pick & (side == 1)
+    lef = pick & (side == 2)
+    rig = pick & (side == 3)
+    offset[..., ax_y][top] = -(H + pad_h + dist[top])
+    offset[..., ax_y][bot] = (H + pad_h + dist[bot])
+    offset[..., ax_x][lef] = -(W + pad_w + dist[lef])
+    offset[..., ax_x][rig] = (W + pad_w + dist[rig])
+    return pick
+
+
+def core_case(*, N, H, W, G, C, kh=3, kw=3, stride=(1, 1), pad=(1, 1), dil=(1, 1),
+              dtype="f32", offset_std=2.0, mask="uniform", oob_frac=0.0, seed=0,
+              x_kind="normal"):
+    """Inputs of the channels-last DCNv3/v4 core.
+
+    x      [N, H, W, G*C] of ``dtype``, N(0,1) (or small integers for x_kind="int")
+    offset [N, Ho, Wo, G, K, 2] fp32 (dx, dy) ~ N(0, offset_std) pixels
+    mask   [N, Ho, Wo, G, K] fp32: "uniform" U(0,1), "logits" N(0,1), "ones", None
+    """
+    r = rng(seed)
+    Ho, Wo = out_size(H, kh, stride[0], pad[0], dil[0]), out_size(W, kw, stride[1], pad[1], dil[1])
+    K = kh * kw
+    if x_kind == "int":
+        x = r.integers(-4, 5, size=(N, H, W, G * C)).astype(np.float64)
+    else:
+        x = r.standard_normal((N, H, W, G * C))
+    off = r.standard_normal((N, Ho, Wo, G, K, 2)) * offset_std
+    if mask == "uniform":
+        m = r.random((N, Ho, Wo, G, K))
+    elif mask == "logits":
+        m = r.standard_normal((N, Ho, Wo, G, K))
+    elif mask == "ones":
+        m = np.ones((N, Ho, Wo, G, K))
+    else:
+        m = None
+    oob = None
+    if oob_frac > 0:
+        oob = _force_oob(r, off, oob_frac, H, W, pad[0], pad[1])
+    return dict(
+        x=_t(x, dtype), offset=_t(off, "f32"), mask=None if m is None else _t(m, "f32"),
+        oob=oob, N=N, H=H, W=W, G=G, C=C, kh=kh, kw=kw, stride=tuple(stride), pad=tuple(pad),
+        dil=tuple(dil), Ho=Ho, Wo=Wo, dtype=dtype, softmax=(mask == "logits"))
+
+
+def v2_case(*, N, Cin, H, W, Cout, kh=3, kw=3, stride=(1, 1), pad=(1, 1), dil=(1, 1),
+            dg=1, dtype="bf16", offset_std=2.0, mask="sigmoid", w_std=0.02, seed=0,
+            x_kind="normal"):
+    """Inputs of the NCHW DCNv2 (modulated deformable convolution).
+
+    x      [N, Cin, H, W] dtype ~ N(0,1)
+    offset [N, dg*K*2, Ho, Wo] fp32 ~ N(0, offset_std); channel (g*K+k)*2 is dx, +1 is dy
+    mask   [N, dg*K, Ho, Wo] fp32: "sigmoid" = sigmoid of N(0,1) draws (the module
+           applies the sigmoid before the op), "uniform", "ones", "logits" or None
+    weight [Cout, Cin, kh, kw] dtype ~ N(0, w_std)
+    """
+    r = rng(seed)
+    Ho, Wo = out_size(H, kh, stride[0], pad[0], dil[0]), out_size(W, kw, stride[1], pad[1], dil[1])
+    K = kh * kw
+    if x_kind == "int":
+        x = r.integers(-4, 5, size=(N, Cin, H, W)).astype(np.float64)
+    else:
+        x = r.standard_normal((N, Cin, H, W))
+    off = r.standard_normal((N, dg * K * 2, Ho, Wo)) * offset_std
+    if mask == "sigmoid":
+        m = 1.0 / (1.0 + np.exp(-r.standard_normal((N, dg * K, Ho, Wo))))
+    elif mask == "uniform":
+        m = r.random((N, dg * K, Ho, Wo))
+    elif mask == "logits":
+        m = r.standard_normal((N, dg * K, Ho, Wo))
+    elif mask == "ones":
+        m = np.ones((N, dg * K, Ho, Wo))
+    else:
+        m = None
+    if x_kind == "int":
+        w = r.integers(-2, 3, size=(Cout, Cin, kh, kw)).astype(np.float64)
+    else:
+        w = r.standard_normal((Cout, Cin, kh, kw)) * w_std
+    return dict(
+        x=_t(x, dtype), offset=_t(off, "f32"), mask=None if m is None else _t(m, "f32"),
+        weight=_t(w, dtype), N=N, Cin=Cin, H=H, W=W, Cout=Cout, kh=kh, kw=kw,
+        stride=tuple(stride), pad=tuple(pad), dil=tuple(dil), dg=dg, Ho=Ho, Wo=Wo,
+        dtype=dtype, softmax=(mask == "logits"))
+
+
+def agg_case(*, B, shapes, A, pts, G, Cg, dtype="f32", weights="logits", seed=0,
+             cam_major=True, loc_lo=0.0, loc_hi=1.0):
+    """Inputs of the multi-camera multi-scale aggregation.
+
+    shapes       list over cameras of lists over scales of (H, W)
+    feat         [B, P_total, G*Cg] ~ N(0,1); maps flattened cam-major (cam, scale,
+                 h, w) when cam_major, else scale-major (scale, cam, h, w)
+    spatial_shape int32 [cams, scales, 2] (H, W); scale_start int32 [cams, scales]
+    loc          [B, A, pts, cams, 2] (u, v) ~ U(loc_lo, loc_hi)
+    weights      [B, A, pts, cams, scales, G]: "logits" N(0,1) (for the op's softmax),
+                 "simplex" = normalised Exp(1) draws (a uniform point of the simplex
+                 per (b, a, g), for runs without the softmax) or "ones"
+    """
+    r = rng(seed)
+    cams, scales = len(shapes), len(shapes[0])
+    ss = np.array(shapes, dtype=np.int32).reshape(cams, scales, 2)
+    st = np.zeros((cams, scales), np.int32)
+    pos = 0
+    order = [(c, s) for c in range(cams) for s in range(scales)] if cam_major else \
+            [(c, s) for s in range(scales) for c in range(cams)]
+    for c, s in order:
+        st[c, s] = pos
+        pos += int(ss[c, s, 0]) * int(ss[c, s, 1])
+    P_total = pos
+    feat = r.standard_normal((B, P_total, G * Cg))
+    loc = r.uniform(loc_lo, loc_hi, size=(B, A, pts, cams, 2))
+    if weights == "logits":
+        w = r.standard_normal((B, A, pts, cams, scales, G))
+    elif weights == "simplex":
+        e = r.exponential(1.0, size=(B, A, pts, cams, scales, G))
+        w = e / e.sum(axis=(2, 3, 4), keepdims=True)
+    else:
+        w = np.ones((B, A, pts, cams, scales, G))
+    return dict(
+        feat=_t(feat, dtype), spatial_shape=ss, scale_start=st, loc=_t(loc, "f32"),
+        weights=_t(w, "f32"), B=B, P_total=P_total, A=A, pts=pts, cams=cams, scales=scales,
+        G=G, Cg=Cg, dtype=dtype, softmax=(weights == "logits"))
+
+
+# Named workloads: the five shapes the ops are exercised and measured on.
+SPARSE4D_SHAPES = [[(64, 176), (32, 88), (16, 44), (8, 22)]] * 6
+
+WORKLOADS = {
+    # DCNv4 block, fp32, one 32x32 map with 4 groups of 16 channels.
+    "dcnv4_f32_n1_32x32_g4c16": dict(
+        op="core", seed=1001,
+        args=dict(N=1, H=32, W=32, G=4, C=16, dtype="f32", offset_std=2.0, mask="uniform")),
+    # DCNv3 stage, fp32, batch 8 of 56x56 maps, softmax over the 9 points.
+    "dcnv3_f32_n8_56x56_g4c16_softmax": dict(
+        op="core", seed=1002,
+        args=dict(N=8, H=56, W=56, G=4, C=16, dtype="f32", offset_std=1.5, mask="logits")),
+    # DCNv4 at the stride-8 level of a 640-pixel detector: fp16 x [16,80,80,256].
+    "dcnv4_f16_n16_80x80_g16c16": dict(
+        op="core", seed=1003,
+        args=dict(N=16, H=80, W=80, G=16, C=16, dtype="f16", offset_std=3.0, mask="uniform",
+                  oob_frac=0.05)),
+    # DCNv2 modulated deformable conv, bf16, 8x256x40x40 -> 8x256x40x40.
+    "dcnv2_bf16_n8_c256_40x40": dict(
+        op="v2", seed=1004,
+        args=dict(N=8, Cin=256, H=40, W=40, Cout=256, dtype="bf16", offset_std=2.0,
+                  mask="sigmoid", w_std=0.02)),
+    # Six-camera, four-scale aggregation, 900 anchors x 13 points, 8 groups of 32.
+    "agg_f32_6cam_4scale_a900p13_g8c32": dict(
+        op="agg", seed=1005,
+        args=dict(B=1, shapes=SPARSE4D_SHAPES, A=900, pts=13, G=8, Cg=32, dtype="f32",
+                  weights="logits")),
+}
+
+
+def make(name: str, **override):
+    """Build a named workload (optionally overriding some of its arguments)."""
+    spec = WORKLOADS[name]
+    args = dict(spec["args"])
+    args.update(override)
+    seed = args.pop("seed", spec["seed"])
+    fn = {"core": core_case, "v2": v2_case, "agg": agg_case}[spec["op"]]
+    case = fn(seed=seed, **args)
+    case["op"] = spec["op"]
+    case["name"] = name
+    return case
