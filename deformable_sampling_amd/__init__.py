@@ -1,0 +1,212 @@
+"""deformable_sampling_amd — MI355X (gfx950) deformable sampling.
+
+Thin ctypes binding over the C ABI of ``libdcn.so`` (declared in ``include/dcn.h``).
+Each function below has the name of the C entry point it calls and only marshals
+arguments: it checks device, dtype and contiguity of torch tensors, passes their
+device pointers and torch's current HIP stream, and raises on a non-OK status.
+Every step of the computation runs in the library's HIP kernels; there is no
+CPU or PyTorch fallback, and a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdcn.so")
+
+DCN_F32, DCN_F16, DCN_BF16 = 0, 1, 2
+_DTYPE_ID = {torch.float32: DCN_F32, torch.float16: DCN_F16, torch.bfloat16: DCN_BF16}
+
+STATUS = {0: "DCN_OK", 1: "DCN_ERR_NULL", 2: "DCN_ERR_SHAPE", 3: "DCN_ERR_PARAM",
+          4: "DCN_ERR_DTYPE", 5: "DCN_ERR_ALIGN", 6: "DCN_ERR_WORKSPACE", 7: "DCN_ERR_HIP"}
+
+# every symbol include/dcn.h declares
+EXPORTS = ("dcn_core_forward", "dcn_v2_workspace_bytes", "dcn_v2_forward",
+           "deform_agg_forward", "dcn_status_string", "dcn_last_hip_error")
+
+
+class DcnError(RuntimeError):
+    def __init__(self, fn, status, lib):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        msg = "%s failed: %s (%s)" % (fn, self.name, lib.dcn_status_string(status).decode())
+        if status == 7:
+            msg += ", hipError %d" % lib.dcn_last_hip_error()
+        super().__init__(msg)
+
+
+_lib = None
+_c = ctypes
+
+
+def load(path: str | None = None):
+    """Load libdcn.so (built by ``deformable_sampling_amd.build``); raise if missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError(
+            "libdcn.so not found at %s; build it with `python -m deformable_sampling_amd.build`" % p)
+    lib = ctypes.CDLL(p)
+    i, f, vp = _c.c_int, _c.c_float, _c.c_void_p
+    lib.dcn_core_forward.restype = i
+    lib.dcn_core_forward.argtypes = [vp, vp, vp, vp] + [i] * 13 + [f, i, i, vp]
+    lib.dcn_v2_workspace_bytes.restype = _c.c_size_t
+    lib.dcn_v2_workspace_bytes.argtypes = [i] * 13 + [i]
+    lib.dcn_v2_forward.restype = i
+    lib.dcn_v2_forward.argtypes = [vp, vp, vp, vp, vp, vp, _c.c_size_t] + [i] * 15 + [i, vp]
+    lib.deform_agg_forward.restype = i
+    lib.deform_agg_forward.argtypes = [vp, vp, vp, vp, vp, vp] + [i] * 9 + [i, vp]
+    lib.dcn_status_string.restype = _c.c_char_p
+    lib.dcn_status_string.argtypes = [i]
+    lib.dcn_last_hip_error.restype = i
+    lib.dcn_last_hip_error.argtypes = []
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return int(stream)
+    if torch.cuda.is_available():
+        return torch.cuda.current_stream().cuda_stream
+    return None
+
+
+def _check(t, name, dtype=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return
+        raise ValueError("%s is required" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def _pair(v):
+    return (v, v) if isinstance(v, int) else tuple(v)
+
+
+def out_size(n, k, s, p, d):
+    return (n + 2 * p - d * (k - 1) - 1) // s + 1
+
+
+def _call(fn, *args):
+    lib = load()
+    st = getattr(lib, fn)(*args)
+    if st != 0:
+        raise DcnError(fn, st, lib)
+
+
+def dcn_core_forward(x, offset, mask, out=None, *, kernel=(3, 3), stride=1, pad=1, dilation=1,
+                     offset_scale=1.0, softmax=False, stream=None):
+    """DCNv3/v4 core. x [N,H,W,G*C]; offset [N,Ho,Wo,G,K,2] fp32 (dx,dy); mask
+    [N,Ho,Wo,G,K] fp32 or None (logits if softmax). Returns out [N,Ho,Wo,G*C]."""
+    kh, kw = _pair(kernel)
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    dh, dw = _pair(dilation)
+    _check(x, "x")
+    _check(offset, "offset", torch.float32)
+    _check(mask, "mask", torch.float32, allow_none=True)
+    N, H, W, GC = x.shape
+    G = offset.shape[3]
+    if offset.dim() != 6 or offset.shape[4] != kh * kw or offset.shape[5] != 2 or GC % G:
+        raise ValueError("offset must be [N,Ho,Wo,G,K,2] with G dividing the channels")
+    Ho, Wo = out_size(H, kh, sh, ph, dh), out_size(W, kw, sw, pw, dw)
+    if tuple(offset.shape[:3]) != (N, Ho, Wo):
+        raise ValueError("offset spatial shape %s != %s" % (tuple(offset.shape[:3]), (N, Ho, Wo)))
+    if mask is not None and tuple(mask.shape) != (N, Ho, Wo, G, kh * kw):
+        raise ValueError("mask must be [N,Ho,Wo,G,K]")
+    if out is None:
+        out = torch.empty((N, Ho, Wo, GC), dtype=x.dtype, device=x.device)
+    _check(out, "out", x.dtype)
+    _call("dcn_core_forward", _ptr(x), _ptr(offset), _ptr(mask), _ptr(out), N, H, W, G, GC // G,
+          kh, kw, sh, sw, ph, pw, dh, dw, float(offset_scale), int(bool(softmax)),
+          _DTYPE_ID[x.dtype], _stream(stream))
+    return out
+
+
+def dcn_v2_workspace_bytes(N, Cin, H, W, Cout, kernel=(3, 3), stride=1, pad=1, dilation=1,
+                           dtype=torch.bfloat16):
+    kh, kw = _pair(kernel)
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    dh, dw = _pair(dilation)
+    return int(load().dcn_v2_workspace_bytes(N, Cin, H, W, Cout, kh, kw, sh, sw, ph, pw, dh, dw,
+                                             _DTYPE_ID[dtype]))
+
+
+def dcn_v2_forward(x, offset, mask, weight, out=None, workspace=None, *, stride=1, pad=1,
+                   dilation=1, deform_groups=None, softmax=False, stream=None):
+    """DCNv2. x [N,Cin,H,W] bf16/fp16; offset [N,dg*K*2,Ho,Wo] fp32; mask [N,dg*K,Ho,Wo]
+    fp32 or None; weight [Cout,Cin,kh,kw]. Returns out [N,Cout,Ho,Wo]."""
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    dh, dw = _pair(dilation)
+    _check(x, "x")
+    _check(weight, "weight", x.dtype)
+    _check(offset, "offset", torch.float32)
+    _check(mask, "mask", torch.float32, allow_none=True)
+    N, Cin, H, W = x.shape
+    Cout, Cin_w, kh, kw = weight.shape
+    if Cin_w != Cin:
+        raise ValueError("weight has %d input channels, x has %d" % (Cin_w, Cin))
+    K = kh * kw
+    dg = deform_groups if deform_groups is not None else offset.shape[1] // (2 * K)
+    Ho, Wo = out_size(H, kh, sh, ph, dh), out_size(W, kw, sw, pw, dw)
+    if tuple(offset.shape) != (N, dg * K * 2, Ho, Wo):
+        raise ValueError("offset must be [N, dg*K*2, Ho, Wo]")
+    if mask is not None and tuple(mask.shape) != (N, dg * K, Ho, Wo):
+        raise ValueError("mask must be [N, dg*K, Ho, Wo]")
+    if out is None:
+        out = torch.empty((N, Cout, Ho, Wo), dtype=x.dtype, device=x.device)
+    _check(out, "out", x.dtype)
+    need = dcn_v2_workspace_bytes(N, Cin, H, W, Cout, (kh, kw), (sh, sw), (ph, pw), (dh, dw), x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _call("dcn_v2_forward", _ptr(x), _ptr(offset), _ptr(mask), _ptr(weight), _ptr(out),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), N, Cin, H, W, Cout, kh, kw,
+          sh, sw, ph, pw, dh, dw, dg, int(bool(softmax)), _DTYPE_ID[x.dtype], _stream(stream))
+    return out
+
+
+def deform_agg_forward(feat, spatial_shape, scale_start, loc, weights, out=None, *, softmax=False,
+                       stream=None):
+    """Aggregation. feat [B,P_total,G*Cg]; spatial_shape int [cams,scales,2] (host);
+    scale_start int [cams,scales] (host); loc [B,A,pts,cams,2] fp32; weights
+    [B,A,pts,cams,scales,G] fp32. Returns out [B,A,G*Cg]."""
+    import numpy as np
+    _check(feat, "feat")
+    _check(loc, "loc", torch.float32)
+    _check(weights, "weights", torch.float32)
+    ss = np.ascontiguousarray(np.asarray(
+        spatial_shape.cpu() if hasattr(spatial_shape, "cpu") else spatial_shape, dtype=np.int32))
+    st = np.ascontiguousarray(np.asarray(
+        scale_start.cpu() if hasattr(scale_start, "cpu") else scale_start, dtype=np.int32))
+    B, P_total, GC = feat.shape
+    _, A, pts, cams, two = loc.shape
+    scales, G = weights.shape[4], weights.shape[5]
+    if two != 2 or tuple(weights.shape) != (B, A, pts, cams, scales, G) or GC % G:
+        raise ValueError("loc must be [B,A,pts,cams,2] and weights [B,A,pts,cams,scales,G]")
+    if ss.shape != (cams, scales, 2) or st.shape != (cams, scales):
+        raise ValueError("spatial_shape must be [cams,scales,2] and scale_start [cams,scales]")
+    if out is None:
+        out = torch.empty((B, A, GC), dtype=feat.dtype, device=feat.device)
+    _check(out, "out", feat.dtype)
+    _call("deform_agg_forward", _ptr(feat), ss.ctypes.data, st.ctypes.data, _ptr(loc),
+          _ptr(weights), _ptr(out), B, P_total, A, pts, cams, scales, G, GC // G,
+          int(bool(softmax)), _DTYPE_ID[feat.dtype], _stream(stream))
+    return out

@@ -1,0 +1,174 @@
+// C ABI of libdcn: argument validation on the host, then dispatch to the kernels.
+// Every check below runs before any HIP API call, so a rejected call has no effect
+// (this also lets the checks be exercised on a machine without a GPU).
+#include <stdint.h>
+
+#include "dcn.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr long long kI32 = 2147483647LL;
+
+bool valid_dtype(dcn_dtype d) { return d == DCN_F32 || d == DCN_F16 || d == DCN_BF16; }
+size_t dtype_size(dcn_dtype d) { return d == DCN_F32 ? 4 : 2; }
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+long long out_extent(int in, int k, int s, int p, int d) {
+    return ((long long)in + 2LL * p - (long long)d * (k - 1) - 1) / s + 1;
+}
+
+dcn_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return DCN_OK;
+    g_last_hip_error = (int)e;
+    return DCN_ERR_HIP;
+}
+
+// Shared window checks of the core and DCNv2 paths.
+dcn_status check_window(int kh, int kw, int sh, int sw, int ph, int pw, int dh, int dw) {
+    if (kh <= 0 || kw <= 0) return DCN_ERR_SHAPE;
+    if ((long long)kh * kw > 64) return DCN_ERR_SHAPE;
+    if (sh <= 0 || sw <= 0 || dh <= 0 || dw <= 0 || ph < 0 || pw < 0) return DCN_ERR_PARAM;
+    return DCN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dcn_status_string(dcn_status s) {
+    switch (s) {
+        case DCN_OK: return "ok";
+        case DCN_ERR_NULL: return "null pointer";
+        case DCN_ERR_SHAPE: return "invalid shape or size limit exceeded";
+        case DCN_ERR_PARAM: return "invalid parameter";
+        case DCN_ERR_DTYPE: return "unsupported dtype";
+        case DCN_ERR_ALIGN: return "misaligned pointer";
+        case DCN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case DCN_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+int dcn_last_hip_error(void) { return g_last_hip_error; }
+
+dcn_status dcn_core_forward(const void *x, const float *offset, const float *mask, void *out,
+                            int N, int H, int W, int G, int C, int kh, int kw, int stride_h,
+                            int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                            float offset_scale, int softmax, dcn_dtype dtype, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return DCN_ERR_DTYPE;
+    if (N < 0 || H <= 0 || W <= 0 || G <= 0 || C <= 0) return DCN_ERR_SHAPE;
+    dcn_status st = check_window(kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w);
+    if (st != DCN_OK) return st;
+    const long long Ho = out_extent(H, kh, stride_h, pad_h, dil_h);
+    const long long Wo = out_extent(W, kw, stride_w, pad_w, dil_w);
+    if (Ho <= 0 || Wo <= 0) return DCN_ERR_SHAPE;
+    // index limits of the kernels (32-bit pair and in-image element offsets)
+    if ((long long)(H + 1) * (W + 1) * G * C > kI32) return DCN_ERR_SHAPE;
+    if ((long long)N * Ho * Wo * G > kI32) return DCN_ERR_SHAPE;
+    if (N == 0) return DCN_OK;
+    if (!x || !offset || !out) return DCN_ERR_NULL;
+    const size_t es = dtype_size(dtype);
+    if (!aligned(x, es) || !aligned(out, es) || !aligned(offset, 4) ||
+        (mask && !aligned(mask, 4)))
+        return DCN_ERR_ALIGN;
+
+    dcn::CoreLaunch a;
+    a.x = x; a.offset = offset; a.mask = mask; a.out = out;
+    a.N = N; a.H = H; a.W = W; a.G = G; a.C = C; a.kh = kh; a.kw = kw;
+    a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w; a.dh = dil_h; a.dw = dil_w;
+    a.Ho = (int)Ho; a.Wo = (int)Wo;
+    a.offset_scale = offset_scale;
+    a.softmax = softmax;
+    a.dtype = dtype;
+    return hip_status(dcn::launch_dcn_core(a, stream));
+}
+
+size_t dcn_v2_workspace_bytes(int N, int Cin, int H, int W, int Cout, int kh, int kw, int stride_h,
+                              int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                              dcn_dtype dtype) {
+    if (check_window(kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w) != DCN_OK) return 0;
+    if (H <= 0 || W <= 0) return 0;
+    dcn::V2Plan plan;
+    if (!dcn::plan_dcn_v2(N, Cin, H, W, Cout, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h,
+                          dil_w, dtype, plan))
+        return 0;
+    return plan.total;
+}
+
+dcn_status dcn_v2_forward(const void *x, const float *offset, const float *mask, const void *weight,
+                          void *out, void *workspace, size_t workspace_bytes, int N, int Cin, int H,
+                          int W, int Cout, int kh, int kw, int stride_h, int stride_w, int pad_h,
+                          int pad_w, int dil_h, int dil_w, int deform_groups, int softmax,
+                          dcn_dtype dtype, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return DCN_ERR_DTYPE;
+    if (dtype == DCN_F32) return DCN_ERR_DTYPE;
+    if (N < 0 || Cin <= 0 || H <= 0 || W <= 0 || Cout <= 0) return DCN_ERR_SHAPE;
+    dcn_status st = check_window(kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w);
+    if (st != DCN_OK) return st;
+    if (deform_groups <= 0 || Cin % deform_groups != 0) return DCN_ERR_PARAM;
+    if (deform_groups > 1 && (Cin / deform_groups) % 8 != 0) return DCN_ERR_PARAM;
+    dcn::V2Plan plan;
+    if (!dcn::plan_dcn_v2(N, Cin, H, W, Cout, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h,
+                          dil_w, dtype, plan))
+        return DCN_ERR_SHAPE;
+    // 32-bit limits of the kernels' in-image offsets and pixel counts
+    if ((long long)(H + 1) * (W + 1) * plan.Cin_pad > kI32) return DCN_ERR_SHAPE;
+    if (plan.Pp > kI32 || (long long)N * Cin * H * W > (1LL << 40)) return DCN_ERR_SHAPE;
+    if (N == 0) return DCN_OK;
+    if (!x || !offset || !weight || !out) return DCN_ERR_NULL;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < plan.total)
+        return DCN_ERR_WORKSPACE;
+    if (!aligned(x, 2) || !aligned(weight, 2) || !aligned(out, 2) || !aligned(offset, 4) ||
+        (mask && !aligned(mask, 4)))
+        return DCN_ERR_ALIGN;
+
+    dcn::V2Launch a;
+    a.x = x; a.offset = offset; a.mask = mask; a.weight = weight; a.out = out;
+    a.workspace = workspace;
+    a.N = N; a.Cin = Cin; a.H = H; a.W = W; a.Cout = Cout; a.kh = kh; a.kw = kw;
+    a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w; a.dh = dil_h; a.dw = dil_w;
+    a.dg = deform_groups;
+    a.softmax = softmax;
+    a.dtype = dtype;
+    a.plan = plan;
+    return hip_status(dcn::launch_dcn_v2(a, stream));
+}
+
+dcn_status deform_agg_forward(const void *feat, const int32_t *spatial_shape,
+                              const int32_t *scale_start, const float *loc, const float *weights,
+                              void *out, int B, int P_total, int A, int pts, int cams, int scales,
+                              int G, int Cg, int softmax, dcn_dtype dtype, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return DCN_ERR_DTYPE;
+    if (B < 0 || A < 0 || P_total <= 0 || pts <= 0 || cams <= 0 || scales <= 0 || G <= 0 ||
+        Cg <= 0)
+        return DCN_ERR_SHAPE;
+    if ((long long)cams * scales > dcn::kAggMaxMaps) return DCN_ERR_SHAPE;
+    if ((long long)B * P_total * G * Cg > kI32) return DCN_ERR_SHAPE;
+    if ((long long)B * A * G > kI32) return DCN_ERR_SHAPE;
+    if ((long long)pts * cams * scales * G > kI32) return DCN_ERR_SHAPE;
+    if (!spatial_shape || !scale_start) return DCN_ERR_NULL;
+    dcn::AggLaunch a;
+    for (int i = 0; i < cams * scales; ++i) {
+        const int h = spatial_shape[2 * i], w = spatial_shape[2 * i + 1], s0 = scale_start[i];
+        if (h <= 0 || w <= 0 || s0 < 0) return DCN_ERR_SHAPE;
+        if ((long long)s0 + (long long)h * w > P_total) return DCN_ERR_SHAPE;
+        a.maps.H[i] = h;
+        a.maps.W[i] = w;
+        a.maps.start[i] = s0;
+    }
+    if (B == 0 || A == 0) return DCN_OK;
+    if (!feat || !loc || !weights || !out) return DCN_ERR_NULL;
+    const size_t es = dtype_size(dtype);
+    if (!aligned(feat, es) || !aligned(out, es) || !aligned(loc, 8) || !aligned(weights, 4))
+        return DCN_ERR_ALIGN;
+    a.feat = feat; a.loc = loc; a.weights = weights; a.out = out;
+    a.B = B; a.P_total = P_total; a.A = A; a.pts = pts; a.cams = cams; a.scales = scales;
+    a.G = G; a.Cg = Cg; a.softmax = softmax;
+    a.dtype = dtype;
+    return hip_status(dcn::launch_deform_agg(a, stream));
+}
+
+}  // extern "C"

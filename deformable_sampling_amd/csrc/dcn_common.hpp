@@ -1,0 +1,157 @@
+// Device helpers shared by the deformable-sampling kernels (gfx950 / CDNA4).
+//
+// Element types are handled as raw bits: fp32, fp16 (IEEE binary16) and bf16.
+// Loads and stores move 2/4/8/16 bytes per lane; arithmetic is always fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dcn.h"
+
+namespace dcn {
+
+// ---------------------------------------------------------------- elements --
+
+struct EF32 { using bits = uint32_t; static constexpr dcn_dtype id = DCN_F32; };
+struct EF16 { using bits = uint16_t; static constexpr dcn_dtype id = DCN_F16; };
+struct EBF16 { using bits = uint16_t; static constexpr dcn_dtype id = DCN_BF16; };
+
+__device__ __forceinline__ float to_f32(EF32, uint32_t b) { return __uint_as_float(b); }
+__device__ __forceinline__ float to_f32(EF16, uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+__device__ __forceinline__ float to_f32(EBF16, uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+__device__ __forceinline__ uint32_t from_f32(EF32, float f) { return __float_as_uint(f); }
+__device__ __forceinline__ uint16_t from_f32(EF16, float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
+}
+__device__ __forceinline__ uint16_t from_f32(EBF16, float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);  // round to nearest even
+}
+
+// Raw vector of BYTES bytes.
+template <int BYTES> struct Raw;
+template <> struct Raw<16> { using t = uint4; };
+template <> struct Raw<8> { using t = uint2; };
+template <> struct Raw<4> { using t = uint32_t; };
+template <> struct Raw<2> { using t = uint16_t; };
+
+// Load V consecutive elements starting at p (aligned to V*sizeof) as fp32.
+template <class E, int V>
+__device__ __forceinline__ void load_f32(const typename E::bits *p, float (&f)[V]) {
+    using B = typename E::bits;
+    constexpr int BYTES = V * (int)sizeof(B);
+    using R = typename Raw<BYTES>::t;
+    R r = *reinterpret_cast<const R *>(p);
+    B b[V];
+    __builtin_memcpy(b, &r, BYTES);
+#pragma unroll
+    for (int i = 0; i < V; ++i) f[i] = to_f32(E{}, b[i]);
+}
+
+// Store V fp32 values as V consecutive elements at p (aligned to V*sizeof).
+template <class E, int V>
+__device__ __forceinline__ void store_f32(typename E::bits *p, const float (&f)[V]) {
+    using B = typename E::bits;
+    constexpr int BYTES = V * (int)sizeof(B);
+    using R = typename Raw<BYTES>::t;
+    B b[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) b[i] = from_f32(E{}, f[i]);
+    R r;
+    __builtin_memcpy(&r, b, BYTES);
+    *reinterpret_cast<R *>(p) = r;
+}
+
+// ---------------------------------------------------------------- bilinear --
+
+// Split a sampling coordinate base + t (base integer, t fp32) into the integer
+// corner c0 = base + floor(t) and the fraction f = t - floor(t). The fraction is
+// exact in fp32 (t and floor(t) share their leading bits), so the position is
+// never rounded to the grid's precision. |t| is clamped at 2^24 px: such taps are
+// outside any image this library accepts, so clamping changes nothing.
+__device__ __forceinline__ void split_coord(int base, float t, int &c0, float &f) {
+    t = fminf(fmaxf(t, -16777216.0f), 16777216.0f);
+    float fl = floorf(t);
+    f = t - fl;
+    c0 = base + (int)fl;
+}
+
+// The four corners of one tap as element offsets (pixel index * pstride) and
+// weights pre-multiplied by the modulation m. A corner outside [0,H) x [0,W) gets
+// weight exactly 0 and its read is redirected to the nearest pixel inside the
+// image, so every corner load is in bounds and the loads of a whole window can be
+// issued back to back without branches (it then adds 0 * finite = 0).
+struct Tap {
+    int o00, o01, o10, o11;
+    float w00, w01, w10, w11;
+};
+
+__device__ __forceinline__ Tap make_tap(int y0, int x0, float fy, float fx, float m, int H, int W,
+                                        int pstride) {
+    const bool vy0 = (unsigned)y0 < (unsigned)H, vy1 = (unsigned)(y0 + 1) < (unsigned)H;
+    const bool vx0 = (unsigned)x0 < (unsigned)W, vx1 = (unsigned)(x0 + 1) < (unsigned)W;
+    const int yc0 = min(max(y0, 0), H - 1), yc1 = min(max(y0 + 1, 0), H - 1);
+    const int xc0 = min(max(x0, 0), W - 1), xc1 = min(max(x0 + 1, 0), W - 1);
+    const float gy0 = vy0 ? (1.0f - fy) * m : 0.0f, gy1 = vy1 ? fy * m : 0.0f;
+    const float gx0 = vx0 ? 1.0f - fx : 0.0f, gx1 = vx1 ? fx : 0.0f;
+    Tap t;
+    t.w00 = gy0 * gx0;
+    t.w01 = gy0 * gx1;
+    t.w10 = gy1 * gx0;
+    t.w11 = gy1 * gx1;
+    const int r0 = yc0 * W, r1 = yc1 * W;
+    t.o00 = (r0 + xc0) * pstride;
+    t.o01 = (r0 + xc1) * pstride;
+    t.o10 = (r1 + xc0) * pstride;
+    t.o11 = (r1 + xc1) * pstride;
+    return t;
+}
+
+// acc += sum over the four corners of w * X[corner]; `img` points at pixel (0, 0)
+// of the image, already advanced to this lane's channels.
+template <class E, int V>
+__device__ __forceinline__ void accumulate_tap(const typename E::bits *img, const Tap &t,
+                                               float (&acc)[V]) {
+    float a[V], b[V], c[V], d[V];
+    load_f32<E, V>(img + t.o00, a);
+    load_f32<E, V>(img + t.o01, b);
+    load_f32<E, V>(img + t.o10, c);
+    load_f32<E, V>(img + t.o11, d);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        acc[i] = fmaf(t.w00, a[i], acc[i]);
+        acc[i] = fmaf(t.w01, b[i], acc[i]);
+        acc[i] = fmaf(t.w10, c[i], acc[i]);
+        acc[i] = fmaf(t.w11, d[i], acc[i]);
+    }
+}
+
+// --------------------------------------------------------------- launching --
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD b % 8).
+// Remap so that each XCD works on one contiguous range of logical blocks: tiles
+// that share input rows then share that XCD's L2 instead of being spread over all
+// eight. Bijective for any block count.
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+    constexpr int NX = 8;
+    const int q = nb / NX, r = nb % NX;
+    const int x = b % NX, j = b / NX;
+    return x * q + (x < r ? x : r) + j;
+}
+
+// Sum over the `width` lanes of an aligned segment (width a power of two <= 64).
+__device__ __forceinline__ float seg_sum_pow2(float v, int width) {
+    for (int o = 1; o < width; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float seg_max_pow2(float v, int width) {
+    for (int o = 1; o < width; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+}  // namespace dcn

@@ -1,0 +1,69 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernel files.
+// Arguments reaching a launcher have already been validated.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dcn.h"
+
+namespace dcn {
+
+struct CoreLaunch {
+    const void *x;
+    const float *offset;
+    const float *mask;  // may be NULL
+    void *out;
+    int N, H, W, G, C, kh, kw, sh, sw, ph, pw, dh, dw, Ho, Wo;
+    float offset_scale;
+    int softmax;
+    dcn_dtype dtype;
+};
+hipError_t launch_dcn_core(const CoreLaunch &a, hipStream_t stream);
+
+// Workspace plan of the DCNv2 path (all offsets 256-byte aligned).
+struct V2Plan {
+    int Ho, Wo, K;
+    long long P;      // N*Ho*Wo output pixels
+    int Cin_pad;      // Cin rounded up to the channel vector (8 elements)
+    int R;            // K*Cin_pad: columns per pixel (tap-major, channel-minor)
+    int Rp;           // R rounded up to the GEMM K tile
+    long long Pp;     // P rounded up to the GEMM N tile
+    int Mp;           // Cout rounded up to the GEMM M tile
+    size_t off_xt, off_wp, off_col, total;
+};
+bool plan_dcn_v2(int N, int Cin, int H, int W, int Cout, int kh, int kw, int sh, int sw, int ph,
+                 int pw, int dh, int dw, dcn_dtype dtype, V2Plan &plan);
+
+struct V2Launch {
+    const void *x;
+    const float *offset;
+    const float *mask;  // may be NULL
+    const void *weight;
+    void *out;
+    void *workspace;
+    int N, Cin, H, W, Cout, kh, kw, sh, sw, ph, pw, dh, dw, dg, softmax;
+    dcn_dtype dtype;
+    V2Plan plan;
+};
+hipError_t launch_dcn_v2(const V2Launch &a, hipStream_t stream);
+
+constexpr int kAggMaxMaps = 64;
+struct AggMaps {
+    int H[kAggMaxMaps];
+    int W[kAggMaxMaps];
+    int start[kAggMaxMaps];
+};
+struct AggLaunch {
+    const void *feat;
+    const float *loc;
+    const float *weights;
+    void *out;
+    int B, P_total, A, pts, cams, scales, G, Cg, softmax;
+    dcn_dtype dtype;
+    AggMaps maps;
+};
+hipError_t launch_deform_agg(const AggLaunch &a, hipStream_t stream);
+
+}  // namespace dcn

@@ -1,0 +1,159 @@
+/*
+ * dcn.h — C ABI of the MI355X (gfx950) deformable-sampling library, libdcn.so.
+ *
+ * Three forward operations, each enqueued on a caller-supplied HIP stream:
+ *
+ *   dcn_core_forward    DCNv3/v4 core (also DCNv1 when mask == NULL), channels-last.
+ *   dcn_v2_forward      DCNv2 modulated deformable convolution, NCHW:
+ *                       deform-im2col into a caller workspace, then an MFMA GEMM.
+ *   deform_agg_forward  Sparse4D-style multi-camera, multi-scale aggregation.
+ *
+ * What is computed (page title, section):
+ *  - Deformable sum y(p0) = sum_n w(p_n) x(p0 + p_n + dp_n), fractional positions
+ *    read through the bilinear kernel G(q,p) = g(qx,px) g(qy,py),
+ *    g(a,b) = max(0, 1 - |a-b|): "Hands-on DCNv1 in PyTorch" (agent.csdn.net),
+ *    sections 1 and 2.
+ *  - Modulation scalars multiplying each sample: "DCNv2 in YOLOv5" (cyqw.cn),
+ *    section 1.
+ *  - Channel groups with their own offsets and modulation; DCNv3 normalises the
+ *    modulation with a softmax over the K points of a group, DCNv4 does not;
+ *    channels-last tensors and offset_scale: "DCNv4 in YOLOv11" (lpnh.cn),
+ *    sections 1.1 and 3.2.
+ *  - Aggregation inputs (features flattened to [B, N*H*W, C], spatial shapes, scale
+ *    start index, sampling locations, weights) and softmax-normalised weights:
+ *    "Sparse4D deformable_aggregation" (mlqm.cn), sections 2.1, 2.2 and 7.
+ *
+ * Conventions shared by all entry points
+ *  - Every tensor argument is dense, contiguous device memory in the stated
+ *    order, owned by the caller. The library allocates nothing, copies nothing
+ *    between host and device and never synchronises: it validates the arguments
+ *    on the host, enqueues its kernels on `stream` and returns. Buffers must stay
+ *    alive until that stream work has completed. `out` is fully overwritten and
+ *    must not overlap any input.
+ *  - Sampling: zero outside the image, per bilinear corner. A corner whose weight
+ *    is zero is never read. Kernel point k = i*kw + j (i along H). The grid base of
+ *    output (ho, wo) and point (i, j) is (ho*stride_h - pad_h + i*dil_h,
+ *    wo*stride_w - pad_w + j*dil_w); offsets are (dx, dy) pairs, x first.
+ *  - Ho = (H + 2*pad_h - dil_h*(kh-1) - 1)/stride_h + 1, likewise Wo.
+ *  - Arithmetic is fp32 with fp32 accumulation; fp16/bf16 outputs are rounded
+ *    once (round-to-nearest-even).
+ *  - Errors: an integer status, never an abort. All argument checks run on the
+ *    host before any HIP call, so a rejected call has no effect. DCN_ERR_HIP means
+ *    a launch failed; dcn_last_hip_error() then returns the hipError_t (per thread).
+ *    Zero-sized work (N, H, W or A equal to 0) returns DCN_OK and launches nothing.
+ *  - Thread-safe and re-entrant; the only state is the per-thread last HIP error.
+ */
+#ifndef DCN_H_
+#define DCN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DCN_F32 = 0, DCN_F16 = 1, DCN_BF16 = 2 } dcn_dtype;
+
+typedef enum {
+    DCN_OK = 0,
+    DCN_ERR_NULL = 1,      /* a required pointer is NULL                           */
+    DCN_ERR_SHAPE = 2,     /* a size is negative, Ho/Wo <= 0, or a size limit hit   */
+    DCN_ERR_PARAM = 3,     /* stride/dilation <= 0, pad < 0, bad group split, ...   */
+    DCN_ERR_DTYPE = 4,     /* dtype not supported by this entry point               */
+    DCN_ERR_ALIGN = 5,     /* a pointer is not aligned to its element size          */
+    DCN_ERR_WORKSPACE = 6, /* workspace NULL, misaligned (256 B) or too small       */
+    DCN_ERR_HIP = 7        /* a HIP launch failed; see dcn_last_hip_error()         */
+} dcn_status;
+
+/*
+ * DCNv3/v4 core forward (DCNv1-style when mask == NULL), channels-last.
+ *
+ *   x       [N, H, W, G*C]        dtype
+ *   offset  [N, Ho, Wo, G, K, 2]  fp32, (dx, dy) in pixels, K = kh*kw
+ *   mask    [N, Ho, Wo, G, K]     fp32 modulation (logits when softmax != 0), or NULL
+ *   out     [N, Ho, Wo, G*C]      dtype
+ *
+ * out[n,ho,wo,g*C+c] = sum_k m_k * bilinear(x[n,:,:,g*C+c], y_k, x_k), where
+ * y_k = base_y + fl32(offset_scale*dy_k) and x_k = base_x + fl32(offset_scale*dx_k),
+ * and m_k = mask (1 when NULL) or, with softmax != 0, the softmax over the K points
+ * of (n, ho, wo, g) (DCNv3). Limits: K <= 64; each image H*W*G*C < 2^31 elements.
+ * Pointers must be aligned to their element size; 16-byte alignment of x/out with
+ * C*sizeof(dtype) a multiple of 16 selects the widest vector path.
+ */
+dcn_status dcn_core_forward(const void *x, const float *offset, const float *mask, void *out,
+                            int N, int H, int W, int G, int C, int kh, int kw,
+                            int stride_h, int stride_w, int pad_h, int pad_w,
+                            int dil_h, int dil_w, float offset_scale, int softmax,
+                            dcn_dtype dtype, hipStream_t stream);
+
+/*
+ * Workspace bytes dcn_v2_forward needs for these sizes (0 if they are invalid).
+ * Layout (internal, 256-byte aligned regions): x transposed to channels-last,
+ * the weight permuted to [Cout_pad][K*Cin_pad] (tap-major) and the deform-im2col
+ * columns [P_pad][K*Cin_pad] with P = N*Ho*Wo (one K-contiguous row per pixel).
+ */
+size_t dcn_v2_workspace_bytes(int N, int Cin, int H, int W, int Cout, int kh, int kw,
+                              int stride_h, int stride_w, int pad_h, int pad_w,
+                              int dil_h, int dil_w, dcn_dtype dtype);
+
+/*
+ * DCNv2 modulated deformable convolution (DCNv1 when mask == NULL), NCHW.
+ *
+ *   x        [N, Cin, H, W]                 dtype (DCN_F16 or DCN_BF16)
+ *   offset   [N, dg*K*2, Ho, Wo]            fp32; channel (g*K + k)*2 is dx, +1 is dy
+ *   mask     [N, dg*K, Ho, Wo]              fp32 (post-sigmoid modulation) or NULL;
+ *                                           logits when softmax != 0 (softmax over K
+ *                                           per deformable group)
+ *   weight   [Cout, Cin, kh, kw]            dtype
+ *   out      [N, Cout, Ho, Wo]              dtype, fp32 accumulation, no bias
+ *   workspace, workspace_bytes              >= dcn_v2_workspace_bytes(...), 256-B aligned
+ *
+ * out[n,co,ho,wo] = sum_{ci,k} weight[co,ci,k] * m_k * bilinear(x[n,ci], pos_k), channel ci
+ * using deformable group ci / (Cin/dg). The sampled columns are rounded to dtype before
+ * the MFMA contraction. Limits: K <= 64, dg divides Cin.
+ */
+dcn_status dcn_v2_forward(const void *x, const float *offset, const float *mask,
+                          const void *weight, void *out, void *workspace, size_t workspace_bytes,
+                          int N, int Cin, int H, int W, int Cout, int kh, int kw,
+                          int stride_h, int stride_w, int pad_h, int pad_w,
+                          int dil_h, int dil_w, int deform_groups, int softmax,
+                          dcn_dtype dtype, hipStream_t stream);
+
+/*
+ * Multi-camera, multi-scale deformable aggregation (Sparse4D).
+ *
+ *   feat           [B, P_total, G*Cg]          dtype, all maps flattened (rows = pixels)
+ *   spatial_shape  HOST int32 [cams, scales, 2] (H_s, W_s) of map (cam, s)
+ *   scale_start    HOST int32 [cams, scales]    first row of map (cam, s) in feat
+ *   loc            [B, A, pts, cams, 2]         fp32 (u, v) normalised to the camera image
+ *   weights        [B, A, pts, cams, scales, G] fp32 (logits when softmax != 0)
+ *   out            [B, A, G*Cg]                 dtype
+ *
+ * out[b,a,g*Cg+c] = sum over (p, cam, s) of w[b,a,p,cam,s,g] *
+ *   bilinear(map_{cam,s}[:, :, g*Cg+c], y, x) with x = fl32(u*W_s) - 0.5 and
+ *   y = fl32(v*H_s) - 0.5 (pixel centres at (i + 1/2)/W_s). With softmax != 0 the
+ *   weights of (b, a, g) are softmax-normalised over all pts*cams*scales taps.
+ * The two small host arrays are copied by value into the launch; they need not
+ * outlive the call. Limits: cams*scales <= 64; every map must satisfy
+ * scale_start + H_s*W_s <= P_total; B*P_total*G*Cg < 2^31 elements.
+ */
+dcn_status deform_agg_forward(const void *feat, const int32_t *spatial_shape,
+                              const int32_t *scale_start, const float *loc,
+                              const float *weights, void *out,
+                              int B, int P_total, int A, int pts, int cams, int scales,
+                              int G, int Cg, int softmax, dcn_dtype dtype, hipStream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char *dcn_status_string(dcn_status s);
+
+/* hipError_t of this thread's last DCN_ERR_HIP (0 if none). */
+int dcn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCN_H_ */

@@ -59,6 +59,8 @@ def _load():
         lib.oracle_bilinear.restype = ctypes.c_double
         lib.oracle_bilinear.argtypes = [_dp, _i64, _i64, _i64, ctypes.c_double,
                                         ctypes.c_double, _dp]
+        lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_threads.argtypes = []
         lib.oracle_softmax.restype = None
         lib.oracle_softmax.argtypes = [_dp, _i64, _dp]
         lib.oracle_dcn_core.restype = ctypes.c_int
@@ -96,6 +98,11 @@ def _idx(sel):
         return None, 0
     s = np.ascontiguousarray(np.asarray(sel, dtype=np.int64).reshape(-1))
     return s, int(s.size)
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's loops use."""
+    return int(_load().oracle_threads())
 
 
 def out_size(n, k, s, p, d):

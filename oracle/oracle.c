@@ -37,6 +37,9 @@
  * values of all product terms ("absum"), used by the tests' error bound.
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -94,6 +97,16 @@ static void softmax_d(const double *l, int64_t n, int64_t lstride, double *m)
 }
 
 void oracle_softmax(const double *l, int64_t n, double *m) { softmax_d(l, n, 1, m); }
+
+/* Threads the parallel loops below run on (reported with timings). */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 static int64_t out_size(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d)
 {
