@@ -1,0 +1,305 @@
+"""Benchmark of the deformable-sampling forward path on one MI355X.
+
+One step = one DCNv4 core forward (dcn_core_forward) over the detector stride-8
+workload: fp16 x [16, 80, 80, 256] (16 groups of 16 channels), 3x3 window, fp32
+offsets ~ N(0, 3) px with 5% of taps forced outside the image, fp32 masks ~ U(0,1),
+fp32 arithmetic and accumulation, fp16 output. Inputs are resident in HBM before
+the timed region.
+
+Printed (one JSON line): bilinear taps/s (whole job), ms per step, the roofline
+object of the core kernel (algorithmic bytes per launch / HIP-event launch time vs
+8 TB/s), the CPU oracle's rate on a bounded sample, and side measurements of the
+other ops (DCNv4/DCNv3 small maps, DCNv2 im2col + MFMA GEMM, aggregation).
+
+  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--only core]
+  python bench.py --calib-copy     # plain copy of known size, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
+METRIC = "bilinear taps/sec + achieved HBM GB/s (% roofline), DCNv4 core fwd"
+HEADLINE = "dcnv4_f16_n16_80x80_g16c16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dcn_core_f16_n16_80x80_hbm_traffic.txt")
+CORE_SOURCES = ["dcn_core.hip", "dcn_common.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "deformable_sampling_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the core kernel from the committed counter summary,
+    or None if it is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_hash") != source_hash(CORE_SOURCES):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream every launch below uses)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, iters, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return (t1 - t0) / iters, e0.elapsed_time(e1) / 1e3 / iters
+
+
+def raw_core_call(lib, c, x, off, mask, out, stream, softmax):
+    """Argument tuple of the C entry point, prepared once (the timed loop then only
+    crosses the ctypes boundary)."""
+    N, H, W, GC = x.shape
+    G = off.shape[3]
+    dt = {"f32": 0, "f16": 1, "bf16": 2}[c["dtype"]]
+    args = (x.data_ptr(), off.data_ptr(), None if mask is None else mask.data_ptr(),
+            out.data_ptr(), N, H, W, G, GC // G, c["kh"], c["kw"], c["stride"][0],
+            c["stride"][1], c["pad"][0], c["pad"][1], c["dil"][0], c["dil"][1],
+            ctypes.c_float(1.0), int(bool(softmax)), dt, stream)
+    fn = lib.dcn_core_forward
+
+    def call():
+        st = fn(*args)
+        if st:
+            raise RuntimeError("dcn_core_forward status %d" % st)
+    return call
+
+
+def bench_core(dsa, torch, timer, name, iters, warmup):
+    import workloads as wl
+    c = wl.make(name)
+    dev = lambda t: None if t is None else t.to("cuda").contiguous()
+    x, off, m = dev(c["x"]), dev(c["offset"]), dev(c["mask"])
+    out = torch.empty((c["N"], c["Ho"], c["Wo"], c["G"] * c["C"]), dtype=x.dtype, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    call = raw_core_call(dsa.load(), c, x, off, m, out, stream, c["softmax"])
+    wall, kern = timer.run(call, iters, warmup)
+    taps = c["N"] * c["Ho"] * c["Wo"] * c["G"] * c["kh"] * c["kw"]
+    nbytes = (x.numel() * x.element_size() + off.numel() * 4 + (m.numel() * 4 if m is not None else 0)
+              + out.numel() * out.element_size())
+    return dict(workload=name, taps=taps, channel_taps=taps * c["C"], algo_bytes=nbytes,
+                wall_s=wall, kernel_s=kern, taps_per_s=taps / kern,
+                gbs=nbytes / kern / 1e9, frac=nbytes / kern / 1e9 / HBM_PEAK_GBS), c
+
+
+def bench_v2(dsa, torch, timer, iters, warmup):
+    import workloads as wl
+    name = "dcnv2_bf16_n8_c256_40x40"
+    c = wl.make(name)
+    dev = lambda t: None if t is None else t.to("cuda").contiguous()
+    x, off, m, w = dev(c["x"]), dev(c["offset"]), dev(c["mask"]), dev(c["weight"])
+    N, Cin, H, W, Cout = c["N"], c["Cin"], c["H"], c["W"], c["Cout"]
+    need = dsa.dcn_v2_workspace_bytes(N, Cin, H, W, Cout, dtype=torch.bfloat16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty((N, Cout, c["Ho"], c["Wo"]), dtype=torch.bfloat16, device="cuda")
+    lib = dsa.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    args = (x.data_ptr(), off.data_ptr(), m.data_ptr(), w.data_ptr(), out.data_ptr(), ws.data_ptr(),
+            need, N, Cin, H, W, Cout, 3, 3, 1, 1, 1, 1, 1, 1, 1, 0, 2, stream)
+
+    def call():
+        st = lib.dcn_v2_forward(*args)
+        if st:
+            raise RuntimeError("dcn_v2_forward status %d" % st)
+    wall, kern = timer.run(call, iters, warmup)
+    P = N * c["Ho"] * c["Wo"]
+    flops = 2.0 * Cout * Cin * 9 * P
+    nbytes = x.numel() * 2 + off.numel() * 4 + m.numel() * 4 + w.numel() * 2 + out.numel() * 2
+    return dict(workload=name, taps=P * 9, channel_taps=P * 9 * Cin, algo_bytes=nbytes,
+                flops=flops, wall_s=wall, kernel_s=kern, tflops=flops / kern / 1e12,
+                mfma_frac=flops / kern / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                note="three launches: layout prep, deform-im2col, MFMA GEMM")
+
+
+def bench_agg(dsa, torch, timer, iters, warmup, softmax=True):
+    import workloads as wl
+    name = "agg_f32_6cam_4scale_a900p13_g8c32"
+    c = wl.make(name, weights="logits" if softmax else "simplex")
+    dev = lambda t: t.to("cuda").contiguous()
+    feat, loc, wts = dev(c["feat"]), dev(c["loc"]), dev(c["weights"])
+    out = torch.empty((c["B"], c["A"], c["G"] * c["Cg"]), dtype=feat.dtype, device="cuda")
+    import numpy as np
+    ss = np.ascontiguousarray(c["spatial_shape"], dtype=np.int32)
+    st = np.ascontiguousarray(c["scale_start"], dtype=np.int32)
+    lib = dsa.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    args = (feat.data_ptr(), ss.ctypes.data, st.ctypes.data, loc.data_ptr(), wts.data_ptr(),
+            out.data_ptr(), c["B"], c["P_total"], c["A"], c["pts"], c["cams"], c["scales"], c["G"],
+            c["Cg"], int(softmax), 0, stream)
+
+    def call():
+        s = lib.deform_agg_forward(*args)
+        if s:
+            raise RuntimeError("deform_agg_forward status %d" % s)
+    wall, kern = timer.run(call, iters, warmup)
+    taps = c["B"] * c["A"] * c["pts"] * c["cams"] * c["scales"] * c["G"]
+    nbytes = feat.numel() * 4 + loc.numel() * 4 + wts.numel() * 4 + out.numel() * 4
+    return dict(workload=name + ("_softmax" if softmax else ""), taps=taps,
+                channel_taps=taps * c["Cg"], algo_bytes=nbytes, wall_s=wall, kernel_s=kern,
+                taps_per_s=taps / kern, gbs=nbytes / kern / 1e9,
+                frac=nbytes / kern / 1e9 / HBM_PEAK_GBS)
+
+
+def cpu_baseline(case, target_s=12.0):
+    """The oracle (as it stands) on a bounded sample of the headline workload."""
+    import numpy as np
+    import oracle
+    xs = oracle._f64(case["x"])
+    off = oracle._f64(case["offset"])
+    m = oracle._f64(case["mask"])
+    npix_all = case["N"] * case["Ho"] * case["Wo"]
+    per_pix_taps = case["G"] * case["kh"] * case["kw"]
+    r = np.random.default_rng(123)
+
+    def run(n):
+        pix = np.sort(r.choice(npix_all, size=n, replace=False))
+        t0 = time.perf_counter()
+        oracle.dcn_core(xs, off, m, kh=case["kh"], kw=case["kw"], stride=case["stride"],
+                        pad=case["pad"], dil=case["dil"], pix=pix)
+        return time.perf_counter() - t0
+
+    n0 = 256
+    t = run(n0)
+    n = int(min(npix_all, max(n0, n0 * target_s / max(t, 1e-6))))
+    t = run(n)
+    taps = n * per_pix_taps
+    return dict(value=taps / t, unit="taps/s", cores=oracle.threads(), kind="oracle",
+                sample="%d of %d output pixels (x %d groups x %d taps each), %.1f s" % (
+                    n, npix_all, case["G"], case["kh"] * case["kw"], t))
+
+
+def calib_copy(torch, mb=1024, iters=5):
+    """A plain device copy of known size, to scale FETCH_SIZE/WRITE_SIZE counters."""
+    n = mb * (1 << 20) // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(iters):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("calib copy: %d launches of %d bytes read + %d bytes written" % (iters, n * 4, n * 4))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["core", "all"], default="all")
+    ap.add_argument("--calib-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the forward path has no cross-GPU exchange "
+              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import deformable_sampling_amd as dsa
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dsa.load()
+    if args.calib_copy:
+        calib_copy(torch)
+        return
+    timer = Timer(torch)
+
+    log("headline: %s, warmup %d, steps %d" % (HEADLINE, args.warmup, args.steps))
+    head, case = bench_core(dsa, torch, timer, HEADLINE, args.steps, args.warmup)
+    log("headline done: %.2f us/launch" % (head["kernel_s"] * 1e6))
+    extra = []
+    if args.only == "all":
+        for nm in ["dcnv4_f32_n1_32x32_g4c16", "dcnv3_f32_n8_56x56_g4c16_softmax"]:
+            r, _ = bench_core(dsa, torch, timer, nm, 200, 20)
+            extra.append(r)
+            log("%s done" % nm)
+        extra.append(bench_v2(dsa, torch, timer, 100, 10))
+        log("dcnv2 done")
+        extra.append(bench_agg(dsa, torch, timer, 100, 10, softmax=True))
+        extra.append(bench_agg(dsa, torch, timer, 100, 10, softmax=False))
+        log("aggregation done")
+        for r in extra:
+            r["kernel_us"] = round(r.pop("kernel_s") * 1e6, 2)
+            r["wall_us"] = round(r.pop("wall_s") * 1e6, 2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(case)
+        log("cpu baseline done: %s" % cpu["sample"])
+
+    achieved = head["algo_bytes"] / head["kernel_s"] / 1e9
+    traffic = read_traffic()
+    line = {
+        "metric": METRIC,
+        "value": head["taps"] / head["wall_s"],
+        "unit": "taps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["wall_s"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; shapes and distributions of the workload, no dataset)",
+        "config": {"workload": HEADLINE, "op": "dcn_core_forward", "N": 16, "H": 80, "W": 80,
+                   "groups": 16, "group_channels": 16, "kernel": "3x3", "stride": 1, "pad": 1,
+                   "dilation": 1, "storage": "x/out fp16, offsets/masks fp32",
+                   "taps_per_step": head["taps"], "kernel_us": round(head["kernel_s"] * 1e6, 2),
+                   "kernel_taps_per_s": head["taps_per_s"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "algo_bytes_per_launch": head["algo_bytes"],
+                     "kernel": "dcn_core_kernel<fp16, 8 channels/lane, 3x3>"},
+        "cpu_baseline": cpu,
+        "other_ops": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -221,6 +221,8 @@ hipError_t launch_e(const CoreLaunch &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_dcn_core(const CoreLaunch &a, hipStream_t stream) {
+    CoreTilePlan tp;
+    if (plan_core_tile(a, tp)) return launch_dcn_core_tile(a, tp, stream);
     switch (a.dtype) {
         case DCN_F32: return launch_e<EF32>(a, stream);
         case DCN_F16: return launch_e<EF16>(a, stream);

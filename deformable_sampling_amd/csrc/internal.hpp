@@ -22,6 +22,21 @@ struct CoreLaunch {
 };
 hipError_t launch_dcn_core(const CoreLaunch &a, hipStream_t stream);
 
+// LDS halo-tile variant of the core (dcn_core_tile.hip).
+struct CoreTilePlan {
+    int N, H, W, G, C, kh, kw, sh, sw, ph, pw, dh, dw, Ho, Wo;
+    float offset_scale;
+    int softmax, has_mask;
+    int GB, S, NC;           // groups per block, lanes per pair, 16-B chunks per lane
+    int cpp, cpp_log2, lpp;  // 16-B chunks per region pixel (2^cpp_log2), lanes per pixel
+    int TH, TW, halo, RH, RW;
+    float inv_rw;
+    int tiles_x, tiles_y, gblocks, nblocks, threads;
+    size_t lds_bytes;
+};
+bool plan_core_tile(const CoreLaunch &a, CoreTilePlan &plan);
+hipError_t launch_dcn_core_tile(const CoreLaunch &a, const CoreTilePlan &plan, hipStream_t stream);
+
 // Workspace plan of the DCNv2 path (all offsets 256-byte aligned).
 struct V2Plan {
     int Ho, Wo, K;
