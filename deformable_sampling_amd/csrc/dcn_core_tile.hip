@@ -1,4 +1,4 @@
-// DCNv3/v4 core forward, LDS halo-tile variant (gfx950).
+// DCNv3/v4 core forward, LDS halo-tile kernels (gfx950).
 //
 // Same operation as dcn_core.hip ("DCNv4 in YOLOv11", lpnh.cn, sections 1.1 and 3.2;
 // bilinear kernel of "Hands-on DCNv1 in PyTorch", agent.csdn.net, section 2).
@@ -6,29 +6,60 @@
 // Why: with channels-last x, one group's channel vector at one pixel is 32-64 bytes,
 // a fraction of a 128-byte cache line whose other bytes belong to groups that sample
 // elsewhere. Gathering corners straight from global memory moves a whole line from
-// L2 for nearly every corner, so L2->L1 traffic, not HBM, bounds that kernel. Here
-// each block owns an output tile (TH x TW pixels) of GB groups whose channels form
-// one contiguous slice of SB bytes per pixel, and first copies the input region
-// those pixels reach with offsets up to +-halo pixels into LDS (zeros outside the
-// image). Corners are then read from LDS; only taps that leave the region (and
-// still touch the image) read global memory.
+// L2 for nearly every corner, so L2->L1 traffic, not HBM, bounds that kernel. Here a
+// tile is TH x TW output pixels of GB groups whose channels form one contiguous
+// slice of SB bytes per pixel; the input region those pixels reach with offsets up
+// to +-halo pixels is copied into LDS (zeros outside the image), corners are read
+// from LDS, and only taps that leave the region (and still touch the image) read
+// global memory, in a deferred pass.
 //
-// Per block:
-//   1. each lane loads its (pixel, group)'s K offsets and K masks into registers;
-//   2. the block stages the input region [RH x RW pixels x SB bytes] into LDS;
-//   3. DCNv3: softmax over K per pair; the S lanes of a pair split the exponentials
-//      and exchange sum and values with wavefront shuffles;
-//   4. per tap: fraction/corner split once per lane, 4*NC 16-byte LDS reads (or the
-//      global fallback), fp32 FMAs with the mask folded into the weights.
-// A lane holds NC 16-byte chunks (32 bytes when the group's channels allow), so the
-// position and weight arithmetic of a tap is shared by as many channels as possible.
+// Two kernels share the per-tile code:
+//  - dcn_core_tile_kernel (default): one tile per block, the region staged with direct
+//    global->LDS loads (global_load_lds_dwordx4); two 8-wave blocks share a CU, so one
+//    block's staging overlaps the other's compute.
+//  - dcn_core_pipe_kernel: persistent blocks, one per CU, each walking a contiguous
+//    run of tiles of its XCD with two static LDS buffers: while the block computes
+//    tile i from one, tile i+1's region is copied into the other and its offsets and
+//    masks load into registers. Measured slower than two one-tile blocks per CU on
+//    the workloads here (8 waves per CU hide less LDS and ALU latency), so it is
+//    selected only when DCN_PIPE_ENABLE is defined to 1.
+// Per tile: DCNv3 softmax over K per pair (the S lanes of a pair split the
+// exponentials and exchange sum and values with wavefront shuffles); per tap the
+// fraction/corner split once per lane, 4*NC 16-byte LDS reads, fp32 FMAs with the
+// mask folded into the four bilinear weights; one store per 16-byte chunk.
 #include "dcn_common.hpp"
 #include "internal.hpp"
 
 namespace dcn {
+
+// 16 zero bytes: the source of direct-to-LDS loads for region pixels outside the image.
+__device__ __attribute__((aligned(16))) uint4 g_dcn_zero_chunk[1];
+
 namespace {
 
 using TileParams = CoreTilePlan;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Pipelined kernel geometry: 512 threads, two LDS buffers of kPipeSlots * 512 chunks of
+// 16 bytes (2 x 80 KB of the CU's 160 KB).
+constexpr int kPipeThreads = 512;
+constexpr int kPipeSlots = 10;
+constexpr int kPipeChunks = kPipeSlots * kPipeThreads;
+
+// s_waitcnt with only the vector-memory counter constrained to <= n (gfx9 encoding:
+// vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8, vmcnt[5:4] bits 15:14).
+#define DCN_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
+// s_waitcnt lgkmcnt(0) only.
+#define DCN_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14))
+
+// Workgroup barrier that does not wait for outstanding global loads (so prefetches stay
+// in flight); the LDS-scoped acquire keeps later LDS reads below it.
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 template <class E, int V>
 __device__ __forceinline__ void unpack(const uint4 &r, float (&f)[V]) {
@@ -39,139 +70,145 @@ __device__ __forceinline__ void unpack(const uint4 &r, float (&f)[V]) {
     for (int i = 0; i < V; ++i) f[i] = to_f32(E{}, b[i]);
 }
 
-constexpr int kStageBatch = 8;  // 16-byte staging loads kept in flight per thread
-
-template <class E, int KH, int KW, int S, int NC>
-__global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::bits *__restrict__ x,
-                                                             const float *__restrict__ offset,
-                                                             const float *__restrict__ mask,
-                                                             typename E::bits *__restrict__ out,
-                                                             const TileParams p) {
-    using Bt = typename E::bits;
-    constexpr int V = 16 / (int)sizeof(Bt);
-    constexpr int K = KH * KW;
-    extern __shared__ uint4 lds[];  // [RH][RW][cpp]
-
-    // block -> (image, tile row, tile column, group block), group block fastest: the
-    // group blocks of one tile share every input cache line, so they run on the same
-    // XCD (contiguous logical ranges per XCD) and the line is fetched into one L2.
-    int t = xcd_remap((int)blockIdx.x, p.nblocks);
+// Tile t -> (image, tile row, tile column, group block), group block fastest: the
+// group blocks of one tile share every input cache line, so consecutive tiles (which
+// run on one XCD) fetch each line into one L2.
+struct TileAt {
+    int n, ho0, wo0, g0, ry0, rx0;
+};
+__device__ __forceinline__ TileAt tile_at(int t, const TileParams &p) {
+    TileAt a;
     const int gb = t % p.gblocks;
     t /= p.gblocks;
     const int tx = t % p.tiles_x;
     t /= p.tiles_x;
     const int ty = t % p.tiles_y;
-    const int n = t / p.tiles_y;
-    const int ho0 = ty * p.TH, wo0 = tx * p.TW, g0 = gb * p.GB;
-    const int ry0 = ho0 * p.sh - p.ph - p.halo;
-    const int rx0 = wo0 * p.sw - p.pw - p.halo;
+    a.n = t / p.tiles_y;
+    a.ho0 = ty * p.TH;
+    a.wo0 = tx * p.TW;
+    a.g0 = gb * p.GB;
+    a.ry0 = a.ho0 * p.sh - p.ph - p.halo;
+    a.rx0 = a.wo0 * p.sw - p.pw - p.halo;
+    return a;
+}
 
-    // thread -> (pixel in tile, group in block, lane s of the pair)
+// This lane's (pixel, group) within a tile: lane lp of the pixel is gl*S + s.
+struct LaneAt {
+    int s, gl, q, ho, wo, g;
+    bool active;
+};
+template <int S>
+__device__ __forceinline__ LaneAt lane_at(const TileAt &a, const TileParams &p) {
+    LaneAt l;
     const int tid = threadIdx.x;
-    const int lp = tid % p.lpp;  // lane within the pixel = gl*S + s
-    const int s = lp % S;
-    const int gl = lp / S;
-    const int q = tid / p.lpp;
-    const int qy = q / p.TW, qx = q - qy * p.TW;
-    const int ho = ho0 + qy, wo = wo0 + qx;
-    const bool active = q < p.TH * p.TW && ho < p.Ho && wo < p.Wo;
-    const int g = g0 + gl;
+    const int lp = tid % p.lpp;
+    l.s = lp % S;
+    l.gl = lp / S;
+    l.q = tid / p.lpp;
+    const int qy = l.q / p.TW, qx = l.q - qy * p.TW;
+    l.ho = a.ho0 + qy;
+    l.wo = a.wo0 + qx;
+    l.active = l.q < p.TH * p.TW && l.ho < p.Ho && l.wo < p.Wo;
+    l.g = a.g0 + l.gl;
+    return l;
+}
+
+// Corner/fraction split of base + t as split_coord does, with the fraction taken by
+// v_fract_f32 (t - floor(t), held below 1) and the corner by a floor-convert. The
+// offsets reaching here are already scaled by offset_scale (see scale_offsets).
+__device__ __forceinline__ void split_coord_fast(int base, float t, int &c0, float &f) {
+    t = __builtin_amdgcn_fmed3f(t, -16777216.0f, 16777216.0f);
+    f = __builtin_amdgcn_fractf(t);
+    c0 = base + (int)floorf(t);
+}
+
+// fl32(offset_scale * d) for every offset, once per pair (skipped when the scale is 1,
+// which leaves every value unchanged).
+template <int K>
+__device__ __forceinline__ void scale_offsets(float (&d)[2 * K], float scale) {
+    if (scale != 1.0f) {
+#pragma unroll
+        for (int i = 0; i < 2 * K; ++i) d[i] = __fmul_rn(scale, d[i]);
+    }
+}
+
+// The pair's K (dx, dy) offsets and K masks into registers (pair 0 for idle lanes).
+template <int K>
+__device__ __forceinline__ void load_dm(float (&d)[2 * K], float (&m)[K], const TileAt &a,
+                                        const LaneAt &l, const float *offset, const float *mask,
+                                        const TileParams &p) {
+    const size_t pr = l.active ? (((size_t)a.n * p.Ho + l.ho) * p.Wo + l.wo) * p.G + l.g : 0;
+    const float2 *o2 = reinterpret_cast<const float2 *>(offset + pr * K * 2);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const float2 v = o2[k];
+        d[2 * k] = v.x;
+        d[2 * k + 1] = v.y;
+    }
+    if (p.has_mask) {
+        const float *mm = mask + pr * K;
+#pragma unroll
+        for (int k = 0; k < K; ++k) m[k] = mm[k];
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) m[k] = 1.0f;
+    }
+}
+
+// DCNv3 softmax over the K points: lane s of the pair's S lanes takes the
+// exponentials of k = s, s+S, ...; the sum and the values are exchanged with
+// wavefront shuffles inside the pair's aligned S-lane segment. All lanes call it.
+template <int K, int S>
+__device__ __forceinline__ void softmax_k(float (&m)[K], int s) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < K; ++k) mx = fmaxf(mx, m[k]);
+    constexpr int J = (K + S - 1) / S;
+    float e[J];
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int k = j * S + s;
+        float mk = m[0];
+#pragma unroll
+        for (int kk = 1; kk < K; ++kk) mk = (kk == k) ? m[kk] : mk;
+        e[j] = k < K ? expf(mk - mx) : 0.0f;
+        sum += e[j];
+    }
+#pragma unroll
+    for (int o = 1; o < S; o <<= 1) sum += __shfl_xor(sum, o, 64);
+    const float inv = 1.0f / sum;
+    const int seg = (threadIdx.x & 63) - s;  // first lane of this pair's segment
+#pragma unroll
+    for (int k = 0; k < K; ++k) m[k] = __shfl(e[k / S], seg + k % S, 64) * inv;
+}
+
+// Taps of one active lane from the staged region `buf`, then the store. Taps whose
+// 2x2 corners are not all inside the region get weight 0 in the LDS pass; those that
+// still touch the image are redone from global memory in the deferred pass.
+template <class E, int KH, int KW, int S, int NC>
+__device__ __forceinline__ void taps_and_store(const uint4 *buf, const typename E::bits *x,
+                                               typename E::bits *out, float (&d)[2 * KH * KW],
+                                               const float (&m)[KH * KW], const TileAt &a,
+                                               const LaneAt &l, const TileParams &p) {
+    using Bt = typename E::bits;
+    constexpr int V = 16 / (int)sizeof(Bt);
+    constexpr int K = KH * KW;
     const int GC = p.G * p.C;
-    const Bt *ximg = x + (size_t)n * p.H * p.W * GC;
-
-    // 1. this pair's offsets and masks -> registers (in flight during staging)
-    float d[2 * K], m[K];
-    {
-        const size_t pr = active ? (((size_t)n * p.Ho + ho) * p.Wo + wo) * p.G + g : 0;
-        const float2 *o2 = reinterpret_cast<const float2 *>(offset + pr * K * 2);
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const float2 v = o2[k];
-            d[2 * k] = v.x;
-            d[2 * k + 1] = v.y;
-        }
-        if (p.has_mask) {
-            const float *mm = mask + pr * K;
-#pragma unroll
-            for (int k = 0; k < K; ++k) m[k] = mm[k];
-        } else {
-#pragma unroll
-            for (int k = 0; k < K; ++k) m[k] = 1.0f;
-        }
-    }
-
-    // 2. stage the input region: chunk i -> region pixel i >> log2(cpp), chunk i & (cpp-1)
-    {
-        const Bt *img = ximg + (size_t)g0 * p.C;
-        const int total = p.RH * p.RW * p.cpp;
-        const int nt = blockDim.x;
-        for (int i0 = tid; i0 < total; i0 += kStageBatch * nt) {
-            uint4 v[kStageBatch];
-#pragma unroll
-            for (int u = 0; u < kStageBatch; ++u) {
-                const int i = i0 + u * nt;
-                v[u] = make_uint4(0, 0, 0, 0);
-                const int r = i >> p.cpp_log2;
-                const int c = i & (p.cpp - 1);
-                const int ry = __float2int_rz(((float)r + 0.5f) * p.inv_rw);  // exact r / RW
-                const int yy = ry0 + ry, xx = rx0 + (r - ry * p.RW);
-                if (i < total && (unsigned)yy < (unsigned)p.H && (unsigned)xx < (unsigned)p.W)
-                    v[u] = *reinterpret_cast<const uint4 *>(
-                        img + __umul24(__umul24(yy, p.W) + xx, GC) + c * V);
-            }
-#pragma unroll
-            for (int u = 0; u < kStageBatch; ++u) {
-                const int i = i0 + u * nt;
-                if (i < total) lds[i] = v[u];
-            }
-        }
-    }
-    __syncthreads();
-
-    // 3. DCNv3 softmax over the K points: lane s of the pair's S lanes takes the
-    //    exponentials of k = s, s+S, ...; the sum and the values are exchanged with
-    //    wavefront shuffles inside the pair's aligned S-lane segment.
-    if (p.softmax) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < K; ++k) mx = fmaxf(mx, m[k]);
-        constexpr int J = (K + S - 1) / S;
-        float e[J];
-        float sum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int k = j * S + s;
-            float mk = m[0];
-#pragma unroll
-            for (int kk = 1; kk < K; ++kk) mk = (kk == k) ? m[kk] : mk;
-            e[j] = k < K ? expf(mk - mx) : 0.0f;
-            sum += e[j];
-        }
-#pragma unroll
-        for (int o = 1; o < S; o <<= 1) sum += __shfl_xor(sum, o, 64);
-        const float inv = 1.0f / sum;
-        const int seg = (threadIdx.x & 63) - s;  // first lane of this pair's segment
-#pragma unroll
-        for (int k = 0; k < K; ++k) m[k] = __shfl(e[k / S], seg + k % S, 64) * inv;
-    }
-    if (!active) return;
-
-    // 4. taps. Region coordinates of a tap are (ly, lx); taps whose 2x2 corners are
-    //    not all inside the staged region get weight 0 here and are recorded in `far`
-    //    for the global pass below (taps wholly outside the image read the region's
-    //    zeros or are skipped there).
+    scale_offsets<K>(d, p.offset_scale);
     float acc[NC][V];
 #pragma unroll
     for (int u = 0; u < NC; ++u)
 #pragma unroll
         for (int i = 0; i < V; ++i) acc[u][i] = 0.0f;
     const int rowc = p.RW * p.cpp;
+    const int lp = l.gl * S + l.s;
+    const int slot0 = lp * NC;
     // chunk order alternates with the pixel's parity so that lanes of neighbouring
     // pixels start on different LDS banks; acc[uu] accumulates chunk uu ^ flip and the
-    // swap is undone once at the store
-    const int slot0 = lp * NC;
-    const int flip = (NC == 2) ? (q & 1) : 0;
-    const int by0 = ho * p.sh - p.ph, bx0 = wo * p.sw - p.pw;
+    // swap is undone at the store
+    const int flip = (NC == 2) ? (l.q & 1) : 0;
+    const int by0 = l.ho * p.sh - p.ph, bx0 = l.wo * p.sw - p.pw;
     unsigned far = 0;
 #pragma unroll
     for (int i = 0; i < KH; ++i) {
@@ -180,39 +217,40 @@ __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::b
             const int k = i * KW + j;
             int y0, x0;
             float fy, fx;
-            split_coord(by0 + i * p.dh, __fmul_rn(p.offset_scale, d[2 * k + 1]), y0, fy);
-            split_coord(bx0 + j * p.dw, __fmul_rn(p.offset_scale, d[2 * k]), x0, fx);
-            const int ly = y0 - ry0, lx = x0 - rx0;
+            split_coord_fast(by0 + i * p.dh, d[2 * k + 1], y0, fy);
+            split_coord_fast(bx0 + j * p.dw, d[2 * k], x0, fx);
+            const int ly = y0 - a.ry0, lx = x0 - a.rx0;
             const bool inreg = (unsigned)ly <= (unsigned)(p.RH - 2) && (unsigned)lx <= (unsigned)(p.RW - 2);
-            far |= inreg ? 0u : (1u << k);
+            // some corner inside the image: y0 in [-1, H-1] and x0 in [-1, W-1]
+            const bool touch = (unsigned)(y0 + 1) <= (unsigned)p.H && (unsigned)(x0 + 1) <= (unsigned)p.W;
+            far |= (!inreg && touch) ? (1u << k) : 0u;
             const float mk = inreg ? m[k] : 0.0f;
             const int cell = (int)__umul24((unsigned)ly, (unsigned)rowc) + (lx << p.cpp_log2);
             const int base = (inreg ? cell : 0) + slot0;
-            const float gy0 = (1.0f - fy) * mk, gy1 = fy * mk;
-            const float w00 = gy0 * (1.0f - fx), w01 = gy0 * fx;
-            const float w10 = gy1 * (1.0f - fx), w11 = gy1 * fx;
+            const float gy1 = fy * mk, gy0 = mk - gy1;
+            const float w01 = gy0 * fx, w00 = gy0 - w01;
+            const float w11 = gy1 * fx, w10 = gy1 - w11;
 #pragma unroll
             for (int uu = 0; uu < NC; ++uu) {
                 const int u = uu ^ flip;
-                float a[V], b[V], c[V], e[V];
-                unpack<E, V>(lds[base + u], a);
-                unpack<E, V>(lds[base + p.cpp + u], b);
-                unpack<E, V>(lds[base + rowc + u], c);
-                unpack<E, V>(lds[base + rowc + p.cpp + u], e);
+                float va[V], vb[V], vc[V], ve[V];
+                unpack<E, V>(buf[base + u], va);
+                unpack<E, V>(buf[base + p.cpp + u], vb);
+                unpack<E, V>(buf[base + rowc + u], vc);
+                unpack<E, V>(buf[base + rowc + p.cpp + u], ve);
 #pragma unroll
                 for (int z = 0; z < V; ++z) {
-                    acc[uu][z] = fmaf(w00, a[z], acc[uu][z]);
-                    acc[uu][z] = fmaf(w01, b[z], acc[uu][z]);
-                    acc[uu][z] = fmaf(w10, c[z], acc[uu][z]);
-                    acc[uu][z] = fmaf(w11, e[z], acc[uu][z]);
+                    acc[uu][z] = fmaf(w00, va[z], acc[uu][z]);
+                    acc[uu][z] = fmaf(w01, vb[z], acc[uu][z]);
+                    acc[uu][z] = fmaf(w10, vc[z], acc[uu][z]);
+                    acc[uu][z] = fmaf(w11, ve[z], acc[uu][z]);
                 }
             }
         }
     }
-    // global pass for taps that left the region (rare): corners read from x with the
-    // per-corner image bounds; taps wholly outside the image contribute nothing
-    if (far) {
-        const Bt *imgc = ximg + (size_t)g * p.C + s * NC * V;
+    const Bt *ximg = x + (size_t)a.n * p.H * p.W * GC;
+    if (far) {  // deferred global pass (rare)
+        const Bt *imgc = ximg + (size_t)l.g * p.C + l.s * NC * V;
         while (far) {
             const int k = __builtin_ctz(far);
             far &= far - 1;
@@ -226,9 +264,8 @@ __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::b
             const int i = k / KW, j = k - (k / KW) * KW;
             int y0, x0;
             float fy, fx;
-            split_coord(by0 + i * p.dh, __fmul_rn(p.offset_scale, dy), y0, fy);
-            split_coord(bx0 + j * p.dw, __fmul_rn(p.offset_scale, dx), x0, fx);
-            if (y0 < -1 || y0 >= p.H || x0 < -1 || x0 >= p.W) continue;
+            split_coord_fast(by0 + i * p.dh, dy, y0, fy);
+            split_coord_fast(bx0 + j * p.dw, dx, x0, fx);
             const Tap tp = make_tap(y0, x0, fy, fx, mk, p.H, p.W, GC);
 #pragma unroll
             for (int uu = 0; uu < NC; ++uu) accumulate_tap<E, V>(imgc + (uu ^ flip) * V, tp, acc[uu]);
@@ -242,13 +279,177 @@ __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::b
             acc[NC - 1][z] = tmp;
         }
     }
-    Bt *o = out + (((size_t)n * p.Ho + ho) * p.Wo + wo) * GC + (size_t)g * p.C + s * NC * V;
+    Bt *o = out + (((size_t)a.n * p.Ho + l.ho) * p.Wo + l.wo) * GC + (size_t)l.g * p.C + l.s * NC * V;
 #pragma unroll
     for (int u = 0; u < NC; ++u) store_f32<E, V>(o + u * V, acc[u]);
 }
 
-// Tile shape knobs: threads per block, tile width, LDS bytes per block (two blocks
-// fit in the 160 KB of a CU at <= 80 KB), the largest halo tried and the target
+// ---------------------------------------------------------- one tile/block --
+
+template <class E, int KH, int KW, int S, int NC>
+__global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::bits *__restrict__ x,
+                                                             const float *__restrict__ offset,
+                                                             const float *__restrict__ mask,
+                                                             typename E::bits *__restrict__ out,
+                                                             const TileParams p) {
+    using Bt = typename E::bits;
+    constexpr int V = 16 / (int)sizeof(Bt);
+    constexpr int K = KH * KW;
+    extern __shared__ uint4 lds[];  // [RH][RW][cpp]
+
+    const TileAt a = tile_at(xcd_remap((int)blockIdx.x, p.nblocks), p);
+    const LaneAt l = lane_at<S>(a, p);
+    const int tid = threadIdx.x;
+    const int GC = p.G * p.C;
+
+    float d[2 * K], m[K];
+    load_dm<K>(d, m, a, l, offset, mask, p);
+
+    // Stage the region with direct global->LDS copies: each wave moves 64 consecutive
+    // 16-byte chunks per instruction (lane order = LDS order); chunks outside the
+    // image copy the zero chunk. Thread t always moves chunk t & (cpp-1) of region
+    // pixels r = t >> log2(cpp), r + dr, ... with the row/column advanced incrementally.
+    {
+        const Bt *img = x + (size_t)a.n * p.H * p.W * GC + (size_t)a.g0 * p.C + (tid & (p.cpp - 1)) * V;
+        const int total = p.RH * p.RW * p.cpp;
+        const int nt = blockDim.x;
+        const int dr = nt >> p.cpp_log2;
+        const int ddy = dr / p.RW, ddx = dr - ddy * p.RW;
+        int r = tid >> p.cpp_log2;
+        int ry = r / p.RW, rx = r - ry * p.RW;
+        for (int i0 = tid & ~63; i0 < total; i0 += nt) {
+            const int yy = a.ry0 + ry, xx = a.rx0 + rx;
+            const bool ok = i0 + (tid & 63) < total && (unsigned)yy < (unsigned)p.H && (unsigned)xx < (unsigned)p.W;
+            const void *src = ok ? (const void *)(img + __umul24(__umul24(yy, p.W) + xx, GC))
+                                 : (const void *)g_dcn_zero_chunk;
+            __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(lds + i0), 16, 0, 0);
+            rx += ddx;
+            ry += ddy;
+            if (rx >= p.RW) { rx -= p.RW; ++ry; }
+        }
+    }
+    __syncthreads();
+    if (p.softmax) softmax_k<K, S>(m, l.s);
+    if (!l.active) return;
+    taps_and_store<E, KH, KW, S, NC>(lds, x, out, d, m, a, l, p);
+}
+
+// ------------------------------------------------------ pipelined persistent --
+
+__shared__ uint4 s_pipe_a[kPipeChunks];
+__shared__ uint4 s_pipe_b[kPipeChunks];
+
+// Direct global->LDS copy of tile a's region into buf: kPipeSlots instructions per
+// wave, each moving 64 consecutive 16-byte chunks (lane order = LDS order). Chunks
+// outside the image, or past the region, copy the zero chunk.
+template <class Bt>
+__device__ __forceinline__ void stage_dma(uint4 *buf, const Bt *x, const TileAt &a,
+                                          const TileParams &p) {
+    constexpr int V = 16 / (int)sizeof(Bt);
+    const int tid = threadIdx.x;
+    const int GC = p.G * p.C;
+    const Bt *img = x + (size_t)a.n * p.H * p.W * GC + (size_t)a.g0 * p.C + (tid & (p.cpp - 1)) * V;
+    const int npx = p.RH * p.RW;
+    constexpr int dr0 = kPipeThreads;  // chunks advanced per slot
+    const int dr = dr0 >> p.cpp_log2;  // region pixels advanced per slot
+    const int ddy = dr / p.RW, ddx = dr - ddy * p.RW;
+    int r = tid >> p.cpp_log2;
+    int ry = r / p.RW, rx = r - ry * p.RW;
+    uint4 *wbase = buf + (tid & ~63);
+#pragma unroll
+    for (int j = 0; j < kPipeSlots; ++j) {
+        const int yy = a.ry0 + ry, xx = a.rx0 + rx;
+        const bool ok = r < npx && (unsigned)yy < (unsigned)p.H && (unsigned)xx < (unsigned)p.W;
+        const void *src = ok ? (const void *)(img + __umul24(__umul24(yy, p.W) + xx, GC))
+                             : (const void *)g_dcn_zero_chunk;
+        __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(wbase + j * kPipeThreads),
+                                         16, 0, 0);
+        r += dr;
+        rx += ddx;
+        ry += ddy;
+        if (rx >= p.RW) { rx -= p.RW; ++ry; }
+    }
+}
+
+template <class E, int KH, int KW, int S, int NC>
+__device__ __forceinline__ void pipe_phase(uint4 *cur, uint4 *nxt, int t, int tn, bool has_next,
+                                           float (&d)[2 * KH * KW], float (&m)[KH * KW],
+                                           float (&dn)[2 * KH * KW], float (&mn)[KH * KW],
+                                           const typename E::bits *x, const float *offset,
+                                           const float *mask, typename E::bits *out,
+                                           const TileParams &p) {
+    constexpr int K = KH * KW;
+    const TileAt a = tile_at(t, p);
+    const LaneAt l = lane_at<S>(a, p);
+    TileAt an;
+    if (has_next) {
+        an = tile_at(tn, p);
+        stage_dma(nxt, x, an, p);
+        // The kPipeSlots copies just issued are the newest vector-memory events, with at
+        // most NC output stores of the previous tile issued before them; vector loads
+        // retire in order, so <= kPipeSlots + NC outstanding means this tile's region
+        // copies (issued a whole tile earlier) have landed.
+        DCN_WAIT_VMCNT(kPipeSlots + NC);
+    } else {
+        DCN_WAIT_VMCNT(0);
+    }
+    barrier_lds();  // every wave's copies of this tile's region are in LDS
+    if (has_next) load_dm<K>(dn, mn, an, lane_at<S>(an, p), offset, mask, p);
+    if (p.softmax) softmax_k<K, S>(m, l.s);
+    if (l.active) taps_and_store<E, KH, KW, S, NC>(cur, x, out, d, m, a, l, p);
+    DCN_WAIT_LGKM0();  // this wave's reads of `cur` are done before it may be refilled
+    barrier_lds();
+}
+
+template <class E, int KH, int KW, int S, int NC>
+__global__ __launch_bounds__(kPipeThreads) void dcn_core_pipe_kernel(const typename E::bits *__restrict__ x,
+                                                                     const float *__restrict__ offset,
+                                                                     const float *__restrict__ mask,
+                                                                     typename E::bits *__restrict__ out,
+                                                                     const TileParams p) {
+    constexpr int K = KH * KW;
+    // tiles of this block: XCD xc = b % 8 owns the contiguous logical range
+    // [lo, lo + cnt); its gridDim/8 blocks take every (gridDim/8)-th tile of it
+    const int b = blockIdx.x;
+    const int xc = b & 7, jb = b >> 3, nbx = gridDim.x >> 3;
+    const int q8 = p.nblocks >> 3, r8 = p.nblocks & 7;
+    const int lo = xc * q8 + (xc < r8 ? xc : r8);
+    const int end = lo + q8 + (xc < r8 ? 1 : 0);
+    int t = lo + jb;
+    if (t >= end) return;
+
+    float d[2 * K], m[K], dn[2 * K], mn[K];
+    {
+        const TileAt a0 = tile_at(t, p);
+        stage_dma(s_pipe_a, x, a0, p);
+        load_dm<K>(d, m, a0, lane_at<S>(a0, p), offset, mask, p);
+    }
+    for (;;) {
+        int tn = t + nbx;
+        bool more = tn < end;
+        pipe_phase<E, KH, KW, S, NC>(s_pipe_a, s_pipe_b, t, tn, more, d, m, dn, mn, x, offset, mask, out, p);
+        if (!more) break;
+#pragma unroll
+        for (int i = 0; i < 2 * K; ++i) d[i] = dn[i];
+#pragma unroll
+        for (int i = 0; i < K; ++i) m[i] = mn[i];
+        t = tn;
+        tn = t + nbx;
+        more = tn < end;
+        pipe_phase<E, KH, KW, S, NC>(s_pipe_b, s_pipe_a, t, tn, more, d, m, dn, mn, x, offset, mask, out, p);
+        if (!more) break;
+#pragma unroll
+        for (int i = 0; i < 2 * K; ++i) d[i] = dn[i];
+#pragma unroll
+        for (int i = 0; i < K; ++i) m[i] = mn[i];
+        t = tn;
+    }
+}
+
+// --------------------------------------------------------------- launching --
+
+// Tile knobs of the one-tile kernel: threads per block, tile width, LDS bytes per
+// block (two blocks fit in a CU's 160 KB at <= 80 KB), largest halo tried, target
 // slice bytes per region pixel.
 #ifndef DCN_TILE_THREADS
 #define DCN_TILE_THREADS 512
@@ -265,17 +466,39 @@ __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::b
 #ifndef DCN_TILE_SLICE
 #define DCN_TILE_SLICE 64
 #endif
+#ifndef DCN_PIPE_ENABLE
+#define DCN_PIPE_ENABLE 0
+#endif
+
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 template <class E, int S, int NC>
 hipError_t launch_tile(const CoreLaunch &a, const TileParams &p, hipStream_t stream) {
     using Bt = typename E::bits;
+    const Bt *x = static_cast<const Bt *>(a.x);
+    Bt *out = static_cast<Bt *>(a.out);
+    if (p.pipelined) {
+        hipLaunchKernelGGL((dcn_core_pipe_kernel<E, 3, 3, S, NC>), dim3(p.grid), dim3(kPipeThreads), 0,
+                           stream, x, a.offset, a.mask, out, p);
+        return hipGetLastError();
+    }
     auto kern = dcn_core_tile_kernel<E, 3, 3, S, NC>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
         DCN_TILE_LDS_BYTES);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kern, dim3(p.nblocks), dim3(p.threads), p.lds_bytes, stream,
-                       static_cast<const Bt *>(a.x), a.offset, a.mask, static_cast<Bt *>(a.out), p);
+    hipLaunchKernelGGL(kern, dim3(p.nblocks), dim3(p.threads), p.lds_bytes, stream, x, a.offset,
+                       a.mask, out, p);
     return hipGetLastError();
 }
 
@@ -305,9 +528,22 @@ int ilog2(int v) {
     return l;
 }
 
+// LDS bytes of a region: whole 1 KB blocks, since every wave's direct-to-LDS copy
+// writes 64 consecutive 16-byte chunks.
+size_t region_bytes(size_t rh, size_t rw, size_t sb) { return (rh * rw * sb + 1023) / 1024 * 1024; }
+
+int pick_halo(const CoreLaunch &a, int TH, int TW, size_t sb, size_t budget) {
+    for (int h = DCN_TILE_MAX_HALO; h >= 1; --h) {
+        const size_t rh = (size_t)(TH - 1) * a.sh + (size_t)(a.kh - 1) * a.dh + 2 + 2 * h;
+        const size_t rw = (size_t)(TW - 1) * a.sw + (size_t)(a.kw - 1) * a.dw + 2 + 2 * h;
+        if (region_bytes(rh, rw, sb) <= budget) return h;
+    }
+    return -1;
+}
+
 }  // namespace
 
-// Choose a tile for the LDS path; false if this call should use the direct kernel
+// Choose a tile for the LDS kernels; false if this call should use the direct kernel
 // (window other than 3x3, channel slice not a multiple of 16 bytes or over 256
 // bytes, misaligned pointers, image too large for 24-bit offsets, or no useful halo
 // fits in LDS).
@@ -321,27 +557,40 @@ bool plan_core_tile(const CoreLaunch &a, TileParams &p) {
     // 16-byte chunks per lane: two where the channels allow, except for bf16, whose
     // widening (no mixed-precision FMA) would need twice the registers
     const int NC = (cbytes % 32 == 0 && a.dtype != DCN_BF16) ? 2 : 1;
-    const int S = cbytes / (16 * NC);         // lanes per (pixel, group): 1, 2, 4 or 8
+    const int S = cbytes / (16 * NC);  // lanes per (pixel, group): 1, 2, 4 or 8
     if (S & (S - 1)) return false;
-    int GB = 1;  // groups per block: a power of two dividing G, slice <= DCN_TILE_SLICE
+    int GB = 1;  // groups per tile: a power of two dividing G, slice <= DCN_TILE_SLICE
     while (a.G % (2 * GB) == 0 && 2 * GB * cbytes <= DCN_TILE_SLICE) GB *= 2;
     const int cpp = GB * cbytes / 16;  // chunks per region pixel (a power of two)
     const int lpp = GB * S;            // lanes per output pixel
-    const int pix = DCN_TILE_THREADS / lpp;
-    if (pix < 1) return false;
-    int TW = DCN_TILE_TW < pix ? DCN_TILE_TW : pix;
-    if (TW > a.Wo) TW = a.Wo;
-    int TH = pix / TW;
-    if (TH > a.Ho) TH = a.Ho;
-    if (TH < 1) return false;
     const size_t sb = (size_t)cpp * 16;
-    int halo = -1;
-    for (int h = DCN_TILE_MAX_HALO; h >= 1; --h) {
-        const size_t rh = (size_t)(TH - 1) * a.sh + (size_t)(a.kh - 1) * a.dh + 2 + 2 * h;
-        const size_t rw = (size_t)(TW - 1) * a.sw + (size_t)(a.kw - 1) * a.dw + 2 + 2 * h;
-        if (rh * rw * sb <= DCN_TILE_LDS_BYTES) { halo = h; break; }
+
+    // pipelined persistent kernel: kPipeThreads lanes per tile, region <= kPipeChunks
+    bool pipe = false;
+    int TH = 0, TW = 0, halo = -1;
+    const int ppix = kPipeThreads / lpp;
+    if (DCN_PIPE_ENABLE && ppix >= 1 && kPipeThreads % cpp == 0) {
+        TW = DCN_TILE_TW < ppix ? DCN_TILE_TW : ppix;
+        if (TW > a.Wo) TW = a.Wo;
+        TH = ppix / TW;
+        if (TH > a.Ho) TH = a.Ho;
+        if (TH >= 1) {
+            halo = pick_halo(a, TH, TW, sb, (size_t)kPipeChunks * 16);
+            pipe = halo >= 2;
+        }
     }
-    if (halo < 2) return false;
+    if (!pipe) {
+        const int pix = DCN_TILE_THREADS / lpp;
+        if (pix < 1) return false;
+        TW = DCN_TILE_TW < pix ? DCN_TILE_TW : pix;
+        if (TW > a.Wo) TW = a.Wo;
+        TH = pix / TW;
+        if (TH > a.Ho) TH = a.Ho;
+        if (TH < 1) return false;
+        if ((TH * TW) % NC != 0) return false;  // staging needs blockDim % cpp == 0
+        halo = pick_halo(a, TH, TW, sb, DCN_TILE_LDS_BYTES);
+        if (halo < 2) return false;
+    }
     p.N = a.N; p.H = a.H; p.W = a.W; p.G = a.G; p.C = a.C; p.kh = a.kh; p.kw = a.kw;
     p.sh = a.sh; p.sw = a.sw; p.ph = a.ph; p.pw = a.pw; p.dh = a.dh; p.dw = a.dw;
     p.Ho = a.Ho; p.Wo = a.Wo;
@@ -356,11 +605,22 @@ bool plan_core_tile(const CoreLaunch &a, TileParams &p) {
     p.tiles_x = (a.Wo + TW - 1) / TW;
     p.tiles_y = (a.Ho + TH - 1) / TH;
     p.gblocks = a.G / GB;
-    const long long nb = (long long)p.gblocks * a.N * p.tiles_y * p.tiles_x;
-    if (nb > 0x7fffffffLL) return false;
-    p.nblocks = (int)nb;
-    p.threads = TH * TW * lpp;
-    p.lds_bytes = (size_t)p.RH * p.RW * sb;
+    const long long nt = (long long)p.gblocks * a.N * p.tiles_y * p.tiles_x;
+    if (nt > 0x7fffffffLL) return false;
+    p.nblocks = (int)nt;  // tiles
+    p.threads = pipe ? kPipeThreads : TH * TW * lpp;
+    p.lds_bytes = region_bytes(p.RH, p.RW, sb);
+    p.pipelined = pipe ? 1 : 0;
+    if (pipe) {
+        // one persistent block per CU, a multiple of 8 so every XCD gets the same count
+        int cus = device_cus();
+        if (cus < 8) cus = 8;
+        long long g = nt < cus ? nt : cus;
+        g = (g + 7) / 8 * 8;
+        p.grid = (int)g;
+    } else {
+        p.grid = p.nblocks;
+    }
     return true;
 }
 
