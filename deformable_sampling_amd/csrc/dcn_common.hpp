@@ -131,6 +131,30 @@ __device__ __forceinline__ void accumulate_tap(const typename E::bits *img, cons
     }
 }
 
+// ------------------------------------------------------- global -> LDS copy --
+
+// One direct global->LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l
+// of the wave writes LDS bytes [lds_wave_base + 16*l, +16). lds_wave_base must be the
+// same for the whole wave. The copy is issued from inline assembly so that the
+// compiler's wait insertion does not drain copies still in flight before unrelated
+// LDS reads; the caller orders it with s_waitcnt vmcnt and a barrier. It writes no
+// register, so nothing of the copy is left in flight in a register.
+__device__ __forceinline__ void lds_copy16(unsigned lds_wave_base, const void *src) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_wave_base)), "v"(src)
+        : "memory", "m0");
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+template <class T>
+__device__ __forceinline__ unsigned lds_addr(const T *p) {
+    return (unsigned)(size_t)(const __attribute__((address_space(3))) T *)p;
+}
+
 // --------------------------------------------------------------- launching --
 
 // Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD b % 8).

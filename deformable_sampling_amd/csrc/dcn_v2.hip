@@ -11,8 +11,9 @@
 //              one K-contiguous row per output pixel p = (n*Ho + ho)*Wo + wo.
 //   3. gemm:   out[n][co][hw] = sum_r wp[co][r] * col[p][r]; both operands are
 //              K-contiguous, so every MFMA fragment is one 16-byte read. 128x128
-//              block tiles, 64-deep K steps double-buffered through LDS,
-//              v_mfma_f32_32x32x16 (bf16/fp16 in, fp32 accumulate).
+//              block tiles, 64-deep K steps through a 4-slot LDS ring filled by
+//              direct global->LDS copies, v_mfma_f32_32x32x16 (bf16/fp16 in, fp32
+//              accumulate).
 #include "dcn_common.hpp"
 #include "internal.hpp"
 
@@ -23,7 +24,6 @@ constexpr int kVec = 8;    // channel vector (16 bytes of bf16/fp16)
 constexpr int kBM = 128;   // GEMM tile: output channels
 constexpr int kBN = 128;   // GEMM tile: output pixels
 constexpr int kBK = 64;    // GEMM tile: reduction
-constexpr int kLdsPad = 8; // elements of padding per LDS row (bank spreading)
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 long long round_up(long long v, long long m) { return (v + m - 1) / m * m; }
@@ -214,44 +214,105 @@ struct GemmParams {
     int nblocks;
 };
 
-constexpr int kLdsRow = kBK + kLdsPad;  // elements per LDS row
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
 
+// s_waitcnt with only the vector-memory counter constrained to <= n (gfx9 encoding).
+#define V2_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
+
+constexpr int kStages = 4;                          // K tiles in flight (LDS ring)
+constexpr int kTileChunks = kBM * kBK / 8;          // 16-byte chunks per operand tile (1024)
+constexpr int kDmaPerWave = kTileChunks / 256;      // direct-to-LDS copies per wave per operand (4)
+
+// Operand tiles live in LDS as [128 rows][8 chunks of 8 elements], chunk cc of row r
+// stored at position cc ^ (r & 7): the 8 lanes an LDS cycle serves (8 consecutive
+// rows, same logical chunk) then hit 8 different 16-byte bank groups.
+__shared__ uint4 s_gA0[kTileChunks], s_gA1[kTileChunks], s_gA2[kTileChunks], s_gA3[kTileChunks];
+__shared__ uint4 s_gB0[kTileChunks], s_gB1[kTileChunks], s_gB2[kTileChunks], s_gB3[kTileChunks];
+template <int S> __device__ __forceinline__ uint4 *ring_a() {
+    if constexpr (S == 0) return s_gA0;
+    else if constexpr (S == 1) return s_gA1;
+    else if constexpr (S == 2) return s_gA2;
+    else return s_gA3;
+}
+template <int S> __device__ __forceinline__ uint4 *ring_b() {
+    if constexpr (S == 0) return s_gB0;
+    else if constexpr (S == 1) return s_gB1;
+    else if constexpr (S == 2) return s_gB2;
+    else return s_gB3;
+}
+static_assert(kStages == 4, "the ring has four named slots");
+
+// Copy a 128 x 64 operand tile (rows row0.., reduction k0..k0+63) into an LDS ring slot:
+// wave w, copy i moves LDS chunks (i*4 + w)*64 + lane, i.e. row c >> 3, position c & 7.
+__device__ __forceinline__ void gemm_dma(uint4 *slot, const uint16_t *g, int Rp, int k0) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+        const int c = (i * 4 + w) * 64 + lane;
+        const int row = c >> 3, pos = c & 7;
+        const int cc = pos ^ (row & 7);
+        const uint16_t *src = g + (size_t)row * Rp + k0 + cc * 8;
+        lds_copy16(lds_addr(slot + (i * 4 + w) * 64), src);
+    }
+}
+
+// One K step from ring slot S: wait until its tile has landed, barrier, refill the slot
+// the previous step used with tile kt + kStages - 1, then 4 x (2 x 2) MFMAs.
+template <class E, int S>
+__device__ __forceinline__ void gemm_step(int kt, int nk, const uint16_t *ga, const uint16_t *gb, int Rp,
+                                          f32x16_t (&acc)[2][2], int wm, int wn, int frow, int fhalf) {
+    if (kt >= nk) return;
+    // this wave's copies issued after tile kt: min(nk-1-kt, kStages-2) tiles x 2 operands
+    const int after = (nk - 1 - kt) < (kStages - 2) ? (nk - 1 - kt) : (kStages - 2);
+    if (after >= 2) V2_WAIT_VMCNT(2 * 2 * kDmaPerWave);
+    else if (after == 1) V2_WAIT_VMCNT(1 * 2 * kDmaPerWave);
+    else V2_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();  // all waves: tile kt in LDS, tile kt-1 consumed
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    const int nx = kt + kStages - 1;
+    if (nx < nk) {
+        constexpr int R = (S + kStages - 1) % kStages;
+        gemm_dma(ring_a<R>(), ga, Rp, nx * kBK);
+        gemm_dma(ring_b<R>(), gb, Rp, nx * kBK);
+    }
+    const uint4 *sa = ring_a<S>();
+    const uint4 *sb = ring_b<S>();
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+        const int cc = 2 * ks + fhalf;
+        uint4 fa[2], fb[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int ra = wm * 64 + t * 32 + frow;
+            const int rb = wn * 64 + t * 32 + frow;
+            fa[t] = sa[ra * 8 + (cc ^ (ra & 7))];
+            fb[t] = sb[rb * 8 + (cc ^ (rb & 7))];
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) acc[a][b] = mfma32<E>(fa[a], fb[b], acc[a][b]);
+    }
+}
+
+// out[n][co][hw] = sum_r wp[co][r] * col[p][r] for a 128 (co) x 128 (p) tile; 4 waves in
+// a 2 x 2 grid, each 64 x 64 = 2 x 2 v_mfma_f32_32x32x16 tiles with fp32 accumulators.
+// The K loop runs over a kStages-deep ring of LDS tiles filled by direct global->LDS
+// copies, so HBM/L2 latency overlaps the MFMA work of the previous stages.
 template <class E>
 __global__ __launch_bounds__(256) void v2_gemm_kernel(const uint16_t *__restrict__ wp,
                                                       const uint16_t *__restrict__ col,
                                                       uint16_t *__restrict__ out, GemmParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kLdsRow];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kLdsRow];
-
     const int blk = xcd_remap((int)blockIdx.x, p.nblocks);
     const int mt = blk % p.Mtiles, nt = blk / p.Mtiles;
     const int m0 = mt * kBM;
     const long long n0 = (long long)nt * kBN;
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;  // 2 x 2 waves, 64 x 64 each
-
-    // global -> register staging: 128 rows x 64 elements = 1024 chunks of 16 B per
-    // operand; thread t moves chunks t, t+256, t+512, t+768 (row = c/8, col = c%8).
     const uint16_t *ga = wp + (size_t)m0 * p.Rp;
     const uint16_t *gb = col + (size_t)n0 * p.Rp;
-    uint4 ra[4], rb[4];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + i * 256, row = c >> 3, cc = (c & 7) * 8;
-            ra[i] = *reinterpret_cast<const uint4 *>(ga + (size_t)row * p.Rp + k0 + cc);
-            rb[i] = *reinterpret_cast<const uint4 *>(gb + (size_t)row * p.Rp + k0 + cc);
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + i * 256, row = c >> 3, cc = (c & 7) * 8;
-            *reinterpret_cast<uint4 *>(&sA[buf][row * kLdsRow + cc]) = ra[i];
-            *reinterpret_cast<uint4 *>(&sB[buf][row * kLdsRow + cc]) = rb[i];
-        }
-    };
 
     f32x16_t acc[2][2];
 #pragma unroll
@@ -262,32 +323,17 @@ __global__ __launch_bounds__(256) void v2_gemm_kernel(const uint16_t *__restrict
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
     const int nk = p.Rp / kBK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    // fragment addressing: lane l reads row (l % 32), elements 8*(l/32) .. +8 of a
-    // 16-deep k step.
-    const int frow = lane & 31, fk = (lane >> 5) * 8;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * kBK);
-        const uint16_t *a_base = &sA[buf][(wm * 64 + frow) * kLdsRow + fk];
-        const uint16_t *b_base = &sB[buf][(wn * 64 + frow) * kLdsRow + fk];
-#pragma unroll
-        for (int ks = 0; ks < kBK; ks += 16) {
-            uint4 fa[2], fb[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                fa[t] = *reinterpret_cast<const uint4 *>(a_base + t * 32 * kLdsRow + ks);
-                fb[t] = *reinterpret_cast<const uint4 *>(b_base + t * 32 * kLdsRow + ks);
-            }
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) acc[a][b] = mfma32<E>(fa[a], fb[b], acc[a][b]);
-        }
-        if (kt + 1 < nk) sstore(buf ^ 1);
-        __syncthreads();
+    // prologue: tiles 0 .. kStages-2 in flight
+    if (0 < nk) { gemm_dma(ring_a<0>(), ga, p.Rp, 0); gemm_dma(ring_b<0>(), gb, p.Rp, 0); }
+    if (1 < nk) { gemm_dma(ring_a<1>(), ga, p.Rp, kBK); gemm_dma(ring_b<1>(), gb, p.Rp, kBK); }
+    if (2 < nk) { gemm_dma(ring_a<2>(), ga, p.Rp, 2 * kBK); gemm_dma(ring_b<2>(), gb, p.Rp, 2 * kBK); }
+    // fragment of lane l in a 16-deep k step ks: row (l % 32), logical chunk 2*ks + l/32
+    const int frow = lane & 31, fhalf = lane >> 5;
+    for (int kt = 0; kt < nk; kt += kStages) {
+        gemm_step<E, 0>(kt + 0, nk, ga, gb, p.Rp, acc, wm, wn, frow, fhalf);
+        gemm_step<E, 1>(kt + 1, nk, ga, gb, p.Rp, acc, wm, wn, frow, fhalf);
+        gemm_step<E, 2>(kt + 2, nk, ga, gb, p.Rp, acc, wm, wn, frow, fhalf);
+        gemm_step<E, 3>(kt + 3, nk, ga, gb, p.Rp, acc, wm, wn, frow, fhalf);
     }
 
     // epilogue: D[i][j] of a 32x32 tile sits in lane j + 32*((i/4)%2), register
@@ -345,7 +391,7 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     cp.nchunk = pl.Cin_pad / kVec;
     cp.S = cp.nchunk < 64 ? cp.nchunk : 64;
     cp.Q = 64 / cp.S;
-    cp.TP = 32;
+    cp.TP = 8;  // 4 waves x 2 items x 9 passes: many small blocks hide gather latency
     cp.nblocks = (int)((pl.Pp + cp.TP - 1) / cp.TP);
     const size_t lds = (size_t)cp.TP * a.dg * pl.K * 3 * sizeof(float);
     hipLaunchKernelGGL(v2_im2col_kernel<E>, dim3(cp.nblocks), dim3(256), lds, stream, xt,
