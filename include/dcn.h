@@ -30,8 +30,10 @@
  *    on the host, enqueues its kernels on `stream` and returns. Buffers must stay
  *    alive until that stream work has completed. `out` is fully overwritten and
  *    must not overlap any input.
- *  - Sampling: zero outside the image, per bilinear corner. A corner whose weight
- *    is zero is never read. Kernel point k = i*kw + j (i along H). The grid base of
+ *  - Sampling: zero outside the image, per bilinear corner. A corner outside the
+ *    image contributes exactly 0; every memory read stays inside the image (such
+ *    corners read a clamped in-image pixel or on-chip zeros), so inputs must be
+ *    finite. Kernel point k = i*kw + j (i along H). The grid base of
  *    output (ho, wo) and point (i, j) is (ho*stride_h - pad_h + i*dil_h,
  *    wo*stride_w - pad_w + j*dil_w); offsets are (dx, dy) pairs, x first.
  *  - Ho = (H + 2*pad_h - dil_h*(kh-1) - 1)/stride_h + 1, likewise Wo.
