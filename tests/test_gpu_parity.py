@@ -249,6 +249,21 @@ AGG_SWEEP = [
                              loc_lo=-0.3, loc_hi=1.3)),
     ("f16_small", dict(B=1, shapes=[[(9, 13), (5, 7)]] * 2, A=33, pts=3, G=2, Cg=16, dtype="f16")),
     ("bf16_small", dict(B=1, shapes=[[(9, 13), (5, 7)]] * 2, A=33, pts=3, G=2, Cg=16, dtype="bf16")),
+    # group channels of 64/128/256 bytes: the pipelined path with 4/8/16 lanes per slice;
+    # T = pts*cams*scales below one 64-tap chunk, just over one, and several with a tail
+    ("f32_cg16_s4_t12", dict(B=2, shapes=[[(9, 13), (5, 7)], [(6, 10), (3, 5)]], A=37, pts=3,
+                             G=2, Cg=16)),
+    ("f32_cg32_s8_t81", dict(B=1, shapes=[[(12, 20), (6, 10), (3, 5)]] * 3, A=45, pts=9, G=3,
+                             Cg=32)),
+    ("f32_cg64_s16_t68", dict(B=1, shapes=[[(8, 11), (4, 6)]] * 2, A=13, pts=17, G=2, Cg=64)),
+    ("f32_cg32_s8_t312", dict(B=1, shapes=[[(6, 9), (3, 5), (2, 3), (1, 2)]] * 6, A=9, pts=13,
+                              G=2, Cg=32)),
+    ("f16_cg32_s4_t130", dict(B=2, shapes=[[(10, 14)]] * 5, A=11, pts=26, G=3, Cg=32,
+                              dtype="f16")),
+    ("bf16_cg64_s8_t40", dict(B=1, shapes=[[(9, 13), (5, 7)]] * 4, A=27, pts=5, G=2, Cg=64,
+                              dtype="bf16")),
+    ("bf16_cg128_s16_t24", dict(B=1, shapes=[[(7, 9), (4, 5), (2, 3)]] * 2, A=7, pts=4, G=1,
+                                Cg=128, dtype="bf16")),
 ]
 
 
@@ -261,6 +276,28 @@ def test_agg_sweep(gpu, name, args, softmax):
     o, ab = oracle_agg(c)
     st = check(g, o, ab, c["dtype"], name)
     _say(name, softmax, st)
+
+
+@pytest.mark.parametrize("Cg", [8, 32])
+def test_agg_masked_logits(gpu, Cg):
+    # -inf logits (masked taps) get softmax weight 0. Anchor 0 has every tap of its
+    # first 64 (camera-major) masked, so the running maximum starts at -inf; anchor 1 is
+    # masked everywhere except one tap; elsewhere 30% of the logits are masked.
+    c = wl.agg_case(B=1, shapes=[[(6, 9), (3, 5), (2, 3), (1, 2)]] * 6, A=12, pts=13, G=2,
+                    Cg=Cg, seed=77)
+    w = c["weights"].clone()  # [B, A, pts, cams, scales, G]
+    rng = np.random.default_rng(5)
+    w[torch.from_numpy(rng.random(w.shape) < 0.3)] = -float("inf")
+    w[0, 0, :, :3] = -float("inf")  # cameras 0-2 of anchor 0: its first 156 camera-major taps
+    w[0, 1] = -float("inf")
+    w[0, 1, 7, 4, 2] = 0.5
+    c["weights"] = w
+    _say("agg masked logits", Cg)
+    g = host(run_agg(c))
+    o, ab = oracle_agg(c)
+    assert np.isfinite(o).all()
+    st = check(g, o, ab, c["dtype"], "agg masked Cg=%d" % Cg)
+    _say(Cg, st)
 
 
 def test_agg_deterministic(gpu):
