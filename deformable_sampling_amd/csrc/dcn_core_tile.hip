@@ -13,16 +13,9 @@
 // from LDS, and only taps that leave the region (and still touch the image) read
 // global memory, in a deferred pass.
 //
-// Two kernels share the per-tile code:
-//  - dcn_core_tile_kernel (default): one tile per block, the region staged with direct
-//    global->LDS loads (global_load_lds_dwordx4); two 8-wave blocks share a CU, so one
-//    block's staging overlaps the other's compute.
-//  - dcn_core_pipe_kernel: persistent blocks, one per CU, each walking a contiguous
-//    run of tiles of its XCD with two static LDS buffers: while the block computes
-//    tile i from one, tile i+1's region is copied into the other and its offsets and
-//    masks load into registers. Measured slower than two one-tile blocks per CU on
-//    the workloads here (8 waves per CU hide less LDS and ALU latency), so it is
-//    selected only when DCN_PIPE_ENABLE is defined to 1.
+// One tile per block: the region is staged with direct global->LDS loads
+// (global_load_lds_dwordx4); two 8-wave blocks share a CU, so one block's staging
+// overlaps the other's compute.
 // Per tile: DCNv3 softmax over K per pair (the S lanes of a pair split the
 // exponentials and exchange sum and values with wavefront shuffles); per tap the
 // fraction/corner split once per lane, 4*NC 16-byte LDS reads, fp32 FMAs with the
@@ -40,26 +33,6 @@ namespace {
 using TileParams = CoreTilePlan;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
-
-// Pipelined kernel geometry: 512 threads, two LDS buffers of kPipeSlots * 512 chunks of
-// 16 bytes (2 x 80 KB of the CU's 160 KB).
-constexpr int kPipeThreads = 512;
-constexpr int kPipeSlots = 10;
-constexpr int kPipeChunks = kPipeSlots * kPipeThreads;
-
-// s_waitcnt with only the vector-memory counter constrained to <= n (gfx9 encoding:
-// vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8, vmcnt[5:4] bits 15:14).
-#define DCN_WAIT_VMCNT(n) \
-    __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
-// s_waitcnt lgkmcnt(0) only.
-#define DCN_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14))
-
-// Workgroup barrier that does not wait for outstanding global loads (so prefetches stay
-// in flight); the LDS-scoped acquire keeps later LDS reads below it.
-__device__ __forceinline__ void barrier_lds() {
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 template <class E, int V>
 __device__ __forceinline__ void unpack(const uint4 &r, float (&f)[V]) {
@@ -186,11 +159,16 @@ __device__ __forceinline__ void softmax_k(float (&m)[K], int s) {
 // Taps of one active lane from the staged region `buf`, then the store. Taps whose
 // 2x2 corners are not all inside the region get weight 0 in the LDS pass; those that
 // still touch the image are redone from global memory in the deferred pass.
-template <class E, int KH, int KW, int S, int NC>
+// CPP_ and RW_ fix the chunks per region pixel and the region width at compile time
+// (0: taken from p): the four corners of a chunk are then one address plus constant
+// offsets that the LDS reads encode as immediates.
+// coff: this pair's 2K offsets in memory (re-read for taps of the deferred pass).
+template <class E, int KH, int KW, int S, int NC, int CPP_ = 0, int RW_ = 0>
 __device__ __forceinline__ void taps_and_store(const uint4 *buf, const typename E::bits *x,
                                                typename E::bits *out, float (&d)[2 * KH * KW],
                                                const float (&m)[KH * KW], const TileAt &a,
-                                               const LaneAt &l, const TileParams &p) {
+                                               const LaneAt &l, const TileParams &p,
+                                               const float *coff) {
     using Bt = typename E::bits;
     constexpr int V = 16 / (int)sizeof(Bt);
     constexpr int K = KH * KW;
@@ -201,66 +179,100 @@ __device__ __forceinline__ void taps_and_store(const uint4 *buf, const typename 
     for (int u = 0; u < NC; ++u)
 #pragma unroll
         for (int i = 0; i < V; ++i) acc[u][i] = 0.0f;
-    const int rowc = p.RW * p.cpp;
+    const int cpp = CPP_ ? CPP_ : p.cpp;
+    const int rw = RW_ ? RW_ : p.RW;
+    const int rowc = rw * cpp;
     const int lp = l.gl * S + l.s;
-    const int slot0 = lp * NC;
     // chunk order alternates with the pixel's parity so that lanes of neighbouring
     // pixels start on different LDS banks; acc[uu] accumulates chunk uu ^ flip and the
     // swap is undone at the store
     const int flip = (NC == 2) ? (l.q & 1) : 0;
-    const int by0 = l.ho * p.sh - p.ph, bx0 = l.wo * p.sw - p.pw;
+    int slot[NC];
+#pragma unroll
+    for (int uu = 0; uu < NC; ++uu) slot[uu] = lp * NC + (uu ^ flip);
+    // grid base of the output pixel relative to the region origin; the image bounds
+    // test adds the origin back (y0 + 1 = ly + ry0 + 1)
+    const int lby = l.ho * p.sh - p.ph - a.ry0, lbx = l.wo * p.sw - p.pw - a.rx0;
+    const int ty = a.ry0 + 1, tx = a.rx0 + 1;
     unsigned far = 0;
+    // One tap's LDS address (its chunk-0 slot is added per unit) and four weights.
+    struct TapW {
+        const uint4 *c0;
+        float w00, w01, w10, w11;
+    };
+    auto tap = [&](int k) __attribute__((always_inline)) {
+        const int i = k / KW, j = k - (k / KW) * KW;
+        int ly, lx;
+        float fy, fx;
+        split_coord_fast(lby + i * p.dh, d[2 * k + 1], ly, fy);
+        split_coord_fast(lbx + j * p.dw, d[2 * k], lx, fx);
+        const bool inreg = (unsigned)ly <= (unsigned)(p.RH - 2) && (unsigned)lx <= (unsigned)(rw - 2);
+        // some corner inside the image: y0 in [-1, H-1] and x0 in [-1, W-1]
+        const bool touch = (unsigned)(ly + ty) <= (unsigned)p.H && (unsigned)(lx + tx) <= (unsigned)p.W;
+        far |= (!inreg && touch) ? (1u << k) : 0u;
+        const float mk = inreg ? m[k] : 0.0f;
+        const int cell = (int)__umul24((unsigned)ly, (unsigned)rowc) + lx * cpp;
+        TapW t;
+        t.c0 = buf + (inreg ? cell : 0);
+        const float gy1 = fy * mk, gy0 = mk - gy1;
+        t.w01 = gy0 * fx;
+        t.w00 = gy0 - t.w01;
+        t.w11 = gy1 * fx;
+        t.w10 = gy1 - t.w11;
+        return t;
+    };
+    // Units (tap k, chunk uu) in order; unit n + 1's four corner reads are written
+    // before unit n's multiply-adds.
+    constexpr int NU = K * NC;
+    TapW tw[K];
+    uint4 buf4[2][4];
+    auto issue = [&](int n) __attribute__((always_inline)) {
+        const int k = n / NC, uu = n % NC;
+        if (uu == 0) tw[k] = tap(k);
+        const uint4 *q = tw[k].c0 + slot[uu];
+        buf4[n & 1][0] = q[0];
+        buf4[n & 1][1] = q[cpp];
+        buf4[n & 1][2] = q[rowc];
+        buf4[n & 1][3] = q[rowc + cpp];
+    };
+    auto accum = [&](int n) __attribute__((always_inline)) {
+        const int k = n / NC, uu = n % NC;
+        float va[V], vb[V], vc[V], ve[V];
+        unpack<E, V>(buf4[n & 1][0], va);
+        unpack<E, V>(buf4[n & 1][1], vb);
+        unpack<E, V>(buf4[n & 1][2], vc);
+        unpack<E, V>(buf4[n & 1][3], ve);
 #pragma unroll
-    for (int i = 0; i < KH; ++i) {
-#pragma unroll
-        for (int j = 0; j < KW; ++j) {
-            const int k = i * KW + j;
-            int y0, x0;
-            float fy, fx;
-            split_coord_fast(by0 + i * p.dh, d[2 * k + 1], y0, fy);
-            split_coord_fast(bx0 + j * p.dw, d[2 * k], x0, fx);
-            const int ly = y0 - a.ry0, lx = x0 - a.rx0;
-            const bool inreg = (unsigned)ly <= (unsigned)(p.RH - 2) && (unsigned)lx <= (unsigned)(p.RW - 2);
-            // some corner inside the image: y0 in [-1, H-1] and x0 in [-1, W-1]
-            const bool touch = (unsigned)(y0 + 1) <= (unsigned)p.H && (unsigned)(x0 + 1) <= (unsigned)p.W;
-            far |= (!inreg && touch) ? (1u << k) : 0u;
-            const float mk = inreg ? m[k] : 0.0f;
-            const int cell = (int)__umul24((unsigned)ly, (unsigned)rowc) + (lx << p.cpp_log2);
-            const int base = (inreg ? cell : 0) + slot0;
-            const float gy1 = fy * mk, gy0 = mk - gy1;
-            const float w01 = gy0 * fx, w00 = gy0 - w01;
-            const float w11 = gy1 * fx, w10 = gy1 - w11;
-#pragma unroll
-            for (int uu = 0; uu < NC; ++uu) {
-                const int u = uu ^ flip;
-                float va[V], vb[V], vc[V], ve[V];
-                unpack<E, V>(buf[base + u], va);
-                unpack<E, V>(buf[base + p.cpp + u], vb);
-                unpack<E, V>(buf[base + rowc + u], vc);
-                unpack<E, V>(buf[base + rowc + p.cpp + u], ve);
-#pragma unroll
-                for (int z = 0; z < V; ++z) {
-                    acc[uu][z] = fmaf(w00, va[z], acc[uu][z]);
-                    acc[uu][z] = fmaf(w01, vb[z], acc[uu][z]);
-                    acc[uu][z] = fmaf(w10, vc[z], acc[uu][z]);
-                    acc[uu][z] = fmaf(w11, ve[z], acc[uu][z]);
-                }
-            }
+        for (int z = 0; z < V; ++z) {
+            acc[uu][z] = fmaf(tw[k].w00, va[z], acc[uu][z]);
+            acc[uu][z] = fmaf(tw[k].w01, vb[z], acc[uu][z]);
+            acc[uu][z] = fmaf(tw[k].w10, vc[z], acc[uu][z]);
+            acc[uu][z] = fmaf(tw[k].w11, ve[z], acc[uu][z]);
         }
+    };
+#pragma unroll
+    for (int n = 0; n <= NU; ++n) {
+        if (n < NU) issue(n);
+        if (n >= 1) accum(n - 1);
     }
+    const int by0 = l.ho * p.sh - p.ph, bx0 = l.wo * p.sw - p.pw;
     const Bt *ximg = x + (size_t)a.n * p.H * p.W * GC;
     if (far) {  // deferred global pass (rare)
         const Bt *imgc = ximg + (size_t)l.g * p.C + l.s * NC * V;
         while (far) {
             const int k = __builtin_ctz(far);
             far &= far - 1;
-            float dx = d[0], dy = d[1], mk = m[0];
-#pragma unroll
-            for (int kk = 1; kk < K; ++kk) {
-                dx = (kk == k) ? d[2 * kk] : dx;
-                dy = (kk == k) ? d[2 * kk + 1] : dy;
-                mk = (kk == k) ? m[kk] : mk;
+            // the tap's offsets again from memory (the pair's row, just read, is in
+            // cache): the loop above frees each tap's offset registers after use
+            const float2 dv = reinterpret_cast<const float2 *>(coff)[k];
+            float dx = dv.x, dy = dv.y;
+            if (p.offset_scale != 1.0f) {
+                dx = __fmul_rn(p.offset_scale, dx);
+                dy = __fmul_rn(p.offset_scale, dy);
             }
+            float mk = m[0];
+#pragma unroll
+            for (int kk = 1; kk < K; ++kk) mk = (kk == k) ? m[kk] : mk;
             const int i = k / KW, j = k - (k / KW) * KW;
             int y0, x0;
             float fy, fx;
@@ -286,7 +298,7 @@ __device__ __forceinline__ void taps_and_store(const uint4 *buf, const typename 
 
 // ---------------------------------------------------------- one tile/block --
 
-template <class E, int KH, int KW, int S, int NC>
+template <class E, int KH, int KW, int S, int NC, int CPP_, int RW_>
 __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::bits *__restrict__ x,
                                                              const float *__restrict__ offset,
                                                              const float *__restrict__ mask,
@@ -331,119 +343,8 @@ __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::b
     __syncthreads();
     if (p.softmax) softmax_k<K, S>(m, l.s);
     if (!l.active) return;
-    taps_and_store<E, KH, KW, S, NC>(lds, x, out, d, m, a, l, p);
-}
-
-// ------------------------------------------------------ pipelined persistent --
-
-__shared__ uint4 s_pipe_a[kPipeChunks];
-__shared__ uint4 s_pipe_b[kPipeChunks];
-
-// Direct global->LDS copy of tile a's region into buf: kPipeSlots instructions per
-// wave, each moving 64 consecutive 16-byte chunks (lane order = LDS order). Chunks
-// outside the image, or past the region, copy the zero chunk.
-template <class Bt>
-__device__ __forceinline__ void stage_dma(uint4 *buf, const Bt *x, const TileAt &a,
-                                          const TileParams &p) {
-    constexpr int V = 16 / (int)sizeof(Bt);
-    const int tid = threadIdx.x;
-    const int GC = p.G * p.C;
-    const Bt *img = x + (size_t)a.n * p.H * p.W * GC + (size_t)a.g0 * p.C + (tid & (p.cpp - 1)) * V;
-    const int npx = p.RH * p.RW;
-    constexpr int dr0 = kPipeThreads;  // chunks advanced per slot
-    const int dr = dr0 >> p.cpp_log2;  // region pixels advanced per slot
-    const int ddy = dr / p.RW, ddx = dr - ddy * p.RW;
-    int r = tid >> p.cpp_log2;
-    int ry = r / p.RW, rx = r - ry * p.RW;
-    uint4 *wbase = buf + (tid & ~63);
-#pragma unroll
-    for (int j = 0; j < kPipeSlots; ++j) {
-        const int yy = a.ry0 + ry, xx = a.rx0 + rx;
-        const bool ok = r < npx && (unsigned)yy < (unsigned)p.H && (unsigned)xx < (unsigned)p.W;
-        const void *src = ok ? (const void *)(img + __umul24(__umul24(yy, p.W) + xx, GC))
-                             : (const void *)g_dcn_zero_chunk;
-        __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(wbase + j * kPipeThreads),
-                                         16, 0, 0);
-        r += dr;
-        rx += ddx;
-        ry += ddy;
-        if (rx >= p.RW) { rx -= p.RW; ++ry; }
-    }
-}
-
-template <class E, int KH, int KW, int S, int NC>
-__device__ __forceinline__ void pipe_phase(uint4 *cur, uint4 *nxt, int t, int tn, bool has_next,
-                                           float (&d)[2 * KH * KW], float (&m)[KH * KW],
-                                           float (&dn)[2 * KH * KW], float (&mn)[KH * KW],
-                                           const typename E::bits *x, const float *offset,
-                                           const float *mask, typename E::bits *out,
-                                           const TileParams &p) {
-    constexpr int K = KH * KW;
-    const TileAt a = tile_at(t, p);
-    const LaneAt l = lane_at<S>(a, p);
-    TileAt an;
-    if (has_next) {
-        an = tile_at(tn, p);
-        stage_dma(nxt, x, an, p);
-        // The kPipeSlots copies just issued are the newest vector-memory events, with at
-        // most NC output stores of the previous tile issued before them; vector loads
-        // retire in order, so <= kPipeSlots + NC outstanding means this tile's region
-        // copies (issued a whole tile earlier) have landed.
-        DCN_WAIT_VMCNT(kPipeSlots + NC);
-    } else {
-        DCN_WAIT_VMCNT(0);
-    }
-    barrier_lds();  // every wave's copies of this tile's region are in LDS
-    if (has_next) load_dm<K>(dn, mn, an, lane_at<S>(an, p), offset, mask, p);
-    if (p.softmax) softmax_k<K, S>(m, l.s);
-    if (l.active) taps_and_store<E, KH, KW, S, NC>(cur, x, out, d, m, a, l, p);
-    DCN_WAIT_LGKM0();  // this wave's reads of `cur` are done before it may be refilled
-    barrier_lds();
-}
-
-template <class E, int KH, int KW, int S, int NC>
-__global__ __launch_bounds__(kPipeThreads) void dcn_core_pipe_kernel(const typename E::bits *__restrict__ x,
-                                                                     const float *__restrict__ offset,
-                                                                     const float *__restrict__ mask,
-                                                                     typename E::bits *__restrict__ out,
-                                                                     const TileParams p) {
-    constexpr int K = KH * KW;
-    // tiles of this block: XCD xc = b % 8 owns the contiguous logical range
-    // [lo, lo + cnt); its gridDim/8 blocks take every (gridDim/8)-th tile of it
-    const int b = blockIdx.x;
-    const int xc = b & 7, jb = b >> 3, nbx = gridDim.x >> 3;
-    const int q8 = p.nblocks >> 3, r8 = p.nblocks & 7;
-    const int lo = xc * q8 + (xc < r8 ? xc : r8);
-    const int end = lo + q8 + (xc < r8 ? 1 : 0);
-    int t = lo + jb;
-    if (t >= end) return;
-
-    float d[2 * K], m[K], dn[2 * K], mn[K];
-    {
-        const TileAt a0 = tile_at(t, p);
-        stage_dma(s_pipe_a, x, a0, p);
-        load_dm<K>(d, m, a0, lane_at<S>(a0, p), offset, mask, p);
-    }
-    for (;;) {
-        int tn = t + nbx;
-        bool more = tn < end;
-        pipe_phase<E, KH, KW, S, NC>(s_pipe_a, s_pipe_b, t, tn, more, d, m, dn, mn, x, offset, mask, out, p);
-        if (!more) break;
-#pragma unroll
-        for (int i = 0; i < 2 * K; ++i) d[i] = dn[i];
-#pragma unroll
-        for (int i = 0; i < K; ++i) m[i] = mn[i];
-        t = tn;
-        tn = t + nbx;
-        more = tn < end;
-        pipe_phase<E, KH, KW, S, NC>(s_pipe_b, s_pipe_a, t, tn, more, d, m, dn, mn, x, offset, mask, out, p);
-        if (!more) break;
-#pragma unroll
-        for (int i = 0; i < 2 * K; ++i) d[i] = dn[i];
-#pragma unroll
-        for (int i = 0; i < K; ++i) m[i] = mn[i];
-        t = tn;
-    }
+    const size_t pc = (((size_t)a.n * p.Ho + l.ho) * p.Wo + l.wo) * p.G + l.g;
+    taps_and_store<E, KH, KW, S, NC, CPP_, RW_>(lds, x, out, d, m, a, l, p, offset + pc * K * 2);
 }
 
 // --------------------------------------------------------------- launching --
@@ -466,40 +367,26 @@ __global__ __launch_bounds__(kPipeThreads) void dcn_core_pipe_kernel(const typen
 #ifndef DCN_TILE_SLICE
 #define DCN_TILE_SLICE 64
 #endif
-#ifndef DCN_PIPE_ENABLE
-#define DCN_PIPE_ENABLE 0
-#endif
-
-int device_cus() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
 
 template <class E, int S, int NC>
 hipError_t launch_tile(const CoreLaunch &a, const TileParams &p, hipStream_t stream) {
     using Bt = typename E::bits;
     const Bt *x = static_cast<const Bt *>(a.x);
     Bt *out = static_cast<Bt *>(a.out);
-    if (p.pipelined) {
-        hipLaunchKernelGGL((dcn_core_pipe_kernel<E, 3, 3, S, NC>), dim3(p.grid), dim3(kPipeThreads), 0,
-                           stream, x, a.offset, a.mask, out, p);
+    auto go = [&](auto kern) {
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+            DCN_TILE_LDS_BYTES);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL(kern, dim3(p.nblocks), dim3(p.threads), p.lds_bytes, stream, x, a.offset,
+                           a.mask, out, p);
         return hipGetLastError();
-    }
-    auto kern = dcn_core_tile_kernel<E, 3, 3, S, NC>;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-        DCN_TILE_LDS_BYTES);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kern, dim3(p.nblocks), dim3(p.threads), p.lds_bytes, stream, x, a.offset,
-                       a.mask, out, p);
-    return hipGetLastError();
+    };
+    // 16x16-pixel tiles with halo 8 (region width 35) of 64-byte slices: the common
+    // plan, with its region geometry compiled in
+    if (p.cpp == 4 && p.RW == 35) return go(dcn_core_tile_kernel<E, 3, 3, S, NC, 4, 35>);
+    if (p.cpp == 2 && p.RW == 35) return go(dcn_core_tile_kernel<E, 3, 3, S, NC, 2, 35>);
+    return go(dcn_core_tile_kernel<E, 3, 3, S, NC, 0, 0>);
 }
 
 template <class E, int NC>
@@ -565,32 +452,16 @@ bool plan_core_tile(const CoreLaunch &a, TileParams &p) {
     const int lpp = GB * S;            // lanes per output pixel
     const size_t sb = (size_t)cpp * 16;
 
-    // pipelined persistent kernel: kPipeThreads lanes per tile, region <= kPipeChunks
-    bool pipe = false;
-    int TH = 0, TW = 0, halo = -1;
-    const int ppix = kPipeThreads / lpp;
-    if (DCN_PIPE_ENABLE && ppix >= 1 && kPipeThreads % cpp == 0) {
-        TW = DCN_TILE_TW < ppix ? DCN_TILE_TW : ppix;
-        if (TW > a.Wo) TW = a.Wo;
-        TH = ppix / TW;
-        if (TH > a.Ho) TH = a.Ho;
-        if (TH >= 1) {
-            halo = pick_halo(a, TH, TW, sb, (size_t)kPipeChunks * 16);
-            pipe = halo >= 2;
-        }
-    }
-    if (!pipe) {
-        const int pix = DCN_TILE_THREADS / lpp;
-        if (pix < 1) return false;
-        TW = DCN_TILE_TW < pix ? DCN_TILE_TW : pix;
-        if (TW > a.Wo) TW = a.Wo;
-        TH = pix / TW;
-        if (TH > a.Ho) TH = a.Ho;
-        if (TH < 1) return false;
-        if ((TH * TW) % NC != 0) return false;  // staging needs blockDim % cpp == 0
-        halo = pick_halo(a, TH, TW, sb, DCN_TILE_LDS_BYTES);
-        if (halo < 2) return false;
-    }
+    const int pix = DCN_TILE_THREADS / lpp;
+    if (pix < 1) return false;
+    int TW = DCN_TILE_TW < pix ? DCN_TILE_TW : pix;
+    if (TW > a.Wo) TW = a.Wo;
+    int TH = pix / TW;
+    if (TH > a.Ho) TH = a.Ho;
+    if (TH < 1) return false;
+    if ((TH * TW) % NC != 0) return false;  // staging needs blockDim % cpp == 0
+    const int halo = pick_halo(a, TH, TW, sb, DCN_TILE_LDS_BYTES);
+    if (halo < 2) return false;
     p.N = a.N; p.H = a.H; p.W = a.W; p.G = a.G; p.C = a.C; p.kh = a.kh; p.kw = a.kw;
     p.sh = a.sh; p.sw = a.sw; p.ph = a.ph; p.pw = a.pw; p.dh = a.dh; p.dw = a.dw;
     p.Ho = a.Ho; p.Wo = a.Wo;
@@ -601,26 +472,14 @@ bool plan_core_tile(const CoreLaunch &a, TileParams &p) {
     p.TH = TH; p.TW = TW; p.halo = halo;
     p.RH = (TH - 1) * a.sh + (a.kh - 1) * a.dh + 2 + 2 * halo;
     p.RW = (TW - 1) * a.sw + (a.kw - 1) * a.dw + 2 + 2 * halo;
-    p.inv_rw = 1.0f / (float)p.RW;
     p.tiles_x = (a.Wo + TW - 1) / TW;
     p.tiles_y = (a.Ho + TH - 1) / TH;
     p.gblocks = a.G / GB;
     const long long nt = (long long)p.gblocks * a.N * p.tiles_y * p.tiles_x;
     if (nt > 0x7fffffffLL) return false;
     p.nblocks = (int)nt;  // tiles
-    p.threads = pipe ? kPipeThreads : TH * TW * lpp;
+    p.threads = TH * TW * lpp;
     p.lds_bytes = region_bytes(p.RH, p.RW, sb);
-    p.pipelined = pipe ? 1 : 0;
-    if (pipe) {
-        // one persistent block per CU, a multiple of 8 so every XCD gets the same count
-        int cus = device_cus();
-        if (cus < 8) cus = 8;
-        long long g = nt < cus ? nt : cus;
-        g = (g + 7) / 8 * 8;
-        p.grid = (int)g;
-    } else {
-        p.grid = p.nblocks;
-    }
     return true;
 }
 

@@ -30,9 +30,7 @@ struct CoreTilePlan {
     int GB, S, NC;           // groups per block, lanes per pair, 16-B chunks per lane
     int cpp, cpp_log2, lpp;  // 16-B chunks per region pixel (2^cpp_log2), lanes per pixel
     int TH, TW, halo, RH, RW;
-    float inv_rw;
     int tiles_x, tiles_y, gblocks, nblocks, threads;  // nblocks = number of tiles
-    int pipelined, grid;                               // persistent pipelined kernel, its grid
     size_t lds_bytes;
 };
 bool plan_core_tile(const CoreLaunch &a, CoreTilePlan &plan);
