@@ -24,7 +24,7 @@ STATUS = {0: "DCN_OK", 1: "DCN_ERR_NULL", 2: "DCN_ERR_SHAPE", 3: "DCN_ERR_PARAM"
           4: "DCN_ERR_DTYPE", 5: "DCN_ERR_ALIGN", 6: "DCN_ERR_WORKSPACE", 7: "DCN_ERR_HIP"}
 
 # every symbol include/dcn.h declares
-EXPORTS = ("dcn_core_forward", "dcn_v2_workspace_bytes", "dcn_v2_forward",
+EXPORTS = ("dcn_core_forward", "dcn_v2_workspace_bytes", "dcn_v2_forward", "dcn_v2_im2col",
            "deform_agg_forward", "dcn_status_string", "dcn_last_hip_error")
 
 
@@ -59,6 +59,8 @@ def load(path: str | None = None):
     lib.dcn_v2_workspace_bytes.argtypes = [i] * 13 + [i]
     lib.dcn_v2_forward.restype = i
     lib.dcn_v2_forward.argtypes = [vp, vp, vp, vp, vp, vp, _c.c_size_t] + [i] * 15 + [i, vp]
+    lib.dcn_v2_im2col.restype = i
+    lib.dcn_v2_im2col.argtypes = [vp, vp, vp, vp, _c.c_size_t] + [i] * 15 + [i, vp]
     lib.deform_agg_forward.restype = i
     lib.deform_agg_forward.argtypes = [vp, vp, vp, vp, vp, vp] + [i] * 9 + [i, vp]
     lib.dcn_status_string.restype = _c.c_char_p
@@ -181,6 +183,32 @@ def dcn_v2_forward(x, offset, mask, weight, out=None, workspace=None, *, stride=
           _ptr(workspace), workspace.numel() * workspace.element_size(), N, Cin, H, W, Cout, kh, kw,
           sh, sw, ph, pw, dh, dw, dg, int(bool(softmax)), _DTYPE_ID[x.dtype], _stream(stream))
     return out
+
+
+def dcn_v2_im2col(x, offset, mask, Cout, workspace, *, kernel=(3, 3), stride=1, pad=1,
+                  dilation=1, deform_groups=None, softmax=False, stream=None):
+    """The deform-im2col stage of DCNv2 alone: x channels-last and the columns
+    [P_pad][Rp] land in `workspace` (laid out as for dcn_v2_forward with this Cout).
+    Returns `workspace`."""
+    kh, kw = _pair(kernel)
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    dh, dw = _pair(dilation)
+    _check(x, "x")
+    _check(offset, "offset", torch.float32)
+    _check(mask, "mask", torch.float32, allow_none=True)
+    N, Cin, H, W = x.shape
+    K = kh * kw
+    dg = deform_groups if deform_groups is not None else offset.shape[1] // (2 * K)
+    Ho, Wo = out_size(H, kh, sh, ph, dh), out_size(W, kw, sw, pw, dw)
+    if tuple(offset.shape) != (N, dg * K * 2, Ho, Wo):
+        raise ValueError("offset must be [N, dg*K*2, Ho, Wo]")
+    if mask is not None and tuple(mask.shape) != (N, dg * K, Ho, Wo):
+        raise ValueError("mask must be [N, dg*K, Ho, Wo]")
+    _call("dcn_v2_im2col", _ptr(x), _ptr(offset), _ptr(mask), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), N, Cin, H, W, Cout, kh, kw,
+          sh, sw, ph, pw, dh, dw, dg, int(bool(softmax)), _DTYPE_ID[x.dtype], _stream(stream))
+    return workspace
 
 
 def deform_agg_forward(feat, spatial_shape, scale_start, loc, weights, out=None, *, softmax=False,

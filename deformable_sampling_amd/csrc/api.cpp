@@ -98,11 +98,12 @@ size_t dcn_v2_workspace_bytes(int N, int Cin, int H, int W, int Cout, int kh, in
     return plan.total;
 }
 
-dcn_status dcn_v2_forward(const void *x, const float *offset, const float *mask, const void *weight,
+// Shared by dcn_v2_forward and dcn_v2_im2col (weight == out == NULL: columns only).
+static dcn_status v2_call(const void *x, const float *offset, const float *mask, const void *weight,
                           void *out, void *workspace, size_t workspace_bytes, int N, int Cin, int H,
                           int W, int Cout, int kh, int kw, int stride_h, int stride_w, int pad_h,
                           int pad_w, int dil_h, int dil_w, int deform_groups, int softmax,
-                          dcn_dtype dtype, hipStream_t stream) {
+                          dcn_dtype dtype, hipStream_t stream, bool columns_only) {
     if (!valid_dtype(dtype)) return DCN_ERR_DTYPE;
     if (dtype == DCN_F32) return DCN_ERR_DTYPE;
     if (N < 0 || Cin <= 0 || H <= 0 || W <= 0 || Cout <= 0) return DCN_ERR_SHAPE;
@@ -118,12 +119,16 @@ dcn_status dcn_v2_forward(const void *x, const float *offset, const float *mask,
     if ((long long)(H + 1) * (W + 1) * plan.Cin_pad > kI32) return DCN_ERR_SHAPE;
     if (plan.Pp > kI32 || (long long)N * Cin * H * W > (1LL << 40)) return DCN_ERR_SHAPE;
     if (N == 0) return DCN_OK;
-    if (!x || !offset || !weight || !out) return DCN_ERR_NULL;
+    if (!x || !offset || (!columns_only && (!weight || !out))) return DCN_ERR_NULL;
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < plan.total)
         return DCN_ERR_WORKSPACE;
     if (!aligned(x, 2) || !aligned(weight, 2) || !aligned(out, 2) || !aligned(offset, 4) ||
         (mask && !aligned(mask, 4)))
         return DCN_ERR_ALIGN;
+    if (columns_only) {
+        weight = nullptr;
+        out = nullptr;
+    }
 
     dcn::V2Launch a;
     a.x = x; a.offset = offset; a.mask = mask; a.weight = weight; a.out = out;
@@ -135,6 +140,26 @@ dcn_status dcn_v2_forward(const void *x, const float *offset, const float *mask,
     a.dtype = dtype;
     a.plan = plan;
     return hip_status(dcn::launch_dcn_v2(a, stream));
+}
+
+dcn_status dcn_v2_forward(const void *x, const float *offset, const float *mask, const void *weight,
+                          void *out, void *workspace, size_t workspace_bytes, int N, int Cin, int H,
+                          int W, int Cout, int kh, int kw, int stride_h, int stride_w, int pad_h,
+                          int pad_w, int dil_h, int dil_w, int deform_groups, int softmax,
+                          dcn_dtype dtype, hipStream_t stream) {
+    return v2_call(x, offset, mask, weight, out, workspace, workspace_bytes, N, Cin, H, W, Cout, kh,
+                   kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, deform_groups, softmax,
+                   dtype, stream, false);
+}
+
+dcn_status dcn_v2_im2col(const void *x, const float *offset, const float *mask, void *workspace,
+                         size_t workspace_bytes, int N, int Cin, int H, int W, int Cout, int kh,
+                         int kw, int stride_h, int stride_w, int pad_h, int pad_w, int dil_h,
+                         int dil_w, int deform_groups, int softmax, dcn_dtype dtype,
+                         hipStream_t stream) {
+    return v2_call(x, offset, mask, nullptr, nullptr, workspace, workspace_bytes, N, Cin, H, W,
+                   Cout, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, deform_groups,
+                   softmax, dtype, stream, true);
 }
 
 dcn_status deform_agg_forward(const void *feat, const int32_t *spatial_shape,

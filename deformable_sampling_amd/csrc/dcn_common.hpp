@@ -131,6 +131,40 @@ __device__ __forceinline__ void accumulate_tap(const typename E::bits *img, cons
     }
 }
 
+// ------------------------------------------------------------ buffer loads --
+
+// A buffer resource over `bytes` bytes from `base` (gfx9 descriptor word 3); reads
+// past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 2/4/8/16-byte loads through a buffer resource: per-lane byte offset `off` plus a
+// wave-uniform byte offset `soff`.
+template <class R>
+__device__ __forceinline__ R buffer_load(__amdgpu_buffer_rsrc_t r, int off, int soff = 0);
+template <>
+__device__ __forceinline__ uint4 buffer_load<uint4>(__amdgpu_buffer_rsrc_t r, int off, int soff) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <>
+__device__ __forceinline__ uint2 buffer_load<uint2>(__amdgpu_buffer_rsrc_t r, int off, int soff) {
+    typedef unsigned v2u __attribute__((ext_vector_type(2)));
+    const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+    return make_uint2(v.x, v.y);
+}
+template <>
+__device__ __forceinline__ uint32_t buffer_load<uint32_t>(__amdgpu_buffer_rsrc_t r, int off, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+}
+template <>
+__device__ __forceinline__ uint16_t buffer_load<uint16_t>(__amdgpu_buffer_rsrc_t r, int off, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
+}
+
 // ------------------------------------------------------- global -> LDS copy --
 
 // One direct global->LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l

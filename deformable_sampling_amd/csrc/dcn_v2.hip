@@ -223,11 +223,22 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 
 constexpr int kStages = 4;                          // K tiles in flight (LDS ring)
 constexpr int kTileChunks = kBM * kBK / 8;          // 16-byte chunks per operand tile (1024)
-constexpr int kDmaPerWave = kTileChunks / 256;      // direct-to-LDS copies per wave per operand (4)
+// Waves per GEMM block: 8 (2 x 4, 64 x 32 each: two per SIMD, so one wave's LDS
+// waits overlap the other's MFMAs) or 4 (2 x 2, 64 x 64 each).
+#ifndef DCN_V2_GEMM_WAVES
+#define DCN_V2_GEMM_WAVES 8
+#endif
+constexpr int kGemmWaves = DCN_V2_GEMM_WAVES;
+constexpr int kGemmThreads = 64 * kGemmWaves;
+constexpr int kDmaPerWave = kTileChunks / kGemmThreads;  // direct-to-LDS copies per wave per operand
+constexpr int kWaveN = kBN / (kGemmWaves / 2);           // pixels per wave (64 or 32)
+constexpr int kTB = kWaveN / 32;                         // 32-wide MFMA tiles per wave along N
 
 // Operand tiles live in LDS as [128 rows][8 chunks of 8 elements], chunk cc of row r
-// stored at position cc ^ (r & 7): the 8 lanes an LDS cycle serves (8 consecutive
-// rows, same logical chunk) then hit 8 different 16-byte bank groups.
+// stored at position cc ^ ((r >> 1) & 7). A 16-byte read by 64 lanes is served 16 lanes
+// (256 bytes, all 64 banks) at a time; the 16 lanes of a fragment read take 16
+// consecutive rows of one logical chunk, and the swizzle puts them on 16 different
+// 16-byte bank groups (two rows share a 256-byte bank period).
 __shared__ uint4 s_gA0[kTileChunks], s_gA1[kTileChunks], s_gA2[kTileChunks], s_gA3[kTileChunks];
 __shared__ uint4 s_gB0[kTileChunks], s_gB1[kTileChunks], s_gB2[kTileChunks], s_gB3[kTileChunks];
 template <int S> __device__ __forceinline__ uint4 *ring_a() {
@@ -245,24 +256,24 @@ template <int S> __device__ __forceinline__ uint4 *ring_b() {
 static_assert(kStages == 4, "the ring has four named slots");
 
 // Copy a 128 x 64 operand tile (rows row0.., reduction k0..k0+63) into an LDS ring slot:
-// wave w, copy i moves LDS chunks (i*4 + w)*64 + lane, i.e. row c >> 3, position c & 7.
+// wave w, copy i moves LDS chunks (i*W + w)*64 + lane, i.e. row c >> 3, position c & 7.
 __device__ __forceinline__ void gemm_dma(uint4 *slot, const uint16_t *g, int Rp, int k0) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
-        const int c = (i * 4 + w) * 64 + lane;
+        const int c = (i * kGemmWaves + w) * 64 + lane;
         const int row = c >> 3, pos = c & 7;
-        const int cc = pos ^ (row & 7);
+        const int cc = pos ^ ((row >> 1) & 7);
         const uint16_t *src = g + (size_t)row * Rp + k0 + cc * 8;
-        lds_copy16(lds_addr(slot + (i * 4 + w) * 64), src);
+        lds_copy16(lds_addr(slot + (i * kGemmWaves + w) * 64), src);
     }
 }
 
 // One K step from ring slot S: wait until its tile has landed, barrier, refill the slot
-// the previous step used with tile kt + kStages - 1, then 4 x (2 x 2) MFMAs.
+// the previous step used with tile kt + kStages - 1, then 4 x (2 x kTB) MFMAs.
 template <class E, int S>
 __device__ __forceinline__ void gemm_step(int kt, int nk, const uint16_t *ga, const uint16_t *gb, int Rp,
-                                          f32x16_t (&acc)[2][2], int wm, int wn, int frow, int fhalf) {
+                                          f32x16_t (&acc)[2][kTB], int wm, int wn, int frow, int fhalf) {
     if (kt >= nk) return;
     // this wave's copies issued after tile kt: min(nk-1-kt, kStages-2) tiles x 2 operands
     const int after = (nk - 1 - kt) < (kStages - 2) ? (nk - 1 - kt) : (kStages - 2);
@@ -282,27 +293,30 @@ __device__ __forceinline__ void gemm_step(int kt, int nk, const uint16_t *ga, co
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
         const int cc = 2 * ks + fhalf;
-        uint4 fa[2], fb[2];
+        uint4 fa[2], fb[kTB];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int ra = wm * 64 + t * 32 + frow;
-            const int rb = wn * 64 + t * 32 + frow;
-            fa[t] = sa[ra * 8 + (cc ^ (ra & 7))];
-            fb[t] = sb[rb * 8 + (cc ^ (rb & 7))];
+            fa[t] = sa[ra * 8 + (cc ^ ((ra >> 1) & 7))];
+        }
+#pragma unroll
+        for (int t = 0; t < kTB; ++t) {
+            const int rb = wn * kWaveN + t * 32 + frow;
+            fb[t] = sb[rb * 8 + (cc ^ ((rb >> 1) & 7))];
         }
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int b = 0; b < 2; ++b) acc[a][b] = mfma32<E>(fa[a], fb[b], acc[a][b]);
+            for (int b = 0; b < kTB; ++b) acc[a][b] = mfma32<E>(fa[a], fb[b], acc[a][b]);
     }
 }
 
-// out[n][co][hw] = sum_r wp[co][r] * col[p][r] for a 128 (co) x 128 (p) tile; 4 waves in
-// a 2 x 2 grid, each 64 x 64 = 2 x 2 v_mfma_f32_32x32x16 tiles with fp32 accumulators.
-// The K loop runs over a kStages-deep ring of LDS tiles filled by direct global->LDS
-// copies, so HBM/L2 latency overlaps the MFMA work of the previous stages.
+// out[n][co][hw] = sum_r wp[co][r] * col[p][r] for a 128 (co) x 128 (p) tile; the waves
+// form a 2 x (W/2) grid, each 64 x kWaveN = 2 x kTB v_mfma_f32_32x32x16 tiles with fp32
+// accumulators. The K loop runs over a kStages-deep ring of LDS tiles filled by direct
+// global->LDS copies, so HBM/L2 latency overlaps the MFMA work of the previous stages.
 template <class E>
-__global__ __launch_bounds__(256) void v2_gemm_kernel(const uint16_t *__restrict__ wp,
+__global__ __launch_bounds__(kGemmThreads) void v2_gemm_kernel(const uint16_t *__restrict__ wp,
                                                       const uint16_t *__restrict__ col,
                                                       uint16_t *__restrict__ out, GemmParams p) {
     const int blk = xcd_remap((int)blockIdx.x, p.nblocks);
@@ -310,15 +324,15 @@ __global__ __launch_bounds__(256) void v2_gemm_kernel(const uint16_t *__restrict
     const int m0 = mt * kBM;
     const long long n0 = (long long)nt * kBN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave & 1, wn = wave >> 1;  // 2 x 2 waves, 64 x 64 each
+    const int wm = wave & 1, wn = wave >> 1;  // 2 x (W/2) waves, 64 x kWaveN each
     const uint16_t *ga = wp + (size_t)m0 * p.Rp;
     const uint16_t *gb = col + (size_t)n0 * p.Rp;
 
-    f32x16_t acc[2][2];
+    f32x16_t acc[2][kTB];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < kTB; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
@@ -341,8 +355,8 @@ __global__ __launch_bounds__(256) void v2_gemm_kernel(const uint16_t *__restrict
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const long long pg = n0 + wn * 64 + b * 32 + (lane & 31);
+        for (int b = 0; b < kTB; ++b) {
+            const long long pg = n0 + wn * kWaveN + b * 32 + (lane & 31);
             if (pg >= p.P) continue;
             const long long nimg = pg / p.HWo;
             const int hw = (int)(pg - nimg * p.HWo);
@@ -351,6 +365,285 @@ __global__ __launch_bounds__(256) void v2_gemm_kernel(const uint16_t *__restrict
                 const int co = m0 + wm * 64 + a * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 if (co < p.Cout)
                     out[((size_t)nimg * p.Cout + co) * p.HWo + hw] = from_f32(E{}, acc[a][b][r]);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ fused --
+//
+// Deform-im2col fused into the GEMM (implicit GEMM): the columns never reach memory.
+// A block computes all kFBM output channels of kFBN output pixels. The K loop runs
+// tap-major in steps of 64 channels of one tap (Cin_pad % 64 == 0). Per step:
+//  - A (weight rows, [kFBM][64]) comes from wp in memory, loaded two steps ahead into
+//    registers and written to one of two LDS buffers;
+//  - B ([kFBN pixels][64 channels]) is computed: each thread owns one (pixel, 8-channel
+//    chunk), gathers its four corners two steps ahead, and in the step before use forms
+//    m * bilinear in fp32 exactly as the deform-im2col stage does, rounds it to the
+//    input dtype and writes one 16-byte chunk of the B buffer;
+//  - 8 waves (4 along channels x 2 along pixels, 64 x 32 each) run the MFMAs.
+// Both operands sit in LDS as [row][8 chunks] with chunk cc stored at cc ^ ((row >> 1) & 7).
+
+#ifndef DCN_V2_FUSED
+#define DCN_V2_FUSED 1
+#endif
+constexpr int kFBM = 256;                    // output channels per block
+constexpr int kFBN = 64;                     // output pixels per block
+constexpr int kFThreads = 512;               // one B chunk per thread per step
+constexpr int kFAChunks = kFBM * kBK / 8;    // 2048 16-byte chunks of A per step
+constexpr int kFBChunks = kFBN * kBK / 8;    // 512 of B
+constexpr int kFAPer = kFAChunks / kFThreads;  // A chunks per thread (4)
+#ifndef DCN_V2_FUSED_STAGES
+#define DCN_V2_FUSED_STAGES 2
+#endif
+constexpr int kFStages = DCN_V2_FUSED_STAGES;  // register stages of loads in flight
+
+struct FusedParams {
+    int N, H, W, Ho, Wo, kw, sh, sw, ph, pw, dh, dw;
+    int dg, cpg, Cin_pad, K, CB, Rp, Mp;
+    int Cout, HWo;
+    long long P;
+    int has_mask, softmax;
+    int Mtiles, nblocks;
+    unsigned xt_bytes;  // all of xt
+};
+
+template <class E>
+__global__ __launch_bounds__(kFThreads) void v2_fused_kernel(const uint16_t *__restrict__ xt,
+                                                             const float *__restrict__ offset,
+                                                             const float *__restrict__ mask,
+                                                             const uint16_t *__restrict__ wp,
+                                                             uint16_t *__restrict__ out,
+                                                             const FusedParams p) {
+    __shared__ uint4 sA[2][kFAChunks];
+    __shared__ uint4 sB[2][kFBChunks];
+    extern __shared__ float smem[];  // offsets [kFBN][dg][K][2], then masks [kFBN][dg][K]
+    const int K = p.K;
+    const int per_pix = p.dg * K;
+    float *s_off = smem;
+    float *s_m = smem + kFBN * per_pix * 2;
+
+    const int blk = xcd_remap((int)blockIdx.x, p.nblocks);
+    const int mt = blk % p.Mtiles, nt = blk / p.Mtiles;
+    const int m0 = mt * kFBM;
+    const long long n0 = (long long)nt * kFBN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const long long HWo = p.HWo;
+
+    // offsets and masks of this block's pixels (pixel-fastest: coalesced NCHW rows)
+    for (int i = tid; i < kFBN * per_pix * 2; i += kFThreads) {
+        const int pl = i % kFBN, c = i / kFBN;
+        const long long pg = n0 + pl;
+        float v = 0.0f;
+        if (pg < p.P) {
+            const long long n = pg / HWo, r = pg % HWo;
+            v = offset[((size_t)n * per_pix * 2 + c) * HWo + r];
+        }
+        s_off[pl * per_pix * 2 + c] = v;
+    }
+    for (int i = tid; i < kFBN * per_pix; i += kFThreads) {
+        const int pl = i % kFBN, c = i / kFBN;
+        const long long pg = n0 + pl;
+        float v = 1.0f;
+        if (p.has_mask && pg < p.P) {
+            const long long n = pg / HWo, r = pg % HWo;
+            v = mask[((size_t)n * per_pix + c) * HWo + r];
+        }
+        s_m[pl * per_pix + c] = v;
+    }
+    __syncthreads();
+    if (p.softmax) {  // softmax over K per (pixel, deformable group)
+        for (int i = tid; i < kFBN * p.dg; i += kFThreads) {
+            float *ml = s_m + i * K;
+            float mx = -INFINITY;
+            for (int k = 0; k < K; ++k) mx = fmaxf(mx, ml[k]);
+            float sum = 0.0f;
+            for (int k = 0; k < K; ++k) sum += expf(ml[k] - mx);
+            const float inv = 1.0f / sum;
+            for (int k = 0; k < K; ++k) ml[k] = expf(ml[k] - mx) * inv;
+        }
+        __syncthreads();
+    }
+
+    // this thread's B item: pixel row br, chunk bc (channels cb*64 + bc*8 .. +8)
+    const int br = tid >> 3, bc = tid & 7;
+    const long long pg = n0 + br;
+    const bool pvalid = pg < p.P;
+    const long long pgc = pvalid ? pg : 0;
+    const int n = (int)(pgc / HWo);
+    const int rr = (int)(pgc - (long long)n * HWo);
+    const int ho = rr / p.Wo, wo = rr - (rr / p.Wo) * p.Wo;
+    // one resource over all of xt (wave-uniform); the image is part of the lane offset
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xt, p.xt_bytes);
+    const int img_off = n * p.H * p.W * p.Cin_pad;  // elements
+    const unsigned wp_bytes = (unsigned)((size_t)(p.Mp - m0) * p.Rp * 2);  // rows m0 .. Mp-1
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(wp + (size_t)m0 * p.Rp, wp_bytes);
+    const int bdst = br * 8 + (bc ^ ((br >> 1) & 7));
+
+    // A chunk i of this thread: LDS position c = i*512 + tid, row c >> 3, logical
+    // chunk (c & 7) ^ ((row >> 1) & 7); rows past Mp read past the buffer's end (zeros)
+    int aoff[kFAPer];
+#pragma unroll
+    for (int i = 0; i < kFAPer; ++i) {
+        const int c = i * kFThreads + tid;
+        const int row = c >> 3, cc = (c & 7) ^ ((row >> 1) & 7);
+        aoff[i] = (m0 + row < p.Mp) ? (row * p.Rp + cc * 8) * 2 : (int)wp_bytes;
+    }
+
+    // corner byte offsets (this thread's channels folded in) and weights of one tap
+    struct TapB {
+        int o[4];
+        float w[4];
+    };
+    // Corners and weights of tap (i, j) for this thread's channels in 64-channel block cb
+    // (the block's byte offset cb*128 is added by the loads' scalar offset).
+    auto tap_of = [&](int k, int i, int j, int cb, TapB &t) __attribute__((always_inline)) {
+        const int grp = p.dg == 1 ? 0 : min((cb * 64 + bc * 8) / p.cpg, p.dg - 1);
+        const float *so = s_off + ((br * p.dg + grp) * K + k) * 2;
+        int y0, x0;
+        float fy, fx;
+        split_coord(ho * p.sh - p.ph + i * p.dh, so[1], y0, fy);
+        split_coord(wo * p.sw - p.pw + j * p.dw, so[0], x0, fx);
+        const float mk = pvalid ? s_m[(br * p.dg + grp) * K + k] : 0.0f;
+        const Tap tp = make_tap(y0, x0, fy, fx, mk, p.H, p.W, p.Cin_pad);
+        const int cl = img_off + bc * 8;
+        t.o[0] = (cl + tp.o00) * 2; t.o[1] = (cl + tp.o01) * 2;
+        t.o[2] = (cl + tp.o10) * 2; t.o[3] = (cl + tp.o11) * 2;
+        t.w[0] = tp.w00; t.w[1] = tp.w01; t.w[2] = tp.w10; t.w[3] = tp.w11;
+    };
+    struct Stage {
+        uint4 a[kFAPer];
+        uint4 g[4];
+        float w[4];
+    };
+    const int NS = K * p.CB;
+    // Loads run in step order 0, 1, ..., NS-1 (then NS-1 again): counters track the next
+    // step's tap (k = i*kw + j) and 64-channel block cb, and the tap's corners and
+    // weights are recomputed only when the tap changes (every step when dg > 1, where a
+    // lane's group can change with the block).
+    int ld_n = 0, ld_s = 0, ld_k = 0, ld_i = 0, ld_j = 0, ld_cb = 0;
+    TapB tb;
+    auto load = [&](Stage &st) __attribute__((always_inline)) {
+        const int soff = ld_s * kBK * 2;  // this step's 64 columns of wp
+#pragma unroll
+        for (int i = 0; i < kFAPer; ++i) st.a[i] = buffer_load<uint4>(ra, aoff[i], soff);
+        if (p.dg > 1 || ld_cb == 0) tap_of(ld_k, ld_i, ld_j, ld_cb, tb);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            st.g[c] = buffer_load<uint4>(rx, tb.o[c], ld_cb * kBK * 2);
+            st.w[c] = tb.w[c];
+        }
+        if (ld_n < NS - 1) {  // after the last step, further loads repeat it (unused)
+            ++ld_n;
+            ++ld_s;
+            if (++ld_cb == p.CB) {
+                ld_cb = 0;
+                ++ld_k;
+                if (++ld_j == p.kw) {
+                    ld_j = 0;
+                    ++ld_i;
+                }
+            }
+        }
+    };
+    auto fill = [&](const Stage &st, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kFAPer; ++i) sA[buf][i * kFThreads + tid] = st.a[i];
+        // m * bilinear of 8 channels in fp32, in the deform-im2col stage's order
+        float acc[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) acc[e] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float f[kVec];
+            load_f32<E, kVec>(reinterpret_cast<const typename E::bits *>(&st.g[c]), f);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) acc[e] = fmaf(st.w[c], f[e], acc[e]);
+        }
+        typename E::bits b[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) b[e] = from_f32(E{}, acc[e]);
+        uint4 v;
+        __builtin_memcpy(&v, b, 16);
+        sB[buf][bdst] = v;
+    };
+
+    f32x16_t acc[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][r] = 0.0f;
+    const int wm = wave & 3, wn = wave >> 2;  // 4 x 2 waves, 64 channels x 32 pixels each
+    const int frow = lane & 31, fhalf = lane >> 5;
+    // All 12 fragments of the step are read first; the empty asm takes them as in/out
+    // operands, so the MFMAs (which use its outputs) start after a single wait instead of
+    // each waiting for its own reads.
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    auto mma = [&](int buf) __attribute__((always_inline)) {
+        const v4u *sa = reinterpret_cast<const v4u *>(sA[buf]);
+        const v4u *sb = reinterpret_cast<const v4u *>(sB[buf]);
+        v4u fa[4][2], fb[4];
+#pragma unroll
+        for (int ks = 0; ks < kBK / 16; ++ks) {
+            const int cc = 2 * ks + fhalf;
+            const int rb = wn * 32 + frow;
+            fb[ks] = sb[rb * 8 + (cc ^ ((rb >> 1) & 7))];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int ra_ = wm * 64 + t * 32 + frow;
+                fa[ks][t] = sa[ra_ * 8 + (cc ^ ((ra_ >> 1) & 7))];
+            }
+        }
+        asm volatile("" : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fa[1][0]), "+v"(fa[1][1]),
+                          "+v"(fa[2][0]), "+v"(fa[2][1]), "+v"(fa[3][0]), "+v"(fa[3][1]),
+                          "+v"(fb[0]), "+v"(fb[1]), "+v"(fb[2]), "+v"(fb[3]));
+#pragma unroll
+        for (int ks = 0; ks < kBK / 16; ++ks)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                acc[t] = mfma32<E>(__builtin_bit_cast(uint4, fa[ks][t]),
+                                   __builtin_bit_cast(uint4, fb[ks]), acc[t]);
+    };
+
+    // Step s: LDS buffers s & 1 hold step s; the NST register stages hold the next NST
+    // steps. Load step s + NST into the stage step s used, run step s's MFMAs, then fill
+    // the other buffers with step s + 1. Loads past the last step repeat it: no branches
+    // around loads, so the compiler's wait counts stay exact.
+    constexpr int NST = kFStages;
+    Stage st[NST];
+#pragma unroll
+    for (int i = 0; i < NST; ++i) load(st[i]);
+    fill(st[0], 0);
+    auto step = [&](int s, Stage &mine, Stage &next) __attribute__((always_inline)) {
+        __syncthreads();
+        load(mine);  // step min(s + NST, NS - 1)
+        mma(s & 1);
+        if (s + 1 < NS) fill(next, (s + 1) & 1);
+    };
+    for (int s = 0; s < NS; s += NST) {
+        step(s, st[0], st[1 % NST]);
+        if (s + 1 >= NS) break;
+        step(s + 1, st[1 % NST], st[2 % NST]);
+        if constexpr (NST == 3) {
+            if (s + 2 >= NS) break;
+            step(s + 2, st[2], st[0]);
+        }
+    }
+
+    // epilogue: D[i][j] of a 32x32 tile sits in lane j + 32*((i/4)%2), register
+    // 4*(i/8) + i%4; row i is an output channel, column j an output pixel
+    const long long po = n0 + wn * 32 + (lane & 31);
+    if (po < p.P) {
+        const long long nimg = po / HWo;
+        const int hw = (int)(po - nimg * HWo);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int co = m0 + wm * 64 + a * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                if (co < p.Cout)
+                    out[((size_t)nimg * p.Cout + co) * HWo + hw] = from_f32(E{}, acc[a][r]);
             }
         }
     }
@@ -372,12 +665,30 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     pp.tiles_hw = (pp.HW + 63) / 64;
     pp.n_tr_blocks = a.N * pp.tiles_c * pp.tiles_hw;
     const long long wchunks = (long long)pl.Mp * (pl.Rp / kVec);
-    const int nwb = (int)((wchunks + 255) / 256);
+    const int nwb = a.weight ? (int)((wchunks + 255) / 256) : 0;  // no weight: columns only
     hipLaunchKernelGGL(v2_prep_kernel, dim3(pp.n_tr_blocks + nwb), dim3(256), 0, stream,
                        static_cast<const uint16_t *>(a.x), static_cast<const uint16_t *>(a.weight),
                        xt, wp, pp);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+
+    const size_t fused_lds = (size_t)kFBN * a.dg * pl.K * 3 * sizeof(float);
+    if (a.weight && pl.fused && fused_lds <= 64 * 1024) {  // 2+3. deform-im2col fused into the GEMM
+        FusedParams fp;
+        fp.N = a.N; fp.H = a.H; fp.W = a.W; fp.Ho = pl.Ho; fp.Wo = pl.Wo; fp.kw = a.kw;
+        fp.sh = a.sh; fp.sw = a.sw; fp.ph = a.ph; fp.pw = a.pw; fp.dh = a.dh; fp.dw = a.dw;
+        fp.dg = a.dg; fp.cpg = a.Cin / a.dg; fp.Cin_pad = pl.Cin_pad; fp.K = pl.K;
+        fp.CB = pl.Cin_pad / kBK; fp.Rp = pl.Rp; fp.Mp = pl.Mp;
+        fp.Cout = a.Cout; fp.HWo = pl.Ho * pl.Wo; fp.P = pl.P;
+        fp.has_mask = a.mask != nullptr;
+        fp.softmax = a.softmax ? 1 : 0;
+        fp.Mtiles = (pl.Mp + kFBM - 1) / kFBM;
+        fp.nblocks = (int)(fp.Mtiles * ((pl.P + kFBN - 1) / kFBN));
+        fp.xt_bytes = (unsigned)((size_t)a.N * a.H * a.W * pl.Cin_pad * 2);
+        hipLaunchKernelGGL(v2_fused_kernel<E>, dim3(fp.nblocks), dim3(kFThreads), fused_lds, stream, xt,
+                           a.offset, a.mask, wp, static_cast<uint16_t *>(a.out), fp);
+        return hipGetLastError();
+    }
 
     // 2. im2col
     ColParams cp;
@@ -399,12 +710,14 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     err = hipGetLastError();
     if (err != hipSuccess) return err;
 
+    if (!a.weight) return hipSuccess;  // columns only
+
     // 3. gemm
     GemmParams gp;
     gp.Cout = a.Cout; gp.Rp = pl.Rp; gp.HWo = pl.Ho * pl.Wo; gp.P = pl.P;
     gp.Mtiles = pl.Mp / kBM;
     gp.nblocks = (int)(gp.Mtiles * (pl.Pp / kBN));
-    hipLaunchKernelGGL(v2_gemm_kernel<E>, dim3(gp.nblocks), dim3(256), 0, stream, wp, col,
+    hipLaunchKernelGGL(v2_gemm_kernel<E>, dim3(gp.nblocks), dim3(kGemmThreads), 0, stream, wp, col,
                        static_cast<uint16_t *>(a.out), gp);
     return hipGetLastError();
 }
@@ -437,6 +750,11 @@ bool plan_dcn_v2(int N, int Cin, int H, int W, int Cout, int kh, int kw, int sh,
     pl.off_col = off;
     off = align256(off + (size_t)pl.Pp * pl.Rp * elt);
     pl.total = off;
+    // fused deform-im2col + GEMM: 64-channel steps within one tap, and byte offsets of
+    // one image of xt and of the weight fit the 32-bit buffer range
+    pl.fused = DCN_V2_FUSED && pl.Cin_pad % kBK == 0 &&
+               (size_t)N * H * W * pl.Cin_pad * elt < (1ull << 31) &&
+               (size_t)pl.Mp * pl.Rp * elt < (1ull << 31);
     return true;
 }
 

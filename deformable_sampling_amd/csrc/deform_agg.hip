@@ -58,30 +58,6 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// 2/4/8/16-byte loads through a buffer resource (32-bit byte offset).
-template <class R>
-__device__ __forceinline__ R buffer_load(__amdgpu_buffer_rsrc_t r, int off);
-template <>
-__device__ __forceinline__ uint4 buffer_load<uint4>(__amdgpu_buffer_rsrc_t r, int off) {
-    typedef unsigned v4u __attribute__((ext_vector_type(4)));
-    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-template <>
-__device__ __forceinline__ uint2 buffer_load<uint2>(__amdgpu_buffer_rsrc_t r, int off) {
-    typedef unsigned v2u __attribute__((ext_vector_type(2)));
-    const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-    return make_uint2(v.x, v.y);
-}
-template <>
-__device__ __forceinline__ uint32_t buffer_load<uint32_t>(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-template <>
-__device__ __forceinline__ uint16_t buffer_load<uint16_t>(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-}
-
 // One sampling tap: offsets of the 4 corners from the group's feature base (bytes
 // for buffer loads, elements otherwise) and their weights (bilinear x tap weight; 0 for corners outside the map).
 struct alignas(16) TapRec {

@@ -46,6 +46,7 @@ struct V2Plan {
     long long Pp;     // P rounded up to the GEMM N tile
     int Mp;           // Cout rounded up to the GEMM M tile
     size_t off_xt, off_wp, off_col, total;
+    bool fused;       // deform-im2col fused into the GEMM (the column region unused)
 };
 bool plan_dcn_v2(int N, int Cin, int H, int W, int Cout, int kh, int kw, int sh, int sw, int ph,
                  int pw, int dh, int dw, dcn_dtype dtype, V2Plan &plan);

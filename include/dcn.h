@@ -4,8 +4,9 @@
  * Three forward operations, each enqueued on a caller-supplied HIP stream:
  *
  *   dcn_core_forward    DCNv3/v4 core (also DCNv1 when mask == NULL), channels-last.
- *   dcn_v2_forward      DCNv2 modulated deformable convolution, NCHW:
- *                       deform-im2col into a caller workspace, then an MFMA GEMM.
+ *   dcn_v2_forward      DCNv2 modulated deformable convolution, NCHW: deform-im2col
+ *                       and an MFMA GEMM (fused, or in two stages through the workspace).
+ *   dcn_v2_im2col       the deform-im2col stage alone: columns into the workspace.
  *   deform_agg_forward  Sparse4D-style multi-camera, multi-scale aggregation.
  *
  * What is computed (page title, section):
@@ -92,10 +93,13 @@ dcn_status dcn_core_forward(const void *x, const float *offset, const float *mas
                             dcn_dtype dtype, hipStream_t stream);
 
 /*
- * Workspace bytes dcn_v2_forward needs for these sizes (0 if they are invalid).
- * Layout (internal, 256-byte aligned regions): x transposed to channels-last,
- * the weight permuted to [Cout_pad][K*Cin_pad] (tap-major) and the deform-im2col
- * columns [P_pad][K*Cin_pad] with P = N*Ho*Wo (one K-contiguous row per pixel).
+ * Workspace bytes dcn_v2_forward and dcn_v2_im2col need for these sizes (0 if they
+ * are invalid). Layout (256-byte aligned regions, in this order): x transposed to
+ * channels-last [N][H][W][Cin_pad], the weight permuted to [Cout_pad][Rp] (entry
+ * k*Cin_pad + ci, tap-major) and the deform-im2col columns [P_pad][Rp], one row per
+ * output pixel p = (n*Ho + ho)*Wo + wo with column k*Cin_pad + ci. Cin_pad = Cin
+ * rounded up to 8, Rp = K*Cin_pad rounded up to 64, Cout_pad = Cout rounded up to
+ * 128, P_pad = N*Ho*Wo rounded up to 128; padding entries are zero.
  */
 size_t dcn_v2_workspace_bytes(int N, int Cin, int H, int W, int Cout, int kh, int kw,
                               int stride_h, int stride_w, int pad_h, int pad_w,
@@ -115,7 +119,10 @@ size_t dcn_v2_workspace_bytes(int N, int Cin, int H, int W, int Cout, int kh, in
  *
  * out[n,co,ho,wo] = sum_{ci,k} weight[co,ci,k] * m_k * bilinear(x[n,ci], pos_k), channel ci
  * using deformable group ci / (Cin/dg). The sampled columns are rounded to dtype before
- * the MFMA contraction. Limits: K <= 64, dg divides Cin.
+ * the MFMA contraction. Limits: K <= 64, dg divides Cin (and Cin/dg is a multiple of 8
+ * when dg > 1). When Cin is a multiple of 64 the columns are formed on chip inside the
+ * GEMM and never written (the workspace's column region is then left untouched);
+ * otherwise they pass through the workspace.
  */
 dcn_status dcn_v2_forward(const void *x, const float *offset, const float *mask,
                           const void *weight, void *out, void *workspace, size_t workspace_bytes,
@@ -123,6 +130,18 @@ dcn_status dcn_v2_forward(const void *x, const float *offset, const float *mask,
                           int stride_h, int stride_w, int pad_h, int pad_w,
                           int dil_h, int dil_w, int deform_groups, int softmax,
                           dcn_dtype dtype, hipStream_t stream);
+
+/*
+ * The deform-im2col stage of dcn_v2_forward on its own (same arguments without weight
+ * and out; Cout only fixes the workspace layout): writes x channels-last and the
+ * columns col[p][k*Cin_pad + ci] = m_k(p) * bilinear(x[n,ci], pos_k(p)), rounded to
+ * dtype, into their workspace regions. Same validation and errors as dcn_v2_forward.
+ */
+dcn_status dcn_v2_im2col(const void *x, const float *offset, const float *mask, void *workspace,
+                         size_t workspace_bytes, int N, int Cin, int H, int W, int Cout, int kh,
+                         int kw, int stride_h, int stride_w, int pad_h, int pad_w, int dil_h,
+                         int dil_w, int deform_groups, int softmax, dcn_dtype dtype,
+                         hipStream_t stream);
 
 /*
  * Multi-camera, multi-scale deformable aggregation (Sparse4D).

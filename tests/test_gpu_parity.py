@@ -164,6 +164,9 @@ def test_v2_named_workload_sampled(gpu):
     st = check(g_pix, o, ab, "bf16", name)
     _say(name, "out", st)
     # the deform-im2col stage on its own: columns in the workspace vs the oracle's
+    ws.zero_()
+    dsa.dcn_v2_im2col(dev(c["x"]), dev(c["offset"]), dev(c["mask"]), Cout, ws)
+    torch.cuda.synchronize()
     lay = v2_workspace_layout(N, Cin, H, W, Cout, 3, 3, 40, 40)
     col = ws[lay["off_col"]:lay["off_col"] + 12800 * lay["Rp"] * 2].view(torch.bfloat16)
     col = col.view(12800, lay["Rp"])[:, :lay["R"]].reshape(12800, 9, lay["cin_pad"])[:, :, :Cin]
@@ -186,6 +189,16 @@ V2_SWEEP = [
     ("bf16_mask_none", dict(N=1, Cin=16, H=8, W=8, Cout=8, mask=None, dtype="bf16")),
     ("bf16_softmax", dict(N=1, Cin=16, H=8, W=8, Cout=8, mask="logits", dtype="bf16")),
     ("bf16_many_pixels", dict(N=3, Cin=64, H=23, W=29, Cout=96, dtype="bf16")),
+    # Cin a multiple of 64: columns formed inside the GEMM. Pixel counts that are not
+    # multiples of the 64-pixel block, Cout over one 256-channel block, groups, softmax
+    ("fused_f16", dict(N=2, Cin=64, H=11, W=13, Cout=40, dtype="f16")),
+    ("fused_cout300", dict(N=1, Cin=128, H=9, W=10, Cout=300, dtype="bf16")),
+    ("fused_dg4", dict(N=2, Cin=128, H=8, W=9, Cout=64, dg=4, dtype="bf16")),
+    ("fused_softmax_stride2", dict(N=1, Cin=64, H=15, W=14, Cout=32, stride=(2, 2),
+                                   mask="logits", dtype="bf16")),
+    ("fused_mask_none_dil2", dict(N=1, Cin=64, H=12, W=12, Cout=16, pad=(2, 2), dil=(2, 2),
+                                  mask=None, dtype="f16")),
+    ("fused_k1x3", dict(N=1, Cin=64, H=9, W=10, Cout=8, kh=1, kw=3, pad=(0, 1), dtype="bf16")),
 ]
 
 
