@@ -32,6 +32,7 @@ long long round_up(long long v, long long m) { return (v + m - 1) / m * m; }
 
 struct PrepParams {
     int N, Cin, HW, Cin_pad;
+    int vec;  // 16-byte transpose path: HW % 8 == 0 and x 16-byte aligned
     int Cout, K, Mp, Rp;
     int n_tr_blocks;  // blocks doing the transpose; the rest permute the weight
     int tiles_c, tiles_hw;
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void v2_prep_kernel(const uint16_t *__restrict
                                                       const uint16_t *__restrict__ w,
                                                       uint16_t *__restrict__ xt,
                                                       uint16_t *__restrict__ wp, PrepParams p) {
-    __shared__ uint16_t tile[64][66];
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // [channel][pixel], 144-byte rows
     const int b = blockIdx.x;
     if (b < p.n_tr_blocks) {
         const int tc = b % p.tiles_c;
@@ -51,6 +52,33 @@ __global__ __launch_bounds__(256) void v2_prep_kernel(const uint16_t *__restrict
         const int c0 = tc * 64, hw0 = th * 64;
         const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
         const uint16_t *xn = x + (size_t)n * p.Cin * p.HW;
+        if (p.vec) {
+            // 16-byte accesses: a thread loads 8 pixels of one channel, then stores 8
+            // channels of one pixel
+            const int q = threadIdx.x & 7, r = threadIdx.x >> 3;  // 8 chunks x 32 rows
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int c = c0 + r + 32 * j, hw = hw0 + q * kVec;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (c < p.Cin && hw < p.HW)
+                    v = *reinterpret_cast<const uint4 *>(xn + (size_t)c * p.HW + hw);
+                *reinterpret_cast<uint4 *>(&tile[r + 32 * j][q * kVec]) = v;
+            }
+            __syncthreads();
+            uint16_t *xtn = xt + (size_t)n * p.HW * p.Cin_pad;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int hw = hw0 + r + 32 * j, c = c0 + q * kVec;
+                uint16_t e[kVec];
+#pragma unroll
+                for (int i = 0; i < kVec; ++i) e[i] = tile[q * kVec + i][r + 32 * j];
+                uint4 v;
+                __builtin_memcpy(&v, e, 16);
+                if (hw < p.HW && c < p.Cin_pad)
+                    *reinterpret_cast<uint4 *>(xtn + (size_t)hw * p.Cin_pad + c) = v;
+            }
+            return;
+        }
         for (int cy = ty; cy < 64; cy += 4) {
             const int c = c0 + cy, hw = hw0 + tx;
             tile[cy][tx] = (c < p.Cin && hw < p.HW) ? xn[(size_t)c * p.HW + hw] : (uint16_t)0;
@@ -660,6 +688,7 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     // 1. prep
     PrepParams pp;
     pp.N = a.N; pp.Cin = a.Cin; pp.HW = a.H * a.W; pp.Cin_pad = pl.Cin_pad;
+    pp.vec = (pp.HW % kVec == 0) && ((uintptr_t)a.x % 16 == 0);
     pp.Cout = a.Cout; pp.K = pl.K; pp.Mp = pl.Mp; pp.Rp = pl.Rp;
     pp.tiles_c = (pl.Cin_pad + 63) / 64;
     pp.tiles_hw = (pp.HW + 63) / 64;
