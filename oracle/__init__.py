@@ -11,6 +11,7 @@ Functions (each follows the page/section cited in ``oracle.c``):
   bilinear     — one bilinear sample, zero outside the image
   softmax      — fp64 max-subtracted softmax
   dcn_core     — DCNv3/v4 core forward, channels-last
+  dcn_core_backward — gradients of dcn_core w.r.t. x, offsets and modulation
   dcn_v2_columns, dcn_v2 — DCNv2 deform-im2col and modulated deformable conv
   deform_agg   — multi-camera multi-scale deformable aggregation
 """
@@ -66,6 +67,9 @@ def _load():
         lib.oracle_dcn_core.restype = ctypes.c_int
         lib.oracle_dcn_core.argtypes = [_dp, _dp, _dp, _dp, _dp] + [_i64] * 13 + [
             ctypes.c_float, ctypes.c_int, _i64p, _i64]
+        lib.oracle_dcn_core_backward.restype = ctypes.c_int
+        lib.oracle_dcn_core_backward.argtypes = [_dp] * 10 + [_i64] * 13 + [
+            ctypes.c_float, ctypes.c_int]
         lib.oracle_dcn_v2_columns.restype = ctypes.c_int
         lib.oracle_dcn_v2_columns.argtypes = [_dp, _dp, _dp, _dp] + [_i64] * 13 + [
             ctypes.c_int, _i64p, _i64]
@@ -152,6 +156,36 @@ def dcn_core(x, offset, mask, *, kh, kw, stride=(1, 1), pad=(0, 0), dil=(1, 1),
         out = out.reshape(N, Ho, Wo, GC)
         ab = ab.reshape(N, Ho, Wo, GC)
     return out, ab
+
+
+def dcn_core_backward(x, offset, mask, grad_out, *, kh, kw, stride=(1, 1), pad=(0, 0),
+                      dil=(1, 1), offset_scale=1.0, softmax=False, G=None):
+    """Gradients of dcn_core. Shapes as dcn_core; grad_out [N,Ho,Wo,G*C].
+
+    Returns a dict with grad_x [N,H,W,G*C], grad_offset (offset's shape),
+    grad_mask (mask's shape, or [N,Ho,Wo,G,K] when mask is None: the gradient
+    w.r.t. the unit modulation), and the matching *_abs arrays of summed
+    |product terms| for error bounds."""
+    x, offset, mask, gout = _f64(x), _f64(offset), _f64(mask), _f64(grad_out)
+    N, H, W = x.shape[:3]
+    G = offset.shape[3] if G is None else G
+    GC = int(np.prod(x.shape[3:]))
+    C = GC // G
+    K = kh * kw
+    Ho, Wo = out_size(H, kh, stride[0], pad[0], dil[0]), out_size(W, kw, stride[1], pad[1], dil[1])
+    if gout.size != N * Ho * Wo * GC or offset.size != N * Ho * Wo * G * K * 2:
+        raise ValueError("dcn_core_backward: shape mismatch")
+    gx = np.zeros((N, H, W, GC)); gxa = np.zeros_like(gx)
+    goff = np.zeros((N, Ho, Wo, G, K, 2)); goffa = np.zeros_like(goff)
+    gm = np.zeros((N, Ho, Wo, G, K)); gma = np.zeros_like(gm)
+    rc = _load().oracle_dcn_core_backward(
+        _ptr(x), _ptr(offset), _ptr(mask), _ptr(gout), _ptr(gx), _ptr(goff), _ptr(gm),
+        _ptr(gxa), _ptr(goffa), _ptr(gma), N, H, W, G, C, kh, kw, stride[0], stride[1],
+        pad[0], pad[1], dil[0], dil[1], float(offset_scale), int(bool(softmax)))
+    if rc:
+        raise ValueError("oracle_dcn_core_backward rejected its arguments (%d)" % rc)
+    return dict(grad_x=gx, grad_offset=goff, grad_mask=gm,
+                grad_x_abs=gxa, grad_offset_abs=goffa, grad_mask_abs=gma)
 
 
 def _v2_dims(x, offset, kh, kw, stride, pad, dil):

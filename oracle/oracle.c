@@ -35,6 +35,11 @@
  *
  * Every function also returns, per output element, the sum of the absolute
  * values of all product terms ("absum"), used by the tests' error bound.
+ *
+ * oracle_dcn_core_backward is the derivative of oracle_dcn_core's sum,
+ * written out by hand (the pages print no backward pass); its pins are
+ * finite differences, adjoint identities and torch autograd of an
+ * independent fp64 formulation.
  */
 #include <math.h>
 #ifdef _OPENMP
@@ -170,6 +175,122 @@ int oracle_dcn_core(const double *x, const double *offset, const double *mask,
         free(m);
     }
     return bad ? 2 : 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Gradients of the DCNv3/v4 core above (the derivative of its sum; no      */
+/* page prints it). With G = grad_out[n,ho,wo,g*C+c] and, for tap k at      */
+/* (y, x) = (y0 + fy, x0 + fx), corner values X_ab = x[n, y0+a, x0+b, .]    */
+/* (0 outside the image) and bilinear weights                               */
+/*   w_00 = (1-fy)(1-fx), w_01 = (1-fy)fx, w_10 = fy(1-fx), w_11 = fy fx:   */
+/*   B    = sum_ab w_ab X_ab                                                 */
+/*   dB/dy = (1-fx)(X_10 - X_00) + fx(X_11 - X_01)                           */
+/*   dB/dx = (1-fy)(X_01 - X_00) + fy(X_11 - X_10)                           */
+/* (derivatives taken from the right at integer positions, where floor()     */
+/* moves), so that                                                          */
+/*   grad_x[corner ab] += m_k w_ab G        (every corner inside the image)  */
+/*   grad_m_k           = sum_c G B                                          */
+/*   grad_offset[k]     = (s m_k sum_c G dB/dx, s m_k sum_c G dB/dy), s =    */
+/*                        offset_scale (d fl32(s d)/dd taken as s)           */
+/*   and with softmax, grad_logit_k = m_k (grad_m_k - sum_j m_j grad_m_j).   */
+/* Outputs may be NULL. gx is overwritten (not accumulated into). The *_abs  */
+/* arrays (NULL allowed) receive the matching sums of |product terms|.       */
+/* ---------------------------------------------------------------------- */
+int oracle_dcn_core_backward(const double *x, const double *offset, const double *mask,
+                             const double *gout, double *gx, double *goff, double *gmask,
+                             double *gx_abs, double *goff_abs, double *gmask_abs,
+                             int64_t N, int64_t H, int64_t W, int64_t G, int64_t C,
+                             int64_t kh, int64_t kw, int64_t sh, int64_t sw,
+                             int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                             float offset_scale, int softmax)
+{
+    int64_t Ho = out_size(H, kh, sh, ph, dh), Wo = out_size(W, kw, sw, pw, dw);
+    int64_t K = kh * kw, GC = G * C;
+    if (Ho <= 0 || Wo <= 0) return 1;
+    double s = (double)offset_scale;
+    if (gx) for (int64_t i = 0; i < N * H * W * GC; ++i) gx[i] = 0.0;
+    if (gx_abs) for (int64_t i = 0; i < N * H * W * GC; ++i) gx_abs[i] = 0.0;
+    /* one image per iteration: the scatter into gx never crosses images */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t n = 0; n < N; ++n) {
+        double *m = (double *)malloc(sizeof(double) * (size_t)K * 4);
+        double *gm = m + K, *gma = m + 2 * K, *unused = m + 3 * K;
+        (void)unused;
+        for (int64_t ho = 0; ho < Ho; ++ho)
+        for (int64_t wo = 0; wo < Wo; ++wo)
+        for (int64_t g = 0; g < G; ++g) {
+            int64_t pg = ((n * Ho + ho) * Wo + wo) * G + g;  /* (pixel, group) pair */
+            const double *om = offset + pg * K * 2;
+            const double *mm = mask ? mask + pg * K : NULL;
+            const double *Gv = gout + ((n * Ho + ho) * Wo + wo) * GC + g * C;
+            for (int64_t k = 0; k < K; ++k) m[k] = mm ? mm[k] : 1.0;
+            if (softmax) softmax_d(mm ? mm : m, K, 1, m);
+            for (int64_t i = 0; i < kh; ++i)
+            for (int64_t j = 0; j < kw; ++j) {
+                int64_t k = i * kw + j;
+                double yy = (double)(ho * sh - ph + i * dh) + fl32_mul(offset_scale, om[2 * k + 1]);
+                double xx = (double)(wo * sw - pw + j * dw) + fl32_mul(offset_scale, om[2 * k + 0]);
+                double y0 = floor(yy), x0 = floor(xx);
+                double fy = yy - y0, fx = xx - x0;
+                double w[2][2] = {{(1.0 - fy) * (1.0 - fx), (1.0 - fy) * fx},
+                                  {fy * (1.0 - fx), fy * fx}};
+                double dwy[2][2] = {{-(1.0 - fx), -fx}, {1.0 - fx, fx}};  /* d w_ab / d fy */
+                double dwx[2][2] = {{-(1.0 - fy), 1.0 - fy}, {-fy, fy}};  /* d w_ab / d fx */
+                int inside[2][2];
+                int64_t idx[2][2];
+                for (int a = 0; a < 2; ++a)
+                    for (int b = 0; b < 2; ++b) {
+                        double qy = y0 + a, qx = x0 + b;
+                        inside[a][b] = !(qy < 0.0 || qy >= (double)H || qx < 0.0 || qx >= (double)W);
+                        idx[a][b] = inside[a][b]
+                                        ? ((n * H + (int64_t)qy) * W + (int64_t)qx) * GC + g * C
+                                        : 0;
+                    }
+                double sb = 0.0, sba = 0.0, sy = 0.0, sya = 0.0, sx = 0.0, sxa = 0.0;
+                for (int64_t c = 0; c < C; ++c) {
+                    double gc = Gv[c];
+                    for (int a = 0; a < 2; ++a)
+                        for (int b = 0; b < 2; ++b) {
+                            if (!inside[a][b]) continue;
+                            double X = x[idx[a][b] + c];
+                            sb += gc * w[a][b] * X;
+                            sba += fabs(gc * w[a][b] * X);
+                            sy += gc * dwy[a][b] * X;
+                            sya += fabs(gc * dwy[a][b] * X);
+                            sx += gc * dwx[a][b] * X;
+                            sxa += fabs(gc * dwx[a][b] * X);
+                            if (gx && w[a][b] != 0.0) gx[idx[a][b] + c] += m[k] * w[a][b] * gc;
+                            if (gx_abs) gx_abs[idx[a][b] + c] += fabs(m[k] * w[a][b] * gc);
+                        }
+                }
+                gm[k] = sb;
+                gma[k] = sba;
+                if (goff) {
+                    goff[pg * K * 2 + 2 * k + 0] = s * m[k] * sx;
+                    goff[pg * K * 2 + 2 * k + 1] = s * m[k] * sy;
+                }
+                if (goff_abs) {
+                    goff_abs[pg * K * 2 + 2 * k + 0] = fabs(s * m[k]) * sxa;
+                    goff_abs[pg * K * 2 + 2 * k + 1] = fabs(s * m[k]) * sya;
+                }
+            }
+            if (gmask || gmask_abs) {
+                double dot = 0.0, dota = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    dot += m[k] * gm[k];
+                    dota += fabs(m[k]) * gma[k];
+                }
+                for (int64_t k = 0; k < K; ++k) {
+                    double v = softmax ? m[k] * (gm[k] - dot) : gm[k];
+                    double va = softmax ? fabs(m[k]) * (gma[k] + dota) : gma[k];
+                    if (gmask) gmask[pg * K + k] = v;
+                    if (gmask_abs) gmask_abs[pg * K + k] = va;
+                }
+            }
+        }
+        free(m);
+    }
+    return 0;
 }
 
 /* ---------------------------------------------------------------------- */

@@ -30,13 +30,42 @@ MUTANTS = [
     ("v2_swap_dx_dy", "double dx = offset[(oc + 0) * HWo + r];", "double dx = offset[(oc + 1) * HWo + r];", 1),
     ("v2_mask_ignores_group", "mask[(n * dg * K + g * K + k) * HWo + r]", "mask[(n * dg * K + k) * HWo + r]", 1),
     ("v2_weight_transposed", "s += wr[rr] * col[rr];", "s += weight[(rr % Cout) * R + rr / Cout] * col[rr];", 1),
-    ("v2_point_order_col_major", "int64_t k = i * kw + j;", "int64_t k = j * kh + i;", 2),
+    ("v2_point_order_col_major", "int64_t k = i * kw + j;", "int64_t k = j * kh + i;", 3),
     ("agg_no_half_pixel", "(double)(float)(uv[0] * (double)Ws) - 0.5", "(double)(float)(uv[0] * (double)Ws)", 1),
     ("agg_uv_swapped", "double yy = (double)(float)(uv[1] * (double)Hs) - 0.5;",
      "double yy = (double)(float)(uv[0] * (double)Hs) - 0.5;", 1),
     ("agg_weight_order", "w[(p * cams + cam) * scales + sc]", "w[(sc * cams + cam) * pts + p]", 1),
     ("agg_ignores_scale_start", "(b * P_total + scale_start[cs]) * GC", "(b * P_total) * GC", 1),
     ("agg_weight_group_stride", "weights + ba * T * G + g;", "weights + ba * T * G;", 1),
+]
+
+# Mistakes in the core backward (oracle_dcn_core_backward), caught by its own pins.
+BWD_MUTANTS = [
+    ("bwd_swap_dx_dy", "fl32_mul(offset_scale, om[2 * k + 1])", "fl32_mul(offset_scale, om[2 * k + 0])", 2),
+    ("bwd_pad_sign", "(double)(ho * sh - ph + i * dh)", "(double)(ho * sh + ph + i * dh)", 2),
+    ("bwd_dy_weights_use_fy", "double dwy[2][2] = {{-(1.0 - fx), -fx}, {1.0 - fx, fx}};",
+     "double dwy[2][2] = {{-(1.0 - fy), -fy}, {1.0 - fy, fy}};", 1),
+    ("bwd_dx_sign", "double dwx[2][2] = {{-(1.0 - fy), 1.0 - fy}, {-fy, fy}};",
+     "double dwx[2][2] = {{(1.0 - fy), -(1.0 - fy)}, {fy, -fy}};", 1),
+    ("bwd_offset_pair_swapped", "goff[pg * K * 2 + 2 * k + 0] = s * m[k] * sx;",
+     "goff[pg * K * 2 + 2 * k + 0] = s * m[k] * sy;", 1),
+    ("bwd_no_offset_scale", "goff[pg * K * 2 + 2 * k + 1] = s * m[k] * sy;",
+     "goff[pg * K * 2 + 2 * k + 1] = m[k] * sy;", 1),
+    ("bwd_offset_no_modulation", "goff[pg * K * 2 + 2 * k + 0] = s * m[k] * sx;",
+     "goff[pg * K * 2 + 2 * k + 0] = s * sx;", 1),
+    ("bwd_grad_x_no_modulation", "gx[idx[a][b] + c] += m[k] * w[a][b] * gc;",
+     "gx[idx[a][b] + c] += w[a][b] * gc;", 1),
+    ("bwd_grad_x_transposed_corner", "((n * H + (int64_t)qy) * W + (int64_t)qx) * GC + g * C",
+     "((n * H + (int64_t)qx) * W + (int64_t)qy) * GC + g * C", 1),
+    ("bwd_grad_x_wrong_group", "((n * H + (int64_t)qy) * W + (int64_t)qx) * GC + g * C",
+     "((n * H + (int64_t)qy) * W + (int64_t)qx) * GC", 1),
+    ("bwd_softmax_no_centering", "double v = softmax ? m[k] * (gm[k] - dot) : gm[k];",
+     "double v = softmax ? m[k] * gm[k] : gm[k];", 1),
+    ("bwd_softmax_dot_unweighted", "dot += m[k] * gm[k];", "dot += gm[k];", 1),
+    ("bwd_mask_grad_times_m", "double v = softmax ? m[k] * (gm[k] - dot) : gm[k];",
+     "double v = softmax ? m[k] * (gm[k] - dot) : m[k] * gm[k];", 1),
+    ("bwd_mask_grad_group_stride", "const double *Gv = gout + ((n * Ho + ho) * Wo + wo) * GC + g * C;",
+     "const double *Gv = gout + ((n * Ho + ho) * Wo + wo) * GC;", 1),
 ]
 
 
@@ -57,16 +86,18 @@ def _build(src_text, tmp_path, name):
     return str(so)
 
 
-def _run_pins(lib):
+def _run_pins(lib, pins="test_oracle_pins.py"):
     env = dict(os.environ, DS_ORACLE_LIB=lib, OMP_NUM_THREADS="2")
     return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                           os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                           os.path.join(ROOT, "tests", pins)],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
 
 
 def test_unmodified_oracle_passes_pins(tmp_path):
     lib = _build(open(SRC).read(), tmp_path, "orig")
     res = _run_pins(lib)
+    assert res.returncode == 0, res.stdout[-3000:]
+    res = _run_pins(lib, "test_oracle_backward_pins.py")
     assert res.returncode == 0, res.stdout[-3000:]
 
 
@@ -76,3 +107,11 @@ def test_pins_catch_mutant(tmp_path, name, old, new, nth):
     lib = _build(text, tmp_path, name)
     res = _run_pins(lib)
     assert res.returncode != 0, "mutant %s survived the pins" % name
+
+
+@pytest.mark.parametrize("name,old,new,nth", BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
+def test_backward_pins_catch_mutant(tmp_path, name, old, new, nth):
+    text = _replace_nth(open(SRC).read(), old, new, nth)
+    lib = _build(text, tmp_path, name)
+    res = _run_pins(lib, "test_oracle_backward_pins.py")
+    assert res.returncode != 0, "mutant %s survived the backward pins" % name
