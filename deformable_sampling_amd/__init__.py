@@ -24,7 +24,8 @@ STATUS = {0: "DCN_OK", 1: "DCN_ERR_NULL", 2: "DCN_ERR_SHAPE", 3: "DCN_ERR_PARAM"
           4: "DCN_ERR_DTYPE", 5: "DCN_ERR_ALIGN", 6: "DCN_ERR_WORKSPACE", 7: "DCN_ERR_HIP"}
 
 # every symbol include/dcn.h declares
-EXPORTS = ("dcn_core_forward", "dcn_v2_workspace_bytes", "dcn_v2_forward", "dcn_v2_im2col",
+EXPORTS = ("dcn_core_forward", "dcn_core_backward_workspace_bytes", "dcn_core_backward",
+           "dcn_v2_workspace_bytes", "dcn_v2_forward", "dcn_v2_im2col",
            "deform_agg_forward", "dcn_status_string", "dcn_last_hip_error")
 
 
@@ -55,6 +56,10 @@ def load(path: str | None = None):
     i, f, vp = _c.c_int, _c.c_float, _c.c_void_p
     lib.dcn_core_forward.restype = i
     lib.dcn_core_forward.argtypes = [vp, vp, vp, vp] + [i] * 13 + [f, i, i, vp]
+    lib.dcn_core_backward_workspace_bytes.restype = _c.c_size_t
+    lib.dcn_core_backward_workspace_bytes.argtypes = [i] * 6
+    lib.dcn_core_backward.restype = i
+    lib.dcn_core_backward.argtypes = [vp] * 8 + [_c.c_size_t] + [i] * 13 + [f, i, i, vp]
     lib.dcn_v2_workspace_bytes.restype = _c.c_size_t
     lib.dcn_v2_workspace_bytes.argtypes = [i] * 13 + [i]
     lib.dcn_v2_forward.restype = i
@@ -139,6 +144,59 @@ def dcn_core_forward(x, offset, mask, out=None, *, kernel=(3, 3), stride=1, pad=
           kh, kw, sh, sw, ph, pw, dh, dw, float(offset_scale), int(bool(softmax)),
           _DTYPE_ID[x.dtype], _stream(stream))
     return out
+
+
+def dcn_core_backward_workspace_bytes(N, H, W, G, C, dtype=torch.float16):
+    return int(load().dcn_core_backward_workspace_bytes(N, H, W, G, C, _DTYPE_ID[dtype]))
+
+
+def dcn_core_backward(x, offset, mask, grad_out, *, kernel=(3, 3), stride=1, pad=1, dilation=1,
+                      offset_scale=1.0, softmax=False, need=("x", "offset", "mask"),
+                      grad_x=None, grad_offset=None, grad_mask=None, workspace=None,
+                      stream=None):
+    """Gradients of dcn_core_forward w.r.t. x, offset and mask (the names in `need`).
+    grad_out [N,Ho,Wo,G*C] in x's dtype. Returns (grad_x, grad_offset, grad_mask),
+    None for a gradient not asked for; grad_mask is w.r.t. the mask argument (the
+    unit modulation / zero logits when mask is None)."""
+    kh, kw = _pair(kernel)
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    dh, dw = _pair(dilation)
+    _check(x, "x")
+    _check(offset, "offset", torch.float32)
+    _check(mask, "mask", torch.float32, allow_none=True)
+    _check(grad_out, "grad_out", x.dtype)
+    N, H, W, GC = x.shape
+    G = offset.shape[3]
+    K = kh * kw
+    if offset.dim() != 6 or offset.shape[4] != K or offset.shape[5] != 2 or GC % G:
+        raise ValueError("offset must be [N,Ho,Wo,G,K,2] with G dividing the channels")
+    Ho, Wo = out_size(H, kh, sh, ph, dh), out_size(W, kw, sw, pw, dw)
+    if tuple(offset.shape[:3]) != (N, Ho, Wo):
+        raise ValueError("offset spatial shape %s != %s" % (tuple(offset.shape[:3]), (N, Ho, Wo)))
+    if mask is not None and tuple(mask.shape) != (N, Ho, Wo, G, K):
+        raise ValueError("mask must be [N,Ho,Wo,G,K]")
+    if tuple(grad_out.shape) != (N, Ho, Wo, GC):
+        raise ValueError("grad_out must be [N,Ho,Wo,G*C]")
+    dev = x.device
+    if "x" in need and grad_x is None:
+        grad_x = torch.empty_like(x)
+    if "offset" in need and grad_offset is None:
+        grad_offset = torch.empty_like(offset)
+    if "mask" in need and grad_mask is None:
+        grad_mask = torch.empty((N, Ho, Wo, G, K), dtype=torch.float32, device=dev)
+    _check(grad_x, "grad_x", x.dtype, allow_none=True)
+    _check(grad_offset, "grad_offset", torch.float32, allow_none=True)
+    _check(grad_mask, "grad_mask", torch.float32, allow_none=True)
+    wsb = dcn_core_backward_workspace_bytes(N, H, W, G, GC // G, x.dtype) if grad_x is not None else 0
+    if workspace is None and wsb:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _call("dcn_core_backward", _ptr(x), _ptr(offset), _ptr(mask), _ptr(grad_out), _ptr(grad_x),
+          _ptr(grad_offset), _ptr(grad_mask), _ptr(workspace),
+          0 if workspace is None else workspace.numel() * workspace.element_size(),
+          N, H, W, G, GC // G, kh, kw, sh, sw, ph, pw, dh, dw, float(offset_scale),
+          int(bool(softmax)), _DTYPE_ID[x.dtype], _stream(stream))
+    return grad_x, grad_offset, grad_mask
 
 
 def dcn_v2_workspace_bytes(N, Cin, H, W, Cout, kernel=(3, 3), stride=1, pad=1, dilation=1,

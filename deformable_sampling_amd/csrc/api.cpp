@@ -86,6 +86,53 @@ dcn_status dcn_core_forward(const void *x, const float *offset, const float *mas
     return hip_status(dcn::launch_dcn_core(a, stream));
 }
 
+size_t dcn_core_backward_workspace_bytes(int N, int H, int W, int G, int C, dcn_dtype dtype) {
+    if (!valid_dtype(dtype) || N < 0 || H <= 0 || W <= 0 || G <= 0 || C <= 0) return 0;
+    return dcn::core_bwd_workspace_bytes((long long)N * H * W * G * C, dtype);
+}
+
+dcn_status dcn_core_backward(const void *x, const float *offset, const float *mask,
+                             const void *grad_out, void *grad_x, float *grad_offset,
+                             float *grad_mask, void *workspace, size_t workspace_bytes, int N,
+                             int H, int W, int G, int C, int kh, int kw, int stride_h, int stride_w,
+                             int pad_h, int pad_w, int dil_h, int dil_w, float offset_scale,
+                             int softmax, dcn_dtype dtype, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return DCN_ERR_DTYPE;
+    if (N < 0 || H <= 0 || W <= 0 || G <= 0 || C <= 0) return DCN_ERR_SHAPE;
+    dcn_status st = check_window(kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w);
+    if (st != DCN_OK) return st;
+    const long long Ho = out_extent(H, kh, stride_h, pad_h, dil_h);
+    const long long Wo = out_extent(W, kw, stride_w, pad_w, dil_w);
+    if (Ho <= 0 || Wo <= 0) return DCN_ERR_SHAPE;
+    if ((long long)(H + 1) * (W + 1) * G * C > kI32) return DCN_ERR_SHAPE;
+    if ((long long)N * Ho * Wo * G > kI32) return DCN_ERR_SHAPE;
+    if (N == 0) return DCN_OK;
+    if (!x || !offset || !grad_out) return DCN_ERR_NULL;
+    const size_t es = dtype_size(dtype);
+    if (!aligned(x, es) || !aligned(grad_out, es) || !aligned(grad_x, es) ||
+        !aligned(offset, 4) || (mask && !aligned(mask, 4)) || !aligned(grad_offset, 4) ||
+        !aligned(grad_mask, 4))
+        return DCN_ERR_ALIGN;
+    if (grad_x && dtype != DCN_F32) {
+        const size_t need = dcn::core_bwd_workspace_bytes((long long)N * H * W * G * C, dtype);
+        if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+            return DCN_ERR_WORKSPACE;
+    }
+    if (!grad_x && !grad_offset && !grad_mask) return DCN_OK;
+
+    dcn::CoreBwdLaunch a;
+    a.x = x; a.offset = offset; a.mask = mask; a.grad_out = grad_out;
+    a.grad_x = grad_x; a.grad_offset = grad_offset; a.grad_mask = grad_mask;
+    a.workspace = workspace;
+    a.N = N; a.H = H; a.W = W; a.G = G; a.C = C; a.kh = kh; a.kw = kw;
+    a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w; a.dh = dil_h; a.dw = dil_w;
+    a.Ho = (int)Ho; a.Wo = (int)Wo;
+    a.offset_scale = offset_scale;
+    a.softmax = softmax;
+    a.dtype = dtype;
+    return hip_status(dcn::launch_dcn_core_bwd(a, stream));
+}
+
 size_t dcn_v2_workspace_bytes(int N, int Cin, int H, int W, int Cout, int kh, int kw, int stride_h,
                               int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
                               dcn_dtype dtype) {

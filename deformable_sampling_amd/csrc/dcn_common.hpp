@@ -71,9 +71,10 @@ __device__ __forceinline__ void store_f32(typename E::bits *p, const float (&f)[
 
 // Split a sampling coordinate base + t (base integer, t fp32) into the integer
 // corner c0 = base + floor(t) and the fraction f = t - floor(t). The fraction is
-// exact in fp32 (t and floor(t) share their leading bits), so the position is
-// never rounded to the grid's precision. |t| is clamped at 2^24 px: such taps are
-// outside any image this library accepts, so clamping changes nothing.
+// exact in fp32 except for t in (-1/2, 0), where f = 1 + t is rounded (by at most
+// 2^-25), so the position is never rounded to the grid's precision. |t| is clamped
+// at 2^24 px: such taps are outside any image this library accepts, so clamping
+// changes nothing.
 __device__ __forceinline__ void split_coord(int base, float t, int &c0, float &f) {
     t = fminf(fmaxf(t, -16777216.0f), 16777216.0f);
     float fl = floorf(t);

@@ -22,6 +22,25 @@ struct CoreLaunch {
 };
 hipError_t launch_dcn_core(const CoreLaunch &a, hipStream_t stream);
 
+// Core backward (dcn_core_bwd.hip). grad_x / grad_offset / grad_mask may be NULL;
+// fp16/bf16 grad_x accumulates in `workspace` (core_bwd_workspace_bytes).
+struct CoreBwdLaunch {
+    const void *x;
+    const float *offset;
+    const float *mask;  // may be NULL
+    const void *grad_out;
+    void *grad_x;
+    float *grad_offset;
+    float *grad_mask;
+    void *workspace;
+    int N, H, W, G, C, kh, kw, sh, sw, ph, pw, dh, dw, Ho, Wo;
+    float offset_scale;
+    int softmax;
+    dcn_dtype dtype;
+};
+size_t core_bwd_workspace_bytes(long long x_elems, dcn_dtype dtype);
+hipError_t launch_dcn_core_bwd(const CoreBwdLaunch &a, hipStream_t stream);
+
 // LDS halo-tile variant of the core (dcn_core_tile.hip).
 struct CoreTilePlan {
     int N, H, W, G, C, kh, kw, sh, sw, ph, pw, dh, dw, Ho, Wo;

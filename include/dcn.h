@@ -1,9 +1,10 @@
 /*
  * dcn.h — C ABI of the MI355X (gfx950) deformable-sampling library, libdcn.so.
  *
- * Three forward operations, each enqueued on a caller-supplied HIP stream:
+ * Forward operations and the core's backward, each enqueued on a caller-supplied HIP stream:
  *
  *   dcn_core_forward    DCNv3/v4 core (also DCNv1 when mask == NULL), channels-last.
+ *   dcn_core_backward   gradients of the core w.r.t. x, offsets and modulation.
  *   dcn_v2_forward      DCNv2 modulated deformable convolution, NCHW: deform-im2col
  *                       and an MFMA GEMM (fused, or in two stages through the workspace).
  *   dcn_v2_im2col       the deform-im2col stage alone: columns into the workspace.
@@ -91,6 +92,47 @@ dcn_status dcn_core_forward(const void *x, const float *offset, const float *mas
                             int stride_h, int stride_w, int pad_h, int pad_w,
                             int dil_h, int dil_w, float offset_scale, int softmax,
                             dcn_dtype dtype, hipStream_t stream);
+
+/*
+ * Workspace bytes dcn_core_backward needs for these sizes: 0 for DCN_F32, else an
+ * fp32 accumulator of N*H*W*G*C floats (rounded up to 256 bytes). 0 if invalid.
+ */
+size_t dcn_core_backward_workspace_bytes(int N, int H, int W, int G, int C, dcn_dtype dtype);
+
+/*
+ * DCNv3/v4 core backward: the gradients of dcn_core_forward's output (same
+ * arguments) w.r.t. x, the offsets and the mask. The pages define only the forward
+ * sum; these are its derivatives:
+ *
+ *   grad_out     [N, Ho, Wo, G*C]        dtype, the gradient of the loss w.r.t. out
+ *   grad_x       [N, H, W, G*C]          dtype, overwritten, or NULL (not computed)
+ *   grad_offset  [N, Ho, Wo, G, K, 2]    fp32, overwritten, or NULL
+ *   grad_mask    [N, Ho, Wo, G, K]       fp32, overwritten, or NULL; w.r.t. the mask
+ *                                        argument (the logits when softmax != 0), or,
+ *                                        when mask == NULL, w.r.t. the implied unit
+ *                                        modulation (zero logits with softmax)
+ *
+ * With w_ab the bilinear weights of tap k's corners and B_k, dB_k/dy, dB_k/dx the
+ * sample and its derivatives in the position (taken from the right at integer
+ * positions):
+ *   grad_x[corner]   += m_k * w_ab * grad_out          (corners inside the image)
+ *   grad_m_k          = sum_c grad_out[c] * B_k[c]
+ *   grad_offset[k]    = offset_scale * m_k * sum_c grad_out[c] * (dB_k/dx, dB_k/dy)[c]
+ *   softmax != 0:     grad_logit_k = m_k * (grad_m_k - sum_j m_j grad_m_j)
+ * grad_x accumulates in fp32 with atomic adds (so its rounding varies run to run
+ * within fp32 accumulation error) and is rounded once to dtype; grad_offset and
+ * grad_mask are deterministic. workspace: dcn_core_backward_workspace_bytes bytes,
+ * 256-byte aligned, used only when grad_x != NULL and dtype != DCN_F32 (may be NULL
+ * otherwise); its contents on entry are ignored. Limits and alignment as
+ * dcn_core_forward; the outputs must not overlap each other or any input.
+ */
+dcn_status dcn_core_backward(const void *x, const float *offset, const float *mask,
+                             const void *grad_out, void *grad_x, float *grad_offset,
+                             float *grad_mask, void *workspace, size_t workspace_bytes,
+                             int N, int H, int W, int G, int C, int kh, int kw,
+                             int stride_h, int stride_w, int pad_h, int pad_w,
+                             int dil_h, int dil_w, float offset_scale, int softmax,
+                             dcn_dtype dtype, hipStream_t stream);
 
 /*
  * Workspace bytes dcn_v2_forward and dcn_v2_im2col need for these sizes (0 if they

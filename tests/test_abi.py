@@ -82,6 +82,44 @@ def test_core_validation(lib):
     assert lib.dcn_last_hip_error() == 0
 
 
+def core_bwd(lib, x=A, off=A, mask=A, go=A, gx=A, goff=A, gm=A, ws=A, wsb=1 << 40, N=1, H=8,
+             W=8, G=2, C=4, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, scale=1.0, softmax=0,
+             dtype=1):
+    return lib.dcn_core_backward(x, off, mask, go, gx, goff, gm, ws, wsb, N, H, W, G, C, kh, kw,
+                                 sh, sw, ph, pw, dh, dw, scale, softmax, dtype, None)
+
+
+def test_core_backward_workspace_bytes(lib):
+    assert lib.dcn_core_backward_workspace_bytes(16, 80, 80, 16, 16, 1) == 16 * 80 * 80 * 256 * 4
+    assert lib.dcn_core_backward_workspace_bytes(1, 3, 5, 1, 3, 2) == 256  # 45 floats -> 256 B
+    assert lib.dcn_core_backward_workspace_bytes(1, 3, 5, 1, 3, 0) == 0    # fp32: in place
+    assert lib.dcn_core_backward_workspace_bytes(1, 0, 5, 1, 3, 1) == 0    # invalid
+    assert lib.dcn_core_backward_workspace_bytes(1, 3, 5, 1, 3, 9) == 0    # bad dtype
+
+
+def test_core_backward_validation(lib):
+    assert core_bwd(lib, dtype=7) == DTYPE
+    assert core_bwd(lib, N=-1) == SHAPE
+    assert core_bwd(lib, C=0) == SHAPE
+    assert core_bwd(lib, kh=5, kw=13) == SHAPE
+    assert core_bwd(lib, sh=0) == PARAM
+    assert core_bwd(lib, H=2, kh=5, ph=0) == SHAPE
+    assert core_bwd(lib, H=40000, W=40000) == SHAPE
+    assert core_bwd(lib, N=0, x=None, off=None, go=None) == OK
+    assert core_bwd(lib, x=None) == NULL
+    assert core_bwd(lib, off=None) == NULL
+    assert core_bwd(lib, go=None) == NULL
+    assert core_bwd(lib, go=A + 1) == ALIGN          # fp16 grad_out on an odd address
+    assert core_bwd(lib, gx=A + 1) == ALIGN
+    assert core_bwd(lib, goff=A + 2) == ALIGN
+    assert core_bwd(lib, gm=A + 2) == ALIGN
+    assert core_bwd(lib, ws=None) == WORKSPACE       # fp16 grad_x needs the accumulator
+    assert core_bwd(lib, ws=A + 128) == WORKSPACE    # not 256-byte aligned
+    assert core_bwd(lib, wsb=1024) == WORKSPACE      # 8*8*8 floats = 2048 B needed
+    assert core_bwd(lib, gx=None, goff=None, gm=None, ws=None) == OK  # nothing asked for
+    assert lib.dcn_last_hip_error() == 0
+
+
 def v2(lib, x=A, off=A, mask=A, w=A, out=A, ws=A, wsb=1 << 40, N=1, Cin=16, H=8, W=8, Cout=8,
        kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, dg=1, softmax=0, dtype=2):
     return lib.dcn_v2_forward(x, off, mask, w, out, ws, wsb, N, Cin, H, W, Cout, kh, kw, sh, sw,

@@ -97,6 +97,18 @@ def core_case(*, N, H, W, G, C, kh=3, kw=3, stride=(1, 1), pad=(1, 1), dil=(1, 1
         dil=tuple(dil), Ho=Ho, Wo=Wo, dtype=dtype, softmax=(mask == "logits"))
 
 
+def core_grad_out(c, seed=0, kind="normal"):
+    """An upstream gradient for the core's output [N, Ho, Wo, G*C] in x's dtype:
+    N(0,1) draws (or small integers for kind="int") from their own seeded stream."""
+    r = rng(seed + 7919)
+    shape = (c["N"], c["Ho"], c["Wo"], c["G"] * c["C"])
+    if kind == "int":
+        g = r.integers(-3, 4, size=shape).astype(np.float64)
+    else:
+        g = r.standard_normal(shape)
+    return _t(g, c["dtype"])
+
+
 def v2_case(*, N, Cin, H, W, Cout, kh=3, kw=3, stride=(1, 1), pad=(1, 1), dil=(1, 1),
             dg=1, dtype="bf16", offset_std=2.0, mask="sigmoid", w_std=0.02, seed=0,
             x_kind="normal"):
