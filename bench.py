@@ -9,9 +9,10 @@ the timed region.
 Printed (one JSON line): bilinear taps/s (whole job), ms per step, the roofline
 object of the core kernel (algorithmic bytes per launch / HIP-event launch time vs
 8 TB/s), the CPU oracle's rate on a bounded sample, and side measurements of the
-other ops (DCNv4/DCNv3 small maps, DCNv2 im2col + MFMA GEMM, aggregation).
+other ops (DCNv4/DCNv3 small maps, the core backward, DCNv2 im2col + MFMA GEMM,
+aggregation).
 
-  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--only core]
+  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--only core|bwd]
   python bench.py --calib-copy     # plain copy of known size, for counter scaling
 """
 from __future__ import annotations
@@ -122,6 +123,48 @@ def bench_core(dsa, torch, timer, name, iters, warmup):
     return dict(workload=name, taps=taps, channel_taps=taps * c["C"], algo_bytes=nbytes,
                 wall_s=wall, kernel_s=kern, taps_per_s=taps / kern,
                 gbs=nbytes / kern / 1e9, frac=nbytes / kern / 1e9 / HBM_PEAK_GBS), c
+
+
+def bench_core_bwd(dsa, torch, timer, name, iters, warmup):
+    """dcn_core_backward (grad_x, grad_offset, grad_mask) on a core workload: the
+    whole call (bin count, scan, pair pass with the sample records, tile gather)."""
+    import workloads as wl
+    c = wl.make(name)
+    dev = lambda t: None if t is None else t.to("cuda").contiguous()
+    x, off, m = dev(c["x"]), dev(c["offset"]), dev(c["mask"])
+    go = dev(wl.core_grad_out(c, seed=1))
+    gx = torch.empty_like(x)
+    goff = torch.empty_like(off)
+    gm = torch.empty_like(m) if m is not None else torch.empty(
+        (c["N"], c["Ho"], c["Wo"], c["G"], c["kh"] * c["kw"]), device="cuda")
+    N, H, W, GC = x.shape
+    G = c["G"]
+    dt = {"f32": 0, "f16": 1, "bf16": 2}[c["dtype"]]
+    lib = dsa.load()
+    wsb = lib.dcn_core_backward_workspace_bytes(N, H, W, G, GC // G, c["kh"], c["kw"],
+                                                c["stride"][0], c["stride"][1], c["pad"][0],
+                                                c["pad"][1], c["dil"][0], c["dil"][1], dt)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    args = (x.data_ptr(), off.data_ptr(), None if m is None else m.data_ptr(), go.data_ptr(),
+            gx.data_ptr(), goff.data_ptr(), gm.data_ptr(), ws.data_ptr(), wsb, N, H, W, G,
+            GC // G, c["kh"], c["kw"], c["stride"][0], c["stride"][1], c["pad"][0], c["pad"][1],
+            c["dil"][0], c["dil"][1], ctypes.c_float(1.0), int(bool(c["softmax"])), dt, stream)
+    fn = lib.dcn_core_backward
+
+    def call():
+        st = fn(*args)
+        if st:
+            raise RuntimeError("dcn_core_backward status %d" % st)
+    wall, kern = timer.run(call, iters, warmup)
+    taps = c["N"] * c["Ho"] * c["Wo"] * G * c["kh"] * c["kw"]
+    es = x.element_size()
+    # read x, offsets, masks, grad_out; write grad_x, grad_offset, grad_mask
+    nbytes = (2 * x.numel() * es + 2 * off.numel() * 4 + 2 * gm.numel() * 4
+              + go.numel() * es)
+    return dict(workload=name + " backward", taps=taps, algo_bytes=nbytes, wall_s=wall,
+                kernel_s=kern, taps_per_s=taps / kern, gbs=nbytes / kern / 1e9,
+                frac=nbytes / kern / 1e9 / HBM_PEAK_GBS)
 
 
 def bench_v2(dsa, torch, timer, iters, warmup):
@@ -241,7 +284,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["core", "all"], default="all")
+    ap.add_argument("--only", choices=["core", "all", "bwd"], default="all")
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -260,6 +303,10 @@ def main():
         return
     timer = Timer(torch)
 
+    if args.only == "bwd":  # the core backward alone (for profiling)
+        r = bench_core_bwd(dsa, torch, timer, HEADLINE, args.steps, args.warmup)
+        log("core backward: %.2f us/call" % (r["kernel_s"] * 1e6))
+        return
     log("headline: %s, warmup %d, steps %d" % (HEADLINE, args.warmup, args.steps))
     head, case = bench_core(dsa, torch, timer, HEADLINE, args.steps, args.warmup)
     log("headline done: %.2f us/launch" % (head["kernel_s"] * 1e6))
@@ -269,6 +316,8 @@ def main():
             r, _ = bench_core(dsa, torch, timer, nm, 200, 20)
             extra.append(r)
             log("%s done" % nm)
+        extra.append(bench_core_bwd(dsa, torch, timer, HEADLINE, 100, 10))
+        log("core backward done")
         extra.append(bench_v2(dsa, torch, timer, 100, 10))
         log("dcnv2 done")
         extra.append(bench_agg(dsa, torch, timer, 100, 10, softmax=True))

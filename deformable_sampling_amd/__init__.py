@@ -57,7 +57,7 @@ def load(path: str | None = None):
     lib.dcn_core_forward.restype = i
     lib.dcn_core_forward.argtypes = [vp, vp, vp, vp] + [i] * 13 + [f, i, i, vp]
     lib.dcn_core_backward_workspace_bytes.restype = _c.c_size_t
-    lib.dcn_core_backward_workspace_bytes.argtypes = [i] * 6
+    lib.dcn_core_backward_workspace_bytes.argtypes = [i] * 14
     lib.dcn_core_backward.restype = i
     lib.dcn_core_backward.argtypes = [vp] * 8 + [_c.c_size_t] + [i] * 13 + [f, i, i, vp]
     lib.dcn_v2_workspace_bytes.restype = _c.c_size_t
@@ -146,8 +146,14 @@ def dcn_core_forward(x, offset, mask, out=None, *, kernel=(3, 3), stride=1, pad=
     return out
 
 
-def dcn_core_backward_workspace_bytes(N, H, W, G, C, dtype=torch.float16):
-    return int(load().dcn_core_backward_workspace_bytes(N, H, W, G, C, _DTYPE_ID[dtype]))
+def dcn_core_backward_workspace_bytes(N, H, W, G, C, kernel=(3, 3), stride=1, pad=1,
+                                      dilation=1, dtype=torch.float16):
+    kh, kw = _pair(kernel)
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    dh, dw = _pair(dilation)
+    return int(load().dcn_core_backward_workspace_bytes(N, H, W, G, C, kh, kw, sh, sw, ph, pw,
+                                                        dh, dw, _DTYPE_ID[dtype]))
 
 
 def dcn_core_backward(x, offset, mask, grad_out, *, kernel=(3, 3), stride=1, pad=1, dilation=1,
@@ -188,7 +194,8 @@ def dcn_core_backward(x, offset, mask, grad_out, *, kernel=(3, 3), stride=1, pad
     _check(grad_x, "grad_x", x.dtype, allow_none=True)
     _check(grad_offset, "grad_offset", torch.float32, allow_none=True)
     _check(grad_mask, "grad_mask", torch.float32, allow_none=True)
-    wsb = dcn_core_backward_workspace_bytes(N, H, W, G, GC // G, x.dtype) if grad_x is not None else 0
+    wsb = dcn_core_backward_workspace_bytes(N, H, W, G, GC // G, kernel, stride, pad, dilation,
+                                            x.dtype) if grad_x is not None else 0
     if workspace is None and wsb:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
     _call("dcn_core_backward", _ptr(x), _ptr(offset), _ptr(mask), _ptr(grad_out), _ptr(grad_x),

@@ -2,6 +2,7 @@
 // Every check below runs before any HIP API call, so a rejected call has no effect
 // (this also lets the checks be exercised on a machine without a GPU).
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "dcn.h"
 #include "internal.hpp"
@@ -86,9 +87,26 @@ dcn_status dcn_core_forward(const void *x, const float *offset, const float *mas
     return hip_status(dcn::launch_dcn_core(a, stream));
 }
 
-size_t dcn_core_backward_workspace_bytes(int N, int H, int W, int G, int C, dcn_dtype dtype) {
+// DCN_CORE_BWD_ATOMIC=1 selects the atomic fallback of the backward at any size
+// (so that it can be tested); read on each call.
+static bool core_bwd_force_atomic() {
+    const char *e = getenv("DCN_CORE_BWD_ATOMIC");
+    return e && e[0] == '1';
+}
+
+size_t dcn_core_backward_workspace_bytes(int N, int H, int W, int G, int C, int kh, int kw,
+                                         int stride_h, int stride_w, int pad_h, int pad_w,
+                                         int dil_h, int dil_w, dcn_dtype dtype) {
     if (!valid_dtype(dtype) || N < 0 || H <= 0 || W <= 0 || G <= 0 || C <= 0) return 0;
-    return dcn::core_bwd_workspace_bytes((long long)N * H * W * G * C, dtype);
+    if (check_window(kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w) != DCN_OK) return 0;
+    const long long Ho = out_extent(H, kh, stride_h, pad_h, dil_h);
+    const long long Wo = out_extent(W, kw, stride_w, pad_w, dil_w);
+    if (Ho <= 0 || Wo <= 0) return 0;
+    if ((long long)(H + 1) * (W + 1) * G * C > kI32 || (long long)N * Ho * Wo * G > kI32) return 0;
+    dcn::CoreBwdPlan plan;
+    dcn::plan_core_bwd(N, H, W, G, C, (int)Ho, (int)Wo, kh * kw, dtype, core_bwd_force_atomic(),
+                       plan);
+    return plan.total;
 }
 
 dcn_status dcn_core_backward(const void *x, const float *offset, const float *mask,
@@ -113,9 +131,11 @@ dcn_status dcn_core_backward(const void *x, const float *offset, const float *ma
         !aligned(offset, 4) || (mask && !aligned(mask, 4)) || !aligned(grad_offset, 4) ||
         !aligned(grad_mask, 4))
         return DCN_ERR_ALIGN;
-    if (grad_x && dtype != DCN_F32) {
-        const size_t need = dcn::core_bwd_workspace_bytes((long long)N * H * W * G * C, dtype);
-        if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+    dcn::CoreBwdPlan plan;
+    dcn::plan_core_bwd(N, H, W, G, C, (int)Ho, (int)Wo, kh * kw, dtype, core_bwd_force_atomic(),
+                       plan);
+    if (grad_x && plan.total > 0) {
+        if (!workspace || !aligned(workspace, 256) || workspace_bytes < plan.total)
             return DCN_ERR_WORKSPACE;
     }
     if (!grad_x && !grad_offset && !grad_mask) return DCN_OK;
@@ -130,7 +150,7 @@ dcn_status dcn_core_backward(const void *x, const float *offset, const float *ma
     a.offset_scale = offset_scale;
     a.softmax = softmax;
     a.dtype = dtype;
-    return hip_status(dcn::launch_dcn_core_bwd(a, stream));
+    return hip_status(dcn::launch_dcn_core_bwd(a, plan, stream));
 }
 
 size_t dcn_v2_workspace_bytes(int N, int Cin, int H, int W, int Cout, int kh, int kw, int stride_h,

@@ -15,20 +15,34 @@
 // Derivatives at integer positions are taken from the right (the cell the
 // position's floor selects), where a zero-weight corner still enters d/dx, d/dy.
 //
-// Mapping (the forward's): the unit is a (pixel, group) pair; a pair's C channels
-// are spread over S lanes of V channels each (16-byte vectors where alignment
-// allows), Q = 64/S pairs per wavefront, PB = 4Q pairs per 256-thread block.
-//   1. offsets and modulation of the block's pairs -> LDS (coalesced), softmax;
-//   2. per lane and tap: four corner vector loads, the four partial dots D_ab over
-//      the lane's channels, and the grad_x scatter as fp32 atomic adds (corners
-//      inside the image with nonzero weight only); the partial dots are summed over
-//      the pair's S lanes and kept in LDS;
-//   3. per pair: grad_offset and grad_mask from the dots, written over the staged
-//      offsets and modulation in LDS, then stored with coalesced writes.
-// grad_x accumulates in fp32: in the caller's buffer for fp32, in the workspace
-// for fp16/bf16 (then rounded once into grad_x by a conversion kernel). The
-// accumulator is cleared by a fill kernel first. Atomic order varies, so grad_x is
-// not bitwise reproducible run to run; grad_offset and grad_mask are.
+// grad_offset and grad_mask: one pass over (pixel, group) pairs, as the forward
+// (S lanes of V channels per pair, 16-byte vectors where alignment allows): the
+// four corner dots are summed over the pair's lanes and kept in LDS; the pair's
+// gradients are formed there and stored with contiguous writes.
+//
+// grad_x is a scatter: every tap adds to four input pixels. fp32 atomic adds are
+// slow on this GPU (in global memory and in LDS alike, about 40-340 G adds/s
+// depending on coalescing), so the scatter is turned into a gather by sorting the
+// samples by destination, and grad_x is written once, without atomics:
+//   1. count: each sample (pair, tap) whose bilinear cell has a corner inside the
+//      image belongs to the 16x16 destination tile holding the cell's corner
+//      (y0+1, x0+1) (its "home"); each block counts its samples per home bin in an
+//      LDS hash table and adds one count per distinct bin to the global counters
+//      (one atomic per bin and block). A bin is (image, group, tile, sub-bin),
+//      the sub-bin telling whether the cell lies on the tile's first row and/or
+//      column, i.e. whether it also touches the tile above / to the left.
+//   2. scan: exclusive prefix sum over the bins.
+//   3. the pair pass above also writes one 16-byte record per sample into its bin
+//      (source pixel, cell within the tile, the two scaled offsets, m_k), ranges
+//      being reserved the same way, per block and bin.
+//   4. gather: one block per destination tile reads its own bin and the first-row /
+//      first-column sub-bins of the tiles below and to the right, sorts the
+//      records by cell in LDS (a counting sort with integer LDS atomics, which are
+//      fast), and every destination pixel sums, in registers, m_k * w * G over the
+//      records of the four cells it is a corner of. grad_x is stored once, in the
+//      output dtype.
+// Sizes beyond the record packing (Ho*Wo >= 2^24 pixels, or 2^31 samples) use a
+// fallback: fp32 atomic adds into an accumulator that is then rounded to dtype.
 #include "dcn_common.hpp"
 #include "internal.hpp"
 
@@ -36,6 +50,9 @@ namespace dcn {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kTile = 16;           // destination tile edge (pixels)
+constexpr int kCells = kTile + 1;   // cells touching a tile, per axis
+constexpr int kGatherCap = 3072;    // records per LDS chunk in the gather
 
 struct BwdParams {
     int N, H, W, G, C, kh, kw, sh, sw, ph, pw, dh, dw, Ho, Wo;
@@ -43,6 +60,8 @@ struct BwdParams {
     int softmax, has_mask, vec_io;
     int want_x, want_off, want_mask;
     int npairs, S, Q, nchunk, PB, nblocks;
+    int TY, TX;  // bin grid: tiles per image column / row (floor(H/16)+1, floor(W/16)+1)
+    int TXo, otiles;  // tiled pair order: output tiles per row, per image and group
 };
 
 // Copy n floats between global memory and LDS with the whole block (float4 when
@@ -75,14 +94,6 @@ __device__ __forceinline__ float seg_max(float v, int S, int q) {
     return r;
 }
 
-// Corner geometry of one tap: integer corner (y0, x0), fractions f and their
-// complements u = 1 - f, and which of the four corners lie inside the image.
-struct TapGeo {
-    int y0, x0;
-    float fy, fx, uy, ux;
-    bool vy0, vy1, vx0, vx1;
-};
-
 // base + t -> corner c0 = base + floor(t), f = t - floor(t), u = (floor(t) + 1) - t.
 // Each of f and u is exact whenever it is below 1/2 (f = 1 + t rounds only for t in
 // (-1/2, 0), where u = -t is exact; u = 1 - t rounds only for t in (0, 1/2), where f
@@ -98,6 +109,14 @@ __device__ __forceinline__ void split_coord_fu(int base, float t, int &c0, float
     c0 = base + (int)fl;
 }
 
+// Corner geometry of one tap: integer corner (y0, x0), fractions f and their
+// complements u = 1 - f, and which of the four corners lie inside the image.
+struct TapGeo {
+    int y0, x0;
+    float fy, fx, uy, ux;
+    bool vy0, vy1, vx0, vx1;
+};
+
 __device__ __forceinline__ TapGeo tap_geo(int by, int bx, float2 d, float s, int H, int W) {
     TapGeo t;
     split_coord_fu(by, __fmul_rn(s, d.y), t.y0, t.fy, t.uy);
@@ -109,15 +128,181 @@ __device__ __forceinline__ TapGeo tap_geo(int by, int bx, float2 d, float s, int
     return t;
 }
 
-template <class E, int V, int KH, int KW>
-__global__ __launch_bounds__(kThreads) void dcn_core_bwd_kernel(
+// Pair index e -> (image n, group g, output pixel pix in [0, Ho*Wo)); false for
+// the padding pairs of the tiled order.
+// Pixel-major: e = (n*Ho*Wo + pix)*G + g (the memory order of offsets and masks).
+// Tiled: e = ((n*TYo*TXo + tile)*G + g)*256 + 16*ly + lx: output pixels in 16x16
+// tiles (ragged tiles padded), one group per 256 pairs. A wavefront then takes one
+// tap of 4 rows of 16 neighbouring pixels of one group, whose samples fall into
+// few destination bins, while the G groups of a tile stay adjacent (with the XCD
+// remap of the blocks, in one L2: the groups share the cache lines of offsets,
+// x and grad_out).
+template <bool TILED>
+__device__ __forceinline__ bool decode_pair(int e, const BwdParams &p, int &n, int &g, int &pix) {
+    if constexpr (TILED) {
+        const int per = (p.otiles * p.G) << 8;
+        n = e / per;
+        const int rem = e - n * per;
+        const int tg = rem >> 8, l = rem & 255;
+        const int tile = tg / p.G;
+        g = tg - tile * p.G;
+        const int oty = tile / p.TXo, otx = tile - oty * p.TXo;
+        const int ho = oty * kTile + (l >> 4), wo = otx * kTile + (l & 15);
+        pix = ho * p.Wo + wo;
+        return ho < p.Ho && wo < p.Wo;
+    } else {
+        const int P = p.Ho * p.Wo;
+        const int pg = e / p.G;
+        g = e - pg * p.G;
+        n = pg / P;
+        pix = pg - n * P;
+        return true;
+    }
+}
+
+// Home bin of a sample whose bilinear cell has top-left corner (y0, x0); false
+// when no corner of the cell is inside the image. The home tile holds the corner
+// (y0+1, x0+1); `local` packs the cell's position in that tile (4 bits each).
+__device__ __forceinline__ bool home_bin(int y0, int x0, int n, int g, const BwdParams &p,
+                                         unsigned &bin, unsigned &local) {
+    if (y0 < -1 || y0 > p.H - 1 || x0 < -1 || x0 > p.W - 1) return false;
+    const int ty = (y0 + 1) / kTile, tx = (x0 + 1) / kTile;
+    const int ly = y0 + 1 - ty * kTile, lx = x0 + 1 - tx * kTile;
+    const unsigned sub = (ly == 0 ? 1u : 0u) | (lx == 0 ? 2u : 0u);
+    bin = ((((unsigned)(n * p.G + g) * (unsigned)p.TY + (unsigned)ty) * (unsigned)p.TX +
+            (unsigned)tx) << 2) | sub;
+    local = ((unsigned)ly << 4) | (unsigned)lx;
+    return true;
+}
+
+// Block-level aggregation of bin counters: an LDS hash table (open addressing,
+// kHash slots) from bin to a local count. block_bin_slot() inserts a sample's bin
+// and returns its slot and its rank among the block's samples of that bin (the
+// integer LDS atomics used here are fast); a full table returns kHash and the
+// caller falls back to a global atomic for that sample.
+constexpr int kHash = 256;
+constexpr unsigned kEmpty = 0xffffffffu;
+// samples per block of the pair pass: PB * K <= 4 * (65536 / (28 * K)) * K < 2344
+constexpr int kBinMaxSamples = 2344;
+
+__device__ __forceinline__ int hash_insert(unsigned *s_key, unsigned bin) {
+    unsigned h = (bin * 2654435761u) >> 24;
+    for (int probe = 0; probe < kHash; ++probe) {
+        const unsigned cur = atomicCAS(&s_key[h], kEmpty, bin);
+        if (cur == kEmpty || cur == bin) return (int)h;
+        h = (h + 1) & (kHash - 1);
+    }
+    return kHash;
+}
+
+// Slot of `bin` in the table and the sample's rank among the block's samples of
+// that bin (kHash when the table is full). Callers spread a block's samples over
+// its lanes tap-fastest, so the lanes of one instruction mostly hold different
+// bins and rarely contend on one LDS word.
+__device__ __forceinline__ int block_bin_slot(unsigned *s_key, unsigned *s_cnt, unsigned bin,
+                                              unsigned &rank) {
+    const int slot = hash_insert(s_key, bin);
+    if (slot < kHash) rank = atomicAdd(&s_cnt[slot], 1u);
+    return slot;
+}
+
+// 1. Samples per home bin. A block takes the 256 pairs of one output tile of one
+// group (tiled order) and its samples tap-fastest; it counts them per bin in LDS
+// and adds one count per distinct bin to the global counters.
+template <int KH, int KW>
+__global__ __launch_bounds__(kThreads) void bwd_count_kernel(const float *__restrict__ offset,
+                                                             unsigned *__restrict__ counts,
+                                                             BwdParams p) {
+    __shared__ unsigned s_key[kHash], s_cnt[kHash];
+    for (int i = threadIdx.x; i < kHash; i += kThreads) {
+        s_key[i] = kEmpty;
+        s_cnt[i] = 0;
+    }
+    __syncthreads();
+    const int kh = KH > 0 ? KH : p.kh, kw = KW > 0 ? KW : p.kw, K = kh * kw;
+    const int blk = xcd_remap((int)blockIdx.x, (int)gridDim.x);  // (image, tile, group)
+    int n, g, pix0;
+    decode_pair<true>(blk * kThreads, p, n, g, pix0);  // local pixel 0 of the tile
+    const int tile = (blk / p.G) % p.otiles;
+    const int oy = (tile / p.TXo) * kTile, ox = (tile % p.TXo) * kTile;
+    const float2 *od = reinterpret_cast<const float2 *>(offset);
+    for (int r = 0; r < K; ++r) {
+        const int idx = r * kThreads + (int)threadIdx.x;  // sample: local pair idx/K, tap idx%K
+        const int lq = idx / K, k = idx - lq * K;
+        const int ho = oy + (lq >> 4), wo = ox + (lq & 15);
+        bool want = false;
+        unsigned bin = 0, local, rank = 0;
+        if (ho < p.Ho && wo < p.Wo) {
+            const int i = k / kw, j = k - i * kw;
+            const float2 d = od[(((size_t)n * p.Ho * p.Wo + (size_t)ho * p.Wo + wo) * p.G + g) * K + k];
+            int y0, x0;
+            float f, u;
+            split_coord_fu(ho * p.sh - p.ph + i * p.dh, __fmul_rn(p.offset_scale, d.y), y0, f, u);
+            split_coord_fu(wo * p.sw - p.pw + j * p.dw, __fmul_rn(p.offset_scale, d.x), x0, f, u);
+            want = home_bin(y0, x0, n, g, p, bin, local);
+        }
+        if (want && block_bin_slot(s_key, s_cnt, bin, rank) == kHash)
+            atomicAdd(&counts[bin], 1u);  // table full: direct
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kHash; i += kThreads)
+        if (s_cnt[i]) atomicAdd(&counts[s_key[i]], s_cnt[i]);
+}
+
+// 2. Exclusive prefix sum of nb counts (one block of 1024 threads, 4096 counts
+// per step, coalesced); starts[nb] = total.
+__global__ __launch_bounds__(1024) void bwd_scan_kernel(const unsigned *__restrict__ counts,
+                                                        unsigned *__restrict__ starts, int nb) {
+    __shared__ unsigned s_wave[16];
+    __shared__ unsigned s_carry;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    if (t == 0) s_carry = 0;
+    __syncthreads();
+    for (int c0 = 0; c0 < nb; c0 += 4096) {
+        unsigned v[4], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = c0 + t * 4 + i;
+            v[i] = idx < nb ? counts[idx] : 0u;
+            sum += v[i];
+        }
+        unsigned incl = sum;
+        for (int o = 1; o < 64; o <<= 1) {
+            const unsigned w = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += w;
+        }
+        if (lane == 63) s_wave[wave] = incl;
+        __syncthreads();
+        unsigned before = s_carry;
+        for (int w = 0; w < wave; ++w) before += s_wave[w];
+        unsigned run = before + incl - sum;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = c0 + t * 4 + i;
+            if (idx < nb) starts[idx] = run;
+            run += v[i];
+        }
+        __syncthreads();
+        if (t == 1023) s_carry = run;
+        __syncthreads();
+    }
+    if (t == 0) starts[nb] = s_carry;
+}
+
+// 3. The pair pass: corner dots -> grad_offset, grad_mask; grad_x either as sample
+// records (BIN) or as fp32 atomic adds into gacc (fallback).
+template <class E, int V, int KH, int KW, bool BIN>
+__global__ __launch_bounds__(kThreads) void bwd_pair_kernel(
     const typename E::bits *__restrict__ x, const float *__restrict__ offset,
     const float *__restrict__ mask, const typename E::bits *__restrict__ gout,
-    float *__restrict__ gacc, float *__restrict__ goff, float *__restrict__ gmask, BwdParams p) {
+    float *__restrict__ gacc, float *__restrict__ goff, float *__restrict__ gmask,
+    uint4 *__restrict__ rec, const unsigned *__restrict__ starts, unsigned *__restrict__ fill,
+    BwdParams p) {
     extern __shared__ float smem[];
     const int kh = KH > 0 ? KH : p.kh;
     const int kw = KW > 0 ? KW : p.kw;
     const int K = kh * kw;
+    const int P = p.Ho * p.Wo;
     float *s_off = smem;               // [PB][K][2] offsets, later grad_offset
     float *s_m = s_off + p.PB * K * 2; // [PB][K] modulation m_k, later grad_mask
     float *s_d = s_m + p.PB * K;       // [PB][K][4] corner dots D_ab
@@ -126,19 +311,44 @@ __global__ __launch_bounds__(kThreads) void dcn_core_bwd_kernel(
     const int pair0 = blk * p.PB;
     const int npb = min(p.PB, p.npairs - pair0);
 
-    // 1. offsets and modulation of pairs [pair0, pair0 + npb) -> LDS
-    block_copy(s_off, offset + (size_t)pair0 * K * 2, npb * K * 2, p.vec_io);
-    if (p.has_mask) {
-        block_copy(s_m, mask + (size_t)pair0 * K, npb * K, p.vec_io);
+    // 1. offsets and modulation of the block's pairs -> LDS
+    __shared__ int s_pn[BIN ? 256 : 1], s_pg[BIN ? 256 : 1], s_phw[BIN ? 256 : 1];
+    if constexpr (BIN) {  // tiled pairs: one 2K-float run per pair
+        for (int lq = threadIdx.x; lq < npb; lq += kThreads) {
+            int n, g, pix;
+            const bool ok = decode_pair<true>(pair0 + lq, p, n, g, pix);
+            s_pn[lq] = ok ? n : -1;
+            s_pg[lq] = g;
+            s_phw[lq] = pix;
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < npb * K; idx += kThreads) {
+            const int lq = idx / K, k = idx - lq * K;
+            const int n = s_pn[lq];
+            if (n >= 0) {
+                const size_t src = (((size_t)n * P + s_phw[lq]) * p.G + s_pg[lq]) * K + k;
+                reinterpret_cast<float2 *>(s_off)[idx] = reinterpret_cast<const float2 *>(offset)[src];
+                s_m[idx] = p.has_mask ? mask[src] : (p.softmax ? 0.0f : 1.0f);
+            } else {
+                reinterpret_cast<float2 *>(s_off)[idx] = make_float2(0.0f, 0.0f);
+                s_m[idx] = 0.0f;
+            }
+        }
     } else {
-        for (int i = threadIdx.x; i < npb * K; i += kThreads) s_m[i] = p.softmax ? 0.0f : 1.0f;
+        block_copy(s_off, offset + (size_t)pair0 * K * 2, npb * K * 2, p.vec_io);
+        if (p.has_mask) {
+            block_copy(s_m, mask + (size_t)pair0 * K, npb * K, p.vec_io);
+        } else {
+            for (int i = threadIdx.x; i < npb * K; i += kThreads) s_m[i] = p.softmax ? 0.0f : 1.0f;
+        }
     }
     __syncthreads();
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int q = lane / p.S, s = lane - q * p.S;
     const int lp = wave * p.Q + q;
-    const bool active = (q < p.Q) && (lp < npb);
+    int n = 0, g = 0, pix = 0;
+    const bool active = (q < p.Q) && (lp < npb) && decode_pair<BIN>(pair0 + lp, p, n, g, pix);
 
     if (p.softmax) {  // DCNv3: softmax over the K logits of each pair, in place
         float *ml = s_m + lp * K;
@@ -157,30 +367,32 @@ __global__ __launch_bounds__(kThreads) void dcn_core_bwd_kernel(
         __syncthreads();
     }
 
-    const int e = pair0 + lp;
-    const int pix = e / p.G;
-    const int g = e - pix * p.G;
-    const int wo = pix % p.Wo;
-    const int t2 = pix / p.Wo;
-    const int ho = t2 % p.Ho;
-    const int n = t2 / p.Ho;
+    const int ho = pix / p.Wo, wo = pix - ho * p.Wo;
     const int GC = p.G * p.C;
     float *so = s_off + lp * K * 2;
     float *sm = s_m + lp * K;
     float *sd = s_d + lp * K * 4;
     const int by0 = ho * p.sh - p.ph, bx0 = wo * p.sw - p.pw;
 
-    // 2. corner dots and the grad_x scatter
+    // 2. corner dots (and, in the fallback, the grad_x atomics). Every lane of a pair
+    // runs the same number of channel rounds, so the segment sums see all S lanes.
     if (active) {
         const size_t img_base = (size_t)n * p.H * p.W * GC + (size_t)g * p.C;
         const typename E::bits *img = x + img_base;
-        float *acc = p.want_x ? gacc + img_base : nullptr;
-        const typename E::bits *gp = gout + (size_t)pix * GC + g * p.C;
+        float *acc = (!BIN && p.want_x) ? gacc + img_base : nullptr;
+        const typename E::bits *gp = gout + ((size_t)n * P + pix) * GC + g * p.C;
         int round = 0;
-        for (int ch = s; ch < p.nchunk; ch += p.S, ++round) {
+        for (int ch0 = 0; ch0 < p.nchunk; ch0 += p.S, ++round) {
+            const int ch = ch0 + s;
+            const bool has = ch < p.nchunk;
+            const int chc = has ? ch : 0;
             float gv[V];
-            load_f32<E, V>(gp + ch * V, gv);
-            const typename E::bits *imgc = img + ch * V;
+            load_f32<E, V>(gp + chc * V, gv);
+            if (!has) {
+#pragma unroll
+                for (int u = 0; u < V; ++u) gv[u] = 0.0f;
+            }
+            const typename E::bits *imgc = img + chc * V;
             auto tap = [&](int i, int j) {
                 const int k = i * kw + j;
                 const float2 d = *reinterpret_cast<const float2 *>(so + 2 * k);
@@ -202,7 +414,7 @@ __global__ __launch_bounds__(kThreads) void dcn_core_bwd_kernel(
                     D10 = fmaf(gv[u], c[u], D10);
                     D11 = fmaf(gv[u], dd[u], D11);
                 }
-                if (acc) {
+                if (!BIN && acc && has) {
                     const float m = sm[k];
                     const float gy0 = t.vy0 ? t.uy * m : 0.0f;
                     const float gy1 = t.vy1 ? t.fy * m : 0.0f;
@@ -244,6 +456,74 @@ __global__ __launch_bounds__(kThreads) void dcn_core_bwd_kernel(
             }
         }
     }
+    // grad_x records: one per sample with a corner inside the image, in its home
+    // bin. The block first counts its samples per bin in LDS (samples spread over
+    // the threads tap-fastest: a table slot, the cell and a rank per sample),
+    // reserves one range per bin with a single global atomic, then writes the
+    // records; slots are checked against the count pass (same arithmetic).
+    if constexpr (BIN) {
+        if (p.want_x) {
+            __shared__ unsigned s_key[kHash], s_cnt[kHash], s_base[kHash], s_lim[kHash];
+            __shared__ unsigned s_sr[kBinMaxSamples];  // slot << 24 | cell << 16 | rank
+            for (int i = threadIdx.x; i < kHash; i += kThreads) {
+                s_key[i] = kEmpty;
+                s_cnt[i] = 0;
+            }
+            __syncthreads();
+            const int ns = npb * K;  // <= kBinMaxSamples (the host caps PB * K)
+            for (int idx = threadIdx.x; idx < ns; idx += kThreads) {
+                const int lq = idx / K, k = idx - lq * K;
+                const int nn = s_pn[lq];
+                unsigned code = 0xffffffffu;
+                if (nn >= 0) {
+                    const int gg = s_pg[lq], pp = s_phw[lq];
+                    const int ho2 = pp / p.Wo, wo2 = pp - ho2 * p.Wo;
+                    const int i = k / kw, j = k - i * kw;
+                    const float2 d = reinterpret_cast<const float2 *>(s_off)[idx];
+                    int y0, x0;
+                    float f, u;
+                    split_coord_fu(ho2 * p.sh - p.ph + i * p.dh, __fmul_rn(p.offset_scale, d.y), y0, f, u);
+                    split_coord_fu(wo2 * p.sw - p.pw + j * p.dw, __fmul_rn(p.offset_scale, d.x), x0, f, u);
+                    unsigned bin, local, rank = 0;
+                    if (home_bin(y0, x0, nn, gg, p, bin, local)) {
+                        const int slot = block_bin_slot(s_key, s_cnt, bin, rank);
+                        if (slot < kHash) {
+                            code = ((unsigned)slot << 24) | (local << 16) | rank;
+                        } else {  // table full: reserve directly
+                            const unsigned at = starts[bin] + atomicAdd(&fill[bin], 1u);
+                            if (at < starts[bin + 1])
+                                rec[at] = make_uint4(((unsigned)pp << 8) | local,
+                                                     __float_as_uint(__fmul_rn(p.offset_scale, d.y)),
+                                                     __float_as_uint(__fmul_rn(p.offset_scale, d.x)),
+                                                     __float_as_uint(s_m[idx]));
+                        }
+                    }
+                }
+                s_sr[idx] = code;
+            }
+            __syncthreads();
+            for (int i = threadIdx.x; i < kHash; i += kThreads) {
+                if (s_cnt[i]) {
+                    const unsigned key = s_key[i];
+                    s_base[i] = starts[key] + atomicAdd(&fill[key], s_cnt[i]);
+                    s_lim[i] = starts[key + 1];
+                }
+            }
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < ns; idx += kThreads) {
+                const unsigned code = s_sr[idx];
+                if (code == 0xffffffffu) continue;
+                const int slot = (int)(code >> 24);
+                const float2 d = reinterpret_cast<const float2 *>(s_off)[idx];
+                const unsigned at = s_base[slot] + (code & 0xffffu);
+                if (at < s_lim[slot])
+                    rec[at] = make_uint4(((unsigned)s_phw[idx / K] << 8) | ((code >> 16) & 0xffu),
+                                         __float_as_uint(__fmul_rn(p.offset_scale, d.y)),
+                                         __float_as_uint(__fmul_rn(p.offset_scale, d.x)),
+                                         __float_as_uint(s_m[idx]));
+            }
+        }
+    }
     if (!p.want_off && !p.want_mask) return;  // uniform over the grid
     __syncthreads();
 
@@ -281,11 +561,179 @@ __global__ __launch_bounds__(kThreads) void dcn_core_bwd_kernel(
         }
     }
     __syncthreads();
-    if (p.want_off) block_copy(goff + (size_t)pair0 * K * 2, s_off, npb * K * 2, p.vec_io);
-    if (p.want_mask) block_copy(gmask + (size_t)pair0 * K, s_m, npb * K, p.vec_io);
+    if constexpr (BIN) {
+        for (int idx = threadIdx.x; idx < npb * K; idx += kThreads) {
+            const int lq = idx / K, k = idx - lq * K;
+            const int nn = s_pn[lq];
+            if (nn < 0) continue;
+            const size_t dst = (((size_t)nn * P + s_phw[lq]) * p.G + s_pg[lq]) * K + k;
+            if (p.want_off)
+                reinterpret_cast<float2 *>(goff)[dst] = reinterpret_cast<const float2 *>(s_off)[idx];
+            if (p.want_mask) gmask[dst] = s_m[idx];
+        }
+    } else {
+        if (p.want_off) block_copy(goff + (size_t)pair0 * K * 2, s_off, npb * K * 2, p.vec_io);
+        if (p.want_mask) block_copy(gmask + (size_t)pair0 * K, s_m, npb * K, p.vec_io);
+    }
 }
 
-// Clear n floats (vectorised when dst is 16-byte aligned).
+struct GatherParams {
+    int N, G, C, H, W, Ho, Wo;
+    int TY, TX;    // bin grid
+    int TYr, TXr;  // destination tiles (ceil(H/16), ceil(W/16))
+    int S, nchunk, nblocks;
+};
+
+// 4. grad_x of one destination tile (image n, group g, 16x16 pixels) from the
+// records of the cells touching it. Threads: 256 pixels x S channel lanes. Per LDS
+// chunk of records: load them, counting-sort them by cell, then every destination
+// pixel walks the records of the four cells it is a corner of.
+template <class E, int V>
+__global__ __launch_bounds__(1024) void bwd_gather_kernel(const uint4 *__restrict__ rec,
+                                                          const unsigned *__restrict__ starts,
+                                                          const typename E::bits *__restrict__ gout,
+                                                          typename E::bits *__restrict__ gx,
+                                                          GatherParams q) {
+    __shared__ uint4 s_rec[kGatherCap];
+    __shared__ unsigned short s_cell[kGatherCap];
+    __shared__ unsigned short s_idx[kGatherCap];
+    __shared__ unsigned s_cnt[kCells * kCells];
+    __shared__ unsigned s_pos[kCells * kCells];
+    __shared__ unsigned s_fill[kCells * kCells];
+
+    const int nthreads = kTile * kTile * q.S;
+    const int tid = threadIdx.x;
+    const int blk = xcd_remap((int)blockIdx.x, q.nblocks);
+    // block order (image, tile, group): the groups of a tile share an L2
+    const int g = blk % q.G;
+    const int t1 = blk / q.G;
+    const int ntile = q.TYr * q.TXr;
+    const int n = t1 / ntile;
+    const int tile = t1 - n * ntile;
+    const int tyi = tile / q.TXr, txi = tile - tyi * q.TXr;
+    const int ng = n * q.G + g;
+
+    // record ranges: own bin (4 sub-bins), first-row sub-bins of the tile below,
+    // first-column sub-bins of the tile to the right, the corner sub-bin of the tile
+    // below-right; each with the shift of its cells into this tile's cell grid
+    int rb[5], re[5], sy[5], sx[5];
+    {
+        auto base = [&](int yy, int xx) { return ((ng * q.TY + yy) * q.TX + xx) << 2; };
+        const int own = base(tyi, txi);
+        rb[0] = (int)starts[own]; re[0] = (int)starts[own + 4]; sy[0] = 0; sx[0] = 0;
+        for (int r = 1; r < 5; ++r) { rb[r] = re[r] = 0; sy[r] = sx[r] = 0; }
+        if (tyi + 1 < q.TY) {
+            const int d = base(tyi + 1, txi);
+            rb[1] = (int)starts[d + 1]; re[1] = (int)starts[d + 2]; sy[1] = kTile;
+            rb[2] = (int)starts[d + 3]; re[2] = (int)starts[d + 4]; sy[2] = kTile;
+        }
+        if (txi + 1 < q.TX) {
+            const int r = base(tyi, txi + 1);
+            rb[3] = (int)starts[r + 2]; re[3] = (int)starts[r + 4]; sx[3] = kTile;
+        }
+        if (tyi + 1 < q.TY && txi + 1 < q.TX) {
+            const int dr = base(tyi + 1, txi + 1);
+            rb[4] = (int)starts[dr + 3]; re[4] = (int)starts[dr + 4]; sy[4] = kTile; sx[4] = kTile;
+        }
+    }
+    int total = 0;
+    for (int r = 0; r < 5; ++r) total += re[r] - rb[r];
+
+    const int dp = tid / q.S, s = tid - dp * q.S;
+    const int qy = dp / kTile, qx = dp - qy * kTile;
+    const int Y = tyi * kTile + qy, X = txi * kTile + qx;
+    const bool inside = Y < q.H && X < q.W;
+    const int GC = q.G * q.C;
+    const size_t gbase = (size_t)n * q.Ho * q.Wo * GC + (size_t)g * q.C;
+
+    for (int ch0 = 0; ch0 < q.nchunk; ch0 += q.S) {
+        const int ch = ch0 + s;
+        const bool has = ch < q.nchunk;
+        float acc[V];
+#pragma unroll
+        for (int u = 0; u < V; ++u) acc[u] = 0.0f;
+        for (int c0 = 0; c0 < total; c0 += kGatherCap) {
+            const int nrec = min(kGatherCap, total - c0);
+            __syncthreads();  // the previous chunk's readers are done
+            for (int i = tid; i < kCells * kCells; i += nthreads) {
+                s_cnt[i] = 0;
+                s_fill[i] = 0;
+            }
+            __syncthreads();
+            for (int r = tid; r < nrec; r += nthreads) {
+                int gi = c0 + r, k = 0;
+                while (k < 4 && gi >= re[k] - rb[k]) {
+                    gi -= re[k] - rb[k];
+                    ++k;
+                }
+                const uint4 v = rec[rb[k] + gi];
+                const int cy = (int)((v.x >> 4) & 15u) + sy[k];
+                const int cx = (int)(v.x & 15u) + sx[k];
+                const int cell = cy * kCells + cx;
+                s_rec[r] = v;
+                s_cell[r] = (unsigned short)cell;
+                atomicAdd(&s_cnt[cell], 1u);
+            }
+            __syncthreads();
+            if (tid < 64) {  // exclusive scan of the 289 cell counts by one wavefront
+                constexpr int kPer = (kCells * kCells + 63) / 64;
+                unsigned v[kPer], sum = 0;
+#pragma unroll
+                for (int i = 0; i < kPer; ++i) {
+                    const int c = tid * kPer + i;
+                    v[i] = c < kCells * kCells ? s_cnt[c] : 0u;
+                    sum += v[i];
+                }
+                unsigned incl = sum;
+                for (int o = 1; o < 64; o <<= 1) {
+                    const unsigned w = __shfl_up(incl, o, 64);
+                    if (tid >= o) incl += w;
+                }
+                unsigned run = incl - sum;
+#pragma unroll
+                for (int i = 0; i < kPer; ++i) {
+                    const int c = tid * kPer + i;
+                    if (c < kCells * kCells) s_pos[c] = run;
+                    run += v[i];
+                }
+            }
+            __syncthreads();
+            for (int r = tid; r < nrec; r += nthreads) {
+                const int cell = s_cell[r];
+                const unsigned slot = atomicAdd(&s_fill[cell], 1u);
+                s_idx[s_pos[cell] + slot] = (unsigned short)r;
+            }
+            __syncthreads();
+            if (inside && has) {
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        // the cell whose corner (a, b) is this pixel
+                        const int cell = (qy + 1 - a) * kCells + (qx + 1 - b);
+                        const int i0 = (int)s_pos[cell], i1 = i0 + (int)s_cnt[cell];
+                        for (int i = i0; i < i1; ++i) {
+                            const uint4 v = s_rec[s_idx[i]];
+                            int cyy, cxx;
+                            float fy, uy, fx, ux;
+                            split_coord_fu(0, __uint_as_float(v.y), cyy, fy, uy);
+                            split_coord_fu(0, __uint_as_float(v.z), cxx, fx, ux);
+                            const float w = __uint_as_float(v.w) * (a ? fy : uy) * (b ? fx : ux);
+                            float gv[V];
+                            load_f32<E, V>(gout + gbase + (size_t)(v.x >> 8) * GC + ch * V, gv);
+#pragma unroll
+                            for (int u = 0; u < V; ++u) acc[u] = fmaf(w, gv[u], acc[u]);
+                        }
+                    }
+                }
+            }
+        }
+        if (inside && has)
+            store_f32<E, V>(gx + ((size_t)(n * q.H + Y) * q.W + X) * GC + g * q.C + ch * V, acc);
+    }
+}
+
+// Clear n 32-bit words (vectorised when dst is 16-byte aligned).
 __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ dst, long long n, int vec) {
     const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     const long long stride = (long long)gridDim.x * blockDim.x;
@@ -299,8 +747,8 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ dst,
     for (long long i = done + tid; i < n; i += stride) dst[i] = 0.0f;
 }
 
-// Round the fp32 accumulator into the fp16/bf16 gradient, 8 elements per step
-// where both ends allow it.
+// Round the fp32 accumulator into the fp16/bf16 gradient (fallback path), 8
+// elements per step where both ends allow it.
 template <class E>
 __global__ __launch_bounds__(256) void round_out_kernel(const float *__restrict__ src,
                                                         typename E::bits *__restrict__ dst,
@@ -326,8 +774,20 @@ int elementwise_blocks(long long n) {
     return (int)(b < 1 ? 1 : (b > 8192 ? 8192 : b));
 }
 
-template <class E, int V>
-hipError_t launch_v(const CoreBwdLaunch &a, const BwdParams &p, float *gacc, hipStream_t stream) {
+// Widest vector (16, 8, 4, 2 bytes) dividing C that both pointers are aligned to.
+template <class E>
+int pick_vec(int C, const void *p0, const void *p1) {
+    constexpr int elt = (int)sizeof(typename E::bits);
+    int V = 16 / elt;
+    while (V > 1 && (C % V != 0 || ((uintptr_t)p0 % (V * elt)) != 0 ||
+                     (p1 && ((uintptr_t)p1 % (V * elt)) != 0)))
+        V >>= 1;
+    return V;
+}
+
+template <class E, int V, bool BIN>
+hipError_t launch_pair(const CoreBwdLaunch &a, const BwdParams &p, float *gacc, uint4 *rec,
+                       const unsigned *starts, unsigned *fill, hipStream_t stream) {
     const int K = a.kh * a.kw;
     const size_t lds = (size_t)p.PB * K * 7 * sizeof(float);
     const dim3 grid(p.nblocks), block(kThreads);
@@ -335,22 +795,53 @@ hipError_t launch_v(const CoreBwdLaunch &a, const BwdParams &p, float *gacc, hip
     const B *x = static_cast<const B *>(a.x);
     const B *go = static_cast<const B *>(a.grad_out);
     if (a.kh == 3 && a.kw == 3)
-        hipLaunchKernelGGL((dcn_core_bwd_kernel<E, V, 3, 3>), grid, block, lds, stream, x,
-                           a.offset, a.mask, go, gacc, a.grad_offset, a.grad_mask, p);
+        hipLaunchKernelGGL((bwd_pair_kernel<E, V, 3, 3, BIN>), grid, block, lds, stream, x,
+                           a.offset, a.mask, go, gacc, a.grad_offset, a.grad_mask, rec, starts,
+                           fill, p);
     else
-        hipLaunchKernelGGL((dcn_core_bwd_kernel<E, V, 0, 0>), grid, block, lds, stream, x,
-                           a.offset, a.mask, go, gacc, a.grad_offset, a.grad_mask, p);
+        hipLaunchKernelGGL((bwd_pair_kernel<E, V, 0, 0, BIN>), grid, block, lds, stream, x,
+                           a.offset, a.mask, go, gacc, a.grad_offset, a.grad_mask, rec, starts,
+                           fill, p);
+    return hipGetLastError();
+}
+
+template <class E, bool BIN>
+hipError_t launch_pair_v(int V, const CoreBwdLaunch &a, const BwdParams &p, float *gacc,
+                         uint4 *rec, const unsigned *starts, unsigned *fill, hipStream_t stream) {
+    constexpr int elt = (int)sizeof(typename E::bits);
+    switch (V) {
+        case 8:
+            if constexpr (elt == 2) return launch_pair<E, 8, BIN>(a, p, gacc, rec, starts, fill, stream);
+            break;
+        case 4: return launch_pair<E, 4, BIN>(a, p, gacc, rec, starts, fill, stream);
+        case 2: return launch_pair<E, 2, BIN>(a, p, gacc, rec, starts, fill, stream);
+        default: return launch_pair<E, 1, BIN>(a, p, gacc, rec, starts, fill, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class E>
+hipError_t launch_gather(int V, const CoreBwdLaunch &a, const GatherParams &q, const uint4 *rec,
+                         const unsigned *starts, hipStream_t stream) {
+    constexpr int elt = (int)sizeof(typename E::bits);
+    using B = typename E::bits;
+    const B *go = static_cast<const B *>(a.grad_out);
+    B *gx = static_cast<B *>(a.grad_x);
+    const dim3 grid(q.nblocks), block(kTile * kTile * q.S);
+    switch (V) {
+        case 8:
+            if constexpr (elt == 2)
+                hipLaunchKernelGGL((bwd_gather_kernel<E, 8>), grid, block, 0, stream, rec, starts, go, gx, q);
+            break;
+        case 4: hipLaunchKernelGGL((bwd_gather_kernel<E, 4>), grid, block, 0, stream, rec, starts, go, gx, q); break;
+        case 2: hipLaunchKernelGGL((bwd_gather_kernel<E, 2>), grid, block, 0, stream, rec, starts, go, gx, q); break;
+        default: hipLaunchKernelGGL((bwd_gather_kernel<E, 1>), grid, block, 0, stream, rec, starts, go, gx, q); break;
+    }
     return hipGetLastError();
 }
 
 template <class E>
-hipError_t launch_e(const CoreBwdLaunch &a, hipStream_t stream) {
-    constexpr int elt = (int)sizeof(typename E::bits);
-    // Widest vector that divides C and that x and grad_out are aligned to.
-    int V = 16 / elt;
-    while (V > 1 && (a.C % V != 0 || ((uintptr_t)a.x % (V * elt)) != 0 ||
-                     ((uintptr_t)a.grad_out % (V * elt)) != 0))
-        V >>= 1;
+hipError_t launch_e(const CoreBwdLaunch &a, const CoreBwdPlan &pl, hipStream_t stream) {
     BwdParams p;
     p.N = a.N; p.H = a.H; p.W = a.W; p.G = a.G; p.C = a.C; p.kh = a.kh; p.kw = a.kw;
     p.sh = a.sh; p.sw = a.sw; p.ph = a.ph; p.pw = a.pw; p.dh = a.dh; p.dw = a.dw;
@@ -363,7 +854,13 @@ hipError_t launch_e(const CoreBwdLaunch &a, hipStream_t stream) {
     p.want_mask = a.grad_mask != nullptr;
     auto a16 = [](const void *ptr) { return ptr == nullptr || (uintptr_t)ptr % 16 == 0; };
     p.vec_io = a16(a.offset) && a16(a.mask) && a16(a.grad_offset) && a16(a.grad_mask);
-    p.npairs = a.N * a.Ho * a.Wo * a.G;
+    p.TY = pl.TY;
+    p.TX = pl.TX;
+    p.TXo = (a.Wo + kTile - 1) / kTile;
+    p.otiles = ((a.Ho + kTile - 1) / kTile) * p.TXo;
+    const bool bin = a.grad_x && pl.binned;
+    p.npairs = bin ? a.N * a.G * p.otiles * 256 : a.N * a.Ho * a.Wo * a.G;
+    const int V = pick_vec<E>(a.C, a.x, a.grad_out);
     p.nchunk = a.C / V;
     p.S = p.nchunk < 64 ? p.nchunk : 64;
     const int K = a.kh * a.kw;
@@ -374,23 +871,47 @@ hipError_t launch_e(const CoreBwdLaunch &a, hipStream_t stream) {
     p.PB = 4 * p.Q;
     p.nblocks = (p.npairs + p.PB - 1) / p.PB;
 
-    const long long nx = (long long)a.N * a.H * a.W * a.G * a.C;
+    char *ws = static_cast<char *>(a.workspace);
+    hipError_t err;
+    if (bin) {
+        unsigned *counts = reinterpret_cast<unsigned *>(ws + pl.off_counts);
+        unsigned *starts = reinterpret_cast<unsigned *>(ws + pl.off_starts);
+        unsigned *fill = reinterpret_cast<unsigned *>(ws + pl.off_fill);
+        uint4 *rec = reinterpret_cast<uint4 *>(ws + pl.off_rec);
+        const long long nb = pl.nbins;
+        // the counts and the fill cursors lie in [0, off_starts): one clear
+        const long long nclr = (long long)(pl.off_starts / 4);
+        hipLaunchKernelGGL(fill_zero_kernel, dim3(elementwise_blocks(nclr)), dim3(256), 0, stream,
+                           reinterpret_cast<float *>(ws), nclr, 1);
+        const dim3 cgrid((unsigned)((p.npairs + kThreads - 1) / kThreads));
+        if (a.kh == 3 && a.kw == 3)
+            hipLaunchKernelGGL((bwd_count_kernel<3, 3>), cgrid, dim3(kThreads), 0, stream, a.offset, counts, p);
+        else
+            hipLaunchKernelGGL((bwd_count_kernel<0, 0>), cgrid, dim3(kThreads), 0, stream, a.offset, counts, p);
+        hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, starts, (int)nb);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if ((err = launch_pair_v<E, true>(V, a, p, nullptr, rec, starts, fill, stream)) != hipSuccess)
+            return err;
+        GatherParams q;
+        q.N = a.N; q.G = a.G; q.C = a.C; q.H = a.H; q.W = a.W; q.Ho = a.Ho; q.Wo = a.Wo;
+        q.TY = pl.TY; q.TX = pl.TX; q.TYr = pl.TYr; q.TXr = pl.TXr;
+        const int Vg = pick_vec<E>(a.C, a.grad_out, a.grad_x);
+        q.nchunk = a.C / Vg;
+        q.S = q.nchunk < 4 ? q.nchunk : 4;
+        q.nblocks = a.N * a.G * pl.TYr * pl.TXr;
+        return launch_gather<E>(Vg, a, q, rec, starts, stream);
+    }
     float *gacc = nullptr;
+    const long long nx = (long long)a.N * a.H * a.W * a.G * a.C;
     if (a.grad_x) {
-        gacc = (E::id == DCN_F32) ? static_cast<float *>(a.grad_x) : static_cast<float *>(a.workspace);
+        gacc = (E::id == DCN_F32) ? static_cast<float *>(a.grad_x)
+                                  : reinterpret_cast<float *>(ws + pl.off_acc);
         hipLaunchKernelGGL(fill_zero_kernel, dim3(elementwise_blocks(nx)), dim3(256), 0, stream,
                            gacc, nx, (int)((uintptr_t)gacc % 16 == 0));
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
+        if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    hipError_t err = hipErrorInvalidValue;
-    switch (V) {
-        case 8: if constexpr (elt == 2) err = launch_v<E, 8>(a, p, gacc, stream); break;
-        case 4: err = launch_v<E, 4>(a, p, gacc, stream); break;
-        case 2: err = launch_v<E, 2>(a, p, gacc, stream); break;
-        default: err = launch_v<E, 1>(a, p, gacc, stream); break;
-    }
-    if (err != hipSuccess) return err;
+    if ((err = launch_pair_v<E, false>(V, a, p, gacc, nullptr, nullptr, nullptr, stream)) != hipSuccess)
+        return err;
     if constexpr (E::id != DCN_F32) {
         if (!a.grad_x) return err;
         using B = typename E::bits;
@@ -403,18 +924,48 @@ hipError_t launch_e(const CoreBwdLaunch &a, hipStream_t stream) {
     return err;
 }
 
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
 }  // namespace
 
-size_t core_bwd_workspace_bytes(long long x_elems, dcn_dtype dtype) {
-    if (dtype == DCN_F32) return 0;
-    return (size_t)((x_elems * 4 + 255) / 256 * 256);
+void plan_core_bwd(int N, int H, int W, int G, int C, int Ho, int Wo, int K, dcn_dtype dtype,
+                   bool force_fallback, CoreBwdPlan &pl) {
+    pl = CoreBwdPlan();
+    pl.TY = H / kTile + 1;
+    pl.TX = W / kTile + 1;
+    pl.TYr = (H + kTile - 1) / kTile;
+    pl.TXr = (W + kTile - 1) / kTile;
+    pl.nbins = (long long)N * G * pl.TY * pl.TX * 4;
+    pl.nsamples = (long long)N * Ho * Wo * G * K;
+    const long long tiled_pairs = (long long)N * G * ((Ho + kTile - 1) / kTile) *
+                                  ((Wo + kTile - 1) / kTile) * kTile * kTile;
+    pl.binned = !force_fallback && (long long)Ho * Wo < (1LL << 24) &&
+                pl.nsamples < (1LL << 31) && pl.nbins < (1LL << 30) && tiled_pairs < (1LL << 31);
+    if (pl.binned) {
+        size_t off = 0;
+        pl.off_counts = off;
+        off += (size_t)pl.nbins * 4 + 4;  // counts, then one spare word
+        off = (off + 15) / 16 * 16;
+        pl.off_fill = off;
+        off += (size_t)pl.nbins * 4;
+        off = align256(off);              // [0, off_starts) is cleared at once
+        pl.off_starts = off;
+        off += (size_t)pl.nbins * 4 + 4;
+        off = align256(off);
+        pl.off_rec = off;
+        off += (size_t)pl.nsamples * 16;
+        pl.total = align256(off);
+    } else {
+        pl.off_acc = 0;
+        pl.total = dtype == DCN_F32 ? 0 : align256((size_t)N * H * W * G * C * 4);
+    }
 }
 
-hipError_t launch_dcn_core_bwd(const CoreBwdLaunch &a, hipStream_t stream) {
+hipError_t launch_dcn_core_bwd(const CoreBwdLaunch &a, const CoreBwdPlan &plan, hipStream_t stream) {
     switch (a.dtype) {
-        case DCN_F32: return launch_e<EF32>(a, stream);
-        case DCN_F16: return launch_e<EF16>(a, stream);
-        case DCN_BF16: return launch_e<EBF16>(a, stream);
+        case DCN_F32: return launch_e<EF32>(a, plan, stream);
+        case DCN_F16: return launch_e<EF16>(a, plan, stream);
+        case DCN_BF16: return launch_e<EBF16>(a, plan, stream);
     }
     return hipErrorInvalidValue;
 }

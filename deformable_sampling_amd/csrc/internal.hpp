@@ -22,8 +22,7 @@ struct CoreLaunch {
 };
 hipError_t launch_dcn_core(const CoreLaunch &a, hipStream_t stream);
 
-// Core backward (dcn_core_bwd.hip). grad_x / grad_offset / grad_mask may be NULL;
-// fp16/bf16 grad_x accumulates in `workspace` (core_bwd_workspace_bytes).
+// Core backward (dcn_core_bwd.hip). grad_x / grad_offset / grad_mask may be NULL.
 struct CoreBwdLaunch {
     const void *x;
     const float *offset;
@@ -38,8 +37,18 @@ struct CoreBwdLaunch {
     int softmax;
     dcn_dtype dtype;
 };
-size_t core_bwd_workspace_bytes(long long x_elems, dcn_dtype dtype);
-hipError_t launch_dcn_core_bwd(const CoreBwdLaunch &a, hipStream_t stream);
+// Workspace plan of the backward. Binned (the default): bin counts, fill cursors,
+// bin starts and one 16-byte record per sample. Fallback (sizes beyond the record
+// packing, or force_fallback): an fp32 grad_x accumulator for fp16/bf16.
+struct CoreBwdPlan {
+    bool binned;
+    int TY, TX, TYr, TXr;  // bin grid (floor(H/16)+1 x floor(W/16)+1), real tiles (ceil)
+    long long nbins, nsamples;
+    size_t off_counts, off_fill, off_starts, off_rec, off_acc, total;
+};
+void plan_core_bwd(int N, int H, int W, int G, int C, int Ho, int Wo, int K, dcn_dtype dtype,
+                   bool force_fallback, CoreBwdPlan &plan);
+hipError_t launch_dcn_core_bwd(const CoreBwdLaunch &a, const CoreBwdPlan &plan, hipStream_t stream);
 
 // LDS halo-tile variant of the core (dcn_core_tile.hip).
 struct CoreTilePlan {

@@ -94,10 +94,18 @@ dcn_status dcn_core_forward(const void *x, const float *offset, const float *mas
                             dcn_dtype dtype, hipStream_t stream);
 
 /*
- * Workspace bytes dcn_core_backward needs for these sizes: 0 for DCN_F32, else an
- * fp32 accumulator of N*H*W*G*C floats (rounded up to 256 bytes). 0 if invalid.
+ * Workspace bytes dcn_core_backward needs when grad_x is requested (0 if the sizes
+ * are invalid). grad_x is formed without atomics: the samples are sorted by
+ * destination tile through the workspace, which holds per-bin counters and start
+ * offsets (4 * N*G*(H/16+1)*(W/16+1) bins of 4 bytes, three arrays) and one
+ * 16-byte record per sample (N*Ho*Wo*G*K records), each region 256-byte aligned.
+ * Beyond N*Ho*Wo*G*K >= 2^31 or Ho*Wo >= 2^24 (or with the environment variable
+ * DCN_CORE_BWD_ATOMIC=1) the backward instead accumulates grad_x with fp32 atomic
+ * adds, and the workspace is an fp32 copy of x's shape for fp16/bf16 (0 for fp32).
  */
-size_t dcn_core_backward_workspace_bytes(int N, int H, int W, int G, int C, dcn_dtype dtype);
+size_t dcn_core_backward_workspace_bytes(int N, int H, int W, int G, int C, int kh, int kw,
+                                         int stride_h, int stride_w, int pad_h, int pad_w,
+                                         int dil_h, int dil_w, dcn_dtype dtype);
 
 /*
  * DCNv3/v4 core backward: the gradients of dcn_core_forward's output (same
@@ -119,11 +127,11 @@ size_t dcn_core_backward_workspace_bytes(int N, int H, int W, int G, int C, dcn_
  *   grad_m_k          = sum_c grad_out[c] * B_k[c]
  *   grad_offset[k]    = offset_scale * m_k * sum_c grad_out[c] * (dB_k/dx, dB_k/dy)[c]
  *   softmax != 0:     grad_logit_k = m_k * (grad_m_k - sum_j m_j grad_m_j)
- * grad_x accumulates in fp32 with atomic adds (so its rounding varies run to run
- * within fp32 accumulation error) and is rounded once to dtype; grad_offset and
- * grad_mask are deterministic. workspace: dcn_core_backward_workspace_bytes bytes,
- * 256-byte aligned, used only when grad_x != NULL and dtype != DCN_F32 (may be NULL
- * otherwise); its contents on entry are ignored. Limits and alignment as
+ * grad_x sums in fp32 and is rounded once to dtype; the order of its sums varies
+ * from run to run (within fp32 accumulation error); grad_offset and grad_mask are
+ * deterministic. workspace: dcn_core_backward_workspace_bytes bytes, 256-byte
+ * aligned, used only when grad_x != NULL (may be NULL otherwise, or when that size
+ * is 0); its contents on entry are ignored. Limits and alignment as
  * dcn_core_forward; the outputs must not overlap each other or any input.
  */
 dcn_status dcn_core_backward(const void *x, const float *offset, const float *mask,

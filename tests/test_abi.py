@@ -89,12 +89,30 @@ def core_bwd(lib, x=A, off=A, mask=A, go=A, gx=A, goff=A, gm=A, ws=A, wsb=1 << 4
                                  sh, sw, ph, pw, dh, dw, scale, softmax, dtype, None)
 
 
+def bwd_ws(lib, N, H, W, G, C, kh=3, kw=3, s=1, p=1, d=1, dtype=1):
+    return lib.dcn_core_backward_workspace_bytes(N, H, W, G, C, kh, kw, s, s, p, p, d, d, dtype)
+
+
 def test_core_backward_workspace_bytes(lib):
-    assert lib.dcn_core_backward_workspace_bytes(16, 80, 80, 16, 16, 1) == 16 * 80 * 80 * 256 * 4
-    assert lib.dcn_core_backward_workspace_bytes(1, 3, 5, 1, 3, 2) == 256  # 45 floats -> 256 B
-    assert lib.dcn_core_backward_workspace_bytes(1, 3, 5, 1, 3, 0) == 0    # fp32: in place
-    assert lib.dcn_core_backward_workspace_bytes(1, 0, 5, 1, 3, 1) == 0    # invalid
-    assert lib.dcn_core_backward_workspace_bytes(1, 3, 5, 1, 3, 9) == 0    # bad dtype
+    # binned: counts + fill cursors, starts (256-B aligned), 16-B records per sample
+    N, H, W, G, C = 16, 80, 80, 16, 16
+    nb = N * G * (80 // 16 + 1) ** 2 * 4
+    a256 = lambda v: (v + 255) // 256 * 256
+    head = a256((nb * 4 + 4 + 15) // 16 * 16 + nb * 4)
+    starts = a256(nb * 4 + 4)
+    assert bwd_ws(lib, N, H, W, G, C) == a256(head + starts + N * 80 * 80 * G * 9 * 16)
+    assert bwd_ws(lib, 1, 3, 5, 1, 3, dtype=0) > 0            # fp32 binned too
+    assert bwd_ws(lib, 1, 0, 5, 1, 3) == 0                    # invalid
+    assert bwd_ws(lib, 1, 3, 5, 1, 3, dtype=9) == 0           # bad dtype
+    assert bwd_ws(lib, 1, 3, 5, 1, 3, s=0) == 0               # stride 0
+    assert bwd_ws(lib, 1, 2, 2, 1, 3, kh=5, kw=5, p=0) == 0   # Ho <= 0
+
+
+def test_core_backward_workspace_bytes_atomic_fallback(lib, monkeypatch):
+    monkeypatch.setenv("DCN_CORE_BWD_ATOMIC", "1")
+    assert bwd_ws(lib, 16, 80, 80, 16, 16) == 16 * 80 * 80 * 256 * 4
+    assert bwd_ws(lib, 1, 3, 5, 1, 3, dtype=2) == 256          # 45 floats -> 256 B
+    assert bwd_ws(lib, 1, 3, 5, 1, 3, dtype=0) == 0            # fp32: in place
 
 
 def test_core_backward_validation(lib):
@@ -115,7 +133,7 @@ def test_core_backward_validation(lib):
     assert core_bwd(lib, gm=A + 2) == ALIGN
     assert core_bwd(lib, ws=None) == WORKSPACE       # fp16 grad_x needs the accumulator
     assert core_bwd(lib, ws=A + 128) == WORKSPACE    # not 256-byte aligned
-    assert core_bwd(lib, wsb=1024) == WORKSPACE      # 8*8*8 floats = 2048 B needed
+    assert core_bwd(lib, wsb=bwd_ws(lib, 1, 8, 8, 2, 4) - 1) == WORKSPACE
     assert core_bwd(lib, gx=None, goff=None, gm=None, ws=None) == OK  # nothing asked for
     assert lib.dcn_last_hip_error() == 0
 

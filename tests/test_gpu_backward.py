@@ -107,6 +107,10 @@ BWD_SWEEP = [
     ("f32_wide_c320", dict(N=1, H=5, W=6, G=1, C=320, dtype="f32"), {}),
     ("f16_wide_c1024_two_rounds", dict(N=1, H=4, W=5, G=1, C=1024, dtype="f16"), {}),
     ("f16_many_groups", dict(N=1, H=8, W=8, G=32, C=8, dtype="f16"), {}),
+    ("f16_c1040_uneven_rounds", dict(N=1, H=3, W=4, G=1, C=1040, dtype="f16"), {}),
+    ("f32_tiles_exact_32x48", dict(N=1, H=32, W=48, G=2, C=4, offset_std=6.0, dtype="f32"), {}),
+    ("bf16_tiles_ragged_37x21", dict(N=2, H=37, W=21, G=2, C=16, offset_std=4.0, dtype="bf16"), {}),
+    ("f32_c48_three_gather_rounds", dict(N=1, H=18, W=17, G=1, C=48, dtype="f32"), {}),
 ]
 
 
@@ -145,7 +149,7 @@ def test_backward_detector_p3_fp16_two_images(gpu):
 
 def test_backward_integer_inputs_bit_exact(gpu):
     """Small-integer x and grad_out, integer offsets, unit modulation: all products
-    and sums are exact integers in fp32 whatever the atomic order, and integer
+    and sums are exact integers in fp32 whatever the summation order, and integer
     positions take the right derivative on both sides, so all three gradients equal
     the oracle bit for bit (fp16 grad_x too: the integers are representable)."""
     c = wl.core_case(N=2, H=12, W=13, G=3, C=8, dtype="f32", mask="ones", seed=5, x_kind="int")
@@ -175,6 +179,46 @@ def test_backward_subsets_and_determinism(gpu):
     assert torch.equal(only_off[1], full[1]) and torch.equal(only_m[2], full[2])
     o = oracle_bwd(c, go)
     check_grad(host(only_x[0]), o["grad_x"], o["grad_x_abs"], "f16", "grad_x alone")
+
+
+def test_backward_one_tile_receives_every_sample(gpu):
+    """Every sample of a 48x48 map lands inside input tile (1, 1): that tile's gather
+    walks its records in several LDS chunks, all other tiles have none."""
+    c = wl.core_case(N=1, H=48, W=48, G=2, C=8, dtype="f32", seed=21)
+    r = np.random.default_rng(21)
+    Ho, Wo, K = c["Ho"], c["Wo"], 9
+    ho = np.arange(Ho).reshape(Ho, 1, 1, 1)
+    wo = np.arange(Wo).reshape(1, Wo, 1, 1)
+    ki = (np.arange(K) // 3).reshape(1, 1, 1, K)
+    kj = (np.arange(K) % 3).reshape(1, 1, 1, K)
+    ty = r.uniform(16.0, 31.0, (Ho, Wo, 2, K))
+    tx = r.uniform(16.0, 31.0, (Ho, Wo, 2, K))
+    off = np.stack([tx - (wo - 1 + kj), ty - (ho - 1 + ki)], -1)[None]
+    c["offset"] = torch.from_numpy(off).float().contiguous()
+    go = wl.core_grad_out(c, seed=21)
+    res = run_bwd(c, go)
+    o = oracle_bwd(c, go)
+    gx = host(res[0])
+    assert not gx[:, :16].any() and not gx[:, 32:].any() and not gx[:, :, :16].any()
+    _say("one tile", check_all(res, o, "f32", "one tile"))
+
+
+FALLBACK_CASES = [s for s in BWD_SWEEP if s[0] in (
+    "f32_vec4_tails", "f16_vec8", "bf16_scalar_c3", "f32_softmax", "f32_k5x5",
+    "f16_c1040_uneven_rounds")]
+
+
+@pytest.mark.parametrize("name,args,extra", FALLBACK_CASES, ids=[s[0] for s in FALLBACK_CASES])
+def test_backward_atomic_fallback(gpu, monkeypatch, name, args, extra):
+    """The fp32-atomic fallback (used beyond the record packing's limits), selected
+    here at small sizes through DCN_CORE_BWD_ATOMIC=1."""
+    monkeypatch.setenv("DCN_CORE_BWD_ATOMIC", "1")
+    c = wl.core_case(seed=300 + len(name), **args)
+    go = wl.core_grad_out(c, seed=len(name))
+    _say("core backward atomic fallback", name)
+    r = run_bwd(c, go, **extra)
+    o = oracle_bwd(c, go, **extra)
+    _say(name, check_all(r, o, c["dtype"], name))
 
 
 def test_backward_empty_batch(gpu):
