@@ -14,6 +14,7 @@ Functions (each follows the page/section cited in ``oracle.c``):
   dcn_core_backward — gradients of dcn_core w.r.t. x, offsets and modulation
   dcn_v2_columns, dcn_v2 — DCNv2 deform-im2col and modulated deformable conv
   deform_agg   — multi-camera multi-scale deformable aggregation
+  deform_agg_backward — gradients of deform_agg w.r.t. features, locations, weights
 """
 from __future__ import annotations
 
@@ -79,6 +80,9 @@ def _load():
         lib.oracle_deform_agg.restype = ctypes.c_int
         lib.oracle_deform_agg.argtypes = [_dp, _i32p, _i32p, _dp, _dp, _dp, _dp] + [
             _i64] * 8 + [ctypes.c_int, _i64p, _i64]
+        lib.oracle_deform_agg_backward.restype = ctypes.c_int
+        lib.oracle_deform_agg_backward.argtypes = [_dp, _i32p, _i32p, _dp, _dp, _dp] + [_dp] * 6 + [
+            _i64] * 8 + [ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -258,3 +262,31 @@ def deform_agg(feat, spatial_shape, scale_start, loc, weights, *, softmax=False,
         out = out.reshape(B, A, GC)
         ab = ab.reshape(B, A, GC)
     return out, ab
+
+
+def deform_agg_backward(feat, spatial_shape, scale_start, loc, weights, grad_out, *,
+                        softmax=False):
+    """Gradients of deform_agg. grad_out [B,A,G*Cg]. Returns a dict with grad_feat
+    (feat's shape), grad_loc (loc's shape), grad_weights (weights' shape) and the
+    matching *_abs arrays (sums of |product terms|)."""
+    feat, loc, weights, gout = _f64(feat), _f64(loc), _f64(weights), _f64(grad_out)
+    ss = np.ascontiguousarray(np.asarray(spatial_shape, dtype=np.int32))
+    st = np.ascontiguousarray(np.asarray(scale_start, dtype=np.int32))
+    B, P_total, GC = feat.shape
+    _, A, pts, cams, _ = loc.shape
+    scales, G = weights.shape[4], weights.shape[5]
+    Cg = GC // G
+    if gout.size != B * A * GC:
+        raise ValueError("deform_agg_backward: grad_out must be [B,A,G*Cg]")
+    gf, gfa = np.zeros_like(feat), np.zeros_like(feat)
+    gl, gla = np.zeros_like(loc), np.zeros_like(loc)
+    gw, gwa = np.zeros_like(weights), np.zeros_like(weights)
+    rc = _load().oracle_deform_agg_backward(
+        _ptr(feat), _ptr(ss, _i32p), _ptr(st, _i32p), _ptr(loc), _ptr(weights), _ptr(gout),
+        _ptr(gf), _ptr(gl), _ptr(gw), _ptr(gfa), _ptr(gla), _ptr(gwa), B, P_total, A, pts, cams,
+        scales, G, Cg, int(bool(softmax)))
+    if rc:
+        raise ValueError("oracle_deform_agg_backward rejected its arguments (%d)" % rc)
+    return dict(grad_feat=gf, grad_loc=gl, grad_weights=gw, grad_feat_abs=gfa,
+                grad_loc_abs=gla, grad_weights_abs=gwa)
+

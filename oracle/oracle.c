@@ -472,3 +472,119 @@ int oracle_deform_agg(const double *feat, const int32_t *spatial_shape,
     }
     return bad ? 2 : 0;
 }
+
+/* ---------------------------------------------------------------------- */
+/* Gradients of the aggregation above (its derivative; [AGG] section 2.1   */
+/* names the gradients of the features, the sampling locations and the     */
+/* weights). With G the group's grad_out, wt the (softmax-normalised)       */
+/* weight of sample t = (p, cam, s) and B_t, dB_t/dy, dB_t/dx the bilinear  */
+/* sample and its derivatives in the pixel position (from the right at     */
+/* integer positions):                                                      */
+/*   grad_feat[corner ab of t] += wt * w_ab * G         (inside the map)    */
+/*   grad_w_t = sum_c G_c B_t,c  (softmax: wt (grad_w_t - sum_j wj grad_w_j))*/
+/*   grad_u(p,cam) += wt * W_s * sum_c G_c dB_t/dx,c   over scales, groups  */
+/*   grad_v(p,cam) += wt * H_s * sum_c G_c dB_t/dy,c                        */
+/* (x = fl32(u*W_s) - 0.5, whose derivative in u is taken as W_s). Outputs  */
+/* are overwritten; any may be NULL; the *_abs arrays (NULL allowed) get    */
+/* the matching sums of |product terms|. One thread per group: the groups   */
+/* write disjoint channels of grad_feat and grad_w; grad_loc sums the       */
+/* groups' partials in group order.                                         */
+/* ---------------------------------------------------------------------- */
+int oracle_deform_agg_backward(const double *feat, const int32_t *spatial_shape,
+                               const int32_t *scale_start, const double *loc,
+                               const double *weights, const double *gout,
+                               double *gfeat, double *gloc, double *gw,
+                               double *gfeat_abs, double *gloc_abs, double *gw_abs,
+                               int64_t B, int64_t P_total, int64_t A, int64_t pts,
+                               int64_t cams, int64_t scales, int64_t G, int64_t Cg,
+                               int softmax)
+{
+    int64_t GC = G * Cg, T = pts * cams * scales, NL = B * A * pts * cams * 2;
+    for (int64_t cs = 0; cs < cams * scales; ++cs) {
+        int64_t Hs = spatial_shape[2 * cs], Ws = spatial_shape[2 * cs + 1];
+        if (Hs <= 0 || Ws <= 0 || scale_start[cs] < 0 || scale_start[cs] + Hs * Ws > P_total)
+            return 1;
+    }
+    if (gfeat) for (int64_t i = 0; i < B * P_total * GC; ++i) gfeat[i] = 0.0;
+    if (gfeat_abs) for (int64_t i = 0; i < B * P_total * GC; ++i) gfeat_abs[i] = 0.0;
+    double *part = (double *)calloc((size_t)(G * NL * 2), sizeof(double)); /* loc partials, abs */
+    if (!part) return 3;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t g = 0; g < G; ++g) {
+        double *w = (double *)malloc(sizeof(double) * (size_t)T * 3);
+        double *gt = w + T, *gta = w + 2 * T;
+        double *pl = part + g * NL * 2, *pla = pl + NL;
+        for (int64_t ba = 0; ba < B * A; ++ba) {
+            int64_t b = ba / A;
+            const double *wl = weights + ba * T * G + g;
+            if (softmax) softmax_d(wl, T, G, w);
+            else for (int64_t i = 0; i < T; ++i) w[i] = wl[i * G];
+            const double *Gv = gout + ba * GC + g * Cg;
+            for (int64_t p = 0; p < pts; ++p)
+            for (int64_t cam = 0; cam < cams; ++cam) {
+                const double *uv = loc + ((ba * pts + p) * cams + cam) * 2;
+                double *lg = pl + ((ba * pts + p) * cams + cam) * 2;
+                double *lga = pla + ((ba * pts + p) * cams + cam) * 2;
+                for (int64_t sc = 0; sc < scales; ++sc) {
+                    int64_t cs = cam * scales + sc, t = (p * cams + cam) * scales + sc;
+                    int64_t Hs = spatial_shape[2 * cs], Ws = spatial_shape[2 * cs + 1];
+                    double xx = (double)(float)(uv[0] * (double)Ws) - 0.5;
+                    double yy = (double)(float)(uv[1] * (double)Hs) - 0.5;
+                    double y0 = floor(yy), x0 = floor(xx), fy = yy - y0, fx = xx - x0;
+                    double wb[2][2] = {{(1.0 - fy) * (1.0 - fx), (1.0 - fy) * fx},
+                                       {fy * (1.0 - fx), fy * fx}};
+                    double dwy[2][2] = {{-(1.0 - fx), -fx}, {1.0 - fx, fx}};
+                    double dwx[2][2] = {{-(1.0 - fy), 1.0 - fy}, {-fy, fy}};
+                    double sb = 0.0, sba = 0.0, sy = 0.0, sya = 0.0, sx = 0.0, sxa = 0.0;
+                    for (int a = 0; a < 2; ++a)
+                    for (int bb = 0; bb < 2; ++bb) {
+                        double qy = y0 + a, qx = x0 + bb;
+                        if (qy < 0.0 || qy >= (double)Hs || qx < 0.0 || qx >= (double)Ws) continue;
+                        int64_t row = b * P_total + scale_start[cs] + (int64_t)qy * Ws + (int64_t)qx;
+                        const double *X = feat + row * GC + g * Cg;
+                        for (int64_t c = 0; c < Cg; ++c) {
+                            double gx = Gv[c] * X[c];
+                            sb += wb[a][bb] * gx;
+                            sba += fabs(wb[a][bb] * gx);
+                            sy += dwy[a][bb] * gx;
+                            sya += fabs(dwy[a][bb] * gx);
+                            sx += dwx[a][bb] * gx;
+                            sxa += fabs(dwx[a][bb] * gx);
+                            if (gfeat) gfeat[row * GC + g * Cg + c] += w[t] * wb[a][bb] * Gv[c];
+                            if (gfeat_abs) gfeat_abs[row * GC + g * Cg + c] += fabs(w[t] * wb[a][bb] * Gv[c]);
+                        }
+                    }
+                    gt[t] = sb;
+                    gta[t] = sba;
+                    lg[0] += w[t] * (double)Ws * sx;
+                    lg[1] += w[t] * (double)Hs * sy;
+                    lga[0] += fabs(w[t]) * (double)Ws * sxa;
+                    lga[1] += fabs(w[t]) * (double)Hs * sya;
+                }
+            }
+            double dot = 0.0, dota = 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                dot += w[t] * gt[t];
+                dota += fabs(w[t]) * gta[t];
+            }
+            for (int64_t t = 0; t < T; ++t) {
+                double v = softmax ? w[t] * (gt[t] - dot) : gt[t];
+                double va = softmax ? fabs(w[t]) * (gta[t] + dota) : gta[t];
+                if (gw) gw[(ba * T + t) * G + g] = v;
+                if (gw_abs) gw_abs[(ba * T + t) * G + g] = va;
+            }
+        }
+        free(w);
+    }
+    for (int64_t i = 0; i < NL; ++i) {
+        double v = 0.0, va = 0.0;
+        for (int64_t g = 0; g < G; ++g) {
+            v += part[g * NL * 2 + i];
+            va += part[g * NL * 2 + NL + i];
+        }
+        if (gloc) gloc[i] = v;
+        if (gloc_abs) gloc_abs[i] = va;
+    }
+    free(part);
+    return 0;
+}

@@ -68,6 +68,25 @@ BWD_MUTANTS = [
      "const double *Gv = gout + ((n * Ho + ho) * Wo + wo) * GC;", 1),
 ]
 
+# Mistakes in the aggregation backward (oracle_deform_agg_backward), caught by its pins.
+AGG_BWD_MUTANTS = [
+    ("aggbwd_loc_scale_factor", "lg[0] += w[t] * (double)Ws * sx;", "lg[0] += w[t] * (double)Hs * sx;", 1),
+    ("aggbwd_loc_uv_swapped", "lg[1] += w[t] * (double)Hs * sy;", "lg[1] += w[t] * (double)Hs * sx;", 1),
+    ("aggbwd_loc_no_weight", "lg[0] += w[t] * (double)Ws * sx;", "lg[0] += (double)Ws * sx;", 1),
+    ("aggbwd_feat_no_weight", "gfeat[row * GC + g * Cg + c] += w[t] * wb[a][bb] * Gv[c];",
+     "gfeat[row * GC + g * Cg + c] += wb[a][bb] * Gv[c];", 1),
+    ("aggbwd_feat_ignores_scale_start",
+     "int64_t row = b * P_total + scale_start[cs] + (int64_t)qy * Ws + (int64_t)qx;",
+     "int64_t row = b * P_total + (int64_t)qy * Ws + (int64_t)qx;", 1),
+    ("aggbwd_softmax_no_centering", "double v = softmax ? w[t] * (gt[t] - dot) : gt[t];",
+     "double v = softmax ? w[t] * gt[t] : gt[t];", 1),
+    ("aggbwd_weights_layout", "if (gw) gw[(ba * T + t) * G + g] = v;", "if (gw) gw[(ba * G + g) * T + t] = v;", 1),
+    ("aggbwd_dx_sign", "double dwx[2][2] = {{-(1.0 - fy), 1.0 - fy}, {-fy, fy}};",
+     "double dwx[2][2] = {{(1.0 - fy), -(1.0 - fy)}, {fy, -fy}};", 2),
+    ("aggbwd_grad_out_group_stride", "const double *Gv = gout + ba * GC + g * Cg;",
+     "const double *Gv = gout + ba * GC;", 1),
+]
+
 
 def _replace_nth(text, old, new, n):
     idx = -1
@@ -99,6 +118,8 @@ def test_unmodified_oracle_passes_pins(tmp_path):
     assert res.returncode == 0, res.stdout[-3000:]
     res = _run_pins(lib, "test_oracle_backward_pins.py")
     assert res.returncode == 0, res.stdout[-3000:]
+    res = _run_pins(lib, "test_oracle_agg_backward_pins.py")
+    assert res.returncode == 0, res.stdout[-3000:]
 
 
 @pytest.mark.parametrize("name,old,new,nth", MUTANTS, ids=[m[0] for m in MUTANTS])
@@ -115,3 +136,12 @@ def test_backward_pins_catch_mutant(tmp_path, name, old, new, nth):
     lib = _build(text, tmp_path, name)
     res = _run_pins(lib, "test_oracle_backward_pins.py")
     assert res.returncode != 0, "mutant %s survived the backward pins" % name
+
+
+@pytest.mark.parametrize("name,old,new,nth", AGG_BWD_MUTANTS, ids=[m[0] for m in AGG_BWD_MUTANTS])
+def test_agg_backward_pins_catch_mutant(tmp_path, name, old, new, nth):
+    text = _replace_nth(open(SRC).read(), old, new, nth)
+    lib = _build(text, tmp_path, name)
+    res = _run_pins(lib, "test_oracle_agg_backward_pins.py")
+    assert res.returncode != 0, "mutant %s survived the aggregation backward pins" % name
+
