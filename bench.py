@@ -10,9 +10,9 @@ Printed (one JSON line): bilinear taps/s (whole job), ms per step, the roofline
 object of the core kernel (algorithmic bytes per launch / HIP-event launch time vs
 8 TB/s), the CPU oracle's rate on a bounded sample, and side measurements of the
 other ops (DCNv4/DCNv3 small maps, the core backward, DCNv2 im2col + MFMA GEMM,
-aggregation).
+aggregation forward and backward).
 
-  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--only core|bwd]
+  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--only core|bwd|aggbwd]
   python bench.py --calib-copy     # plain copy of known size, for counter scaling
 """
 from __future__ import annotations
@@ -225,6 +225,42 @@ def bench_agg(dsa, torch, timer, iters, warmup, softmax=True):
                 frac=nbytes / kern / 1e9 / HBM_PEAK_GBS)
 
 
+def bench_agg_bwd(dsa, torch, timer, iters, warmup):
+    """deform_agg_backward (features, locations, weights) on the six-camera workload,
+    softmax weights: the whole call (clear, gradient kernel, grad_loc reduction)."""
+    import numpy as np
+    import workloads as wl
+    name = "agg_f32_6cam_4scale_a900p13_g8c32"
+    c = wl.make(name)
+    dev = lambda t: t.to("cuda").contiguous()
+    feat, loc, wts = dev(c["feat"]), dev(c["loc"]), dev(c["weights"])
+    go = dev(wl.agg_grad_out(c, seed=1))
+    gf, gl, gw = torch.empty_like(feat), torch.empty_like(loc), torch.empty_like(wts)
+    ss = np.ascontiguousarray(c["spatial_shape"], dtype=np.int32)
+    st = np.ascontiguousarray(c["scale_start"], dtype=np.int32)
+    lib = dsa.load()
+    wsb = lib.deform_agg_backward_workspace_bytes(c["B"], c["P_total"], c["A"], c["pts"],
+                                                  c["cams"], c["scales"], c["G"], c["Cg"], 0)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    args = (feat.data_ptr(), ss.ctypes.data, st.ctypes.data, loc.data_ptr(), wts.data_ptr(),
+            go.data_ptr(), gf.data_ptr(), gl.data_ptr(), gw.data_ptr(), ws.data_ptr(), wsb,
+            c["B"], c["P_total"], c["A"], c["pts"], c["cams"], c["scales"], c["G"], c["Cg"], 1, 0,
+            stream)
+
+    def call():
+        s = lib.deform_agg_backward(*args)
+        if s:
+            raise RuntimeError("deform_agg_backward status %d" % s)
+    wall, kern = timer.run(call, iters, warmup)
+    taps = c["B"] * c["A"] * c["pts"] * c["cams"] * c["scales"] * c["G"]
+    # read feat, loc, weights, grad_out; write grad_feat, grad_loc, grad_weights
+    nbytes = 2 * feat.numel() * 4 + 2 * loc.numel() * 4 + 2 * wts.numel() * 4 + go.numel() * 4
+    return dict(workload=name + "_softmax backward", taps=taps, algo_bytes=nbytes, wall_s=wall,
+                kernel_s=kern, taps_per_s=taps / kern, gbs=nbytes / kern / 1e9,
+                frac=nbytes / kern / 1e9 / HBM_PEAK_GBS)
+
+
 def cpu_baseline(case, target_s=10.0, max_reps=200):
     """The oracle (as it stands, fp64 C with OpenMP) timed on the headline workload.
 
@@ -284,7 +320,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["core", "all", "bwd"], default="all")
+    ap.add_argument("--only", choices=["core", "all", "bwd", "aggbwd"], default="all")
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -303,6 +339,10 @@ def main():
         return
     timer = Timer(torch)
 
+    if args.only == "aggbwd":  # the aggregation backward alone (for profiling)
+        r = bench_agg_bwd(dsa, torch, timer, args.steps, args.warmup)
+        log("aggregation backward: %.2f us/call" % (r["kernel_s"] * 1e6))
+        return
     if args.only == "bwd":  # the core backward alone (for profiling)
         r = bench_core_bwd(dsa, torch, timer, HEADLINE, args.steps, args.warmup)
         log("core backward: %.2f us/call" % (r["kernel_s"] * 1e6))
@@ -322,6 +362,7 @@ def main():
         log("dcnv2 done")
         extra.append(bench_agg(dsa, torch, timer, 100, 10, softmax=True))
         extra.append(bench_agg(dsa, torch, timer, 100, 10, softmax=False))
+        extra.append(bench_agg_bwd(dsa, torch, timer, 20, 3))
         log("aggregation done")
         for r in extra:
             r["kernel_us"] = round(r.pop("kernel_s") * 1e6, 2)

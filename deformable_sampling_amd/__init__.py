@@ -26,7 +26,8 @@ STATUS = {0: "DCN_OK", 1: "DCN_ERR_NULL", 2: "DCN_ERR_SHAPE", 3: "DCN_ERR_PARAM"
 # every symbol include/dcn.h declares
 EXPORTS = ("dcn_core_forward", "dcn_core_backward_workspace_bytes", "dcn_core_backward",
            "dcn_v2_workspace_bytes", "dcn_v2_forward", "dcn_v2_im2col",
-           "deform_agg_forward", "dcn_status_string", "dcn_last_hip_error")
+           "deform_agg_forward", "deform_agg_backward_workspace_bytes", "deform_agg_backward",
+           "dcn_status_string", "dcn_last_hip_error")
 
 
 class DcnError(RuntimeError):
@@ -68,6 +69,10 @@ def load(path: str | None = None):
     lib.dcn_v2_im2col.argtypes = [vp, vp, vp, vp, _c.c_size_t] + [i] * 15 + [i, vp]
     lib.deform_agg_forward.restype = i
     lib.deform_agg_forward.argtypes = [vp, vp, vp, vp, vp, vp] + [i] * 9 + [i, vp]
+    lib.deform_agg_backward_workspace_bytes.restype = _c.c_size_t
+    lib.deform_agg_backward_workspace_bytes.argtypes = [i] * 9
+    lib.deform_agg_backward.restype = i
+    lib.deform_agg_backward.argtypes = [vp] * 10 + [_c.c_size_t] + [i] * 9 + [i, vp]
     lib.dcn_status_string.restype = _c.c_char_p
     lib.dcn_status_string.argtypes = [i]
     lib.dcn_last_hip_error.restype = i
@@ -303,3 +308,46 @@ def deform_agg_forward(feat, spatial_shape, scale_start, loc, weights, out=None,
           _ptr(weights), _ptr(out), B, P_total, A, pts, cams, scales, G, GC // G,
           int(bool(softmax)), _DTYPE_ID[feat.dtype], _stream(stream))
     return out
+
+
+def deform_agg_backward_workspace_bytes(B, P_total, A, pts, cams, scales, G, Cg,
+                                        dtype=torch.float32):
+    return int(load().deform_agg_backward_workspace_bytes(B, P_total, A, pts, cams, scales, G,
+                                                          Cg, _DTYPE_ID[dtype]))
+
+
+def deform_agg_backward(feat, spatial_shape, scale_start, loc, weights, grad_out, *,
+                        softmax=False, need=("feat", "loc", "weights"), workspace=None,
+                        stream=None):
+    """Gradients of deform_agg_forward w.r.t. feat, loc and weights (the names in
+    `need`). Returns (grad_feat, grad_loc, grad_weights), None where not asked."""
+    _check(feat, "feat")
+    _check(loc, "loc", torch.float32)
+    _check(weights, "weights", torch.float32)
+    import numpy as np
+    _check(grad_out, "grad_out", feat.dtype)
+    ss = np.ascontiguousarray(np.asarray(
+        spatial_shape.cpu() if hasattr(spatial_shape, "cpu") else spatial_shape, dtype=np.int32))
+    st = np.ascontiguousarray(np.asarray(
+        scale_start.cpu() if hasattr(scale_start, "cpu") else scale_start, dtype=np.int32))
+    B, P_total, GC = feat.shape
+    _, A, pts, cams, _ = loc.shape
+    scales, G = weights.shape[4], weights.shape[5]
+    if GC % G or tuple(weights.shape[:4]) != (B, A, pts, cams) or ss.shape != (cams, scales, 2):
+        raise ValueError("inconsistent aggregation shapes")
+    if tuple(grad_out.shape) != (B, A, GC):
+        raise ValueError("grad_out must be [B, A, G*Cg]")
+    gf = torch.empty_like(feat) if "feat" in need else None
+    gl = torch.empty_like(loc) if "loc" in need else None
+    gw = torch.empty_like(weights) if "weights" in need else None
+    wsb = deform_agg_backward_workspace_bytes(B, P_total, A, pts, cams, scales, G, GC // G,
+                                              feat.dtype)
+    if workspace is None and wsb:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=feat.device)
+    _call("deform_agg_backward", _ptr(feat), ss.ctypes.data, st.ctypes.data, _ptr(loc),
+          _ptr(weights), _ptr(grad_out), _ptr(gf), _ptr(gl), _ptr(gw), _ptr(workspace),
+          0 if workspace is None else workspace.numel() * workspace.element_size(),
+          B, P_total, A, pts, cams, scales, G, GC // G, int(bool(softmax)), _DTYPE_ID[feat.dtype],
+          _stream(stream))
+    return gf, gl, gw
+

@@ -263,4 +263,63 @@ dcn_status deform_agg_forward(const void *feat, const int32_t *spatial_shape,
     return hip_status(dcn::launch_deform_agg(a, stream));
 }
 
+size_t deform_agg_backward_workspace_bytes(int B, int P_total, int A, int pts, int cams,
+                                           int scales, int G, int Cg, dcn_dtype dtype) {
+    if (!valid_dtype(dtype) || B < 0 || A < 0 || P_total <= 0 || pts <= 0 || cams <= 0 ||
+        scales <= 0 || G <= 0 || Cg <= 0)
+        return 0;
+    dcn::AggBwdPlan plan;
+    dcn::plan_agg_bwd(B, P_total, A, pts, cams, G, Cg, dtype, plan);
+    return plan.total;
+}
+
+dcn_status deform_agg_backward(const void *feat, const int32_t *spatial_shape,
+                               const int32_t *scale_start, const float *loc, const float *weights,
+                               const void *grad_out, void *grad_feat, float *grad_loc,
+                               float *grad_weights, void *workspace, size_t workspace_bytes, int B,
+                               int P_total, int A, int pts, int cams, int scales, int G, int Cg,
+                               int softmax, dcn_dtype dtype, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return DCN_ERR_DTYPE;
+    if (B < 0 || A < 0 || P_total <= 0 || pts <= 0 || cams <= 0 || scales <= 0 || G <= 0 ||
+        Cg <= 0)
+        return DCN_ERR_SHAPE;
+    if ((long long)cams * scales > dcn::kAggMaxMaps) return DCN_ERR_SHAPE;
+    if (Cg > 512) return DCN_ERR_SHAPE;  // channel rounds of the backward kernel
+    if ((long long)B * P_total * G * Cg > kI32) return DCN_ERR_SHAPE;
+    if ((long long)B * A * G > kI32) return DCN_ERR_SHAPE;
+    if ((long long)pts * cams * scales * G > kI32) return DCN_ERR_SHAPE;
+    if ((long long)B * A * pts * cams * scales * G > kI32) return DCN_ERR_SHAPE;
+    if (!spatial_shape || !scale_start) return DCN_ERR_NULL;
+    dcn::AggBwdLaunch a;
+    for (int i = 0; i < cams * scales; ++i) {
+        const int h = spatial_shape[2 * i], w = spatial_shape[2 * i + 1], s0 = scale_start[i];
+        if (h <= 0 || w <= 0 || s0 < 0) return DCN_ERR_SHAPE;
+        if ((long long)s0 + (long long)h * w > P_total) return DCN_ERR_SHAPE;
+        a.maps.H[i] = h;
+        a.maps.W[i] = w;
+        a.maps.start[i] = s0;
+    }
+    if (B == 0) return DCN_OK;
+    if (A == 0 && !grad_feat) return DCN_OK;  // with A == 0 grad_feat is all zeros
+    if (!feat || (A > 0 && (!loc || !weights || !grad_out))) return DCN_ERR_NULL;
+    const size_t es = dtype_size(dtype);
+    if (!aligned(feat, es) || !aligned(grad_out, es) || !aligned(grad_feat, es) ||
+        !aligned(loc, 8) || !aligned(weights, 4) || !aligned(grad_loc, 4) ||
+        !aligned(grad_weights, 4))
+        return DCN_ERR_ALIGN;
+    dcn::AggBwdPlan plan;
+    dcn::plan_agg_bwd(B, P_total, A, pts, cams, G, Cg, dtype, plan);
+    const bool needs_ws = (grad_loc || (grad_feat && dtype != DCN_F32)) && plan.total > 0;
+    if (needs_ws && (!workspace || !aligned(workspace, 256) || workspace_bytes < plan.total))
+        return DCN_ERR_WORKSPACE;
+    if (!grad_feat && !grad_loc && !grad_weights) return DCN_OK;
+    a.feat = feat; a.loc = loc; a.weights = weights; a.grad_out = grad_out;
+    a.grad_feat = grad_feat; a.grad_loc = grad_loc; a.grad_weights = grad_weights;
+    a.workspace = workspace;
+    a.B = B; a.P_total = P_total; a.A = A; a.pts = pts; a.cams = cams; a.scales = scales;
+    a.G = G; a.Cg = Cg; a.softmax = softmax;
+    a.dtype = dtype;
+    return hip_status(dcn::launch_deform_agg_bwd(a, plan, stream));
+}
+
 }  // extern "C"

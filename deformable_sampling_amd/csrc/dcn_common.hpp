@@ -69,6 +69,13 @@ __device__ __forceinline__ void store_f32(typename E::bits *p, const float (&f)[
 
 // ---------------------------------------------------------------- bilinear --
 
+// a * b rounded to fp32 by itself. hipcc contracts a*b +- c into one FMA by default
+// and __fmul_rn is a plain multiply here, so a position such as fl32(u*W) - 0.5 or
+// fl32(s*d) - floor(...) could otherwise be formed with a single rounding. An
+// explicit fma with a zero addend is the correctly rounded product (a*b + 0 rounded
+// once), and an fma is never fused into a following add.
+__device__ __forceinline__ float mul_rn(float a, float b) { return __builtin_fmaf(a, b, 0.0f); }
+
 // Split a sampling coordinate base + t (base integer, t fp32) into the integer
 // corner c0 = base + floor(t) and the fraction f = t - floor(t). The fraction is
 // exact in fp32 except for t in (-1/2, 0), where f = 1 + t is rounded (by at most

@@ -147,8 +147,8 @@ __global__ __launch_bounds__(kThreads) void dcn_core_kernel(const typename E::bi
             const float2 d = *reinterpret_cast<const float2 *>(so + 2 * k);
             int y0, x0;
             float fy, fx;
-            split_coord(by0 + i * p.dh, __fmul_rn(p.offset_scale, d.y), y0, fy);
-            split_coord(bx0 + j * p.dw, __fmul_rn(p.offset_scale, d.x), x0, fx);
+            split_coord(by0 + i * p.dh, mul_rn(p.offset_scale, d.y), y0, fy);
+            split_coord(bx0 + j * p.dw, mul_rn(p.offset_scale, d.x), x0, fx);
             const Tap t = make_tap(y0, x0, fy, fx, sm[k], p.H, p.W, GC);
             accumulate_tap<E, V>(imgc, t, acc);
         };

@@ -119,8 +119,8 @@ struct TapGeo {
 
 __device__ __forceinline__ TapGeo tap_geo(int by, int bx, float2 d, float s, int H, int W) {
     TapGeo t;
-    split_coord_fu(by, __fmul_rn(s, d.y), t.y0, t.fy, t.uy);
-    split_coord_fu(bx, __fmul_rn(s, d.x), t.x0, t.fx, t.ux);
+    split_coord_fu(by, mul_rn(s, d.y), t.y0, t.fy, t.uy);
+    split_coord_fu(bx, mul_rn(s, d.x), t.x0, t.fx, t.ux);
     t.vy0 = (unsigned)t.y0 < (unsigned)H;
     t.vy1 = (unsigned)(t.y0 + 1) < (unsigned)H;
     t.vx0 = (unsigned)t.x0 < (unsigned)W;
@@ -237,8 +237,8 @@ __global__ __launch_bounds__(kThreads) void bwd_count_kernel(const float *__rest
             const float2 d = od[(((size_t)n * p.Ho * p.Wo + (size_t)ho * p.Wo + wo) * p.G + g) * K + k];
             int y0, x0;
             float f, u;
-            split_coord_fu(ho * p.sh - p.ph + i * p.dh, __fmul_rn(p.offset_scale, d.y), y0, f, u);
-            split_coord_fu(wo * p.sw - p.pw + j * p.dw, __fmul_rn(p.offset_scale, d.x), x0, f, u);
+            split_coord_fu(ho * p.sh - p.ph + i * p.dh, mul_rn(p.offset_scale, d.y), y0, f, u);
+            split_coord_fu(wo * p.sw - p.pw + j * p.dw, mul_rn(p.offset_scale, d.x), x0, f, u);
             want = home_bin(y0, x0, n, g, p, bin, local);
         }
         if (want && block_bin_slot(s_key, s_cnt, bin, rank) == kHash)
@@ -482,8 +482,8 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(
                     const float2 d = reinterpret_cast<const float2 *>(s_off)[idx];
                     int y0, x0;
                     float f, u;
-                    split_coord_fu(ho2 * p.sh - p.ph + i * p.dh, __fmul_rn(p.offset_scale, d.y), y0, f, u);
-                    split_coord_fu(wo2 * p.sw - p.pw + j * p.dw, __fmul_rn(p.offset_scale, d.x), x0, f, u);
+                    split_coord_fu(ho2 * p.sh - p.ph + i * p.dh, mul_rn(p.offset_scale, d.y), y0, f, u);
+                    split_coord_fu(wo2 * p.sw - p.pw + j * p.dw, mul_rn(p.offset_scale, d.x), x0, f, u);
                     unsigned bin, local, rank = 0;
                     if (home_bin(y0, x0, nn, gg, p, bin, local)) {
                         const int slot = block_bin_slot(s_key, s_cnt, bin, rank);
@@ -493,8 +493,8 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(
                             const unsigned at = starts[bin] + atomicAdd(&fill[bin], 1u);
                             if (at < starts[bin + 1])
                                 rec[at] = make_uint4(((unsigned)pp << 8) | local,
-                                                     __float_as_uint(__fmul_rn(p.offset_scale, d.y)),
-                                                     __float_as_uint(__fmul_rn(p.offset_scale, d.x)),
+                                                     __float_as_uint(mul_rn(p.offset_scale, d.y)),
+                                                     __float_as_uint(mul_rn(p.offset_scale, d.x)),
                                                      __float_as_uint(s_m[idx]));
                         }
                     }
@@ -518,8 +518,8 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(
                 const unsigned at = s_base[slot] + (code & 0xffffu);
                 if (at < s_lim[slot])
                     rec[at] = make_uint4(((unsigned)s_phw[idx / K] << 8) | ((code >> 16) & 0xffu),
-                                         __float_as_uint(__fmul_rn(p.offset_scale, d.y)),
-                                         __float_as_uint(__fmul_rn(p.offset_scale, d.x)),
+                                         __float_as_uint(mul_rn(p.offset_scale, d.y)),
+                                         __float_as_uint(mul_rn(p.offset_scale, d.x)),
                                          __float_as_uint(s_m[idx]));
             }
         }

@@ -101,7 +101,7 @@ template <int K>
 __device__ __forceinline__ void scale_offsets(float (&d)[2 * K], float scale) {
     if (scale != 1.0f) {
 #pragma unroll
-        for (int i = 0; i < 2 * K; ++i) d[i] = __fmul_rn(scale, d[i]);
+        for (int i = 0; i < 2 * K; ++i) d[i] = mul_rn(scale, d[i]);
     }
 }
 
@@ -267,8 +267,8 @@ __device__ __forceinline__ void taps_and_store(const uint4 *buf, const typename 
             const float2 dv = reinterpret_cast<const float2 *>(coff)[k];
             float dx = dv.x, dy = dv.y;
             if (p.offset_scale != 1.0f) {
-                dx = __fmul_rn(p.offset_scale, dx);
-                dy = __fmul_rn(p.offset_scale, dy);
+                dx = mul_rn(p.offset_scale, dx);
+                dy = mul_rn(p.offset_scale, dy);
             }
             float mk = m[0];
 #pragma unroll

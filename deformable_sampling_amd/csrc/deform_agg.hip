@@ -166,8 +166,8 @@ void deform_agg_kernel(const typename E::bits *__restrict__ feat,
                 }
                 const int Hs = s_h[cs], Ws = s_w[cs];
                 // one fp32 rounding of u*W, then the half-pixel shift
-                const float xf = __fsub_rn(__fmul_rn(uv.x, (float)Ws), 0.5f);
-                const float yf = __fsub_rn(__fmul_rn(uv.y, (float)Hs), 0.5f);
+                const float xf = __fsub_rn(mul_rn(uv.x, (float)Ws), 0.5f);
+                const float yf = __fsub_rn(mul_rn(uv.y, (float)Hs), 0.5f);
                 int x0, y0;
                 float fx, fy;
                 split_coord(0, xf, x0, fx);
@@ -351,8 +351,8 @@ void deform_agg_pipe_kernel(const typename E::bits *__restrict__ feat,
             const int cs = cam * p.scales + rem / p.pts;
             const int Hs = s_h[cs], Ws = s_w[cs];
             // one fp32 rounding of u*W, then the half-pixel shift
-            const float xf = __fsub_rn(__fmul_rn(uv.x, (float)Ws), 0.5f);
-            const float yf = __fsub_rn(__fmul_rn(uv.y, (float)Hs), 0.5f);
+            const float xf = __fsub_rn(mul_rn(uv.x, (float)Ws), 0.5f);
+            const float yf = __fsub_rn(mul_rn(uv.y, (float)Hs), 0.5f);
             int x0, y0;
             float fx, fy;
             split_coord(0, xf, x0, fx);

@@ -1,0 +1,352 @@
+// Backward of the multi-camera, multi-scale deformable aggregation, for gfx950.
+//
+// The Sparse4D deformable_aggregation page ("Sparse4D deformable_aggregation",
+// mlqm.cn, section 2.1) names gradients of the features, the sampling locations and
+// the weights; these are the derivatives of the forward sum (sections 2.1-2.2 and 7;
+// bilinear kernel from "Hands-on DCNv1 in PyTorch", agent.csdn.net, section 2). With
+// G the (anchor, group)'s grad_out, wt the (softmax-normalised) weight of sample
+// t = (point, camera, scale) at x = fl32(u*W_s) - 0.5, y = fl32(v*H_s) - 0.5, and
+// D_ab = sum_c G_c X_ab,c the dot products of G with the four corners:
+//   grad_feat[corner ab] += wt * w_ab * G                       (inside the map)
+//   g_t    = sum_ab w_ab D_ab        grad_weight_t = g_t, or wt (g_t - sum_j wj g_j)
+//   grad_u += wt * W_s * ((1-fy)(D_01 - D_00) + fy (D_11 - D_10))  over scales, groups
+//   grad_v += wt * H_s * ((1-fx)(D_10 - D_00) + fx (D_11 - D_01))
+// (derivatives from the right at integer positions; d fl32(u*W)/du taken as W).
+//
+// Mapping: one wavefront per (anchor, group) unit, units group-major (as the
+// forward). A round takes 64/scales (point, camera) pairs: each lane first turns one
+// sample into an LDS record (clamped corner offsets, validity, fractions and their
+// exact complements, wt); then slices of S lanes (one channel per lane, S >= Cg a
+// power of two) walk the records: four corner loads, the partial dots D_ab, and the
+// feature gradient as fp32 atomic adds of wt * w_ab * G_c (one slice's adds cover a
+// contiguous run of channels); the dots are summed over the slice and the sample's
+// g_t, grad_u, grad_v go to LDS. The owner lane of each (point, camera) sums its
+// scales and stores that group's grad_loc partial; the lane that built a sample
+// stores its g_t (and, with softmax, rewrites it as wt (g_t - sum_j wj g_j) once
+// the sum is known). A second kernel adds the G partials of grad_loc in group order.
+// The features accumulate in fp32 (in grad_feat for fp32, else in the workspace,
+// rounded once at the end), so their rounding varies run to run within fp32
+// accumulation error; grad_loc and grad_weights are deterministic.
+#include "dcn_common.hpp"
+#include "internal.hpp"
+
+namespace dcn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxRounds = 8;  // channel rounds of 64 lanes: Cg <= 512
+
+struct AggBwdParams {
+    int B, P_total, A, pts, cams, scales, G, Cg, softmax;
+    int S, Z, crounds;  // slice width, slices per wave, channel rounds (Cg > 64)
+    int npc;            // (point, camera) pairs per round
+    int BA, nunits, nblocks;
+    int want_feat, want_loc, want_w;
+    AggMaps maps;
+};
+
+struct alignas(16) AggRec {
+    int o00, o01, o10, o11;  // element offsets of the corners (clamped into the map)
+    float fy, fx, uy, ux;
+    float wt, Ws, Hs;
+    int valid;               // bit per corner: 1 = 00, 2 = 01, 4 = 10, 8 = 11
+};
+
+__device__ __forceinline__ float wsum(float v) {
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wmax(float v) {
+    for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// base + t -> corner, fraction f and its complement u = (floor(t) + 1) - t; each
+// of f and u is exact when below 1/2, so both weight factors have full relative
+// precision.
+__device__ __forceinline__ void split_fu(float t, int &c0, float &f, float &u) {
+    t = fminf(fmaxf(t, -16777216.0f), 16777216.0f);
+    const float fl = floorf(t);
+    f = t - fl;
+    u = (fl + 1.0f) - t;
+    c0 = (int)fl;
+}
+
+template <class E>
+__global__ __launch_bounds__(kThreads) void agg_bwd_kernel(
+    const typename E::bits *__restrict__ feat, const float *__restrict__ loc,
+    const float *__restrict__ weights, const typename E::bits *__restrict__ gout,
+    float *__restrict__ gacc, float *__restrict__ gloc_part, float *__restrict__ gw,
+    const AggBwdParams p) {
+    __shared__ int s_h[kAggMaxMaps], s_w[kAggMaxMaps], s_start[kAggMaxMaps];
+    __shared__ AggRec s_rec[kWaves][64];
+    __shared__ float s_res[kWaves][64][3];  // g_t, grad_u, grad_v per record
+
+    const int nmaps = p.cams * p.scales;
+    for (int i = threadIdx.x; i < nmaps; i += kThreads) {
+        s_h[i] = p.maps.H[i];
+        s_w[i] = p.maps.W[i];
+        s_start[i] = p.maps.start[i];
+    }
+    __syncthreads();
+
+    const int blk = xcd_remap((int)blockIdx.x, p.nblocks);
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int unit = blk * kWaves + wv;
+    if (unit >= p.nunits) return;  // whole wavefronts leave together; no barrier follows
+    const int lane = threadIdx.x & 63;
+    const int z = lane / p.S, s = lane - z * p.S;
+    const int g = unit / p.BA, ba = unit - g * p.BA;  // group-major
+    const int b = ba / p.A;
+    const int T = p.pts * p.cams * p.scales;
+    const int NPC = p.pts * p.cams;
+    const int GC = p.G * p.Cg;
+    const float *wrow = weights + (size_t)ba * T * p.G + g;  // sample t at wrow[t*G]
+    const float *lrow = loc + (size_t)ba * NPC * 2;
+    const typename E::bits *fb = feat + (size_t)b * p.P_total * GC + g * p.Cg;
+    float *ab = gacc ? gacc + (size_t)b * p.P_total * GC + g * p.Cg : nullptr;
+    AggRec *rec = s_rec[wv];
+    float(*res)[3] = s_res[wv];
+
+    // softmax over the unit's T logits
+    float mx = 0.0f, inv = 1.0f;
+    if (p.softmax) {
+        float m = -INFINITY;
+        for (int t = lane; t < T; t += 64) m = fmaxf(m, wrow[(size_t)t * p.G]);
+        mx = wmax(m);
+        float e = 0.0f;
+        for (int t = lane; t < T; t += 64) e += expf(wrow[(size_t)t * p.G] - mx);
+        inv = 1.0f / wsum(e);
+    }
+    // this lane's channels of G
+    float gc[kMaxRounds];
+#pragma unroll
+    for (int r = 0; r < kMaxRounds; ++r) {
+        const int c = r * p.S + s;
+        gc[r] = (r < p.crounds && c < p.Cg)
+                    ? to_f32(E{}, gout[(size_t)ba * GC + g * p.Cg + c])
+                    : 0.0f;
+    }
+
+    const int per_round = p.npc * p.scales;  // records per round (<= 64)
+    float dot = 0.0f;                        // sum_t wt g_t over this lane's samples
+    for (int pc0 = 0; pc0 < NPC; pc0 += p.npc) {
+        // ---- records: lane l < per_round describes sample (pc0 + l / scales, l % scales)
+        const int lpc = lane / p.scales, lsc = lane - lpc * p.scales;
+        const int pc = pc0 + lpc;
+        const bool own = lane < per_round && pc < NPC;
+        int t_nat = 0;
+        float wt = 0.0f;
+        if (own) {
+            const int cam = pc % p.cams;
+            const int cs = cam * p.scales + lsc;
+            t_nat = pc * p.scales + lsc;  // (point, camera, scale) natural order
+            const float l = wrow[(size_t)t_nat * p.G];
+            wt = p.softmax ? expf(l - mx) * inv : l;
+            const float2 uv = *reinterpret_cast<const float2 *>(lrow + 2 * pc);
+            const int Hs = s_h[cs], Ws = s_w[cs];
+            const float xf = __fsub_rn(mul_rn(uv.x, (float)Ws), 0.5f);
+            const float yf = __fsub_rn(mul_rn(uv.y, (float)Hs), 0.5f);
+            int x0, y0;
+            AggRec r;
+            split_fu(yf, y0, r.fy, r.uy);
+            split_fu(xf, x0, r.fx, r.ux);
+            const bool vy0 = (unsigned)y0 < (unsigned)Hs, vy1 = (unsigned)(y0 + 1) < (unsigned)Hs;
+            const bool vx0 = (unsigned)x0 < (unsigned)Ws, vx1 = (unsigned)(x0 + 1) < (unsigned)Ws;
+            const int yc0 = min(max(y0, 0), Hs - 1), yc1 = min(max(y0 + 1, 0), Hs - 1);
+            const int xc0 = min(max(x0, 0), Ws - 1), xc1 = min(max(x0 + 1, 0), Ws - 1);
+            const int base = s_start[cs];
+            r.o00 = (base + yc0 * Ws + xc0) * GC;
+            r.o01 = (base + yc0 * Ws + xc1) * GC;
+            r.o10 = (base + yc1 * Ws + xc0) * GC;
+            r.o11 = (base + yc1 * Ws + xc1) * GC;
+            r.valid = (vy0 && vx0 ? 1 : 0) | (vy0 && vx1 ? 2 : 0) | (vy1 && vx0 ? 4 : 0) |
+                      (vy1 && vx1 ? 8 : 0);
+            r.wt = wt;
+            r.Ws = (float)Ws;
+            r.Hs = (float)Hs;
+            rec[lane] = r;
+        }
+        const int nrec = min(per_round, (NPC - pc0) * p.scales);
+        // ---- gathers: slice z takes records z, z + Z, ... (one channel per lane)
+        for (int j0 = 0; j0 < nrec; j0 += p.Z) {
+            const int j = j0 + z;
+            const bool on = z < p.Z && j < nrec;
+            const AggRec r = rec[on ? j : 0];
+            float D00 = 0.0f, D01 = 0.0f, D10 = 0.0f, D11 = 0.0f;
+            if (on) {
+                const float w00 = ((r.valid & 1) ? r.uy * r.ux : 0.0f) * r.wt;
+                const float w01 = ((r.valid & 2) ? r.uy * r.fx : 0.0f) * r.wt;
+                const float w10 = ((r.valid & 4) ? r.fy * r.ux : 0.0f) * r.wt;
+                const float w11 = ((r.valid & 8) ? r.fy * r.fx : 0.0f) * r.wt;
+#pragma unroll
+                for (int cr = 0; cr < kMaxRounds; ++cr) {
+                    if (cr >= p.crounds) break;
+                    const int c = cr * p.S + s;
+                    if (c < p.Cg) {
+                        const float G = gc[cr];
+                        D00 = fmaf(G, to_f32(E{}, fb[r.o00 + c]), D00);
+                        D01 = fmaf(G, to_f32(E{}, fb[r.o01 + c]), D01);
+                        D10 = fmaf(G, to_f32(E{}, fb[r.o10 + c]), D10);
+                        D11 = fmaf(G, to_f32(E{}, fb[r.o11 + c]), D11);
+                        if (ab) {
+                            if (w00 != 0.0f) unsafeAtomicAdd(ab + r.o00 + c, w00 * G);
+                            if (w01 != 0.0f) unsafeAtomicAdd(ab + r.o01 + c, w01 * G);
+                            if (w10 != 0.0f) unsafeAtomicAdd(ab + r.o10 + c, w10 * G);
+                            if (w11 != 0.0f) unsafeAtomicAdd(ab + r.o11 + c, w11 * G);
+                        }
+                    }
+                }
+            }
+            D00 = seg_sum_pow2(D00, p.S);
+            D01 = seg_sum_pow2(D01, p.S);
+            D10 = seg_sum_pow2(D10, p.S);
+            D11 = seg_sum_pow2(D11, p.S);
+            if (on && s == 0) {
+                const float d00 = (r.valid & 1) ? D00 : 0.0f, d01 = (r.valid & 2) ? D01 : 0.0f;
+                const float d10 = (r.valid & 4) ? D10 : 0.0f, d11 = (r.valid & 8) ? D11 : 0.0f;
+                // weights applied outside the differences
+                res[j][0] = r.uy * (r.ux * d00 + r.fx * d01) + r.fy * (r.ux * d10 + r.fx * d11);
+                res[j][1] = r.wt * r.Ws * (r.uy * (d01 - d00) + r.fy * (d11 - d10));
+                res[j][2] = r.wt * r.Hs * (r.ux * (d10 - d00) + r.fx * (d11 - d01));
+            }
+        }
+        // ---- per-sample and per-(point, camera) results (a wavefront's own LDS
+        // writes are visible to its later reads: LDS keeps a wave's accesses in order)
+        if (own) {
+            const float gt = res[lane][0];
+            dot = fmaf(wt, gt, dot);
+            if (p.want_w) gw[((size_t)ba * T + t_nat) * p.G + g] = gt;
+        }
+        if (p.want_loc && lane < p.npc && pc0 + lane < NPC) {
+            float su = 0.0f, sv = 0.0f;
+            for (int k = 0; k < p.scales; ++k) {
+                su += res[lane * p.scales + k][1];
+                sv += res[lane * p.scales + k][2];
+            }
+            float *dst = gloc_part + (((size_t)g * p.BA + ba) * NPC + pc0 + lane) * 2;
+            dst[0] = su;
+            dst[1] = sv;
+        }
+    }
+    // ---- softmax: grad_logit_t = wt (g_t - sum_j wj g_j); each lane rewrites the
+    // samples it stored above (its own earlier writes)
+    if (p.softmax && p.want_w) {
+        const float tot = wsum(dot);
+        for (int pc0 = 0; pc0 < NPC; pc0 += p.npc) {
+            const int lpc = lane / p.scales, lsc = lane - lpc * p.scales;
+            const int pc = pc0 + lpc;
+            if (lane < per_round && pc < NPC) {
+                const int t_nat = pc * p.scales + lsc;
+                const float wt = expf(wrow[(size_t)t_nat * p.G] - mx) * inv;
+                float *q = gw + ((size_t)ba * T + t_nat) * p.G + g;
+                *q = wt * (*q - tot);
+            }
+        }
+    }
+}
+
+// grad_loc = sum over groups (in group order) of the per-group partials.
+__global__ __launch_bounds__(256) void agg_loc_reduce_kernel(const float *__restrict__ part,
+                                                             float *__restrict__ gloc, long long n,
+                                                             int G) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float s = 0.0f;
+    for (int g = 0; g < G; ++g) s += part[(size_t)g * n + i];
+    gloc[i] = s;
+}
+
+__global__ __launch_bounds__(256) void agg_zero_kernel(float *__restrict__ dst, long long n) {
+    const long long stride = (long long)gridDim.x * 256;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) dst[i] = 0.0f;
+}
+
+template <class E>
+__global__ __launch_bounds__(256) void agg_round_kernel(const float *__restrict__ src,
+                                                        typename E::bits *__restrict__ dst,
+                                                        long long n) {
+    const long long stride = (long long)gridDim.x * 256;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+        dst[i] = from_f32(E{}, src[i]);
+}
+
+int grid_for(long long n) {
+    const long long b = (n + 255) / 256;
+    return (int)(b < 1 ? 1 : (b > 16384 ? 16384 : b));
+}
+
+template <class E>
+hipError_t launch_e(const AggBwdLaunch &a, const AggBwdPlan &pl, hipStream_t stream) {
+    AggBwdParams p;
+    p.B = a.B; p.P_total = a.P_total; p.A = a.A; p.pts = a.pts; p.cams = a.cams;
+    p.scales = a.scales; p.G = a.G; p.Cg = a.Cg; p.softmax = a.softmax ? 1 : 0;
+    p.maps = a.maps;
+    int S = 1;
+    while (S < a.Cg && S < 64) S <<= 1;
+    p.S = S;
+    p.Z = 64 / S;
+    p.crounds = (a.Cg + S - 1) / S;
+    p.npc = 64 / a.scales;
+    p.BA = a.B * a.A;
+    p.nunits = p.BA * a.G;
+    p.nblocks = (p.nunits + kWaves - 1) / kWaves;
+    p.want_feat = a.grad_feat != nullptr;
+    p.want_loc = a.grad_loc != nullptr;
+    p.want_w = a.grad_weights != nullptr;
+
+    char *ws = static_cast<char *>(a.workspace);
+    float *part = a.grad_loc ? reinterpret_cast<float *>(ws + pl.off_loc) : nullptr;
+    const long long nfeat = (long long)a.B * a.P_total * a.G * a.Cg;
+    float *gacc = nullptr;
+    if (a.grad_feat) {
+        gacc = (E::id == DCN_F32) ? static_cast<float *>(a.grad_feat)
+                                  : reinterpret_cast<float *>(ws + pl.off_acc);
+        hipLaunchKernelGGL(agg_zero_kernel, dim3(grid_for(nfeat / 4)), dim3(256), 0, stream, gacc, nfeat);
+    }
+    using B = typename E::bits;
+    if (p.nunits > 0)  // no anchors: only the (zero) feature gradient is written
+        hipLaunchKernelGGL((agg_bwd_kernel<E>), dim3(p.nblocks), dim3(kThreads), 0, stream,
+                           static_cast<const B *>(a.feat), a.loc, a.weights,
+                           static_cast<const B *>(a.grad_out), gacc, part, a.grad_weights, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (a.grad_loc && p.nunits > 0) {
+        const long long nl = (long long)p.BA * a.pts * a.cams * 2;
+        hipLaunchKernelGGL(agg_loc_reduce_kernel, dim3((unsigned)((nl + 255) / 256)), dim3(256), 0,
+                           stream, part, a.grad_loc, nl, a.G);
+    }
+    if constexpr (E::id != DCN_F32) {
+        if (a.grad_feat)
+            hipLaunchKernelGGL((agg_round_kernel<E>), dim3(grid_for(nfeat / 4)), dim3(256), 0,
+                               stream, gacc, static_cast<B *>(a.grad_feat), nfeat);
+    }
+    return hipGetLastError();
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+void plan_agg_bwd(int B, int P_total, int A, int pts, int cams, int G, int Cg, dcn_dtype dtype,
+                  AggBwdPlan &pl) {
+    pl = AggBwdPlan();
+    size_t off = 0;
+    pl.off_loc = off;
+    off = align256(off + (size_t)G * B * A * pts * cams * 2 * sizeof(float));
+    pl.off_acc = off;
+    if (dtype != DCN_F32) off = align256(off + (size_t)B * P_total * G * Cg * sizeof(float));
+    pl.total = off;
+}
+
+hipError_t launch_deform_agg_bwd(const AggBwdLaunch &a, const AggBwdPlan &plan, hipStream_t stream) {
+    switch (a.dtype) {
+        case DCN_F32: return launch_e<EF32>(a, plan, stream);
+        case DCN_F16: return launch_e<EF16>(a, plan, stream);
+        case DCN_BF16: return launch_e<EBF16>(a, plan, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dcn

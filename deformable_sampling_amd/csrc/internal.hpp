@@ -109,4 +109,27 @@ struct AggLaunch {
 };
 hipError_t launch_deform_agg(const AggLaunch &a, hipStream_t stream);
 
+// Aggregation backward (deform_agg_bwd.hip). grad_feat / grad_loc / grad_weights
+// may be NULL. Workspace: per-group grad_loc partials, then (fp16/bf16) an fp32
+// grad_feat accumulator.
+struct AggBwdLaunch {
+    const void *feat;
+    const float *loc;
+    const float *weights;
+    const void *grad_out;
+    void *grad_feat;
+    float *grad_loc;
+    float *grad_weights;
+    void *workspace;
+    int B, P_total, A, pts, cams, scales, G, Cg, softmax;
+    dcn_dtype dtype;
+    AggMaps maps;
+};
+struct AggBwdPlan {
+    size_t off_loc, off_acc, total;
+};
+void plan_agg_bwd(int B, int P_total, int A, int pts, int cams, int G, int Cg, dcn_dtype dtype,
+                  AggBwdPlan &plan);
+hipError_t launch_deform_agg_bwd(const AggBwdLaunch &a, const AggBwdPlan &plan, hipStream_t stream);
+
 }  // namespace dcn

@@ -1,7 +1,7 @@
 /*
  * dcn.h — C ABI of the MI355X (gfx950) deformable-sampling library, libdcn.so.
  *
- * Forward operations and the core's backward, each enqueued on a caller-supplied HIP stream:
+ * Forward operations and two backward passes, each enqueued on a caller-supplied HIP stream:
  *
  *   dcn_core_forward    DCNv3/v4 core (also DCNv1 when mask == NULL), channels-last.
  *   dcn_core_backward   gradients of the core w.r.t. x, offsets and modulation.
@@ -9,6 +9,7 @@
  *                       and an MFMA GEMM (fused, or in two stages through the workspace).
  *   dcn_v2_im2col       the deform-im2col stage alone: columns into the workspace.
  *   deform_agg_forward  Sparse4D-style multi-camera, multi-scale aggregation.
+ *   deform_agg_backward gradients of the aggregation w.r.t. features, locations, weights.
  *
  * What is computed (page title, section):
  *  - Deformable sum y(p0) = sum_n w(p_n) x(p0 + p_n + dp_n), fractional positions
@@ -219,6 +220,49 @@ dcn_status deform_agg_forward(const void *feat, const int32_t *spatial_shape,
 
 /* Human-readable name of a status code (static string). */
 const char *dcn_status_string(dcn_status s);
+
+/*
+ * Workspace bytes deform_agg_backward needs (0 if the sizes are invalid): per-group
+ * partial sums of grad_loc (G*B*A*pts*cams*2 floats), then, for fp16/bf16, an fp32
+ * accumulator of grad_feat (B*P_total*G*Cg floats); each region 256-byte aligned.
+ */
+size_t deform_agg_backward_workspace_bytes(int B, int P_total, int A, int pts, int cams,
+                                           int scales, int G, int Cg, dcn_dtype dtype);
+
+/*
+ * Backward of deform_agg_forward (same arguments): the gradients of its output
+ * w.r.t. the features, the sampling locations and the weights ("Sparse4D
+ * deformable_aggregation", section 2.1, names these three; the spatial shapes and
+ * scale starts have none). The pages give no formulas; these are the derivatives:
+ *
+ *   grad_out      [B, A, G*Cg]                 dtype
+ *   grad_feat     [B, P_total, G*Cg]           dtype, overwritten (rows outside every
+ *                                              map get 0), or NULL
+ *   grad_loc      [B, A, pts, cams, 2]         fp32, overwritten, or NULL
+ *   grad_weights  [B, A, pts, cams, scales, G] fp32 w.r.t. the weights argument (the
+ *                                              logits when softmax != 0), or NULL
+ *
+ * With wt the (normalised) weight of sample t at x = fl32(u*W_s) - 0.5,
+ * y = fl32(v*H_s) - 0.5, w_ab its bilinear weights and B_t, dB_t/dx, dB_t/dy the
+ * sample and its derivatives in the pixel position (from the right at integer
+ * positions): grad_feat[corner] += wt * w_ab * grad_out; grad_w_t = sum_c
+ * grad_out[c] B_t[c] (softmax: wt (grad_w_t - sum_j wj grad_w_j)); grad_u =
+ * sum over scales and groups of wt * W_s * sum_c grad_out[c] dB_t/dx[c], grad_v
+ * likewise with H_s and dB_t/dy. grad_feat sums in fp32 with atomic adds (its
+ * rounding varies run to run within fp32 accumulation error) and is rounded once
+ * to dtype; grad_loc and grad_weights are deterministic. workspace:
+ * deform_agg_backward_workspace_bytes bytes, 256-byte aligned, needed when
+ * grad_loc != NULL or (grad_feat != NULL and dtype != DCN_F32), else may be NULL;
+ * contents on entry are ignored. Limits as the forward, and Cg <= 512. With A == 0
+ * and grad_feat != NULL the call writes zeros to grad_feat (the one exception to
+ * "zero-sized work launches nothing").
+ */
+dcn_status deform_agg_backward(const void *feat, const int32_t *spatial_shape,
+                               const int32_t *scale_start, const float *loc, const float *weights,
+                               const void *grad_out, void *grad_feat, float *grad_loc,
+                               float *grad_weights, void *workspace, size_t workspace_bytes, int B,
+                               int P_total, int A, int pts, int cams, int scales, int G, int Cg,
+                               int softmax, dcn_dtype dtype, hipStream_t stream);
 
 /* hipError_t of this thread's last DCN_ERR_HIP (0 if none). */
 int dcn_last_hip_error(void);

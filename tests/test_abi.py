@@ -205,10 +205,40 @@ def test_agg_validation(lib):
     assert agg(lib, starts=[0, 0, 0, 801]) == SHAPE  # 801 + 200 rows > P_total
     assert agg(lib, shapes=[(10, 20), (0, 5), (10, 20), (10, 20)]) == SHAPE
     assert agg(lib, starts=[0, -1, 0, 0]) == SHAPE
-    assert agg(lib, starts=[0, 0, 0, 800]) != SHAPE or True  # exactly fits: passes the map check
+    assert agg(lib, starts=[0, 0, 0, 800], B=0) == OK  # exactly fits: passes the map check
     assert agg(lib, Anc=0) == OK
     assert agg(lib, B=0) == OK
     assert agg(lib, feat=None) == NULL
     assert agg(lib, w=None) == NULL
     assert agg(lib, loc=A + 4) == ALIGN              # (u, v) pairs need 8-byte alignment
     assert agg(lib, feat=A + 2, dtype=0) == ALIGN
+    assert lib.dcn_last_hip_error() == 0             # nothing above reached a launch
+
+
+def agg_bwd(lib, feat=A, ss=None, st=None, loc=A, w=A, go=A, gf=A, gl=A, gw=A, ws=A, wsb=1 << 40,
+            B=1, P=100, An=4, pts=2, cams=2, scales=2, G=2, Cg=8, softmax=0, dtype=0):
+    ss = (ctypes.c_int32 * 8)(5, 5, 2, 3, 5, 5, 2, 3) if ss is None else ss
+    st = (ctypes.c_int32 * 4)(0, 25, 31, 56) if st is None else st
+    return lib.deform_agg_backward(feat, ss, st, loc, w, go, gf, gl, gw, ws, wsb, B, P, An, pts,
+                                   cams, scales, G, Cg, softmax, dtype, None)
+
+
+def test_agg_backward_workspace_and_validation(lib):
+    n = lib.deform_agg_backward_workspace_bytes(1, 89760, 900, 13, 6, 4, 8, 32, 0)
+    assert n == (8 * 900 * 13 * 6 * 2 * 4 + 255) // 256 * 256      # fp32: loc partials only
+    n16 = lib.deform_agg_backward_workspace_bytes(1, 89760, 900, 13, 6, 4, 8, 32, 1)
+    assert n16 == n + 89760 * 256 * 4                                # + fp32 feature accumulator
+    assert lib.deform_agg_backward_workspace_bytes(1, 0, 9, 1, 1, 1, 1, 8, 0) == 0
+    assert agg_bwd(lib, dtype=5) == DTYPE
+    assert agg_bwd(lib, Cg=513) == SHAPE                              # channel rounds limit
+    assert agg_bwd(lib, cams=9, scales=8) == SHAPE                    # > 64 maps
+    assert agg_bwd(lib, st=(ctypes.c_int32 * 4)(0, 25, 31, 96)) == SHAPE  # map past P_total
+    assert agg_bwd(lib, B=0, feat=None, loc=None, w=None, go=None) == OK
+    assert agg_bwd(lib, go=None) == NULL
+    assert agg_bwd(lib, gl=A + 2) == ALIGN
+    assert agg_bwd(lib, loc=A + 4) == ALIGN                            # (u, v) pairs: 8-byte aligned
+    assert agg_bwd(lib, ws=None) == WORKSPACE                          # grad_loc needs partials
+    assert agg_bwd(lib, wsb=16) == WORKSPACE
+    assert agg_bwd(lib, gf=None, gl=None, gw=None, ws=None) == OK     # nothing asked for
+    assert lib.dcn_last_hip_error() == 0
+

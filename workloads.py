@@ -191,6 +191,13 @@ def agg_case(*, B, shapes, A, pts, G, Cg, dtype="f32", weights="logits", seed=0,
 # Named workloads: the five shapes the ops are exercised and measured on.
 SPARSE4D_SHAPES = [[(64, 176), (32, 88), (16, 44), (8, 22)]] * 6
 
+def agg_grad_out(c, seed=0):
+    """An upstream gradient for the aggregation output [B, A, G*Cg] in feat's dtype:
+    N(0,1) draws from their own seeded stream."""
+    r = rng(seed + 104729)
+    return _t(r.standard_normal((c["B"], c["A"], c["G"] * c["Cg"])), c["dtype"])
+
+
 WORKLOADS = {
     # DCNv4 block, fp32, one 32x32 map with 4 groups of 16 channels.
     "dcnv4_f32_n1_32x32_g4c16": dict(
