@@ -15,6 +15,7 @@ Functions (each follows the page/section cited in ``oracle.c``):
   dcn_v2_columns, dcn_v2 — DCNv2 deform-im2col and modulated deformable conv
   deform_agg   — multi-camera multi-scale deformable aggregation
   deform_agg_backward — gradients of deform_agg w.r.t. features, locations, weights
+  deform_roi_pool — deformable RoI pooling (per-bin offsets scaled by the RoI size)
 """
 from __future__ import annotations
 
@@ -83,6 +84,8 @@ def _load():
         lib.oracle_deform_agg_backward.restype = ctypes.c_int
         lib.oracle_deform_agg_backward.argtypes = [_dp, _i32p, _i32p, _dp, _dp, _dp] + [_dp] * 6 + [
             _i64] * 8 + [ctypes.c_int]
+        lib.oracle_deform_roi_pool.restype = ctypes.c_int
+        lib.oracle_deform_roi_pool.argtypes = [_dp] * 5 + [_i64] * 7 + [ctypes.c_double] * 2
         _lib = lib
     return _lib
 
@@ -289,4 +292,19 @@ def deform_agg_backward(feat, spatial_shape, scale_start, loc, weights, grad_out
         raise ValueError("oracle_deform_agg_backward rejected its arguments (%d)" % rc)
     return dict(grad_feat=gf, grad_loc=gl, grad_weights=gw, grad_feat_abs=gfa,
                 grad_loc_abs=gla, grad_weights_abs=gwa)
+
+
+def deform_roi_pool(x, rois, offset, *, k, S, spatial_scale=1.0, gamma=0.1):
+    """Deformable RoI pooling. x [N,H,W,C] channels-last, rois [R,5] (batch, x1, y1, x2,
+    y2), offset [R,k,k,2] (dx, dy) or None. Returns (out, absum), each [R,k,k,C]."""
+    x, rois, offset = _f64(x), _f64(rois), _f64(offset)
+    N, H, W, C = x.shape
+    R = rois.shape[0]
+    out = np.zeros((R, k, k, C))
+    ab = np.zeros((R, k, k, C))
+    rc = _load().oracle_deform_roi_pool(_ptr(x), _ptr(rois), _ptr(offset), _ptr(out), _ptr(ab),
+                                        N, H, W, C, R, k, S, float(spatial_scale), float(gamma))
+    if rc:
+        raise ValueError("oracle_deform_roi_pool rejected its arguments (%d)" % rc)
+    return out, ab
 

@@ -588,3 +588,60 @@ int oracle_deform_agg_backward(const double *feat, const int32_t *spatial_shape,
     free(part);
     return 0;
 }
+
+/* ---------------------------------------------------------------------- */
+/* Deformable RoI pooling ([P-DCNv1] section 3: per-bin offsets normalised  */
+/* as dp_ij = gamma * dp^_ij o (w, h), bilinear sampling, pooling).         */
+/* Readings where the page is silent: rois[r] = (batch, x1, y1, x2, y2) in  */
+/* input coordinates, multiplied by spatial_scale; w = (x2 - x1)*scale,     */
+/* h = (y2 - y1)*scale; bin (i, j) of a k x k grid averages S x S samples   */
+/* at (y1s + (i + (sy + 1/2)/S) h/k + gamma*dy_ij*h,                        */
+/*     x1s + (j + (sx + 1/2)/S) w/k + gamma*dx_ij*w)                        */
+/* in pixel-index coordinates (pixel q at integer q), each read through the */
+/* bilinear kernel with zero outside the image per corner; offsets are      */
+/* [R, k, k, 2] (dx, dy) pairs, x first. x is channels-last [N, H, W, C],   */
+/* out [R, k, k, C]. All arithmetic in fp64 (the GPU forms the same terms   */
+/* in fp32). offset may be NULL (plain RoIAlign-style average pooling).     */
+/* ---------------------------------------------------------------------- */
+int oracle_deform_roi_pool(const double *x, const double *rois, const double *offset,
+                           double *out, double *absum, int64_t N, int64_t H, int64_t W,
+                           int64_t C, int64_t R, int64_t k, int64_t S, double spatial_scale,
+                           double gamma)
+{
+    if (k <= 0 || S <= 0) return 1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < R; ++r) {
+        const double *ro = rois + r * 5;
+        int64_t n = (int64_t)ro[0];
+        if (n < 0 || n >= N) { bad = 1; continue; }
+        double x1 = ro[1] * spatial_scale, y1 = ro[2] * spatial_scale;
+        double w = (ro[3] - ro[1]) * spatial_scale, h = (ro[4] - ro[2]) * spatial_scale;
+        double bw = w / (double)k, bh = h / (double)k;
+        const double *X = x + n * H * W * C;
+        for (int64_t i = 0; i < k; ++i)
+        for (int64_t j = 0; j < k; ++j) {
+            double dx = 0.0, dy = 0.0;
+            if (offset) {
+                dx = gamma * offset[((r * k + i) * k + j) * 2 + 0] * w;
+                dy = gamma * offset[((r * k + i) * k + j) * 2 + 1] * h;
+            }
+            double *o = out + ((r * k + i) * k + j) * C;
+            double *oa = absum ? absum + ((r * k + i) * k + j) * C : NULL;
+            for (int64_t c = 0; c < C; ++c) {
+                double sum = 0.0, sa = 0.0;
+                for (int64_t sy = 0; sy < S; ++sy)
+                for (int64_t sx = 0; sx < S; ++sx) {
+                    double yy = y1 + ((double)i + ((double)sy + 0.5) / (double)S) * bh + dy;
+                    double xx = x1 + ((double)j + ((double)sx + 0.5) / (double)S) * bw + dx;
+                    double ab = 0.0;
+                    sum += oracle_bilinear(X + c, H, W, C, yy, xx, &ab);
+                    sa += ab;
+                }
+                o[c] = sum / (double)(S * S);
+                if (oa) oa[c] = sa / (double)(S * S);
+            }
+        }
+    }
+    return bad ? 2 : 0;
+}

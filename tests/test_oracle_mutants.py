@@ -87,6 +87,23 @@ AGG_BWD_MUTANTS = [
      "const double *Gv = gout + ba * GC;", 1),
 ]
 
+# Mistakes in deformable RoI pooling (oracle_deform_roi_pool), caught by its pins.
+ROI_MUTANTS = [
+    ("roi_swap_dx_dy", "dx = gamma * offset[((r * k + i) * k + j) * 2 + 0] * w;",
+     "dx = gamma * offset[((r * k + i) * k + j) * 2 + 1] * w;", 1),
+    ("roi_offset_scaled_by_h", "dx = gamma * offset[((r * k + i) * k + j) * 2 + 0] * w;",
+     "dx = gamma * offset[((r * k + i) * k + j) * 2 + 0] * h;", 1),
+    ("roi_no_gamma", "dy = gamma * offset[((r * k + i) * k + j) * 2 + 1] * h;",
+     "dy = offset[((r * k + i) * k + j) * 2 + 1] * h;", 1),
+    ("roi_no_half_sample", "((double)sx + 0.5) / (double)S) * bw + dx;", "((double)sx) / (double)S) * bw + dx;", 1),
+    ("roi_bins_transposed", "double bw = w / (double)k, bh = h / (double)k;",
+     "double bw = h / (double)k, bh = w / (double)k;", 1),
+    ("roi_mean_over_S", "o[c] = sum / (double)(S * S);", "o[c] = sum / (double)S;", 1),
+    ("roi_ignores_batch", "const double *X = x + n * H * W * C;", "const double *X = x;", 1),
+    ("roi_scale_x1_only", "double x1 = ro[1] * spatial_scale, y1 = ro[2] * spatial_scale;",
+     "double x1 = ro[1], y1 = ro[2] * spatial_scale;", 1),
+]
+
 
 def _replace_nth(text, old, new, n):
     idx = -1
@@ -120,6 +137,8 @@ def test_unmodified_oracle_passes_pins(tmp_path):
     assert res.returncode == 0, res.stdout[-3000:]
     res = _run_pins(lib, "test_oracle_agg_backward_pins.py")
     assert res.returncode == 0, res.stdout[-3000:]
+    res = _run_pins(lib, "test_oracle_roi_pins.py")
+    assert res.returncode == 0, res.stdout[-3000:]
 
 
 @pytest.mark.parametrize("name,old,new,nth", MUTANTS, ids=[m[0] for m in MUTANTS])
@@ -144,4 +163,12 @@ def test_agg_backward_pins_catch_mutant(tmp_path, name, old, new, nth):
     lib = _build(text, tmp_path, name)
     res = _run_pins(lib, "test_oracle_agg_backward_pins.py")
     assert res.returncode != 0, "mutant %s survived the aggregation backward pins" % name
+
+
+@pytest.mark.parametrize("name,old,new,nth", ROI_MUTANTS, ids=[m[0] for m in ROI_MUTANTS])
+def test_roi_pins_catch_mutant(tmp_path, name, old, new, nth):
+    text = _replace_nth(open(SRC).read(), old, new, nth)
+    lib = _build(text, tmp_path, name)
+    res = _run_pins(lib, "test_oracle_roi_pins.py")
+    assert res.returncode != 0, "mutant %s survived the RoI pooling pins" % name
 

@@ -1,0 +1,133 @@
+"""Pins of the oracle's deformable RoI pooling (CPU only).
+
+The DCNv1 page (section 3) gives per-bin offsets normalised by the RoI size,
+dp_ij = gamma * dp^_ij o (w, h), bilinear sampling and pooling; the sampling grid
+inside a bin and the coordinate convention are readings (see oracle.c). Checked
+against: an independent fp64 formulation on torch's grid_sample (align_corners=True
+in pixel-index coordinates, zero padding); the lattice definition of the bilinear
+kernel; exact reproduction of bilinear ramps (closed form at the mean sample
+position); integer offset shifts equal to shifted RoIs (the (w, h) scaling and the
+(dx, dy) order); batch index, spatial_scale and NULL offsets.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+f64 = torch.float64
+
+
+def _rois(r, R, N, H, W, scale=1.0):
+    x1 = r.uniform(-2, W * 0.7, R)
+    y1 = r.uniform(-2, H * 0.7, R)
+    x2 = x1 + r.uniform(0.5, W * 0.6, R)
+    y2 = y1 + r.uniform(0.5, H * 0.6, R)
+    b = r.integers(0, N, R)
+    return np.stack([b, x1 / scale, y1 / scale, x2 / scale, y2 / scale], 1)
+
+
+def _torch_roi(x, rois, off, k, S, scale, gamma):
+    """grid_sample formulation: all k*k*S*S sample positions of a RoI at once."""
+    N, H, W, C = x.shape
+    img = torch.tensor(x).permute(0, 3, 1, 2)
+    outs = []
+    for r in range(rois.shape[0]):
+        b, x1, y1, x2, y2 = rois[r]
+        x1, y1 = x1 * scale, y1 * scale
+        w, h = (x2 * scale - x1), (y2 * scale - y1)
+        ii = torch.arange(k, dtype=f64).view(k, 1, 1, 1)
+        jj = torch.arange(k, dtype=f64).view(1, k, 1, 1)
+        sy = ((torch.arange(S, dtype=f64) + 0.5) / S).view(1, 1, S, 1)
+        sx = ((torch.arange(S, dtype=f64) + 0.5) / S).view(1, 1, 1, S)
+        dx = torch.zeros(k, k, dtype=f64) if off is None else torch.tensor(off[r, :, :, 0])
+        dy = torch.zeros(k, k, dtype=f64) if off is None else torch.tensor(off[r, :, :, 1])
+        py = y1 + (ii + sy) * (h / k) + (gamma * dy * h).view(k, k, 1, 1)
+        px = x1 + (jj + sx) * (w / k) + (gamma * dx * w).view(k, k, 1, 1)
+        py, px = torch.broadcast_tensors(py, px)
+        grid = torch.stack([2 * px / (W - 1) - 1, 2 * py / (H - 1) - 1], -1).reshape(1, k * k, S * S, 2)
+        smp = F.grid_sample(img[int(b):int(b) + 1], grid, mode="bilinear", padding_mode="zeros",
+                            align_corners=True)  # [1, C, k*k, S*S]
+        outs.append(smp.mean(-1).reshape(C, k, k).permute(1, 2, 0))
+    return torch.stack(outs).numpy()
+
+
+@pytest.mark.parametrize("k,S,scale,gamma", [(3, 2, 1.0, 0.1), (7, 1, 0.5, 0.2), (2, 3, 0.25, 1.0)])
+def test_matches_grid_sample_formulation(k, S, scale, gamma):
+    r = np.random.default_rng(k * 10 + S)
+    N, H, W, C = 2, 13, 17, 3
+    x = r.standard_normal((N, H, W, C))
+    rois = _rois(r, 6, N, H, W, scale)
+    off = r.standard_normal((6, k, k, 2))
+    o, ab = oracle.deform_roi_pool(x, rois, off, k=k, S=S, spatial_scale=scale, gamma=gamma)
+    want = _torch_roi(x, rois, off, k, S, scale, gamma)
+    np.testing.assert_allclose(o, want, rtol=0, atol=1e-12)
+    assert np.all(ab >= np.abs(o) - 1e-12)
+    o0, _ = oracle.deform_roi_pool(x, rois, None, k=k, S=S, spatial_scale=scale, gamma=gamma)
+    np.testing.assert_allclose(o0, _torch_roi(x, rois, None, k, S, scale, gamma), rtol=0, atol=1e-12)
+
+
+def lattice(X, y, x):
+    H, W = X.shape
+    return sum(max(0.0, 1 - abs(qy - y)) * max(0.0, 1 - abs(qx - x)) * X[qy, qx]
+               for qy in range(H) for qx in range(W))
+
+
+def test_single_sample_is_lattice_bilinear():
+    r = np.random.default_rng(1)
+    X = r.standard_normal((7, 9))
+    for _ in range(20):
+        x1, y1 = r.uniform(-2, 9), r.uniform(-2, 7)
+        w, h = r.uniform(0, 3), r.uniform(0, 3)
+        rois = np.array([[0, x1, y1, x1 + w, y1 + h]])
+        o, _ = oracle.deform_roi_pool(X[None, :, :, None], rois, None, k=1, S=1)
+        assert abs(o[0, 0, 0, 0] - lattice(X, y1 + h / 2, x1 + w / 2)) < 1e-12
+
+
+def test_bilinear_ramp_reproduced_at_mean_position():
+    H, W = 20, 24
+    yy, xx = np.meshgrid(np.arange(H), np.arange(W), indexing="ij")
+    a, b, c, e = 0.3, -1.25, 0.75, 0.0625
+    X = (a + b * xx + c * yy + e * xx * yy)[None, :, :, None]
+    rois = np.array([[0, 3.25, 2.5, 14.0, 11.75], [0, 1.0, 1.0, 9.5, 13.0]])
+    k, S, gamma = 3, 2, 0.1
+    r = np.random.default_rng(2)
+    off = r.uniform(-1, 1, (2, k, k, 2))
+    o, _ = oracle.deform_roi_pool(X, rois, off, k=k, S=S, gamma=gamma)
+    for ri, (_, x1, y1, x2, y2) in enumerate(rois):
+        w, h = x2 - x1, y2 - y1
+        for i in range(k):
+            for j in range(k):
+                ym = y1 + (i + 0.5) * h / k + gamma * off[ri, i, j, 1] * h
+                xm = x1 + (j + 0.5) * w / k + gamma * off[ri, i, j, 0] * w
+                assert abs(o[ri, i, j, 0] - (a + b * xm + c * ym + e * xm * ym)) < 1e-10
+
+
+def test_integer_offset_shifts_equal_shifted_rois():
+    """gamma * dx * w = 2 and gamma * dy * h = -1 px move every sample of the bin by
+    (2, -1): the same as pooling a RoI moved by that much (where all bins move)."""
+    r = np.random.default_rng(3)
+    x = r.standard_normal((1, 16, 20, 4))
+    k, S, gamma = 2, 2, 0.5
+    roi = np.array([[0, 4.0, 6.0, 12.0, 10.0]])  # w = 8, h = 4
+    off = np.zeros((1, k, k, 2))
+    off[..., 0] = 2.0 / (gamma * 8.0)
+    off[..., 1] = -1.0 / (gamma * 4.0)
+    o, _ = oracle.deform_roi_pool(x, roi, off, k=k, S=S, gamma=gamma)
+    moved = roi + np.array([[0, 2.0, -1.0, 2.0, -1.0]])
+    o2, _ = oracle.deform_roi_pool(x, moved, None, k=k, S=S, gamma=gamma)
+    np.testing.assert_array_equal(o, o2)
+
+
+def test_batch_index_scale_and_constant_image():
+    r = np.random.default_rng(4)
+    x = r.standard_normal((3, 8, 8, 2))
+    roi = np.array([[2, 2.0, 2.0, 10.0, 10.0]])
+    o, _ = oracle.deform_roi_pool(x, roi, None, k=2, S=2, spatial_scale=0.5)
+    o2, _ = oracle.deform_roi_pool(x[2:3], np.array([[0, 1.0, 1.0, 5.0, 5.0]]), None, k=2, S=2)
+    np.testing.assert_array_equal(o, o2)
+    ones = np.ones((1, 10, 10, 1))
+    o, _ = oracle.deform_roi_pool(ones, np.array([[0, 2.0, 2.0, 7.0, 6.0]]),
+                                  r.uniform(-1, 1, (1, 3, 3, 2)), k=3, S=2, gamma=0.1)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-14)  # all samples inside: partition of unity
