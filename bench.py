@@ -10,7 +10,7 @@ Printed (one JSON line): bilinear taps/s (whole job), ms per step, the roofline
 object of the core kernel (algorithmic bytes per launch / HIP-event launch time vs
 8 TB/s), the CPU oracle's rate on a bounded sample, and side measurements of the
 other ops (DCNv4/DCNv3 small maps, the core backward, DCNv2 im2col + MFMA GEMM,
-aggregation forward and backward).
+aggregation forward and backward, deformable RoI pooling).
 
   python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--only core|bwd|aggbwd]
   python bench.py --calib-copy     # plain copy of known size, for counter scaling
@@ -261,6 +261,34 @@ def bench_agg_bwd(dsa, torch, timer, iters, warmup):
                 frac=nbytes / kern / 1e9 / HBM_PEAK_GBS)
 
 
+def bench_roi(dsa, torch, timer, iters, warmup):
+    """deform_roi_pool_forward on the 512-RoI, 7x7-bin workload."""
+    import workloads as wl
+    name = "droi_f32_n2_64x64_c256_r512_k7"
+    c = wl.make(name)
+    dev = lambda t: t.to("cuda").contiguous()
+    x, rois, off = dev(c["x"]), dev(c["rois"]), dev(c["offset"])
+    out = torch.empty((c["R"], c["k"], c["k"], c["C"]), dtype=x.dtype, device="cuda")
+    lib = dsa.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    dt = {"f32": 0, "f16": 1, "bf16": 2}[c["dtype"]]
+    args = (x.data_ptr(), rois.data_ptr(), off.data_ptr(), out.data_ptr(), c["N"], c["H"], c["W"],
+            c["C"], c["R"], c["k"], c["S"], ctypes.c_float(c["spatial_scale"]),
+            ctypes.c_float(c["gamma"]), dt, stream)
+
+    def call():
+        s = lib.deform_roi_pool_forward(*args)
+        if s:
+            raise RuntimeError("deform_roi_pool_forward status %d" % s)
+    wall, kern = timer.run(call, iters, warmup)
+    samples = c["R"] * c["k"] * c["k"] * c["S"] * c["S"]
+    # the feature map once, RoIs, offsets, output
+    nbytes = (x.numel() + out.numel()) * x.element_size() + rois.numel() * 4 + off.numel() * 4
+    return dict(workload=name, taps=samples, algo_bytes=nbytes, wall_s=wall, kernel_s=kern,
+                taps_per_s=samples / kern, gbs=nbytes / kern / 1e9,
+                frac=nbytes / kern / 1e9 / HBM_PEAK_GBS)
+
+
 def cpu_baseline(case, target_s=10.0, max_reps=200):
     """The oracle (as it stands, fp64 C with OpenMP) timed on the headline workload.
 
@@ -364,6 +392,8 @@ def main():
         extra.append(bench_agg(dsa, torch, timer, 100, 10, softmax=False))
         extra.append(bench_agg_bwd(dsa, torch, timer, 20, 3))
         log("aggregation done")
+        extra.append(bench_roi(dsa, torch, timer, 100, 10))
+        log("roi pooling done")
         for r in extra:
             r["kernel_us"] = round(r.pop("kernel_s") * 1e6, 2)
             r["wall_us"] = round(r.pop("wall_s") * 1e6, 2)

@@ -27,6 +27,7 @@ STATUS = {0: "DCN_OK", 1: "DCN_ERR_NULL", 2: "DCN_ERR_SHAPE", 3: "DCN_ERR_PARAM"
 EXPORTS = ("dcn_core_forward", "dcn_core_backward_workspace_bytes", "dcn_core_backward",
            "dcn_v2_workspace_bytes", "dcn_v2_forward", "dcn_v2_im2col",
            "deform_agg_forward", "deform_agg_backward_workspace_bytes", "deform_agg_backward",
+           "deform_roi_pool_forward",
            "dcn_status_string", "dcn_last_hip_error")
 
 
@@ -73,6 +74,8 @@ def load(path: str | None = None):
     lib.deform_agg_backward_workspace_bytes.argtypes = [i] * 9
     lib.deform_agg_backward.restype = i
     lib.deform_agg_backward.argtypes = [vp] * 10 + [_c.c_size_t] + [i] * 9 + [i, vp]
+    lib.deform_roi_pool_forward.restype = i
+    lib.deform_roi_pool_forward.argtypes = [vp] * 4 + [i] * 7 + [f, f, i, vp]
     lib.dcn_status_string.restype = _c.c_char_p
     lib.dcn_status_string.argtypes = [i]
     lib.dcn_last_hip_error.restype = i
@@ -350,4 +353,27 @@ def deform_agg_backward(feat, spatial_shape, scale_start, loc, weights, grad_out
           B, P_total, A, pts, cams, scales, G, GC // G, int(bool(softmax)), _DTYPE_ID[feat.dtype],
           _stream(stream))
     return gf, gl, gw
+
+
+def deform_roi_pool_forward(x, rois, offset, *, output_size, sampling_ratio=2, spatial_scale=1.0,
+                            gamma=0.1, out=None, stream=None):
+    """Deformable RoI pooling. x [N,H,W,C] channels-last; rois [R,5] fp32 (batch, x1, y1,
+    x2, y2); offset [R,k,k,2] fp32 (dx, dy) or None. Returns out [R,k,k,C]."""
+    k = int(output_size)
+    _check(x, "x")
+    _check(rois, "rois", torch.float32)
+    _check(offset, "offset", torch.float32, allow_none=True)
+    N, H, W, C = x.shape
+    R = rois.shape[0]
+    if rois.dim() != 2 or rois.shape[1] != 5:
+        raise ValueError("rois must be [R, 5]")
+    if offset is not None and tuple(offset.shape) != (R, k, k, 2):
+        raise ValueError("offset must be [R, k, k, 2]")
+    if out is None:
+        out = torch.empty((R, k, k, C), dtype=x.dtype, device=x.device)
+    _check(out, "out", x.dtype)
+    _call("deform_roi_pool_forward", _ptr(x), _ptr(rois), _ptr(offset), _ptr(out), N, H, W, C, R, k,
+          int(sampling_ratio), float(spatial_scale), float(gamma), _DTYPE_ID[x.dtype],
+          _stream(stream))
+    return out
 

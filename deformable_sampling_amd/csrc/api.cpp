@@ -322,4 +322,27 @@ dcn_status deform_agg_backward(const void *feat, const int32_t *spatial_shape,
     return hip_status(dcn::launch_deform_agg_bwd(a, plan, stream));
 }
 
+
+dcn_status deform_roi_pool_forward(const void *x, const float *rois, const float *offset, void *out,
+                                   int N, int H, int W, int C, int R, int k, int sampling_ratio,
+                                   float spatial_scale, float gamma, dcn_dtype dtype,
+                                   hipStream_t stream) {
+    if (!valid_dtype(dtype)) return DCN_ERR_DTYPE;
+    if (N <= 0 || H <= 0 || W <= 0 || C <= 0 || R < 0) return DCN_ERR_SHAPE;
+    if (k <= 0 || sampling_ratio <= 0 || sampling_ratio > 64) return DCN_ERR_PARAM;
+    if ((long long)(H + 1) * (W + 1) * C > kI32) return DCN_ERR_SHAPE;
+    if ((long long)R * k * k * C > kI32) return DCN_ERR_SHAPE;
+    if (R == 0) return DCN_OK;
+    if (!x || !rois || !out) return DCN_ERR_NULL;
+    const size_t es = dtype_size(dtype);
+    if (!aligned(x, es) || !aligned(out, es) || !aligned(rois, 4) || !aligned(offset, 8))
+        return DCN_ERR_ALIGN;
+    dcn::RoiLaunch a;
+    a.x = x; a.rois = rois; a.offset = offset; a.out = out;
+    a.N = N; a.H = H; a.W = W; a.C = C; a.R = R; a.k = k; a.S = sampling_ratio;
+    a.spatial_scale = spatial_scale; a.gamma = gamma;
+    a.dtype = dtype;
+    return hip_status(dcn::launch_deform_roi_pool(a, stream));
+}
+
 }  // extern "C"

@@ -132,4 +132,16 @@ void plan_agg_bwd(int B, int P_total, int A, int pts, int cams, int G, int Cg, d
                   AggBwdPlan &plan);
 hipError_t launch_deform_agg_bwd(const AggBwdLaunch &a, const AggBwdPlan &plan, hipStream_t stream);
 
+// Deformable RoI pooling (deform_roi_pool.hip).
+struct RoiLaunch {
+    const void *x;
+    const float *rois;
+    const float *offset;  // may be NULL
+    void *out;
+    int N, H, W, C, R, k, S;
+    float spatial_scale, gamma;
+    dcn_dtype dtype;
+};
+hipError_t launch_deform_roi_pool(const RoiLaunch &a, hipStream_t stream);
+
 }  // namespace dcn

@@ -10,6 +10,7 @@
  *   dcn_v2_im2col       the deform-im2col stage alone: columns into the workspace.
  *   deform_agg_forward  Sparse4D-style multi-camera, multi-scale aggregation.
  *   deform_agg_backward gradients of the aggregation w.r.t. features, locations, weights.
+ *   deform_roi_pool_forward  deformable RoI pooling, channels-last.
  *
  * What is computed (page title, section):
  *  - Deformable sum y(p0) = sum_n w(p_n) x(p0 + p_n + dp_n), fractional positions
@@ -263,6 +264,31 @@ dcn_status deform_agg_backward(const void *feat, const int32_t *spatial_shape,
                                float *grad_weights, void *workspace, size_t workspace_bytes, int B,
                                int P_total, int A, int pts, int cams, int scales, int G, int Cg,
                                int softmax, dcn_dtype dtype, hipStream_t stream);
+
+/*
+ * Deformable RoI pooling ("Hands-on DCNv1 in PyTorch", section 3: per-bin offsets
+ * normalised by the RoI size, dp_ij = gamma * dp^_ij o (w, h); bilinear sampling;
+ * pooling), channels-last:
+ *
+ *   x       [N, H, W, C]   dtype
+ *   rois    [R, 5]         fp32 (batch index, x1, y1, x2, y2) in input coordinates
+ *   offset  [R, k, k, 2]   fp32 normalised (dx, dy) per bin, x first, or NULL (none)
+ *   out     [R, k, k, C]   dtype
+ *
+ * With x1s = x1*spatial_scale, w = (x2 - x1)*spatial_scale (y likewise), bin (i, j)
+ * is the mean of S x S bilinear samples (S = sampling_ratio) at
+ *   y = y1s + (i + (sy + 1/2)/S) * h/k + gamma*dy_ij*h,
+ *   x = x1s + (j + (sx + 1/2)/S) * w/k + gamma*dx_ij*w,
+ * pixel q at integer coordinate q, zero outside the image per corner (the page names
+ * no sampling grid, coordinate convention or border rule; these are the readings).
+ * Positions are formed in fp32. A RoI whose batch index is not in [0, N) pools to
+ * zeros. Limits: 1 <= sampling_ratio <= 64; (H+1)*(W+1)*C < 2^31; R*k*k*C < 2^31.
+ * offset must be 8-byte aligned; x and out aligned to their element size.
+ */
+dcn_status deform_roi_pool_forward(const void *x, const float *rois, const float *offset, void *out,
+                                   int N, int H, int W, int C, int R, int k, int sampling_ratio,
+                                   float spatial_scale, float gamma, dcn_dtype dtype,
+                                   hipStream_t stream);
 
 /* hipError_t of this thread's last DCN_ERR_HIP (0 if none). */
 int dcn_last_hip_error(void);

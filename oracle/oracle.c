@@ -604,9 +604,9 @@ int oracle_deform_agg_backward(const double *feat, const int32_t *spatial_shape,
 /* in fp32). offset may be NULL (plain RoIAlign-style average pooling).     */
 /* ---------------------------------------------------------------------- */
 int oracle_deform_roi_pool(const double *x, const double *rois, const double *offset,
-                           double *out, double *absum, int64_t N, int64_t H, int64_t W,
-                           int64_t C, int64_t R, int64_t k, int64_t S, double spatial_scale,
-                           double gamma)
+                           double *out, double *absum, double *csum, int64_t N, int64_t H,
+                           int64_t W, int64_t C, int64_t R, int64_t k, int64_t S,
+                           double spatial_scale, double gamma)
 {
     if (k <= 0 || S <= 0) return 1;
     int bad = 0;
@@ -628,8 +628,9 @@ int oracle_deform_roi_pool(const double *x, const double *rois, const double *of
             }
             double *o = out + ((r * k + i) * k + j) * C;
             double *oa = absum ? absum + ((r * k + i) * k + j) * C : NULL;
+            double *oc = csum ? csum + ((r * k + i) * k + j) * C : NULL;
             for (int64_t c = 0; c < C; ++c) {
-                double sum = 0.0, sa = 0.0;
+                double sum = 0.0, sa = 0.0, sc = 0.0;
                 for (int64_t sy = 0; sy < S; ++sy)
                 for (int64_t sx = 0; sx < S; ++sx) {
                     double yy = y1 + ((double)i + ((double)sy + 0.5) / (double)S) * bh + dy;
@@ -637,9 +638,19 @@ int oracle_deform_roi_pool(const double *x, const double *rois, const double *of
                     double ab = 0.0;
                     sum += oracle_bilinear(X + c, H, W, C, yy, xx, &ab);
                     sa += ab;
+                    /* sum of |corner| inside the image: the bound on how much a shift of
+                       the position by delta can change the sample (delta per corner) */
+                    double y0 = floor(yy), x0 = floor(xx);
+                    for (int a = 0; a < 2; ++a)
+                        for (int b = 0; b < 2; ++b) {
+                            double qy = y0 + a, qx = x0 + b;
+                            if (qy < 0.0 || qy >= (double)H || qx < 0.0 || qx >= (double)W) continue;
+                            sc += fabs(X[((int64_t)qy * W + (int64_t)qx) * C + c]);
+                        }
                 }
                 o[c] = sum / (double)(S * S);
                 if (oa) oa[c] = sa / (double)(S * S);
+                if (oc) oc[c] = sc / (double)(S * S);
             }
         }
     }

@@ -242,3 +242,25 @@ def test_agg_backward_workspace_and_validation(lib):
     assert agg_bwd(lib, gf=None, gl=None, gw=None, ws=None) == OK     # nothing asked for
     assert lib.dcn_last_hip_error() == 0
 
+
+def roi(lib, x=A, rois=A, off=A, out=A, N=1, H=8, W=8, C=16, R=4, k=3, S=2, dtype=0):
+    return lib.deform_roi_pool_forward(x, rois, off, out, N, H, W, C, R, k, S, 1.0, 0.1, dtype, None)
+
+
+def test_roi_pool_validation(lib):
+    assert roi(lib, dtype=4) == DTYPE
+    assert roi(lib, N=0) == SHAPE
+    assert roi(lib, C=0) == SHAPE
+    assert roi(lib, R=-1) == SHAPE
+    assert roi(lib, k=0) == PARAM
+    assert roi(lib, S=0) == PARAM
+    assert roi(lib, S=65) == PARAM
+    assert roi(lib, H=50000, W=50000) == SHAPE
+    assert roi(lib, R=0, x=None, rois=None, out=None) == OK
+    assert roi(lib, x=None) == NULL
+    assert roi(lib, rois=None) == NULL
+    assert roi(lib, out=None) == NULL
+    assert roi(lib, off=A + 4) == ALIGN            # (dx, dy) pairs: 8-byte aligned
+    assert roi(lib, x=A + 2, dtype=0) == ALIGN
+    assert lib.dcn_last_hip_error() == 0
+

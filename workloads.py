@@ -198,6 +198,31 @@ def agg_grad_out(c, seed=0):
     return _t(r.standard_normal((c["B"], c["A"], c["G"] * c["Cg"])), c["dtype"])
 
 
+def roi_case(*, N, H, W, C, R, k=7, S=2, spatial_scale=1.0 / 16, gamma=0.1, dtype="f32",
+             offsets=True, seed=0):
+    """Inputs of deformable RoI pooling.
+
+    x       [N, H, W, C] of dtype ~ N(0,1) (channels-last)
+    rois    [R, 5] fp32 (batch, x1, y1, x2, y2) in input coordinates (the map times
+            1/spatial_scale): batch uniform, box centre uniform over the input, width
+            and height log-uniform between 1/16 and 1/2 of the input size
+    offset  [R, k, k, 2] fp32 normalised (dx, dy) ~ N(0, 1), or None
+    """
+    r = rng(seed)
+    x = r.standard_normal((N, H, W, C))
+    Wi, Hi = W / spatial_scale, H / spatial_scale
+    cx = r.uniform(0, Wi, R)
+    cy = r.uniform(0, Hi, R)
+    bw = Wi * np.exp(r.uniform(np.log(1 / 16), np.log(1 / 2), R))
+    bh = Hi * np.exp(r.uniform(np.log(1 / 16), np.log(1 / 2), R))
+    b = r.integers(0, N, R).astype(np.float64)
+    rois = np.stack([b, cx - bw / 2, cy - bh / 2, cx + bw / 2, cy + bh / 2], 1)
+    off = r.standard_normal((R, k, k, 2)) if offsets else None
+    return dict(x=_t(x, dtype), rois=_t(rois, "f32"), offset=None if off is None else _t(off, "f32"),
+                N=N, H=H, W=W, C=C, R=R, k=k, S=S, spatial_scale=spatial_scale, gamma=gamma,
+                dtype=dtype)
+
+
 WORKLOADS = {
     # DCNv4 block, fp32, one 32x32 map with 4 groups of 16 channels.
     "dcnv4_f32_n1_32x32_g4c16": dict(
@@ -217,6 +242,12 @@ WORKLOADS = {
         op="v2", seed=1004,
         args=dict(N=8, Cin=256, H=40, W=40, Cout=256, dtype="bf16", offset_std=2.0,
                   mask="sigmoid", w_std=0.02)),
+    # Deformable RoI pooling on the stride-16 map of a 1024x1024 input: fp32 x
+    # [2,64,64,256], 512 RoIs, 7x7 bins of 2x2 samples, gamma 0.1.
+    "droi_f32_n2_64x64_c256_r512_k7": dict(
+        op="roi", seed=1006,
+        args=dict(N=2, H=64, W=64, C=256, R=512, k=7, S=2, spatial_scale=1.0 / 16, gamma=0.1,
+                  dtype="f32")),
     # Six-camera, four-scale aggregation, 900 anchors x 13 points, 8 groups of 32.
     "agg_f32_6cam_4scale_a900p13_g8c32": dict(
         op="agg", seed=1005,
@@ -231,7 +262,7 @@ def make(name: str, **override):
     args = dict(spec["args"])
     args.update(override)
     seed = args.pop("seed", spec["seed"])
-    fn = {"core": core_case, "v2": v2_case, "agg": agg_case}[spec["op"]]
+    fn = {"core": core_case, "v2": v2_case, "agg": agg_case, "roi": roi_case}[spec["op"]]
     case = fn(seed=seed, **args)
     case["op"] = spec["op"]
     case["name"] = name
