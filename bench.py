@@ -125,6 +125,37 @@ def bench_core(dsa, torch, timer, name, iters, warmup):
                 gbs=nbytes / kern / 1e9, frac=nbytes / kern / 1e9 / HBM_PEAK_GBS), c
 
 
+def bench_core_packed(dsa, torch, timer, name, iters, warmup):
+    """dcn_core_forward_packed on a core workload with DCNv4's packed offset+mask
+    tensor in fp16 (the same values rounded to fp16): offsets and masks in 6 bytes
+    per tap instead of 12."""
+    import workloads as wl
+    c = wl.make(name)
+    dev = lambda t: None if t is None else t.to("cuda").contiguous()
+    x = dev(c["x"])
+    om = dsa.pack_offset_mask(dev(c["offset"]), dev(c["mask"]), dtype=torch.float16)
+    out = torch.empty((c["N"], c["Ho"], c["Wo"], c["G"] * c["C"]), dtype=x.dtype, device="cuda")
+    lib = dsa.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    dt = {"f32": 0, "f16": 1, "bf16": 2}[c["dtype"]]
+    N, H, W, GC = x.shape
+    G = c["G"]
+    args = (x.data_ptr(), om.data_ptr(), out.data_ptr(), N, H, W, G, GC // G, c["kh"], c["kw"],
+            c["stride"][0], c["stride"][1], c["pad"][0], c["pad"][1], c["dil"][0], c["dil"][1],
+            ctypes.c_float(1.0), int(bool(c["softmax"])), om.shape[3], 1, dt, stream)
+
+    def call():
+        st = lib.dcn_core_forward_packed(*args)
+        if st:
+            raise RuntimeError("dcn_core_forward_packed status %d" % st)
+    wall, kern = timer.run(call, iters, warmup)
+    taps = c["N"] * c["Ho"] * c["Wo"] * c["G"] * c["kh"] * c["kw"]
+    nbytes = (x.numel() + out.numel()) * x.element_size() + om.numel() * 2
+    return dict(workload=name + " packed fp16 offset+mask", taps=taps, channel_taps=taps * c["C"],
+                algo_bytes=nbytes, wall_s=wall, kernel_s=kern, taps_per_s=taps / kern,
+                gbs=nbytes / kern / 1e9, frac=nbytes / kern / 1e9 / HBM_PEAK_GBS)
+
+
 def bench_core_bwd(dsa, torch, timer, name, iters, warmup):
     """dcn_core_backward (grad_x, grad_offset, grad_mask) on a core workload: the
     whole call (bin count, scan, pair pass with the sample records, tile gather)."""
@@ -384,6 +415,8 @@ def main():
             r, _ = bench_core(dsa, torch, timer, nm, 200, 20)
             extra.append(r)
             log("%s done" % nm)
+        extra.append(bench_core_packed(dsa, torch, timer, HEADLINE, 200, 20))
+        log("packed offset+mask done")
         extra.append(bench_core_bwd(dsa, torch, timer, HEADLINE, 100, 10))
         log("core backward done")
         extra.append(bench_v2(dsa, torch, timer, 100, 10))

@@ -24,7 +24,7 @@ STATUS = {0: "DCN_OK", 1: "DCN_ERR_NULL", 2: "DCN_ERR_SHAPE", 3: "DCN_ERR_PARAM"
           4: "DCN_ERR_DTYPE", 5: "DCN_ERR_ALIGN", 6: "DCN_ERR_WORKSPACE", 7: "DCN_ERR_HIP"}
 
 # every symbol include/dcn.h declares
-EXPORTS = ("dcn_core_forward", "dcn_core_backward_workspace_bytes", "dcn_core_backward",
+EXPORTS = ("dcn_core_forward", "dcn_core_forward_packed", "dcn_core_backward_workspace_bytes", "dcn_core_backward",
            "dcn_v2_workspace_bytes", "dcn_v2_forward", "dcn_v2_im2col",
            "deform_agg_forward", "deform_agg_backward_workspace_bytes", "deform_agg_backward",
            "deform_roi_pool_forward",
@@ -58,6 +58,8 @@ def load(path: str | None = None):
     i, f, vp = _c.c_int, _c.c_float, _c.c_void_p
     lib.dcn_core_forward.restype = i
     lib.dcn_core_forward.argtypes = [vp, vp, vp, vp] + [i] * 13 + [f, i, i, vp]
+    lib.dcn_core_forward_packed.restype = i
+    lib.dcn_core_forward_packed.argtypes = [vp] * 3 + [i] * 13 + [f, i, i, i, i, vp]
     lib.dcn_core_backward_workspace_bytes.restype = _c.c_size_t
     lib.dcn_core_backward_workspace_bytes.argtypes = [i] * 14
     lib.dcn_core_backward.restype = i
@@ -151,6 +153,47 @@ def dcn_core_forward(x, offset, mask, out=None, *, kernel=(3, 3), stride=1, pad=
     _call("dcn_core_forward", _ptr(x), _ptr(offset), _ptr(mask), _ptr(out), N, H, W, G, GC // G,
           kh, kw, sh, sw, ph, pw, dh, dw, float(offset_scale), int(bool(softmax)),
           _DTYPE_ID[x.dtype], _stream(stream))
+    return out
+
+
+def pack_offset_mask(offset, mask, dtype=torch.float16, pixel_stride=None):
+    """DCNv4's packed layout [N,Ho,Wo,pixel_stride]: per group K (dx, dy) pairs then K
+    masks (ones when mask is None), padded rows zero. Layout helper for callers and
+    tests (plain torch reshaping, no sampling arithmetic)."""
+    N, Ho, Wo, G, K, _ = offset.shape
+    m = torch.ones((N, Ho, Wo, G, K), dtype=offset.dtype, device=offset.device) if mask is None else mask
+    rows = torch.cat([offset.reshape(N, Ho, Wo, G, 2 * K), m], -1).reshape(N, Ho, Wo, G * 3 * K)
+    stride = G * 3 * K if pixel_stride is None else int(pixel_stride)
+    if stride > G * 3 * K:
+        rows = torch.nn.functional.pad(rows, (0, stride - G * 3 * K))
+    return rows.to(dtype).contiguous()
+
+
+def dcn_core_forward_packed(x, offset_mask, *, groups, kernel=(3, 3), stride=1, pad=1, dilation=1,
+                            offset_scale=1.0, softmax=False, out=None, stream=None):
+    """DCNv4 core with the packed offset+mask tensor [N,Ho,Wo,stride >= G*3K] (fp32/fp16/
+    bf16; per group K (dx, dy) pairs then K masks). Returns out [N,Ho,Wo,G*C]."""
+    kh, kw = _pair(kernel)
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    dh, dw = _pair(dilation)
+    _check(x, "x")
+    _check(offset_mask, "offset_mask")
+    if offset_mask.dtype not in _DTYPE_ID:
+        raise ValueError("offset_mask must be fp32, fp16 or bf16")
+    N, H, W, GC = x.shape
+    G = int(groups)
+    if GC % G:
+        raise ValueError("groups must divide the channels")
+    Ho, Wo = out_size(H, kh, sh, ph, dh), out_size(W, kw, sw, pw, dw)
+    if offset_mask.dim() != 4 or tuple(offset_mask.shape[:3]) != (N, Ho, Wo):
+        raise ValueError("offset_mask must be [N,Ho,Wo,stride]")
+    if out is None:
+        out = torch.empty((N, Ho, Wo, GC), dtype=x.dtype, device=x.device)
+    _check(out, "out", x.dtype)
+    _call("dcn_core_forward_packed", _ptr(x), _ptr(offset_mask), _ptr(out), N, H, W, G, GC // G,
+          kh, kw, sh, sw, ph, pw, dh, dw, float(offset_scale), int(bool(softmax)),
+          offset_mask.shape[3], _DTYPE_ID[offset_mask.dtype], _DTYPE_ID[x.dtype], _stream(stream))
     return out
 
 

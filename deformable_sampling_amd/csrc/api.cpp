@@ -84,6 +84,48 @@ dcn_status dcn_core_forward(const void *x, const float *offset, const float *mas
     a.offset_scale = offset_scale;
     a.softmax = softmax;
     a.dtype = dtype;
+    const int K = kh * kw;
+    a.om_dtype = DCN_F32;
+    a.off_grp = 2 * K; a.off_pix = G * 2 * K; a.mask_grp = K; a.mask_pix = G * K;
+    a.om_plain = true;
+    return hip_status(dcn::launch_dcn_core(a, stream));
+}
+
+dcn_status dcn_core_forward_packed(const void *x, const void *offset_mask, void *out, int N, int H,
+                                   int W, int G, int C, int kh, int kw, int stride_h, int stride_w,
+                                   int pad_h, int pad_w, int dil_h, int dil_w, float offset_scale,
+                                   int softmax, int om_pixel_stride, dcn_dtype om_dtype,
+                                   dcn_dtype dtype, hipStream_t stream) {
+    if (!valid_dtype(dtype) || !valid_dtype(om_dtype)) return DCN_ERR_DTYPE;
+    if (N < 0 || H <= 0 || W <= 0 || G <= 0 || C <= 0) return DCN_ERR_SHAPE;
+    dcn_status st = check_window(kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w);
+    if (st != DCN_OK) return st;
+    const long long Ho = out_extent(H, kh, stride_h, pad_h, dil_h);
+    const long long Wo = out_extent(W, kw, stride_w, pad_w, dil_w);
+    if (Ho <= 0 || Wo <= 0) return DCN_ERR_SHAPE;
+    const int K = kh * kw;
+    if ((long long)om_pixel_stride < (long long)G * 3 * K) return DCN_ERR_PARAM;
+    if ((long long)(H + 1) * (W + 1) * G * C > kI32) return DCN_ERR_SHAPE;
+    if ((long long)N * Ho * Wo * G > kI32) return DCN_ERR_SHAPE;
+    if (N == 0) return DCN_OK;
+    if (!x || !offset_mask || !out) return DCN_ERR_NULL;
+    if (!aligned(x, dtype_size(dtype)) || !aligned(out, dtype_size(dtype)) ||
+        !aligned(offset_mask, dtype_size(om_dtype)))
+        return DCN_ERR_ALIGN;
+    const size_t oe = dtype_size(om_dtype);
+    dcn::CoreLaunch a;
+    a.x = x; a.offset = offset_mask;
+    a.mask = static_cast<const char *>(offset_mask) + (size_t)2 * K * oe;
+    a.out = out;
+    a.N = N; a.H = H; a.W = W; a.G = G; a.C = C; a.kh = kh; a.kw = kw;
+    a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w; a.dh = dil_h; a.dw = dil_w;
+    a.Ho = (int)Ho; a.Wo = (int)Wo;
+    a.offset_scale = offset_scale;
+    a.softmax = softmax;
+    a.dtype = dtype;
+    a.om_dtype = om_dtype;
+    a.off_grp = 3 * K; a.off_pix = om_pixel_stride; a.mask_grp = 3 * K; a.mask_pix = om_pixel_stride;
+    a.om_plain = false;
     return hip_status(dcn::launch_dcn_core(a, stream));
 }
 

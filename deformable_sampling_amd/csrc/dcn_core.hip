@@ -7,7 +7,9 @@
 //
 // Mapping. The unit of work is a (pixel, group) pair: the pair index e = pixel*G + g
 // runs over [0, N*Ho*Wo*G), and the offsets [.., G, K, 2] and masks [.., G, K] of
-// consecutive pairs are consecutive in memory. A pair's C channels are covered by S
+// consecutive pairs are consecutive in memory (other layouts and fp16/bf16 offsets
+// and masks, such as DCNv4's packed per-group rows of K (dx, dy) pairs then K masks,
+// are staged element by element and widened to fp32). A pair's C channels are covered by S
 // lanes, each holding V channels (16 bytes when alignment allows), so a wavefront
 // works on Q = 64/S pairs and every corner read of a tap is one contiguous vector
 // per lane (the channel-fastest mapping of the DCNv3 kernel page, widened to 16 B).
@@ -31,6 +33,7 @@ struct CoreParams {
     int N, H, W, G, C, kh, kw, sh, sw, ph, pw, dh, dw, Ho, Wo;
     float offset_scale;
     int softmax, has_mask, vec_stage;
+    int off_pix, off_grp, mask_pix, mask_grp, om_plain;  // offset/mask addressing
     int npairs;  // N*Ho*Wo*G (< 2^31, checked by the host)
     int S;       // lanes per pair
     int Q;       // pairs per wavefront
@@ -72,10 +75,25 @@ __device__ __forceinline__ float seg_reduce(float v, int S, int q) {
     return r;
 }
 
-template <class E, int V, int KH, int KW>
+// Offsets/masks of pairs [pair0, pair0 + npb) -> LDS as fp32, for any layout and
+// element type (the plain fp32 layout takes stage_range instead): element r of pair
+// e = pixel*G + g sits at base + pixel*pix + g*grp + r.
+template <class OM>
+__device__ __forceinline__ void stage_strided(float *dst, const typename OM::bits *src, int pair0,
+                                              int npb, int per, int pix_stride, int grp_stride,
+                                              int G) {
+    for (int idx = threadIdx.x; idx < npb * per; idx += kThreads) {
+        const int lq = idx / per, r = idx - lq * per;
+        const int e = pair0 + lq;
+        const int pixel = e / G, g = e - pixel * G;
+        dst[idx] = to_f32(OM{}, src[(size_t)pixel * pix_stride + (size_t)g * grp_stride + r]);
+    }
+}
+
+template <class E, class OM, int V, int KH, int KW>
 __global__ __launch_bounds__(kThreads) void dcn_core_kernel(const typename E::bits *__restrict__ x,
-                                                            const float *__restrict__ offset,
-                                                            const float *__restrict__ mask,
+                                                            const typename OM::bits *__restrict__ offset,
+                                                            const typename OM::bits *__restrict__ mask,
                                                             typename E::bits *__restrict__ out,
                                                             CoreParams p) {
     extern __shared__ float smem[];
@@ -90,9 +108,18 @@ __global__ __launch_bounds__(kThreads) void dcn_core_kernel(const typename E::bi
     const int npb = min(p.PB, p.npairs - pair0);
 
     // 1. offsets and masks of pairs [pair0, pair0 + npb) -> LDS
-    stage_range(s_off, offset + (size_t)pair0 * K * 2, npb * K * 2, p.vec_stage);
+    if (p.om_plain) {  // fp32 [.., G, K, 2] and [.., G, K]: two contiguous ranges
+        const float *of = reinterpret_cast<const float *>(offset);
+        stage_range(s_off, of + (size_t)pair0 * K * 2, npb * K * 2, p.vec_stage);
+    } else {
+        stage_strided<OM>(s_off, offset, pair0, npb, 2 * K, p.off_pix, p.off_grp, p.G);
+    }
     if (p.has_mask) {
-        stage_range(s_m, mask + (size_t)pair0 * K, npb * K, p.vec_stage);
+        if (p.om_plain)
+            stage_range(s_m, reinterpret_cast<const float *>(mask) + (size_t)pair0 * K, npb * K,
+                        p.vec_stage);
+        else
+            stage_strided<OM>(s_m, mask, pair0, npb, K, p.mask_pix, p.mask_grp, p.G);
     } else {
         for (int i = threadIdx.x; i < npb * K; i += kThreads) s_m[i] = 1.0f;
     }
@@ -165,21 +192,34 @@ __global__ __launch_bounds__(kThreads) void dcn_core_kernel(const typename E::bi
     }
 }
 
-template <class E, int V>
-hipError_t launch_v(const CoreLaunch &a, CoreParams &p, hipStream_t stream) {
+template <class E, class OM, int V>
+hipError_t launch_om(const CoreLaunch &a, CoreParams &p, hipStream_t stream) {
     const int K = a.kh * a.kw;
     const size_t lds = (size_t)p.PB * K * 3 * sizeof(float);
     const dim3 grid(p.nblocks), block(kThreads);
     using B = typename E::bits;
+    using OB = typename OM::bits;
     const B *x = static_cast<const B *>(a.x);
+    const OB *off = static_cast<const OB *>(a.offset);
+    const OB *msk = static_cast<const OB *>(a.mask);
     B *out = static_cast<B *>(a.out);
     if (a.kh == 3 && a.kw == 3)
-        hipLaunchKernelGGL((dcn_core_kernel<E, V, 3, 3>), grid, block, lds, stream, x, a.offset,
-                           a.mask, out, p);
+        hipLaunchKernelGGL((dcn_core_kernel<E, OM, V, 3, 3>), grid, block, lds, stream, x, off, msk,
+                           out, p);
     else
-        hipLaunchKernelGGL((dcn_core_kernel<E, V, 0, 0>), grid, block, lds, stream, x, a.offset,
-                           a.mask, out, p);
+        hipLaunchKernelGGL((dcn_core_kernel<E, OM, V, 0, 0>), grid, block, lds, stream, x, off, msk,
+                           out, p);
     return hipGetLastError();
+}
+
+template <class E, int V>
+hipError_t launch_v(const CoreLaunch &a, CoreParams &p, hipStream_t stream) {
+    switch (a.om_dtype) {
+        case DCN_F32: return launch_om<E, EF32, V>(a, p, stream);
+        case DCN_F16: return launch_om<E, EF16, V>(a, p, stream);
+        case DCN_BF16: return launch_om<E, EBF16, V>(a, p, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <class E>
@@ -199,6 +239,8 @@ hipError_t launch_e(const CoreLaunch &a, hipStream_t stream) {
     p.softmax = a.softmax ? 1 : 0;
     p.has_mask = a.mask != nullptr;
     p.vec_stage = ((uintptr_t)a.offset % 16 == 0) && (a.mask == nullptr || (uintptr_t)a.mask % 16 == 0);
+    p.off_pix = a.off_pix; p.off_grp = a.off_grp; p.mask_pix = a.mask_pix; p.mask_grp = a.mask_grp;
+    p.om_plain = a.om_plain ? 1 : 0;
     p.npairs = a.N * a.Ho * a.Wo * a.G;
     p.nchunk = a.C / V;
     p.S = p.nchunk < 64 ? p.nchunk : 64;

@@ -105,26 +105,52 @@ __device__ __forceinline__ void scale_offsets(float (&d)[2 * K], float scale) {
     }
 }
 
-// The pair's K (dx, dy) offsets and K masks into registers (pair 0 for idle lanes).
-template <int K>
+// Offset/mask element tags: the plain fp32 layout of dcn_core_forward ([.., G, K, 2]
+// offsets, [.., G, K] masks) is a type of its own so that its addressing and 8-byte
+// (dx, dy) loads are compiled in; EF32/EF16/EBF16 name DCNv4's packed rows (pixel and
+// group strides from the parameters) of that element type.
+struct OMPlain : EF32 {};
+template <class OM> constexpr bool kOmPlain = false;
+template <> constexpr bool kOmPlain<OMPlain> = true;
+
+// The pair's K (dx, dy) offsets and K masks into registers as fp32 (pair 0 for idle
+// lanes). The plain layout takes the tap's pair as one 8-byte load; packed rows, and
+// fp16/bf16 values, are read element by element and widened exactly.
+template <int K, class OM>
 __device__ __forceinline__ void load_dm(float (&d)[2 * K], float (&m)[K], const TileAt &a,
-                                        const LaneAt &l, const float *offset, const float *mask,
-                                        const TileParams &p) {
-    const size_t pr = l.active ? (((size_t)a.n * p.Ho + l.ho) * p.Wo + l.wo) * p.G + l.g : 0;
-    const float2 *o2 = reinterpret_cast<const float2 *>(offset + pr * K * 2);
+                                        const LaneAt &l, const typename OM::bits *offset,
+                                        const typename OM::bits *mask, const TileParams &p) {
+    if constexpr (kOmPlain<OM>) {
+        const size_t pr = l.active ? (((size_t)a.n * p.Ho + l.ho) * p.Wo + l.wo) * p.G + l.g : 0;
+        const float2 *o2 = reinterpret_cast<const float2 *>(offset + pr * K * 2);
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const float2 v = o2[k];
-        d[2 * k] = v.x;
-        d[2 * k + 1] = v.y;
-    }
-    if (p.has_mask) {
-        const float *mm = mask + pr * K;
+        for (int k = 0; k < K; ++k) {
+            const float2 v = o2[k];
+            d[2 * k] = v.x;
+            d[2 * k + 1] = v.y;
+        }
+        if (p.has_mask) {
+            const typename OM::bits *mm = mask + pr * K;
 #pragma unroll
-        for (int k = 0; k < K; ++k) m[k] = mm[k];
+            for (int k = 0; k < K; ++k) m[k] = to_f32(OM{}, mm[k]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < K; ++k) m[k] = 1.0f;
+        }
     } else {
+        const size_t pixel = l.active ? ((size_t)a.n * p.Ho + l.ho) * p.Wo + l.wo : 0;
+        const int g = l.active ? l.g : 0;
+        const typename OM::bits *od = offset + pixel * p.off_pix + (size_t)g * p.off_grp;
 #pragma unroll
-        for (int k = 0; k < K; ++k) m[k] = 1.0f;
+        for (int i = 0; i < 2 * K; ++i) d[i] = to_f32(OM{}, od[i]);
+        if (p.has_mask) {
+            const typename OM::bits *mm = mask + pixel * p.mask_pix + (size_t)g * p.mask_grp;
+#pragma unroll
+            for (int k = 0; k < K; ++k) m[k] = to_f32(OM{}, mm[k]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < K; ++k) m[k] = 1.0f;
+        }
     }
 }
 
@@ -163,12 +189,12 @@ __device__ __forceinline__ void softmax_k(float (&m)[K], int s) {
 // (0: taken from p): the four corners of a chunk are then one address plus constant
 // offsets that the LDS reads encode as immediates.
 // coff: this pair's 2K offsets in memory (re-read for taps of the deferred pass).
-template <class E, int KH, int KW, int S, int NC, int CPP_ = 0, int RW_ = 0>
+template <class E, class OM, int KH, int KW, int S, int NC, int CPP_ = 0, int RW_ = 0>
 __device__ __forceinline__ void taps_and_store(const uint4 *buf, const typename E::bits *x,
                                                typename E::bits *out, float (&d)[2 * KH * KW],
                                                const float (&m)[KH * KW], const TileAt &a,
                                                const LaneAt &l, const TileParams &p,
-                                               const float *coff) {
+                                               const typename OM::bits *coff) {
     using Bt = typename E::bits;
     constexpr int V = 16 / (int)sizeof(Bt);
     constexpr int K = KH * KW;
@@ -264,8 +290,15 @@ __device__ __forceinline__ void taps_and_store(const uint4 *buf, const typename 
             far &= far - 1;
             // the tap's offsets again from memory (the pair's row, just read, is in
             // cache): the loop above frees each tap's offset registers after use
-            const float2 dv = reinterpret_cast<const float2 *>(coff)[k];
-            float dx = dv.x, dy = dv.y;
+            float dx, dy;
+            if constexpr (kOmPlain<OM>) {
+                const float2 dv = reinterpret_cast<const float2 *>(coff)[k];
+                dx = dv.x;
+                dy = dv.y;
+            } else {
+                dx = to_f32(OM{}, coff[2 * k]);
+                dy = to_f32(OM{}, coff[2 * k + 1]);
+            }
             if (p.offset_scale != 1.0f) {
                 dx = mul_rn(p.offset_scale, dx);
                 dy = mul_rn(p.offset_scale, dy);
@@ -298,10 +331,10 @@ __device__ __forceinline__ void taps_and_store(const uint4 *buf, const typename 
 
 // ---------------------------------------------------------- one tile/block --
 
-template <class E, int KH, int KW, int S, int NC, int CPP_, int RW_>
+template <class E, class OM, int KH, int KW, int S, int NC, int CPP_, int RW_>
 __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::bits *__restrict__ x,
-                                                             const float *__restrict__ offset,
-                                                             const float *__restrict__ mask,
+                                                             const typename OM::bits *__restrict__ offset,
+                                                             const typename OM::bits *__restrict__ mask,
                                                              typename E::bits *__restrict__ out,
                                                              const TileParams p) {
     using Bt = typename E::bits;
@@ -315,7 +348,7 @@ __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::b
     const int GC = p.G * p.C;
 
     float d[2 * K], m[K];
-    load_dm<K>(d, m, a, l, offset, mask, p);
+    load_dm<K, OM>(d, m, a, l, offset, mask, p);
 
     // Stage the region with direct global->LDS copies: each wave moves 64 consecutive
     // 16-byte chunks per instruction (lane order = LDS order); chunks outside the
@@ -343,8 +376,10 @@ __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::b
     __syncthreads();
     if (p.softmax) softmax_k<K, S>(m, l.s);
     if (!l.active) return;
-    const size_t pc = (((size_t)a.n * p.Ho + l.ho) * p.Wo + l.wo) * p.G + l.g;
-    taps_and_store<E, KH, KW, S, NC, CPP_, RW_>(lds, x, out, d, m, a, l, p, offset + pc * K * 2);
+    const size_t pixel = ((size_t)a.n * p.Ho + l.ho) * p.Wo + l.wo;
+    const typename OM::bits *coff = kOmPlain<OM> ? offset + (pixel * p.G + l.g) * K * 2
+                                                 : offset + pixel * p.off_pix + (size_t)l.g * p.off_grp;
+    taps_and_store<E, OM, KH, KW, S, NC, CPP_, RW_>(lds, x, out, d, m, a, l, p, coff);
 }
 
 // --------------------------------------------------------------- launching --
@@ -368,34 +403,48 @@ __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::b
 #define DCN_TILE_SLICE 64
 #endif
 
-template <class E, int S, int NC>
+template <class E, class OM, int S, int NC>
 hipError_t launch_tile(const CoreLaunch &a, const TileParams &p, hipStream_t stream) {
     using Bt = typename E::bits;
+    using OB = typename OM::bits;
     const Bt *x = static_cast<const Bt *>(a.x);
+    const OB *off = static_cast<const OB *>(a.offset);
+    const OB *msk = static_cast<const OB *>(a.mask);
     Bt *out = static_cast<Bt *>(a.out);
     auto go = [&](auto kern) {
         static const hipError_t attr = hipFuncSetAttribute(
             reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
             DCN_TILE_LDS_BYTES);
         if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL(kern, dim3(p.nblocks), dim3(p.threads), p.lds_bytes, stream, x, a.offset,
-                           a.mask, out, p);
+        hipLaunchKernelGGL(kern, dim3(p.nblocks), dim3(p.threads), p.lds_bytes, stream, x, off, msk,
+                           out, p);
         return hipGetLastError();
     };
     // 16x16-pixel tiles with halo 8 (region width 35) of 64-byte slices: the common
     // plan, with its region geometry compiled in
-    if (p.cpp == 4 && p.RW == 35) return go(dcn_core_tile_kernel<E, 3, 3, S, NC, 4, 35>);
-    if (p.cpp == 2 && p.RW == 35) return go(dcn_core_tile_kernel<E, 3, 3, S, NC, 2, 35>);
-    return go(dcn_core_tile_kernel<E, 3, 3, S, NC, 0, 0>);
+    if (p.cpp == 4 && p.RW == 35) return go(dcn_core_tile_kernel<E, OM, 3, 3, S, NC, 4, 35>);
+    if (p.cpp == 2 && p.RW == 35) return go(dcn_core_tile_kernel<E, OM, 3, 3, S, NC, 2, 35>);
+    return go(dcn_core_tile_kernel<E, OM, 3, 3, S, NC, 0, 0>);
+}
+
+template <class E, int S, int NC>
+hipError_t launch_tile_om(const CoreLaunch &a, const TileParams &p, hipStream_t stream) {
+    if (a.om_plain) return launch_tile<E, OMPlain, S, NC>(a, p, stream);
+    switch (a.om_dtype) {
+        case DCN_F32: return launch_tile<E, EF32, S, NC>(a, p, stream);
+        case DCN_F16: return launch_tile<E, EF16, S, NC>(a, p, stream);
+        case DCN_BF16: return launch_tile<E, EBF16, S, NC>(a, p, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <class E, int NC>
 hipError_t launch_tile_s(const CoreLaunch &a, const TileParams &p, hipStream_t stream) {
     switch (p.S) {
-        case 1: return launch_tile<E, 1, NC>(a, p, stream);
-        case 2: return launch_tile<E, 2, NC>(a, p, stream);
-        case 4: return launch_tile<E, 4, NC>(a, p, stream);
-        case 8: return launch_tile<E, 8, NC>(a, p, stream);
+        case 1: return launch_tile_om<E, 1, NC>(a, p, stream);
+        case 2: return launch_tile_om<E, 2, NC>(a, p, stream);
+        case 4: return launch_tile_om<E, 4, NC>(a, p, stream);
+        case 8: return launch_tile_om<E, 8, NC>(a, p, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -439,7 +488,8 @@ bool plan_core_tile(const CoreLaunch &a, TileParams &p) {
     const int elt = a.dtype == DCN_F32 ? 4 : 2;
     const int cbytes = a.C * elt;
     if (cbytes % 16 != 0 || cbytes > 256) return false;
-    if ((uintptr_t)a.x % 16 || (uintptr_t)a.out % 16 || (uintptr_t)a.offset % 8) return false;
+    if ((uintptr_t)a.x % 16 || (uintptr_t)a.out % 16) return false;
+    if (a.om_plain && (uintptr_t)a.offset % 8) return false;  // 8-byte (dx, dy) loads
     if ((long long)a.H * a.W >= (1LL << 24) || (long long)a.G * a.C >= (1LL << 24)) return false;
     // 16-byte chunks per lane: two where the channels allow, except for bf16, whose
     // widening (no mixed-precision FMA) would need twice the registers
@@ -468,6 +518,7 @@ bool plan_core_tile(const CoreLaunch &a, TileParams &p) {
     p.offset_scale = a.offset_scale;
     p.softmax = a.softmax ? 1 : 0;
     p.has_mask = a.mask != nullptr;
+    p.off_pix = a.off_pix; p.off_grp = a.off_grp; p.mask_pix = a.mask_pix; p.mask_grp = a.mask_grp;
     p.GB = GB; p.S = S; p.NC = NC; p.cpp = cpp; p.cpp_log2 = ilog2(cpp); p.lpp = lpp;
     p.TH = TH; p.TW = TW; p.halo = halo;
     p.RH = (TH - 1) * a.sh + (a.kh - 1) * a.dh + 2 + 2 * halo;

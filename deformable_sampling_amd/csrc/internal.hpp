@@ -12,13 +12,20 @@ namespace dcn {
 
 struct CoreLaunch {
     const void *x;
-    const float *offset;
-    const float *mask;  // may be NULL
+    const void *offset;  // elements of om_dtype
+    const void *mask;    // may be NULL
     void *out;
     int N, H, W, G, C, kh, kw, sh, sw, ph, pw, dh, dw, Ho, Wo;
     float offset_scale;
     int softmax;
     dcn_dtype dtype;
+    // Offsets and masks: pair (output pixel p = (n*Ho + ho)*Wo + wo, group g) reads its
+    // K (dx, dy) pairs at offset + p*off_pix + g*off_grp and its K masks at
+    // mask + p*mask_pix + g*mask_grp (elements of om_dtype). om_plain: fp32 with
+    // off_grp = 2K, off_pix = G*2K, mask_grp = K, mask_pix = G*K (separate tensors).
+    dcn_dtype om_dtype;
+    int off_pix, off_grp, mask_pix, mask_grp;
+    bool om_plain;
 };
 hipError_t launch_dcn_core(const CoreLaunch &a, hipStream_t stream);
 
@@ -55,6 +62,7 @@ struct CoreTilePlan {
     int N, H, W, G, C, kh, kw, sh, sw, ph, pw, dh, dw, Ho, Wo;
     float offset_scale;
     int softmax, has_mask;
+    int off_pix, off_grp, mask_pix, mask_grp;  // as CoreLaunch (packed layouts)
     int GB, S, NC;           // groups per block, lanes per pair, 16-B chunks per lane
     int cpp, cpp_log2, lpp;  // 16-B chunks per region pixel (2^cpp_log2), lanes per pixel
     int TH, TW, halo, RH, RW;

@@ -4,6 +4,7 @@
  * Forward operations and two backward passes, each enqueued on a caller-supplied HIP stream:
  *
  *   dcn_core_forward    DCNv3/v4 core (also DCNv1 when mask == NULL), channels-last.
+ *   dcn_core_forward_packed  the same with DCNv4's packed offset+mask tensor, fp32/fp16/bf16.
  *   dcn_core_backward   gradients of the core w.r.t. x, offsets and modulation.
  *   dcn_v2_forward      DCNv2 modulated deformable convolution, NCHW: deform-im2col
  *                       and an MFMA GEMM (fused, or in two stages through the workspace).
@@ -94,6 +95,28 @@ dcn_status dcn_core_forward(const void *x, const float *offset, const float *mas
                             int stride_h, int stride_w, int pad_h, int pad_w,
                             int dil_h, int dil_w, float offset_scale, int softmax,
                             dcn_dtype dtype, hipStream_t stream);
+
+/*
+ * dcn_core_forward with DCNv4's packed offset+mask tensor ("DCNv4 in YOLOv11",
+ * section 3.2: one offset-generating projection per group yields both the offsets
+ * and the modulation) in fp32, fp16 or bf16:
+ *
+ *   offset_mask  [N, Ho, Wo, om_pixel_stride]  om_dtype; for group g the row at
+ *                element g*3K holds the K (dx, dy) pairs (x first) and then the K
+ *                masks (logits when softmax != 0); om_pixel_stride >= G*3K (pixel
+ *                rows may be padded, e.g. to a multiple of 8 elements)
+ *
+ * Offsets and masks are widened exactly to fp32; everything else, results included,
+ * is as dcn_core_forward (the scaled offset fl32(offset_scale * dx) is the same fp32
+ * quantity). Halving the offset/mask bytes is what the fp16/bf16 forms are for.
+ * offset_mask must be aligned to its element size. DCN_ERR_PARAM if
+ * om_pixel_stride < G*3K.
+ */
+dcn_status dcn_core_forward_packed(const void *x, const void *offset_mask, void *out, int N, int H,
+                                   int W, int G, int C, int kh, int kw, int stride_h, int stride_w,
+                                   int pad_h, int pad_w, int dil_h, int dil_w, float offset_scale,
+                                   int softmax, int om_pixel_stride, dcn_dtype om_dtype,
+                                   dcn_dtype dtype, hipStream_t stream);
 
 /*
  * Workspace bytes dcn_core_backward needs when grad_x is requested (0 if the sizes

@@ -264,3 +264,21 @@ def test_roi_pool_validation(lib):
     assert roi(lib, x=A + 2, dtype=0) == ALIGN
     assert lib.dcn_last_hip_error() == 0
 
+
+def core_packed(lib, x=A, om=A, out=A, N=1, H=8, W=8, G=2, C=4, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1,
+                dh=1, dw=1, stride=54, om_dtype=1, dtype=1):
+    return lib.dcn_core_forward_packed(x, om, out, N, H, W, G, C, kh, kw, sh, sw, ph, pw, dh, dw,
+                                       1.0, 0, stride, om_dtype, dtype, None)
+
+
+def test_core_packed_validation(lib):
+    assert core_packed(lib, om_dtype=9) == DTYPE
+    assert core_packed(lib, dtype=9) == DTYPE
+    assert core_packed(lib, stride=53) == PARAM          # G*3K = 54 elements per pixel
+    assert core_packed(lib, kh=0) == SHAPE
+    assert core_packed(lib, N=0, x=None, om=None, out=None) == OK
+    assert core_packed(lib, om=None) == NULL
+    assert core_packed(lib, om=A + 1) == ALIGN           # fp16 offsets on an odd address
+    assert core_packed(lib, om=A + 2, om_dtype=0) == ALIGN
+    assert lib.dcn_last_hip_error() == 0
+
