@@ -78,6 +78,8 @@ def _load():
         lib.oracle_dcn_v2.restype = ctypes.c_int
         lib.oracle_dcn_v2.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp] + [_i64] * 14 + [
             ctypes.c_int, _i64p, _i64]
+        lib.oracle_dcn_v2_backward.restype = ctypes.c_int
+        lib.oracle_dcn_v2_backward.argtypes = [_dp] * 13 + [_i64] * 14 + [ctypes.c_int]
         lib.oracle_deform_agg.restype = ctypes.c_int
         lib.oracle_deform_agg.argtypes = [_dp, _i32p, _i32p, _dp, _dp, _dp, _dp] + [
             _i64] * 8 + [ctypes.c_int, _i64p, _i64]
@@ -239,6 +241,32 @@ def dcn_v2(x, offset, mask, weight, *, stride=(1, 1), pad=(0, 0), dil=(1, 1),
         out = out.reshape(N, Ho, Wo, Cout).transpose(0, 3, 1, 2).copy()
         ab = ab.reshape(N, Ho, Wo, Cout).transpose(0, 3, 1, 2).copy()
     return out, ab
+
+
+def dcn_v2_backward(x, offset, mask, weight, grad_out, *, stride=(1, 1), pad=(0, 0), dil=(1, 1),
+                    softmax=False):
+    """Gradients of dcn_v2. Returns a dict with grad_x [N,Cin,H,W], grad_offset
+    [N,dg*K*2,Ho,Wo], grad_mask [N,dg*K,Ho,Wo] (w.r.t. the mask argument; the implied
+    unit modulation when mask is None), grad_weight [Cout,Cin,kh,kw] and the matching
+    *_abs arrays of summed |product terms|."""
+    x, offset, mask, weight, gout = _f64(x), _f64(offset), _f64(mask), _f64(weight), _f64(grad_out)
+    Cout, _, kh, kw = weight.shape
+    N, Cin, H, W, Ho, Wo, dg = _v2_dims(x, offset, kh, kw, stride, pad, dil)
+    K = kh * kw
+    if gout.shape != (N, Cout, Ho, Wo) or offset.shape != (N, dg * K * 2, Ho, Wo):
+        raise ValueError("dcn_v2_backward: shape mismatch")
+    gx = np.zeros_like(x); gxa = np.zeros_like(x)
+    goff = np.zeros_like(offset); goffa = np.zeros_like(offset)
+    gm = np.zeros((N, dg * K, Ho, Wo)); gma = np.zeros_like(gm)
+    gw = np.zeros_like(weight); gwa = np.zeros_like(weight)
+    rc = _load().oracle_dcn_v2_backward(
+        _ptr(x), _ptr(offset), _ptr(mask), _ptr(weight), _ptr(gout), _ptr(gx), _ptr(goff),
+        _ptr(gm), _ptr(gw), _ptr(gxa), _ptr(goffa), _ptr(gma), _ptr(gwa), N, Cin, H, W, Cout,
+        kh, kw, stride[0], stride[1], pad[0], pad[1], dil[0], dil[1], dg, int(bool(softmax)))
+    if rc:
+        raise ValueError("oracle_dcn_v2_backward rejected its arguments (%d)" % rc)
+    return dict(grad_x=gx, grad_offset=goff, grad_mask=gm, grad_weight=gw,
+                grad_x_abs=gxa, grad_offset_abs=goffa, grad_mask_abs=gma, grad_weight_abs=gwa)
 
 
 def deform_agg(feat, spatial_shape, scale_start, loc, weights, *, softmax=False, anchors=None):

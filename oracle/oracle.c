@@ -36,7 +36,8 @@
  * Every function also returns, per output element, the sum of the absolute
  * values of all product terms ("absum"), used by the tests' error bound.
  *
- * oracle_dcn_core_backward is the derivative of oracle_dcn_core's sum,
+ * oracle_dcn_core_backward (and oracle_dcn_v2_backward) is the derivative of
+ * the forward sum,
  * written out by hand (the pages print no backward pass); its pins are
  * finite differences, adjoint identities and torch autograd of an
  * independent fp64 formulation.
@@ -405,6 +406,165 @@ int oracle_dcn_v2(const double *x, const double *offset, const double *mask,
         free(m);
     }
     return bad ? 2 : 0;
+}
+
+/* DCNv2 backward: the derivative of oracle_dcn_v2's sum (no page prints it).
+ *  gout  [N, Cout, Ho, Wo]
+ *  gx    [N, Cin, H, W]      gradient w.r.t. x
+ *  goff  [N, dg*K*2, Ho, Wo] gradient w.r.t. the offsets (dx, dy channels)
+ *  gmask [N, dg*K, Ho, Wo]   gradient w.r.t. the mask argument (the logits when
+ *                            softmax != 0; with mask == NULL, w.r.t. the implied
+ *                            modulation: ones, or zero logits with softmax)
+ *  gw    [Cout, Cin, kh, kw] gradient w.r.t. the weight
+ * and the matching sums of |product terms| (*_abs; any output may be NULL).
+ * Three steps: the column gradient gc[p][ci*K + k] = sum_co weight[co,ci,k] *
+ * gout[n,co,p]; the weight gradient sum_p gout[n,co,p] * col_p[ci*K + k]; the
+ * sampling derivative of each column entry m_k * bilinear(x[n,ci], pos_k) with
+ * upstream value gc (as oracle_dcn_core_backward, one upstream value per tap). */
+int oracle_dcn_v2_backward(const double *x, const double *offset, const double *mask,
+                           const double *weight, const double *gout,
+                           double *gx, double *goff, double *gmask, double *gw,
+                           double *gx_abs, double *goff_abs, double *gmask_abs, double *gw_abs,
+                           int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
+                           int64_t kh, int64_t kw, int64_t sh, int64_t sw,
+                           int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                           int64_t dg, int softmax)
+{
+    int64_t Ho = out_size(H, kh, sh, ph, dh), Wo = out_size(W, kw, sw, pw, dw);
+    int64_t K = kh * kw, R = Cin * K, HWo = Ho * Wo, P = N * HWo;
+    if (Ho <= 0 || Wo <= 0 || dg <= 0 || Cin % dg) return 1;
+    int64_t cpg = Cin / dg;
+    double *col = (double *)malloc(sizeof(double) * (size_t)(P * R > 0 ? P * R : 1));
+    double *cab = (double *)malloc(sizeof(double) * (size_t)(P * R > 0 ? P * R : 1));
+    double *gc = (double *)malloc(sizeof(double) * (size_t)(P * R > 0 ? P * R : 1));
+    double *gca = (double *)malloc(sizeof(double) * (size_t)(P * R > 0 ? P * R : 1));
+    if (!col || !cab || !gc || !gca) {
+        free(col); free(cab); free(gc); free(gca);
+        return 3;
+    }
+    /* forward columns and the column gradient, per output pixel */
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t n = p / HWo, r = p % HWo;
+        double *m = (double *)malloc(sizeof(double) * (size_t)K);
+        v2_column(x, offset, mask, col + p * R, cab + p * R, p, Cin, H, W, Ho, Wo,
+                  kh, kw, sh, sw, ph, pw, dh, dw, dg, softmax, m);
+        free(m);
+        for (int64_t rr = 0; rr < R; ++rr) {
+            double s = 0.0, a = 0.0;
+            for (int64_t co = 0; co < Cout; ++co) {
+                double go = gout[(n * Cout + co) * HWo + r];
+                s += weight[co * R + rr] * go;
+                a += fabs(weight[co * R + rr] * go);
+            }
+            gc[p * R + rr] = s;
+            gca[p * R + rr] = a;
+        }
+    }
+    /* weight gradient: one (co, ci*K + k) entry per iteration */
+    if (gw || gw_abs) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t co = 0; co < Cout; ++co) {
+            for (int64_t rr = 0; rr < R; ++rr) {
+                double s = 0.0, a = 0.0;
+                for (int64_t p = 0; p < P; ++p) {
+                    double go = gout[((p / HWo) * Cout + co) * HWo + p % HWo];
+                    s += go * col[p * R + rr];
+                    a += fabs(go) * cab[p * R + rr];
+                }
+                if (gw) gw[co * R + rr] = s;
+                if (gw_abs) gw_abs[co * R + rr] = a;
+            }
+        }
+    }
+    if (gx) for (int64_t i = 0; i < N * Cin * H * W; ++i) gx[i] = 0.0;
+    if (gx_abs) for (int64_t i = 0; i < N * Cin * H * W; ++i) gx_abs[i] = 0.0;
+    /* sampling derivative; one image per iteration (the scatter stays in it) */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t n = 0; n < N; ++n) {
+        double *m = (double *)malloc(sizeof(double) * (size_t)K * 3);
+        double *gm = m + K, *gma = m + 2 * K;
+        for (int64_t r = 0; r < HWo; ++r) {
+            int64_t p = n * HWo + r, ho = r / Wo, wo = r % Wo;
+            for (int64_t g = 0; g < dg; ++g) {
+                for (int64_t k = 0; k < K; ++k)
+                    m[k] = mask ? mask[(n * dg * K + g * K + k) * HWo + r] : 1.0;
+                if (softmax && mask)
+                    softmax_d(mask + (n * dg * K + g * K) * HWo + r, K, HWo, m);
+                else if (softmax)
+                    for (int64_t k = 0; k < K; ++k) m[k] = 1.0 / (double)K;
+                for (int64_t i = 0; i < kh; ++i)
+                for (int64_t j = 0; j < kw; ++j) {
+                    int64_t k = i * kw + j;
+                    int64_t oc = (n * dg * K + g * K + k) * 2;
+                    double dx = offset[(oc + 0) * HWo + r];
+                    double dy = offset[(oc + 1) * HWo + r];
+                    double yy = (double)(ho * sh - ph + i * dh) + dy;
+                    double xx = (double)(wo * sw - pw + j * dw) + dx;
+                    double y0 = floor(yy), x0 = floor(xx);
+                    double fy = yy - y0, fx = xx - x0;
+                    double w[2][2] = {{(1.0 - fy) * (1.0 - fx), (1.0 - fy) * fx},
+                                      {fy * (1.0 - fx), fy * fx}};
+                    double dwy[2][2] = {{-(1.0 - fx), -fx}, {1.0 - fx, fx}};  /* d w_ab / d fy */
+                    double dwx[2][2] = {{-(1.0 - fy), 1.0 - fy}, {-fy, fy}};  /* d w_ab / d fx */
+                    int inside[2][2];
+                    int64_t q[2][2];
+                    for (int a = 0; a < 2; ++a)
+                        for (int b = 0; b < 2; ++b) {
+                            double qy = y0 + a, qx = x0 + b;
+                            inside[a][b] = !(qy < 0.0 || qy >= (double)H || qx < 0.0 || qx >= (double)W);
+                            q[a][b] = inside[a][b] ? (int64_t)qy * W + (int64_t)qx : 0;
+                        }
+                    double sb = 0.0, sba = 0.0, sy = 0.0, sya = 0.0, sx = 0.0, sxa = 0.0;
+                    for (int64_t ci = g * cpg; ci < (g + 1) * cpg; ++ci) {
+                        double u = gc[p * R + ci * K + k], ua = gca[p * R + ci * K + k];
+                        const double *X = x + (n * Cin + ci) * H * W;
+                        for (int a = 0; a < 2; ++a)
+                            for (int b = 0; b < 2; ++b) {
+                                if (!inside[a][b]) continue;
+                                double v = X[q[a][b]];
+                                sb += u * w[a][b] * v;
+                                sba += ua * fabs(w[a][b] * v);
+                                sy += u * dwy[a][b] * v;
+                                sya += ua * fabs(dwy[a][b] * v);
+                                sx += u * dwx[a][b] * v;
+                                sxa += ua * fabs(dwx[a][b] * v);
+                                int64_t xi = (n * Cin + ci) * H * W + q[a][b];
+                                if (gx && w[a][b] != 0.0) gx[xi] += m[k] * w[a][b] * u;
+                                if (gx_abs) gx_abs[xi] += fabs(m[k] * w[a][b]) * ua;
+                            }
+                    }
+                    gm[k] = sb;
+                    gma[k] = sba;
+                    if (goff) {
+                        goff[(oc + 0) * HWo + r] = m[k] * sx;
+                        goff[(oc + 1) * HWo + r] = m[k] * sy;
+                    }
+                    if (goff_abs) {
+                        goff_abs[(oc + 0) * HWo + r] = fabs(m[k]) * sxa;
+                        goff_abs[(oc + 1) * HWo + r] = fabs(m[k]) * sya;
+                    }
+                }
+                if (gmask || gmask_abs) {
+                    double dot = 0.0, dota = 0.0;
+                    for (int64_t k = 0; k < K; ++k) {
+                        dot += m[k] * gm[k];
+                        dota += fabs(m[k]) * gma[k];
+                    }
+                    for (int64_t k = 0; k < K; ++k) {
+                        double v = softmax ? m[k] * (gm[k] - dot) : gm[k];
+                        double va = softmax ? fabs(m[k]) * (gma[k] + dota) : gma[k];
+                        int64_t mi = (n * dg * K + g * K + k) * HWo + r;
+                        if (gmask) gmask[mi] = v;
+                        if (gmask_abs) gmask_abs[mi] = va;
+                    }
+                }
+            }
+        }
+        free(m);
+    }
+    free(col); free(cab); free(gc); free(gca);
+    return 0;
 }
 
 /* ---------------------------------------------------------------------- */

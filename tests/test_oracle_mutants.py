@@ -87,6 +87,25 @@ AGG_BWD_MUTANTS = [
      "const double *Gv = gout + ba * GC;", 1),
 ]
 
+# Mistakes in the DCNv2 backward (oracle_dcn_v2_backward), caught by its pins.
+V2_BWD_MUTANTS = [
+    ("v2bwd_weight_tap_major", "s += weight[co * R + rr] * go;",
+     "s += weight[co * R + (rr % K) * Cin + rr / K] * go;", 1),
+    ("v2bwd_gout_batch_channel_swapped", "double go = gout[(n * Cout + co) * HWo + r];",
+     "double go = gout[(co * N + n) * HWo + r];", 1),
+    ("v2bwd_weight_grad_from_column_grad", "s += go * col[p * R + rr];", "s += go * gc[p * R + rr];", 1),
+    ("v2bwd_grad_x_no_modulation", "if (gx && w[a][b] != 0.0) gx[xi] += m[k] * w[a][b] * u;",
+     "if (gx && w[a][b] != 0.0) gx[xi] += w[a][b] * u;", 1),
+    ("v2bwd_offset_pair_swapped", "goff[(oc + 0) * HWo + r] = m[k] * sx;",
+     "goff[(oc + 0) * HWo + r] = m[k] * sy;", 1),
+    ("v2bwd_column_grad_tap_major", "double u = gc[p * R + ci * K + k], ua = gca[p * R + ci * K + k];",
+     "double u = gc[p * R + k * Cin + ci], ua = gca[p * R + k * Cin + ci];", 1),
+    ("v2bwd_softmax_no_centering", "double v = softmax ? m[k] * (gm[k] - dot) : gm[k];",
+     "double v = softmax ? m[k] * gm[k] : gm[k];", 2),
+    ("v2bwd_dy_sign", "double dwy[2][2] = {{-(1.0 - fx), -fx}, {1.0 - fx, fx}};",
+     "double dwy[2][2] = {{(1.0 - fx), fx}, {-(1.0 - fx), -fx}};", 2),
+]
+
 # Mistakes in deformable RoI pooling (oracle_deform_roi_pool), caught by its pins.
 ROI_MUTANTS = [
     ("roi_swap_dx_dy", "dx = gamma * offset[((r * k + i) * k + j) * 2 + 0] * w;",
@@ -139,6 +158,8 @@ def test_unmodified_oracle_passes_pins(tmp_path):
     assert res.returncode == 0, res.stdout[-3000:]
     res = _run_pins(lib, "test_oracle_roi_pins.py")
     assert res.returncode == 0, res.stdout[-3000:]
+    res = _run_pins(lib, "test_oracle_v2_backward_pins.py")
+    assert res.returncode == 0, res.stdout[-3000:]
 
 
 @pytest.mark.parametrize("name,old,new,nth", MUTANTS, ids=[m[0] for m in MUTANTS])
@@ -172,3 +193,10 @@ def test_roi_pins_catch_mutant(tmp_path, name, old, new, nth):
     res = _run_pins(lib, "test_oracle_roi_pins.py")
     assert res.returncode != 0, "mutant %s survived the RoI pooling pins" % name
 
+
+@pytest.mark.parametrize("name,old,new,nth", V2_BWD_MUTANTS, ids=[m[0] for m in V2_BWD_MUTANTS])
+def test_v2_backward_pins_catch_mutant(tmp_path, name, old, new, nth):
+    text = _replace_nth(open(SRC).read(), old, new, nth)
+    lib = _build(text, tmp_path, name)
+    res = _run_pins(lib, "test_oracle_v2_backward_pins.py")
+    assert res.returncode != 0, "mutant %s survived the DCNv2 backward pins" % name
