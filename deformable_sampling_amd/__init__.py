@@ -26,6 +26,7 @@ STATUS = {0: "DCN_OK", 1: "DCN_ERR_NULL", 2: "DCN_ERR_SHAPE", 3: "DCN_ERR_PARAM"
 # every symbol include/dcn.h declares
 EXPORTS = ("dcn_core_forward", "dcn_core_forward_packed", "dcn_core_backward_workspace_bytes", "dcn_core_backward",
            "dcn_v2_workspace_bytes", "dcn_v2_forward", "dcn_v2_im2col",
+           "dcn_v2_backward_workspace_bytes", "dcn_v2_backward",
            "deform_agg_forward", "deform_agg_backward_workspace_bytes", "deform_agg_backward",
            "deform_roi_pool_forward",
            "dcn_status_string", "dcn_last_hip_error")
@@ -68,6 +69,10 @@ def load(path: str | None = None):
     lib.dcn_v2_workspace_bytes.argtypes = [i] * 13 + [i]
     lib.dcn_v2_forward.restype = i
     lib.dcn_v2_forward.argtypes = [vp, vp, vp, vp, vp, vp, _c.c_size_t] + [i] * 15 + [i, vp]
+    lib.dcn_v2_backward_workspace_bytes.restype = _c.c_size_t
+    lib.dcn_v2_backward_workspace_bytes.argtypes = [i] * 15
+    lib.dcn_v2_backward.restype = i
+    lib.dcn_v2_backward.argtypes = [vp] * 10 + [_c.c_size_t] + [i] * 16 + [vp]
     lib.dcn_v2_im2col.restype = i
     lib.dcn_v2_im2col.argtypes = [vp, vp, vp, vp, _c.c_size_t] + [i] * 15 + [i, vp]
     lib.deform_agg_forward.restype = i
@@ -299,6 +304,65 @@ def dcn_v2_forward(x, offset, mask, weight, out=None, workspace=None, *, stride=
           _ptr(workspace), workspace.numel() * workspace.element_size(), N, Cin, H, W, Cout, kh, kw,
           sh, sw, ph, pw, dh, dw, dg, int(bool(softmax)), _DTYPE_ID[x.dtype], _stream(stream))
     return out
+
+
+def dcn_v2_backward_workspace_bytes(N, Cin, H, W, Cout, kernel=(3, 3), stride=1, pad=1,
+                                    dilation=1, deform_groups=1, dtype=torch.bfloat16):
+    kh, kw = _pair(kernel)
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    dh, dw = _pair(dilation)
+    return int(load().dcn_v2_backward_workspace_bytes(N, Cin, H, W, Cout, kh, kw, sh, sw, ph, pw,
+                                                      dh, dw, int(deform_groups), _DTYPE_ID[dtype]))
+
+
+def dcn_v2_backward(x, offset, mask, weight, grad_out, *, stride=1, pad=1, dilation=1,
+                    deform_groups=None, softmax=False, need=("x", "offset", "mask", "weight"),
+                    workspace=None, stream=None):
+    """Gradients of dcn_v2_forward. Returns a dict with the requested entries of
+    grad_x [N,Cin,H,W] (x's dtype), grad_offset, grad_mask (fp32, shaped as offset and
+    mask; mask's shape [N,dg*K,Ho,Wo] when mask is None) and grad_weight (fp32)."""
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    dh, dw = _pair(dilation)
+    _check(x, "x")
+    _check(weight, "weight", x.dtype)
+    _check(grad_out, "grad_out", x.dtype)
+    _check(offset, "offset", torch.float32)
+    _check(mask, "mask", torch.float32, allow_none=True)
+    N, Cin, H, W = x.shape
+    Cout, Cin_w, kh, kw = weight.shape
+    if Cin_w != Cin:
+        raise ValueError("weight has %d input channels, x has %d" % (Cin_w, Cin))
+    K = kh * kw
+    dg = deform_groups if deform_groups is not None else offset.shape[1] // (2 * K)
+    Ho, Wo = out_size(H, kh, sh, ph, dh), out_size(W, kw, sw, pw, dw)
+    if tuple(offset.shape) != (N, dg * K * 2, Ho, Wo):
+        raise ValueError("offset must be [N, dg*K*2, Ho, Wo]")
+    if mask is not None and tuple(mask.shape) != (N, dg * K, Ho, Wo):
+        raise ValueError("mask must be [N, dg*K, Ho, Wo]")
+    if tuple(grad_out.shape) != (N, Cout, Ho, Wo):
+        raise ValueError("grad_out must be [N, Cout, Ho, Wo]")
+    dev = x.device
+    res = {}
+    if "x" in need:
+        res["grad_x"] = torch.empty_like(x)
+    if "offset" in need:
+        res["grad_offset"] = torch.empty((N, dg * K * 2, Ho, Wo), dtype=torch.float32, device=dev)
+    if "mask" in need:
+        res["grad_mask"] = torch.empty((N, dg * K, Ho, Wo), dtype=torch.float32, device=dev)
+    if "weight" in need:
+        res["grad_weight"] = torch.empty((Cout, Cin, kh, kw), dtype=torch.float32, device=dev)
+    nbytes = dcn_v2_backward_workspace_bytes(N, Cin, H, W, Cout, (kh, kw), (sh, sw), (ph, pw),
+                                             (dh, dw), dg, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _call("dcn_v2_backward", _ptr(x), _ptr(offset), _ptr(mask), _ptr(weight), _ptr(grad_out),
+          _ptr(res.get("grad_x")), _ptr(res.get("grad_offset")), _ptr(res.get("grad_mask")),
+          _ptr(res.get("grad_weight")), _ptr(workspace), workspace.numel() * workspace.element_size(),
+          N, Cin, H, W, Cout, kh, kw, sh, sw, ph, pw, dh, dw, dg, int(bool(softmax)),
+          _DTYPE_ID[x.dtype], _stream(stream))
+    return res
 
 
 def dcn_v2_im2col(x, offset, mask, Cout, workspace, *, kernel=(3, 3), stride=1, pad=1,

@@ -271,6 +271,70 @@ dcn_status dcn_v2_im2col(const void *x, const float *offset, const float *mask, 
                    softmax, dtype, stream, true);
 }
 
+// Shape checks and plan of the DCNv2 backward (the forward's limits).
+static dcn_status v2_bwd_plan(int N, int Cin, int H, int W, int Cout, int kh, int kw, int stride_h,
+                              int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                              int deform_groups, dcn_dtype dtype, dcn::V2BwdPlan &plan) {
+    if (!valid_dtype(dtype)) return DCN_ERR_DTYPE;
+    if (dtype == DCN_F32) return DCN_ERR_DTYPE;
+    if (N < 0 || Cin <= 0 || H <= 0 || W <= 0 || Cout <= 0) return DCN_ERR_SHAPE;
+    dcn_status st = check_window(kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w);
+    if (st != DCN_OK) return st;
+    if (deform_groups <= 0 || Cin % deform_groups != 0) return DCN_ERR_PARAM;
+    if (deform_groups > 1 && (Cin / deform_groups) % 8 != 0) return DCN_ERR_PARAM;
+    if (!dcn::plan_dcn_v2_bwd(N, Cin, H, W, Cout, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h,
+                              dil_w, deform_groups, dtype, plan))
+        return DCN_ERR_SHAPE;
+    // 32-bit limits: in-image offsets, pixel counts, bucket entries and sample ids
+    if ((long long)(H + 1) * (W + 1) * plan.Cin_pad > kI32) return DCN_ERR_SHAPE;
+    if (plan.Pp > kI32 || plan.entries > kI32 || plan.D > kI32) return DCN_ERR_SHAPE;
+    if ((long long)N * Cin * H * W > (1LL << 40)) return DCN_ERR_SHAPE;
+    return DCN_OK;
+}
+
+size_t dcn_v2_backward_workspace_bytes(int N, int Cin, int H, int W, int Cout, int kh, int kw,
+                                       int stride_h, int stride_w, int pad_h, int pad_w, int dil_h,
+                                       int dil_w, int deform_groups, dcn_dtype dtype) {
+    dcn::V2BwdPlan plan;
+    if (v2_bwd_plan(N, Cin, H, W, Cout, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w,
+                    deform_groups, dtype, plan) != DCN_OK)
+        return 0;
+    return plan.total;
+}
+
+dcn_status dcn_v2_backward(const void *x, const float *offset, const float *mask, const void *weight,
+                           const void *grad_out, void *grad_x, float *grad_offset, float *grad_mask,
+                           float *grad_weight, void *workspace, size_t workspace_bytes, int N,
+                           int Cin, int H, int W, int Cout, int kh, int kw, int stride_h,
+                           int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                           int deform_groups, int softmax, dcn_dtype dtype, hipStream_t stream) {
+    dcn::V2BwdPlan plan;
+    dcn_status st = v2_bwd_plan(N, Cin, H, W, Cout, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h,
+                                dil_w, deform_groups, dtype, plan);
+    if (st != DCN_OK) return st;
+    if (N == 0) return DCN_OK;
+    if (!x || !offset || !weight || !grad_out) return DCN_ERR_NULL;
+    if (!grad_x && !grad_offset && !grad_mask && !grad_weight) return DCN_OK;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < plan.total)
+        return DCN_ERR_WORKSPACE;
+    if (!aligned(x, 2) || !aligned(weight, 2) || !aligned(grad_out, 2) || !aligned(grad_x, 2) ||
+        !aligned(offset, 4) || (mask && !aligned(mask, 4)) || !aligned(grad_offset, 4) ||
+        !aligned(grad_mask, 4) || !aligned(grad_weight, 4))
+        return DCN_ERR_ALIGN;
+    dcn::V2BwdLaunch a;
+    a.x = x; a.offset = offset; a.mask = mask; a.weight = weight; a.grad_out = grad_out;
+    a.grad_x = grad_x; a.grad_offset = grad_offset; a.grad_mask = grad_mask;
+    a.grad_weight = grad_weight;
+    a.workspace = workspace;
+    a.N = N; a.Cin = Cin; a.H = H; a.W = W; a.Cout = Cout; a.kh = kh; a.kw = kw;
+    a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w; a.dh = dil_h; a.dw = dil_w;
+    a.dg = deform_groups;
+    a.softmax = softmax;
+    a.dtype = dtype;
+    a.plan = plan;
+    return hip_status(dcn::launch_dcn_v2_bwd(a, stream));
+}
+
 dcn_status deform_agg_forward(const void *feat, const int32_t *spatial_shape,
                               const int32_t *scale_start, const float *loc, const float *weights,
                               void *out, int B, int P_total, int A, int pts, int cams, int scales,

@@ -94,21 +94,6 @@ __device__ __forceinline__ float seg_max(float v, int S, int q) {
     return r;
 }
 
-// base + t -> corner c0 = base + floor(t), f = t - floor(t), u = (floor(t) + 1) - t.
-// Each of f and u is exact whenever it is below 1/2 (f = 1 + t rounds only for t in
-// (-1/2, 0), where u = -t is exact; u = 1 - t rounds only for t in (0, 1/2), where f
-// = t is exact), so both bilinear weight factors carry a relative error of at most
-// one rounding. Deriving u as 1 - f instead would give a small u an absolute error
-// of up to 2^-25, and a large relative one. |t| is clamped at 2^24 px as in the
-// forward.
-__device__ __forceinline__ void split_coord_fu(int base, float t, int &c0, float &f, float &u) {
-    t = fminf(fmaxf(t, -16777216.0f), 16777216.0f);
-    const float fl = floorf(t);
-    f = t - fl;
-    u = (fl + 1.0f) - t;
-    c0 = base + (int)fl;
-}
-
 // Corner geometry of one tap: integer corner (y0, x0), fractions f and their
 // complements u = 1 - f, and which of the four corners lie inside the image.
 struct TapGeo {

@@ -100,6 +100,36 @@ struct V2Launch {
 };
 hipError_t launch_dcn_v2(const V2Launch &a, hipStream_t stream);
 
+// DCNv2 backward (dcn_v2_bwd.hip). Workspace regions (byte offsets, 256-aligned):
+// xt [N,H,W,Cin_pad], wT [Rr][CoK], gcl [Pp][CoK], goT [CoM][Pp], colT [Rr][Pp] (dtype);
+// gcol [P][R], weight partials [splits][Cout][R] (fp32); bucket counts + fill cursors
+// [2][D], starts [D] (int32, D = N*H*W*dg); entries [P*dg*K*4] (8 bytes); gx_cl
+// [N,H,W,Cin_pad] fp32.
+struct V2BwdPlan {
+    int Ho, Wo, K, Cin_pad, R, Rr, CoK, CoM, splits;
+    long long P, Pp, D, entries;
+    size_t off_xt, off_wt, off_gcl, off_got, off_colt, off_gcol, off_wpart, off_cnt, off_starts,
+        off_entries, off_gxcl, total;
+};
+bool plan_dcn_v2_bwd(int N, int Cin, int H, int W, int Cout, int kh, int kw, int sh, int sw, int ph,
+                     int pw, int dh, int dw, int dg, dcn_dtype dtype, V2BwdPlan &plan);
+struct V2BwdLaunch {
+    const void *x;
+    const float *offset;
+    const float *mask;  // may be NULL
+    const void *weight;
+    const void *grad_out;
+    void *grad_x;         // may be NULL
+    float *grad_offset;   // may be NULL
+    float *grad_mask;     // may be NULL
+    float *grad_weight;   // may be NULL
+    void *workspace;
+    int N, Cin, H, W, Cout, kh, kw, sh, sw, ph, pw, dh, dw, dg, softmax;
+    dcn_dtype dtype;
+    V2BwdPlan plan;
+};
+hipError_t launch_dcn_v2_bwd(const V2BwdLaunch &a, hipStream_t stream);
+
 constexpr int kAggMaxMaps = 64;
 struct AggMaps {
     int H[kAggMaxMaps];

@@ -1,0 +1,296 @@
+// Pieces shared by the DCNv2 forward and backward, included inside namespace dcn's
+// anonymous namespace by each, after dcn_common.hpp: tile constants, the NCHW ->
+// channels-last transpose with the weight permutation, and the MFMA GEMM over
+// K-contiguous operands.
+#pragma once
+
+constexpr int kVec = 8;    // channel vector (16 bytes of bf16/fp16)
+constexpr int kBM = 128;   // GEMM tile: output channels
+constexpr int kBN = 128;   // GEMM tile: output pixels
+constexpr int kBK = 64;    // GEMM tile: reduction
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+long long round_up(long long v, long long m) { return (v + m - 1) / m * m; }
+
+// ------------------------------------------------------------------- prep --
+
+struct PrepParams {
+    int N, Cin, HW, Cin_pad;
+    int vec;  // 16-byte transpose path: HW % 8 == 0 and x 16-byte aligned
+    int Cout, K, Mp, Rp;
+    int n_tr_blocks;  // blocks doing the transpose; the rest permute the weight
+    int tiles_c, tiles_hw;
+};
+
+// Transpose of 64 channels x 64 pixels through LDS, or 8 weight elements per thread.
+__global__ __launch_bounds__(256) void v2_prep_kernel(const uint16_t *__restrict__ x,
+                                                      const uint16_t *__restrict__ w,
+                                                      uint16_t *__restrict__ xt,
+                                                      uint16_t *__restrict__ wp, PrepParams p) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // [channel][pixel], 144-byte rows
+    const int b = blockIdx.x;
+    if (b < p.n_tr_blocks) {
+        const int tc = b % p.tiles_c;
+        const int th = (b / p.tiles_c) % p.tiles_hw;
+        const int n = b / (p.tiles_c * p.tiles_hw);
+        const int c0 = tc * 64, hw0 = th * 64;
+        const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+        const uint16_t *xn = x + (size_t)n * p.Cin * p.HW;
+        if (p.vec) {
+            // 16-byte accesses: a thread loads 8 pixels of one channel, then stores 8
+            // channels of one pixel
+            const int q = threadIdx.x & 7, r = threadIdx.x >> 3;  // 8 chunks x 32 rows
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int c = c0 + r + 32 * j, hw = hw0 + q * kVec;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (c < p.Cin && hw < p.HW)
+                    v = *reinterpret_cast<const uint4 *>(xn + (size_t)c * p.HW + hw);
+                *reinterpret_cast<uint4 *>(&tile[r + 32 * j][q * kVec]) = v;
+            }
+            __syncthreads();
+            uint16_t *xtn = xt + (size_t)n * p.HW * p.Cin_pad;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int hw = hw0 + r + 32 * j, c = c0 + q * kVec;
+                uint16_t e[kVec];
+#pragma unroll
+                for (int i = 0; i < kVec; ++i) e[i] = tile[q * kVec + i][r + 32 * j];
+                uint4 v;
+                __builtin_memcpy(&v, e, 16);
+                if (hw < p.HW && c < p.Cin_pad)
+                    *reinterpret_cast<uint4 *>(xtn + (size_t)hw * p.Cin_pad + c) = v;
+            }
+            return;
+        }
+        for (int cy = ty; cy < 64; cy += 4) {
+            const int c = c0 + cy, hw = hw0 + tx;
+            tile[cy][tx] = (c < p.Cin && hw < p.HW) ? xn[(size_t)c * p.HW + hw] : (uint16_t)0;
+        }
+        __syncthreads();
+        uint16_t *xtn = xt + (size_t)n * p.HW * p.Cin_pad;
+        for (int py = ty; py < 64; py += 4) {
+            const int hw = hw0 + py, c = c0 + tx;
+            if (hw < p.HW && c < p.Cin_pad) xtn[(size_t)hw * p.Cin_pad + c] = tile[tx][py];
+        }
+        return;
+    }
+    // weight: wp[co][k*Cin_pad + ci] = w[co][ci][k]; 8 consecutive r per thread
+    const long long t = (long long)(b - p.n_tr_blocks) * 256 + threadIdx.x;
+    const int rv = p.Rp / kVec;
+    if (t >= (long long)p.Mp * rv) return;
+    const int co = (int)(t / rv);
+    const int r0 = (int)(t % rv) * kVec;
+    uint16_t v[kVec];
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+        const int r = r0 + i;
+        const int k = r / p.Cin_pad, ci = r % p.Cin_pad;
+        v[i] = (co < p.Cout && k < p.K && ci < p.Cin) ? w[((size_t)co * p.Cin + ci) * p.K + k]
+                                                      : (uint16_t)0;
+    }
+    uint4 o;
+    __builtin_memcpy(&o, v, 16);
+    *reinterpret_cast<uint4 *>(wp + (size_t)co * p.Rp + r0) = o;
+}
+
+// ------------------------------------------------------------------- gemm --
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <class E>
+__device__ __forceinline__ f32x16_t mfma32(const uint4 &a, const uint4 &b, f32x16_t c) {
+    if constexpr (E::id == DCN_BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// C[m][n] = sum_k A[m][k] * B[n][k] over 128 x 128 tiles; A and B hold K contiguous
+// (row strides lda, ldb, rows padded to whole tiles, K to whole 64-deep steps).
+// Split-K: block (mt, nt, split) takes K steps [split*nk, min((split+1)*nk, nk_total)).
+// MODE 0 stores out[img][m][hw] in the input dtype (n = img*HWo + hw, m < Cout,
+// n < P: the DCNv2 forward's NCHW output); MODE 1 stores fp32 out[split*split_stride +
+// m*ldc + n] for m < Mstore, n < Nstore.
+struct GemmParams {
+    int lda, ldb, nk, nk_total;
+    int Mtiles, Ntiles, nblocks;
+    int Cout, HWo;
+    long long P;
+    int ldc, Mstore, Nstore;
+    long long split_stride;
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// s_waitcnt with only the vector-memory counter constrained to <= n (gfx9 encoding).
+#define V2_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
+
+constexpr int kStages = 4;                          // K tiles in flight (LDS ring)
+constexpr int kTileChunks = kBM * kBK / 8;          // 16-byte chunks per operand tile (1024)
+// Waves per GEMM block: 8 (2 x 4, 64 x 32 each: two per SIMD, so one wave's LDS
+// waits overlap the other's MFMAs) or 4 (2 x 2, 64 x 64 each).
+#ifndef DCN_V2_GEMM_WAVES
+#define DCN_V2_GEMM_WAVES 8
+#endif
+constexpr int kGemmWaves = DCN_V2_GEMM_WAVES;
+constexpr int kGemmThreads = 64 * kGemmWaves;
+constexpr int kDmaPerWave = kTileChunks / kGemmThreads;  // direct-to-LDS copies per wave per operand
+constexpr int kWaveN = kBN / (kGemmWaves / 2);           // pixels per wave (64 or 32)
+constexpr int kTB = kWaveN / 32;                         // 32-wide MFMA tiles per wave along N
+
+// Operand tiles live in LDS as [128 rows][8 chunks of 8 elements], chunk cc of row r
+// stored at position cc ^ ((r >> 1) & 7). A 16-byte read by 64 lanes is served 16 lanes
+// (256 bytes, all 64 banks) at a time; the 16 lanes of a fragment read take 16
+// consecutive rows of one logical chunk, and the swizzle puts them on 16 different
+// 16-byte bank groups (two rows share a 256-byte bank period).
+__shared__ uint4 s_gA0[kTileChunks], s_gA1[kTileChunks], s_gA2[kTileChunks], s_gA3[kTileChunks];
+__shared__ uint4 s_gB0[kTileChunks], s_gB1[kTileChunks], s_gB2[kTileChunks], s_gB3[kTileChunks];
+template <int S> __device__ __forceinline__ uint4 *ring_a() {
+    if constexpr (S == 0) return s_gA0;
+    else if constexpr (S == 1) return s_gA1;
+    else if constexpr (S == 2) return s_gA2;
+    else return s_gA3;
+}
+template <int S> __device__ __forceinline__ uint4 *ring_b() {
+    if constexpr (S == 0) return s_gB0;
+    else if constexpr (S == 1) return s_gB1;
+    else if constexpr (S == 2) return s_gB2;
+    else return s_gB3;
+}
+static_assert(kStages == 4, "the ring has four named slots");
+
+// Copy a 128 x 64 operand tile (rows row0.., reduction k0..k0+63) into an LDS ring slot:
+// wave w, copy i moves LDS chunks (i*W + w)*64 + lane, i.e. row c >> 3, position c & 7.
+__device__ __forceinline__ void gemm_dma(uint4 *slot, const uint16_t *g, int ld, int k0) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+        const int c = (i * kGemmWaves + w) * 64 + lane;
+        const int row = c >> 3, pos = c & 7;
+        const int cc = pos ^ ((row >> 1) & 7);
+        const uint16_t *src = g + (size_t)row * ld + k0 + cc * 8;
+        lds_copy16(lds_addr(slot + (i * kGemmWaves + w) * 64), src);
+    }
+}
+
+// One K step from ring slot S: wait until its tile has landed, barrier, refill the slot
+// the previous step used with tile kt + kStages - 1, then 4 x (2 x kTB) MFMAs.
+template <class E, int S>
+__device__ __forceinline__ void gemm_step(int kt, int nk, const uint16_t *ga, const uint16_t *gb, int lda,
+                                          int ldb, f32x16_t (&acc)[2][kTB], int wm, int wn, int frow,
+                                          int fhalf) {
+    if (kt >= nk) return;
+    // this wave's copies issued after tile kt: min(nk-1-kt, kStages-2) tiles x 2 operands
+    const int after = (nk - 1 - kt) < (kStages - 2) ? (nk - 1 - kt) : (kStages - 2);
+    if (after >= 2) V2_WAIT_VMCNT(2 * 2 * kDmaPerWave);
+    else if (after == 1) V2_WAIT_VMCNT(1 * 2 * kDmaPerWave);
+    else V2_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();  // all waves: tile kt in LDS, tile kt-1 consumed
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    const int nx = kt + kStages - 1;
+    if (nx < nk) {
+        constexpr int R = (S + kStages - 1) % kStages;
+        gemm_dma(ring_a<R>(), ga, lda, nx * kBK);
+        gemm_dma(ring_b<R>(), gb, ldb, nx * kBK);
+    }
+    const uint4 *sa = ring_a<S>();
+    const uint4 *sb = ring_b<S>();
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+        const int cc = 2 * ks + fhalf;
+        uint4 fa[2], fb[kTB];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int ra = wm * 64 + t * 32 + frow;
+            fa[t] = sa[ra * 8 + (cc ^ ((ra >> 1) & 7))];
+        }
+#pragma unroll
+        for (int t = 0; t < kTB; ++t) {
+            const int rb = wn * kWaveN + t * 32 + frow;
+            fb[t] = sb[rb * 8 + (cc ^ ((rb >> 1) & 7))];
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < kTB; ++b) acc[a][b] = mfma32<E>(fa[a], fb[b], acc[a][b]);
+    }
+}
+
+// One 128 x 128 tile of C (see GemmParams); the waves form a 2 x (W/2) grid, each
+// 64 x kWaveN = 2 x kTB v_mfma_f32_32x32x16 tiles with fp32 accumulators. The K loop
+// runs over a kStages-deep ring of LDS tiles filled by direct global->LDS copies, so
+// HBM/L2 latency overlaps the MFMA work of the previous stages.
+template <class E, int MODE>
+__global__ __launch_bounds__(kGemmThreads) void v2_gemm_kernel(const uint16_t *__restrict__ A,
+                                                      const uint16_t *__restrict__ B,
+                                                      void *__restrict__ out, GemmParams p) {
+    const int blk = xcd_remap((int)blockIdx.x, p.nblocks);
+    const int mt = blk % p.Mtiles, rest = blk / p.Mtiles;
+    const int nt = rest % p.Ntiles, split = rest / p.Ntiles;
+    const int m0 = mt * kBM;
+    const long long n0 = (long long)nt * kBN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave & 1, wn = wave >> 1;  // 2 x (W/2) waves, 64 x kWaveN each
+    const int kt0 = split * p.nk;
+    const int nk = min(p.nk, p.nk_total - kt0);
+    const uint16_t *ga = A + (size_t)m0 * p.lda + (size_t)kt0 * kBK;
+    const uint16_t *gb = B + (size_t)n0 * p.ldb + (size_t)kt0 * kBK;
+
+    f32x16_t acc[2][kTB];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < kTB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+    // prologue: tiles 0 .. kStages-2 in flight
+    if (0 < nk) { gemm_dma(ring_a<0>(), ga, p.lda, 0); gemm_dma(ring_b<0>(), gb, p.ldb, 0); }
+    if (1 < nk) { gemm_dma(ring_a<1>(), ga, p.lda, kBK); gemm_dma(ring_b<1>(), gb, p.ldb, kBK); }
+    if (2 < nk) { gemm_dma(ring_a<2>(), ga, p.lda, 2 * kBK); gemm_dma(ring_b<2>(), gb, p.ldb, 2 * kBK); }
+    // fragment of lane l in a 16-deep k step ks: row (l % 32), logical chunk 2*ks + l/32
+    const int frow = lane & 31, fhalf = lane >> 5;
+    for (int kt = 0; kt < nk; kt += kStages) {
+        gemm_step<E, 0>(kt + 0, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
+        gemm_step<E, 1>(kt + 1, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
+        gemm_step<E, 2>(kt + 2, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
+        gemm_step<E, 3>(kt + 3, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
+    }
+
+    // epilogue: D[i][j] of a 32x32 tile sits in lane j + 32*((i/4)%2), register
+    // 4*(i/8) + i%4. Row i indexes m, column j indexes n.
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+        for (int b = 0; b < kTB; ++b) {
+            const long long n = n0 + wn * kWaveN + b * 32 + (lane & 31);
+            if constexpr (MODE == 0) {
+                if (n >= p.P) continue;
+                const long long nimg = n / p.HWo;
+                const int hw = (int)(n - nimg * p.HWo);
+                typename E::bits *o = static_cast<typename E::bits *>(out);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int co = m0 + wm * 64 + a * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                    if (co < p.Cout) o[((size_t)nimg * p.Cout + co) * p.HWo + hw] = from_f32(E{}, acc[a][b][r]);
+                }
+            } else {
+                if (n >= p.Nstore) continue;
+                float *o = static_cast<float *>(out) + (size_t)split * p.split_stride;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + wm * 64 + a * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                    if (m < p.Mstore) o[(size_t)m * p.ldc + n] = acc[a][b][r];
+                }
+            }
+        }
+    }
+}
+

@@ -9,6 +9,7 @@
  *   dcn_v2_forward      DCNv2 modulated deformable convolution, NCHW: deform-im2col
  *                       and an MFMA GEMM (fused, or in two stages through the workspace).
  *   dcn_v2_im2col       the deform-im2col stage alone: columns into the workspace.
+ *   dcn_v2_backward     gradients of DCNv2 w.r.t. x, offsets, masks and the weight.
  *   deform_agg_forward  Sparse4D-style multi-camera, multi-scale aggregation.
  *   deform_agg_backward gradients of the aggregation w.r.t. features, locations, weights.
  *   deform_roi_pool_forward  deformable RoI pooling, channels-last.
@@ -217,6 +218,45 @@ dcn_status dcn_v2_im2col(const void *x, const float *offset, const float *mask, 
                          int kw, int stride_h, int stride_w, int pad_h, int pad_w, int dil_h,
                          int dil_w, int deform_groups, int softmax, dcn_dtype dtype,
                          hipStream_t stream);
+
+/*
+ * Workspace bytes dcn_v2_backward needs (0 if the sizes are invalid). Regions, each
+ * 256-byte aligned: x channels-last, the weight transposed, grad_out channels-last
+ * and pixel-major, the forward's columns transposed (dtype); the column gradient
+ * [N*Ho*Wo][K*Cin_pad] and split partial sums of the weight gradient (fp32); bucket
+ * counters and entries of the grad_x gather; an fp32 channels-last grad_x.
+ */
+size_t dcn_v2_backward_workspace_bytes(int N, int Cin, int H, int W, int Cout, int kh, int kw,
+                                       int stride_h, int stride_w, int pad_h, int pad_w,
+                                       int dil_h, int dil_w, int deform_groups, dcn_dtype dtype);
+
+/*
+ * Gradients of dcn_v2_forward (the derivative of the modulated deformable
+ * convolution of "DCNv2 in YOLOv5" (cyqw.cn), section 1, with the bilinear kernel of
+ * "Hands-on DCNv1 in PyTorch", section 2; the pages print no backward pass).
+ * Inputs as dcn_v2_forward, plus
+ *   grad_out     [N, Cout, Ho, Wo]        dtype
+ * Outputs (any may be NULL to skip it; each is fully overwritten):
+ *   grad_x       [N, Cin, H, W]           dtype (fp32 accumulation, one rounding)
+ *   grad_offset  [N, dg*K*2, Ho, Wo]      fp32
+ *   grad_mask    [N, dg*K, Ho, Wo]        fp32, w.r.t. the mask argument (the logits
+ *                                         with softmax); with mask == NULL w.r.t. the
+ *                                         implied modulation (ones; zero logits)
+ *   grad_weight  [Cout, Cin, kh, kw]      fp32
+ * grad_weight contracts grad_out with the columns as the forward forms them (rounded
+ * to dtype); the column gradient sum_co weight * grad_out is kept in fp32 for the
+ * sampling derivative. At an integer position the derivative w.r.t. the offset is
+ * taken from the cell floor() selects. grad_x sums its contributions in an order set
+ * by atomic bucket filling, so its last bits may differ between runs. Limits as
+ * dcn_v2_forward, and N*Ho*Wo*dg*K*4 < 2^31.
+ */
+dcn_status dcn_v2_backward(const void *x, const float *offset, const float *mask,
+                           const void *weight, const void *grad_out, void *grad_x,
+                           float *grad_offset, float *grad_mask, float *grad_weight,
+                           void *workspace, size_t workspace_bytes, int N, int Cin, int H, int W,
+                           int Cout, int kh, int kw, int stride_h, int stride_w, int pad_h,
+                           int pad_w, int dil_h, int dil_w, int deform_groups, int softmax,
+                           dcn_dtype dtype, hipStream_t stream);
 
 /*
  * Multi-camera, multi-scale deformable aggregation (Sparse4D).

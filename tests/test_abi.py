@@ -282,3 +282,42 @@ def test_core_packed_validation(lib):
     assert core_packed(lib, om=A + 2, om_dtype=0) == ALIGN
     assert lib.dcn_last_hip_error() == 0
 
+
+
+def v2b(lib, x=A, off=A, mask=A, w=A, go=A, gx=A, goff=A, gm=A, gw=A, ws=A, wsb=1 << 40, N=1,
+        Cin=16, H=8, W=8, Cout=8, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, dg=1, softmax=0,
+        dtype=2):
+    return lib.dcn_v2_backward(x, off, mask, w, go, gx, goff, gm, gw, ws, wsb, N, Cin, H, W, Cout,
+                               kh, kw, sh, sw, ph, pw, dh, dw, dg, softmax, dtype, None)
+
+
+def test_v2_backward_workspace_bytes(lib):
+    a256 = lambda v: (v + 255) // 256 * 256
+    n = lib.dcn_v2_backward_workspace_bytes(8, 256, 40, 40, 256, 3, 3, 1, 1, 1, 1, 1, 1, 1, 2)
+    P, R, D = 12800, 2304, 8 * 40 * 40
+    splits = 7  # 2 x 18 output tiles of the weight gradient -> 256 // 36 splits over 200 K steps
+    want = (a256(8 * 40 * 40 * 256 * 2) + a256(2304 * 256 * 2) + a256(P * 256 * 2)
+            + a256(256 * P * 2) + a256(2304 * P * 2) + a256(P * R * 4) + a256(splits * 256 * R * 4)
+            + a256(D * 8) + a256(D * 4) + a256(P * 9 * 4 * 8) + a256(8 * 40 * 40 * 256 * 4))
+    assert n == want
+    assert lib.dcn_v2_backward_workspace_bytes(1, 3, 5, 5, 2, 3, 3, 1, 1, 1, 1, 1, 1, 1, 1) > 0
+    assert lib.dcn_v2_backward_workspace_bytes(1, 3, 5, 5, 2, 3, 3, 1, 1, 1, 1, 1, 1, 1, 0) == 0
+    assert lib.dcn_v2_backward_workspace_bytes(1, 16, 5, 5, 2, 3, 3, 1, 1, 1, 1, 1, 1, 3, 2) == 0
+
+
+def test_v2_backward_validation(lib):
+    assert v2b(lib, dtype=0) == DTYPE
+    assert v2b(lib, N=-1) == SHAPE
+    assert v2b(lib, kh=9, kw=9) == SHAPE
+    assert v2b(lib, dg=3) == PARAM
+    assert v2b(lib, Cin=24, dg=2) == PARAM
+    assert v2b(lib, N=0) == OK
+    assert v2b(lib, x=None) == NULL
+    assert v2b(lib, go=None) == NULL
+    assert v2b(lib, gx=None, goff=None, gm=None, gw=None) == OK  # nothing requested
+    assert v2b(lib, ws=None) == WORKSPACE
+    need = lib.dcn_v2_backward_workspace_bytes(1, 16, 8, 8, 8, 3, 3, 1, 1, 1, 1, 1, 1, 1, 2)
+    assert v2b(lib, wsb=need - 1) == WORKSPACE
+    assert v2b(lib, gx=A + 1) == ALIGN
+    assert v2b(lib, gw=A + 2) == ALIGN
+    assert lib.dcn_last_hip_error() == 0

@@ -149,6 +149,18 @@ def v2_case(*, N, Cin, H, W, Cout, kh=3, kw=3, stride=(1, 1), pad=(1, 1), dil=(1
         dtype=dtype, softmax=(mask == "logits"))
 
 
+def v2_grad_out(c, seed=0, kind="normal"):
+    """An upstream gradient for the DCNv2 output [N, Cout, Ho, Wo] in x's dtype: N(0,1)
+    draws (or small integers for kind="int") from their own seeded stream."""
+    r = rng(seed + 7927)
+    shape = (c["N"], c["Cout"], c["Ho"], c["Wo"])
+    if kind == "int":
+        g = r.integers(-3, 4, size=shape).astype(np.float64)
+    else:
+        g = r.standard_normal(shape)
+    return _t(g, c["dtype"])
+
+
 def agg_case(*, B, shapes, A, pts, G, Cg, dtype="f32", weights="logits", seed=0,
              cam_major=True, loc_lo=0.0, loc_hi=1.0):
     """Inputs of the multi-camera multi-scale aggregation.
