@@ -12,7 +12,7 @@ object of the core kernel (algorithmic bytes per launch / HIP-event launch time 
 other ops (DCNv4/DCNv3 small maps, the core backward, DCNv2 im2col + MFMA GEMM,
 aggregation forward and backward, deformable RoI pooling).
 
-  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--only core|bwd|aggbwd]
+  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--only core|bwd|aggbwd|v2bwd]
   python bench.py --calib-copy     # plain copy of known size, for counter scaling
 """
 from __future__ import annotations
@@ -227,6 +227,46 @@ def bench_v2(dsa, torch, timer, iters, warmup):
                 note="three launches: layout prep, deform-im2col, MFMA GEMM")
 
 
+def bench_v2_bwd(dsa, torch, timer, iters, warmup):
+    """dcn_v2_backward (grad x, offsets, masks, weight) on the 8x256x40x40 bf16 layer:
+    the whole call (layouts, transposed columns, two MFMA GEMMs, bucket count/scan,
+    sample pass, destination gather, NCHW grad_x)."""
+    import workloads as wl
+    name = "dcnv2_bf16_n8_c256_40x40"
+    c = wl.make(name)
+    dev = lambda t: None if t is None else t.to("cuda").contiguous()
+    x, off, m, w = dev(c["x"]), dev(c["offset"]), dev(c["mask"]), dev(c["weight"])
+    go = dev(wl.v2_grad_out(c, seed=502))
+    N, Cin, H, W, Cout = c["N"], c["Cin"], c["H"], c["W"], c["Cout"]
+    Ho, Wo = c["Ho"], c["Wo"]
+    need = dsa.dcn_v2_backward_workspace_bytes(N, Cin, H, W, Cout, dtype=torch.bfloat16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    gx = torch.empty_like(x)
+    goff = torch.empty_like(off)
+    gm = torch.empty_like(m)
+    gw = torch.empty((Cout, Cin, 3, 3), dtype=torch.float32, device="cuda")
+    lib = dsa.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    args = (x.data_ptr(), off.data_ptr(), m.data_ptr(), w.data_ptr(), go.data_ptr(), gx.data_ptr(),
+            goff.data_ptr(), gm.data_ptr(), gw.data_ptr(), ws.data_ptr(), need, N, Cin, H, W, Cout,
+            3, 3, 1, 1, 1, 1, 1, 1, 1, 0, 2, stream)
+
+    def call():
+        st = lib.dcn_v2_backward(*args)
+        if st:
+            raise RuntimeError("dcn_v2_backward status %d" % st)
+    wall, kern = timer.run(call, iters, warmup)
+    P = N * Ho * Wo
+    flops = 2 * 2.0 * Cout * Cin * 9 * P  # column gradient + weight gradient
+    # inputs read once (x, offsets, masks, weight, grad_out), gradients written once
+    nbytes = (2 * x.numel() * 2 + 2 * off.numel() * 4 + 2 * m.numel() * 4 + w.numel() * 2
+              + gw.numel() * 4 + go.numel() * 2)
+    return dict(workload=name + " backward", taps=P * 9, algo_bytes=nbytes, flops=flops,
+                wall_s=wall, kernel_s=kern, tflops=flops / kern / 1e12,
+                mfma_frac=flops / kern / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                gbs=nbytes / kern / 1e9, frac=nbytes / kern / 1e9 / HBM_PEAK_GBS)
+
+
 def bench_agg(dsa, torch, timer, iters, warmup, softmax=True):
     import workloads as wl
     name = "agg_f32_6cam_4scale_a900p13_g8c32"
@@ -379,7 +419,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["core", "all", "bwd", "aggbwd"], default="all")
+    ap.add_argument("--only", choices=["core", "all", "bwd", "aggbwd", "v2bwd"], default="all")
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -398,6 +438,10 @@ def main():
         return
     timer = Timer(torch)
 
+    if args.only == "v2bwd":  # the DCNv2 backward alone (for profiling)
+        r = bench_v2_bwd(dsa, torch, timer, args.steps, args.warmup)
+        log("dcnv2 backward: %.2f us/call" % (r["kernel_s"] * 1e6))
+        return
     if args.only == "aggbwd":  # the aggregation backward alone (for profiling)
         r = bench_agg_bwd(dsa, torch, timer, args.steps, args.warmup)
         log("aggregation backward: %.2f us/call" % (r["kernel_s"] * 1e6))
@@ -421,6 +465,8 @@ def main():
         log("core backward done")
         extra.append(bench_v2(dsa, torch, timer, 100, 10))
         log("dcnv2 done")
+        extra.append(bench_v2_bwd(dsa, torch, timer, 50, 5))
+        log("dcnv2 backward done")
         extra.append(bench_agg(dsa, torch, timer, 100, 10, softmax=True))
         extra.append(bench_agg(dsa, torch, timer, 100, 10, softmax=False))
         extra.append(bench_agg_bwd(dsa, torch, timer, 20, 3))
