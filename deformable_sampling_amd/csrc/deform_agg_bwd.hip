@@ -16,11 +16,13 @@
 // Mapping: one wavefront per (anchor, group) unit, units group-major (as the
 // forward). A round takes 64/scales (point, camera) pairs: each lane first turns one
 // sample into an LDS record (clamped corner offsets, validity, fractions and their
-// exact complements, wt); then slices of S lanes (one channel per lane, S >= Cg a
-// power of two) walk the records: four corner loads, the partial dots D_ab, and the
-// feature gradient as fp32 atomic adds of wt * w_ab * G_c (one slice's adds cover a
-// contiguous run of channels); the dots are summed over the slice and the sample's
-// g_t, grad_u, grad_v go to LDS. The owner lane of each (point, camera) sums its
+// exact complements, wt); then slices of S lanes (V = 4, 2 or 1 channels per lane,
+// S*V >= Cg, S a power of two) walk the records: four V-wide corner loads and the
+// partial dots D_ab, summed over the slice into the sample's g_t, grad_u, grad_v in
+// LDS. The feature gradient follows each batch of records as fp32 atomic adds of
+// wt * w_ab * G_c laid out for the atomics instead: half a wavefront per corner, 32
+// contiguous channels per half (G from LDS), two instructions per record. The owner
+// lane of each (point, camera) sums its
 // scales and stores that group's grad_loc partial; the lane that built a sample
 // stores its g_t (and, with softmax, rewrites it as wt (g_t - sum_j wj g_j) once
 // the sum is known). A second kernel adds the G partials of grad_loc in group order.
@@ -73,7 +75,7 @@ __device__ __forceinline__ void split_fu(float t, int &c0, float &f, float &u) {
     c0 = (int)fl;
 }
 
-template <class E>
+template <class E, int V>
 __global__ __launch_bounds__(kThreads) void agg_bwd_kernel(
     const typename E::bits *__restrict__ feat, const float *__restrict__ loc,
     const float *__restrict__ weights, const typename E::bits *__restrict__ gout,
@@ -82,6 +84,7 @@ __global__ __launch_bounds__(kThreads) void agg_bwd_kernel(
     __shared__ int s_h[kAggMaxMaps], s_w[kAggMaxMaps], s_start[kAggMaxMaps];
     __shared__ AggRec s_rec[kWaves][64];
     __shared__ float s_res[kWaves][64][3];  // g_t, grad_u, grad_v per record
+    __shared__ float s_g[kWaves][64 * kMaxRounds];  // the unit's grad_out (atomic path)
 
     const int nmaps = p.cams * p.scales;
     for (int i = threadIdx.x; i < nmaps; i += kThreads) {
@@ -119,15 +122,20 @@ __global__ __launch_bounds__(kThreads) void agg_bwd_kernel(
         for (int t = lane; t < T; t += 64) e += expf(wrow[(size_t)t * p.G] - mx);
         inv = 1.0f / wsum(e);
     }
-    // this lane's channels of G
-    float gc[kMaxRounds];
+    // this lane's channels of G for the loads: channels (cr*S + s)*V + u; for the
+    // atomic adds the whole of G waits in LDS
+    constexpr int RM = kMaxRounds / V;  // Cg <= 512 = 64 * kMaxRounds
+    float gc[RM][V];
 #pragma unroll
-    for (int r = 0; r < kMaxRounds; ++r) {
-        const int c = r * p.S + s;
-        gc[r] = (r < p.crounds && c < p.Cg)
-                    ? to_f32(E{}, gout[(size_t)ba * GC + g * p.Cg + c])
-                    : 0.0f;
-    }
+    for (int r = 0; r < RM; ++r)
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            const int c = (r * p.S + s) * V + u;
+            gc[r][u] = (r < p.crounds && c < p.Cg) ? to_f32(E{}, gout[(size_t)ba * GC + g * p.Cg + c]) : 0.0f;
+        }
+    float *sg = s_g[wv];
+    if (ab)
+        for (int c = lane; c < p.Cg; c += 64) sg[c] = to_f32(E{}, gout[(size_t)ba * GC + g * p.Cg + c]);
 
     const int per_round = p.npc * p.scales;  // records per round (<= 64)
     float dot = 0.0f;                        // sum_t wt g_t over this lane's samples
@@ -181,20 +189,22 @@ __global__ __launch_bounds__(kThreads) void agg_bwd_kernel(
                 const float w10 = ((r.valid & 4) ? r.fy * r.ux : 0.0f) * r.wt;
                 const float w11 = ((r.valid & 8) ? r.fy * r.fx : 0.0f) * r.wt;
 #pragma unroll
-                for (int cr = 0; cr < kMaxRounds; ++cr) {
+                for (int cr = 0; cr < RM; ++cr) {
                     if (cr >= p.crounds) break;
-                    const int c = cr * p.S + s;
-                    if (c < p.Cg) {
-                        const float G = gc[cr];
-                        D00 = fmaf(G, to_f32(E{}, fb[r.o00 + c]), D00);
-                        D01 = fmaf(G, to_f32(E{}, fb[r.o01 + c]), D01);
-                        D10 = fmaf(G, to_f32(E{}, fb[r.o10 + c]), D10);
-                        D11 = fmaf(G, to_f32(E{}, fb[r.o11 + c]), D11);
-                        if (ab) {
-                            if (w00 != 0.0f) unsafeAtomicAdd(ab + r.o00 + c, w00 * G);
-                            if (w01 != 0.0f) unsafeAtomicAdd(ab + r.o01 + c, w01 * G);
-                            if (w10 != 0.0f) unsafeAtomicAdd(ab + r.o10 + c, w10 * G);
-                            if (w11 != 0.0f) unsafeAtomicAdd(ab + r.o11 + c, w11 * G);
+                    const int c = (cr * p.S + s) * V;
+                    if (c < p.Cg) {  // Cg % V == 0: the whole vector is in range
+                        float a[V], b[V], cc[V], d[V];
+                        load_f32<E, V>(fb + r.o00 + c, a);
+                        load_f32<E, V>(fb + r.o01 + c, b);
+                        load_f32<E, V>(fb + r.o10 + c, cc);
+                        load_f32<E, V>(fb + r.o11 + c, d);
+#pragma unroll
+                        for (int u = 0; u < V; ++u) {
+                            const float G = gc[cr][u];
+                            D00 = fmaf(G, a[u], D00);
+                            D01 = fmaf(G, b[u], D01);
+                            D10 = fmaf(G, cc[u], D10);
+                            D11 = fmaf(G, d[u], D11);
                         }
                     }
                 }
@@ -210,6 +220,26 @@ __global__ __launch_bounds__(kThreads) void agg_bwd_kernel(
                 res[j][0] = r.uy * (r.ux * d00 + r.fx * d01) + r.fy * (r.ux * d10 + r.fx * d11);
                 res[j][1] = r.wt * r.Ws * (r.uy * (d01 - d00) + r.fy * (d11 - d10));
                 res[j][2] = r.wt * r.Hs * (r.ux * (d10 - d00) + r.fx * (d11 - d01));
+            }
+            // feature gradient of these Z records: per record two atomic instructions,
+            // each covering two corners with 32 contiguous channels apiece
+            if (ab) {
+                const int half = lane >> 5, cl = lane & 31;
+                for (int jj = 0; jj < p.Z; ++jj) {
+                    const int jr = j0 + jj;
+                    if (jr >= nrec) break;
+                    const AggRec q = rec[jr];
+                    const float wy = half ? q.fy : q.uy;
+                    const bool va = (q.valid >> (2 * half)) & 1, vb = (q.valid >> (2 * half + 1)) & 1;
+                    const float wa = (va ? wy * q.ux : 0.0f) * q.wt;
+                    const float wb = (vb ? wy * q.fx : 0.0f) * q.wt;
+                    const int oa = half ? q.o10 : q.o00, ob = half ? q.o11 : q.o01;
+                    for (int c = cl; c < p.Cg; c += 32) {
+                        const float G = sg[c];
+                        if (wa != 0.0f) unsafeAtomicAdd(ab + oa + c, wa * G);
+                        if (wb != 0.0f) unsafeAtomicAdd(ab + ob + c, wb * G);
+                    }
+                }
             }
         }
         // ---- per-sample and per-(point, camera) results (a wavefront's own LDS
@@ -283,11 +313,15 @@ hipError_t launch_e(const AggBwdLaunch &a, const AggBwdPlan &pl, hipStream_t str
     p.B = a.B; p.P_total = a.P_total; p.A = a.A; p.pts = a.pts; p.cams = a.cams;
     p.scales = a.scales; p.G = a.G; p.Cg = a.Cg; p.softmax = a.softmax ? 1 : 0;
     p.maps = a.maps;
+    constexpr int elt = (int)sizeof(typename E::bits);
+    int V = 4;  // channel vector of the corner loads: V | Cg, feat 4*V-byte aligned
+    while (V > 1 && (a.Cg % V != 0 || ((uintptr_t)a.feat % (V * elt)) != 0)) V >>= 1;
+    const int lanes = (a.Cg + V - 1) / V;
     int S = 1;
-    while (S < a.Cg && S < 64) S <<= 1;
+    while (S < lanes && S < 64) S <<= 1;
     p.S = S;
     p.Z = 64 / S;
-    p.crounds = (a.Cg + S - 1) / S;
+    p.crounds = (lanes + S - 1) / S;
     p.npc = 64 / a.scales;
     p.BA = a.B * a.A;
     p.nunits = p.BA * a.G;
@@ -306,10 +340,16 @@ hipError_t launch_e(const AggBwdLaunch &a, const AggBwdPlan &pl, hipStream_t str
         hipLaunchKernelGGL(agg_zero_kernel, dim3(grid_for(nfeat / 4)), dim3(256), 0, stream, gacc, nfeat);
     }
     using B = typename E::bits;
-    if (p.nunits > 0)  // no anchors: only the (zero) feature gradient is written
-        hipLaunchKernelGGL((agg_bwd_kernel<E>), dim3(p.nblocks), dim3(kThreads), 0, stream,
-                           static_cast<const B *>(a.feat), a.loc, a.weights,
-                           static_cast<const B *>(a.grad_out), gacc, part, a.grad_weights, p);
+    if (p.nunits > 0) {  // no anchors: only the (zero) feature gradient is written
+        const B *ft = static_cast<const B *>(a.feat);
+        const B *go = static_cast<const B *>(a.grad_out);
+        const dim3 grid(p.nblocks), block(kThreads);
+        switch (V) {
+            case 4: hipLaunchKernelGGL((agg_bwd_kernel<E, 4>), grid, block, 0, stream, ft, a.loc, a.weights, go, gacc, part, a.grad_weights, p); break;
+            case 2: hipLaunchKernelGGL((agg_bwd_kernel<E, 2>), grid, block, 0, stream, ft, a.loc, a.weights, go, gacc, part, a.grad_weights, p); break;
+            default: hipLaunchKernelGGL((agg_bwd_kernel<E, 1>), grid, block, 0, stream, ft, a.loc, a.weights, go, gacc, part, a.grad_weights, p); break;
+        }
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (a.grad_loc && p.nunits > 0) {

@@ -121,6 +121,23 @@ def test_agg_backward_subsets_and_determinism(gpu):
     check_grad(host(only_f[0]), o["grad_feat"], o["grad_feat_abs"], "f32", "grad_feat alone")
 
 
+def test_agg_backward_spare_rows_and_unaligned_grad_out(gpu):
+    """Feature rows outside every map get exact zeros; a grad_out whose address is only
+    4-byte aligned is read one channel per lane."""
+    c = wl.agg_case(B=1, shapes=TWO_CAM, A=10, pts=3, G=4, Cg=32, seed=43)
+    go = wl.agg_grad_out(c, seed=44)
+    buf = torch.zeros(go.numel() + 4, device="cuda")
+    buf[1:1 + go.numel()] = dev(go).view(-1)
+    go_mis = buf[1:1 + go.numel()].view(go.shape)
+    r = dsa.deform_agg_backward(dev(c["feat"]), c["spatial_shape"], c["scale_start"], dev(c["loc"]),
+                                dev(c["weights"]), go_mis, softmax=True)
+    torch.cuda.synchronize()
+    o = ref(c, go, softmax=True)
+    check_all(r, o, "f32", "unaligned grad_out")
+    used = int(sum(h * w for h, w in np.asarray(c["spatial_shape"]).reshape(-1, 2)))
+    assert not host(r[0])[:, used:].any()
+
+
 def test_agg_backward_empty(gpu):
     c = wl.agg_case(B=1, shapes=TWO_CAM, A=0, pts=3, G=4, Cg=32, seed=1)
     go = torch.zeros((1, 0, 128))
