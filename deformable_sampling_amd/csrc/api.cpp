@@ -369,13 +369,20 @@ dcn_status deform_agg_forward(const void *feat, const int32_t *spatial_shape,
     return hip_status(dcn::launch_deform_agg(a, stream));
 }
 
+// DCN_AGG_BWD_ATOMIC=1 selects the fp32-atomic feature gradient of the aggregation
+// backward at any size (the path used past the bucket limits)
+static bool agg_bwd_force_atomic() {
+    const char *e = getenv("DCN_AGG_BWD_ATOMIC");
+    return e && e[0] == '1';
+}
+
 size_t deform_agg_backward_workspace_bytes(int B, int P_total, int A, int pts, int cams,
                                            int scales, int G, int Cg, dcn_dtype dtype) {
     if (!valid_dtype(dtype) || B < 0 || A < 0 || P_total <= 0 || pts <= 0 || cams <= 0 ||
         scales <= 0 || G <= 0 || Cg <= 0)
         return 0;
     dcn::AggBwdPlan plan;
-    dcn::plan_agg_bwd(B, P_total, A, pts, cams, G, Cg, dtype, plan);
+    dcn::plan_agg_bwd(B, P_total, A, pts, cams, scales, G, Cg, dtype, agg_bwd_force_atomic(), plan);
     return plan.total;
 }
 
@@ -414,8 +421,9 @@ dcn_status deform_agg_backward(const void *feat, const int32_t *spatial_shape,
         !aligned(grad_weights, 4))
         return DCN_ERR_ALIGN;
     dcn::AggBwdPlan plan;
-    dcn::plan_agg_bwd(B, P_total, A, pts, cams, G, Cg, dtype, plan);
-    const bool needs_ws = (grad_loc || (grad_feat && dtype != DCN_F32)) && plan.total > 0;
+    dcn::plan_agg_bwd(B, P_total, A, pts, cams, scales, G, Cg, dtype, agg_bwd_force_atomic(), plan);
+    const bool needs_ws =
+        (grad_loc || (grad_feat && (plan.binned || dtype != DCN_F32))) && plan.total > 0;
     if (needs_ws && (!workspace || !aligned(workspace, 256) || workspace_bytes < plan.total))
         return DCN_ERR_WORKSPACE;
     if (!grad_feat && !grad_loc && !grad_weights) return DCN_OK;

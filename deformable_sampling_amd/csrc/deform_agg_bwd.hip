@@ -19,16 +19,27 @@
 // exact complements, wt); then slices of S lanes (V = 4, 2 or 1 channels per lane,
 // S*V >= Cg, S a power of two) walk the records: four V-wide corner loads and the
 // partial dots D_ab, summed over the slice into the sample's g_t, grad_u, grad_v in
-// LDS. The feature gradient follows each batch of records as fp32 atomic adds of
-// wt * w_ab * G_c laid out for the atomics instead: half a wavefront per corner, 32
-// contiguous channels per half (G from LDS), two instructions per record. The owner
-// lane of each (point, camera) sums its
-// scales and stores that group's grad_loc partial; the lane that built a sample
-// stores its g_t (and, with softmax, rewrites it as wt (g_t - sum_j wj g_j) once
-// the sum is known). A second kernel adds the G partials of grad_loc in group order.
-// The features accumulate in fp32 (in grad_feat for fp32, else in the workspace,
-// rounded once at the end), so their rounding varies run to run within fp32
-// accumulation error; grad_loc and grad_weights are deterministic.
+// LDS. The owner lane of each (point, camera) sums its scales and stores that
+// group's grad_loc partial; the lane that built a sample stores its g_t (and, with
+// softmax, rewrites it as wt (g_t - sum_j wj g_j) once the sum is known) and its
+// normalised weight wt. A second kernel adds the G partials of grad_loc in group
+// order.
+//
+// The feature gradient is a scatter (each sample adds to four feature rows); it runs
+// as a gather. Sample corners are bucketed by destination feature row (shared by all
+// groups, as the locations are): a count pass and a fill pass enumerate the samples
+// map by map, so a block's samples fall on few rows of a small map, and merge them
+// per row in an LDS hash table before touching the global counters (one atomic per
+// row and block); a one-block scan turns counts into bucket starts. After the main
+// kernel, one wavefront per (feature row, 16*V channels) sums wt[g] * w_ab * G over
+// the bucket, four entries at a time in four 16-lane groups, and stores the row once
+// in its dtype. No float atomics; the summation order within a bucket follows the
+// fill order, so grad_feat's last bits may vary between runs, while grad_loc and
+// grad_weights are deterministic. Past the bucket limits (or with
+// DCN_AGG_BWD_ATOMIC=1) the feature gradient is accumulated with fp32 atomic adds
+// after each batch of records (half a wavefront per corner, 32 contiguous channels
+// per half, G from LDS) into grad_feat (fp32) or a workspace accumulator rounded
+// once at the end.
 #include "dcn_common.hpp"
 #include "internal.hpp"
 
@@ -80,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void agg_bwd_kernel(
     const typename E::bits *__restrict__ feat, const float *__restrict__ loc,
     const float *__restrict__ weights, const typename E::bits *__restrict__ gout,
     float *__restrict__ gacc, float *__restrict__ gloc_part, float *__restrict__ gw,
-    const AggBwdParams p) {
+    float *__restrict__ wn, const AggBwdParams p) {
     __shared__ int s_h[kAggMaxMaps], s_w[kAggMaxMaps], s_start[kAggMaxMaps];
     __shared__ AggRec s_rec[kWaves][64];
     __shared__ float s_res[kWaves][64][3];  // g_t, grad_u, grad_v per record
@@ -248,6 +259,7 @@ __global__ __launch_bounds__(kThreads) void agg_bwd_kernel(
             const float gt = res[lane][0];
             dot = fmaf(wt, gt, dot);
             if (p.want_w) gw[((size_t)ba * T + t_nat) * p.G + g] = gt;
+            if (wn) wn[((size_t)ba * T + t_nat) * p.G + g] = wt;
         }
         if (p.want_loc && lane < p.npc && pc0 + lane < NPC) {
             float su = 0.0f, sv = 0.0f;
@@ -274,6 +286,291 @@ __global__ __launch_bounds__(kThreads) void agg_bwd_kernel(
                 *q = wt * (*q - tot);
             }
         }
+    }
+}
+
+// ------------------------------------------------------ feature buckets --
+
+constexpr int kHashSlots = 2048;  // >= 4 corners x 256 samples per block, load <= 1/2
+constexpr unsigned kNoKey = 0xffffffffu;
+
+// Sample index i of the bucket passes, map-major: i = (cs * BA + ba) * pts + point
+// for map cs = cam * scales + scale; returns (ba, t) with t the natural sample index
+// (point * cams + cam) * scales + scale.
+__device__ __forceinline__ void bucket_sample(long long i, const AggBwdParams &p, int &ba, int &t) {
+    const int pt = (int)(i % p.pts);
+    const long long rest = i / p.pts;
+    ba = (int)(rest % p.BA);
+    const int cs = (int)(rest / p.BA);
+    const int cam = cs / p.scales, sc = cs - cam * p.scales;
+    t = (pt * p.cams + cam) * p.scales + sc;
+}
+
+// The four corner rows (in [B*P_total)) and bilinear weights of sample (ba, t), with
+// the main kernel's position arithmetic; a weight is zero for a corner outside its map.
+__device__ __forceinline__ void bucket_corners(const float *__restrict__ loc, const AggBwdParams &p,
+                                               const int *s_h, const int *s_w, const int *s_start,
+                                               int ba, int t, unsigned (&row)[4], float (&w)[4]) {
+    const int pc = t / p.scales, sc = t - pc * p.scales;
+    const int cam = pc % p.cams;
+    const int cs = cam * p.scales + sc;
+    const float2 uv = *reinterpret_cast<const float2 *>(loc + ((size_t)ba * p.pts * p.cams + pc) * 2);
+    const int Hs = s_h[cs], Ws = s_w[cs];
+    const float xf = __fsub_rn(mul_rn(uv.x, (float)Ws), 0.5f);
+    const float yf = __fsub_rn(mul_rn(uv.y, (float)Hs), 0.5f);
+    int x0, y0;
+    float fy, uy, fx, ux;
+    split_fu(yf, y0, fy, uy);
+    split_fu(xf, x0, fx, ux);
+    const bool vy0 = (unsigned)y0 < (unsigned)Hs, vy1 = (unsigned)(y0 + 1) < (unsigned)Hs;
+    const bool vx0 = (unsigned)x0 < (unsigned)Ws, vx1 = (unsigned)(x0 + 1) < (unsigned)Ws;
+    w[0] = (vy0 && vx0) ? uy * ux : 0.0f;
+    w[1] = (vy0 && vx1) ? uy * fx : 0.0f;
+    w[2] = (vy1 && vx0) ? fy * ux : 0.0f;
+    w[3] = (vy1 && vx1) ? fy * fx : 0.0f;
+    const unsigned r00 = (unsigned)((ba / p.A) * p.P_total + s_start[cs]) + (unsigned)(y0 * Ws + x0);
+    row[0] = r00;
+    row[1] = r00 + 1u;
+    row[2] = r00 + (unsigned)Ws;
+    row[3] = r00 + (unsigned)Ws + 1u;
+}
+
+// Insert one occurrence of key: returns its slot; *rank = occurrences before it in
+// this block.
+__device__ __forceinline__ int hash_add(unsigned *keys, unsigned *cnts, unsigned key, unsigned &rank) {
+    int h = (int)((key * 2654435761u) >> 21);  // 11 bits
+    for (;;) {
+        const unsigned k = keys[h];
+        if (k == key) break;
+        if (k == kNoKey) {
+            const unsigned prev = atomicCAS(&keys[h], kNoKey, key);
+            if (prev == kNoKey || prev == key) break;
+        }
+        h = (h + 1) & (kHashSlots - 1);
+    }
+    rank = atomicAdd(&cnts[h], 1u);
+    return h;
+}
+
+// Count (FILL = false) or file (FILL = true) every corner with a non-zero weight in its
+// row's bucket. Per block: merge the corners per row in LDS, then one global atomic
+// per row (the count, or the reservation of the block's range in the bucket).
+template <bool FILL>
+__global__ __launch_bounds__(256) void agg_bucket_kernel(const float *__restrict__ loc,
+                                                         unsigned *__restrict__ cnt,
+                                                         const unsigned *__restrict__ starts,
+                                                         uint2 *__restrict__ entries, AggBwdParams p) {
+    __shared__ int s_h[kAggMaxMaps], s_w[kAggMaxMaps], s_start[kAggMaxMaps];
+    __shared__ unsigned s_key[kHashSlots], s_cnt[kHashSlots], s_base[kHashSlots];
+    const int nmaps = p.cams * p.scales;
+    for (int i = threadIdx.x; i < nmaps; i += 256) {
+        s_h[i] = p.maps.H[i];
+        s_w[i] = p.maps.W[i];
+        s_start[i] = p.maps.start[i];
+    }
+    for (int i = threadIdx.x; i < kHashSlots; i += 256) {
+        s_key[i] = kNoKey;
+        s_cnt[i] = 0;
+    }
+    __syncthreads();
+    const int T = p.pts * p.cams * p.scales;
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    const bool on = i < (long long)p.BA * T;
+    int ba = 0, t = 0;
+    unsigned row[4];
+    float w[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int slot[4];
+    unsigned rank[4];
+    if (on) {
+        bucket_sample(i, p, ba, t);
+        bucket_corners(loc, p, s_h, s_w, s_start, ba, t, row, w);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (w[q] != 0.0f) slot[q] = hash_add(s_key, s_cnt, row[q], rank[q]);
+    }
+    __syncthreads();
+    unsigned *fill = cnt + (size_t)p.B * p.P_total;  // fill cursors follow the counts
+    for (int h = threadIdx.x; h < kHashSlots; h += 256) {
+        const unsigned n = s_cnt[h];
+        if (n == 0) continue;
+        const unsigned key = s_key[h];
+        if constexpr (FILL) s_base[h] = starts[key] + atomicAdd(&fill[key], n);
+        else atomicAdd(&cnt[key], n);
+    }
+    if constexpr (FILL) {
+        __syncthreads();
+        if (on) {
+            const unsigned smp = (unsigned)ba * (unsigned)T + (unsigned)t;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (w[q] != 0.0f) entries[s_base[slot[q]] + rank[q]] = make_uint2(smp, __float_as_uint(w[q]));
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void agg_u32_zero_kernel(unsigned *__restrict__ p, long long n) {
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+        p[i] = 0u;
+}
+
+// Exclusive prefix sum of cnt[0..D) into starts in three launches: per-block sums of
+// 4096-value chunks (1024 threads, 4 consecutive values each), one block scanning
+// those sums, and a second pass over the chunks adding each block's offset.
+__device__ __forceinline__ void load4(const unsigned *__restrict__ src, long long b, long long D,
+                                      unsigned (&v)[4]) {
+    if (b + 3 < D) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(src + b);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (b + i < D) ? src[b + i] : 0u;
+    }
+}
+
+// Block-wide exclusive scan of one value per thread (1024 threads); returns the
+// thread's exclusive prefix and the block total in *total.
+__device__ __forceinline__ unsigned block_scan(unsigned x, unsigned *s_wave, unsigned &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    unsigned incl = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const unsigned u = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += u;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    unsigned before = 0;
+    total = 0;
+    for (int w = 0; w < 16; ++w) {
+        const unsigned sw = s_wave[w];
+        if (w < wave) before += sw;
+        total += sw;
+    }
+    __syncthreads();  // s_wave is reused by the next call
+    return before + incl - x;
+}
+
+__global__ __launch_bounds__(1024) void agg_scan_sums_kernel(const unsigned *__restrict__ cnt,
+                                                             unsigned *__restrict__ bsum, long long D) {
+    __shared__ unsigned s_wave[16];
+    unsigned v[4];
+    load4(cnt, (long long)blockIdx.x * 4096 + 4LL * threadIdx.x, D, v);
+    unsigned total;
+    block_scan(v[0] + v[1] + v[2] + v[3], s_wave, total);
+    if (threadIdx.x == 0) bsum[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(1024) void agg_scan_top_kernel(unsigned *__restrict__ bsum, int nb) {
+    __shared__ unsigned s_wave[16];
+    unsigned carry = 0;
+    for (int c0 = 0; c0 < nb; c0 += 1024) {
+        const int i = c0 + (int)threadIdx.x;
+        const unsigned x = i < nb ? bsum[i] : 0u;
+        unsigned total;
+        const unsigned ex = block_scan(x, s_wave, total);
+        if (i < nb) bsum[i] = carry + ex;
+        carry += total;
+    }
+}
+
+__global__ __launch_bounds__(1024) void agg_scan_final_kernel(const unsigned *__restrict__ cnt,
+                                                              const unsigned *__restrict__ bsum,
+                                                              unsigned *__restrict__ starts, long long D) {
+    __shared__ unsigned s_wave[16];
+    const long long b = (long long)blockIdx.x * 4096 + 4LL * threadIdx.x;
+    unsigned v[4];
+    load4(cnt, b, D, v);
+    unsigned total;
+    unsigned run = bsum[blockIdx.x] + block_scan(v[0] + v[1] + v[2] + v[3], s_wave, total);
+    if (b + 3 < D) {
+        uint4 q;
+        q.x = run; run += v[0];
+        q.y = run; run += v[1];
+        q.z = run; run += v[2];
+        q.w = run;
+        *reinterpret_cast<uint4 *>(starts + b) = q;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (b + i < D) starts[b + i] = run;
+            run += v[i];
+        }
+    }
+}
+
+struct AggGatherParams {
+    int GC, Cg, G, T;  // channels per row and per group; groups; samples per anchor
+    int CT;            // tiles of 16*V channels per row (<= 4*NB per item)
+    int NB;            // tile blocks per row: an item takes 4 tiles
+    long long nitems;
+    int nblocks;
+};
+
+// One wavefront per (feature row, block of up to 4 tiles of 16*V channels): four
+// 16-lane groups take every fourth entry of the row's bucket, two entries at a time;
+// each lane holds V channels of each tile (within one group since Cg % V == 0) and
+// sums wt[g] * w_ab * grad_out[anchor]; two shuffles combine the groups and the tile
+// is stored once in the dtype (rows outside every map get zeros).
+template <class E, int V>
+__global__ __launch_bounds__(256) void agg_feat_gather_kernel(
+    const typename E::bits *__restrict__ gout, const float *__restrict__ wn,
+    const unsigned *__restrict__ starts, const unsigned *__restrict__ cnt,
+    const uint2 *__restrict__ entries, typename E::bits *__restrict__ gfeat, AggGatherParams q) {
+    const int blk = xcd_remap((int)blockIdx.x, q.nblocks);
+    const long long item = (long long)blk * 4 + (threadIdx.x >> 6);
+    if (item >= q.nitems) return;  // whole wavefronts; no barrier in this kernel
+    const int lane = threadIdx.x & 63, grp = lane >> 4, l = lane & 15;
+    const long long row = item / q.NB;
+    const int tb = (int)(item - row * q.NB);
+    int cc[4], gg[4];
+    bool has[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int c = ((tb * 4 + k) * 16 + l) * V;
+        has[k] = (tb * 4 + k) < q.CT && c < q.GC;
+        cc[k] = has[k] ? c : 0;
+        gg[k] = cc[k] / q.Cg;
+    }
+    const unsigned b0 = starts[row], e = b0 + cnt[row];
+    float acc[4][V];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int u = 0; u < V; ++u) acc[k][u] = 0.0f;
+    auto add = [&](const uint2 en) {
+        const unsigned smp = en.x;
+        const float w = __uint_as_float(en.y);
+        const unsigned ba = smp / (unsigned)q.T;
+        const typename E::bits *gr = gout + (size_t)ba * q.GC;
+        const float *wr = wn + (size_t)smp * q.G;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (!has[k]) continue;
+            const float coef = w * wr[gg[k]];
+            float gv[V];
+            load_f32<E, V>(gr + cc[k], gv);
+#pragma unroll
+            for (int u = 0; u < V; ++u) acc[k][u] = fmaf(coef, gv[u], acc[k][u]);
+        }
+    };
+    unsigned i = b0 + grp;
+    for (; i + 4 < e; i += 8) {
+        const uint2 e0 = entries[i], e1 = entries[i + 4];
+        add(e0);
+        add(e1);
+    }
+    if (i < e) add(entries[i]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            acc[k][u] += __shfl_xor(acc[k][u], 16, 64);
+            acc[k][u] += __shfl_xor(acc[k][u], 32, 64);
+        }
+    if (grp == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (has[k]) store_f32<E, V>(gfeat + (size_t)row * q.GC + cc[k], acc[k]);
     }
 }
 
@@ -333,21 +630,47 @@ hipError_t launch_e(const AggBwdLaunch &a, const AggBwdPlan &pl, hipStream_t str
     char *ws = static_cast<char *>(a.workspace);
     float *part = a.grad_loc ? reinterpret_cast<float *>(ws + pl.off_loc) : nullptr;
     const long long nfeat = (long long)a.B * a.P_total * a.G * a.Cg;
+    const bool bins = a.grad_feat && pl.binned;
     float *gacc = nullptr;
-    if (a.grad_feat) {
+    float *wn = nullptr;
+    unsigned *cnt = nullptr, *starts = nullptr;
+    uint2 *entries = nullptr;
+    const long long nsamp = (long long)p.BA * a.pts * a.cams * a.scales;
+    if (bins) {
+        wn = reinterpret_cast<float *>(ws + pl.off_wn);
+        cnt = reinterpret_cast<unsigned *>(ws + pl.off_cnt);
+        starts = reinterpret_cast<unsigned *>(ws + pl.off_starts);
+        entries = reinterpret_cast<uint2 *>(ws + pl.off_ent);
+        hipLaunchKernelGGL(agg_u32_zero_kernel, dim3(grid_for(2 * pl.D / 4)), dim3(256), 0, stream, cnt,
+                           2 * pl.D);
+        if (nsamp > 0)
+            hipLaunchKernelGGL((agg_bucket_kernel<false>), dim3((unsigned)((nsamp + 255) / 256)), dim3(256),
+                               0, stream, a.loc, cnt, (const unsigned *)nullptr, (uint2 *)nullptr, p);
+        const int nsb = (int)((pl.D + 4095) / 4096);
+        unsigned *bsum = reinterpret_cast<unsigned *>(ws + pl.off_bsum);
+        hipLaunchKernelGGL(agg_scan_sums_kernel, dim3(nsb), dim3(1024), 0, stream, cnt, bsum, pl.D);
+        hipLaunchKernelGGL(agg_scan_top_kernel, dim3(1), dim3(1024), 0, stream, bsum, nsb);
+        hipLaunchKernelGGL(agg_scan_final_kernel, dim3(nsb), dim3(1024), 0, stream, cnt, bsum, starts,
+                           pl.D);
+        if (nsamp > 0)
+            hipLaunchKernelGGL((agg_bucket_kernel<true>), dim3((unsigned)((nsamp + 255) / 256)), dim3(256),
+                               0, stream, a.loc, cnt, starts, entries, p);
+    } else if (a.grad_feat) {
         gacc = (E::id == DCN_F32) ? static_cast<float *>(a.grad_feat)
                                   : reinterpret_cast<float *>(ws + pl.off_acc);
         hipLaunchKernelGGL(agg_zero_kernel, dim3(grid_for(nfeat / 4)), dim3(256), 0, stream, gacc, nfeat);
     }
+    hipError_t err0 = hipGetLastError();
+    if (err0 != hipSuccess) return err0;
     using B = typename E::bits;
     if (p.nunits > 0) {  // no anchors: only the (zero) feature gradient is written
         const B *ft = static_cast<const B *>(a.feat);
         const B *go = static_cast<const B *>(a.grad_out);
         const dim3 grid(p.nblocks), block(kThreads);
         switch (V) {
-            case 4: hipLaunchKernelGGL((agg_bwd_kernel<E, 4>), grid, block, 0, stream, ft, a.loc, a.weights, go, gacc, part, a.grad_weights, p); break;
-            case 2: hipLaunchKernelGGL((agg_bwd_kernel<E, 2>), grid, block, 0, stream, ft, a.loc, a.weights, go, gacc, part, a.grad_weights, p); break;
-            default: hipLaunchKernelGGL((agg_bwd_kernel<E, 1>), grid, block, 0, stream, ft, a.loc, a.weights, go, gacc, part, a.grad_weights, p); break;
+            case 4: hipLaunchKernelGGL((agg_bwd_kernel<E, 4>), grid, block, 0, stream, ft, a.loc, a.weights, go, gacc, part, a.grad_weights, wn, p); break;
+            case 2: hipLaunchKernelGGL((agg_bwd_kernel<E, 2>), grid, block, 0, stream, ft, a.loc, a.weights, go, gacc, part, a.grad_weights, wn, p); break;
+            default: hipLaunchKernelGGL((agg_bwd_kernel<E, 1>), grid, block, 0, stream, ft, a.loc, a.weights, go, gacc, part, a.grad_weights, wn, p); break;
         }
     }
     hipError_t err = hipGetLastError();
@@ -357,7 +680,28 @@ hipError_t launch_e(const AggBwdLaunch &a, const AggBwdPlan &pl, hipStream_t str
         hipLaunchKernelGGL(agg_loc_reduce_kernel, dim3((unsigned)((nl + 255) / 256)), dim3(256), 0,
                            stream, part, a.grad_loc, nl, a.G);
     }
-    if constexpr (E::id != DCN_F32) {
+    if (bins) {
+        AggGatherParams q;
+        q.GC = a.G * a.Cg;
+        q.Cg = a.Cg;
+        q.G = a.G;
+        q.T = a.pts * a.cams * a.scales;
+        int VG = 4;  // channels per lane: VG | Cg, grad_out and grad_feat VG*elt-byte aligned
+        while (VG > 1 && (a.Cg % VG != 0 || ((uintptr_t)a.grad_out % (VG * elt)) != 0 ||
+                          ((uintptr_t)a.grad_feat % (VG * elt)) != 0))
+            VG >>= 1;
+        q.CT = (q.GC + 16 * VG - 1) / (16 * VG);
+        q.NB = (q.CT + 3) / 4;
+        q.nitems = (long long)a.B * a.P_total * q.NB;
+        q.nblocks = (int)((q.nitems + 3) / 4);
+        const B *gop = static_cast<const B *>(a.grad_out);
+        B *gf = static_cast<B *>(a.grad_feat);
+        switch (VG) {
+            case 4: hipLaunchKernelGGL((agg_feat_gather_kernel<E, 4>), dim3(q.nblocks), dim3(256), 0, stream, gop, wn, starts, cnt, entries, gf, q); break;
+            case 2: hipLaunchKernelGGL((agg_feat_gather_kernel<E, 2>), dim3(q.nblocks), dim3(256), 0, stream, gop, wn, starts, cnt, entries, gf, q); break;
+            default: hipLaunchKernelGGL((agg_feat_gather_kernel<E, 1>), dim3(q.nblocks), dim3(256), 0, stream, gop, wn, starts, cnt, entries, gf, q); break;
+        }
+    } else if constexpr (E::id != DCN_F32) {
         if (a.grad_feat)
             hipLaunchKernelGGL((agg_round_kernel<E>), dim3(grid_for(nfeat / 4)), dim3(256), 0,
                                stream, gacc, static_cast<B *>(a.grad_feat), nfeat);
@@ -369,14 +713,32 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 }  // namespace
 
-void plan_agg_bwd(int B, int P_total, int A, int pts, int cams, int G, int Cg, dcn_dtype dtype,
-                  AggBwdPlan &pl) {
+void plan_agg_bwd(int B, int P_total, int A, int pts, int cams, int scales, int G, int Cg,
+                  dcn_dtype dtype, bool force_atomic, AggBwdPlan &pl) {
     pl = AggBwdPlan();
+    const long long T = (long long)pts * cams * scales;
+    pl.D = (long long)B * P_total;
+    pl.nent = (long long)B * A * T * 4;
+    pl.binned = !force_atomic && pl.nent < (1LL << 31) && 2 * pl.D < (1LL << 31) &&
+                (long long)B * A * T < (1LL << 31);
     size_t off = 0;
     pl.off_loc = off;
     off = align256(off + (size_t)G * B * A * pts * cams * 2 * sizeof(float));
-    pl.off_acc = off;
-    if (dtype != DCN_F32) off = align256(off + (size_t)B * P_total * G * Cg * sizeof(float));
+    if (pl.binned) {
+        pl.off_wn = off;
+        off = align256(off + (size_t)B * A * T * G * sizeof(float));
+        pl.off_cnt = off;
+        off = align256(off + (size_t)pl.D * 2 * sizeof(unsigned));
+        pl.off_starts = off;
+        off = align256(off + (size_t)pl.D * sizeof(unsigned));
+        pl.off_bsum = off;
+        off = align256(off + (size_t)((pl.D + 4095) / 4096) * sizeof(unsigned));
+        pl.off_ent = off;
+        off = align256(off + (size_t)pl.nent * 8);
+    } else {
+        pl.off_acc = off;
+        if (dtype != DCN_F32) off = align256(off + (size_t)B * P_total * G * Cg * sizeof(float));
+    }
     pl.total = off;
 }
 

@@ -148,8 +148,10 @@ struct AggLaunch {
 hipError_t launch_deform_agg(const AggLaunch &a, hipStream_t stream);
 
 // Aggregation backward (deform_agg_bwd.hip). grad_feat / grad_loc / grad_weights
-// may be NULL. Workspace: per-group grad_loc partials, then (fp16/bf16) an fp32
-// grad_feat accumulator.
+// may be NULL. Workspace: per-group grad_loc partials, then either the feature
+// buckets (normalised weights [B*A*T*G] fp32, counts + fill cursors [2][B*P_total],
+// starts [B*P_total] and scan block sums uint32, entries [B*A*T*4] of 8 bytes) or, past the bucket
+// limits, an fp32 grad_feat accumulator (fp16/bf16 only).
 struct AggBwdLaunch {
     const void *feat;
     const float *loc;
@@ -164,10 +166,12 @@ struct AggBwdLaunch {
     AggMaps maps;
 };
 struct AggBwdPlan {
-    size_t off_loc, off_acc, total;
+    bool binned;
+    long long D, nent;
+    size_t off_loc, off_acc, off_wn, off_cnt, off_starts, off_bsum, off_ent, total;
 };
-void plan_agg_bwd(int B, int P_total, int A, int pts, int cams, int G, int Cg, dcn_dtype dtype,
-                  AggBwdPlan &plan);
+void plan_agg_bwd(int B, int P_total, int A, int pts, int cams, int scales, int G, int Cg,
+                  dcn_dtype dtype, bool force_atomic, AggBwdPlan &plan);
 hipError_t launch_deform_agg_bwd(const AggBwdLaunch &a, const AggBwdPlan &plan, hipStream_t stream);
 
 // Deformable RoI pooling (deform_roi_pool.hip).

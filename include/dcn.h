@@ -286,9 +286,15 @@ dcn_status deform_agg_forward(const void *feat, const int32_t *spatial_shape,
 const char *dcn_status_string(dcn_status s);
 
 /*
- * Workspace bytes deform_agg_backward needs (0 if the sizes are invalid): per-group
- * partial sums of grad_loc (G*B*A*pts*cams*2 floats), then, for fp16/bf16, an fp32
- * accumulator of grad_feat (B*P_total*G*Cg floats); each region 256-byte aligned.
+ * Workspace bytes deform_agg_backward needs (0 if the sizes are invalid), each region
+ * 256-byte aligned: per-group partial sums of grad_loc (G*B*A*pts*cams*2 floats); then
+ * the feature-gradient buckets: the normalised weights (B*A*T*G floats, T =
+ * pts*cams*scales), per-feature-row counts and fill cursors (2*B*P_total uint32), their
+ * starts (B*P_total uint32), the scan's block sums (one uint32 per 4096 rows) and one
+ * 8-byte entry per sample corner (B*A*T*4). Where
+ * the entries would reach 2^31 (or with DCN_AGG_BWD_ATOMIC=1 in the environment) the
+ * buckets are replaced by fp32 atomic adds, and fp16/bf16 then need an fp32 grad_feat
+ * accumulator (B*P_total*G*Cg floats) instead.
  */
 size_t deform_agg_backward_workspace_bytes(int B, int P_total, int A, int pts, int cams,
                                            int scales, int G, int Cg, dcn_dtype dtype);
@@ -312,11 +318,13 @@ size_t deform_agg_backward_workspace_bytes(int B, int P_total, int A, int pts, i
  * positions): grad_feat[corner] += wt * w_ab * grad_out; grad_w_t = sum_c
  * grad_out[c] B_t[c] (softmax: wt (grad_w_t - sum_j wj grad_w_j)); grad_u =
  * sum over scales and groups of wt * W_s * sum_c grad_out[c] dB_t/dx[c], grad_v
- * likewise with H_s and dB_t/dy. grad_feat sums in fp32 with atomic adds (its
- * rounding varies run to run within fp32 accumulation error) and is rounded once
- * to dtype; grad_loc and grad_weights are deterministic. workspace:
- * deform_agg_backward_workspace_bytes bytes, 256-byte aligned, needed when
- * grad_loc != NULL or (grad_feat != NULL and dtype != DCN_F32), else may be NULL;
+ * likewise with H_s and dB_t/dy. grad_feat is gathered per feature row from
+ * buckets of sample corners and summed in fp32 (the order within a bucket follows
+ * an atomic fill, so its rounding varies run to run within fp32 accumulation
+ * error), then rounded once to dtype; grad_loc and grad_weights are deterministic.
+ * workspace: deform_agg_backward_workspace_bytes bytes, 256-byte aligned, needed
+ * when grad_loc != NULL or grad_feat != NULL (with the atomic fallback: grad_feat
+ * in fp16/bf16), else may be NULL;
  * contents on entry are ignored. Limits as the forward, and Cg <= 512. With A == 0
  * and grad_feat != NULL the call writes zeros to grad_feat (the one exception to
  * "zero-sized work launches nothing").

@@ -224,10 +224,15 @@ def agg_bwd(lib, feat=A, ss=None, st=None, loc=A, w=A, go=A, gf=A, gl=A, gw=A, w
 
 
 def test_agg_backward_workspace_and_validation(lib):
+    a256 = lambda v: (v + 255) // 256 * 256
     n = lib.deform_agg_backward_workspace_bytes(1, 89760, 900, 13, 6, 4, 8, 32, 0)
-    assert n == (8 * 900 * 13 * 6 * 2 * 4 + 255) // 256 * 256      # fp32: loc partials only
-    n16 = lib.deform_agg_backward_workspace_bytes(1, 89760, 900, 13, 6, 4, 8, 32, 1)
-    assert n16 == n + 89760 * 256 * 4                                # + fp32 feature accumulator
+    T = 13 * 6 * 4
+    assert n == (a256(8 * 900 * 13 * 6 * 2 * 4)      # grad_loc partials per group
+                 + a256(900 * T * 8 * 4)             # normalised weights
+                 + a256(89760 * 2 * 4) + a256(89760 * 4)  # bucket counts + cursors, starts
+                 + a256((89760 + 4095) // 4096 * 4)  # scan block sums
+                 + a256(900 * T * 4 * 8))            # entries: one per corner
+    assert lib.deform_agg_backward_workspace_bytes(1, 89760, 900, 13, 6, 4, 8, 32, 1) == n
     assert lib.deform_agg_backward_workspace_bytes(1, 0, 9, 1, 1, 1, 1, 8, 0) == 0
     assert agg_bwd(lib, dtype=5) == DTYPE
     assert agg_bwd(lib, Cg=513) == SHAPE                              # channel rounds limit
@@ -321,3 +326,11 @@ def test_v2_backward_validation(lib):
     assert v2b(lib, gx=A + 1) == ALIGN
     assert v2b(lib, gw=A + 2) == ALIGN
     assert lib.dcn_last_hip_error() == 0
+
+
+def test_agg_backward_workspace_atomic_fallback(lib, monkeypatch):
+    monkeypatch.setenv("DCN_AGG_BWD_ATOMIC", "1")
+    n = lib.deform_agg_backward_workspace_bytes(1, 89760, 900, 13, 6, 4, 8, 32, 0)
+    assert n == (8 * 900 * 13 * 6 * 2 * 4 + 255) // 256 * 256      # fp32: loc partials only
+    n16 = lib.deform_agg_backward_workspace_bytes(1, 89760, 900, 13, 6, 4, 8, 32, 1)
+    assert n16 == n + 89760 * 256 * 4                                # + fp32 feature accumulator

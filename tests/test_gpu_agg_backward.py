@@ -121,9 +121,39 @@ def test_agg_backward_subsets_and_determinism(gpu):
     check_grad(host(only_f[0]), o["grad_feat"], o["grad_feat_abs"], "f32", "grad_feat alone")
 
 
+FALLBACK = [
+    ("f32_cg32_softmax", dict(B=1, shapes=TWO_CAM, A=16, pts=3, G=4, Cg=32)),
+    ("bf16_cg16", dict(B=2, shapes=TWO_CAM, A=9, pts=3, G=4, Cg=16, dtype="bf16")),
+    ("f32_cg5_outside", dict(B=1, shapes=TWO_CAM, A=7, pts=2, G=3, Cg=5, loc_lo=-0.3, loc_hi=1.3)),
+]
+
+
+@pytest.mark.parametrize("name,args", FALLBACK, ids=[s[0] for s in FALLBACK])
+def test_agg_backward_atomic_fallback(gpu, monkeypatch, name, args):
+    """The fp32-atomic feature gradient (used past the bucket limits), selected here at
+    small sizes through DCN_AGG_BWD_ATOMIC=1."""
+    monkeypatch.setenv("DCN_AGG_BWD_ATOMIC", "1")
+    c = wl.agg_case(seed=700 + len(name), **args)
+    go = wl.agg_grad_out(c, seed=len(name))
+    _say("agg backward atomic fallback", name)
+    r = run(c, go)
+    o = ref(c, go)
+    _say(name, check_all(r, o, c["dtype"], name))
+
+
+def test_agg_backward_hot_rows(gpu):
+    """Every sample of 64 anchors on one 3x4 map: hundreds of corners per feature row
+    (long buckets, merged per block in LDS)."""
+    c = wl.agg_case(B=1, shapes=[[(3, 4)]] * 2, A=64, pts=8, G=2, Cg=32, seed=45)
+    go = wl.agg_grad_out(c, seed=46)
+    r = run(c, go)
+    o = ref(c, go)
+    _say("hot rows", check_all(r, o, "f32", "hot rows"))
+
+
 def test_agg_backward_spare_rows_and_unaligned_grad_out(gpu):
     """Feature rows outside every map get exact zeros; a grad_out whose address is only
-    4-byte aligned is read one channel per lane."""
+    4-byte aligned takes the one-channel gather."""
     c = wl.agg_case(B=1, shapes=TWO_CAM, A=10, pts=3, G=4, Cg=32, seed=43)
     go = wl.agg_grad_out(c, seed=44)
     buf = torch.zeros(go.numel() + 4, device="cuda")
