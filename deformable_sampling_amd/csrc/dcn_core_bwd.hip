@@ -579,9 +579,9 @@ __global__ __launch_bounds__(1024) void bwd_gather_kernel(const uint4 *__restric
                                                           const typename E::bits *__restrict__ gout,
                                                           typename E::bits *__restrict__ gx,
                                                           GatherParams q) {
-    __shared__ uint4 s_rec[kGatherCap];
+    __shared__ float4 s_w[kGatherCap];      // cell-sorted: the four corner weights m*w_ab
+    __shared__ unsigned s_src[kGatherCap];  // cell-sorted: source pixel of the record
     __shared__ unsigned short s_cell[kGatherCap];
-    __shared__ unsigned short s_idx[kGatherCap];
     __shared__ unsigned s_cnt[kCells * kCells];
     __shared__ unsigned s_pos[kCells * kCells];
     __shared__ unsigned s_fill[kCells * kCells];
@@ -645,17 +645,22 @@ __global__ __launch_bounds__(1024) void bwd_gather_kernel(const uint4 *__restric
                 s_fill[i] = 0;
             }
             __syncthreads();
-            for (int r = tid; r < nrec; r += nthreads) {
-                int gi = c0 + r, k = 0;
+            // record r of this chunk -> its place in the five ranges
+            auto locate = [&](int r, int &k, int &gi) {
+                gi = c0 + r;
+                k = 0;
                 while (k < 4 && gi >= re[k] - rb[k]) {
                     gi -= re[k] - rb[k];
                     ++k;
                 }
-                const uint4 v = rec[rb[k] + gi];
-                const int cy = (int)((v.x >> 4) & 15u) + sy[k];
-                const int cx = (int)(v.x & 15u) + sx[k];
+            };
+            for (int r = tid; r < nrec; r += nthreads) {
+                int k, gi;
+                locate(r, k, gi);
+                const unsigned vx = rec[rb[k] + gi].x;
+                const int cy = (int)((vx >> 4) & 15u) + sy[k];
+                const int cx = (int)(vx & 15u) + sx[k];
                 const int cell = cy * kCells + cx;
-                s_rec[r] = v;
                 s_cell[r] = (unsigned short)cell;
                 atomicAdd(&s_cnt[cell], 1u);
             }
@@ -683,13 +688,25 @@ __global__ __launch_bounds__(1024) void bwd_gather_kernel(const uint4 *__restric
                 }
             }
             __syncthreads();
+            // counting sort by cell; each record's four corner weights are formed once
             for (int r = tid; r < nrec; r += nthreads) {
+                int k, gi;
+                locate(r, k, gi);
+                const uint4 v = rec[rb[k] + gi];
                 const int cell = s_cell[r];
-                const unsigned slot = atomicAdd(&s_fill[cell], 1u);
-                s_idx[s_pos[cell] + slot] = (unsigned short)r;
+                const unsigned at = s_pos[cell] + atomicAdd(&s_fill[cell], 1u);
+                int cyy, cxx;
+                float fy, uy, fx, ux;
+                split_coord_fu(0, __uint_as_float(v.y), cyy, fy, uy);
+                split_coord_fu(0, __uint_as_float(v.z), cxx, fx, ux);
+                const float m = __uint_as_float(v.w);
+                const float my0 = m * uy, my1 = m * fy;
+                s_w[at] = make_float4(my0 * ux, my0 * fx, my1 * ux, my1 * fx);
+                s_src[at] = v.x >> 8;
             }
             __syncthreads();
             if (inside && has) {
+                const float *sw = reinterpret_cast<const float *>(s_w);
 #pragma unroll
                 for (int a = 0; a < 2; ++a) {
 #pragma unroll
@@ -698,14 +715,9 @@ __global__ __launch_bounds__(1024) void bwd_gather_kernel(const uint4 *__restric
                         const int cell = (qy + 1 - a) * kCells + (qx + 1 - b);
                         const int i0 = (int)s_pos[cell], i1 = i0 + (int)s_cnt[cell];
                         for (int i = i0; i < i1; ++i) {
-                            const uint4 v = s_rec[s_idx[i]];
-                            int cyy, cxx;
-                            float fy, uy, fx, ux;
-                            split_coord_fu(0, __uint_as_float(v.y), cyy, fy, uy);
-                            split_coord_fu(0, __uint_as_float(v.z), cxx, fx, ux);
-                            const float w = __uint_as_float(v.w) * (a ? fy : uy) * (b ? fx : ux);
+                            const float w = sw[4 * i + 2 * a + b];
                             float gv[V];
-                            load_f32<E, V>(gout + gbase + (size_t)(v.x >> 8) * GC + ch * V, gv);
+                            load_f32<E, V>(gout + gbase + (size_t)s_src[i] * GC + ch * V, gv);
 #pragma unroll
                             for (int u = 0; u < V; ++u) acc[u] = fmaf(w, gv[u], acc[u]);
                         }
