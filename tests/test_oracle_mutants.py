@@ -82,7 +82,7 @@ AGG_BWD_MUTANTS = [
      "double v = softmax ? w[t] * gt[t] : gt[t];", 1),
     ("aggbwd_weights_layout", "if (gw) gw[(ba * T + t) * G + g] = v;", "if (gw) gw[(ba * G + g) * T + t] = v;", 1),
     ("aggbwd_dx_sign", "double dwx[2][2] = {{-(1.0 - fy), 1.0 - fy}, {-fy, fy}};",
-     "double dwx[2][2] = {{(1.0 - fy), -(1.0 - fy)}, {fy, -fy}};", 2),
+     "double dwx[2][2] = {{(1.0 - fy), -(1.0 - fy)}, {fy, -fy}};", 3),
     ("aggbwd_grad_out_group_stride", "const double *Gv = gout + ba * GC + g * Cg;",
      "const double *Gv = gout + ba * GC;", 1),
 ]
