@@ -46,6 +46,8 @@
 #include "dcn_common.hpp"
 #include "internal.hpp"
 
+#include <stdlib.h>
+
 namespace dcn {
 namespace {
 
@@ -59,6 +61,7 @@ struct BwdParams {
     float offset_scale;
     int softmax, has_mask, vec_io;
     int want_x, want_off, want_mask;
+    int dots;  // 0: the pair pass only files the grad_x records (gradients come from the tile kernel)
     int npairs, S, Q, nchunk, PB, nblocks;
     int TY, TX;  // bin grid: tiles per image column / row (floor(H/16)+1, floor(W/16)+1)
     int TXo, otiles;  // tiled pair order: output tiles per row, per image and group
@@ -361,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(
 
     // 2. corner dots (and, in the fallback, the grad_x atomics). Every lane of a pair
     // runs the same number of channel rounds, so the segment sums see all S lanes.
-    if (active) {
+    if (active && p.dots) {
         const size_t img_base = (size_t)n * p.H * p.W * GC + (size_t)g * p.C;
         const typename E::bits *img = x + img_base;
         float *acc = (!BIN && p.want_x) ? gacc + img_base : nullptr;
@@ -837,6 +840,13 @@ hipError_t launch_gather(int V, const CoreBwdLaunch &a, const GatherParams &q, c
     return hipGetLastError();
 }
 
+// DCN_CORE_BWD_NO_TILE=1 keeps grad_offset / grad_mask in the pair pass (tests compare
+// both paths)
+bool core_bwd_no_tile() {
+    const char *e = getenv("DCN_CORE_BWD_NO_TILE");
+    return e && e[0] == '1';
+}
+
 template <class E>
 hipError_t launch_e(const CoreBwdLaunch &a, const CoreBwdPlan &pl, hipStream_t stream) {
     BwdParams p;
@@ -868,8 +878,34 @@ hipError_t launch_e(const CoreBwdLaunch &a, const CoreBwdPlan &pl, hipStream_t s
     p.PB = 4 * p.Q;
     p.nblocks = (p.npairs + p.PB - 1) / p.PB;
 
+    p.dots = 1;
     char *ws = static_cast<char *>(a.workspace);
     hipError_t err;
+    // grad_offset / grad_mask on the forward's LDS halo tiles where a tile plan with one
+    // lane per pair applies (then the pair pass only files the grad_x records, or does
+    // not run); the atomic fallback keeps its dots, which carry the grad_x adds
+    if ((a.grad_offset || a.grad_mask) && (bin || !a.grad_x) && !core_bwd_no_tile()) {
+        CoreLaunch c;
+        c.x = a.x; c.offset = a.offset; c.mask = a.mask; c.out = const_cast<void *>(a.grad_out);
+        c.N = a.N; c.H = a.H; c.W = a.W; c.G = a.G; c.C = a.C; c.kh = a.kh; c.kw = a.kw;
+        c.sh = a.sh; c.sw = a.sw; c.ph = a.ph; c.pw = a.pw; c.dh = a.dh; c.dw = a.dw;
+        c.Ho = a.Ho; c.Wo = a.Wo;
+        c.offset_scale = a.offset_scale;
+        c.softmax = a.softmax;
+        c.dtype = a.dtype;
+        c.om_dtype = DCN_F32;
+        c.om_plain = true;
+        c.off_grp = 2 * K; c.off_pix = a.G * 2 * K; c.mask_grp = K; c.mask_pix = a.G * K;
+        CoreTilePlan tp;
+        if (a.kh == 3 && a.kw == 3 && plan_core_tile(c, tp) && tp.S == 1) {
+            if ((err = launch_dcn_core_bwd_tile(c, tp, a.grad_offset, a.grad_mask, stream)) != hipSuccess)
+                return err;
+            p.dots = 0;
+            p.want_off = 0;
+            p.want_mask = 0;
+            if (!a.grad_x) return hipSuccess;
+        }
+    }
     if (bin) {
         unsigned *counts = reinterpret_cast<unsigned *>(ws + pl.off_counts);
         unsigned *starts = reinterpret_cast<unsigned *>(ws + pl.off_starts);

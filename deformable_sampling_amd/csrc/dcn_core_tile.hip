@@ -329,6 +329,37 @@ __device__ __forceinline__ void taps_and_store(const uint4 *buf, const typename 
     for (int u = 0; u < NC; ++u) store_f32<E, V>(o + u * V, acc[u]);
 }
 
+// Stage the tile's region with direct global->LDS copies: each wave moves 64
+// consecutive 16-byte chunks per instruction (lane order = LDS order); chunks outside
+// the image copy the zero chunk. Thread t always moves chunk t & (cpp-1) of region
+// pixels r = t >> log2(cpp), r + dr, ... with the row/column advanced incrementally.
+// The caller waits (barrier) before reading.
+template <class E>
+__device__ __forceinline__ void stage_region(uint4 *lds, const typename E::bits *__restrict__ x,
+                                             const TileAt &a, const TileParams &p) {
+    using Bt = typename E::bits;
+    constexpr int V = 16 / (int)sizeof(Bt);
+    const int tid = threadIdx.x;
+    const int GC = p.G * p.C;
+    const Bt *img = x + (size_t)a.n * p.H * p.W * GC + (size_t)a.g0 * p.C + (tid & (p.cpp - 1)) * V;
+    const int total = p.RH * p.RW * p.cpp;
+    const int nt = blockDim.x;
+    const int dr = nt >> p.cpp_log2;
+    const int ddy = dr / p.RW, ddx = dr - ddy * p.RW;
+    int r = tid >> p.cpp_log2;
+    int ry = r / p.RW, rx = r - ry * p.RW;
+    for (int i0 = tid & ~63; i0 < total; i0 += nt) {
+        const int yy = a.ry0 + ry, xx = a.rx0 + rx;
+        const bool ok = i0 + (tid & 63) < total && (unsigned)yy < (unsigned)p.H && (unsigned)xx < (unsigned)p.W;
+        const void *src = ok ? (const void *)(img + __umul24(__umul24(yy, p.W) + xx, GC))
+                             : (const void *)g_dcn_zero_chunk;
+        __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(lds + i0), 16, 0, 0);
+        rx += ddx;
+        ry += ddy;
+        if (rx >= p.RW) { rx -= p.RW; ++ry; }
+    }
+}
+
 // ---------------------------------------------------------- one tile/block --
 
 template <class E, class OM, int KH, int KW, int S, int NC, int CPP_, int RW_>
@@ -337,42 +368,16 @@ __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::b
                                                              const typename OM::bits *__restrict__ mask,
                                                              typename E::bits *__restrict__ out,
                                                              const TileParams p) {
-    using Bt = typename E::bits;
-    constexpr int V = 16 / (int)sizeof(Bt);
     constexpr int K = KH * KW;
     extern __shared__ uint4 lds[];  // [RH][RW][cpp]
 
     const TileAt a = tile_at(xcd_remap((int)blockIdx.x, p.nblocks), p);
     const LaneAt l = lane_at<S>(a, p);
-    const int tid = threadIdx.x;
-    const int GC = p.G * p.C;
 
     float d[2 * K], m[K];
     load_dm<K, OM>(d, m, a, l, offset, mask, p);
 
-    // Stage the region with direct global->LDS copies: each wave moves 64 consecutive
-    // 16-byte chunks per instruction (lane order = LDS order); chunks outside the
-    // image copy the zero chunk. Thread t always moves chunk t & (cpp-1) of region
-    // pixels r = t >> log2(cpp), r + dr, ... with the row/column advanced incrementally.
-    {
-        const Bt *img = x + (size_t)a.n * p.H * p.W * GC + (size_t)a.g0 * p.C + (tid & (p.cpp - 1)) * V;
-        const int total = p.RH * p.RW * p.cpp;
-        const int nt = blockDim.x;
-        const int dr = nt >> p.cpp_log2;
-        const int ddy = dr / p.RW, ddx = dr - ddy * p.RW;
-        int r = tid >> p.cpp_log2;
-        int ry = r / p.RW, rx = r - ry * p.RW;
-        for (int i0 = tid & ~63; i0 < total; i0 += nt) {
-            const int yy = a.ry0 + ry, xx = a.rx0 + rx;
-            const bool ok = i0 + (tid & 63) < total && (unsigned)yy < (unsigned)p.H && (unsigned)xx < (unsigned)p.W;
-            const void *src = ok ? (const void *)(img + __umul24(__umul24(yy, p.W) + xx, GC))
-                                 : (const void *)g_dcn_zero_chunk;
-            __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(lds + i0), 16, 0, 0);
-            rx += ddx;
-            ry += ddy;
-            if (rx >= p.RW) { rx -= p.RW; ++ry; }
-        }
-    }
+    stage_region<E>(lds, x, a, p);
     __syncthreads();
     if (p.softmax) softmax_k<K, S>(m, l.s);
     if (!l.active) return;
@@ -380,6 +385,200 @@ __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::b
     const typename OM::bits *coff = kOmPlain<OM> ? offset + (pixel * p.G + l.g) * K * 2
                                                  : offset + pixel * p.off_pix + (size_t)l.g * p.off_grp;
     taps_and_store<E, OM, KH, KW, S, NC, CPP_, RW_>(lds, x, out, d, m, a, l, p, coff);
+}
+
+// ------------------------------------------------- backward: tap gradients --
+//
+// grad_offset and grad_mask of the core backward with the forward's tile structure
+// (one lane per (pixel, group) pair: S = 1): the region is staged in LDS as in the
+// forward, the lane holds the pair's grad_out channels, and per tap the four corner
+// dots D_ab = sum_c grad_out_c X_ab,c come from LDS (corners outside the image are the
+// staged zeros); taps leaving the region are redone from global memory afterwards.
+// With exact complements u = (floor + 1) - t (split_coord_fu):
+//   g_k = uy (ux D00 + fx D01) + fy (ux D10 + fx D11)
+//   grad_offset_k = s m_k (uy (D01 - D00) + fy (D11 - D10), ux (D10 - D00) + fx (D11 - D01))
+//   grad_mask_k = g_k, or m_k (g_k - sum_j m_j g_j) with the softmax.
+template <class E, int NC>
+__device__ __forceinline__ void dots4(const uint4 (&c)[NC][4], const float (&gv)[NC][16 / sizeof(typename E::bits)],
+                                      float &d00, float &d01, float &d10, float &d11) {
+    constexpr int V = 16 / (int)sizeof(typename E::bits);
+#pragma unroll
+    for (int uu = 0; uu < NC; ++uu) {
+        float va[V], vb[V], vc[V], ve[V];
+        unpack<E, V>(c[uu][0], va);
+        unpack<E, V>(c[uu][1], vb);
+        unpack<E, V>(c[uu][2], vc);
+        unpack<E, V>(c[uu][3], ve);
+#pragma unroll
+        for (int z = 0; z < V; ++z) {
+            d00 = fmaf(gv[uu][z], va[z], d00);
+            d01 = fmaf(gv[uu][z], vb[z], d01);
+            d10 = fmaf(gv[uu][z], vc[z], d10);
+            d11 = fmaf(gv[uu][z], ve[z], d11);
+        }
+    }
+}
+
+template <class E, int NC, int CPP_, int RW_>
+__global__ __launch_bounds__(1024) void dcn_core_bwd_tile_kernel(const typename E::bits *__restrict__ x,
+                                                                 const float *__restrict__ offset,
+                                                                 const float *__restrict__ mask,
+                                                                 const typename E::bits *__restrict__ gout,
+                                                                 float *__restrict__ goff,
+                                                                 float *__restrict__ gmask,
+                                                                 const TileParams p) {
+    using Bt = typename E::bits;
+    constexpr int V = 16 / (int)sizeof(Bt);
+    constexpr int K = 9;
+    extern __shared__ uint4 lds[];  // [RH][RW][cpp]
+
+    const TileAt a = tile_at(xcd_remap((int)blockIdx.x, p.nblocks), p);
+    const LaneAt l = lane_at<1>(a, p);
+    const int GC = p.G * p.C;
+
+    float d[2 * K], m[K];
+    load_dm<K, OMPlain>(d, m, a, l, reinterpret_cast<const uint32_t *>(offset),
+                        reinterpret_cast<const uint32_t *>(mask), p);
+    stage_region<E>(lds, x, a, p);
+    const size_t pixel = l.active ? ((size_t)a.n * p.Ho + l.ho) * p.Wo + l.wo : 0;
+    float gv[NC][V];  // this pair's grad_out channels
+    {
+        const Bt *gp = gout + pixel * GC + (size_t)l.g * p.C;
+#pragma unroll
+        for (int uu = 0; uu < NC; ++uu) load_f32<E, V>(gp + uu * V, gv[uu]);
+    }
+    __syncthreads();
+    if (p.softmax) softmax_k<K, 1>(m, 0);
+    if (!l.active) return;
+    scale_offsets<K>(d, p.offset_scale);
+
+    const int cpp = CPP_ ? CPP_ : p.cpp;
+    const int rw = RW_ ? RW_ : p.RW;
+    const int rowc = rw * cpp;
+    const int lby = l.ho * p.sh - p.ph - a.ry0, lbx = l.wo * p.sw - p.pw - a.rx0;
+    const int ty = a.ry0 + 1, tx = a.rx0 + 1;
+    const size_t pair = pixel * p.G + l.g;
+    float2 *go = reinterpret_cast<float2 *>(goff) + pair * K;
+    float *gm = gmask ? gmask + pair * K : nullptr;
+    unsigned far = 0;
+    float dot = 0.0f;  // sum_k m_k g_k (softmax)
+    // g_k and grad_offset_k of tap k from its corner dots; g_k goes straight to
+    // grad_mask (the softmax rewrites it at the end)
+    auto grads = [&](int k, float mk, float uy, float fy, float ux, float fx, float d00, float d01,
+                     float d10, float d11) __attribute__((always_inline)) {
+        const float gk = uy * (ux * d00 + fx * d01) + fy * (ux * d10 + fx * d11);
+        dot = fmaf(mk, gk, dot);
+        if (gm) gm[k] = gk;
+        if (goff) {
+            const float sc = p.offset_scale * mk;
+            go[k] = make_float2(sc * (uy * (d01 - d00) + fy * (d11 - d10)),
+                                sc * (ux * (d10 - d00) + fx * (d11 - d01)));
+        }
+    };
+    // units (tap k, chunk uu) in order, the next unit's four corner reads issued before
+    // this unit's dots; a tap's dots are complete after its last chunk
+    struct TapG {
+        float fy, uy, fx, ux;
+        bool inreg;
+    };
+    constexpr int NU = K * NC;
+    TapG tg[2];
+    int cellk[2];
+    uint4 cb[2][4];
+    auto issue = [&](int n) __attribute__((always_inline)) {
+        const int k = n / NC, uu = n % NC;
+        TapG &t = tg[k & 1];
+        if (uu == 0) {
+            const int i = k / 3, j = k - (k / 3) * 3;
+            int ly, lx;
+            split_coord_fu(lby + i * p.dh, d[2 * k + 1], ly, t.fy, t.uy);
+            split_coord_fu(lbx + j * p.dw, d[2 * k], lx, t.fx, t.ux);
+            t.inreg = (unsigned)ly <= (unsigned)(p.RH - 2) && (unsigned)lx <= (unsigned)(rw - 2);
+            const bool touch = (unsigned)(ly + ty) <= (unsigned)p.H && (unsigned)(lx + tx) <= (unsigned)p.W;
+            far |= (!t.inreg && touch) ? (1u << k) : 0u;
+            cellk[k & 1] = t.inreg ? (int)__umul24((unsigned)ly, (unsigned)rowc) + lx * cpp : 0;
+        }
+        const uint4 *q = lds + cellk[k & 1] + l.gl * NC + uu;
+        cb[n & 1][0] = q[0];
+        cb[n & 1][1] = q[cpp];
+        cb[n & 1][2] = q[rowc];
+        cb[n & 1][3] = q[rowc + cpp];
+    };
+    float d00 = 0.0f, d01 = 0.0f, d10 = 0.0f, d11 = 0.0f;
+    auto accum = [&](int n) __attribute__((always_inline)) {
+        const int k = n / NC, uu = n % NC;
+        float va[V], vb[V], vc[V], ve[V];
+        unpack<E, V>(cb[n & 1][0], va);
+        unpack<E, V>(cb[n & 1][1], vb);
+        unpack<E, V>(cb[n & 1][2], vc);
+        unpack<E, V>(cb[n & 1][3], ve);
+#pragma unroll
+        for (int z = 0; z < V; ++z) {
+            d00 = fmaf(gv[uu][z], va[z], d00);
+            d01 = fmaf(gv[uu][z], vb[z], d01);
+            d10 = fmaf(gv[uu][z], vc[z], d10);
+            d11 = fmaf(gv[uu][z], ve[z], d11);
+        }
+        if (uu == NC - 1) {
+            const TapG &t = tg[k & 1];
+            if (!t.inreg) d00 = d01 = d10 = d11 = 0.0f;  // outside the image, or redone below
+            grads(k, m[k], t.uy, t.fy, t.ux, t.fx, d00, d01, d10, d11);
+            d00 = d01 = d10 = d11 = 0.0f;
+        }
+    };
+    issue(0);
+#pragma unroll
+    for (int n = 0; n < NU; ++n) {
+        if (n + 1 < NU) issue(n + 1);
+        accum(n);
+    }
+    if (far) {  // deferred global pass (rare): taps leaving the region
+        const Bt *img = x + (size_t)a.n * p.H * p.W * GC + (size_t)l.g * p.C;
+        const float2 *coff = reinterpret_cast<const float2 *>(offset) + pair * K;
+        const int by0 = l.ho * p.sh - p.ph, bx0 = l.wo * p.sw - p.pw;
+        while (far) {
+            const int k = __builtin_ctz(far);
+            far &= far - 1;
+            const float2 dv = coff[k];
+            float dx = dv.x, dy = dv.y;
+            if (p.offset_scale != 1.0f) {
+                dx = mul_rn(p.offset_scale, dx);
+                dy = mul_rn(p.offset_scale, dy);
+            }
+            const int i = k / 3, j = k - (k / 3) * 3;
+            int y0, x0;
+            float fy, uy, fx, ux;
+            split_coord_fu(by0 + i * p.dh, dy, y0, fy, uy);
+            split_coord_fu(bx0 + j * p.dw, dx, x0, fx, ux);
+            const bool vy0 = (unsigned)y0 < (unsigned)p.H, vy1 = (unsigned)(y0 + 1) < (unsigned)p.H;
+            const bool vx0 = (unsigned)x0 < (unsigned)p.W, vx1 = (unsigned)(x0 + 1) < (unsigned)p.W;
+            const int yc0 = min(max(y0, 0), p.H - 1), yc1 = min(max(y0 + 1, 0), p.H - 1);
+            const int xc0 = min(max(x0, 0), p.W - 1), xc1 = min(max(x0 + 1, 0), p.W - 1);
+            const Bt *r0 = img + (size_t)yc0 * p.W * GC, *r1 = img + (size_t)yc1 * p.W * GC;
+            uint4 c[NC][4];
+#pragma unroll
+            for (int uu = 0; uu < NC; ++uu) {
+                c[uu][0] = *reinterpret_cast<const uint4 *>(r0 + (size_t)xc0 * GC + uu * V);
+                c[uu][1] = *reinterpret_cast<const uint4 *>(r0 + (size_t)xc1 * GC + uu * V);
+                c[uu][2] = *reinterpret_cast<const uint4 *>(r1 + (size_t)xc0 * GC + uu * V);
+                c[uu][3] = *reinterpret_cast<const uint4 *>(r1 + (size_t)xc1 * GC + uu * V);
+            }
+            float d00 = 0.0f, d01 = 0.0f, d10 = 0.0f, d11 = 0.0f;
+            dots4<E, NC>(c, gv, d00, d01, d10, d11);
+            if (!(vy0 && vx0)) d00 = 0.0f;
+            if (!(vy0 && vx1)) d01 = 0.0f;
+            if (!(vy1 && vx0)) d10 = 0.0f;
+            if (!(vy1 && vx1)) d11 = 0.0f;
+            float mk = m[0];
+#pragma unroll
+            for (int kk = 1; kk < K; ++kk) mk = (kk == k) ? m[kk] : mk;
+            grads(k, mk, uy, fy, ux, fx, d00, d01, d10, d11);  // adds m_k g_k to dot (was 0)
+        }
+    }
+    if (gm && p.softmax) {  // grad_logit_k = m_k (g_k - sum_j m_j g_j), g_k as stored above
+#pragma unroll
+        for (int k = 0; k < K; ++k) gm[k] = m[k] * (gm[k] - dot);
+    }
 }
 
 // --------------------------------------------------------------- launching --
@@ -534,11 +733,57 @@ bool plan_core_tile(const CoreLaunch &a, TileParams &p) {
     return true;
 }
 
+template <class E, int NC>
+hipError_t launch_bwd_tile_nc(const CoreLaunch &a, const TileParams &p, float *goff, float *gmask,
+                              hipStream_t stream) {
+    using Bt = typename E::bits;
+    const Bt *x = static_cast<const Bt *>(a.x);
+    const Bt *gout = static_cast<const Bt *>(a.out);
+    const float *off = static_cast<const float *>(a.offset);
+    const float *msk = static_cast<const float *>(a.mask);
+    auto go = [&](auto kern) {
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+            DCN_TILE_LDS_BYTES);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL(kern, dim3(p.nblocks), dim3(p.threads), p.lds_bytes, stream, x, off, msk, gout,
+                           goff, gmask, p);
+        return hipGetLastError();
+    };
+    if (p.cpp == 4 && p.RW == 35) return go(dcn_core_bwd_tile_kernel<E, NC, 4, 35>);
+    if (p.cpp == 2 && p.RW == 35) return go(dcn_core_bwd_tile_kernel<E, NC, 2, 35>);
+    return go(dcn_core_bwd_tile_kernel<E, NC, 0, 0>);
+}
+
+template <class E>
+hipError_t launch_bwd_tile_e(const CoreLaunch &a, const TileParams &p, float *goff, float *gmask,
+                             hipStream_t stream) {
+    if constexpr (E::id == DCN_BF16) {
+        return launch_bwd_tile_nc<E, 1>(a, p, goff, gmask, stream);
+    } else {
+        return p.NC == 2 ? launch_bwd_tile_nc<E, 2>(a, p, goff, gmask, stream)
+                         : launch_bwd_tile_nc<E, 1>(a, p, goff, gmask, stream);
+    }
+}
+
 hipError_t launch_dcn_core_tile(const CoreLaunch &a, const TileParams &p, hipStream_t stream) {
     switch (a.dtype) {
         case DCN_F32: return launch_tile_e<EF32>(a, p, stream);
         case DCN_F16: return launch_tile_e<EF16>(a, p, stream);
         case DCN_BF16: return launch_tile_e<EBF16>(a, p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+// grad_offset / grad_mask of the core backward on the tile plan p (S == 1, fp32 plain
+// offsets): a.out carries grad_out.
+hipError_t launch_dcn_core_bwd_tile(const CoreLaunch &a, const TileParams &p, float *goff, float *gmask,
+                                    hipStream_t stream) {
+    if (p.S != 1 || a.kh != 3 || a.kw != 3) return hipErrorInvalidValue;
+    switch (a.dtype) {
+        case DCN_F32: return launch_bwd_tile_e<EF32>(a, p, goff, gmask, stream);
+        case DCN_F16: return launch_bwd_tile_e<EF16>(a, p, goff, gmask, stream);
+        case DCN_BF16: return launch_bwd_tile_e<EBF16>(a, p, goff, gmask, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -71,6 +71,10 @@ struct CoreTilePlan {
 };
 bool plan_core_tile(const CoreLaunch &a, CoreTilePlan &plan);
 hipError_t launch_dcn_core_tile(const CoreLaunch &a, const CoreTilePlan &plan, hipStream_t stream);
+// grad_offset / grad_mask of the core backward on a forward tile plan with S == 1 and
+// plain fp32 offsets (a.out = grad_out); hipErrorInvalidValue for other plans.
+hipError_t launch_dcn_core_bwd_tile(const CoreLaunch &a, const CoreTilePlan &plan, float *goff,
+                                    float *gmask, hipStream_t stream);
 
 // Workspace plan of the DCNv2 path (all offsets 256-byte aligned).
 struct V2Plan {

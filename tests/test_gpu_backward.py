@@ -221,6 +221,23 @@ def test_backward_atomic_fallback(gpu, monkeypatch, name, args, extra):
     _say(name, check_all(r, o, c["dtype"], name))
 
 
+PAIR_GRADS = ["f32_vec4_tails", "f16_vec8", "f32_far_offsets", "f32_softmax", "f16_many_groups"]
+
+
+@pytest.mark.parametrize("name", PAIR_GRADS)
+def test_backward_pair_pass_gradients(gpu, monkeypatch, name):
+    """grad_offset / grad_mask from the pair pass (DCN_CORE_BWD_NO_TILE=1) on shapes whose
+    default path computes them in the LDS-tiled kernel: both paths meet the bound."""
+    args, extra = {n: (a, e) for n, a, e in BWD_SWEEP}[name]
+    monkeypatch.setenv("DCN_CORE_BWD_NO_TILE", "1")
+    c = wl.core_case(seed=100 + len(name), **args)
+    go = wl.core_grad_out(c, seed=len(name))
+    _say("core backward pair-pass gradients", name)
+    r = run_bwd(c, go, **extra)
+    o = oracle_bwd(c, go, **extra)
+    _say(name, check_all(r, o, c["dtype"], name))
+
+
 def test_backward_empty_batch(gpu):
     x = torch.zeros((0, 4, 4, 8), device="cuda")
     off = torch.zeros((0, 4, 4, 2, 9, 2), device="cuda")
