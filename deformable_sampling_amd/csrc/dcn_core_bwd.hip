@@ -878,7 +878,8 @@ hipError_t launch_e(const CoreBwdLaunch &a, const CoreBwdPlan &pl, hipStream_t s
     p.PB = 4 * p.Q;
     p.nblocks = (p.npairs + p.PB - 1) / p.PB;
 
-    p.dots = 1;
+    // the corner dots feed grad_offset / grad_mask, and in the fallback the grad_x adds
+    p.dots = (a.grad_offset || a.grad_mask || !bin) ? 1 : 0;
     char *ws = static_cast<char *>(a.workspace);
     hipError_t err;
     // grad_offset / grad_mask on the forward's LDS halo tiles where a tile plan with one
