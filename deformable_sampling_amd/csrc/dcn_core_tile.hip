@@ -449,7 +449,6 @@ __global__ __launch_bounds__(1024) void dcn_core_bwd_tile_kernel(const typename 
     }
     __syncthreads();
     if (p.softmax) softmax_k<K, 1>(m, 0);
-    if (!l.active) return;
     scale_offsets<K>(d, p.offset_scale);
 
     const int cpp = CPP_ ? CPP_ : p.cpp;
@@ -458,126 +457,172 @@ __global__ __launch_bounds__(1024) void dcn_core_bwd_tile_kernel(const typename 
     const int lby = l.ho * p.sh - p.ph - a.ry0, lbx = l.wo * p.sw - p.pw - a.rx0;
     const int ty = a.ry0 + 1, tx = a.rx0 + 1;
     const size_t pair = pixel * p.G + l.g;
-    float2 *go = reinterpret_cast<float2 *>(goff) + pair * K;
-    float *gm = gmask ? gmask + pair * K : nullptr;
     unsigned far = 0;
     float dot = 0.0f;  // sum_k m_k g_k (softmax)
-    // g_k and grad_offset_k of tap k from its corner dots; g_k goes straight to
-    // grad_mask (the softmax rewrites it at the end)
+    // With the region geometry compiled in, a pair's 27 results wait in registers and
+    // leave through LDS in coalesced runs; the generic variant (more address registers)
+    // stores each tap's results directly.
+    constexpr bool kStage = CPP_ != 0;
+    float rg[K];   // g_k, then grad_mask_k (kStage)
+    float2 ro[K];  // grad_offset_k (kStage)
+    float2 *go = reinterpret_cast<float2 *>(goff) + pair * K;
+    float *gmp = gmask ? gmask + pair * K : nullptr;
+    // g_k and grad_offset_k of tap k (a compile-time index) from its corner dots
     auto grads = [&](int k, float mk, float uy, float fy, float ux, float fx, float d00, float d01,
                      float d10, float d11) __attribute__((always_inline)) {
         const float gk = uy * (ux * d00 + fx * d01) + fy * (ux * d10 + fx * d11);
         dot = fmaf(mk, gk, dot);
-        if (gm) gm[k] = gk;
-        if (goff) {
-            const float sc = p.offset_scale * mk;
-            go[k] = make_float2(sc * (uy * (d01 - d00) + fy * (d11 - d10)),
-                                sc * (ux * (d10 - d00) + fx * (d11 - d01)));
+        const float sc = p.offset_scale * mk;
+        const float2 o = make_float2(sc * (uy * (d01 - d00) + fy * (d11 - d10)),
+                                     sc * (ux * (d10 - d00) + fx * (d11 - d01)));
+        if constexpr (kStage) {
+            rg[k] = gk;
+            ro[k] = o;
+        } else {
+            if (gmp) gmp[k] = gk;
+            if (goff) go[k] = o;
         }
     };
-    // units (tap k, chunk uu) in order, the next unit's four corner reads issued before
-    // this unit's dots; a tap's dots are complete after its last chunk
-    struct TapG {
-        float fy, uy, fx, ux;
-        bool inreg;
-    };
-    constexpr int NU = K * NC;
-    TapG tg[2];
-    int cellk[2];
-    uint4 cb[2][4];
-    auto issue = [&](int n) __attribute__((always_inline)) {
-        const int k = n / NC, uu = n % NC;
-        TapG &t = tg[k & 1];
-        if (uu == 0) {
-            const int i = k / 3, j = k - (k / 3) * 3;
-            int ly, lx;
-            split_coord_fu(lby + i * p.dh, d[2 * k + 1], ly, t.fy, t.uy);
-            split_coord_fu(lbx + j * p.dw, d[2 * k], lx, t.fx, t.ux);
-            t.inreg = (unsigned)ly <= (unsigned)(p.RH - 2) && (unsigned)lx <= (unsigned)(rw - 2);
-            const bool touch = (unsigned)(ly + ty) <= (unsigned)p.H && (unsigned)(lx + tx) <= (unsigned)p.W;
-            far |= (!t.inreg && touch) ? (1u << k) : 0u;
-            cellk[k & 1] = t.inreg ? (int)__umul24((unsigned)ly, (unsigned)rowc) + lx * cpp : 0;
-        }
-        const uint4 *q = lds + cellk[k & 1] + l.gl * NC + uu;
-        cb[n & 1][0] = q[0];
-        cb[n & 1][1] = q[cpp];
-        cb[n & 1][2] = q[rowc];
-        cb[n & 1][3] = q[rowc + cpp];
-    };
-    float d00 = 0.0f, d01 = 0.0f, d10 = 0.0f, d11 = 0.0f;
-    auto accum = [&](int n) __attribute__((always_inline)) {
-        const int k = n / NC, uu = n % NC;
-        float va[V], vb[V], vc[V], ve[V];
-        unpack<E, V>(cb[n & 1][0], va);
-        unpack<E, V>(cb[n & 1][1], vb);
-        unpack<E, V>(cb[n & 1][2], vc);
-        unpack<E, V>(cb[n & 1][3], ve);
-#pragma unroll
-        for (int z = 0; z < V; ++z) {
-            d00 = fmaf(gv[uu][z], va[z], d00);
-            d01 = fmaf(gv[uu][z], vb[z], d01);
-            d10 = fmaf(gv[uu][z], vc[z], d10);
-            d11 = fmaf(gv[uu][z], ve[z], d11);
-        }
-        if (uu == NC - 1) {
-            const TapG &t = tg[k & 1];
-            if (!t.inreg) d00 = d01 = d10 = d11 = 0.0f;  // outside the image, or redone below
-            grads(k, m[k], t.uy, t.fy, t.ux, t.fx, d00, d01, d10, d11);
-            d00 = d01 = d10 = d11 = 0.0f;
-        }
-    };
-    issue(0);
-#pragma unroll
-    for (int n = 0; n < NU; ++n) {
-        if (n + 1 < NU) issue(n + 1);
-        accum(n);
-    }
-    if (far) {  // deferred global pass (rare): taps leaving the region
-        const Bt *img = x + (size_t)a.n * p.H * p.W * GC + (size_t)l.g * p.C;
-        const float2 *coff = reinterpret_cast<const float2 *>(offset) + pair * K;
-        const int by0 = l.ho * p.sh - p.ph, bx0 = l.wo * p.sw - p.pw;
-        while (far) {
-            const int k = __builtin_ctz(far);
-            far &= far - 1;
-            const float2 dv = coff[k];
-            float dx = dv.x, dy = dv.y;
-            if (p.offset_scale != 1.0f) {
-                dx = mul_rn(p.offset_scale, dx);
-                dy = mul_rn(p.offset_scale, dy);
-            }
-            const int i = k / 3, j = k - (k / 3) * 3;
-            int y0, x0;
+    if (l.active) {
+        // units (tap k, chunk uu) in order, the next unit's four corner reads issued
+        // before this unit's dots; a tap's dots are complete after its last chunk
+        struct TapG {
             float fy, uy, fx, ux;
-            split_coord_fu(by0 + i * p.dh, dy, y0, fy, uy);
-            split_coord_fu(bx0 + j * p.dw, dx, x0, fx, ux);
-            const bool vy0 = (unsigned)y0 < (unsigned)p.H, vy1 = (unsigned)(y0 + 1) < (unsigned)p.H;
-            const bool vx0 = (unsigned)x0 < (unsigned)p.W, vx1 = (unsigned)(x0 + 1) < (unsigned)p.W;
-            const int yc0 = min(max(y0, 0), p.H - 1), yc1 = min(max(y0 + 1, 0), p.H - 1);
-            const int xc0 = min(max(x0, 0), p.W - 1), xc1 = min(max(x0 + 1, 0), p.W - 1);
-            const Bt *r0 = img + (size_t)yc0 * p.W * GC, *r1 = img + (size_t)yc1 * p.W * GC;
-            uint4 c[NC][4];
-#pragma unroll
-            for (int uu = 0; uu < NC; ++uu) {
-                c[uu][0] = *reinterpret_cast<const uint4 *>(r0 + (size_t)xc0 * GC + uu * V);
-                c[uu][1] = *reinterpret_cast<const uint4 *>(r0 + (size_t)xc1 * GC + uu * V);
-                c[uu][2] = *reinterpret_cast<const uint4 *>(r1 + (size_t)xc0 * GC + uu * V);
-                c[uu][3] = *reinterpret_cast<const uint4 *>(r1 + (size_t)xc1 * GC + uu * V);
+            bool inreg;
+        };
+        constexpr int NU = K * NC;
+        TapG tg[2];
+        int cellk[2];
+        uint4 cb[2][4];
+        auto issue = [&](int n) __attribute__((always_inline)) {
+            const int k = n / NC, uu = n % NC;
+            TapG &t = tg[k & 1];
+            if (uu == 0) {
+                const int i = k / 3, j = k - (k / 3) * 3;
+                int ly, lx;
+                split_coord_fu(lby + i * p.dh, d[2 * k + 1], ly, t.fy, t.uy);
+                split_coord_fu(lbx + j * p.dw, d[2 * k], lx, t.fx, t.ux);
+                t.inreg = (unsigned)ly <= (unsigned)(p.RH - 2) && (unsigned)lx <= (unsigned)(rw - 2);
+                const bool touch = (unsigned)(ly + ty) <= (unsigned)p.H && (unsigned)(lx + tx) <= (unsigned)p.W;
+                far |= (!t.inreg && touch) ? (1u << k) : 0u;
+                cellk[k & 1] = t.inreg ? (int)__umul24((unsigned)ly, (unsigned)rowc) + lx * cpp : 0;
             }
-            float d00 = 0.0f, d01 = 0.0f, d10 = 0.0f, d11 = 0.0f;
-            dots4<E, NC>(c, gv, d00, d01, d10, d11);
-            if (!(vy0 && vx0)) d00 = 0.0f;
-            if (!(vy0 && vx1)) d01 = 0.0f;
-            if (!(vy1 && vx0)) d10 = 0.0f;
-            if (!(vy1 && vx1)) d11 = 0.0f;
-            float mk = m[0];
+            const uint4 *q = lds + cellk[k & 1] + l.gl * NC + uu;
+            cb[n & 1][0] = q[0];
+            cb[n & 1][1] = q[cpp];
+            cb[n & 1][2] = q[rowc];
+            cb[n & 1][3] = q[rowc + cpp];
+        };
+        float d00 = 0.0f, d01 = 0.0f, d10 = 0.0f, d11 = 0.0f;
+        auto accum = [&](int n) __attribute__((always_inline)) {
+            const int k = n / NC, uu = n % NC;
+            float va[V], vb[V], vc[V], ve[V];
+            unpack<E, V>(cb[n & 1][0], va);
+            unpack<E, V>(cb[n & 1][1], vb);
+            unpack<E, V>(cb[n & 1][2], vc);
+            unpack<E, V>(cb[n & 1][3], ve);
 #pragma unroll
-            for (int kk = 1; kk < K; ++kk) mk = (kk == k) ? m[kk] : mk;
-            grads(k, mk, uy, fy, ux, fx, d00, d01, d10, d11);  // adds m_k g_k to dot (was 0)
+            for (int z = 0; z < V; ++z) {
+                d00 = fmaf(gv[uu][z], va[z], d00);
+                d01 = fmaf(gv[uu][z], vb[z], d01);
+                d10 = fmaf(gv[uu][z], vc[z], d10);
+                d11 = fmaf(gv[uu][z], ve[z], d11);
+            }
+            if (uu == NC - 1) {
+                const TapG &t = tg[k & 1];
+                if (!t.inreg) d00 = d01 = d10 = d11 = 0.0f;  // outside the image, or redone below
+                grads(k, m[k], t.uy, t.fy, t.ux, t.fx, d00, d01, d10, d11);
+                d00 = d01 = d10 = d11 = 0.0f;
+            }
+        };
+        issue(0);
+#pragma unroll
+        for (int n = 0; n < NU; ++n) {
+            if (n + 1 < NU) issue(n + 1);
+            accum(n);
+        }
+        if (far) {  // deferred global pass (rare): taps leaving the region
+            const Bt *img = x + (size_t)a.n * p.H * p.W * GC + (size_t)l.g * p.C;
+            const float2 *coff = reinterpret_cast<const float2 *>(offset) + pair * K;
+            const int by0 = l.ho * p.sh - p.ph, bx0 = l.wo * p.sw - p.pw;
+            while (far) {
+                const int k = __builtin_ctz(far);
+                far &= far - 1;
+                const float2 dv = coff[k];
+                float dx = dv.x, dy = dv.y;
+                if (p.offset_scale != 1.0f) {
+                    dx = mul_rn(p.offset_scale, dx);
+                    dy = mul_rn(p.offset_scale, dy);
+                }
+                const int i = k / 3, j = k - (k / 3) * 3;
+                int y0, x0;
+                float fy, uy, fx, ux;
+                split_coord_fu(by0 + i * p.dh, dy, y0, fy, uy);
+                split_coord_fu(bx0 + j * p.dw, dx, x0, fx, ux);
+                const bool vy0 = (unsigned)y0 < (unsigned)p.H, vy1 = (unsigned)(y0 + 1) < (unsigned)p.H;
+                const bool vx0 = (unsigned)x0 < (unsigned)p.W, vx1 = (unsigned)(x0 + 1) < (unsigned)p.W;
+                const int yc0 = min(max(y0, 0), p.H - 1), yc1 = min(max(y0 + 1, 0), p.H - 1);
+                const int xc0 = min(max(x0, 0), p.W - 1), xc1 = min(max(x0 + 1, 0), p.W - 1);
+                const Bt *r0 = img + (size_t)yc0 * p.W * GC, *r1 = img + (size_t)yc1 * p.W * GC;
+                uint4 c[NC][4];
+#pragma unroll
+                for (int uu = 0; uu < NC; ++uu) {
+                    c[uu][0] = *reinterpret_cast<const uint4 *>(r0 + (size_t)xc0 * GC + uu * V);
+                    c[uu][1] = *reinterpret_cast<const uint4 *>(r0 + (size_t)xc1 * GC + uu * V);
+                    c[uu][2] = *reinterpret_cast<const uint4 *>(r1 + (size_t)xc0 * GC + uu * V);
+                    c[uu][3] = *reinterpret_cast<const uint4 *>(r1 + (size_t)xc1 * GC + uu * V);
+                }
+                float e00 = 0.0f, e01 = 0.0f, e10 = 0.0f, e11 = 0.0f;
+                dots4<E, NC>(c, gv, e00, e01, e10, e11);
+                if (!(vy0 && vx0)) e00 = 0.0f;
+                if (!(vy0 && vx1)) e01 = 0.0f;
+                if (!(vy1 && vx0)) e10 = 0.0f;
+                if (!(vy1 && vx1)) e11 = 0.0f;
+                // results go to registers: select the tap at compile time (its LDS pass
+                // added 0 to dot)
+#pragma unroll
+                for (int kk = 0; kk < K; ++kk)
+                    if (kk == k) grads(kk, m[kk], uy, fy, ux, fx, e00, e01, e10, e11);
+            }
+        }
+        if (p.softmax) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                if constexpr (kStage) rg[k] = m[k] * (rg[k] - dot);
+                else if (gmp) gmp[k] = m[k] * (gmp[k] - dot);
+            }
         }
     }
-    if (gm && p.softmax) {  // grad_logit_k = m_k (g_k - sum_j m_j g_j), g_k as stored above
+    if constexpr (!kStage) return;
+    // Stores through LDS (the region is no longer read): each pair's 27 results in a
+    // staging row, then the block writes every pixel's run of GB pairs (GB*18 floats of
+    // grad_offset, GB*9 of grad_mask, contiguous in memory) with consecutive lanes on
+    // consecutive 8- or 4-byte pieces.
+    __syncthreads();
+    float *stg = reinterpret_cast<float *>(lds);
+    const int tid = threadIdx.x;
+    if (l.active) {
+        float *row = stg + (size_t)tid * 27;  // tid = q * GB + gl (one lane per pair)
 #pragma unroll
-        for (int k = 0; k < K; ++k) gm[k] = m[k] * (gm[k] - dot);
+        for (int k = 0; k < K; ++k) {
+            row[2 * k] = ro[k].x;
+            row[2 * k + 1] = ro[k].y;
+            row[18 + k] = rg[k];
+        }
+    }
+    __syncthreads();
+    const int npix = p.TH * p.TW, GB = p.GB;
+    const int run2 = GB * K;  // float2 pieces of grad_offset per pixel (= grad_mask floats)
+    for (int t = tid; t < npix * run2; t += blockDim.x) {
+        const int q = t / run2, j = t - q * run2;
+        const int qy = q / p.TW, qx = q - qy * p.TW;
+        const int ho = a.ho0 + qy, wo = a.wo0 + qx;
+        if (ho >= p.Ho || wo >= p.Wo) continue;
+        const int gl = j / K, k = j - gl * K;
+        const float *row = stg + (size_t)(q * GB + gl) * 27;
+        const size_t pr = (((size_t)a.n * p.Ho + ho) * p.Wo + wo) * p.G + a.g0 + gl;
+        if (goff) reinterpret_cast<float2 *>(goff)[pr * K + k] = make_float2(row[2 * k], row[2 * k + 1]);
+        if (gmask) gmask[pr * K + k] = row[18 + k];
     }
 }
 
@@ -746,7 +791,9 @@ hipError_t launch_bwd_tile_nc(const CoreLaunch &a, const TileParams &p, float *g
             reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
             DCN_TILE_LDS_BYTES);
         if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL(kern, dim3(p.nblocks), dim3(p.threads), p.lds_bytes, stream, x, off, msk, gout,
+        const size_t stage = (size_t)p.threads * 27 * sizeof(float);  // one staging row per pair
+        const size_t lds = p.lds_bytes > stage ? p.lds_bytes : stage;
+        hipLaunchKernelGGL(kern, dim3(p.nblocks), dim3(p.threads), lds, stream, x, off, msk, gout,
                            goff, gmask, p);
         return hipGetLastError();
     };
