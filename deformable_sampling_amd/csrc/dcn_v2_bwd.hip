@@ -97,18 +97,32 @@ __device__ __forceinline__ void v2b_softmax_stats(const float *__restrict__ mask
 // ------------------------------------------------------------ layout prep --
 
 // goT[co][p] = grad_out[n][co][hw] for p = n*HWo + hw; zero for co >= Cout or p >= P.
+// VEC: 8 consecutive pixels per thread (HWo and P multiples of 8, 16-byte aligned rows).
+template <bool VEC>
 __global__ __launch_bounds__(kB) void v2b_rows_kernel(const uint16_t *__restrict__ gout,
                                                       uint16_t *__restrict__ goT, int Cout, int HWo,
                                                       long long P, long long Pp, long long total) {
     const long long t = (long long)blockIdx.x * kB + threadIdx.x;
-    if (t >= total) return;
-    const long long co = t / Pp, pp = t - co * Pp;
-    uint16_t v = 0;
-    if (co < Cout && pp < P) {
-        const long long n = pp / HWo, hw = pp - n * HWo;
-        v = gout[((size_t)n * Cout + co) * HWo + hw];
+    if constexpr (VEC) {
+        if (t * 8 >= total) return;
+        const long long e = t * 8;
+        const long long co = e / Pp, pp = e - co * Pp;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (co < Cout && pp < P) {
+            const long long n = pp / HWo, hw = pp - n * HWo;
+            v = *reinterpret_cast<const uint4 *>(gout + ((size_t)n * Cout + co) * HWo + hw);
+        }
+        *reinterpret_cast<uint4 *>(goT + e) = v;
+    } else {
+        if (t >= total) return;
+        const long long co = t / Pp, pp = t - co * Pp;
+        uint16_t v = 0;
+        if (co < Cout && pp < P) {
+            const long long n = pp / HWo, hw = pp - n * HWo;
+            v = gout[((size_t)n * Cout + co) * HWo + hw];
+        }
+        goT[t] = v;
     }
-    goT[t] = v;
 }
 
 // wT[r][co] = weight[co][ci][k] for r = k*Cin_pad + ci; zero for padding entries.
@@ -183,21 +197,20 @@ __global__ __launch_bounds__(kB) void v2b_colT_kernel(const uint16_t *__restrict
     }
 }
 
-// grad_weight[co][ci][k] = sum over splits of part[s][co][k*Cin_pad + ci].
+// grad_weight[co][ci][k] = sum over splits of part[s][co][k*Cin_pad + ci]: threads run
+// over (co, r) so the partial rows are read contiguously; the writes are strided by K.
 __global__ __launch_bounds__(kB) void v2b_wsum_kernel(const float *__restrict__ part,
                                                       float *__restrict__ gw, int Cout, int Cin,
                                                       int K, int Cin_pad, int R, int splits) {
     const long long t = (long long)blockIdx.x * kB + threadIdx.x;
-    const long long total = (long long)Cout * Cin * K;
-    if (t >= total) return;
-    const int k = (int)(t % K);
-    const long long cc = t / K;
-    const int ci = (int)(cc % Cin), co = (int)(cc / Cin);
-    const size_t idx = (size_t)co * R + (size_t)k * Cin_pad + ci;
+    if (t >= (long long)Cout * R) return;
+    const int co = (int)(t / R), r = (int)(t - (long long)co * R);
+    const int k = r / Cin_pad, ci = r - k * Cin_pad;
+    if (ci >= Cin) return;
     const size_t stride = (size_t)Cout * R;
     float s = 0.0f;
-    for (int i = 0; i < splits; ++i) s += part[i * stride + idx];
-    gw[t] = s;
+    for (int i = 0; i < splits; ++i) s += part[i * stride + t];
+    gw[((size_t)co * Cin + ci) * K + k] = s;
 }
 
 // ---------------------------------------------------------------- buckets --
@@ -495,9 +508,13 @@ hipError_t launch_e(const V2BwdLaunch &a, hipStream_t stream) {
     }
     if (want_w) {
         const long long nrows = (long long)pl.CoM * pl.Pp;
-        hipLaunchKernelGGL(v2b_rows_kernel, dim3((unsigned)((nrows + kB - 1) / kB)), dim3(kB), 0, stream,
-                           static_cast<const uint16_t *>(a.grad_out), goT, a.Cout, HWo, pl.P, pl.Pp,
-                           nrows);
+        const uint16_t *gsrc = static_cast<const uint16_t *>(a.grad_out);
+        if (HWo % 8 == 0 && (uintptr_t)gsrc % 16 == 0)  // then P % 8 == 0 too
+            hipLaunchKernelGGL((v2b_rows_kernel<true>), dim3((unsigned)((nrows / 8 + kB - 1) / kB)), dim3(kB),
+                               0, stream, gsrc, goT, a.Cout, HWo, pl.P, pl.Pp, nrows);
+        else
+            hipLaunchKernelGGL((v2b_rows_kernel<false>), dim3((unsigned)((nrows + kB - 1) / kB)), dim3(kB),
+                               0, stream, gsrc, goT, a.Cout, HWo, pl.P, pl.Pp, nrows);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         // 2. transposed columns
         V2bColParams cp;
@@ -523,7 +540,7 @@ hipError_t launch_e(const V2BwdLaunch &a, hipStream_t stream) {
         hipLaunchKernelGGL((v2_gemm_kernel<E, 1>), dim3(gp.nblocks), dim3(kGemmThreads), 0, stream,
                            goT, colT, wpart, gp);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        const long long nw = (long long)a.Cout * a.Cin * pl.K;
+        const long long nw = (long long)a.Cout * pl.R;
         hipLaunchKernelGGL(v2b_wsum_kernel, dim3((unsigned)((nw + kB - 1) / kB)), dim3(kB), 0, stream,
                            wpart, a.grad_weight, a.Cout, a.Cin, pl.K, pl.Cin_pad, pl.R, pl.splits);
         if ((err = hipGetLastError()) != hipSuccess) return err;
