@@ -423,8 +423,8 @@ def main():
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the forward path has no cross-GPU exchange "
-              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the path has no cross-GPU exchange (it shards "
+              "by image with nothing to exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -25,7 +25,7 @@
  *             [B, N*H*W, C], spatial shapes, scale start index, sampling
  *             locations, weights) and section 7 (softmax-normalised weights).
  *
- * Readings where the pages are silent (each listed in the design doc):
+ * Readings where the pages are silent:
  *  - zero outside the image, per corner;
  *  - grid base = out*stride - pad + tap*dilation;
  *  - offset pairs are (dx, dy), x first;
