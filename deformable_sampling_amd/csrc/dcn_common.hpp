@@ -53,6 +53,16 @@ __device__ __forceinline__ void load_f32(const typename E::bits *p, float (&f)[V
     for (int i = 0; i < V; ++i) f[i] = to_f32(E{}, b[i]);
 }
 
+// The V = 16/sizeof elements of one 16-byte chunk as fp32.
+template <class E, int V>
+__device__ __forceinline__ void unpack(const uint4 &r, float (&f)[V]) {
+    using B = typename E::bits;
+    B b[V];
+    __builtin_memcpy(b, &r, 16);
+#pragma unroll
+    for (int i = 0; i < V; ++i) f[i] = to_f32(E{}, b[i]);
+}
+
 // Store V fp32 values as V consecutive elements at p (aligned to V*sizeof).
 template <class E, int V>
 __device__ __forceinline__ void store_f32(typename E::bits *p, const float (&f)[V]) {

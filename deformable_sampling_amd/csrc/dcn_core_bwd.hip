@@ -820,6 +820,166 @@ hipError_t launch_pair_v(int V, const CoreBwdLaunch &a, const BwdParams &p, floa
     return hipErrorInvalidValue;
 }
 
+// The gather for a group slice of one or two 16-byte chunks (C * elt = 16 or 32: the
+// lane of a pixel owns one chunk). The cell sort also copies each record's grad_out
+// slice into LDS, so the four destination pixels of a record read it from LDS instead
+// of each fetching it from memory; records pass in chunks of kStageCap (three blocks
+// fit a CU).
+constexpr int kStageCap = 992;
+
+template <class E, int NCH>
+__global__ __launch_bounds__(256 * NCH) void bwd_gather_staged_kernel(
+    const uint4 *__restrict__ rec, const unsigned *__restrict__ starts,
+    const typename E::bits *__restrict__ gout, typename E::bits *__restrict__ gx, GatherParams q) {
+    constexpr int V = 16 / (int)sizeof(typename E::bits);
+    __shared__ uint4 s_g[kStageCap][NCH];   // cell-sorted: the record's grad_out slice
+    __shared__ float4 s_w[kStageCap];       // cell-sorted: the four corner weights m*w_ab
+    __shared__ unsigned short s_cell[kStageCap];
+    __shared__ unsigned s_cnt[kCells * kCells];
+    __shared__ unsigned s_pos[kCells * kCells];
+    __shared__ unsigned s_fill[kCells * kCells];
+
+    const int nthreads = kTile * kTile * NCH;
+    const int tid = threadIdx.x;
+    const int blk = xcd_remap((int)blockIdx.x, q.nblocks);
+    const int g = blk % q.G;
+    const int t1 = blk / q.G;
+    const int ntile = q.TYr * q.TXr;
+    const int n = t1 / ntile;
+    const int tile = t1 - n * ntile;
+    const int tyi = tile / q.TXr, txi = tile - tyi * q.TXr;
+    const int ng = n * q.G + g;
+
+    int rb[5], re[5], sy[5], sx[5];
+    {
+        auto base = [&](int yy, int xx) { return ((ng * q.TY + yy) * q.TX + xx) << 2; };
+        const int own = base(tyi, txi);
+        rb[0] = (int)starts[own]; re[0] = (int)starts[own + 4]; sy[0] = 0; sx[0] = 0;
+        for (int r = 1; r < 5; ++r) { rb[r] = re[r] = 0; sy[r] = sx[r] = 0; }
+        if (tyi + 1 < q.TY) {
+            const int d = base(tyi + 1, txi);
+            rb[1] = (int)starts[d + 1]; re[1] = (int)starts[d + 2]; sy[1] = kTile;
+            rb[2] = (int)starts[d + 3]; re[2] = (int)starts[d + 4]; sy[2] = kTile;
+        }
+        if (txi + 1 < q.TX) {
+            const int r = base(tyi, txi + 1);
+            rb[3] = (int)starts[r + 2]; re[3] = (int)starts[r + 4]; sx[3] = kTile;
+        }
+        if (tyi + 1 < q.TY && txi + 1 < q.TX) {
+            const int dr = base(tyi + 1, txi + 1);
+            rb[4] = (int)starts[dr + 3]; re[4] = (int)starts[dr + 4]; sy[4] = kTile; sx[4] = kTile;
+        }
+    }
+    int total = 0;
+    for (int r = 0; r < 5; ++r) total += re[r] - rb[r];
+
+    const int dp = tid / NCH, s = tid - dp * NCH;
+    const int qy = dp / kTile, qx = dp - qy * kTile;
+    const int Y = tyi * kTile + qy, X = txi * kTile + qx;
+    const bool inside = Y < q.H && X < q.W;
+    const int GC = q.G * q.C;
+    const size_t gbase = (size_t)n * q.Ho * q.Wo * GC + (size_t)g * q.C;
+    float acc[V];
+#pragma unroll
+    for (int u = 0; u < V; ++u) acc[u] = 0.0f;
+
+    for (int c0 = 0; c0 < total; c0 += kStageCap) {
+        const int nrec = min(kStageCap, total - c0);
+        __syncthreads();  // the previous chunk's readers are done
+        for (int i = tid; i < kCells * kCells; i += nthreads) {
+            s_cnt[i] = 0;
+            s_fill[i] = 0;
+        }
+        __syncthreads();
+        auto locate = [&](int r, int &k, int &gi) {
+            gi = c0 + r;
+            k = 0;
+            while (k < 4 && gi >= re[k] - rb[k]) {
+                gi -= re[k] - rb[k];
+                ++k;
+            }
+        };
+        for (int r = tid; r < nrec; r += nthreads) {
+            int k, gi;
+            locate(r, k, gi);
+            const unsigned vx = rec[rb[k] + gi].x;
+            const int cell = ((int)((vx >> 4) & 15u) + sy[k]) * kCells + (int)(vx & 15u) + sx[k];
+            s_cell[r] = (unsigned short)cell;
+            atomicAdd(&s_cnt[cell], 1u);
+        }
+        __syncthreads();
+        if (tid < 64) {  // exclusive scan of the 289 cell counts by one wavefront
+            constexpr int kPer = (kCells * kCells + 63) / 64;
+            unsigned v[kPer], sum = 0;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int c = tid * kPer + i;
+                v[i] = c < kCells * kCells ? s_cnt[c] : 0u;
+                sum += v[i];
+            }
+            unsigned incl = sum;
+            for (int o = 1; o < 64; o <<= 1) {
+                const unsigned w = __shfl_up(incl, o, 64);
+                if (tid >= o) incl += w;
+            }
+            unsigned run = incl - sum;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int c = tid * kPer + i;
+                if (c < kCells * kCells) s_pos[c] = run;
+                run += v[i];
+            }
+        }
+        __syncthreads();
+        // counting sort by cell: weights, and the grad_out slice fetched once per record
+        for (int r = tid; r < nrec; r += nthreads) {
+            int k, gi;
+            locate(r, k, gi);
+            const uint4 v = rec[rb[k] + gi];
+            const int cell = s_cell[r];
+            const unsigned at = s_pos[cell] + atomicAdd(&s_fill[cell], 1u);
+            int cyy, cxx;
+            float fy, uy, fx, ux;
+            split_coord_fu(0, __uint_as_float(v.y), cyy, fy, uy);
+            split_coord_fu(0, __uint_as_float(v.z), cxx, fx, ux);
+            const float m = __uint_as_float(v.w);
+            const float my0 = m * uy, my1 = m * fy;
+            s_w[at] = make_float4(my0 * ux, my0 * fx, my1 * ux, my1 * fx);
+            const uint4 *src = reinterpret_cast<const uint4 *>(gout + gbase + (size_t)(v.x >> 8) * GC);
+#pragma unroll
+            for (int u = 0; u < NCH; ++u) s_g[at][u] = src[u];
+        }
+        __syncthreads();
+        if (inside) {
+            const float *sw = reinterpret_cast<const float *>(s_w);
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const int cell = (qy + 1 - a) * kCells + (qx + 1 - b);
+                    const int i0 = (int)s_pos[cell], i1 = i0 + (int)s_cnt[cell];
+                    for (int i = i0; i < i1; ++i) {
+                        const float w = sw[4 * i + 2 * a + b];
+                        float gv[V];
+                        unpack<E, V>(s_g[i][s], gv);
+#pragma unroll
+                        for (int u = 0; u < V; ++u) acc[u] = fmaf(w, gv[u], acc[u]);
+                    }
+                }
+            }
+        }
+    }
+    if (inside)
+        store_f32<E, V>(gx + ((size_t)(n * q.H + Y) * q.W + X) * GC + g * q.C + s * V, acc);
+}
+
+// DCN_CORE_BWD_UNSTAGED=1 keeps the gather that reads grad_out from memory per visit
+// (tests cover both)
+bool core_bwd_unstaged() {
+    const char *e = getenv("DCN_CORE_BWD_UNSTAGED");
+    return e && e[0] == '1';
+}
+
 template <class E>
 hipError_t launch_gather(int V, const CoreBwdLaunch &a, const GatherParams &q, const uint4 *rec,
                          const unsigned *starts, hipStream_t stream) {
@@ -827,6 +987,17 @@ hipError_t launch_gather(int V, const CoreBwdLaunch &a, const GatherParams &q, c
     using B = typename E::bits;
     const B *go = static_cast<const B *>(a.grad_out);
     B *gx = static_cast<B *>(a.grad_x);
+    const int cbytes = a.C * elt;
+    if ((cbytes == 16 || cbytes == 32) && (uintptr_t)go % 16 == 0 && (uintptr_t)gx % 16 == 0 &&
+        !core_bwd_unstaged()) {
+        const int nch = cbytes / 16;
+        const dim3 grid(q.nblocks), block(kTile * kTile * nch);
+        if (nch == 2)
+            hipLaunchKernelGGL((bwd_gather_staged_kernel<E, 2>), grid, block, 0, stream, rec, starts, go, gx, q);
+        else
+            hipLaunchKernelGGL((bwd_gather_staged_kernel<E, 1>), grid, block, 0, stream, rec, starts, go, gx, q);
+        return hipGetLastError();
+    }
     const dim3 grid(q.nblocks), block(kTile * kTile * q.S);
     switch (V) {
         case 8:

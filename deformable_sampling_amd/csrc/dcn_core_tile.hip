@@ -34,15 +34,6 @@ using TileParams = CoreTilePlan;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-template <class E, int V>
-__device__ __forceinline__ void unpack(const uint4 &r, float (&f)[V]) {
-    using B = typename E::bits;
-    B b[V];
-    __builtin_memcpy(b, &r, 16);
-#pragma unroll
-    for (int i = 0; i < V; ++i) f[i] = to_f32(E{}, b[i]);
-}
-
 // Tile t -> (image, tile row, tile column, group block), group block fastest: the
 // group blocks of one tile share every input cache line, so consecutive tiles (which
 // run on one XCD) fetch each line into one L2.

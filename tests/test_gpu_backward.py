@@ -238,6 +238,19 @@ def test_backward_pair_pass_gradients(gpu, monkeypatch, name):
     _say(name, check_all(r, o, c["dtype"], name))
 
 
+@pytest.mark.parametrize("name", ["f32_vec4_tails", "f16_vec8", "f16_many_groups", "f32_far_offsets"])
+def test_backward_unstaged_gather(gpu, monkeypatch, name):
+    """grad_x through the gather that reads grad_out per visit (DCN_CORE_BWD_UNSTAGED=1) on
+    shapes whose default gather stages each record's grad_out slice in LDS."""
+    args, extra = {n: (a, e) for n, a, e in BWD_SWEEP}[name]
+    monkeypatch.setenv("DCN_CORE_BWD_UNSTAGED", "1")
+    c = wl.core_case(seed=100 + len(name), **args)
+    go = wl.core_grad_out(c, seed=len(name))
+    r = run_bwd(c, go, **extra)
+    o = oracle_bwd(c, go, **extra)
+    _say(name, check_all(r, o, c["dtype"], name))
+
+
 def test_backward_empty_batch(gpu):
     x = torch.zeros((0, 4, 4, 8), device="cuda")
     off = torch.zeros((0, 4, 4, 2, 9, 2), device="cuda")
