@@ -194,6 +194,44 @@ __device__ __forceinline__ int block_bin_slot(unsigned *s_key, unsigned *s_cnt, 
     return slot;
 }
 
+// Bins near a block's output tile are counted in a directly indexed LDS window
+// instead of the hash table: kWin x kWin input tiles (x 4 sub-bins) around the tile
+// holding the grid base of the output tile's first pixel, which covers the taps of
+// a stride-1 3x3 tile with offsets up to about +-16 px. Other bins use the table.
+constexpr int kWin = 5;
+constexpr int kWinSlots = kWin * kWin * 4;
+
+__device__ __forceinline__ int floor_div16(int v) { return v >= 0 ? v / kTile : -((-v + kTile - 1) / kTile); }
+
+struct BinWin {
+    int ty0, tx0;  // first input-tile row / column of the window
+};
+
+__device__ __forceinline__ BinWin bin_window(int ho0, int wo0, const BwdParams &p) {
+    BinWin w;
+    w.ty0 = floor_div16(ho0 * p.sh - p.ph + 1) - 2;
+    w.tx0 = floor_div16(wo0 * p.sw - p.pw + 1) - 2;
+    return w;
+}
+
+// Window slot of a home bin (its tile and sub-bin from home_bin's arithmetic), or -1.
+__device__ __forceinline__ int win_slot(int y0, int x0, const BinWin &w) {
+    const int ty = (y0 + 1) / kTile, tx = (x0 + 1) / kTile;  // y0, x0 >= -1 here
+    const int wy = ty - w.ty0, wx = tx - w.tx0;
+    if ((unsigned)wy >= (unsigned)kWin || (unsigned)wx >= (unsigned)kWin) return -1;
+    const int ly = y0 + 1 - ty * kTile, lx = x0 + 1 - tx * kTile;
+    const int sub = (ly == 0 ? 1 : 0) | (lx == 0 ? 2 : 0);
+    return (wy * kWin + wx) * 4 + sub;
+}
+
+// The global bin of window slot s for (image n, group g).
+__device__ __forceinline__ unsigned win_bin(int s, int n, int g, const BinWin &w, const BwdParams &p) {
+    const int sub = s & 3, t = s >> 2;
+    const int ty = w.ty0 + t / kWin, tx = w.tx0 + t % kWin;
+    return ((((unsigned)(n * p.G + g) * (unsigned)p.TY + (unsigned)ty) * (unsigned)p.TX + (unsigned)tx)
+            << 2) | (unsigned)sub;
+}
+
 // 1. Samples per home bin. A block takes the 256 pairs of one output tile of one
 // group (tiled order) and its samples tap-fastest; it counts them per bin in LDS
 // and adds one count per distinct bin to the global counters.
@@ -201,11 +239,12 @@ template <int KH, int KW>
 __global__ __launch_bounds__(kThreads) void bwd_count_kernel(const float *__restrict__ offset,
                                                              unsigned *__restrict__ counts,
                                                              BwdParams p) {
-    __shared__ unsigned s_key[kHash], s_cnt[kHash];
+    __shared__ unsigned s_key[kHash], s_cnt[kHash], s_win[kWinSlots];
     for (int i = threadIdx.x; i < kHash; i += kThreads) {
         s_key[i] = kEmpty;
         s_cnt[i] = 0;
     }
+    for (int i = threadIdx.x; i < kWinSlots; i += kThreads) s_win[i] = 0;
     __syncthreads();
     const int kh = KH > 0 ? KH : p.kh, kw = KW > 0 ? KW : p.kw, K = kh * kw;
     const int blk = xcd_remap((int)blockIdx.x, (int)gridDim.x);  // (image, tile, group)
@@ -213,6 +252,7 @@ __global__ __launch_bounds__(kThreads) void bwd_count_kernel(const float *__rest
     decode_pair<true>(blk * kThreads, p, n, g, pix0);  // local pixel 0 of the tile
     const int tile = (blk / p.G) % p.otiles;
     const int oy = (tile / p.TXo) * kTile, ox = (tile % p.TXo) * kTile;
+    const BinWin win = bin_window(oy, ox, p);
     const float2 *od = reinterpret_cast<const float2 *>(offset);
     for (int r = 0; r < K; ++r) {
         const int idx = r * kThreads + (int)threadIdx.x;  // sample: local pair idx/K, tap idx%K
@@ -228,6 +268,13 @@ __global__ __launch_bounds__(kThreads) void bwd_count_kernel(const float *__rest
             split_coord_fu(ho * p.sh - p.ph + i * p.dh, mul_rn(p.offset_scale, d.y), y0, f, u);
             split_coord_fu(wo * p.sw - p.pw + j * p.dw, mul_rn(p.offset_scale, d.x), x0, f, u);
             want = home_bin(y0, x0, n, g, p, bin, local);
+            if (want) {
+                const int ws = win_slot(y0, x0, win);
+                if (ws >= 0) {
+                    atomicAdd(&s_win[ws], 1u);
+                    want = false;
+                }
+            }
         }
         if (want && block_bin_slot(s_key, s_cnt, bin, rank) == kHash)
             atomicAdd(&counts[bin], 1u);  // table full: direct
@@ -235,6 +282,8 @@ __global__ __launch_bounds__(kThreads) void bwd_count_kernel(const float *__rest
     __syncthreads();
     for (int i = threadIdx.x; i < kHash; i += kThreads)
         if (s_cnt[i]) atomicAdd(&counts[s_key[i]], s_cnt[i]);
+    for (int i = threadIdx.x; i < kWinSlots; i += kThreads)
+        if (s_win[i]) atomicAdd(&counts[win_bin(i, n, g, win, p)], s_win[i]);
 }
 
 // 2. Exclusive prefix sum of nb counts (one block of 1024 threads, 4096 counts
@@ -452,12 +501,19 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(
     if constexpr (BIN) {
         if (p.want_x) {
             __shared__ unsigned s_key[kHash], s_cnt[kHash], s_base[kHash], s_lim[kHash];
-            __shared__ unsigned s_sr[kBinMaxSamples];  // slot << 24 | cell << 16 | rank
+            __shared__ unsigned s_wcnt[kWinSlots], s_wbase[kWinSlots], s_wlim[kWinSlots];
+            __shared__ unsigned s_sr[kBinMaxSamples];  // slot << 20 | cell << 12 | rank
             for (int i = threadIdx.x; i < kHash; i += kThreads) {
                 s_key[i] = kEmpty;
                 s_cnt[i] = 0;
             }
+            for (int i = threadIdx.x; i < kWinSlots; i += kThreads) s_wcnt[i] = 0;
             __syncthreads();
+            // the bin window applies when the block's pairs are one (image, tile, group)
+            const int unit = pair0 >> 8;
+            const bool use_win = (unit == ((pair0 + npb - 1) >> 8));
+            const int ug = unit % p.G, un = (unit / p.G) / p.otiles, utile = (unit / p.G) % p.otiles;
+            const BinWin win = bin_window((utile / p.TXo) * kTile, (utile % p.TXo) * kTile, p);
             const int ns = npb * K;  // <= kBinMaxSamples (the host caps PB * K)
             for (int idx = threadIdx.x; idx < ns; idx += kThreads) {
                 const int lq = idx / K, k = idx - lq * K;
@@ -474,16 +530,22 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(
                     split_coord_fu(wo2 * p.sw - p.pw + j * p.dw, mul_rn(p.offset_scale, d.x), x0, f, u);
                     unsigned bin, local, rank = 0;
                     if (home_bin(y0, x0, nn, gg, p, bin, local)) {
-                        const int slot = block_bin_slot(s_key, s_cnt, bin, rank);
-                        if (slot < kHash) {
-                            code = ((unsigned)slot << 24) | (local << 16) | rank;
-                        } else {  // table full: reserve directly
-                            const unsigned at = starts[bin] + atomicAdd(&fill[bin], 1u);
-                            if (at < starts[bin + 1])
-                                rec[at] = make_uint4(((unsigned)pp << 8) | local,
-                                                     __float_as_uint(mul_rn(p.offset_scale, d.y)),
-                                                     __float_as_uint(mul_rn(p.offset_scale, d.x)),
-                                                     __float_as_uint(s_m[idx]));
+                        const int ws = use_win ? win_slot(y0, x0, win) : -1;
+                        if (ws >= 0) {
+                            rank = atomicAdd(&s_wcnt[ws], 1u);
+                            code = ((unsigned)(kHash + ws) << 20) | (local << 12) | rank;
+                        } else {
+                            const int slot = block_bin_slot(s_key, s_cnt, bin, rank);
+                            if (slot < kHash) {
+                                code = ((unsigned)slot << 20) | (local << 12) | rank;
+                            } else {  // table full: reserve directly
+                                const unsigned at = starts[bin] + atomicAdd(&fill[bin], 1u);
+                                if (at < starts[bin + 1])
+                                    rec[at] = make_uint4(((unsigned)pp << 8) | local,
+                                                         __float_as_uint(mul_rn(p.offset_scale, d.y)),
+                                                         __float_as_uint(mul_rn(p.offset_scale, d.x)),
+                                                         __float_as_uint(s_m[idx]));
+                            }
                         }
                     }
                 }
@@ -497,15 +559,24 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(
                     s_lim[i] = starts[key + 1];
                 }
             }
+            for (int i = threadIdx.x; i < kWinSlots; i += kThreads) {
+                if (s_wcnt[i]) {
+                    const unsigned key = win_bin(i, un, ug, win, p);
+                    s_wbase[i] = starts[key] + atomicAdd(&fill[key], s_wcnt[i]);
+                    s_wlim[i] = starts[key + 1];
+                }
+            }
             __syncthreads();
             for (int idx = threadIdx.x; idx < ns; idx += kThreads) {
                 const unsigned code = s_sr[idx];
                 if (code == 0xffffffffu) continue;
-                const int slot = (int)(code >> 24);
+                const int slot = (int)(code >> 20);
                 const float2 d = reinterpret_cast<const float2 *>(s_off)[idx];
-                const unsigned at = s_base[slot] + (code & 0xffffu);
-                if (at < s_lim[slot])
-                    rec[at] = make_uint4(((unsigned)s_phw[idx / K] << 8) | ((code >> 16) & 0xffu),
+                const unsigned base = slot < kHash ? s_base[slot] : s_wbase[slot - kHash];
+                const unsigned lim = slot < kHash ? s_lim[slot] : s_wlim[slot - kHash];
+                const unsigned at = base + (code & 0xfffu);
+                if (at < lim)
+                    rec[at] = make_uint4(((unsigned)s_phw[idx / K] << 8) | ((code >> 12) & 0xffu),
                                          __float_as_uint(mul_rn(p.offset_scale, d.y)),
                                          __float_as_uint(mul_rn(p.offset_scale, d.x)),
                                          __float_as_uint(s_m[idx]));
