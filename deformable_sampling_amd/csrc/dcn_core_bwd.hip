@@ -148,89 +148,11 @@ __device__ __forceinline__ bool decode_pair(int e, const BwdParams &p, int &n, i
     }
 }
 
-// Home bin of a sample whose bilinear cell has top-left corner (y0, x0); false
-// when no corner of the cell is inside the image. The home tile holds the corner
-// (y0+1, x0+1); `local` packs the cell's position in that tile (4 bits each).
-__device__ __forceinline__ bool home_bin(int y0, int x0, int n, int g, const BwdParams &p,
-                                         unsigned &bin, unsigned &local) {
-    if (y0 < -1 || y0 > p.H - 1 || x0 < -1 || x0 > p.W - 1) return false;
-    const int ty = (y0 + 1) / kTile, tx = (x0 + 1) / kTile;
-    const int ly = y0 + 1 - ty * kTile, lx = x0 + 1 - tx * kTile;
-    const unsigned sub = (ly == 0 ? 1u : 0u) | (lx == 0 ? 2u : 0u);
-    bin = ((((unsigned)(n * p.G + g) * (unsigned)p.TY + (unsigned)ty) * (unsigned)p.TX +
-            (unsigned)tx) << 2) | sub;
-    local = ((unsigned)ly << 4) | (unsigned)lx;
-    return true;
-}
-
-// Block-level aggregation of bin counters: an LDS hash table (open addressing,
-// kHash slots) from bin to a local count. block_bin_slot() inserts a sample's bin
-// and returns its slot and its rank among the block's samples of that bin (the
-// integer LDS atomics used here are fast); a full table returns kHash and the
-// caller falls back to a global atomic for that sample.
-constexpr int kHash = 256;
-constexpr unsigned kEmpty = 0xffffffffu;
 // samples per block of the pair pass: PB * K <= 4 * (65536 / (28 * K)) * K < 2344
 constexpr int kBinMaxSamples = 2344;
 
-__device__ __forceinline__ int hash_insert(unsigned *s_key, unsigned bin) {
-    unsigned h = (bin * 2654435761u) >> 24;
-    for (int probe = 0; probe < kHash; ++probe) {
-        const unsigned cur = atomicCAS(&s_key[h], kEmpty, bin);
-        if (cur == kEmpty || cur == bin) return (int)h;
-        h = (h + 1) & (kHash - 1);
-    }
-    return kHash;
-}
-
-// Slot of `bin` in the table and the sample's rank among the block's samples of
-// that bin (kHash when the table is full). Callers spread a block's samples over
-// its lanes tap-fastest, so the lanes of one instruction mostly hold different
-// bins and rarely contend on one LDS word.
-__device__ __forceinline__ int block_bin_slot(unsigned *s_key, unsigned *s_cnt, unsigned bin,
-                                              unsigned &rank) {
-    const int slot = hash_insert(s_key, bin);
-    if (slot < kHash) rank = atomicAdd(&s_cnt[slot], 1u);
-    return slot;
-}
-
-// Bins near a block's output tile are counted in a directly indexed LDS window
-// instead of the hash table: kWin x kWin input tiles (x 4 sub-bins) around the tile
-// holding the grid base of the output tile's first pixel, which covers the taps of
-// a stride-1 3x3 tile with offsets up to about +-16 px. Other bins use the table.
-constexpr int kWin = 5;
-constexpr int kWinSlots = kWin * kWin * 4;
-
-__device__ __forceinline__ int floor_div16(int v) { return v >= 0 ? v / kTile : -((-v + kTile - 1) / kTile); }
-
-struct BinWin {
-    int ty0, tx0;  // first input-tile row / column of the window
-};
-
-__device__ __forceinline__ BinWin bin_window(int ho0, int wo0, const BwdParams &p) {
-    BinWin w;
-    w.ty0 = floor_div16(ho0 * p.sh - p.ph + 1) - 2;
-    w.tx0 = floor_div16(wo0 * p.sw - p.pw + 1) - 2;
-    return w;
-}
-
-// Window slot of a home bin (its tile and sub-bin from home_bin's arithmetic), or -1.
-__device__ __forceinline__ int win_slot(int y0, int x0, const BinWin &w) {
-    const int ty = (y0 + 1) / kTile, tx = (x0 + 1) / kTile;  // y0, x0 >= -1 here
-    const int wy = ty - w.ty0, wx = tx - w.tx0;
-    if ((unsigned)wy >= (unsigned)kWin || (unsigned)wx >= (unsigned)kWin) return -1;
-    const int ly = y0 + 1 - ty * kTile, lx = x0 + 1 - tx * kTile;
-    const int sub = (ly == 0 ? 1 : 0) | (lx == 0 ? 2 : 0);
-    return (wy * kWin + wx) * 4 + sub;
-}
-
-// The global bin of window slot s for (image n, group g).
-__device__ __forceinline__ unsigned win_bin(int s, int n, int g, const BinWin &w, const BwdParams &p) {
-    const int sub = s & 3, t = s >> 2;
-    const int ty = w.ty0 + t / kWin, tx = w.tx0 + t % kWin;
-    return ((((unsigned)(n * p.G + g) * (unsigned)p.TY + (unsigned)ty) * (unsigned)p.TX + (unsigned)tx)
-            << 2) | (unsigned)sub;
-}
+#include "core_bwd_bins.hpp"
+static_assert(kBinTile == kTile, "bins and destination tiles share their edge");
 
 // 1. Samples per home bin. A block takes the 256 pairs of one output tile of one
 // group (tiled order) and its samples tap-fastest; it counts them per bin in LDS
@@ -1082,6 +1004,13 @@ hipError_t launch_gather(int V, const CoreBwdLaunch &a, const GatherParams &q, c
     return hipGetLastError();
 }
 
+// DCN_CORE_BWD_TILE_NO_RECORDS=1 leaves the grad_x records to the pair pass even when
+// the tiled gradient kernel could file them (tests cover both)
+bool core_bwd_tile_no_records() {
+    const char *e = getenv("DCN_CORE_BWD_TILE_NO_RECORDS");
+    return e && e[0] == '1';
+}
+
 // DCN_CORE_BWD_NO_TILE=1 keeps grad_offset / grad_mask in the pair pass (tests compare
 // both paths)
 bool core_bwd_no_tile() {
@@ -1125,29 +1054,29 @@ hipError_t launch_e(const CoreBwdLaunch &a, const CoreBwdPlan &pl, hipStream_t s
     char *ws = static_cast<char *>(a.workspace);
     hipError_t err;
     // grad_offset / grad_mask on the forward's LDS halo tiles where a tile plan with one
-    // lane per pair applies (then the pair pass only files the grad_x records, or does
-    // not run); the atomic fallback keeps its dots, which carry the grad_x adds
-    if ((a.grad_offset || a.grad_mask) && (bin || !a.grad_x) && !core_bwd_no_tile()) {
-        CoreLaunch c;
-        c.x = a.x; c.offset = a.offset; c.mask = a.mask; c.out = const_cast<void *>(a.grad_out);
-        c.N = a.N; c.H = a.H; c.W = a.W; c.G = a.G; c.C = a.C; c.kh = a.kh; c.kw = a.kw;
-        c.sh = a.sh; c.sw = a.sw; c.ph = a.ph; c.pw = a.pw; c.dh = a.dh; c.dw = a.dw;
-        c.Ho = a.Ho; c.Wo = a.Wo;
-        c.offset_scale = a.offset_scale;
-        c.softmax = a.softmax;
-        c.dtype = a.dtype;
-        c.om_dtype = DCN_F32;
-        c.om_plain = true;
-        c.off_grp = 2 * K; c.off_pix = a.G * 2 * K; c.mask_grp = K; c.mask_pix = a.G * K;
-        CoreTilePlan tp;
-        if (a.kh == 3 && a.kw == 3 && plan_core_tile(c, tp) && tp.S == 1) {
-            if ((err = launch_dcn_core_bwd_tile(c, tp, a.grad_offset, a.grad_mask, stream)) != hipSuccess)
-                return err;
-            p.dots = 0;
-            p.want_off = 0;
-            p.want_mask = 0;
-            if (!a.grad_x) return hipSuccess;
-        }
+    // lane per pair applies; that kernel then also files the grad_x records where its
+    // variant can, else the pair pass files them (without dots). The atomic fallback
+    // keeps the pair pass's dots, which carry its grad_x adds.
+    CoreLaunch c;
+    c.x = a.x; c.offset = a.offset; c.mask = a.mask; c.out = const_cast<void *>(a.grad_out);
+    c.N = a.N; c.H = a.H; c.W = a.W; c.G = a.G; c.C = a.C; c.kh = a.kh; c.kw = a.kw;
+    c.sh = a.sh; c.sw = a.sw; c.ph = a.ph; c.pw = a.pw; c.dh = a.dh; c.dw = a.dw;
+    c.Ho = a.Ho; c.Wo = a.Wo;
+    c.offset_scale = a.offset_scale;
+    c.softmax = a.softmax;
+    c.dtype = a.dtype;
+    c.om_dtype = DCN_F32;
+    c.om_plain = true;
+    c.off_grp = 2 * K; c.off_pix = a.G * 2 * K; c.mask_grp = K; c.mask_pix = a.G * K;
+    CoreTilePlan tp;
+    const bool tile = (a.grad_offset || a.grad_mask) && (bin || !a.grad_x) && !core_bwd_no_tile() &&
+                      a.kh == 3 && a.kw == 3 && plan_core_tile(c, tp) && tp.S == 1;
+    if (tile) {
+        p.dots = 0;
+        p.want_off = 0;
+        p.want_mask = 0;
+        if (!a.grad_x)
+            return launch_dcn_core_bwd_tile(c, tp, a.grad_offset, a.grad_mask, nullptr, nullptr, stream);
     }
     if (bin) {
         unsigned *counts = reinterpret_cast<unsigned *>(ws + pl.off_counts);
@@ -1166,7 +1095,16 @@ hipError_t launch_e(const CoreBwdLaunch &a, const CoreBwdPlan &pl, hipStream_t s
             hipLaunchKernelGGL((bwd_count_kernel<0, 0>), cgrid, dim3(kThreads), 0, stream, a.offset, counts, p);
         hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, starts, (int)nb);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        if ((err = launch_pair_v<E, true>(V, a, p, nullptr, rec, starts, fill, stream)) != hipSuccess)
+        bool rec_done = false;
+        if (tile) {
+            const CoreRecArgs ra = {rec, starts, fill, pl.TY, pl.TX};
+            if ((err = launch_dcn_core_bwd_tile(c, tp, a.grad_offset, a.grad_mask,
+                                                core_bwd_tile_no_records() ? nullptr : &ra, &rec_done,
+                                                stream)) != hipSuccess)
+                return err;
+        }
+        if (!rec_done &&
+            (err = launch_pair_v<E, true>(V, a, p, nullptr, rec, starts, fill, stream)) != hipSuccess)
             return err;
         GatherParams q;
         q.N = a.N; q.G = a.G; q.C = a.C; q.H = a.H; q.W = a.W; q.Ho = a.Ho; q.Wo = a.Wo;

@@ -31,6 +31,13 @@ __device__ __attribute__((aligned(16))) uint4 g_dcn_zero_chunk[1];
 namespace {
 
 using TileParams = CoreTilePlan;
+
+#include "core_bwd_bins.hpp"
+
+// Bin grid of the grad_x records in the terms the bin helpers use.
+struct RecGrid {
+    int H, W, G, TY, TX, sh, sw, ph, pw;
+};
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
@@ -417,7 +424,8 @@ __global__ __launch_bounds__(1024) void dcn_core_bwd_tile_kernel(const typename 
                                                                  const typename E::bits *__restrict__ gout,
                                                                  float *__restrict__ goff,
                                                                  float *__restrict__ gmask,
-                                                                 const TileParams p) {
+                                                                 const TileParams p,
+                                                                 const CoreRecArgs ra) {
     using Bt = typename E::bits;
     constexpr int V = 16 / (int)sizeof(Bt);
     constexpr int K = 9;
@@ -615,6 +623,94 @@ __global__ __launch_bounds__(1024) void dcn_core_bwd_tile_kernel(const typename 
         if (goff) reinterpret_cast<float2 *>(goff)[pr * K + k] = make_float2(row[2 * k], row[2 * k + 1]);
         if (gmask) gmask[pr * K + k] = row[18 + k];
     }
+    if (!ra.rec) return;  // uniform over the grid
+
+    // grad_x records (the record pass of the core backward, done here while the
+    // offsets are in cache): one 16-byte record per sample with a cell inside the
+    // image, filed in its home bin. Bins in the window around this tile (per group
+    // of the block) are ranked with plain LDS atomics, others through a hash table;
+    // then one range per bin and block is reserved and the records are written.
+    unsigned *s_key = reinterpret_cast<unsigned *>(stg + (size_t)blockDim.x * 27);
+    unsigned *s_hcnt = s_key + kHash, *s_hbase = s_hcnt + kHash, *s_hlim = s_hbase + kHash;
+    unsigned *s_wcnt = s_hlim + kHash;                 // [GB][kWinSlots]
+    unsigned *s_wbase = s_wcnt + GB * kWinSlots, *s_wlim = s_wbase + GB * kWinSlots;
+    for (int i = tid; i < kHash; i += blockDim.x) {
+        s_key[i] = kEmpty;
+        s_hcnt[i] = 0;
+    }
+    for (int i = tid; i < GB * kWinSlots; i += blockDim.x) s_wcnt[i] = 0;
+    __syncthreads();
+    RecGrid rg2;
+    rg2.H = p.H; rg2.W = p.W; rg2.G = p.G; rg2.TY = ra.TY; rg2.TX = ra.TX;
+    rg2.sh = p.sh; rg2.sw = p.sw; rg2.ph = p.ph; rg2.pw = p.pw;
+    const BinWin win = bin_window(a.ho0, a.wo0, rg2);
+    unsigned code[K];
+    float2 dk[K];
+    const int by0 = l.ho * p.sh - p.ph, bx0 = l.wo * p.sw - p.pw;
+    const unsigned pix_in_image = (unsigned)(l.ho * p.Wo + l.wo);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        code[k] = 0xffffffffu;
+        dk[k] = make_float2(0.0f, 0.0f);
+        if (!l.active) continue;
+        float2 dv = reinterpret_cast<const float2 *>(offset)[pair * K + k];
+        if (p.offset_scale != 1.0f) {
+            dv.x = mul_rn(p.offset_scale, dv.x);
+            dv.y = mul_rn(p.offset_scale, dv.y);
+        }
+        dk[k] = dv;
+        const int i = k / 3, j = k - (k / 3) * 3;
+        int y0, x0;
+        float f, u;
+        split_coord_fu(by0 + i * p.dh, dv.y, y0, f, u);
+        split_coord_fu(bx0 + j * p.dw, dv.x, x0, f, u);
+        unsigned bin, local, rank = 0;
+        if (!home_bin(y0, x0, a.n, l.g, rg2, bin, local)) continue;
+        const int ws = win_slot(y0, x0, win);
+        if (ws >= 0) {
+            const int slot = l.gl * kWinSlots + ws;
+            rank = atomicAdd(&s_wcnt[slot], 1u);
+            code[k] = ((unsigned)(kHash + slot) << 20) | (local << 12) | rank;
+        } else {
+            const int slot = block_bin_slot(s_key, s_hcnt, bin, rank);
+            if (slot < kHash) {
+                code[k] = ((unsigned)slot << 20) | (local << 12) | rank;
+            } else {  // table full: reserve directly
+                const unsigned at = ra.starts[bin] + atomicAdd(&ra.fill[bin], 1u);
+                if (at < ra.starts[bin + 1])
+                    ra.rec[at] = make_uint4((pix_in_image << 8) | local, __float_as_uint(dv.y),
+                                            __float_as_uint(dv.x), __float_as_uint(m[k]));
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < kHash; i += blockDim.x) {
+        if (s_hcnt[i]) {
+            const unsigned key = s_key[i];
+            s_hbase[i] = ra.starts[key] + atomicAdd(&ra.fill[key], s_hcnt[i]);
+            s_hlim[i] = ra.starts[key + 1];
+        }
+    }
+    for (int i = tid; i < GB * kWinSlots; i += blockDim.x) {
+        if (s_wcnt[i]) {
+            const unsigned key = win_bin(i % kWinSlots, a.n, a.g0 + i / kWinSlots, win, rg2);
+            s_wbase[i] = ra.starts[key] + atomicAdd(&ra.fill[key], s_wcnt[i]);
+            s_wlim[i] = ra.starts[key + 1];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const unsigned c = code[k];
+        if (c == 0xffffffffu) continue;
+        const int slot = (int)(c >> 20);
+        const unsigned base = slot < kHash ? s_hbase[slot] : s_wbase[slot - kHash];
+        const unsigned lim = slot < kHash ? s_hlim[slot] : s_wlim[slot - kHash];
+        const unsigned at = base + (c & 0xfffu);
+        if (at < lim)
+            ra.rec[at] = make_uint4((pix_in_image << 8) | ((c >> 12) & 0xffu), __float_as_uint(dk[k].y),
+                                    __float_as_uint(dk[k].x), __float_as_uint(m[k]));
+    }
 }
 
 // --------------------------------------------------------------- launching --
@@ -771,7 +867,12 @@ bool plan_core_tile(const CoreLaunch &a, TileParams &p) {
 
 template <class E, int NC>
 hipError_t launch_bwd_tile_nc(const CoreLaunch &a, const TileParams &p, float *goff, float *gmask,
-                              hipStream_t stream) {
+                              const CoreRecArgs *ra, bool *rec_done, hipStream_t stream) {
+    // the variants with the region geometry compiled in also file the grad_x records
+    CoreRecArgs rec = {};
+    const bool staged = p.RW == 35 && (p.cpp == 4 || p.cpp == 2);
+    if (ra && staged) rec = *ra;
+    if (rec_done) *rec_done = rec.rec != nullptr;
     using Bt = typename E::bits;
     const Bt *x = static_cast<const Bt *>(a.x);
     const Bt *gout = static_cast<const Bt *>(a.out);
@@ -782,10 +883,12 @@ hipError_t launch_bwd_tile_nc(const CoreLaunch &a, const TileParams &p, float *g
             reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
             DCN_TILE_LDS_BYTES);
         if (attr != hipSuccess) return attr;
-        const size_t stage = (size_t)p.threads * 27 * sizeof(float);  // one staging row per pair
+        // one staging row per pair, then the record pass's hash table and bin windows
+        const size_t stage = (size_t)p.threads * 27 * sizeof(float) +
+                             (size_t)(4 * kHash + 3 * p.GB * kWinSlots) * sizeof(unsigned);
         const size_t lds = p.lds_bytes > stage ? p.lds_bytes : stage;
         hipLaunchKernelGGL(kern, dim3(p.nblocks), dim3(p.threads), lds, stream, x, off, msk, gout,
-                           goff, gmask, p);
+                           goff, gmask, p, rec);
         return hipGetLastError();
     };
     if (p.cpp == 4 && p.RW == 35) return go(dcn_core_bwd_tile_kernel<E, NC, 4, 35>);
@@ -795,12 +898,12 @@ hipError_t launch_bwd_tile_nc(const CoreLaunch &a, const TileParams &p, float *g
 
 template <class E>
 hipError_t launch_bwd_tile_e(const CoreLaunch &a, const TileParams &p, float *goff, float *gmask,
-                             hipStream_t stream) {
+                             const CoreRecArgs *ra, bool *rec_done, hipStream_t stream) {
     if constexpr (E::id == DCN_BF16) {
-        return launch_bwd_tile_nc<E, 1>(a, p, goff, gmask, stream);
+        return launch_bwd_tile_nc<E, 1>(a, p, goff, gmask, ra, rec_done, stream);
     } else {
-        return p.NC == 2 ? launch_bwd_tile_nc<E, 2>(a, p, goff, gmask, stream)
-                         : launch_bwd_tile_nc<E, 1>(a, p, goff, gmask, stream);
+        return p.NC == 2 ? launch_bwd_tile_nc<E, 2>(a, p, goff, gmask, ra, rec_done, stream)
+                         : launch_bwd_tile_nc<E, 1>(a, p, goff, gmask, ra, rec_done, stream);
     }
 }
 
@@ -816,12 +919,13 @@ hipError_t launch_dcn_core_tile(const CoreLaunch &a, const TileParams &p, hipStr
 // grad_offset / grad_mask of the core backward on the tile plan p (S == 1, fp32 plain
 // offsets): a.out carries grad_out.
 hipError_t launch_dcn_core_bwd_tile(const CoreLaunch &a, const TileParams &p, float *goff, float *gmask,
-                                    hipStream_t stream) {
+                                    const CoreRecArgs *ra, bool *rec_done, hipStream_t stream) {
+    if (rec_done) *rec_done = false;
     if (p.S != 1 || a.kh != 3 || a.kw != 3) return hipErrorInvalidValue;
     switch (a.dtype) {
-        case DCN_F32: return launch_bwd_tile_e<EF32>(a, p, goff, gmask, stream);
-        case DCN_F16: return launch_bwd_tile_e<EF16>(a, p, goff, gmask, stream);
-        case DCN_BF16: return launch_bwd_tile_e<EBF16>(a, p, goff, gmask, stream);
+        case DCN_F32: return launch_bwd_tile_e<EF32>(a, p, goff, gmask, ra, rec_done, stream);
+        case DCN_F16: return launch_bwd_tile_e<EF16>(a, p, goff, gmask, ra, rec_done, stream);
+        case DCN_BF16: return launch_bwd_tile_e<EBF16>(a, p, goff, gmask, ra, rec_done, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -71,10 +71,21 @@ struct CoreTilePlan {
 };
 bool plan_core_tile(const CoreLaunch &a, CoreTilePlan &plan);
 hipError_t launch_dcn_core_tile(const CoreLaunch &a, const CoreTilePlan &plan, hipStream_t stream);
+// grad_x records of the core backward (see dcn_core_bwd.hip): the record array, the
+// bin starts from the scan, the fill cursors, and the bin grid (tiles per column/row).
+struct CoreRecArgs {
+    uint4 *rec;
+    const unsigned *starts;
+    unsigned *fill;
+    int TY, TX;
+};
 // grad_offset / grad_mask of the core backward on a forward tile plan with S == 1 and
-// plain fp32 offsets (a.out = grad_out); hipErrorInvalidValue for other plans.
+// plain fp32 offsets (a.out = grad_out); hipErrorInvalidValue for other plans. With
+// ra != NULL the kernel also files the grad_x records when its variant can (then
+// *rec_done = true; otherwise the caller files them).
 hipError_t launch_dcn_core_bwd_tile(const CoreLaunch &a, const CoreTilePlan &plan, float *goff,
-                                    float *gmask, hipStream_t stream);
+                                    float *gmask, const CoreRecArgs *ra, bool *rec_done,
+                                    hipStream_t stream);
 
 // Workspace plan of the DCNv2 path (all offsets 256-byte aligned).
 struct V2Plan {

@@ -251,6 +251,20 @@ def test_backward_unstaged_gather(gpu, monkeypatch, name):
     _say(name, check_all(r, o, c["dtype"], name))
 
 
+@pytest.mark.parametrize("name", ["f32_vec4_tails", "f16_vec8", "f32_far_offsets", "f32_softmax"])
+def test_backward_pair_pass_records(gpu, monkeypatch, name):
+    """grad_x records filed by the pair pass (DCN_CORE_BWD_TILE_NO_RECORDS=1) while the
+    tiled kernel computes grad_offset / grad_mask: the default files them in the tiled
+    kernel on these shapes."""
+    args, extra = {n: (a, e) for n, a, e in BWD_SWEEP}[name]
+    monkeypatch.setenv("DCN_CORE_BWD_TILE_NO_RECORDS", "1")
+    c = wl.core_case(seed=100 + len(name), **args)
+    go = wl.core_grad_out(c, seed=len(name))
+    r = run_bwd(c, go, **extra)
+    o = oracle_bwd(c, go, **extra)
+    _say(name, check_all(r, o, c["dtype"], name))
+
+
 def test_backward_empty_batch(gpu):
     x = torch.zeros((0, 4, 4, 8), device="cuda")
     off = torch.zeros((0, 4, 4, 2, 9, 2), device="cuda")
