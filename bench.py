@@ -224,7 +224,7 @@ def bench_v2(dsa, torch, timer, iters, warmup):
     return dict(workload=name, taps=P * 9, channel_taps=P * 9 * Cin, algo_bytes=nbytes,
                 flops=flops, wall_s=wall, kernel_s=kern, tflops=flops / kern / 1e12,
                 mfma_frac=flops / kern / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                note="three launches: layout prep, deform-im2col, MFMA GEMM")
+                note="two launches: layout prep, deform-im2col fused into the MFMA GEMM")
 
 
 def bench_v2_bwd(dsa, torch, timer, iters, warmup):
