@@ -13,9 +13,10 @@
 // from LDS, and only taps that leave the region (and still touch the image) read
 // global memory, in a deferred pass.
 //
-// One tile per block: the region is staged with direct global->LDS loads
-// (global_load_lds_dwordx4); two 8-wave blocks share a CU, so one block's staging
-// overlaps the other's compute.
+// One tile per block: the region is staged with direct-to-LDS loads (16 bytes per
+// lane, buffer- or global-address form); while they are in flight each lane turns its
+// pair's offsets into tap cells and weights. Two 8-wave blocks share a CU, so one
+// block's staging also overlaps the other's compute.
 // Per tile: DCNv3 softmax over K per pair (the S lanes of a pair split the
 // exponentials and exchange sum and values with wavefront shuffles); per tap the
 // fraction/corner split once per lane, 4*NC 16-byte LDS reads, fp32 FMAs with the
@@ -180,24 +181,68 @@ __device__ __forceinline__ void softmax_k(float (&m)[K], int s) {
     for (int k = 0; k < K; ++k) m[k] = __shfl(e[k / S], seg + k % S, 64) * inv;
 }
 
-// Taps of one active lane from the staged region `buf`, then the store. Taps whose
-// 2x2 corners are not all inside the region get weight 0 in the LDS pass; those that
-// still touch the image are redone from global memory in the deferred pass.
+// The taps of one lane in two steps. make_taps turns the pair's offsets and masks into
+// each tap's region cell and four weights; it needs no LDS, so it runs while the
+// region is still being copied in. taps_run then reads the corners from the staged
+// region `buf`, accumulates and stores. Taps whose 2x2 corners are not all inside the
+// region get weight 0 in the LDS pass; those that still touch the image (bits of
+// `far`) are redone from global memory in the deferred pass.
 // CPP_ and RW_ fix the chunks per region pixel and the region width at compile time
 // (0: taken from p): the four corners of a chunk are then one address plus constant
 // offsets that the LDS reads encode as immediates.
+struct TapW {
+    int cell;  // region chunk index of the (y0, x0) corner, chunk 0 (0 for weight-0 taps)
+    float w00, w01, w10, w11;
+};
+
+template <class E, int KH, int KW, int S, int NC, int CPP_ = 0, int RW_ = 0>
+__device__ __forceinline__ void make_taps(TapW (&tw)[KH * KW], unsigned &far, float (&d)[2 * KH * KW],
+                                          const float (&m)[KH * KW], const TileAt &a,
+                                          const LaneAt &l, const TileParams &p) {
+    constexpr int K = KH * KW;
+    scale_offsets<K>(d, p.offset_scale);
+    const int cpp = CPP_ ? CPP_ : p.cpp;
+    const int rw = RW_ ? RW_ : p.RW;
+    const int rowc = rw * cpp;
+    const int lby = l.ho * p.sh - p.ph - a.ry0, lbx = l.wo * p.sw - p.pw - a.rx0;
+    // grid base of the output pixel relative to the region origin; the image bounds
+    // test adds the origin back (y0 + 1 = ly + ry0 + 1)
+    const int ty = a.ry0 + 1, tx = a.rx0 + 1;
+    far = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int i = k / KW, j = k - (k / KW) * KW;
+        int ly, lx;
+        float fy, fx;
+        split_coord_fast(lby + i * p.dh, d[2 * k + 1], ly, fy);
+        split_coord_fast(lbx + j * p.dw, d[2 * k], lx, fx);
+        const bool inreg = (unsigned)ly <= (unsigned)(p.RH - 2) && (unsigned)lx <= (unsigned)(rw - 2);
+        const bool touch = (unsigned)(ly + ty) <= (unsigned)p.H && (unsigned)(lx + tx) <= (unsigned)p.W;
+        // some corner inside the image: y0 in [-1, H-1] and x0 in [-1, W-1]
+        far |= (!inreg && touch) ? (1u << k) : 0u;
+        const float mk = inreg ? m[k] : 0.0f;
+        const int cell = (int)__umul24((unsigned)ly, (unsigned)rowc) + lx * cpp;
+        TapW &t = tw[k];
+        t.cell = inreg ? cell : 0;
+        const float gy1 = fy * mk, gy0 = mk - gy1;
+        t.w01 = gy0 * fx;
+        t.w00 = gy0 - t.w01;
+        t.w11 = gy1 * fx;
+        t.w10 = gy1 - t.w11;
+    }
+}
+
 // coff: this pair's 2K offsets in memory (re-read for taps of the deferred pass).
 template <class E, class OM, int KH, int KW, int S, int NC, int CPP_ = 0, int RW_ = 0>
-__device__ __forceinline__ void taps_and_store(const uint4 *buf, const typename E::bits *x,
-                                               typename E::bits *out, float (&d)[2 * KH * KW],
-                                               const float (&m)[KH * KW], const TileAt &a,
-                                               const LaneAt &l, const TileParams &p,
-                                               const typename OM::bits *coff) {
+__device__ __forceinline__ void taps_run(const uint4 *buf, const typename E::bits *x,
+                                         typename E::bits *out, const TapW (&tw)[KH * KW], unsigned far,
+                                         const float (&m)[KH * KW], const TileAt &a,
+                                         const LaneAt &l, const TileParams &p,
+                                         const typename OM::bits *coff) {
     using Bt = typename E::bits;
     constexpr int V = 16 / (int)sizeof(Bt);
     constexpr int K = KH * KW;
     const int GC = p.G * p.C;
-    scale_offsets<K>(d, p.offset_scale);
     float acc[NC][V];
 #pragma unroll
     for (int u = 0; u < NC; ++u)
@@ -214,46 +259,13 @@ __device__ __forceinline__ void taps_and_store(const uint4 *buf, const typename 
     int slot[NC];
 #pragma unroll
     for (int uu = 0; uu < NC; ++uu) slot[uu] = lp * NC + (uu ^ flip);
-    // grid base of the output pixel relative to the region origin; the image bounds
-    // test adds the origin back (y0 + 1 = ly + ry0 + 1)
-    const int lby = l.ho * p.sh - p.ph - a.ry0, lbx = l.wo * p.sw - p.pw - a.rx0;
-    const int ty = a.ry0 + 1, tx = a.rx0 + 1;
-    unsigned far = 0;
-    // One tap's LDS address (its chunk-0 slot is added per unit) and four weights.
-    struct TapW {
-        const uint4 *c0;
-        float w00, w01, w10, w11;
-    };
-    auto tap = [&](int k) __attribute__((always_inline)) {
-        const int i = k / KW, j = k - (k / KW) * KW;
-        int ly, lx;
-        float fy, fx;
-        split_coord_fast(lby + i * p.dh, d[2 * k + 1], ly, fy);
-        split_coord_fast(lbx + j * p.dw, d[2 * k], lx, fx);
-        const bool inreg = (unsigned)ly <= (unsigned)(p.RH - 2) && (unsigned)lx <= (unsigned)(rw - 2);
-        // some corner inside the image: y0 in [-1, H-1] and x0 in [-1, W-1]
-        const bool touch = (unsigned)(ly + ty) <= (unsigned)p.H && (unsigned)(lx + tx) <= (unsigned)p.W;
-        far |= (!inreg && touch) ? (1u << k) : 0u;
-        const float mk = inreg ? m[k] : 0.0f;
-        const int cell = (int)__umul24((unsigned)ly, (unsigned)rowc) + lx * cpp;
-        TapW t;
-        t.c0 = buf + (inreg ? cell : 0);
-        const float gy1 = fy * mk, gy0 = mk - gy1;
-        t.w01 = gy0 * fx;
-        t.w00 = gy0 - t.w01;
-        t.w11 = gy1 * fx;
-        t.w10 = gy1 - t.w11;
-        return t;
-    };
     // Units (tap k, chunk uu) in order; unit n + 1's four corner reads are written
     // before unit n's multiply-adds.
     constexpr int NU = K * NC;
-    TapW tw[K];
     uint4 buf4[2][4];
     auto issue = [&](int n) __attribute__((always_inline)) {
         const int k = n / NC, uu = n % NC;
-        if (uu == 0) tw[k] = tap(k);
-        const uint4 *q = tw[k].c0 + slot[uu];
+        const uint4 *q = buf + tw[k].cell + slot[uu];
         buf4[n & 1][0] = q[0];
         buf4[n & 1][1] = q[cpp];
         buf4[n & 1][2] = q[rowc];
@@ -287,7 +299,7 @@ __device__ __forceinline__ void taps_and_store(const uint4 *buf, const typename 
             const int k = __builtin_ctz(far);
             far &= far - 1;
             // the tap's offsets again from memory (the pair's row, just read, is in
-            // cache): the loop above frees each tap's offset registers after use
+            // cache): no offset register stays live through the LDS pass
             float dx, dy;
             if constexpr (kOmPlain<OM>) {
                 const float2 dv = reinterpret_cast<const float2 *>(coff)[k];
@@ -358,9 +370,46 @@ __device__ __forceinline__ void stage_region(uint4 *lds, const typename E::bits 
     }
 }
 
+// stage_region for a region of RH x RW pixels and a block of NT threads known at
+// compile time: an unrolled sequence of copies per wave (the last one only where
+// chunks remain). The copies go through a buffer resource over the image: a chunk
+// outside the image gets an offset past the resource's end, which reads as zeros.
+// Unlike the global-address form, buffer-form copies let the compiler wait for the
+// pair's offset/mask loads (issued before) without waiting for the copies, so the
+// tap arithmetic runs while the region is in flight. The image must be < 2 GiB.
+template <class E, int RW, int CPP, int RH, int NT>
+__device__ __forceinline__ void stage_region_fixed(uint4 *lds, const typename E::bits *__restrict__ x,
+                                                   const TileAt &a, const TileParams &p) {
+    using Bt = typename E::bits;
+    constexpr int V = 16 / (int)sizeof(Bt);
+    constexpr int elt = (int)sizeof(Bt);
+    constexpr int total = RH * RW * CPP;
+    constexpr int NIT = (total + NT - 1) / NT;
+    const int tid = threadIdx.x;
+    const int GC = p.G * p.C;
+    const unsigned img_bytes = (unsigned)(p.H * p.W * GC * elt);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(x + (size_t)a.n * p.H * p.W * GC, img_bytes);
+    const int cb = ((a.g0 * p.C) + (tid & (CPP - 1)) * V) * elt;
+    const int w0 = __builtin_amdgcn_readfirstlane(tid & ~63);
+    const int lane = tid & 63;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int i0 = w0 + it * NT;
+        if (it < NIT - 1 || i0 < total) {
+            const int c = i0 + lane;
+            const int rr = c / CPP;
+            const int ry = rr / RW, rx = rr - ry * RW;
+            const int yy = a.ry0 + ry, xx = a.rx0 + rx;
+            const bool ok = c < total && (unsigned)yy < (unsigned)p.H && (unsigned)xx < (unsigned)p.W;
+            const int off = ok ? (int)__umul24(__umul24(yy, p.W) + xx, GC) * elt + cb : (int)img_bytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(lds + i0), 16, off, 0, 0, 0);
+        }
+    }
+}
+
 // ---------------------------------------------------------- one tile/block --
 
-template <class E, class OM, int KH, int KW, int S, int NC, int CPP_, int RW_>
+template <class E, class OM, int KH, int KW, int S, int NC, int CPP_, int RW_, int RH_>
 __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::bits *__restrict__ x,
                                                              const typename OM::bits *__restrict__ offset,
                                                              const typename OM::bits *__restrict__ mask,
@@ -375,14 +424,27 @@ __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::b
     float d[2 * K], m[K];
     load_dm<K, OM>(d, m, a, l, offset, mask, p);
 
-    stage_region<E>(lds, x, a, p);
-    __syncthreads();
+    if constexpr (RH_ != 0)
+        stage_region_fixed<E, RW_, CPP_, RH_, 512>(lds, x, a, p);
+    else
+        stage_region<E>(lds, x, a, p);
     if (p.softmax) softmax_k<K, S>(m, l.s);
+    TapW tw[K];
+    unsigned far;
+    make_taps<E, KH, KW, S, NC, CPP_, RW_>(tw, far, d, m, a, l, p);
+    // the empty asm statements take the tap values as operands, so they are computed
+    // here, before the barrier, instead of being sunk behind it into the active-lane
+    // branch
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        asm volatile("" ::"v"(tw[k].cell), "v"(tw[k].w00), "v"(tw[k].w01), "v"(tw[k].w10), "v"(tw[k].w11));
+    asm volatile("" ::"v"(far));
+    __syncthreads();
     if (!l.active) return;
     const size_t pixel = ((size_t)a.n * p.Ho + l.ho) * p.Wo + l.wo;
     const typename OM::bits *coff = kOmPlain<OM> ? offset + (pixel * p.G + l.g) * K * 2
                                                  : offset + pixel * p.off_pix + (size_t)l.g * p.off_grp;
-    taps_and_store<E, OM, KH, KW, S, NC, CPP_, RW_>(lds, x, out, d, m, a, l, p, coff);
+    taps_run<E, OM, KH, KW, S, NC, CPP_, RW_>(lds, x, out, tw, far, m, a, l, p, coff);
 }
 
 // ------------------------------------------------- backward: tap gradients --
@@ -752,10 +814,16 @@ hipError_t launch_tile(const CoreLaunch &a, const TileParams &p, hipStream_t str
         return hipGetLastError();
     };
     // 16x16-pixel tiles with halo 8 (region width 35) of 64-byte slices: the common
-    // plan, with its region geometry compiled in
-    if (p.cpp == 4 && p.RW == 35) return go(dcn_core_tile_kernel<E, OM, 3, 3, S, NC, 4, 35>);
-    if (p.cpp == 2 && p.RW == 35) return go(dcn_core_tile_kernel<E, OM, 3, 3, S, NC, 2, 35>);
-    return go(dcn_core_tile_kernel<E, OM, 3, 3, S, NC, 0, 0>);
+    // plan, with its region geometry compiled in; with region height 35, 512 threads
+    // and an image under 2 GiB, also the staging (RH_ = 35: buffer-form copies)
+    const bool fixed = p.RH == 35 && p.threads == 512 &&
+                       (size_t)p.H * p.W * p.G * p.C * sizeof(Bt) < (size_t(1) << 31);
+
+    if (p.cpp == 4 && p.RW == 35 && fixed) return go(dcn_core_tile_kernel<E, OM, 3, 3, S, NC, 4, 35, 35>);
+    if (p.cpp == 4 && p.RW == 35) return go(dcn_core_tile_kernel<E, OM, 3, 3, S, NC, 4, 35, 0>);
+    if (p.cpp == 2 && p.RW == 35 && fixed) return go(dcn_core_tile_kernel<E, OM, 3, 3, S, NC, 2, 35, 35>);
+    if (p.cpp == 2 && p.RW == 35) return go(dcn_core_tile_kernel<E, OM, 3, 3, S, NC, 2, 35, 0>);
+    return go(dcn_core_tile_kernel<E, OM, 3, 3, S, NC, 0, 0, 0>);
 }
 
 template <class E, int S, int NC>
