@@ -430,7 +430,9 @@ def deform_agg_backward(feat, spatial_shape, scale_start, loc, weights, grad_out
                         softmax=False, need=("feat", "loc", "weights"), workspace=None,
                         stream=None):
     """Gradients of deform_agg_forward w.r.t. feat, loc and weights (the names in
-    `need`). Returns (grad_feat, grad_loc, grad_weights), None where not asked."""
+    `need`). Returns (grad_feat, grad_loc, grad_weights), None where not asked.
+    workspace: a device buffer, None to allocate one, or False to pass none (allowed
+    when only the weights' gradient is asked)."""
     _check(feat, "feat")
     _check(loc, "loc", torch.float32)
     _check(weights, "weights", torch.float32)
@@ -454,6 +456,8 @@ def deform_agg_backward(feat, spatial_shape, scale_start, loc, weights, grad_out
                                               feat.dtype)
     if workspace is None and wsb:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=feat.device)
+    elif workspace is False:
+        workspace = None
     _call("deform_agg_backward", _ptr(feat), ss.ctypes.data, st.ctypes.data, _ptr(loc),
           _ptr(weights), _ptr(grad_out), _ptr(gf), _ptr(gl), _ptr(gw), _ptr(workspace),
           0 if workspace is None else workspace.numel() * workspace.element_size(),

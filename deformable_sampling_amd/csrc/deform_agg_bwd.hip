@@ -20,8 +20,18 @@
 // S*V >= Cg, S a power of two) walk the records: four V-wide corner loads and the
 // partial dots D_ab, summed over the slice into the sample's g_t, grad_u, grad_v in
 // LDS. The owner lane of each (point, camera) sums its scales and stores that
-// group's grad_loc partial; the lane that built a sample stores its g_t (and, with
-// softmax, rewrites it as wt (g_t - sum_j wj g_j) once the sum is known) and its
+// group's grad_loc partial. Where a group's channels are 2-16 vectors of 16 bytes
+// and a workspace is given, agg_bwd_pipe_kernel does this with the corner loads one
+// batch of records ahead (buffer loads, row_shr DPP sums), the unit's logits read
+// once into registers (softmax from them, no further passes), and g_t stored
+// contiguously per unit in the workspace with the unit's max, 1/sum and
+// sum_t wt g_t; a finishing pass then writes grad_weights (g_t, or
+// wt (g_t - sum_j wj g_j)) and the normalised weights along their [sample, G]
+// layout. (Written from the group-major units directly, those 4-byte stores leave
+// every line partly written by eight XCDs: 33 us of the main kernel's 189 us, and
+// the two extra passes over the logits 55 us.) Otherwise agg_bwd_kernel takes the
+// records one batch at a time, and the lane that built a sample stores its g_t (and,
+// with softmax, rewrites it as wt (g_t - sum_j wj g_j) once the sum is known) and its
 // normalised weight wt. A second kernel adds the G partials of grad_loc in group
 // order.
 //
@@ -49,6 +59,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxRounds = 8;  // channel rounds of 64 lanes: Cg <= 512
+constexpr int kRegRounds = 8;  // sample rounds a lane of the pipelined kernel keeps: T <= 8 * 64
 
 struct AggBwdParams {
     int B, P_total, A, pts, cams, scales, G, Cg, softmax;
@@ -285,6 +296,261 @@ __global__ __launch_bounds__(kThreads) void agg_bwd_kernel(
                 float *q = gw + ((size_t)ba * T + t_nat) * p.G + g;
                 *q = wt * (*q - tot);
             }
+        }
+    }
+}
+
+// The main kernel for the bucketed path when a group's channels are S 16-byte vectors
+// (S a power of two, S <= 16): the same records and results, with the corner loads
+// of each batch of Z = 64/S records issued through a buffer resource one batch ahead
+// of the dot products, and the S-lane sums over compile-time widths. Record offsets
+// are element offsets inside the batch's features, which must be under 2 GiB.
+// Sum over each aligned S-lane slice (S <= 16, a power of two), complete in the
+// slice's last lane: row_shr DPP steps, so no LDS permutes and no waits.
+template <int N>
+__device__ __forceinline__ float row_shr(float v) {  // lane i gets lane i - N of its row, or 0
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + N, 0xf, 0xf, true));
+}
+template <int S>
+__device__ __forceinline__ float slice_sum_to_last(float v) {
+    static_assert(S >= 1 && S <= 16 && (S & (S - 1)) == 0, "slice of 1-16 lanes");
+    if constexpr (S > 1) v += row_shr<1>(v);
+    if constexpr (S > 2) v += row_shr<2>(v);
+    if constexpr (S > 4) v += row_shr<4>(v);
+    if constexpr (S > 8) v += row_shr<8>(v);
+    return v;
+}
+
+template <class E, int S, int NV>
+__global__ __launch_bounds__(kThreads) void agg_bwd_pipe_kernel(
+    const typename E::bits *__restrict__ feat, const float *__restrict__ loc,
+    const float *__restrict__ weights, const typename E::bits *__restrict__ gout,
+    float *__restrict__ gloc_part, float *__restrict__ gts, float *__restrict__ us,
+    const AggBwdParams p) {
+    using Bt = typename E::bits;
+    constexpr int elt = (int)sizeof(Bt);
+    constexpr int V = 16 / elt;
+    constexpr int Z = 64 / S;
+    __shared__ int s_h[kAggMaxMaps], s_w[kAggMaxMaps], s_start[kAggMaxMaps];
+    __shared__ AggRec s_rec[kWaves][64];
+    __shared__ float s_res[kWaves][64][3];
+
+    const int nmaps = p.cams * p.scales;
+    for (int i = threadIdx.x; i < nmaps; i += kThreads) {
+        s_h[i] = p.maps.H[i];
+        s_w[i] = p.maps.W[i];
+        s_start[i] = p.maps.start[i];
+    }
+    __syncthreads();
+
+    const int blk = xcd_remap((int)blockIdx.x, p.nblocks);
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int unit = blk * kWaves + wv;
+    if (unit >= p.nunits) return;  // whole wavefronts leave together; no barrier follows
+    const int lane = threadIdx.x & 63;
+    const int z = lane / S, s = lane - z * S;
+    const int g = unit / p.BA, ba = unit - g * p.BA;  // group-major
+    const int b = ba / p.A;
+    const int T = p.pts * p.cams * p.scales;
+    const int NPC = p.pts * p.cams;
+    const int GC = p.G * p.Cg;
+    const float *wrow = weights + (size_t)ba * T * p.G + g;
+    const float *lrow = loc + (size_t)ba * NPC * 2;
+    const Bt *fb = feat + (size_t)b * p.P_total * GC;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(fb, (unsigned)((size_t)p.P_total * GC * elt));
+    const int lane_off = (g * p.Cg + s * NV * V) * elt;  // this lane's channels, bytes
+    AggRec *rec = s_rec[wv];
+    float(*res)[3] = s_res[wv];
+
+    // the lane's logits, round k in lgr[k] (sample k * per_round + lane), read once
+    const int per_round = p.npc * p.scales;
+    const int lpc = lane / p.scales, lsc = lane - lpc * p.scales;
+    float lgr[kRegRounds];
+#pragma unroll
+    for (int k = 0; k < kRegRounds; ++k) {
+        const int pc = k * p.npc + lpc;
+        lgr[k] = (lane < per_round && pc < NPC) ? wrow[(size_t)(pc * p.scales + lsc) * p.G] : -INFINITY;
+    }
+    float mx = 0.0f, inv = 1.0f;
+    if (p.softmax) {
+        float m = lgr[0];
+#pragma unroll
+        for (int k = 1; k < kRegRounds; ++k) m = fmaxf(m, lgr[k]);
+        mx = wmax(m);
+        float e = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kRegRounds; ++k) e += expf(lgr[k] - mx);
+        inv = 1.0f / wsum(e);
+    }
+    float gc[NV][V];  // this lane's channels s*NV*V .. (s+1)*NV*V - 1 of G
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const uint4 graw =
+            *reinterpret_cast<const uint4 *>(gout + (size_t)ba * GC + g * p.Cg + (s * NV + v) * V);
+        unpack<E, V>(graw, gc[v]);
+    }
+
+    // this lane's location for the round at pc0 (read one round ahead)
+    auto fetch = [&](int pc0, float2 &uv) __attribute__((always_inline)) {
+        const int pc = pc0 + lpc;
+        if (lane < per_round && pc < NPC) uv = *reinterpret_cast<const float2 *>(lrow + 2 * pc);
+    };
+    float2 uv_next = make_float2(0.0f, 0.0f);
+    fetch(0, uv_next);
+    float dot = 0.0f;
+    for (int pc0 = 0; pc0 < NPC; pc0 += p.npc) {
+        const int pc = pc0 + lpc;
+        const bool own = lane < per_round && pc < NPC;
+        const float lg = lgr[0];
+#pragma unroll
+        for (int k = 0; k + 1 < kRegRounds; ++k) lgr[k] = lgr[k + 1];
+        const float2 uv = uv_next;
+        fetch(pc0 + p.npc, uv_next);
+        int t_nat = 0;
+        float wt = 0.0f;
+        if (own) {
+            const int cam = pc % p.cams;
+            const int cs = cam * p.scales + lsc;
+            t_nat = pc * p.scales + lsc;
+            wt = p.softmax ? expf(lg - mx) * inv : lg;
+            const int Hs = s_h[cs], Ws = s_w[cs];
+            const float xf = __fsub_rn(mul_rn(uv.x, (float)Ws), 0.5f);
+            const float yf = __fsub_rn(mul_rn(uv.y, (float)Hs), 0.5f);
+            int x0, y0;
+            AggRec r;
+            split_fu(yf, y0, r.fy, r.uy);
+            split_fu(xf, x0, r.fx, r.ux);
+            const bool vy0 = (unsigned)y0 < (unsigned)Hs, vy1 = (unsigned)(y0 + 1) < (unsigned)Hs;
+            const bool vx0 = (unsigned)x0 < (unsigned)Ws, vx1 = (unsigned)(x0 + 1) < (unsigned)Ws;
+            const int yc0 = min(max(y0, 0), Hs - 1), yc1 = min(max(y0 + 1, 0), Hs - 1);
+            const int xc0 = min(max(x0, 0), Ws - 1), xc1 = min(max(x0 + 1, 0), Ws - 1);
+            const int base = s_start[cs];
+            r.o00 = (base + yc0 * Ws + xc0) * GC * elt;  // bytes
+            r.o01 = (base + yc0 * Ws + xc1) * GC * elt;
+            r.o10 = (base + yc1 * Ws + xc0) * GC * elt;
+            r.o11 = (base + yc1 * Ws + xc1) * GC * elt;
+            r.valid = (vy0 && vx0 ? 1 : 0) | (vy0 && vx1 ? 2 : 0) | (vy1 && vx0 ? 4 : 0) |
+                      (vy1 && vx1 ? 8 : 0);
+            r.wt = wt;
+            r.Ws = (float)Ws;
+            r.Hs = (float)Hs;
+            rec[lane] = r;
+        }
+        const int nrec = min(per_round, (NPC - pc0) * p.scales);
+        const int iters = (nrec + Z - 1) / Z;
+        uint4 cb[2][4][NV];
+        // batch it: slice z takes record it*Z + z (record 0 again past the end, unused)
+        auto issue = [&](int it, int slot) __attribute__((always_inline)) {
+            const int j = it * Z + z;
+            const int4 o = *reinterpret_cast<const int4 *>(&rec[j < nrec ? j : 0].o00);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                cb[slot][0][v] = buffer_load<uint4>(rsrc, o.x + lane_off + 16 * v);
+                cb[slot][1][v] = buffer_load<uint4>(rsrc, o.y + lane_off + 16 * v);
+                cb[slot][2][v] = buffer_load<uint4>(rsrc, o.z + lane_off + 16 * v);
+                cb[slot][3][v] = buffer_load<uint4>(rsrc, o.w + lane_off + 16 * v);
+            }
+        };
+        auto compute = [&](int it, int slot) __attribute__((always_inline)) {
+            const int j = it * Z + z;
+            float D00 = 0.0f, D01 = 0.0f, D10 = 0.0f, D11 = 0.0f;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                float va[V], vb[V], vc[V], ve[V];
+                unpack<E, V>(cb[slot][0][v], va);
+                unpack<E, V>(cb[slot][1][v], vb);
+                unpack<E, V>(cb[slot][2][v], vc);
+                unpack<E, V>(cb[slot][3][v], ve);
+#pragma unroll
+                for (int u = 0; u < V; ++u) {
+                    D00 = fmaf(gc[v][u], va[u], D00);
+                    D01 = fmaf(gc[v][u], vb[u], D01);
+                    D10 = fmaf(gc[v][u], vc[u], D10);
+                    D11 = fmaf(gc[v][u], ve[u], D11);
+                }
+            }
+            D00 = slice_sum_to_last<S>(D00);
+            D01 = slice_sum_to_last<S>(D01);
+            D10 = slice_sum_to_last<S>(D10);
+            D11 = slice_sum_to_last<S>(D11);
+            if (j < nrec && s == S - 1) {
+                const AggRec r = rec[j];
+                const float d00 = (r.valid & 1) ? D00 : 0.0f, d01 = (r.valid & 2) ? D01 : 0.0f;
+                const float d10 = (r.valid & 4) ? D10 : 0.0f, d11 = (r.valid & 8) ? D11 : 0.0f;
+                res[j][0] = r.uy * (r.ux * d00 + r.fx * d01) + r.fy * (r.ux * d10 + r.fx * d11);
+                res[j][1] = r.wt * r.Ws * (r.uy * (d01 - d00) + r.fy * (d11 - d10));
+                res[j][2] = r.wt * r.Hs * (r.ux * (d10 - d00) + r.fx * (d11 - d01));
+            }
+        };
+        // issues are unconditional (past the end they reread record 0): a skipped
+        // issue would make the compiler's wait for the current batch also cover the
+        // next one
+        issue(0, 0);
+        for (int it = 0; it < iters; it += 2) {
+            issue(it + 1, 1);
+            compute(it, 0);
+            issue(it + 2, 0);
+            if (it + 1 < iters) compute(it + 1, 1);
+        }
+        if (own) {
+            const float gt = res[lane][0];
+            dot = fmaf(wt, gt, dot);
+            if (p.want_w) gts[(size_t)unit * T + t_nat] = gt;  // contiguous per unit
+        }
+        if (p.want_loc && lane < p.npc && pc0 + lane < NPC) {
+            float su = 0.0f, sv = 0.0f;
+            for (int k = 0; k < p.scales; ++k) {
+                su += res[lane * p.scales + k][1];
+                sv += res[lane * p.scales + k][2];
+            }
+            float *dst = gloc_part + (((size_t)g * p.BA + ba) * NPC + pc0 + lane) * 2;
+            dst[0] = su;
+            dst[1] = sv;
+        }
+    }
+    // normalisation and sum_t wt g_t of the unit, for the finishing pass
+    const float tot = p.softmax ? wsum(dot) : 0.0f;
+    if (lane == 0) {
+        us[unit] = mx;
+        us[p.nunits + unit] = inv;
+        us[2 * p.nunits + unit] = tot;
+    }
+}
+
+// Finishing pass of the pipelined main kernel, one thread per element of the
+// [B*A*T, G] weight layout: wt = exp(l - max) / sum (the main kernel's arithmetic, from
+// its per-unit max and 1/sum) or the weight itself; grad_weights = g_t, or
+// wt (g_t - sum_j wj g_j) with the softmax; wn = wt for the feature gather. Reads and
+// writes run along the layout, so no partial lines are left to other XCDs.
+__global__ __launch_bounds__(256) void agg_bwd_finish_kernel(const float *__restrict__ weights,
+                                                             const float *__restrict__ gts,
+                                                             const float *__restrict__ us,
+                                                             float *__restrict__ gw, float *__restrict__ wn,
+                                                             long long n, int T, int G, int BA, int softmax) {
+    const long long nunits = (long long)G * BA;
+    const bool narrow = n < (1LL << 31);  // 32-bit index arithmetic
+    for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long long)gridDim.x * 256) {
+        long long smp, ba;
+        int g, t;
+        if (narrow) {
+            const unsigned s32 = (unsigned)e / (unsigned)G, b32 = s32 / (unsigned)T;
+            smp = s32;
+            ba = b32;
+            g = (int)((unsigned)e - s32 * (unsigned)G);
+            t = (int)(s32 - b32 * (unsigned)T);
+        } else {
+            smp = e / G;
+            ba = smp / T;
+            g = (int)(e - smp * G);
+            t = (int)(smp - ba * T);
+        }
+        const long long u = (long long)g * BA + ba;
+        const float w = weights[e];
+        const float wt = softmax ? expf(w - us[u]) * us[nunits + u] : w;
+        if (wn) wn[e] = wt;
+        if (gw) {
+            const float gt = gts[u * T + t];
+            gw[e] = softmax ? wt * (gt - us[2 * nunits + u]) : gt;
         }
     }
 }
@@ -599,6 +865,13 @@ __global__ __launch_bounds__(256) void agg_round_kernel(const float *__restrict_
         dst[i] = from_f32(E{}, src[i]);
 }
 
+// DCN_AGG_BWD_NOPIPE=1 keeps the general main kernel on the bucketed path (tests
+// compare both)
+bool agg_bwd_no_pipe() {
+    const char *e = getenv("DCN_AGG_BWD_NOPIPE");
+    return e && e[0] == '1';
+}
+
 int grid_for(long long n) {
     const long long b = (n + 255) / 256;
     return (int)(b < 1 ? 1 : (b > 16384 ? 16384 : b));
@@ -667,7 +940,32 @@ hipError_t launch_e(const AggBwdLaunch &a, const AggBwdPlan &pl, hipStream_t str
         const B *ft = static_cast<const B *>(a.feat);
         const B *go = static_cast<const B *>(a.grad_out);
         const dim3 grid(p.nblocks), block(kThreads);
-        switch (V) {
+        // 16-byte channel vectors, a power-of-two count per group: pipelined kernel
+        // with S lanes of NV vectors per record
+        constexpr int V16 = 16 / elt;
+        const int nv16 = a.Cg % V16 == 0 ? a.Cg / V16 : 0;
+        const int rounds = (a.pts * a.cams + p.npc - 1) / p.npc;
+        const bool pipe = !gacc && a.workspace && !agg_bwd_no_pipe() && rounds <= kRegRounds &&
+                          nv16 >= 2 && nv16 <= 16 &&
+                          (nv16 & (nv16 - 1)) == 0 && (uintptr_t)a.feat % 16 == 0 &&
+                          (uintptr_t)a.grad_out % 16 == 0 &&
+                          (long long)a.P_total * a.G * a.Cg * elt < (1LL << 31);
+        float *gts = pipe ? reinterpret_cast<float *>(ws + pl.off_gt) : nullptr;
+        float *us = pipe ? reinterpret_cast<float *>(ws + pl.off_us) : nullptr;
+        if (pipe) {
+            switch (nv16) {  // S = nv16 lanes of one vector
+                case 2: hipLaunchKernelGGL((agg_bwd_pipe_kernel<E, 2, 1>), grid, block, 0, stream, ft, a.loc, a.weights, go, part, gts, us, p); break;
+                case 4: hipLaunchKernelGGL((agg_bwd_pipe_kernel<E, 4, 1>), grid, block, 0, stream, ft, a.loc, a.weights, go, part, gts, us, p); break;
+                case 8: hipLaunchKernelGGL((agg_bwd_pipe_kernel<E, 8, 1>), grid, block, 0, stream, ft, a.loc, a.weights, go, part, gts, us, p); break;
+                default: hipLaunchKernelGGL((agg_bwd_pipe_kernel<E, 16, 1>), grid, block, 0, stream, ft, a.loc, a.weights, go, part, gts, us, p); break;
+            }
+            if (a.grad_weights || wn) {
+                const long long n = nsamp * a.G;
+                hipLaunchKernelGGL(agg_bwd_finish_kernel, dim3(grid_for(n)), dim3(256), 0, stream, a.weights,
+                                   gts, us, a.grad_weights, wn, n, a.pts * a.cams * a.scales, a.G, p.BA,
+                                   p.softmax);
+            }
+        } else switch (V) {
             case 4: hipLaunchKernelGGL((agg_bwd_kernel<E, 4>), grid, block, 0, stream, ft, a.loc, a.weights, go, gacc, part, a.grad_weights, wn, p); break;
             case 2: hipLaunchKernelGGL((agg_bwd_kernel<E, 2>), grid, block, 0, stream, ft, a.loc, a.weights, go, gacc, part, a.grad_weights, wn, p); break;
             default: hipLaunchKernelGGL((agg_bwd_kernel<E, 1>), grid, block, 0, stream, ft, a.loc, a.weights, go, gacc, part, a.grad_weights, wn, p); break;
@@ -724,6 +1022,10 @@ void plan_agg_bwd(int B, int P_total, int A, int pts, int cams, int scales, int 
     size_t off = 0;
     pl.off_loc = off;
     off = align256(off + (size_t)G * B * A * pts * cams * 2 * sizeof(float));
+    pl.off_gt = off;  // g_t per sample, unit-major (pipelined kernel)
+    off = align256(off + (size_t)B * A * T * G * sizeof(float));
+    pl.off_us = off;  // max, 1/sum and sum_t wt g_t per unit
+    off = align256(off + (size_t)3 * G * B * A * sizeof(float));
     if (pl.binned) {
         pl.off_wn = off;
         off = align256(off + (size_t)B * A * T * G * sizeof(float));

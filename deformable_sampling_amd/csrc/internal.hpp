@@ -183,7 +183,7 @@ struct AggBwdLaunch {
 struct AggBwdPlan {
     bool binned;
     long long D, nent;
-    size_t off_loc, off_acc, off_wn, off_cnt, off_starts, off_bsum, off_ent, total;
+    size_t off_loc, off_acc, off_wn, off_cnt, off_starts, off_bsum, off_ent, off_gt, off_us, total;
 };
 void plan_agg_bwd(int B, int P_total, int A, int pts, int cams, int scales, int G, int Cg,
                   dcn_dtype dtype, bool force_atomic, AggBwdPlan &plan);

@@ -287,9 +287,11 @@ const char *dcn_status_string(dcn_status s);
 
 /*
  * Workspace bytes deform_agg_backward needs (0 if the sizes are invalid), each region
- * 256-byte aligned: per-group partial sums of grad_loc (G*B*A*pts*cams*2 floats); then
- * the feature-gradient buckets: the normalised weights (B*A*T*G floats, T =
- * pts*cams*scales), per-feature-row counts and fill cursors (2*B*P_total uint32), their
+ * 256-byte aligned: per-group partial sums of grad_loc (G*B*A*pts*cams*2 floats); the
+ * per-sample sums g_t of grad_weights (B*A*T*G floats, T = pts*cams*scales) and three
+ * floats per (anchor, group) (3*G*B*A: softmax maximum, 1/sum, sum of wt g_t); then
+ * the feature-gradient buckets: the normalised weights (B*A*T*G floats), per-feature-row
+ * counts and fill cursors (2*B*P_total uint32), their
  * starts (B*P_total uint32), the scan's block sums (one uint32 per 4096 rows) and one
  * 8-byte entry per sample corner (B*A*T*4). Where
  * the entries would reach 2^31 (or with DCN_AGG_BWD_ATOMIC=1 in the environment) the
@@ -324,7 +326,8 @@ size_t deform_agg_backward_workspace_bytes(int B, int P_total, int A, int pts, i
  * error), then rounded once to dtype; grad_loc and grad_weights are deterministic.
  * workspace: deform_agg_backward_workspace_bytes bytes, 256-byte aligned, needed
  * when grad_loc != NULL or grad_feat != NULL (with the atomic fallback: grad_feat
- * in fp16/bf16), else may be NULL;
+ * in fp16/bf16), else may be NULL (grad_weights alone then takes a slower kernel,
+ * whose results may differ in the last bits from a call with a workspace);
  * contents on entry are ignored. Limits as the forward, and Cg <= 512. With A == 0
  * and grad_feat != NULL the call writes zeros to grad_feat (the one exception to
  * "zero-sized work launches nothing").

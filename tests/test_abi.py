@@ -228,6 +228,8 @@ def test_agg_backward_workspace_and_validation(lib):
     n = lib.deform_agg_backward_workspace_bytes(1, 89760, 900, 13, 6, 4, 8, 32, 0)
     T = 13 * 6 * 4
     assert n == (a256(8 * 900 * 13 * 6 * 2 * 4)      # grad_loc partials per group
+                 + a256(900 * T * 8 * 4)             # per-sample g_t
+                 + a256(3 * 8 * 900 * 4)             # per-(anchor, group) max, 1/sum, sum wt g_t
                  + a256(900 * T * 8 * 4)             # normalised weights
                  + a256(89760 * 2 * 4) + a256(89760 * 4)  # bucket counts + cursors, starts
                  + a256((89760 + 4095) // 4096 * 4)  # scan block sums
@@ -331,6 +333,9 @@ def test_v2_backward_validation(lib):
 def test_agg_backward_workspace_atomic_fallback(lib, monkeypatch):
     monkeypatch.setenv("DCN_AGG_BWD_ATOMIC", "1")
     n = lib.deform_agg_backward_workspace_bytes(1, 89760, 900, 13, 6, 4, 8, 32, 0)
-    assert n == (8 * 900 * 13 * 6 * 2 * 4 + 255) // 256 * 256      # fp32: loc partials only
+    a256 = lambda v: (v + 255) // 256 * 256
+    T = 13 * 6 * 4
+    assert n == (a256(8 * 900 * 13 * 6 * 2 * 4)                     # fp32: loc partials,
+                 + a256(900 * T * 8 * 4) + a256(3 * 8 * 900 * 4))    # g_t and unit sums only
     n16 = lib.deform_agg_backward_workspace_bytes(1, 89760, 900, 13, 6, 4, 8, 32, 1)
     assert n16 == n + 89760 * 256 * 4                                # + fp32 feature accumulator

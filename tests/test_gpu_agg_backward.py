@@ -25,10 +25,11 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def run(c, go, softmax=None, need=("feat", "loc", "weights")):
+def run(c, go, softmax=None, need=("feat", "loc", "weights"), workspace=None):
     sm = c["softmax"] if softmax is None else softmax
     r = dsa.deform_agg_backward(dev(c["feat"]), c["spatial_shape"], c["scale_start"],
-                                dev(c["loc"]), dev(c["weights"]), dev(go), softmax=sm, need=need)
+                                dev(c["loc"]), dev(c["weights"]), dev(go), softmax=sm, need=need,
+                                workspace=workspace)
     torch.cuda.synchronize()
     return r
 
@@ -119,6 +120,44 @@ def test_agg_backward_subsets_and_determinism(gpu):
     assert torch.equal(only_w[2], full[2]) and torch.equal(only_l[1], full[1])
     o = ref(c, go)
     check_grad(host(only_f[0]), o["grad_feat"], o["grad_feat_abs"], "f32", "grad_feat alone")
+
+
+GENERAL = [
+    ("f32_cg32_softmax", dict(B=1, shapes=TWO_CAM, A=16, pts=3, G=4, Cg=32)),
+    ("f16_cg32", dict(B=1, shapes=TWO_CAM, A=12, pts=3, G=4, Cg=32, dtype="f16")),
+    ("bf16_cg16", dict(B=1, shapes=TWO_CAM, A=12, pts=3, G=4, Cg=16, dtype="bf16")),
+    ("f32_three_scales_63_records", dict(B=1, shapes=[[(9, 13), (5, 7), (3, 4)]] * 3, A=8, pts=7,
+                                         G=2, Cg=16)),
+]
+
+
+@pytest.mark.parametrize("name,args", GENERAL, ids=[s[0] for s in GENERAL])
+def test_agg_backward_general_main_kernel(gpu, monkeypatch, name, args):
+    """The general main kernel on the bucketed path (channel vectors of 4 elements, no
+    load pipelining), which 16-byte-vector groups otherwise leave to the pipelined
+    kernel; selected through DCN_AGG_BWD_NOPIPE=1."""
+    monkeypatch.setenv("DCN_AGG_BWD_NOPIPE", "1")
+    c = wl.agg_case(seed=900 + len(name), **args)
+    go = wl.agg_grad_out(c, seed=len(name))
+    _say("agg backward general main kernel", name)
+    r = run(c, go)
+    o = ref(c, go)
+    _say(name, check_all(r, o, c["dtype"], name))
+
+
+@pytest.mark.parametrize("softmax", [True, False])
+def test_agg_backward_weights_without_workspace(gpu, softmax):
+    """grad_weights alone with no workspace (the general kernel) against the oracle and
+    against the same call with a workspace (the pipelined kernel and finishing pass)."""
+    c = wl.agg_case(B=1, shapes=TWO_CAM, A=20, pts=3, G=4, Cg=32, seed=43)
+    go = wl.agg_grad_out(c, seed=43)
+    _say("agg backward weights without workspace, softmax", softmax)
+    bare = run(c, go, softmax=softmax, need=("weights",), workspace=False)
+    full = run(c, go, softmax=softmax, need=("weights",))
+    o = ref(c, go, softmax=softmax)
+    for r, what in ((bare, "no workspace"), (full, "workspace")):
+        assert r[0] is None and r[1] is None
+        check_grad(host(r[2]), o["grad_weights"], o["grad_weights_abs"], "f32", what)
 
 
 FALLBACK = [
