@@ -208,22 +208,44 @@ __global__ __launch_bounds__(kThreads) void bwd_count_kernel(const float *__rest
         if (s_win[i]) atomicAdd(&counts[win_bin(i, n, g, win, p)], s_win[i]);
 }
 
-// 2. Exclusive prefix sum of nb counts (one block of 1024 threads, 4096 counts
-// per step, coalesced); starts[nb] = total.
+// 2. Exclusive prefix sum of nb counts, one block of 1024 threads; starts[nb] =
+// total. Chunks of 16384 counts: every 16-byte load of a chunk is issued at once
+// into LDS (one memory latency per chunk, where 4096-count steps of dependent loads
+// had cost one each), each thread scans its 16 consecutive counts, and the starts
+// leave from LDS in 16-byte stores. One 16-byte pad after every four chunk entries
+// keeps a thread's run of four entries off its neighbours' LDS banks. counts and
+// starts are 16-byte aligned.
+constexpr int kScanChunk = 16384;
+constexpr int kScanPer = kScanChunk / 1024;  // counts per thread
 __global__ __launch_bounds__(1024) void bwd_scan_kernel(const unsigned *__restrict__ counts,
                                                         unsigned *__restrict__ starts, int nb) {
+    __shared__ uint4 s_c[kScanChunk / 4 + kScanChunk / 16];
+    auto at = [](int q) { return q + (q >> 2); };  // padded index of entry q
     __shared__ unsigned s_wave[16];
-    __shared__ unsigned s_carry;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    if (t == 0) s_carry = 0;
-    __syncthreads();
-    for (int c0 = 0; c0 < nb; c0 += 4096) {
-        unsigned v[4], sum = 0;
+    unsigned carry = 0;
+    for (int c0 = 0; c0 < nb; c0 += kScanChunk) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = c0 + t * 4 + i;
-            v[i] = idx < nb ? counts[idx] : 0u;
-            sum += v[i];
+        for (int j = 0; j < kScanPer / 4; ++j) {
+            const int q = t + 1024 * j, e = c0 + 4 * q;
+            uint4 v;
+            if (e + 3 < nb) {
+                v = *reinterpret_cast<const uint4 *>(counts + e);
+            } else {
+                v.x = e < nb ? counts[e] : 0u;
+                v.y = e + 1 < nb ? counts[e + 1] : 0u;
+                v.z = e + 2 < nb ? counts[e + 2] : 0u;
+                v.w = 0u;
+            }
+            s_c[at(q)] = v;
+        }
+        __syncthreads();
+        uint4 a[kScanPer / 4];
+        unsigned sum = 0;
+#pragma unroll
+        for (int k = 0; k < kScanPer / 4; ++k) {
+            a[k] = s_c[at(kScanPer / 4 * t + k)];
+            sum += a[k].x + a[k].y + a[k].z + a[k].w;
         }
         unsigned incl = sum;
         for (int o = 1; o < 64; o <<= 1) {
@@ -232,20 +254,36 @@ __global__ __launch_bounds__(1024) void bwd_scan_kernel(const unsigned *__restri
         }
         if (lane == 63) s_wave[wave] = incl;
         __syncthreads();
-        unsigned before = s_carry;
-        for (int w = 0; w < wave; ++w) before += s_wave[w];
-        unsigned run = before + incl - sum;
+        unsigned run = carry + incl - sum;
+        for (int w = 0; w < wave; ++w) run += s_wave[w];
+        unsigned total = carry;
+        for (int w = 0; w < 16; ++w) total += s_wave[w];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = c0 + t * 4 + i;
-            if (idx < nb) starts[idx] = run;
-            run += v[i];
+        for (int k = 0; k < kScanPer / 4; ++k) {
+            uint4 o;
+            o.x = run; run += a[k].x;
+            o.y = run; run += a[k].y;
+            o.z = run; run += a[k].z;
+            o.w = run; run += a[k].w;
+            s_c[at(kScanPer / 4 * t + k)] = o;
         }
         __syncthreads();
-        if (t == 1023) s_carry = run;
-        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kScanPer / 4; ++j) {
+            const int q = t + 1024 * j, e = c0 + 4 * q;
+            const uint4 o = s_c[at(q)];
+            if (e + 3 < nb) {
+                *reinterpret_cast<uint4 *>(starts + e) = o;
+            } else {
+                if (e < nb) starts[e] = o.x;
+                if (e + 1 < nb) starts[e + 1] = o.y;
+                if (e + 2 < nb) starts[e + 2] = o.z;
+            }
+        }
+        carry = total;
+        __syncthreads();  // s_c and s_wave are rewritten by the next chunk
     }
-    if (t == 0) starts[nb] = s_carry;
+    if (t == 0) starts[nb] = carry;
 }
 
 // 3. The pair pass: corner dots -> grad_offset, grad_mask; grad_x either as sample
