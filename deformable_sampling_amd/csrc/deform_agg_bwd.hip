@@ -603,14 +603,20 @@ __device__ __forceinline__ void bucket_corners(const float *__restrict__ loc, co
 
 // Insert one occurrence of key: returns its slot; *rank = occurrences before it in
 // this block.
-__device__ __forceinline__ int hash_add(unsigned *keys, unsigned *cnts, unsigned key, unsigned &rank) {
+// Insert (or find) key; the thread that inserts a key appends its slot to `used`.
+__device__ __forceinline__ int hash_add(unsigned *keys, unsigned *cnts, unsigned *used,
+                                       unsigned *nused, unsigned key, unsigned &rank) {
     int h = (int)((key * 2654435761u) >> 21);  // 11 bits
     for (;;) {
         const unsigned k = keys[h];
         if (k == key) break;
         if (k == kNoKey) {
             const unsigned prev = atomicCAS(&keys[h], kNoKey, key);
-            if (prev == kNoKey || prev == key) break;
+            if (prev == kNoKey) {
+                used[atomicAdd(nused, 1u)] = (unsigned)h;
+                break;
+            }
+            if (prev == key) break;
         }
         h = (h + 1) & (kHashSlots - 1);
     }
@@ -628,6 +634,7 @@ __global__ __launch_bounds__(256) void agg_bucket_kernel(const float *__restrict
                                                          uint2 *__restrict__ entries, AggBwdParams p) {
     __shared__ int s_h[kAggMaxMaps], s_w[kAggMaxMaps], s_start[kAggMaxMaps];
     __shared__ unsigned s_key[kHashSlots], s_cnt[kHashSlots], s_base[kHashSlots];
+    __shared__ unsigned s_used[4 * 256], s_nused;  // slots in use (<= 4 corners x 256 samples)
     const int nmaps = p.cams * p.scales;
     for (int i = threadIdx.x; i < nmaps; i += 256) {
         s_h[i] = p.maps.H[i];
@@ -638,6 +645,7 @@ __global__ __launch_bounds__(256) void agg_bucket_kernel(const float *__restrict
         s_key[i] = kNoKey;
         s_cnt[i] = 0;
     }
+    if (threadIdx.x == 0) s_nused = 0;
     __syncthreads();
     const int T = p.pts * p.cams * p.scales;
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -652,16 +660,30 @@ __global__ __launch_bounds__(256) void agg_bucket_kernel(const float *__restrict
         bucket_corners(loc, p, s_h, s_w, s_start, ba, t, row, w);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            if (w[q] != 0.0f) slot[q] = hash_add(s_key, s_cnt, row[q], rank[q]);
+            if (w[q] != 0.0f) slot[q] = hash_add(s_key, s_cnt, s_used, &s_nused, row[q], rank[q]);
     }
     __syncthreads();
     unsigned *fill = cnt + (size_t)p.B * p.P_total;  // fill cursors follow the counts
-    for (int h = threadIdx.x; h < kHashSlots; h += 256) {
-        const unsigned n = s_cnt[h];
-        if (n == 0) continue;
-        const unsigned key = s_key[h];
-        if constexpr (FILL) s_base[h] = starts[key] + atomicAdd(&fill[key], n);
-        else atomicAdd(&cnt[key], n);
+    // one global atomic per slot in use; the four per thread are issued together
+    const int nused = (int)s_nused;
+    unsigned hs[4], key[4], n[4], res[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int j = threadIdx.x + 256 * r;
+        hs[r] = j < nused ? s_used[j] : 0u;
+        key[r] = s_key[hs[r]];
+        n[r] = j < nused ? s_cnt[hs[r]] : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (n[r] == 0) continue;
+        if constexpr (FILL) res[r] = atomicAdd(&fill[key[r]], n[r]);
+        else atomicAdd(&cnt[key[r]], n[r]);
+    }
+    if constexpr (FILL) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (n[r] != 0) s_base[hs[r]] = starts[key[r]] + res[r];
     }
     if constexpr (FILL) {
         __syncthreads();
