@@ -300,11 +300,6 @@ __global__ __launch_bounds__(kThreads) void agg_bwd_kernel(
     }
 }
 
-// The main kernel for the bucketed path when a group's channels are S 16-byte vectors
-// (S a power of two, S <= 16): the same records and results, with the corner loads
-// of each batch of Z = 64/S records issued through a buffer resource one batch ahead
-// of the dot products, and the S-lane sums over compile-time widths. Record offsets
-// are element offsets inside the batch's features, which must be under 2 GiB.
 // Sum over each aligned S-lane slice (S <= 16, a power of two), complete in the
 // slice's last lane: row_shr DPP steps, so no LDS permutes and no waits.
 template <int N>
@@ -321,7 +316,15 @@ __device__ __forceinline__ float slice_sum_to_last(float v) {
     return v;
 }
 
-template <class E, int S, int NV>
+// The main kernel when a group's channels are S 16-byte vectors (S = 2..16, a power
+// of two), no atomic accumulation is asked for and a workspace is given: the same
+// records and dot products as agg_bwd_kernel, with the corner loads of each batch of
+// Z = 64/S records issued through a buffer resource one batch ahead of the dots
+// (record offsets in bytes inside the batch's features, which must be under 2 GiB),
+// the unit's logits read once into registers (at most kRegRounds rounds), and per
+// unit g_t (unit-major) plus max, 1/sum and sum_t wt g_t into the workspace for
+// agg_bwd_finish_kernel.
+template <class E, int S>
 __global__ __launch_bounds__(kThreads) void agg_bwd_pipe_kernel(
     const typename E::bits *__restrict__ feat, const float *__restrict__ loc,
     const float *__restrict__ weights, const typename E::bits *__restrict__ gout,
@@ -358,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void agg_bwd_pipe_kernel(
     const float *lrow = loc + (size_t)ba * NPC * 2;
     const Bt *fb = feat + (size_t)b * p.P_total * GC;
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(fb, (unsigned)((size_t)p.P_total * GC * elt));
-    const int lane_off = (g * p.Cg + s * NV * V) * elt;  // this lane's channels, bytes
+    const int lane_off = (g * p.Cg + s * V) * elt;  // this lane's channels, bytes
     AggRec *rec = s_rec[wv];
     float(*res)[3] = s_res[wv];
 
@@ -382,13 +385,8 @@ __global__ __launch_bounds__(kThreads) void agg_bwd_pipe_kernel(
         for (int k = 0; k < kRegRounds; ++k) e += expf(lgr[k] - mx);
         inv = 1.0f / wsum(e);
     }
-    float gc[NV][V];  // this lane's channels s*NV*V .. (s+1)*NV*V - 1 of G
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const uint4 graw =
-            *reinterpret_cast<const uint4 *>(gout + (size_t)ba * GC + g * p.Cg + (s * NV + v) * V);
-        unpack<E, V>(graw, gc[v]);
-    }
+    float gc[V];  // this lane's channels s*V .. s*V + V - 1 of G
+    unpack<E, V>(*reinterpret_cast<const uint4 *>(gout + (size_t)ba * GC + g * p.Cg + s * V), gc);
 
     // this lane's location for the round at pc0 (read one round ahead)
     auto fetch = [&](int pc0, float2 &uv) __attribute__((always_inline)) {
@@ -438,36 +436,30 @@ __global__ __launch_bounds__(kThreads) void agg_bwd_pipe_kernel(
         }
         const int nrec = min(per_round, (NPC - pc0) * p.scales);
         const int iters = (nrec + Z - 1) / Z;
-        uint4 cb[2][4][NV];
+        uint4 cb[2][4];
         // batch it: slice z takes record it*Z + z (record 0 again past the end, unused)
         auto issue = [&](int it, int slot) __attribute__((always_inline)) {
             const int j = it * Z + z;
             const int4 o = *reinterpret_cast<const int4 *>(&rec[j < nrec ? j : 0].o00);
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                cb[slot][0][v] = buffer_load<uint4>(rsrc, o.x + lane_off + 16 * v);
-                cb[slot][1][v] = buffer_load<uint4>(rsrc, o.y + lane_off + 16 * v);
-                cb[slot][2][v] = buffer_load<uint4>(rsrc, o.z + lane_off + 16 * v);
-                cb[slot][3][v] = buffer_load<uint4>(rsrc, o.w + lane_off + 16 * v);
-            }
+            cb[slot][0] = buffer_load<uint4>(rsrc, o.x + lane_off);
+            cb[slot][1] = buffer_load<uint4>(rsrc, o.y + lane_off);
+            cb[slot][2] = buffer_load<uint4>(rsrc, o.z + lane_off);
+            cb[slot][3] = buffer_load<uint4>(rsrc, o.w + lane_off);
         };
         auto compute = [&](int it, int slot) __attribute__((always_inline)) {
             const int j = it * Z + z;
+            float va[V], vb[V], vc[V], ve[V];
+            unpack<E, V>(cb[slot][0], va);
+            unpack<E, V>(cb[slot][1], vb);
+            unpack<E, V>(cb[slot][2], vc);
+            unpack<E, V>(cb[slot][3], ve);
             float D00 = 0.0f, D01 = 0.0f, D10 = 0.0f, D11 = 0.0f;
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                float va[V], vb[V], vc[V], ve[V];
-                unpack<E, V>(cb[slot][0][v], va);
-                unpack<E, V>(cb[slot][1][v], vb);
-                unpack<E, V>(cb[slot][2][v], vc);
-                unpack<E, V>(cb[slot][3][v], ve);
-#pragma unroll
-                for (int u = 0; u < V; ++u) {
-                    D00 = fmaf(gc[v][u], va[u], D00);
-                    D01 = fmaf(gc[v][u], vb[u], D01);
-                    D10 = fmaf(gc[v][u], vc[u], D10);
-                    D11 = fmaf(gc[v][u], ve[u], D11);
-                }
+            for (int u = 0; u < V; ++u) {
+                D00 = fmaf(gc[u], va[u], D00);
+                D01 = fmaf(gc[u], vb[u], D01);
+                D10 = fmaf(gc[u], vc[u], D10);
+                D11 = fmaf(gc[u], ve[u], D11);
             }
             D00 = slice_sum_to_last<S>(D00);
             D01 = slice_sum_to_last<S>(D01);
@@ -962,8 +954,8 @@ hipError_t launch_e(const AggBwdLaunch &a, const AggBwdPlan &pl, hipStream_t str
         const B *ft = static_cast<const B *>(a.feat);
         const B *go = static_cast<const B *>(a.grad_out);
         const dim3 grid(p.nblocks), block(kThreads);
-        // 16-byte channel vectors, a power-of-two count per group: pipelined kernel
-        // with S lanes of NV vectors per record
+        // 2-16 channel vectors of 16 bytes per group, no atomics, a workspace and at
+        // most kRegRounds rounds of samples: the pipelined kernel, one lane per vector
         constexpr int V16 = 16 / elt;
         const int nv16 = a.Cg % V16 == 0 ? a.Cg / V16 : 0;
         const int rounds = (a.pts * a.cams + p.npc - 1) / p.npc;
@@ -975,11 +967,11 @@ hipError_t launch_e(const AggBwdLaunch &a, const AggBwdPlan &pl, hipStream_t str
         float *gts = pipe ? reinterpret_cast<float *>(ws + pl.off_gt) : nullptr;
         float *us = pipe ? reinterpret_cast<float *>(ws + pl.off_us) : nullptr;
         if (pipe) {
-            switch (nv16) {  // S = nv16 lanes of one vector
-                case 2: hipLaunchKernelGGL((agg_bwd_pipe_kernel<E, 2, 1>), grid, block, 0, stream, ft, a.loc, a.weights, go, part, gts, us, p); break;
-                case 4: hipLaunchKernelGGL((agg_bwd_pipe_kernel<E, 4, 1>), grid, block, 0, stream, ft, a.loc, a.weights, go, part, gts, us, p); break;
-                case 8: hipLaunchKernelGGL((agg_bwd_pipe_kernel<E, 8, 1>), grid, block, 0, stream, ft, a.loc, a.weights, go, part, gts, us, p); break;
-                default: hipLaunchKernelGGL((agg_bwd_pipe_kernel<E, 16, 1>), grid, block, 0, stream, ft, a.loc, a.weights, go, part, gts, us, p); break;
+            switch (nv16) {  // S = nv16 lanes of one 16-byte vector each
+                case 2: hipLaunchKernelGGL((agg_bwd_pipe_kernel<E, 2>), grid, block, 0, stream, ft, a.loc, a.weights, go, part, gts, us, p); break;
+                case 4: hipLaunchKernelGGL((agg_bwd_pipe_kernel<E, 4>), grid, block, 0, stream, ft, a.loc, a.weights, go, part, gts, us, p); break;
+                case 8: hipLaunchKernelGGL((agg_bwd_pipe_kernel<E, 8>), grid, block, 0, stream, ft, a.loc, a.weights, go, part, gts, us, p); break;
+                default: hipLaunchKernelGGL((agg_bwd_pipe_kernel<E, 16>), grid, block, 0, stream, ft, a.loc, a.weights, go, part, gts, us, p); break;
             }
             if (a.grad_weights || wn) {
                 const long long n = nsamp * a.G;
