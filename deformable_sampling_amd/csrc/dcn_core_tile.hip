@@ -392,17 +392,28 @@ __device__ __forceinline__ void stage_region_fixed(uint4 *lds, const typename E:
     const int cb = ((a.g0 * p.C) + (tid & (CPP - 1)) * V) * elt;
     const int w0 = __builtin_amdgcn_readfirstlane(tid & ~63);
     const int lane = tid & 63;
+    // region pixel of this lane's first copy, then advanced by NT / CPP pixels per copy
+    static_assert(NT % CPP == 0, "whole pixels per step");
+    constexpr int DY = (NT / CPP) / RW, DX = (NT / CPP) % RW;
+    const int r0 = (w0 + lane) / CPP;
+    int ry = r0 / RW, rx = r0 - ry * RW;
+    const int GCe = GC * elt;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
         const int i0 = w0 + it * NT;
         if (it < NIT - 1 || i0 < total) {
-            const int c = i0 + lane;
-            const int rr = c / CPP;
-            const int ry = rr / RW, rx = rr - ry * RW;
+            // only the last step can pass the region's end
+            const bool in = it < NIT - 1 || i0 + lane < total;
             const int yy = a.ry0 + ry, xx = a.rx0 + rx;
-            const bool ok = c < total && (unsigned)yy < (unsigned)p.H && (unsigned)xx < (unsigned)p.W;
-            const int off = ok ? (int)__umul24(__umul24(yy, p.W) + xx, GC) * elt + cb : (int)img_bytes;
+            const bool ok = in && (unsigned)yy < (unsigned)p.H && (unsigned)xx < (unsigned)p.W;
+            const int off = ok ? (yy * p.W + xx) * GCe + cb : (int)img_bytes;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(lds + i0), 16, off, 0, 0, 0);
+        }
+        rx += DX;
+        ry += DY;
+        if (rx >= RW) {
+            rx -= RW;
+            ++ry;
         }
     }
 }
