@@ -865,12 +865,12 @@ __global__ __launch_bounds__(256 * NCH) void bwd_gather_staged_kernel(
     constexpr int V = 16 / (int)sizeof(typename E::bits);
     __shared__ uint4 s_g[kStageCap][NCH];   // cell-sorted: the record's grad_out slice
     __shared__ float4 s_w[kStageCap];       // cell-sorted: the four corner weights m*w_ab
-    __shared__ unsigned short s_cell[kStageCap];
     __shared__ unsigned s_cnt[kCells * kCells];
     __shared__ unsigned s_pos[kCells * kCells];
     __shared__ unsigned s_fill[kCells * kCells];
 
-    const int nthreads = kTile * kTile * NCH;
+    constexpr int nthreads = kTile * kTile * NCH;
+    constexpr int kRecPer = (kStageCap + nthreads - 1) / nthreads;  // records per thread and chunk
     const int tid = threadIdx.x;
     const int blk = xcd_remap((int)blockIdx.x, q.nblocks);
     const int g = blk % q.G;
@@ -930,13 +930,21 @@ __global__ __launch_bounds__(256 * NCH) void bwd_gather_staged_kernel(
                 ++k;
             }
         };
-        for (int r = tid; r < nrec; r += nthreads) {
-            int k, gi;
-            locate(r, k, gi);
-            const unsigned vx = rec[rb[k] + gi].x;
-            const int cell = ((int)((vx >> 4) & 15u) + sy[k]) * kCells + (int)(vx & 15u) + sx[k];
-            s_cell[r] = (unsigned short)cell;
-            atomicAdd(&s_cnt[cell], 1u);
+        // the chunk's records stay in registers from the counting to the sorting pass
+        uint4 rv[kRecPer];
+        int rcell[kRecPer];
+#pragma unroll
+        for (int j = 0; j < kRecPer; ++j) {
+            const int r = tid + j * nthreads;
+            rcell[j] = 0;
+            if (r < nrec) {
+                int k, gi;
+                locate(r, k, gi);
+                rv[j] = rec[rb[k] + gi];
+                const unsigned vx = rv[j].x;
+                rcell[j] = ((int)((vx >> 4) & 15u) + sy[k]) * kCells + (int)(vx & 15u) + sx[k];
+                atomicAdd(&s_cnt[rcell[j]], 1u);
+            }
         }
         __syncthreads();
         if (tid < 64) {  // exclusive scan of the 289 cell counts by one wavefront
@@ -963,11 +971,12 @@ __global__ __launch_bounds__(256 * NCH) void bwd_gather_staged_kernel(
         }
         __syncthreads();
         // counting sort by cell: weights, and the grad_out slice fetched once per record
-        for (int r = tid; r < nrec; r += nthreads) {
-            int k, gi;
-            locate(r, k, gi);
-            const uint4 v = rec[rb[k] + gi];
-            const int cell = s_cell[r];
+#pragma unroll
+        for (int j = 0; j < kRecPer; ++j) {
+            const int r = tid + j * nthreads;
+            if (r >= nrec) continue;
+            const uint4 v = rv[j];
+            const int cell = rcell[j];
             const unsigned at = s_pos[cell] + atomicAdd(&s_fill[cell], 1u);
             int cyy, cxx;
             float fy, uy, fx, ux;
