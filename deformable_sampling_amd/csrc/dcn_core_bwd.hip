@@ -914,6 +914,35 @@ __global__ __launch_bounds__(256 * NCH) void bwd_gather_staged_kernel(
 #pragma unroll
     for (int u = 0; u < V; ++u) acc[u] = 0.0f;
 
+    // record r of the chunk at c0: its run k (own bin or a neighbour's sub-bin) and
+    // index gi in that run
+    auto locate = [&](int c0, int r, int &k, int &gi) {
+        gi = c0 + r;
+        k = 0;
+        while (k < 4 && gi >= re[k] - rb[k]) {
+            gi -= re[k] - rb[k];
+            ++k;
+        }
+    };
+    // a chunk's records, loaded one chunk ahead (during the previous chunk's sums) and
+    // held in registers through its counting and sorting passes
+    uint4 rv[kRecPer];
+    int rk[kRecPer];
+    auto fetch = [&](int c0) __attribute__((always_inline)) {
+        const int nrec = min(kStageCap, total - c0);
+#pragma unroll
+        for (int j = 0; j < kRecPer; ++j) {
+            const int r = tid + j * nthreads;
+            rk[j] = 0;
+            if (r < nrec) {
+                int k, gi;
+                locate(c0, r, k, gi);
+                rk[j] = k;
+                rv[j] = rec[rb[k] + gi];
+            }
+        }
+    };
+    if (total > 0) fetch(0);
     for (int c0 = 0; c0 < total; c0 += kStageCap) {
         const int nrec = min(kStageCap, total - c0);
         __syncthreads();  // the previous chunk's readers are done
@@ -922,25 +951,13 @@ __global__ __launch_bounds__(256 * NCH) void bwd_gather_staged_kernel(
             s_fill[i] = 0;
         }
         __syncthreads();
-        auto locate = [&](int r, int &k, int &gi) {
-            gi = c0 + r;
-            k = 0;
-            while (k < 4 && gi >= re[k] - rb[k]) {
-                gi -= re[k] - rb[k];
-                ++k;
-            }
-        };
-        // the chunk's records stay in registers from the counting to the sorting pass
-        uint4 rv[kRecPer];
         int rcell[kRecPer];
 #pragma unroll
         for (int j = 0; j < kRecPer; ++j) {
             const int r = tid + j * nthreads;
             rcell[j] = 0;
             if (r < nrec) {
-                int k, gi;
-                locate(r, k, gi);
-                rv[j] = rec[rb[k] + gi];
+                const int k = rk[j];
                 const unsigned vx = rv[j].x;
                 rcell[j] = ((int)((vx >> 4) & 15u) + sy[k]) * kCells + (int)(vx & 15u) + sx[k];
                 atomicAdd(&s_cnt[rcell[j]], 1u);
@@ -990,6 +1007,7 @@ __global__ __launch_bounds__(256 * NCH) void bwd_gather_staged_kernel(
             for (int u = 0; u < NCH; ++u) s_g[at][u] = src[u];
         }
         __syncthreads();
+        if (c0 + kStageCap < total) fetch(c0 + kStageCap);
         if (inside) {
             const float *sw = reinterpret_cast<const float *>(s_w);
 #pragma unroll
