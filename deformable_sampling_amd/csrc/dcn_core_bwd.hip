@@ -176,6 +176,50 @@ __global__ __launch_bounds__(kThreads) void bwd_count_kernel(const float *__rest
     const int oy = (tile / p.TXo) * kTile, ox = (tile % p.TXo) * kTile;
     const BinWin win = bin_window(oy, ox, p);
     const float2 *od = reinterpret_cast<const float2 *>(offset);
+    if constexpr (KH > 0 && KW > 0) {
+        // window compiled in: thread = pixel of the tile, its K taps in turn; taps of one
+        // pixel mostly share a few bins, so window counts are merged in registers (up to
+        // four distinct slots) before the LDS atomics
+        const int lq = (int)threadIdx.x;
+        const int ho = oy + (lq >> 4), wo = ox + (lq & 15);
+        int ms[4] = {-1, -1, -1, -1};
+        unsigned mc[4] = {0u, 0u, 0u, 0u};
+        if (ho < p.Ho && wo < p.Wo) {
+            const float2 *pd = od + (((size_t)n * p.Ho * p.Wo + (size_t)ho * p.Wo + wo) * p.G + g) * K;
+            float2 dd[KH * KW];
+#pragma unroll
+            for (int k = 0; k < KH * KW; ++k) dd[k] = pd[k];
+#pragma unroll
+            for (int k = 0; k < KH * KW; ++k) {
+                const int i = k / KW, j = k - i * KW;
+                int y0, x0;
+                float f, u;
+                split_coord_fu(ho * p.sh - p.ph + i * p.dh, mul_rn(p.offset_scale, dd[k].y), y0, f, u);
+                split_coord_fu(wo * p.sw - p.pw + j * p.dw, mul_rn(p.offset_scale, dd[k].x), x0, f, u);
+                unsigned bin = 0, local, rank = 0;
+                if (!home_bin(y0, x0, n, g, p, bin, local)) continue;
+                const int ws = win_slot(y0, x0, win);
+                if (ws < 0) {
+                    if (block_bin_slot(s_key, s_cnt, bin, rank) == kHash)
+                        atomicAdd(&counts[bin], 1u);  // table full: direct
+                    continue;
+                }
+                bool done = false;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (!done && ms[e] == ws) { ++mc[e]; done = true; }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (!done && ms[e] < 0) { ms[e] = ws; mc[e] = 1u; done = true; }
+                }
+                if (!done) atomicAdd(&s_win[ws], 1u);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (ms[e] >= 0) atomicAdd(&s_win[ms[e]], mc[e]);
+    } else
     for (int r = 0; r < K; ++r) {
         const int idx = r * kThreads + (int)threadIdx.x;  // sample: local pair idx/K, tap idx%K
         const int lq = idx / K, k = idx - lq * K;
