@@ -81,14 +81,13 @@ __global__ __launch_bounds__(256) void v2_prep_kernel(const uint16_t *__restrict
     if (t >= (long long)p.Mp * rv) return;
     const int co = (int)(t / rv);
     const int r0 = (int)(t % rv) * kVec;
+    // Cin_pad is a multiple of kVec: the 8 values share their tap k
+    const int k = r0 / p.Cin_pad, ci0 = r0 - k * p.Cin_pad;
+    const uint16_t *wk = w + ((size_t)co * p.Cin + ci0) * p.K + k;
+    const bool row = co < p.Cout && k < p.K;
     uint16_t v[kVec];
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) {
-        const int r = r0 + i;
-        const int k = r / p.Cin_pad, ci = r % p.Cin_pad;
-        v[i] = (co < p.Cout && k < p.K && ci < p.Cin) ? w[((size_t)co * p.Cin + ci) * p.K + k]
-                                                      : (uint16_t)0;
-    }
+    for (int i = 0; i < kVec; ++i) v[i] = (row && ci0 + i < p.Cin) ? wk[(size_t)i * p.K] : (uint16_t)0;
     uint4 o;
     __builtin_memcpy(&o, v, 16);
     *reinterpret_cast<uint4 *>(wp + (size_t)co * p.Rp + r0) = o;
