@@ -65,19 +65,23 @@ __device__ __forceinline__ TileAt tile_at(int t, const TileParams &p) {
 }
 
 // This lane's (pixel, group) within a tile: lane lp of the pixel is gl*S + s.
+// LPP_/TW_ != 0 give lanes per pixel and tile width at compile time (the 16x16,
+// 512-thread plan has 2 and 16), so the lane's indices are shifts and masks.
 struct LaneAt {
     int s, gl, q, ho, wo, g;
     bool active;
 };
-template <int S>
+template <int S, int LPP_ = 0, int TW_ = 0>
 __device__ __forceinline__ LaneAt lane_at(const TileAt &a, const TileParams &p) {
     LaneAt l;
     const int tid = threadIdx.x;
-    const int lp = tid % p.lpp;
+    const int lpp = LPP_ ? LPP_ : p.lpp;
+    const int tw = TW_ ? TW_ : p.TW;
+    const int lp = tid % lpp;
     l.s = lp % S;
     l.gl = lp / S;
-    l.q = tid / p.lpp;
-    const int qy = l.q / p.TW, qx = l.q - qy * p.TW;
+    l.q = tid / lpp;
+    const int qy = l.q / tw, qx = l.q - qy * tw;
     l.ho = a.ho0 + qy;
     l.wo = a.wo0 + qx;
     l.active = l.q < p.TH * p.TW && l.ho < p.Ho && l.wo < p.Wo;
@@ -430,7 +434,8 @@ __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::b
     extern __shared__ uint4 lds[];  // [RH][RW][cpp]
 
     const TileAt a = tile_at(xcd_remap((int)blockIdx.x, p.nblocks), p);
-    const LaneAt l = lane_at<S>(a, p);
+    // the compiled-in staging plan (RH_ != 0) has 16-pixel rows of 2 lanes per pixel
+    const LaneAt l = lane_at<S, RH_ ? 2 : 0, RH_ ? 16 : 0>(a, p);
 
     float d[2 * K], m[K];
     load_dm<K, OM>(d, m, a, l, offset, mask, p);
@@ -827,7 +832,7 @@ hipError_t launch_tile(const CoreLaunch &a, const TileParams &p, hipStream_t str
     // 16x16-pixel tiles with halo 8 (region width 35) of 64-byte slices: the common
     // plan, with its region geometry compiled in; with region height 35, 512 threads
     // and an image under 2 GiB, also the staging (RH_ = 35: buffer-form copies)
-    const bool fixed = p.RH == 35 && p.threads == 512 &&
+    const bool fixed = p.RH == 35 && p.threads == 512 && p.lpp == 2 && p.TW == 16 &&
                        (size_t)p.H * p.W * p.G * p.C * sizeof(Bt) < (size_t(1) << 31);
 
     if (p.cpp == 4 && p.RW == 35 && fixed) return go(dcn_core_tile_kernel<E, OM, 3, 3, S, NC, 4, 35, 35>);
