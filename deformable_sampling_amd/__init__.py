@@ -20,6 +20,10 @@ LIB_PATH = os.path.join(_HERE, "libdcn.so")
 DCN_F32, DCN_F16, DCN_BF16 = 0, 1, 2
 _DTYPE_ID = {torch.float32: DCN_F32, torch.float16: DCN_F16, torch.bfloat16: DCN_BF16}
 
+# alternative backward kernel paths (dcn_bwd_path flags; 0 = the library's choice)
+DCN_BWD_DEFAULT, DCN_BWD_ATOMIC, DCN_BWD_PAIR_PASS = 0, 1, 2
+DCN_BWD_PAIR_PASS_RECORDS, DCN_BWD_UNSTAGED_GATHER, DCN_BWD_GENERAL_MAIN = 4, 8, 16
+
 STATUS = {0: "DCN_OK", 1: "DCN_ERR_NULL", 2: "DCN_ERR_SHAPE", 3: "DCN_ERR_PARAM",
           4: "DCN_ERR_DTYPE", 5: "DCN_ERR_ALIGN", 6: "DCN_ERR_WORKSPACE", 7: "DCN_ERR_HIP"}
 
@@ -29,6 +33,8 @@ EXPORTS = ("dcn_core_forward", "dcn_core_forward_packed", "dcn_core_backward_wor
            "dcn_v2_backward_workspace_bytes", "dcn_v2_backward",
            "deform_agg_forward", "deform_agg_backward_workspace_bytes", "deform_agg_backward",
            "deform_roi_pool_forward",
+           "dcn_core_backward_workspace_bytes_path", "dcn_core_backward_path",
+           "deform_agg_backward_workspace_bytes_path", "deform_agg_backward_path",
            "dcn_status_string", "dcn_last_hip_error")
 
 
@@ -81,6 +87,15 @@ def load(path: str | None = None):
     lib.deform_agg_backward_workspace_bytes.argtypes = [i] * 9
     lib.deform_agg_backward.restype = i
     lib.deform_agg_backward.argtypes = [vp] * 10 + [_c.c_size_t] + [i] * 9 + [i, vp]
+    u = _c.c_uint
+    lib.dcn_core_backward_workspace_bytes_path.restype = _c.c_size_t
+    lib.dcn_core_backward_workspace_bytes_path.argtypes = [i] * 14 + [u]
+    lib.dcn_core_backward_path.restype = i
+    lib.dcn_core_backward_path.argtypes = [vp] * 8 + [_c.c_size_t] + [i] * 13 + [f, i, i, u, vp]
+    lib.deform_agg_backward_workspace_bytes_path.restype = _c.c_size_t
+    lib.deform_agg_backward_workspace_bytes_path.argtypes = [i] * 9 + [u]
+    lib.deform_agg_backward_path.restype = i
+    lib.deform_agg_backward_path.argtypes = [vp] * 10 + [_c.c_size_t] + [i] * 9 + [i, u, vp]
     lib.deform_roi_pool_forward.restype = i
     lib.deform_roi_pool_forward.argtypes = [vp] * 4 + [i] * 7 + [f, f, i, vp]
     lib.dcn_status_string.restype = _c.c_char_p
@@ -203,11 +218,15 @@ def dcn_core_forward_packed(x, offset_mask, *, groups, kernel=(3, 3), stride=1, 
 
 
 def dcn_core_backward_workspace_bytes(N, H, W, G, C, kernel=(3, 3), stride=1, pad=1,
-                                      dilation=1, dtype=torch.float16):
+                                      dilation=1, dtype=torch.float16, path=DCN_BWD_DEFAULT):
+    """Workspace bytes of dcn_core_backward (of dcn_core_backward_path when path != 0)."""
     kh, kw = _pair(kernel)
     sh, sw = _pair(stride)
     ph, pw = _pair(pad)
     dh, dw = _pair(dilation)
+    if path:
+        return int(load().dcn_core_backward_workspace_bytes_path(
+            N, H, W, G, C, kh, kw, sh, sw, ph, pw, dh, dw, _DTYPE_ID[dtype], int(path)))
     return int(load().dcn_core_backward_workspace_bytes(N, H, W, G, C, kh, kw, sh, sw, ph, pw,
                                                         dh, dw, _DTYPE_ID[dtype]))
 
@@ -215,11 +234,12 @@ def dcn_core_backward_workspace_bytes(N, H, W, G, C, kernel=(3, 3), stride=1, pa
 def dcn_core_backward(x, offset, mask, grad_out, *, kernel=(3, 3), stride=1, pad=1, dilation=1,
                       offset_scale=1.0, softmax=False, need=("x", "offset", "mask"),
                       grad_x=None, grad_offset=None, grad_mask=None, workspace=None,
-                      stream=None):
+                      path=DCN_BWD_DEFAULT, stream=None):
     """Gradients of dcn_core_forward w.r.t. x, offset and mask (the names in `need`).
     grad_out [N,Ho,Wo,G*C] in x's dtype. Returns (grad_x, grad_offset, grad_mask),
     None for a gradient not asked for; grad_mask is w.r.t. the mask argument (the
-    unit modulation / zero logits when mask is None)."""
+    unit modulation / zero logits when mask is None). path != 0 calls
+    dcn_core_backward_path with those DCN_BWD_* flags."""
     kh, kw = _pair(kernel)
     sh, sw = _pair(stride)
     ph, pw = _pair(pad)
@@ -251,14 +271,18 @@ def dcn_core_backward(x, offset, mask, grad_out, *, kernel=(3, 3), stride=1, pad
     _check(grad_offset, "grad_offset", torch.float32, allow_none=True)
     _check(grad_mask, "grad_mask", torch.float32, allow_none=True)
     wsb = dcn_core_backward_workspace_bytes(N, H, W, G, GC // G, kernel, stride, pad, dilation,
-                                            x.dtype) if grad_x is not None else 0
+                                            x.dtype, path) if grad_x is not None else 0
     if workspace is None and wsb:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    _call("dcn_core_backward", _ptr(x), _ptr(offset), _ptr(mask), _ptr(grad_out), _ptr(grad_x),
-          _ptr(grad_offset), _ptr(grad_mask), _ptr(workspace),
-          0 if workspace is None else workspace.numel() * workspace.element_size(),
-          N, H, W, G, GC // G, kh, kw, sh, sw, ph, pw, dh, dw, float(offset_scale),
-          int(bool(softmax)), _DTYPE_ID[x.dtype], _stream(stream))
+    args = [_ptr(x), _ptr(offset), _ptr(mask), _ptr(grad_out), _ptr(grad_x), _ptr(grad_offset),
+            _ptr(grad_mask), _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            N, H, W, G, GC // G, kh, kw, sh, sw, ph, pw, dh, dw, float(offset_scale),
+            int(bool(softmax)), _DTYPE_ID[x.dtype]]
+    if path:
+        _call("dcn_core_backward_path", *args, int(path), _stream(stream))
+    else:
+        _call("dcn_core_backward", *args, _stream(stream))
     return grad_x, grad_offset, grad_mask
 
 
@@ -421,18 +445,23 @@ def deform_agg_forward(feat, spatial_shape, scale_start, loc, weights, out=None,
 
 
 def deform_agg_backward_workspace_bytes(B, P_total, A, pts, cams, scales, G, Cg,
-                                        dtype=torch.float32):
+                                        dtype=torch.float32, path=DCN_BWD_DEFAULT):
+    """Workspace bytes of deform_agg_backward (of deform_agg_backward_path when path != 0)."""
+    if path:
+        return int(load().deform_agg_backward_workspace_bytes_path(
+            B, P_total, A, pts, cams, scales, G, Cg, _DTYPE_ID[dtype], int(path)))
     return int(load().deform_agg_backward_workspace_bytes(B, P_total, A, pts, cams, scales, G,
                                                           Cg, _DTYPE_ID[dtype]))
 
 
 def deform_agg_backward(feat, spatial_shape, scale_start, loc, weights, grad_out, *,
                         softmax=False, need=("feat", "loc", "weights"), workspace=None,
-                        stream=None):
+                        path=DCN_BWD_DEFAULT, stream=None):
     """Gradients of deform_agg_forward w.r.t. feat, loc and weights (the names in
     `need`). Returns (grad_feat, grad_loc, grad_weights), None where not asked.
     workspace: a device buffer, None to allocate one, or False to pass none (allowed
-    when only the weights' gradient is asked)."""
+    when only the weights' gradient is asked). path != 0 calls deform_agg_backward_path
+    with those DCN_BWD_* flags."""
     _check(feat, "feat")
     _check(loc, "loc", torch.float32)
     _check(weights, "weights", torch.float32)
@@ -453,16 +482,20 @@ def deform_agg_backward(feat, spatial_shape, scale_start, loc, weights, grad_out
     gl = torch.empty_like(loc) if "loc" in need else None
     gw = torch.empty_like(weights) if "weights" in need else None
     wsb = deform_agg_backward_workspace_bytes(B, P_total, A, pts, cams, scales, G, GC // G,
-                                              feat.dtype)
+                                              feat.dtype, path)
     if workspace is None and wsb:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=feat.device)
     elif workspace is False:
         workspace = None
-    _call("deform_agg_backward", _ptr(feat), ss.ctypes.data, st.ctypes.data, _ptr(loc),
-          _ptr(weights), _ptr(grad_out), _ptr(gf), _ptr(gl), _ptr(gw), _ptr(workspace),
-          0 if workspace is None else workspace.numel() * workspace.element_size(),
-          B, P_total, A, pts, cams, scales, G, GC // G, int(bool(softmax)), _DTYPE_ID[feat.dtype],
-          _stream(stream))
+    args = [_ptr(feat), ss.ctypes.data, st.ctypes.data, _ptr(loc), _ptr(weights), _ptr(grad_out),
+            _ptr(gf), _ptr(gl), _ptr(gw), _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            B, P_total, A, pts, cams, scales, G, GC // G, int(bool(softmax)),
+            _DTYPE_ID[feat.dtype]]
+    if path:
+        _call("deform_agg_backward_path", *args, int(path), _stream(stream))
+    else:
+        _call("deform_agg_backward", *args, _stream(stream))
     return gf, gl, gw
 
 

@@ -12,6 +12,8 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr long long kI32 = 2147483647LL;
+constexpr unsigned kBwdPathMask = DCN_BWD_ATOMIC | DCN_BWD_PAIR_PASS | DCN_BWD_PAIR_PASS_RECORDS |
+                                  DCN_BWD_UNSTAGED_GATHER | DCN_BWD_GENERAL_MAIN;
 
 bool valid_dtype(dcn_dtype d) { return d == DCN_F32 || d == DCN_F16 || d == DCN_BF16; }
 size_t dtype_size(dcn_dtype d) { return d == DCN_F32 ? 4 : 2; }
@@ -129,16 +131,13 @@ dcn_status dcn_core_forward_packed(const void *x, const void *offset_mask, void 
     return hip_status(dcn::launch_dcn_core(a, stream));
 }
 
-// DCN_CORE_BWD_ATOMIC=1 selects the atomic fallback of the backward at any size
-// (so that it can be tested); read on each call.
-static bool core_bwd_force_atomic() {
-    const char *e = getenv("DCN_CORE_BWD_ATOMIC");
-    return e && e[0] == '1';
-}
+static bool valid_path(unsigned path) { return (path & ~kBwdPathMask) == 0; }
 
-size_t dcn_core_backward_workspace_bytes(int N, int H, int W, int G, int C, int kh, int kw,
-                                         int stride_h, int stride_w, int pad_h, int pad_w,
-                                         int dil_h, int dil_w, dcn_dtype dtype) {
+size_t dcn_core_backward_workspace_bytes_path(int N, int H, int W, int G, int C, int kh, int kw,
+                                              int stride_h, int stride_w, int pad_h, int pad_w,
+                                              int dil_h, int dil_w, dcn_dtype dtype,
+                                              unsigned path) {
+    if (!valid_path(path)) return 0;
     if (!valid_dtype(dtype) || N < 0 || H <= 0 || W <= 0 || G <= 0 || C <= 0) return 0;
     if (check_window(kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w) != DCN_OK) return 0;
     const long long Ho = out_extent(H, kh, stride_h, pad_h, dil_h);
@@ -146,18 +145,27 @@ size_t dcn_core_backward_workspace_bytes(int N, int H, int W, int G, int C, int 
     if (Ho <= 0 || Wo <= 0) return 0;
     if ((long long)(H + 1) * (W + 1) * G * C > kI32 || (long long)N * Ho * Wo * G > kI32) return 0;
     dcn::CoreBwdPlan plan;
-    dcn::plan_core_bwd(N, H, W, G, C, (int)Ho, (int)Wo, kh * kw, dtype, core_bwd_force_atomic(),
-                       plan);
+    dcn::plan_core_bwd(N, H, W, G, C, (int)Ho, (int)Wo, kh * kw, dtype,
+                       (path & DCN_BWD_ATOMIC) != 0, plan);
     return plan.total;
 }
 
-dcn_status dcn_core_backward(const void *x, const float *offset, const float *mask,
-                             const void *grad_out, void *grad_x, float *grad_offset,
-                             float *grad_mask, void *workspace, size_t workspace_bytes, int N,
-                             int H, int W, int G, int C, int kh, int kw, int stride_h, int stride_w,
-                             int pad_h, int pad_w, int dil_h, int dil_w, float offset_scale,
-                             int softmax, dcn_dtype dtype, hipStream_t stream) {
+size_t dcn_core_backward_workspace_bytes(int N, int H, int W, int G, int C, int kh, int kw,
+                                         int stride_h, int stride_w, int pad_h, int pad_w,
+                                         int dil_h, int dil_w, dcn_dtype dtype) {
+    return dcn_core_backward_workspace_bytes_path(N, H, W, G, C, kh, kw, stride_h, stride_w,
+                                                  pad_h, pad_w, dil_h, dil_w, dtype, 0u);
+}
+
+dcn_status dcn_core_backward_path(const void *x, const float *offset, const float *mask,
+                                  const void *grad_out, void *grad_x, float *grad_offset,
+                                  float *grad_mask, void *workspace, size_t workspace_bytes, int N,
+                                  int H, int W, int G, int C, int kh, int kw, int stride_h,
+                                  int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                                  float offset_scale, int softmax, dcn_dtype dtype, unsigned path,
+                                  hipStream_t stream) {
     if (!valid_dtype(dtype)) return DCN_ERR_DTYPE;
+    if (!valid_path(path)) return DCN_ERR_PARAM;
     if (N < 0 || H <= 0 || W <= 0 || G <= 0 || C <= 0) return DCN_ERR_SHAPE;
     dcn_status st = check_window(kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w);
     if (st != DCN_OK) return st;
@@ -174,8 +182,8 @@ dcn_status dcn_core_backward(const void *x, const float *offset, const float *ma
         !aligned(grad_mask, 4))
         return DCN_ERR_ALIGN;
     dcn::CoreBwdPlan plan;
-    dcn::plan_core_bwd(N, H, W, G, C, (int)Ho, (int)Wo, kh * kw, dtype, core_bwd_force_atomic(),
-                       plan);
+    dcn::plan_core_bwd(N, H, W, G, C, (int)Ho, (int)Wo, kh * kw, dtype,
+                       (path & DCN_BWD_ATOMIC) != 0, plan);
     if (grad_x && plan.total > 0) {
         if (!workspace || !aligned(workspace, 256) || workspace_bytes < plan.total)
             return DCN_ERR_WORKSPACE;
@@ -192,7 +200,20 @@ dcn_status dcn_core_backward(const void *x, const float *offset, const float *ma
     a.offset_scale = offset_scale;
     a.softmax = softmax;
     a.dtype = dtype;
+    a.path = path;
     return hip_status(dcn::launch_dcn_core_bwd(a, plan, stream));
+}
+
+dcn_status dcn_core_backward(const void *x, const float *offset, const float *mask,
+                             const void *grad_out, void *grad_x, float *grad_offset,
+                             float *grad_mask, void *workspace, size_t workspace_bytes, int N,
+                             int H, int W, int G, int C, int kh, int kw, int stride_h, int stride_w,
+                             int pad_h, int pad_w, int dil_h, int dil_w, float offset_scale,
+                             int softmax, dcn_dtype dtype, hipStream_t stream) {
+    return dcn_core_backward_path(x, offset, mask, grad_out, grad_x, grad_offset, grad_mask,
+                                  workspace, workspace_bytes, N, H, W, G, C, kh, kw, stride_h,
+                                  stride_w, pad_h, pad_w, dil_h, dil_w, offset_scale, softmax,
+                                  dtype, 0u, stream);
 }
 
 size_t dcn_v2_workspace_bytes(int N, int Cin, int H, int W, int Cout, int kh, int kw, int stride_h,
@@ -369,30 +390,34 @@ dcn_status deform_agg_forward(const void *feat, const int32_t *spatial_shape,
     return hip_status(dcn::launch_deform_agg(a, stream));
 }
 
-// DCN_AGG_BWD_ATOMIC=1 selects the fp32-atomic feature gradient of the aggregation
-// backward at any size (the path used past the bucket limits)
-static bool agg_bwd_force_atomic() {
-    const char *e = getenv("DCN_AGG_BWD_ATOMIC");
-    return e && e[0] == '1';
-}
-
-size_t deform_agg_backward_workspace_bytes(int B, int P_total, int A, int pts, int cams,
-                                           int scales, int G, int Cg, dcn_dtype dtype) {
+size_t deform_agg_backward_workspace_bytes_path(int B, int P_total, int A, int pts, int cams,
+                                                int scales, int G, int Cg, dcn_dtype dtype,
+                                                unsigned path) {
+    if (!valid_path(path)) return 0;
     if (!valid_dtype(dtype) || B < 0 || A < 0 || P_total <= 0 || pts <= 0 || cams <= 0 ||
         scales <= 0 || G <= 0 || Cg <= 0)
         return 0;
     dcn::AggBwdPlan plan;
-    dcn::plan_agg_bwd(B, P_total, A, pts, cams, scales, G, Cg, dtype, agg_bwd_force_atomic(), plan);
+    dcn::plan_agg_bwd(B, P_total, A, pts, cams, scales, G, Cg, dtype, (path & DCN_BWD_ATOMIC) != 0,
+                      plan);
     return plan.total;
 }
 
-dcn_status deform_agg_backward(const void *feat, const int32_t *spatial_shape,
-                               const int32_t *scale_start, const float *loc, const float *weights,
-                               const void *grad_out, void *grad_feat, float *grad_loc,
-                               float *grad_weights, void *workspace, size_t workspace_bytes, int B,
-                               int P_total, int A, int pts, int cams, int scales, int G, int Cg,
-                               int softmax, dcn_dtype dtype, hipStream_t stream) {
+size_t deform_agg_backward_workspace_bytes(int B, int P_total, int A, int pts, int cams,
+                                           int scales, int G, int Cg, dcn_dtype dtype) {
+    return deform_agg_backward_workspace_bytes_path(B, P_total, A, pts, cams, scales, G, Cg, dtype,
+                                                    0u);
+}
+
+dcn_status deform_agg_backward_path(const void *feat, const int32_t *spatial_shape,
+                                    const int32_t *scale_start, const float *loc,
+                                    const float *weights, const void *grad_out, void *grad_feat,
+                                    float *grad_loc, float *grad_weights, void *workspace,
+                                    size_t workspace_bytes, int B, int P_total, int A, int pts,
+                                    int cams, int scales, int G, int Cg, int softmax,
+                                    dcn_dtype dtype, unsigned path, hipStream_t stream) {
     if (!valid_dtype(dtype)) return DCN_ERR_DTYPE;
+    if (!valid_path(path)) return DCN_ERR_PARAM;
     if (B < 0 || A < 0 || P_total <= 0 || pts <= 0 || cams <= 0 || scales <= 0 || G <= 0 ||
         Cg <= 0)
         return DCN_ERR_SHAPE;
@@ -421,7 +446,8 @@ dcn_status deform_agg_backward(const void *feat, const int32_t *spatial_shape,
         !aligned(grad_weights, 4))
         return DCN_ERR_ALIGN;
     dcn::AggBwdPlan plan;
-    dcn::plan_agg_bwd(B, P_total, A, pts, cams, scales, G, Cg, dtype, agg_bwd_force_atomic(), plan);
+    dcn::plan_agg_bwd(B, P_total, A, pts, cams, scales, G, Cg, dtype, (path & DCN_BWD_ATOMIC) != 0,
+                      plan);
     const bool needs_ws =
         (grad_loc || (grad_feat && (plan.binned || dtype != DCN_F32))) && plan.total > 0;
     if (needs_ws && (!workspace || !aligned(workspace, 256) || workspace_bytes < plan.total))
@@ -433,7 +459,20 @@ dcn_status deform_agg_backward(const void *feat, const int32_t *spatial_shape,
     a.B = B; a.P_total = P_total; a.A = A; a.pts = pts; a.cams = cams; a.scales = scales;
     a.G = G; a.Cg = Cg; a.softmax = softmax;
     a.dtype = dtype;
+    a.path = path;
     return hip_status(dcn::launch_deform_agg_bwd(a, plan, stream));
+}
+
+dcn_status deform_agg_backward(const void *feat, const int32_t *spatial_shape,
+                               const int32_t *scale_start, const float *loc, const float *weights,
+                               const void *grad_out, void *grad_feat, float *grad_loc,
+                               float *grad_weights, void *workspace, size_t workspace_bytes, int B,
+                               int P_total, int A, int pts, int cams, int scales, int G, int Cg,
+                               int softmax, dcn_dtype dtype, hipStream_t stream) {
+    return deform_agg_backward_path(feat, spatial_shape, scale_start, loc, weights, grad_out,
+                                    grad_feat, grad_loc, grad_weights, workspace, workspace_bytes,
+                                    B, P_total, A, pts, cams, scales, G, Cg, softmax, dtype, 0u,
+                                    stream);
 }
 
 

@@ -1075,13 +1075,6 @@ __global__ __launch_bounds__(256 * NCH) void bwd_gather_staged_kernel(
         store_f32<E, V>(gx + ((size_t)(n * q.H + Y) * q.W + X) * GC + g * q.C + s * V, acc);
 }
 
-// DCN_CORE_BWD_UNSTAGED=1 keeps the gather that reads grad_out from memory per visit
-// (tests cover both)
-bool core_bwd_unstaged() {
-    const char *e = getenv("DCN_CORE_BWD_UNSTAGED");
-    return e && e[0] == '1';
-}
-
 template <class E>
 hipError_t launch_gather(int V, const CoreBwdLaunch &a, const GatherParams &q, const uint4 *rec,
                          const unsigned *starts, hipStream_t stream) {
@@ -1091,7 +1084,7 @@ hipError_t launch_gather(int V, const CoreBwdLaunch &a, const GatherParams &q, c
     B *gx = static_cast<B *>(a.grad_x);
     const int cbytes = a.C * elt;
     if ((cbytes == 16 || cbytes == 32) && (uintptr_t)go % 16 == 0 && (uintptr_t)gx % 16 == 0 &&
-        !core_bwd_unstaged()) {
+        !(a.path & DCN_BWD_UNSTAGED_GATHER)) {
         const int nch = cbytes / 16;
         const dim3 grid(q.nblocks), block(kTile * kTile * nch);
         if (nch == 2)
@@ -1111,20 +1104,6 @@ hipError_t launch_gather(int V, const CoreBwdLaunch &a, const GatherParams &q, c
         default: hipLaunchKernelGGL((bwd_gather_kernel<E, 1>), grid, block, 0, stream, rec, starts, go, gx, q); break;
     }
     return hipGetLastError();
-}
-
-// DCN_CORE_BWD_TILE_NO_RECORDS=1 leaves the grad_x records to the pair pass even when
-// the tiled gradient kernel could file them (tests cover both)
-bool core_bwd_tile_no_records() {
-    const char *e = getenv("DCN_CORE_BWD_TILE_NO_RECORDS");
-    return e && e[0] == '1';
-}
-
-// DCN_CORE_BWD_NO_TILE=1 keeps grad_offset / grad_mask in the pair pass (tests compare
-// both paths)
-bool core_bwd_no_tile() {
-    const char *e = getenv("DCN_CORE_BWD_NO_TILE");
-    return e && e[0] == '1';
 }
 
 template <class E>
@@ -1178,7 +1157,7 @@ hipError_t launch_e(const CoreBwdLaunch &a, const CoreBwdPlan &pl, hipStream_t s
     c.om_plain = true;
     c.off_grp = 2 * K; c.off_pix = a.G * 2 * K; c.mask_grp = K; c.mask_pix = a.G * K;
     CoreTilePlan tp;
-    const bool tile = (a.grad_offset || a.grad_mask) && (bin || !a.grad_x) && !core_bwd_no_tile() &&
+    const bool tile = (a.grad_offset || a.grad_mask) && (bin || !a.grad_x) && !(a.path & DCN_BWD_PAIR_PASS) &&
                       a.kh == 3 && a.kw == 3 && plan_core_tile(c, tp) && tp.S == 1;
     if (tile) {
         p.dots = 0;
@@ -1208,7 +1187,7 @@ hipError_t launch_e(const CoreBwdLaunch &a, const CoreBwdPlan &pl, hipStream_t s
         if (tile) {
             const CoreRecArgs ra = {rec, starts, fill, pl.TY, pl.TX};
             if ((err = launch_dcn_core_bwd_tile(c, tp, a.grad_offset, a.grad_mask,
-                                                core_bwd_tile_no_records() ? nullptr : &ra, &rec_done,
+                                                (a.path & DCN_BWD_PAIR_PASS_RECORDS) ? nullptr : &ra, &rec_done,
                                                 stream)) != hipSuccess)
                 return err;
         }

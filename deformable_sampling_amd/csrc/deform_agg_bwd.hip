@@ -879,13 +879,6 @@ __global__ __launch_bounds__(256) void agg_round_kernel(const float *__restrict_
         dst[i] = from_f32(E{}, src[i]);
 }
 
-// DCN_AGG_BWD_NOPIPE=1 keeps the general main kernel on the bucketed path (tests
-// compare both)
-bool agg_bwd_no_pipe() {
-    const char *e = getenv("DCN_AGG_BWD_NOPIPE");
-    return e && e[0] == '1';
-}
-
 int grid_for(long long n) {
     const long long b = (n + 255) / 256;
     return (int)(b < 1 ? 1 : (b > 16384 ? 16384 : b));
@@ -959,7 +952,7 @@ hipError_t launch_e(const AggBwdLaunch &a, const AggBwdPlan &pl, hipStream_t str
         constexpr int V16 = 16 / elt;
         const int nv16 = a.Cg % V16 == 0 ? a.Cg / V16 : 0;
         const int rounds = (a.pts * a.cams + p.npc - 1) / p.npc;
-        const bool pipe = !gacc && a.workspace && !agg_bwd_no_pipe() && rounds <= kRegRounds &&
+        const bool pipe = !gacc && a.workspace && !(a.path & DCN_BWD_GENERAL_MAIN) && rounds <= kRegRounds &&
                           nv16 >= 2 && nv16 <= 16 &&
                           (nv16 & (nv16 - 1)) == 0 && (uintptr_t)a.feat % 16 == 0 &&
                           (uintptr_t)a.grad_out % 16 == 0 &&

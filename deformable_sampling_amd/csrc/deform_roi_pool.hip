@@ -10,10 +10,16 @@
 //
 // Mapping: a bin's C channels are spread over L lanes of V channels (16-byte vectors
 // where alignment allows); a wavefront takes Z = 64/L bins. Every lane forms the
-// sample positions itself (a handful of fp32 operations per sample) and gathers the
-// four corner vectors of each sample; the average is stored once. Positions are
-// fp32: they differ from an fp64 evaluation by a few ulps of the coordinates, which
-// bounds the output difference by that shift times the corners' magnitudes.
+// sample positions itself and gathers the four corner vectors of each sample; the
+// average is stored once.
+//
+// Sample positions are a fixed sequence of fp32 operations, each rounded once to
+// nearest even and never fused with a neighbour (explicit mul_rn, correctly rounded
+// division, additions in the order written):
+//   x1s = fl(x1*s), w = fl(fl(x2 - x1)*s), bw = fl(w/k), dx = fl(fl(gamma*dx^)*w),
+//   tx = fl((2(j*S + sx) + 1) / (2S)), px = fl(fl(x1s + fl(tx*bw)) + dx),
+// and likewise for y; the corner/fraction split of px is exact. Two implementations
+// that follow this sequence sample at bit-identical positions.
 #include "dcn_common.hpp"
 #include "internal.hpp"
 
@@ -58,9 +64,10 @@ __global__ __launch_bounds__(kThreads) void roi_pool_kernel(const typename E::bi
         }
         return;
     }
-    const float x1 = mul_rn(ro[1], p.scale), y1 = mul_rn(ro[2], p.scale);
-    const float w = mul_rn(ro[3] - ro[1], p.scale), h = mul_rn(ro[4] - ro[2], p.scale);
-    const float bw = w / (float)p.k, bh = h / (float)p.k;
+    const float rx1 = ro[1], ry1 = ro[2], rx2 = ro[3], ry2 = ro[4];
+    const float x1 = mul_rn(rx1, p.scale), y1 = mul_rn(ry1, p.scale);
+    const float w = mul_rn(rx2 - rx1, p.scale), h = mul_rn(ry2 - ry1, p.scale);
+    const float bw = __fdiv_rn(w, (float)p.k), bh = __fdiv_rn(h, (float)p.k);
     float dx = 0.0f, dy = 0.0f;
     if (p.has_offset) {
         const float2 d = reinterpret_cast<const float2 *>(offset)[bin];
@@ -68,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void roi_pool_kernel(const typename E::bi
         dy = mul_rn(mul_rn(p.gamma, d.y), h);
     }
     const typename E::bits *img = x + (size_t)n * p.H * p.W * C;
-    const float invS = 1.0f / (float)p.S;
+    const float den = (float)(2 * p.S);
     const float inv_n = 1.0f / (float)(p.S * p.S);
     for (int ch = l; ch < p.nchunk; ch += p.L) {
         float acc[V];
@@ -76,11 +83,11 @@ __global__ __launch_bounds__(kThreads) void roi_pool_kernel(const typename E::bi
         for (int u = 0; u < V; ++u) acc[u] = 0.0f;
         const typename E::bits *imgc = img + ch * V;
         for (int sy = 0; sy < p.S; ++sy) {
-            const float ty = (float)i + ((float)sy + 0.5f) * invS;
-            const float yy = y1 + mul_rn(ty, bh) + dy;
+            const float ty = __fdiv_rn((float)(2 * (i * p.S + sy) + 1), den);
+            const float yy = (y1 + mul_rn(ty, bh)) + dy;
             for (int sx = 0; sx < p.S; ++sx) {
-                const float tx = (float)j + ((float)sx + 0.5f) * invS;
-                const float xx = x1 + mul_rn(tx, bw) + dx;
+                const float tx = __fdiv_rn((float)(2 * (j * p.S + sx) + 1), den);
+                const float xx = (x1 + mul_rn(tx, bw)) + dx;
                 int y0, x0;
                 float fy, fx;
                 split_coord(0, yy, y0, fy);

@@ -43,6 +43,7 @@ struct CoreBwdLaunch {
     float offset_scale;
     int softmax;
     dcn_dtype dtype;
+    unsigned path;  // DCN_BWD_* flags (0: the default kernels)
 };
 // Workspace plan of the backward. Binned (the default): bin counts, fill cursors,
 // bin starts and one 16-byte record per sample. Fallback (sizes beyond the record
@@ -179,6 +180,7 @@ struct AggBwdLaunch {
     int B, P_total, A, pts, cams, scales, G, Cg, softmax;
     dcn_dtype dtype;
     AggMaps maps;
+    unsigned path;  // DCN_BWD_* flags (0: the default kernels)
 };
 struct AggBwdPlan {
     bool binned;

@@ -13,6 +13,8 @@
  *   deform_agg_forward  Sparse4D-style multi-camera, multi-scale aggregation.
  *   deform_agg_backward gradients of the aggregation w.r.t. features, locations, weights.
  *   deform_roi_pool_forward  deformable RoI pooling, channels-last.
+ *   dcn_core_backward_path, deform_agg_backward_path  the two backward passes with an
+ *                       explicit choice among their alternative kernel paths.
  *
  * What is computed (page title, section):
  *  - Deformable sum y(p0) = sum_n w(p_n) x(p0 + p_n + dp_n), fractional positions
@@ -125,9 +127,9 @@ dcn_status dcn_core_forward_packed(const void *x, const void *offset_mask, void 
  * destination tile through the workspace, which holds per-bin counters and start
  * offsets (4 * N*G*(H/16+1)*(W/16+1) bins of 4 bytes, three arrays) and one
  * 16-byte record per sample (N*Ho*Wo*G*K records), each region 256-byte aligned.
- * Beyond N*Ho*Wo*G*K >= 2^31 or Ho*Wo >= 2^24 (or with the environment variable
- * DCN_CORE_BWD_ATOMIC=1) the backward instead accumulates grad_x with fp32 atomic
- * adds, and the workspace is an fp32 copy of x's shape for fp16/bf16 (0 for fp32).
+ * Beyond N*Ho*Wo*G*K >= 2^31 or Ho*Wo >= 2^24 the backward instead accumulates
+ * grad_x with fp32 atomic adds, and the workspace is an fp32 copy of x's shape for
+ * fp16/bf16 (0 for fp32).
  */
 size_t dcn_core_backward_workspace_bytes(int N, int H, int W, int G, int C, int kh, int kw,
                                          int stride_h, int stride_w, int pad_h, int pad_w,
@@ -294,9 +296,8 @@ const char *dcn_status_string(dcn_status s);
  * counts and fill cursors (2*B*P_total uint32), their
  * starts (B*P_total uint32), the scan's block sums (one uint32 per 4096 rows) and one
  * 8-byte entry per sample corner (B*A*T*4). Where
- * the entries would reach 2^31 (or with DCN_AGG_BWD_ATOMIC=1 in the environment) the
- * buckets are replaced by fp32 atomic adds, and fp16/bf16 then need an fp32 grad_feat
- * accumulator (B*P_total*G*Cg floats) instead.
+ * the entries would reach 2^31 the buckets are replaced by fp32 atomic adds, and
+ * fp16/bf16 then need an fp32 grad_feat accumulator (B*P_total*G*Cg floats) instead.
  */
 size_t deform_agg_backward_workspace_bytes(int B, int P_total, int A, int pts, int cams,
                                            int scales, int G, int Cg, dcn_dtype dtype);
@@ -355,14 +356,70 @@ dcn_status deform_agg_backward(const void *feat, const int32_t *spatial_shape,
  *   x = x1s + (j + (sx + 1/2)/S) * w/k + gamma*dx_ij*w,
  * pixel q at integer coordinate q, zero outside the image per corner (the page names
  * no sampling grid, coordinate convention or border rule; these are the readings).
- * Positions are formed in fp32. A RoI whose batch index is not in [0, N) pools to
- * zeros. Limits: 1 <= sampling_ratio <= 64; (H+1)*(W+1)*C < 2^31; R*k*k*C < 2^31.
+ * Positions are this fixed sequence of fp32 operations, each rounded once to nearest
+ * even and none fused with another: x1s = fl(x1*s), w = fl(fl(x2 - x1)*s),
+ * bw = fl(w/k), dx = fl(fl(gamma*dx^)*w), tx = fl((2(j*S + sx) + 1) / (2S)),
+ * x = fl(fl(x1s + fl(tx*bw)) + dx), y likewise. A RoI whose batch index is not in
+ * [0, N) pools to zeros. Limits: 1 <= sampling_ratio <= 64; (H+1)*(W+1)*C < 2^31; R*k*k*C < 2^31.
  * offset must be 8-byte aligned; x and out aligned to their element size.
  */
 dcn_status deform_roi_pool_forward(const void *x, const float *rois, const float *offset, void *out,
                                    int N, int H, int W, int C, int R, int k, int sampling_ratio,
                                    float spatial_scale, float gamma, dcn_dtype dtype,
                                    hipStream_t stream);
+
+/*
+ * Alternative kernel paths of the two backward passes. dcn_core_backward and
+ * deform_agg_backward pick their kernels from the sizes alone; the *_path entry
+ * points below take that choice as an argument, so that every path can be run and
+ * checked at any size (each computes the same gradients, within fp32 accumulation
+ * error). Flags may be combined; a flag that does not apply to an entry point is
+ * ignored by it. Nothing else selects these paths: the library reads no environment
+ * variable and keeps no setting between calls.
+ *   DCN_BWD_ATOMIC            grad_x (core) / grad_feat (aggregation) by fp32 atomic
+ *                             adds, the path taken past the sorting limits; the
+ *                             workspace size changes with it (use the matching
+ *                             *_workspace_bytes_path call)
+ *   DCN_BWD_PAIR_PASS         core: grad_offset / grad_mask from the per-pair pass with
+ *                             direct corner loads instead of the LDS halo tiles
+ *   DCN_BWD_PAIR_PASS_RECORDS core: the grad_x records filed by the per-pair pass even
+ *                             where the tiled gradient kernel could file them
+ *   DCN_BWD_UNSTAGED_GATHER   core: the grad_x gather reads each record's grad_out
+ *                             slice from memory instead of through LDS
+ *   DCN_BWD_GENERAL_MAIN      aggregation: the general per-sample kernel instead of
+ *                             the pipelined one
+ * An unknown flag bit gives DCN_ERR_PARAM (the workspace-size calls return 0).
+ */
+typedef enum {
+    DCN_BWD_DEFAULT = 0,
+    DCN_BWD_ATOMIC = 1,
+    DCN_BWD_PAIR_PASS = 2,
+    DCN_BWD_PAIR_PASS_RECORDS = 4,
+    DCN_BWD_UNSTAGED_GATHER = 8,
+    DCN_BWD_GENERAL_MAIN = 16
+} dcn_bwd_path;
+
+size_t dcn_core_backward_workspace_bytes_path(int N, int H, int W, int G, int C, int kh, int kw,
+                                              int stride_h, int stride_w, int pad_h, int pad_w,
+                                              int dil_h, int dil_w, dcn_dtype dtype,
+                                              unsigned path);
+dcn_status dcn_core_backward_path(const void *x, const float *offset, const float *mask,
+                                  const void *grad_out, void *grad_x, float *grad_offset,
+                                  float *grad_mask, void *workspace, size_t workspace_bytes,
+                                  int N, int H, int W, int G, int C, int kh, int kw,
+                                  int stride_h, int stride_w, int pad_h, int pad_w,
+                                  int dil_h, int dil_w, float offset_scale, int softmax,
+                                  dcn_dtype dtype, unsigned path, hipStream_t stream);
+size_t deform_agg_backward_workspace_bytes_path(int B, int P_total, int A, int pts, int cams,
+                                                int scales, int G, int Cg, dcn_dtype dtype,
+                                                unsigned path);
+dcn_status deform_agg_backward_path(const void *feat, const int32_t *spatial_shape,
+                                    const int32_t *scale_start, const float *loc,
+                                    const float *weights, const void *grad_out, void *grad_feat,
+                                    float *grad_loc, float *grad_weights, void *workspace,
+                                    size_t workspace_bytes, int B, int P_total, int A, int pts,
+                                    int cams, int scales, int G, int Cg, int softmax,
+                                    dcn_dtype dtype, unsigned path, hipStream_t stream);
 
 /* hipError_t of this thread's last DCN_ERR_HIP (0 if none). */
 int dcn_last_hip_error(void);

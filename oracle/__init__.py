@@ -87,7 +87,7 @@ def _load():
         lib.oracle_deform_agg_backward.argtypes = [_dp, _i32p, _i32p, _dp, _dp, _dp] + [_dp] * 6 + [
             _i64] * 8 + [ctypes.c_int]
         lib.oracle_deform_roi_pool.restype = ctypes.c_int
-        lib.oracle_deform_roi_pool.argtypes = [_dp] * 6 + [_i64] * 7 + [ctypes.c_double] * 2
+        lib.oracle_deform_roi_pool.argtypes = [_dp] * 5 + [_i64] * 7 + [ctypes.c_double] * 2
         _lib = lib
     return _lib
 
@@ -322,20 +322,18 @@ def deform_agg_backward(feat, spatial_shape, scale_start, loc, weights, grad_out
                 grad_loc_abs=gla, grad_weights_abs=gwa)
 
 
-def deform_roi_pool(x, rois, offset, *, k, S, spatial_scale=1.0, gamma=0.1, corner_sum=False):
+def deform_roi_pool(x, rois, offset, *, k, S, spatial_scale=1.0, gamma=0.1):
     """Deformable RoI pooling. x [N,H,W,C] channels-last, rois [R,5] (batch, x1, y1, x2,
-    y2), offset [R,k,k,2] (dx, dy) or None. Returns (out, absum), each [R,k,k,C], plus
-    the mean per-sample sum of |corners| when corner_sum."""
+    y2), offset [R,k,k,2] (dx, dy) or None. Sample positions follow the fixed fp32
+    operation sequence stated in oracle.c. Returns (out, absum), each [R,k,k,C]."""
     x, rois, offset = _f64(x), _f64(rois), _f64(offset)
     N, H, W, C = x.shape
     R = rois.shape[0]
     out = np.zeros((R, k, k, C))
     ab = np.zeros((R, k, k, C))
-    cs = np.zeros((R, k, k, C))
     rc = _load().oracle_deform_roi_pool(_ptr(x), _ptr(rois), _ptr(offset), _ptr(out), _ptr(ab),
-                                        _ptr(cs), N, H, W, C, R, k, S, float(spatial_scale),
-                                        float(gamma))
+                                        N, H, W, C, R, k, S, float(spatial_scale), float(gamma))
     if rc:
         raise ValueError("oracle_deform_roi_pool rejected its arguments (%d)" % rc)
-    return (out, ab, cs) if corner_sum else (out, ab)
+    return out, ab
 

@@ -760,57 +760,65 @@ int oracle_deform_agg_backward(const double *feat, const int32_t *spatial_shape,
 /* in pixel-index coordinates (pixel q at integer q), each read through the */
 /* bilinear kernel with zero outside the image per corner; offsets are      */
 /* [R, k, k, 2] (dx, dy) pairs, x first. x is channels-last [N, H, W, C],   */
-/* out [R, k, k, C]. All arithmetic in fp64 (the GPU forms the same terms   */
-/* in fp32). offset may be NULL (plain RoIAlign-style average pooling).     */
+/* out [R, k, k, C]. offset may be NULL (plain RoIAlign-style average       */
+/* pooling).                                                                */
+/*                                                                          */
+/* The sample position is a fixed sequence of fp32 operations, each rounded */
+/* once to nearest even (rois, offsets, spatial_scale and gamma are fp32    */
+/* quantities; products are never fused with a following addition):        */
+/*   x1s = fl(x1*s)            w  = fl(fl(x2 - x1)*s)     bw = fl(w/k)      */
+/*   dx  = fl(fl(gamma*dx^)*w)                                              */
+/*   tx  = fl((2(j*S + sx) + 1) / (2S))   (the sample's place in bin units) */
+/*   px  = fl(fl(x1s + fl(tx*bw)) + dx)                                     */
+/* and likewise for y. Everything after the position (the corner split and  */
+/* the weighted sum) is exact fp64. Each fl() is evaluated as one fp64      */
+/* operation on fp32 operands followed by a conversion to float: for +, -,  */
+/* * and / the double rounding this implies equals a single fp32 rounding,  */
+/* since 53 >= 2*24 + 2.                                                    */
 /* ---------------------------------------------------------------------- */
+static double fl32(double v) { return (double)(float)v; }
+
 int oracle_deform_roi_pool(const double *x, const double *rois, const double *offset,
-                           double *out, double *absum, double *csum, int64_t N, int64_t H,
-                           int64_t W, int64_t C, int64_t R, int64_t k, int64_t S,
-                           double spatial_scale, double gamma)
+                           double *out, double *absum, int64_t N, int64_t H, int64_t W,
+                           int64_t C, int64_t R, int64_t k, int64_t S, double spatial_scale,
+                           double gamma)
 {
     if (k <= 0 || S <= 0) return 1;
+    const double s = fl32(spatial_scale), gm = fl32(gamma);
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t r = 0; r < R; ++r) {
         const double *ro = rois + r * 5;
         int64_t n = (int64_t)ro[0];
         if (n < 0 || n >= N) { bad = 1; continue; }
-        double x1 = ro[1] * spatial_scale, y1 = ro[2] * spatial_scale;
-        double w = (ro[3] - ro[1]) * spatial_scale, h = (ro[4] - ro[2]) * spatial_scale;
-        double bw = w / (double)k, bh = h / (double)k;
+        const double rx1 = fl32(ro[1]), ry1 = fl32(ro[2]), rx2 = fl32(ro[3]), ry2 = fl32(ro[4]);
+        double x1 = fl32(rx1 * s), y1 = fl32(ry1 * s);
+        double w = fl32(fl32(rx2 - rx1) * s), h = fl32(fl32(ry2 - ry1) * s);
+        double bw = fl32(w / (double)k), bh = fl32(h / (double)k);
         const double *X = x + n * H * W * C;
         for (int64_t i = 0; i < k; ++i)
         for (int64_t j = 0; j < k; ++j) {
             double dx = 0.0, dy = 0.0;
             if (offset) {
-                dx = gamma * offset[((r * k + i) * k + j) * 2 + 0] * w;
-                dy = gamma * offset[((r * k + i) * k + j) * 2 + 1] * h;
+                dx = fl32(fl32(gm * fl32(offset[((r * k + i) * k + j) * 2 + 0])) * w);
+                dy = fl32(fl32(gm * fl32(offset[((r * k + i) * k + j) * 2 + 1])) * h);
             }
             double *o = out + ((r * k + i) * k + j) * C;
             double *oa = absum ? absum + ((r * k + i) * k + j) * C : NULL;
-            double *oc = csum ? csum + ((r * k + i) * k + j) * C : NULL;
             for (int64_t c = 0; c < C; ++c) {
-                double sum = 0.0, sa = 0.0, sc = 0.0;
+                double sum = 0.0, sa = 0.0;
                 for (int64_t sy = 0; sy < S; ++sy)
                 for (int64_t sx = 0; sx < S; ++sx) {
-                    double yy = y1 + ((double)i + ((double)sy + 0.5) / (double)S) * bh + dy;
-                    double xx = x1 + ((double)j + ((double)sx + 0.5) / (double)S) * bw + dx;
+                    double ty = fl32((double)(2 * (i * S + sy) + 1) / (double)(2 * S));
+                    double tx = fl32((double)(2 * (j * S + sx) + 1) / (double)(2 * S));
+                    double yy = fl32(fl32(y1 + fl32(ty * bh)) + dy);
+                    double xx = fl32(fl32(x1 + fl32(tx * bw)) + dx);
                     double ab = 0.0;
                     sum += oracle_bilinear(X + c, H, W, C, yy, xx, &ab);
                     sa += ab;
-                    /* sum of |corner| inside the image: the bound on how much a shift of
-                       the position by delta can change the sample (delta per corner) */
-                    double y0 = floor(yy), x0 = floor(xx);
-                    for (int a = 0; a < 2; ++a)
-                        for (int b = 0; b < 2; ++b) {
-                            double qy = y0 + a, qx = x0 + b;
-                            if (qy < 0.0 || qy >= (double)H || qx < 0.0 || qx >= (double)W) continue;
-                            sc += fabs(X[((int64_t)qy * W + (int64_t)qx) * C + c]);
-                        }
                 }
                 o[c] = sum / (double)(S * S);
                 if (oa) oa[c] = sa / (double)(S * S);
-                if (oc) oc[c] = sc / (double)(S * S);
             }
         }
     }

@@ -108,11 +108,20 @@ def test_core_backward_workspace_bytes(lib):
     assert bwd_ws(lib, 1, 2, 2, 1, 3, kh=5, kw=5, p=0) == 0   # Ho <= 0
 
 
-def test_core_backward_workspace_bytes_atomic_fallback(lib, monkeypatch):
-    monkeypatch.setenv("DCN_CORE_BWD_ATOMIC", "1")
-    assert bwd_ws(lib, 16, 80, 80, 16, 16) == 16 * 80 * 80 * 256 * 4
-    assert bwd_ws(lib, 1, 3, 5, 1, 3, dtype=2) == 256          # 45 floats -> 256 B
-    assert bwd_ws(lib, 1, 3, 5, 1, 3, dtype=0) == 0            # fp32: in place
+def bwd_ws_path(lib, N, H, W, G, C, path, dtype=1):
+    return lib.dcn_core_backward_workspace_bytes_path(N, H, W, G, C, 3, 3, 1, 1, 1, 1, 1, 1,
+                                                      dtype, path)
+
+
+def test_core_backward_workspace_bytes_atomic_fallback(lib):
+    assert bwd_ws_path(lib, 16, 80, 80, 16, 16, 1) == 16 * 80 * 80 * 256 * 4
+    assert bwd_ws_path(lib, 1, 3, 5, 1, 3, 1, dtype=2) == 256   # 45 floats -> 256 B
+    assert bwd_ws_path(lib, 1, 3, 5, 1, 3, 1, dtype=0) == 0     # fp32: in place
+    # the flags that keep the sorted path leave its size unchanged; unknown bits give 0
+    for path in (0, 2, 4, 8, 16, 2 | 4 | 8):
+        assert bwd_ws_path(lib, 16, 80, 80, 16, 16, path) == bwd_ws(lib, 16, 80, 80, 16, 16)
+    assert bwd_ws_path(lib, 16, 80, 80, 16, 16, 32) == 0
+    assert bwd_ws_path(lib, 16, 80, 80, 16, 16, 1 << 31) == 0
 
 
 def test_core_backward_validation(lib):
@@ -330,12 +339,33 @@ def test_v2_backward_validation(lib):
     assert lib.dcn_last_hip_error() == 0
 
 
-def test_agg_backward_workspace_atomic_fallback(lib, monkeypatch):
-    monkeypatch.setenv("DCN_AGG_BWD_ATOMIC", "1")
-    n = lib.deform_agg_backward_workspace_bytes(1, 89760, 900, 13, 6, 4, 8, 32, 0)
+def test_agg_backward_workspace_atomic_fallback(lib):
+    n = lib.deform_agg_backward_workspace_bytes_path(1, 89760, 900, 13, 6, 4, 8, 32, 0, 1)
     a256 = lambda v: (v + 255) // 256 * 256
     T = 13 * 6 * 4
     assert n == (a256(8 * 900 * 13 * 6 * 2 * 4)                     # fp32: loc partials,
                  + a256(900 * T * 8 * 4) + a256(3 * 8 * 900 * 4))    # g_t and unit sums only
-    n16 = lib.deform_agg_backward_workspace_bytes(1, 89760, 900, 13, 6, 4, 8, 32, 1)
+    n16 = lib.deform_agg_backward_workspace_bytes_path(1, 89760, 900, 13, 6, 4, 8, 32, 1, 1)
     assert n16 == n + 89760 * 256 * 4                                # + fp32 feature accumulator
+    dflt = lib.deform_agg_backward_workspace_bytes(1, 89760, 900, 13, 6, 4, 8, 32, 0)
+    assert lib.deform_agg_backward_workspace_bytes_path(1, 89760, 900, 13, 6, 4, 8, 32, 0, 16) == dflt
+    assert lib.deform_agg_backward_workspace_bytes_path(1, 89760, 900, 13, 6, 4, 8, 32, 0, 64) == 0
+
+
+def test_backward_path_variants_validate_their_flags(lib):
+    """The *_path entry points reject unknown flag bits before any HIP call and otherwise
+    validate exactly as the default entry points (a rejected size is rejected by both)."""
+    args = (A, A, A, A, A, A, A, A, 1 << 40, 1, 8, 8, 2, 4, 3, 3, 1, 1, 1, 1, 1, 1, 1.0, 0, 1)
+    assert lib.dcn_core_backward_path(*args, 32, None) == PARAM
+    assert lib.dcn_core_backward_path(*args, 1 << 31, None) == PARAM
+    bad = (A, A, A, A, A, A, A, A, 1 << 40, 1, 8, 8, 2, 4, 3, 3, 0, 1, 1, 1, 1, 1, 1.0, 0, 1)
+    assert lib.dcn_core_backward_path(*bad, 1, None) == PARAM      # stride 0
+    assert lib.dcn_core_backward_path(*args[:-1], 7, 2, None) == DTYPE
+    ss = (ctypes.c_int32 * 8)(5, 5, 2, 3, 5, 5, 2, 3)
+    st = (ctypes.c_int32 * 4)(0, 25, 31, 56)
+    aargs = (A, ss, st, A, A, A, A, A, A, A, 1 << 40, 1, 100, 4, 2, 2, 2, 2, 8, 0, 0)
+    assert lib.deform_agg_backward_path(*aargs, 64, None) == PARAM
+    st_bad = (ctypes.c_int32 * 4)(0, 25, 31, 99)                  # map past P_total
+    aargs_bad = (A, ss, st_bad) + aargs[3:]
+    assert lib.deform_agg_backward_path(*aargs_bad, 1, None) == SHAPE
+    assert lib.dcn_last_hip_error() == 0

@@ -25,11 +25,12 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def run(c, go, softmax=None, need=("feat", "loc", "weights"), workspace=None):
+def run(c, go, softmax=None, need=("feat", "loc", "weights"), workspace=None,
+        path=dsa.DCN_BWD_DEFAULT):
     sm = c["softmax"] if softmax is None else softmax
     r = dsa.deform_agg_backward(dev(c["feat"]), c["spatial_shape"], c["scale_start"],
                                 dev(c["loc"]), dev(c["weights"]), dev(go), softmax=sm, need=need,
-                                workspace=workspace)
+                                workspace=workspace, path=path)
     torch.cuda.synchronize()
     return r
 
@@ -132,15 +133,14 @@ GENERAL = [
 
 
 @pytest.mark.parametrize("name,args", GENERAL, ids=[s[0] for s in GENERAL])
-def test_agg_backward_general_main_kernel(gpu, monkeypatch, name, args):
+def test_agg_backward_general_main_kernel(gpu, name, args):
     """The general main kernel on the bucketed path (channel vectors of 4 elements, no
     load pipelining), which 16-byte-vector groups otherwise leave to the pipelined
-    kernel; selected through DCN_AGG_BWD_NOPIPE=1."""
-    monkeypatch.setenv("DCN_AGG_BWD_NOPIPE", "1")
+    kernel; selected through deform_agg_backward_path(DCN_BWD_GENERAL_MAIN)."""
     c = wl.agg_case(seed=900 + len(name), **args)
     go = wl.agg_grad_out(c, seed=len(name))
     _say("agg backward general main kernel", name)
-    r = run(c, go)
+    r = run(c, go, path=dsa.DCN_BWD_GENERAL_MAIN)
     o = ref(c, go)
     _say(name, check_all(r, o, c["dtype"], name))
 
@@ -168,14 +168,13 @@ FALLBACK = [
 
 
 @pytest.mark.parametrize("name,args", FALLBACK, ids=[s[0] for s in FALLBACK])
-def test_agg_backward_atomic_fallback(gpu, monkeypatch, name, args):
+def test_agg_backward_atomic_fallback(gpu, name, args):
     """The fp32-atomic feature gradient (used past the bucket limits), selected here at
-    small sizes through DCN_AGG_BWD_ATOMIC=1."""
-    monkeypatch.setenv("DCN_AGG_BWD_ATOMIC", "1")
+    small sizes through deform_agg_backward_path(DCN_BWD_ATOMIC)."""
     c = wl.agg_case(seed=700 + len(name), **args)
     go = wl.agg_grad_out(c, seed=len(name))
     _say("agg backward atomic fallback", name)
-    r = run(c, go)
+    r = run(c, go, path=dsa.DCN_BWD_ATOMIC)
     o = ref(c, go)
     _say(name, check_all(r, o, c["dtype"], name))
 

@@ -28,12 +28,14 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def run_bwd(c, go, offset_scale=1.0, softmax=None, mask="keep", need=("x", "offset", "mask")):
+def run_bwd(c, go, offset_scale=1.0, softmax=None, mask="keep", need=("x", "offset", "mask"),
+            path=dsa.DCN_BWD_DEFAULT):
     sm = c["softmax"] if softmax is None else softmax
     m = c["mask"] if mask == "keep" else mask
     r = dsa.dcn_core_backward(dev(c["x"]), dev(c["offset"]), dev(m), dev(go),
                               kernel=(c["kh"], c["kw"]), stride=c["stride"], pad=c["pad"],
-                              dilation=c["dil"], offset_scale=offset_scale, softmax=sm, need=need)
+                              dilation=c["dil"], offset_scale=offset_scale, softmax=sm, need=need,
+                              path=path)
     torch.cuda.synchronize()
     return r
 
@@ -209,14 +211,13 @@ FALLBACK_CASES = [s for s in BWD_SWEEP if s[0] in (
 
 
 @pytest.mark.parametrize("name,args,extra", FALLBACK_CASES, ids=[s[0] for s in FALLBACK_CASES])
-def test_backward_atomic_fallback(gpu, monkeypatch, name, args, extra):
+def test_backward_atomic_fallback(gpu, name, args, extra):
     """The fp32-atomic fallback (used beyond the record packing's limits), selected
-    here at small sizes through DCN_CORE_BWD_ATOMIC=1."""
-    monkeypatch.setenv("DCN_CORE_BWD_ATOMIC", "1")
+    here at small sizes through dcn_core_backward_path(DCN_BWD_ATOMIC)."""
     c = wl.core_case(seed=300 + len(name), **args)
     go = wl.core_grad_out(c, seed=len(name))
     _say("core backward atomic fallback", name)
-    r = run_bwd(c, go, **extra)
+    r = run_bwd(c, go, path=dsa.DCN_BWD_ATOMIC, **extra)
     o = oracle_bwd(c, go, **extra)
     _say(name, check_all(r, o, c["dtype"], name))
 
@@ -225,42 +226,41 @@ PAIR_GRADS = ["f32_vec4_tails", "f16_vec8", "f32_far_offsets", "f32_softmax", "f
 
 
 @pytest.mark.parametrize("name", PAIR_GRADS)
-def test_backward_pair_pass_gradients(gpu, monkeypatch, name):
-    """grad_offset / grad_mask from the pair pass (DCN_CORE_BWD_NO_TILE=1) on shapes whose
+def test_backward_pair_pass_gradients(gpu, name):
+    """grad_offset / grad_mask from the pair pass (DCN_BWD_PAIR_PASS) on shapes whose
     default path computes them in the LDS-tiled kernel: both paths meet the bound."""
     args, extra = {n: (a, e) for n, a, e in BWD_SWEEP}[name]
-    monkeypatch.setenv("DCN_CORE_BWD_NO_TILE", "1")
     c = wl.core_case(seed=100 + len(name), **args)
     go = wl.core_grad_out(c, seed=len(name))
     _say("core backward pair-pass gradients", name)
-    r = run_bwd(c, go, **extra)
+    r = run_bwd(c, go, path=dsa.DCN_BWD_PAIR_PASS, **extra)
     o = oracle_bwd(c, go, **extra)
     _say(name, check_all(r, o, c["dtype"], name))
 
 
 @pytest.mark.parametrize("name", ["f32_vec4_tails", "f16_vec8", "f16_many_groups", "f32_far_offsets"])
-def test_backward_unstaged_gather(gpu, monkeypatch, name):
-    """grad_x through the gather that reads grad_out per visit (DCN_CORE_BWD_UNSTAGED=1) on
-    shapes whose default gather stages each record's grad_out slice in LDS."""
+def test_backward_unstaged_gather(gpu, name):
+    """grad_x through the gather that reads grad_out per visit (DCN_BWD_UNSTAGED_GATHER)
+    on shapes whose default gather stages each record's grad_out slice in LDS."""
     args, extra = {n: (a, e) for n, a, e in BWD_SWEEP}[name]
-    monkeypatch.setenv("DCN_CORE_BWD_UNSTAGED", "1")
     c = wl.core_case(seed=100 + len(name), **args)
     go = wl.core_grad_out(c, seed=len(name))
-    r = run_bwd(c, go, **extra)
+    _say("core backward unstaged gather", name)
+    r = run_bwd(c, go, path=dsa.DCN_BWD_UNSTAGED_GATHER, **extra)
     o = oracle_bwd(c, go, **extra)
     _say(name, check_all(r, o, c["dtype"], name))
 
 
 @pytest.mark.parametrize("name", ["f32_vec4_tails", "f16_vec8", "f32_far_offsets", "f32_softmax"])
-def test_backward_pair_pass_records(gpu, monkeypatch, name):
-    """grad_x records filed by the pair pass (DCN_CORE_BWD_TILE_NO_RECORDS=1) while the
-    tiled kernel computes grad_offset / grad_mask: the default files them in the tiled
-    kernel on these shapes."""
+def test_backward_pair_pass_records(gpu, name):
+    """grad_x records filed by the pair pass (DCN_BWD_PAIR_PASS_RECORDS) while the tiled
+    kernel computes grad_offset / grad_mask: the default files them in the tiled kernel
+    on these shapes."""
     args, extra = {n: (a, e) for n, a, e in BWD_SWEEP}[name]
-    monkeypatch.setenv("DCN_CORE_BWD_TILE_NO_RECORDS", "1")
     c = wl.core_case(seed=100 + len(name), **args)
     go = wl.core_grad_out(c, seed=len(name))
-    r = run_bwd(c, go, **extra)
+    _say("core backward pair-pass records", name)
+    r = run_bwd(c, go, path=dsa.DCN_BWD_PAIR_PASS_RECORDS, **extra)
     o = oracle_bwd(c, go, **extra)
     _say(name, check_all(r, o, c["dtype"], name))
 

@@ -31,6 +31,8 @@ MUTANTS = [
     ("v2_mask_ignores_group", "mask[(n * dg * K + g * K + k) * HWo + r]", "mask[(n * dg * K + k) * HWo + r]", 1),
     ("v2_weight_transposed", "s += wr[rr] * col[rr];", "s += weight[(rr % Cout) * R + rr / Cout] * col[rr];", 1),
     ("v2_point_order_col_major", "int64_t k = i * kw + j;", "int64_t k = j * kh + i;", 3),
+    ("v2_softmax_null_mask_unit", "for (int64_t k = 0; k < K; ++k) m[k] = 1.0 / (double)K;",
+     "for (int64_t k = 0; k < K; ++k) m[k] = 1.0;", 1),
     ("agg_no_half_pixel", "(double)(float)(uv[0] * (double)Ws) - 0.5", "(double)(float)(uv[0] * (double)Ws)", 1),
     ("agg_uv_swapped", "double yy = (double)(float)(uv[1] * (double)Hs) - 0.5;",
      "double yy = (double)(float)(uv[0] * (double)Hs) - 0.5;", 1),
@@ -102,25 +104,30 @@ V2_BWD_MUTANTS = [
      "double u = gc[p * R + k * Cin + ci], ua = gca[p * R + k * Cin + ci];", 1),
     ("v2bwd_softmax_no_centering", "double v = softmax ? m[k] * (gm[k] - dot) : gm[k];",
      "double v = softmax ? m[k] * gm[k] : gm[k];", 2),
+    ("v2bwd_softmax_null_mask_unit", "for (int64_t k = 0; k < K; ++k) m[k] = 1.0 / (double)K;",
+     "for (int64_t k = 0; k < K; ++k) m[k] = 1.0;", 2),
     ("v2bwd_dy_sign", "double dwy[2][2] = {{-(1.0 - fx), -fx}, {1.0 - fx, fx}};",
      "double dwy[2][2] = {{(1.0 - fx), fx}, {-(1.0 - fx), -fx}};", 2),
 ]
 
 # Mistakes in deformable RoI pooling (oracle_deform_roi_pool), caught by its pins.
 ROI_MUTANTS = [
-    ("roi_swap_dx_dy", "dx = gamma * offset[((r * k + i) * k + j) * 2 + 0] * w;",
-     "dx = gamma * offset[((r * k + i) * k + j) * 2 + 1] * w;", 1),
-    ("roi_offset_scaled_by_h", "dx = gamma * offset[((r * k + i) * k + j) * 2 + 0] * w;",
-     "dx = gamma * offset[((r * k + i) * k + j) * 2 + 0] * h;", 1),
-    ("roi_no_gamma", "dy = gamma * offset[((r * k + i) * k + j) * 2 + 1] * h;",
-     "dy = offset[((r * k + i) * k + j) * 2 + 1] * h;", 1),
-    ("roi_no_half_sample", "((double)sx + 0.5) / (double)S) * bw + dx;", "((double)sx) / (double)S) * bw + dx;", 1),
-    ("roi_bins_transposed", "double bw = w / (double)k, bh = h / (double)k;",
-     "double bw = h / (double)k, bh = w / (double)k;", 1),
+    ("roi_swap_dx_dy", "* 2 + 0])) * w);", "* 2 + 1])) * w);", 1),
+    ("roi_offset_scaled_by_h", "* 2 + 0])) * w);", "* 2 + 0])) * h);", 1),
+    ("roi_no_gamma", "dy = fl32(fl32(gm * fl32(offset[", "dy = fl32(fl32(fl32(offset[", 1),
+    ("roi_no_half_sample", "double tx = fl32((double)(2 * (j * S + sx) + 1) / (double)(2 * S));",
+     "double tx = fl32((double)(2 * (j * S + sx)) / (double)(2 * S));", 1),
+    ("roi_bins_transposed", "double bw = fl32(w / (double)k), bh = fl32(h / (double)k);",
+     "double bw = fl32(h / (double)k), bh = fl32(w / (double)k);", 1),
     ("roi_mean_over_S", "o[c] = sum / (double)(S * S);", "o[c] = sum / (double)S;", 1),
     ("roi_ignores_batch", "const double *X = x + n * H * W * C;", "const double *X = x;", 1),
-    ("roi_scale_x1_only", "double x1 = ro[1] * spatial_scale, y1 = ro[2] * spatial_scale;",
-     "double x1 = ro[1], y1 = ro[2] * spatial_scale;", 1),
+    ("roi_scale_x1_only", "double x1 = fl32(rx1 * s), y1 = fl32(ry1 * s);",
+     "double x1 = rx1, y1 = fl32(ry1 * s);", 1),
+    # the fp32 position sequence itself
+    ("roi_bin_width_unrounded", "double bw = fl32(w / (double)k)", "double bw = w / (double)k", 1),
+    ("roi_position_single_rounding", "double xx = fl32(fl32(x1 + fl32(tx * bw)) + dx);",
+     "double xx = fl32(x1 + tx * bw + dx);", 1),
+    ("roi_extent_unrounded", "h = fl32(fl32(ry2 - ry1) * s);", "h = fl32((ry2 - ry1) * s);", 1),
 ]
 
 

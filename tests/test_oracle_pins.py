@@ -406,6 +406,30 @@ def test_v2_mask_none_and_softmax():
     np.testing.assert_allclose(o_sm, o_ref, rtol=0, atol=1e-12)
 
 
+def test_v2_softmax_without_mask_is_uniform_modulation():
+    """softmax over the K points with no mask tensor: the implied logits are all equal,
+    so every point gets 1/K. That is the unmasked result divided by K (the sum is
+    linear in the modulation), and the same as passing any constant logits; with zero
+    offsets it is conv2d / K."""
+    c = wl.v2_case(N=2, Cin=4, H=6, W=7, Cout=3, dg=2, dtype="f32", seed=37, mask="logits")
+    K = 9
+    o_sm, _ = oracle.dcn_v2(c["x"], c["offset"], None, c["weight"], pad=(1, 1), softmax=True)
+    o_plain, _ = oracle.dcn_v2(c["x"], c["offset"], None, c["weight"], pad=(1, 1))
+    np.testing.assert_allclose(o_sm, o_plain / K, rtol=0, atol=1e-13)
+    for v in (0.0, 3.7):
+        o_c, _ = oracle.dcn_v2(c["x"], c["offset"], torch.full_like(c["mask"], v), c["weight"],
+                               pad=(1, 1), softmax=True)
+        np.testing.assert_allclose(o_sm, o_c, rtol=0, atol=1e-13)
+    off0 = torch.zeros_like(c["offset"])
+    o0, _ = oracle.dcn_v2(c["x"], off0, None, c["weight"], pad=(1, 1), softmax=True)
+    ref = F.conv2d(c["x"].double(), c["weight"].double(), padding=1) / K
+    np.testing.assert_allclose(o0, ref.numpy(), rtol=0, atol=1e-13)
+    # the column stage alone
+    col_sm = oracle.dcn_v2_columns(c["x"], c["offset"], None, kh=3, kw=3, pad=(1, 1), softmax=True)
+    col_1 = oracle.dcn_v2_columns(c["x"], c["offset"], None, kh=3, kw=3, pad=(1, 1))
+    np.testing.assert_allclose(col_sm, col_1 / K, rtol=0, atol=1e-14)
+
+
 # ------------------------------------------------------------- aggregation --
 
 def _grid_sample_maps(case, b, cam, s, u, v):

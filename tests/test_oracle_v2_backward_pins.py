@@ -191,3 +191,23 @@ def test_softmax_logit_gradients_sum_to_zero_and_linearity():
     g2 = _bwd(x, off, m, w, -2.5 * go, st, pd, dl, True)
     for k in ("grad_x", "grad_offset", "grad_mask", "grad_weight"):
         np.testing.assert_allclose(g2[k], -2.5 * g[k], rtol=0, atol=1e-11)
+
+
+def test_softmax_without_mask_is_zero_logits():
+    """softmax with no mask tensor differentiates w.r.t. the implied (equal) logits: the
+    same gradients as explicit zero logits; grad_x, grad_offset and grad_weight are the
+    unmodulated ones divided by K (every point has modulation 1/K)."""
+    st, pd, dl, dg = (1, 1), (1, 1), (1, 1), 2
+    x, off, m, w, go = _case(8, 2, 4, 5, 6, 3, 3, 3, st, pd, dl, dg)
+    g = _bwd(x, off, None, w, go, st, pd, dl, True)
+    gz = _bwd(x, off, np.zeros_like(m), w, go, st, pd, dl, True)
+    for k in ("grad_x", "grad_offset", "grad_mask", "grad_weight"):
+        np.testing.assert_allclose(g[k], gz[k], rtol=0, atol=1e-12)
+    g1 = _bwd(x, off, None, w, go, st, pd, dl, False)
+    for k in ("grad_x", "grad_offset", "grad_weight"):
+        np.testing.assert_allclose(g[k], g1[k] / 9.0, rtol=0, atol=1e-12)
+    # logits' gradient: m_k (g_k - sum_j m_j g_j) with m = 1/9 and g_k the unit
+    # modulation's gradient
+    gm = g1["grad_mask"].reshape(2, dg, 9, *go.shape[2:]) / 9.0
+    want = (gm - gm.sum(2, keepdims=True) / 9.0).reshape(g["grad_mask"].shape)
+    np.testing.assert_allclose(g["grad_mask"], want, rtol=0, atol=1e-12)
