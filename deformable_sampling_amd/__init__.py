@@ -25,7 +25,9 @@ DCN_BWD_DEFAULT, DCN_BWD_ATOMIC, DCN_BWD_PAIR_PASS = 0, 1, 2
 DCN_BWD_PAIR_PASS_RECORDS, DCN_BWD_UNSTAGED_GATHER, DCN_BWD_GENERAL_MAIN = 4, 8, 16
 
 STATUS = {0: "DCN_OK", 1: "DCN_ERR_NULL", 2: "DCN_ERR_SHAPE", 3: "DCN_ERR_PARAM",
-          4: "DCN_ERR_DTYPE", 5: "DCN_ERR_ALIGN", 6: "DCN_ERR_WORKSPACE", 7: "DCN_ERR_HIP"}
+          4: "DCN_ERR_DTYPE", 5: "DCN_ERR_ALIGN", 6: "DCN_ERR_WORKSPACE", 7: "DCN_ERR_HIP",
+          8: "DCN_ERR_SCRATCH"}
+DCN_V2_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # every symbol include/dcn.h declares
 EXPORTS = ("dcn_core_forward", "dcn_core_forward_packed", "dcn_core_backward_workspace_bytes", "dcn_core_backward",
@@ -35,6 +37,7 @@ EXPORTS = ("dcn_core_forward", "dcn_core_forward_packed", "dcn_core_backward_wor
            "deform_roi_pool_forward",
            "dcn_core_backward_workspace_bytes_path", "dcn_core_backward_path",
            "deform_agg_backward_workspace_bytes_path", "deform_agg_backward_path",
+           "dcn_v2_noalloc_bytes", "dcn_v2_forward_noalloc",
            "dcn_status_string", "dcn_last_hip_error")
 
 
@@ -96,6 +99,10 @@ def load(path: str | None = None):
     lib.deform_agg_backward_workspace_bytes_path.argtypes = [i] * 9 + [u]
     lib.deform_agg_backward_path.restype = i
     lib.deform_agg_backward_path.argtypes = [vp] * 10 + [_c.c_size_t] + [i] * 9 + [i, u, vp]
+    lib.dcn_v2_noalloc_bytes.restype = _c.c_size_t
+    lib.dcn_v2_noalloc_bytes.argtypes = [i] * 15
+    lib.dcn_v2_forward_noalloc.restype = i
+    lib.dcn_v2_forward_noalloc.argtypes = [vp] * 5 + [i] * 15 + [i, vp]
     lib.deform_roi_pool_forward.restype = i
     lib.deform_roi_pool_forward.argtypes = [vp] * 4 + [i] * 7 + [f, f, i, vp]
     lib.dcn_status_string.restype = _c.c_char_p
@@ -327,6 +334,48 @@ def dcn_v2_forward(x, offset, mask, weight, out=None, workspace=None, *, stride=
     _call("dcn_v2_forward", _ptr(x), _ptr(offset), _ptr(mask), _ptr(weight), _ptr(out),
           _ptr(workspace), workspace.numel() * workspace.element_size(), N, Cin, H, W, Cout, kh, kw,
           sh, sw, ph, pw, dh, dw, dg, int(bool(softmax)), _DTYPE_ID[x.dtype], _stream(stream))
+    return out
+
+
+def dcn_v2_noalloc_bytes(N, Cin, H, W, Cout, kernel=(3, 3), stride=1, pad=1, dilation=1,
+                         deform_groups=1, dtype=torch.bfloat16):
+    """Static-scratch bytes dcn_v2_forward_noalloc needs for these sizes (0 if invalid)."""
+    kh, kw = _pair(kernel)
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    dh, dw = _pair(dilation)
+    return int(load().dcn_v2_noalloc_bytes(N, Cin, H, W, Cout, kh, kw, sh, sw, ph, pw, dh, dw,
+                                           deform_groups, _DTYPE_ID[dtype]))
+
+
+def dcn_v2_forward_noalloc(x, offset, mask, weight, out, *, stride=1, pad=1, dilation=1,
+                           deform_groups=None, softmax=False, stream=None):
+    """dcn_v2_forward with the library's static workspace: allocates nothing, so `out`
+    [N,Cout,Ho,Wo] must be passed in. Overlapping calls on one GPU race."""
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    dh, dw = _pair(dilation)
+    _check(x, "x")
+    _check(weight, "weight", x.dtype)
+    _check(offset, "offset", torch.float32)
+    _check(mask, "mask", torch.float32, allow_none=True)
+    _check(out, "out", x.dtype)
+    N, Cin, H, W = x.shape
+    Cout, Cin_w, kh, kw = weight.shape
+    if Cin_w != Cin:
+        raise ValueError("weight has %d input channels, x has %d" % (Cin_w, Cin))
+    K = kh * kw
+    dg = deform_groups if deform_groups is not None else offset.shape[1] // (2 * K)
+    Ho, Wo = out_size(H, kh, sh, ph, dh), out_size(W, kw, sw, pw, dw)
+    if tuple(offset.shape) != (N, dg * K * 2, Ho, Wo):
+        raise ValueError("offset must be [N, dg*K*2, Ho, Wo]")
+    if mask is not None and tuple(mask.shape) != (N, dg * K, Ho, Wo):
+        raise ValueError("mask must be [N, dg*K, Ho, Wo]")
+    if tuple(out.shape) != (N, Cout, Ho, Wo):
+        raise ValueError("out must be [N, Cout, Ho, Wo]")
+    _call("dcn_v2_forward_noalloc", _ptr(x), _ptr(offset), _ptr(mask), _ptr(weight), _ptr(out),
+          N, Cin, H, W, Cout, kh, kw, sh, sw, ph, pw, dh, dw, dg, int(bool(softmax)),
+          _DTYPE_ID[x.dtype], _stream(stream))
     return out
 
 

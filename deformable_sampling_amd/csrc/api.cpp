@@ -4,6 +4,11 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
+#include <mutex>
+
+#include <hip/hip_runtime.h>
+
 #include "dcn.h"
 #include "internal.hpp"
 
@@ -39,6 +44,41 @@ dcn_status check_window(int kh, int kw, int sh, int sw, int ph, int pw, int dh, 
 
 }  // namespace
 
+// dcn_v2_forward_noalloc: the workspace is this file's static device array instead of a
+// caller buffer, for callers that cannot allocate. Each device holds its own copy of the
+// array; its address on a device comes from hipGetSymbolAddress, taken once per device
+// (with that device current) on the first call there and kept. Host code uses only that
+// address, never the array's name. Nothing in it needs clearing between calls: every
+// byte a call reads was written earlier in the same call.
+static __device__ __align__(256) unsigned char scratch[DCN_V2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// This device's address of `scratch` (hipGetSymbolAddress once per device).
+hipError_t scratch_address(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_acquire);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+}  // namespace
+
 extern "C" {
 
 const char *dcn_status_string(dcn_status s) {
@@ -51,6 +91,7 @@ const char *dcn_status_string(dcn_status s) {
         case DCN_ERR_ALIGN: return "misaligned pointer";
         case DCN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case DCN_ERR_HIP: return "HIP launch error";
+        case DCN_ERR_SCRATCH: return "the call needs more than the library's static scratch";
     }
     return "unknown status";
 }
@@ -228,12 +269,14 @@ size_t dcn_v2_workspace_bytes(int N, int Cin, int H, int W, int Cout, int kh, in
     return plan.total;
 }
 
-// Shared by dcn_v2_forward and dcn_v2_im2col (weight == out == NULL: columns only).
-static dcn_status v2_call(const void *x, const float *offset, const float *mask, const void *weight,
-                          void *out, void *workspace, size_t workspace_bytes, int N, int Cin, int H,
-                          int W, int Cout, int kh, int kw, int stride_h, int stride_w, int pad_h,
-                          int pad_w, int dil_h, int dil_w, int deform_groups, int softmax,
-                          dcn_dtype dtype, hipStream_t stream, bool columns_only) {
+// Argument checks shared by dcn_v2_forward, dcn_v2_forward_noalloc and dcn_v2_im2col
+// (columns_only: no weight and no out). On DCN_OK with N > 0, `a` is ready to launch
+// except for its workspace; all checks here precede any HIP call.
+static dcn_status v2_check(const void *x, const float *offset, const float *mask,
+                           const void *weight, void *out, int N, int Cin, int H, int W, int Cout,
+                           int kh, int kw, int stride_h, int stride_w, int pad_h, int pad_w,
+                           int dil_h, int dil_w, int deform_groups, int softmax, dcn_dtype dtype,
+                           bool columns_only, dcn::V2Launch &a) {
     if (!valid_dtype(dtype)) return DCN_ERR_DTYPE;
     if (dtype == DCN_F32) return DCN_ERR_DTYPE;
     if (N < 0 || Cin <= 0 || H <= 0 || W <= 0 || Cout <= 0) return DCN_ERR_SHAPE;
@@ -250,8 +293,6 @@ static dcn_status v2_call(const void *x, const float *offset, const float *mask,
     if (plan.Pp > kI32 || (long long)N * Cin * H * W > (1LL << 40)) return DCN_ERR_SHAPE;
     if (N == 0) return DCN_OK;
     if (!x || !offset || (!columns_only && (!weight || !out))) return DCN_ERR_NULL;
-    if (!workspace || !aligned(workspace, 256) || workspace_bytes < plan.total)
-        return DCN_ERR_WORKSPACE;
     if (!aligned(x, 2) || !aligned(weight, 2) || !aligned(out, 2) || !aligned(offset, 4) ||
         (mask && !aligned(mask, 4)))
         return DCN_ERR_ALIGN;
@@ -259,16 +300,31 @@ static dcn_status v2_call(const void *x, const float *offset, const float *mask,
         weight = nullptr;
         out = nullptr;
     }
-
-    dcn::V2Launch a;
     a.x = x; a.offset = offset; a.mask = mask; a.weight = weight; a.out = out;
-    a.workspace = workspace;
+    a.workspace = nullptr;
     a.N = N; a.Cin = Cin; a.H = H; a.W = W; a.Cout = Cout; a.kh = kh; a.kw = kw;
     a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w; a.dh = dil_h; a.dw = dil_w;
     a.dg = deform_groups;
     a.softmax = softmax;
     a.dtype = dtype;
     a.plan = plan;
+    return DCN_OK;
+}
+
+// Shared by dcn_v2_forward and dcn_v2_im2col (weight == out == NULL: columns only).
+static dcn_status v2_call(const void *x, const float *offset, const float *mask, const void *weight,
+                          void *out, void *workspace, size_t workspace_bytes, int N, int Cin, int H,
+                          int W, int Cout, int kh, int kw, int stride_h, int stride_w, int pad_h,
+                          int pad_w, int dil_h, int dil_w, int deform_groups, int softmax,
+                          dcn_dtype dtype, hipStream_t stream, bool columns_only) {
+    dcn::V2Launch a;
+    const dcn_status st = v2_check(x, offset, mask, weight, out, N, Cin, H, W, Cout, kh, kw,
+                                   stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, deform_groups,
+                                   softmax, dtype, columns_only, a);
+    if (st != DCN_OK || N == 0) return st;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < a.plan.total)
+        return DCN_ERR_WORKSPACE;
+    a.workspace = workspace;
     return hip_status(dcn::launch_dcn_v2(a, stream));
 }
 
@@ -290,6 +346,38 @@ dcn_status dcn_v2_im2col(const void *x, const float *offset, const float *mask, 
     return v2_call(x, offset, mask, nullptr, nullptr, workspace, workspace_bytes, N, Cin, H, W,
                    Cout, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, deform_groups,
                    softmax, dtype, stream, true);
+}
+
+size_t dcn_v2_noalloc_bytes(int N, int Cin, int H, int W, int Cout, int kh, int kw, int stride_h,
+                            int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                            int deform_groups, dcn_dtype dtype) {
+    if (check_window(kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w) != DCN_OK) return 0;
+    if (H <= 0 || W <= 0 || deform_groups <= 0) return 0;
+    dcn::V2Plan plan;
+    if (!dcn::plan_dcn_v2(N, Cin, H, W, Cout, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h,
+                          dil_w, dtype, plan))
+        return 0;
+    return dcn::v2_fused_applies(plan, deform_groups, true) ? plan.off_col : plan.total;
+}
+
+dcn_status dcn_v2_forward_noalloc(const void *x, const float *offset, const float *mask,
+                                  const void *weight, void *out, int N, int Cin, int H, int W,
+                                  int Cout, int kh, int kw, int stride_h, int stride_w, int pad_h,
+                                  int pad_w, int dil_h, int dil_w, int deform_groups, int softmax,
+                                  dcn_dtype dtype, hipStream_t stream) {
+    dcn::V2Launch a;
+    const dcn_status st = v2_check(x, offset, mask, weight, out, N, Cin, H, W, Cout, kh, kw,
+                                   stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, deform_groups,
+                                   softmax, dtype, false, a);
+    if (st != DCN_OK || N == 0) return st;
+    const size_t need = dcn::v2_fused_applies(a.plan, deform_groups, true) ? a.plan.off_col
+                                                                            : a.plan.total;
+    if (need > (size_t)DCN_V2_NOALLOC_SCRATCH_BYTES) return DCN_ERR_SCRATCH;
+    void *ws = nullptr;
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return hip_status(e);
+    a.workspace = ws;
+    return hip_status(dcn::launch_dcn_v2(a, stream));
 }
 
 // Shape checks and plan of the DCNv2 backward (the forward's limits).

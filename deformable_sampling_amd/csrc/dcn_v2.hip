@@ -436,7 +436,7 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     if (err != hipSuccess) return err;
 
     const size_t fused_lds = (size_t)kFBN * a.dg * pl.K * 3 * sizeof(float);
-    if (a.weight && pl.fused && fused_lds <= 64 * 1024) {  // 2+3. deform-im2col fused into the GEMM
+    if (v2_fused_applies(pl, a.dg, a.weight != nullptr)) {  // 2+3. deform-im2col fused into the GEMM
         FusedParams fp;
         fp.N = a.N; fp.H = a.H; fp.W = a.W; fp.Ho = pl.Ho; fp.Wo = pl.Wo; fp.kw = a.kw;
         fp.sh = a.sh; fp.sw = a.sw; fp.ph = a.ph; fp.pw = a.pw; fp.dh = a.dh; fp.dw = a.dw;
@@ -522,6 +522,11 @@ bool plan_dcn_v2(int N, int Cin, int H, int W, int Cout, int kh, int kw, int sh,
                (size_t)N * H * W * pl.Cin_pad * elt < (1ull << 31) &&
                (size_t)pl.Mp * pl.Rp * elt < (1ull << 31);
     return true;
+}
+
+bool v2_fused_applies(const V2Plan &pl, int dg, bool has_weight) {
+    // the block's offsets and masks ([kFBN][dg][K] x 3 floats) fit its 64 KB of dynamic LDS
+    return has_weight && pl.fused && (size_t)kFBN * dg * pl.K * 3 * sizeof(float) <= 64 * 1024;
 }
 
 hipError_t launch_dcn_v2(const V2Launch &a, hipStream_t stream) {

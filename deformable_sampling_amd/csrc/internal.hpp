@@ -102,6 +102,9 @@ struct V2Plan {
 };
 bool plan_dcn_v2(int N, int Cin, int H, int W, int Cout, int kh, int kw, int sh, int sw, int ph,
                  int pw, int dh, int dw, dcn_dtype dtype, V2Plan &plan);
+// Whether a forward call on this plan forms its columns on chip inside the GEMM (then
+// only the workspace bytes [0, off_col) are touched).
+bool v2_fused_applies(const V2Plan &plan, int dg, bool has_weight);
 
 struct V2Launch {
     const void *x;

@@ -9,6 +9,7 @@
  *   dcn_v2_forward      DCNv2 modulated deformable convolution, NCHW: deform-im2col
  *                       and an MFMA GEMM (fused, or in two stages through the workspace).
  *   dcn_v2_im2col       the deform-im2col stage alone: columns into the workspace.
+ *   dcn_v2_forward_noalloc  dcn_v2_forward with a static in-library workspace.
  *   dcn_v2_backward     gradients of DCNv2 w.r.t. x, offsets, masks and the weight.
  *   deform_agg_forward  Sparse4D-style multi-camera, multi-scale aggregation.
  *   deform_agg_backward gradients of the aggregation w.r.t. features, locations, weights.
@@ -51,7 +52,8 @@
  *    host before any HIP call, so a rejected call has no effect. DCN_ERR_HIP means
  *    a launch failed; dcn_last_hip_error() then returns the hipError_t (per thread).
  *    Zero-sized work (N, H, W or A equal to 0) returns DCN_OK and launches nothing.
- *  - Thread-safe and re-entrant; the only state is the per-thread last HIP error.
+ *  - Thread-safe and re-entrant; the only state is the per-thread last HIP error (and
+ *    the static workspace of dcn_v2_forward_noalloc, whose overlapping calls race).
  */
 #ifndef DCN_H_
 #define DCN_H_
@@ -75,7 +77,9 @@ typedef enum {
     DCN_ERR_DTYPE = 4,     /* dtype not supported by this entry point               */
     DCN_ERR_ALIGN = 5,     /* a pointer is not aligned to its element size          */
     DCN_ERR_WORKSPACE = 6, /* workspace NULL, misaligned (256 B) or too small       */
-    DCN_ERR_HIP = 7        /* a HIP launch failed; see dcn_last_hip_error()         */
+    DCN_ERR_HIP = 7,       /* a HIP launch failed; see dcn_last_hip_error()         */
+    DCN_ERR_SCRATCH = 8    /* dcn_v2_forward_noalloc: the call needs more than the
+                              library's static scratch (DCN_V2_NOALLOC_SCRATCH_BYTES) */
 } dcn_status;
 
 /*
@@ -220,6 +224,32 @@ dcn_status dcn_v2_im2col(const void *x, const float *offset, const float *mask, 
                          int kw, int stride_h, int stride_w, int pad_h, int pad_w, int dil_h,
                          int dil_w, int deform_groups, int softmax, dcn_dtype dtype,
                          hipStream_t stream);
+
+/*
+ * dcn_v2_forward for callers that cannot allocate device memory or pass a workspace:
+ * code being captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments and results as dcn_v2_forward, without workspace and
+ * workspace_bytes; it allocates nothing (no hipMalloc, hipFree or allocating library
+ * call). Its workspace is a static device array of DCN_V2_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) inside the library, one per GPU, which that GPU holds from the library's
+ * first use there until the process ends. A call needing more than that
+ * (dcn_v2_noalloc_bytes) returns DCN_ERR_SCRATCH before any HIP call; the shapes that
+ * form their columns on chip need only the channels-last x and the permuted weight
+ * (7.7 MB for 8x256x40x40 with Cout 256). Every call on one GPU uses the same array:
+ * calls that may overlap on one GPU (several host threads, or several streams without
+ * ordering between them) race and must be serialised by the caller. The first call on
+ * a device looks up the array's address there (hipGetDevice, hipGetSymbolAddress);
+ * later calls only launch.
+ */
+#define DCN_V2_NOALLOC_SCRATCH_BYTES (64u << 20)
+size_t dcn_v2_noalloc_bytes(int N, int Cin, int H, int W, int Cout, int kh, int kw,
+                            int stride_h, int stride_w, int pad_h, int pad_w,
+                            int dil_h, int dil_w, int deform_groups, dcn_dtype dtype);
+dcn_status dcn_v2_forward_noalloc(const void *x, const float *offset, const float *mask,
+                                  const void *weight, void *out, int N, int Cin, int H, int W,
+                                  int Cout, int kh, int kw, int stride_h, int stride_w,
+                                  int pad_h, int pad_w, int dil_h, int dil_w, int deform_groups,
+                                  int softmax, dcn_dtype dtype, hipStream_t stream);
 
 /*
  * Workspace bytes dcn_v2_backward needs (0 if the sizes are invalid). Regions, each

@@ -14,7 +14,7 @@ import deformable_sampling_amd as dsa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dcn.h")
 
-OK, NULL, SHAPE, PARAM, DTYPE, ALIGN, WORKSPACE, HIP = range(8)
+OK, NULL, SHAPE, PARAM, DTYPE, ALIGN, WORKSPACE, HIP, SCRATCH = range(9)
 A = 0x10000  # a 256-byte aligned fake device address (never dereferenced)
 
 
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         s = lib.dcn_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.dcn_status_string(99).decode() == "unknown status"
@@ -368,4 +368,37 @@ def test_backward_path_variants_validate_their_flags(lib):
     st_bad = (ctypes.c_int32 * 4)(0, 25, 31, 99)                  # map past P_total
     aargs_bad = (A, ss, st_bad) + aargs[3:]
     assert lib.deform_agg_backward_path(*aargs_bad, 1, None) == SHAPE
+    assert lib.dcn_last_hip_error() == 0
+
+
+def test_v2_noalloc_sizes_and_validation(lib):
+    """dcn_v2_forward_noalloc: scratch need per call (fused shapes: channels-last x plus
+    the permuted weight; others also the columns), a call beyond the static array is
+    refused with DCN_ERR_SCRATCH before any HIP call, and bad arguments give the same
+    status as dcn_v2_forward."""
+    a256 = lambda v: (v + 255) // 256 * 256
+    # 8x256x40x40, Cout 256, bf16: fused (Cin % 64 == 0)
+    need = lib.dcn_v2_noalloc_bytes(8, 256, 40, 40, 256, 3, 3, 1, 1, 1, 1, 1, 1, 1, 2)
+    assert need == a256(8 * 40 * 40 * 256 * 2) + a256(256 * 2304 * 2)
+    assert need < dsa.DCN_V2_NOALLOC_SCRATCH_BYTES
+    # Cin 16: two-stage, the columns too
+    full = lib.dcn_v2_workspace_bytes(2, 16, 9, 11, 24, 3, 3, 1, 1, 1, 1, 1, 1, 2)
+    assert lib.dcn_v2_noalloc_bytes(2, 16, 9, 11, 24, 3, 3, 1, 1, 1, 1, 1, 1, 1, 2) == full
+    assert lib.dcn_v2_noalloc_bytes(2, 16, 9, 11, 24, 3, 3, 0, 1, 1, 1, 1, 1, 1, 2) == 0
+
+    def call(N=1, Cin=16, H=8, W=8, Cout=8, x=A, off=A, m=A, w=A, out=A, dg=1, dtype=2):
+        return lib.dcn_v2_forward_noalloc(x, off, m, w, out, N, Cin, H, W, Cout, 3, 3, 1, 1, 1,
+                                          1, 1, 1, dg, 0, dtype, None)
+    # 4 x 256 x 160 x 160 (Cin not a multiple of 64 -> columns): far beyond 64 MiB
+    big = lib.dcn_v2_noalloc_bytes(4, 200, 160, 160, 64, 3, 3, 1, 1, 1, 1, 1, 1, 1, 2)
+    assert big > dsa.DCN_V2_NOALLOC_SCRATCH_BYTES
+    assert call(N=4, Cin=200, H=160, W=160, Cout=64) == SCRATCH
+    assert call(dtype=0) == DTYPE
+    assert call(dtype=9) == DTYPE
+    assert call(Cin=0) == SHAPE
+    assert call(dg=3) == PARAM
+    assert call(x=None) == NULL
+    assert call(w=None) == NULL
+    assert call(out=A + 1) == ALIGN
+    assert call(N=0) == OK
     assert lib.dcn_last_hip_error() == 0
