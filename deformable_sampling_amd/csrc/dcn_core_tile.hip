@@ -69,6 +69,7 @@ __device__ __forceinline__ TileAt tile_at(int t, const TileParams &p) {
 // 512-thread plan has 2 and 16), so the lane's indices are shifts and masks.
 struct LaneAt {
     int s, gl, q, ho, wo, g;
+    unsigned pix, pr;  // output pixel (n*Ho + ho)*Wo + wo and pair pix*G + g; 0 if idle
     bool active;
 };
 template <int S, int LPP_ = 0, int TW_ = 0>
@@ -86,6 +87,13 @@ __device__ __forceinline__ LaneAt lane_at(const TileAt &a, const TileParams &p) 
     l.wo = a.wo0 + qx;
     l.active = l.q < p.TH * p.TW && l.ho < p.Ho && l.wo < p.Wo;
     l.g = a.g0 + l.gl;
+    // 24-bit multiplies: the plan keeps N*Ho, Wo and Wo*G below 2^24 and the pair count
+    // below 2^31
+    const unsigned row = __umul24((unsigned)a.n, (unsigned)p.Ho) + (unsigned)l.ho;
+    l.pix = l.active ? __umul24(row, (unsigned)p.Wo) + (unsigned)l.wo : 0u;
+    l.pr = l.active ? __umul24(row, (unsigned)(p.Wo * p.G)) + __umul24((unsigned)l.wo, (unsigned)p.G) +
+                          (unsigned)l.g
+                    : 0u;
     return l;
 }
 
@@ -124,7 +132,7 @@ __device__ __forceinline__ void load_dm(float (&d)[2 * K], float (&m)[K], const 
                                         const LaneAt &l, const typename OM::bits *offset,
                                         const typename OM::bits *mask, const TileParams &p) {
     if constexpr (kOmPlain<OM>) {
-        const size_t pr = l.active ? (((size_t)a.n * p.Ho + l.ho) * p.Wo + l.wo) * p.G + l.g : 0;
+        const size_t pr = l.pr;
         const float2 *o2 = reinterpret_cast<const float2 *>(offset + pr * K * 2);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -141,7 +149,7 @@ __device__ __forceinline__ void load_dm(float (&d)[2 * K], float (&m)[K], const 
             for (int k = 0; k < K; ++k) m[k] = 1.0f;
         }
     } else {
-        const size_t pixel = l.active ? ((size_t)a.n * p.Ho + l.ho) * p.Wo + l.wo : 0;
+        const size_t pixel = l.pix;
         const int g = l.active ? l.g : 0;
         const typename OM::bits *od = offset + pixel * p.off_pix + (size_t)g * p.off_grp;
 #pragma unroll
@@ -208,7 +216,7 @@ __device__ __forceinline__ void make_taps(TapW (&tw)[KH * KW], unsigned &far, fl
     const int cpp = CPP_ ? CPP_ : p.cpp;
     const int rw = RW_ ? RW_ : p.RW;
     const int rowc = rw * cpp;
-    const int lby = l.ho * p.sh - p.ph - a.ry0, lbx = l.wo * p.sw - p.pw - a.rx0;
+    const int lby = __mul24(l.ho, p.sh) - p.ph - a.ry0, lbx = __mul24(l.wo, p.sw) - p.pw - a.rx0;
     // grid base of the output pixel relative to the region origin; the image bounds
     // test adds the origin back (y0 + 1 = ly + ry0 + 1)
     const int ty = a.ry0 + 1, tx = a.rx0 + 1;
@@ -338,7 +346,7 @@ __device__ __forceinline__ void taps_run(const uint4 *buf, const typename E::bit
             acc[NC - 1][z] = tmp;
         }
     }
-    Bt *o = out + (((size_t)a.n * p.Ho + l.ho) * p.Wo + l.wo) * GC + (size_t)l.g * p.C + l.s * NC * V;
+    Bt *o = out + (size_t)l.pr * p.C + l.s * NC * V;
 #pragma unroll
     for (int u = 0; u < NC; ++u) store_f32<E, V>(o + u * V, acc[u]);
 }
@@ -402,22 +410,33 @@ __device__ __forceinline__ void stage_region_fixed(uint4 *lds, const typename E:
     const int r0 = (w0 + lane) / CPP;
     int ry = r0 / RW, rx = r0 - ry * RW;
     const int GCe = GC * elt;
+    // Byte offset of the lane's region pixel in the image, advanced by a constant per copy
+    // (DY rows and DX columns, one more row and RW columns back on a wrap): no multiply
+    // in the loop. Unsigned arithmetic wraps; offsets of pixels outside the image are
+    // never used, and those inside are below img_bytes < 2^31.
+    const unsigned rowb = (unsigned)(p.W * GCe);
+    int yy = a.ry0 + ry, xx = a.rx0 + rx;
+    unsigned off = (unsigned)yy * rowb + (unsigned)(xx * GCe + cb);
+    const int xend = a.rx0 + RW;
+    const unsigned step = (unsigned)DY * rowb + (unsigned)(DX * GCe);
+    const unsigned wrap = rowb - (unsigned)(RW * GCe);
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
         const int i0 = w0 + it * NT;
         if (it < NIT - 1 || i0 < total) {
             // only the last step can pass the region's end
             const bool in = it < NIT - 1 || i0 + lane < total;
-            const int yy = a.ry0 + ry, xx = a.rx0 + rx;
             const bool ok = in && (unsigned)yy < (unsigned)p.H && (unsigned)xx < (unsigned)p.W;
-            const int off = ok ? (yy * p.W + xx) * GCe + cb : (int)img_bytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(lds + i0), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(lds + i0), 16,
+                                                     ok ? (int)off : (int)img_bytes, 0, 0, 0);
         }
-        rx += DX;
-        ry += DY;
-        if (rx >= RW) {
-            rx -= RW;
-            ++ry;
+        xx += DX;
+        yy += DY;
+        off += step;
+        if (xx >= xend) {
+            xx -= RW;
+            ++yy;
+            off += wrap;
         }
     }
 }
@@ -457,9 +476,8 @@ __global__ __launch_bounds__(1024) void dcn_core_tile_kernel(const typename E::b
     asm volatile("" ::"v"(far));
     __syncthreads();
     if (!l.active) return;
-    const size_t pixel = ((size_t)a.n * p.Ho + l.ho) * p.Wo + l.wo;
-    const typename OM::bits *coff = kOmPlain<OM> ? offset + (pixel * p.G + l.g) * K * 2
-                                                 : offset + pixel * p.off_pix + (size_t)l.g * p.off_grp;
+    const typename OM::bits *coff = kOmPlain<OM> ? offset + (size_t)l.pr * K * 2
+                                                 : offset + (size_t)l.pix * p.off_pix + (size_t)l.g * p.off_grp;
     taps_run<E, OM, KH, KW, S, NC, CPP_, RW_>(lds, x, out, tw, far, m, a, l, p, coff);
 }
 
@@ -517,7 +535,7 @@ __global__ __launch_bounds__(1024) void dcn_core_bwd_tile_kernel(const typename 
     load_dm<K, OMPlain>(d, m, a, l, reinterpret_cast<const uint32_t *>(offset),
                         reinterpret_cast<const uint32_t *>(mask), p);
     stage_region<E>(lds, x, a, p);
-    const size_t pixel = l.active ? ((size_t)a.n * p.Ho + l.ho) * p.Wo + l.wo : 0;
+    const size_t pixel = l.pix;
     float gv[NC][V];  // this pair's grad_out channels
     {
         const Bt *gp = gout + pixel * GC + (size_t)l.g * p.C;
@@ -906,6 +924,8 @@ bool plan_core_tile(const CoreLaunch &a, TileParams &p) {
     if ((uintptr_t)a.x % 16 || (uintptr_t)a.out % 16) return false;
     if (a.om_plain && (uintptr_t)a.offset % 8) return false;  // 8-byte (dx, dy) loads
     if ((long long)a.H * a.W >= (1LL << 24) || (long long)a.G * a.C >= (1LL << 24)) return false;
+    // lane indices use 24-bit multiplies (the pair count is below 2^31 by validation)
+    if ((long long)a.N * a.Ho >= (1LL << 24) || (long long)a.Wo * a.G >= (1LL << 24)) return false;
     // 16-byte chunks per lane: two where the channels allow, except for bf16, whose
     // widening (no mixed-precision FMA) would need twice the registers
     const int NC = (cbytes % 32 == 0 && a.dtype != DCN_BF16) ? 2 : 1;
