@@ -12,7 +12,8 @@ object of the core kernel (algorithmic bytes per launch / HIP-event launch time 
 other ops (DCNv4/DCNv3 small maps, the core backward, DCNv2 im2col + MFMA GEMM,
 aggregation forward and backward, deformable RoI pooling).
 
-  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--only core|bwd|aggbwd|v2bwd]
+  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+                  [--only core|c1|c2|packed|bwd|v2|v2bwd|agg|aggbwd|roi|mfma]
   python bench.py --calib-copy     # plain copy of known size, for counter scaling
 """
 from __future__ import annotations
@@ -88,6 +89,77 @@ class Timer:
         t1 = time.perf_counter()
         return (t1 - t0) / iters, e0.elapsed_time(e1) / 1e3 / iters
 
+    def run_cold(self, fn, iters, warmup, flush):
+        """Each launch timed alone (HIP events around it) after flush() has streamed a
+        buffer larger than the 256 MB last-level cache through the device, so that the
+        launch finds none of its inputs cached. Returns (median, p10, p90) seconds."""
+        torch = self.torch
+        for _ in range(warmup):
+            flush()
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(iters):
+            flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) / 1e3 for a, b in evs)
+        q = lambda f: ts[min(len(ts) - 1, int(f * len(ts)))]
+        return q(0.5), q(0.1), q(0.9)
+
+
+class Flush:
+    """Streams 2 x 512 MiB (read one buffer, write the other) between cold launches."""
+
+    def __init__(self, torch, mib=512):
+        n = mib * (1 << 20) // 4
+        self.a = torch.ones(n, device="cuda")
+        self.b = torch.empty_like(self.a)
+
+    def __call__(self):
+        self.b.copy_(self.a)
+
+
+def cold_fields(timer, call, flush, nbytes, iters=50, warmup=3):
+    """Cold-cache timing of one op: median and spread, and its HBM rate."""
+    med, p10, p90 = timer.run_cold(call, iters, warmup, flush)
+    return dict(cold_kernel_us=round(med * 1e6, 2), cold_p10_us=round(p10 * 1e6, 2),
+                cold_p90_us=round(p90 * 1e6, 2), cold_gbs=nbytes / med / 1e9,
+                cold_frac=nbytes / med / 1e9 / HBM_PEAK_GBS)
+
+
+def measure_copy(torch, timer, mib=1024):
+    """Sustained device copy bandwidth (read + write bytes / time) of a plain copy of
+    mib MiB: the measured counterpart of the published HBM peak."""
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    _, kern = timer.run(lambda: b.copy_(a), 20, 5)
+    return 2.0 * n * 4 / kern / 1e9
+
+
+def measure_mfma(dsa, torch, timer, iters=4096):
+    """Sustained dense bf16 MFMA rate of dcn_mfma_probe (register operands only) over
+    two blocks of four waves per compute unit."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 2 * cus
+    sink = torch.empty(blocks * 256, device="cuda")
+    lib = dsa.load()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def call():
+        st = lib.dcn_mfma_probe(sink.data_ptr(), blocks, iters, stream)
+        if st:
+            raise RuntimeError("dcn_mfma_probe status %d" % st)
+    _, kern = timer.run(call, 10, 2)
+    flops = blocks * 4.0 * iters * 4 * 32768
+    return flops / kern / 1e12
+
 
 def raw_core_call(lib, c, x, off, mask, out, stream, softmax):
     """Argument tuple of the C entry point, prepared once (the timed loop then only
@@ -108,7 +180,15 @@ def raw_core_call(lib, c, x, off, mask, out, stream, softmax):
     return call
 
 
-def bench_core(dsa, torch, timer, name, iters, warmup):
+def headline_tensors(torch, c):
+    """Device copies of a core case's x, offsets, masks and an output buffer."""
+    dev = lambda t: None if t is None else t.to("cuda").contiguous()
+    x, off, m = dev(c["x"]), dev(c["offset"]), dev(c["mask"])
+    out = torch.empty((c["N"], c["Ho"], c["Wo"], c["G"] * c["C"]), dtype=x.dtype, device="cuda")
+    return x, off, m, out
+
+
+def bench_core(dsa, torch, timer, name, iters, warmup, flush=None):
     import workloads as wl
     c = wl.make(name)
     dev = lambda t: None if t is None else t.to("cuda").contiguous()
@@ -120,9 +200,12 @@ def bench_core(dsa, torch, timer, name, iters, warmup):
     taps = c["N"] * c["Ho"] * c["Wo"] * c["G"] * c["kh"] * c["kw"]
     nbytes = (x.numel() * x.element_size() + off.numel() * 4 + (m.numel() * 4 if m is not None else 0)
               + out.numel() * out.element_size())
-    return dict(workload=name, taps=taps, channel_taps=taps * c["C"], algo_bytes=nbytes,
-                wall_s=wall, kernel_s=kern, taps_per_s=taps / kern,
-                gbs=nbytes / kern / 1e9, frac=nbytes / kern / 1e9 / HBM_PEAK_GBS), c
+    r = dict(workload=name, taps=taps, channel_taps=taps * c["C"], algo_bytes=nbytes,
+             wall_s=wall, kernel_s=kern, taps_per_s=taps / kern,
+             gbs=nbytes / kern / 1e9, frac=nbytes / kern / 1e9 / HBM_PEAK_GBS)
+    if flush is not None:
+        r.update(cold_fields(timer, call, flush, nbytes))
+    return r, c
 
 
 def bench_core_packed(dsa, torch, timer, name, iters, warmup):
@@ -198,7 +281,7 @@ def bench_core_bwd(dsa, torch, timer, name, iters, warmup):
                 frac=nbytes / kern / 1e9 / HBM_PEAK_GBS)
 
 
-def bench_v2(dsa, torch, timer, iters, warmup):
+def bench_v2(dsa, torch, timer, iters, warmup, flush=None):
     import workloads as wl
     name = "dcnv2_bf16_n8_c256_40x40"
     c = wl.make(name)
@@ -221,10 +304,14 @@ def bench_v2(dsa, torch, timer, iters, warmup):
     P = N * c["Ho"] * c["Wo"]
     flops = 2.0 * Cout * Cin * 9 * P
     nbytes = x.numel() * 2 + off.numel() * 4 + m.numel() * 4 + w.numel() * 2 + out.numel() * 2
-    return dict(workload=name, taps=P * 9, channel_taps=P * 9 * Cin, algo_bytes=nbytes,
-                flops=flops, wall_s=wall, kernel_s=kern, tflops=flops / kern / 1e12,
-                mfma_frac=flops / kern / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                note="two launches: layout prep, deform-im2col fused into the MFMA GEMM")
+    r = dict(workload=name, taps=P * 9, channel_taps=P * 9 * Cin, algo_bytes=nbytes,
+             flops=flops, wall_s=wall, kernel_s=kern, tflops=flops / kern / 1e12,
+             mfma_frac=flops / kern / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+             note="two launches: layout prep, deform-im2col fused into the MFMA GEMM")
+    if flush is not None:
+        r.update(cold_fields(timer, call, flush, nbytes))
+        r["cold_tflops"] = flops / (r["cold_kernel_us"] * 1e-6) / 1e12
+    return r
 
 
 def bench_v2_bwd(dsa, torch, timer, iters, warmup):
@@ -267,7 +354,7 @@ def bench_v2_bwd(dsa, torch, timer, iters, warmup):
                 gbs=nbytes / kern / 1e9, frac=nbytes / kern / 1e9 / HBM_PEAK_GBS)
 
 
-def bench_agg(dsa, torch, timer, iters, warmup, softmax=True):
+def bench_agg(dsa, torch, timer, iters, warmup, softmax=True, flush=None):
     import workloads as wl
     name = "agg_f32_6cam_4scale_a900p13_g8c32"
     c = wl.make(name, weights="logits" if softmax else "simplex")
@@ -290,10 +377,13 @@ def bench_agg(dsa, torch, timer, iters, warmup, softmax=True):
     wall, kern = timer.run(call, iters, warmup)
     taps = c["B"] * c["A"] * c["pts"] * c["cams"] * c["scales"] * c["G"]
     nbytes = feat.numel() * 4 + loc.numel() * 4 + wts.numel() * 4 + out.numel() * 4
-    return dict(workload=name + ("_softmax" if softmax else ""), taps=taps,
-                channel_taps=taps * c["Cg"], algo_bytes=nbytes, wall_s=wall, kernel_s=kern,
-                taps_per_s=taps / kern, gbs=nbytes / kern / 1e9,
-                frac=nbytes / kern / 1e9 / HBM_PEAK_GBS)
+    r = dict(workload=name + ("_softmax" if softmax else ""), taps=taps,
+             channel_taps=taps * c["Cg"], algo_bytes=nbytes, wall_s=wall, kernel_s=kern,
+             taps_per_s=taps / kern, gbs=nbytes / kern / 1e9,
+             frac=nbytes / kern / 1e9 / HBM_PEAK_GBS)
+    if flush is not None:
+        r.update(cold_fields(timer, call, flush, nbytes))
+    return r
 
 
 def bench_agg_bwd(dsa, torch, timer, iters, warmup):
@@ -399,7 +489,38 @@ def cpu_baseline(case, target_s=10.0, max_reps=200):
         taps = reps * npix_all * per_pix_taps
         sample = "full workload (%d output pixels x %d groups x %d taps) x %d runs, %.1f s" % (
             npix_all, case["G"], case["kh"] * case["kw"], reps, t)
-    return dict(value=taps / t, unit="taps/s", cores=oracle.threads(), kind="oracle", sample=sample)
+    out = dict(value=taps / t, unit="taps/s", cores=oracle.threads(), kind="oracle", sample=sample,
+               cores_affinity=len(os.sched_getaffinity(0)))
+    out["single_thread"] = oracle_single_thread()
+    return out
+
+
+def oracle_single_thread(target_s=1.0):
+    """The oracle on one thread over the two small core workloads (whole, repeated to
+    about target_s each): taps/s."""
+    import oracle
+    import workloads as wl
+    res = []
+    n0 = oracle.threads()
+    oracle.set_threads(1)
+    try:
+        for name in ("dcnv4_f32_n1_32x32_g4c16", "dcnv3_f32_n8_56x56_g4c16_softmax"):
+            c = wl.make(name)
+            xs, off = oracle._f64(c["x"]), oracle._f64(c["offset"])
+            m = oracle._f64(c["mask"])
+            taps = c["N"] * c["Ho"] * c["Wo"] * c["G"] * c["kh"] * c["kw"]
+            reps, t = 0, 0.0
+            while t < target_s and reps < 1000:
+                t0 = time.perf_counter()
+                oracle.dcn_core(xs, off, m, kh=c["kh"], kw=c["kw"], stride=c["stride"],
+                                pad=c["pad"], dil=c["dil"], softmax=c["softmax"])
+                t += time.perf_counter() - t0
+                reps += 1
+            res.append(dict(workload=name, value=taps * reps / t, unit="taps/s", threads=1,
+                            runs=reps, seconds=round(t, 3)))
+    finally:
+        oracle.set_threads(n0)
+    return res
 
 
 def calib_copy(torch, mb=1024, iters=5):
@@ -419,7 +540,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["core", "all", "bwd", "aggbwd", "v2bwd"], default="all")
+    ap.add_argument("--only", choices=["core", "all", "bwd", "aggbwd", "v2bwd", "c1", "c2", "v2",
+                                       "agg", "packed", "roi", "mfma"], default="all")
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -438,6 +560,32 @@ def main():
         return
     timer = Timer(torch)
 
+    # one op alone (for profiling its kernels)
+    if args.only in ("c1", "c2"):
+        nm = {"c1": "dcnv4_f32_n1_32x32_g4c16", "c2": "dcnv3_f32_n8_56x56_g4c16_softmax"}[args.only]
+        r, _ = bench_core(dsa, torch, timer, nm, args.steps, args.warmup)
+        log("%s: %.2f us/launch" % (nm, r["kernel_s"] * 1e6))
+        return
+    if args.only == "v2":
+        r = bench_v2(dsa, torch, timer, args.steps, args.warmup)
+        log("dcnv2: %.2f us/call, %.0f TFLOP/s" % (r["kernel_s"] * 1e6, r["tflops"]))
+        return
+    if args.only == "agg":
+        r = bench_agg(dsa, torch, timer, args.steps, args.warmup, softmax=True)
+        log("aggregation: %.2f us/launch" % (r["kernel_s"] * 1e6))
+        return
+    if args.only == "packed":
+        r = bench_core_packed(dsa, torch, timer, HEADLINE, args.steps, args.warmup)
+        log("packed core: %.2f us/launch" % (r["kernel_s"] * 1e6))
+        return
+    if args.only == "roi":
+        r = bench_roi(dsa, torch, timer, args.steps, args.warmup)
+        log("roi pooling: %.2f us/launch" % (r["kernel_s"] * 1e6))
+        return
+    if args.only == "mfma":
+        log("mfma probe: %.0f TFLOP/s; copy %.0f GB/s" % (measure_mfma(dsa, torch, timer),
+                                                        measure_copy(torch, timer)))
+        return
     if args.only == "v2bwd":  # the DCNv2 backward alone (for profiling)
         r = bench_v2_bwd(dsa, torch, timer, args.steps, args.warmup)
         log("dcnv2 backward: %.2f us/call" % (r["kernel_s"] * 1e6))
@@ -454,21 +602,35 @@ def main():
     head, case = bench_core(dsa, torch, timer, HEADLINE, args.steps, args.warmup)
     log("headline done: %.2f us/launch" % (head["kernel_s"] * 1e6))
     extra = []
+    ceilings = None
+    head_cold = None
     if args.only == "all":
+        flush = Flush(torch)
+        head_cold = cold_fields(timer, raw_core_call(dsa.load(), case, *headline_tensors(torch, case),
+                                                     torch.cuda.current_stream().cuda_stream,
+                                                     case["softmax"]),
+                                flush, head["algo_bytes"])
+        ceilings = dict(copy_gbs=measure_copy(torch, timer), mfma_bf16_tflops=measure_mfma(dsa, torch, timer),
+                        note="measured: a 1 GiB device copy (read + write bytes / time) and "
+                             "dcn_mfma_probe (dense bf16 MFMAs on register operands)")
+        log("ceilings: copy %.0f GB/s, mfma %.0f TFLOP/s" % (ceilings["copy_gbs"],
+                                                             ceilings["mfma_bf16_tflops"]))
         for nm in ["dcnv4_f32_n1_32x32_g4c16", "dcnv3_f32_n8_56x56_g4c16_softmax"]:
-            r, _ = bench_core(dsa, torch, timer, nm, 200, 20)
+            r, _ = bench_core(dsa, torch, timer, nm, 200, 20, flush=flush)
             extra.append(r)
             log("%s done" % nm)
         extra.append(bench_core_packed(dsa, torch, timer, HEADLINE, 200, 20))
         log("packed offset+mask done")
         extra.append(bench_core_bwd(dsa, torch, timer, HEADLINE, 100, 10))
         log("core backward done")
-        extra.append(bench_v2(dsa, torch, timer, 100, 10))
+        r = bench_v2(dsa, torch, timer, 100, 10, flush=flush)
+        r["mfma_frac_of_probe"] = r["tflops"] / ceilings["mfma_bf16_tflops"]
+        extra.append(r)
         log("dcnv2 done")
         extra.append(bench_v2_bwd(dsa, torch, timer, 50, 5))
         log("dcnv2 backward done")
-        extra.append(bench_agg(dsa, torch, timer, 100, 10, softmax=True))
-        extra.append(bench_agg(dsa, torch, timer, 100, 10, softmax=False))
+        extra.append(bench_agg(dsa, torch, timer, 100, 10, softmax=True, flush=flush))
+        extra.append(bench_agg(dsa, torch, timer, 100, 10, softmax=False, flush=flush))
         extra.append(bench_agg_bwd(dsa, torch, timer, 20, 3))
         log("aggregation done")
         extra.append(bench_roi(dsa, torch, timer, 100, 10))
@@ -476,6 +638,9 @@ def main():
         for r in extra:
             r["kernel_us"] = round(r.pop("kernel_s") * 1e6, 2)
             r["wall_us"] = round(r.pop("wall_s") * 1e6, 2)
+            if "gbs" in r:
+                r["frac_of_measured_copy"] = r["gbs"] / ceilings["copy_gbs"]
+        del flush
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -502,13 +667,16 @@ def main():
                    "groups": 16, "group_channels": 16, "kernel": "3x3", "stride": 1, "pad": 1,
                    "dilation": 1, "storage": "x/out fp16, offsets/masks fp32",
                    "taps_per_step": head["taps"], "kernel_us": round(head["kernel_s"] * 1e6, 2),
-                   "kernel_taps_per_s": head["taps_per_s"]},
+                   "kernel_taps_per_s": head["taps_per_s"],
+                   "cold": head_cold},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
                      "algo_bytes_per_launch": head["algo_bytes"],
                      "kernel": "dcn_core_tile_kernel (fp16, 3x3, 16x16-pixel x 2-group LDS halo tiles)",
                      "source_hash": source_hash(CORE_SOURCES)},
+        "ceilings": ceilings,
+        "roofline_vs_measured_copy": (achieved / ceilings["copy_gbs"]) if ceilings else None,
         "cpu_baseline": cpu,
         "other_ops": extra,
     }

@@ -38,7 +38,7 @@ EXPORTS = ("dcn_core_forward", "dcn_core_forward_packed", "dcn_core_backward_wor
            "dcn_core_backward_workspace_bytes_path", "dcn_core_backward_path",
            "deform_agg_backward_workspace_bytes_path", "deform_agg_backward_path",
            "dcn_v2_noalloc_bytes", "dcn_v2_forward_noalloc",
-           "dcn_status_string", "dcn_last_hip_error")
+           "dcn_mfma_probe", "dcn_status_string", "dcn_last_hip_error")
 
 
 class DcnError(RuntimeError):
@@ -103,6 +103,8 @@ def load(path: str | None = None):
     lib.dcn_v2_noalloc_bytes.argtypes = [i] * 15
     lib.dcn_v2_forward_noalloc.restype = i
     lib.dcn_v2_forward_noalloc.argtypes = [vp] * 5 + [i] * 15 + [i, vp]
+    lib.dcn_mfma_probe.restype = i
+    lib.dcn_mfma_probe.argtypes = [vp, i, i, vp]
     lib.deform_roi_pool_forward.restype = i
     lib.deform_roi_pool_forward.argtypes = [vp] * 4 + [i] * 7 + [f, f, i, vp]
     lib.dcn_status_string.restype = _c.c_char_p

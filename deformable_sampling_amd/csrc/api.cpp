@@ -586,4 +586,11 @@ dcn_status deform_roi_pool_forward(const void *x, const float *rois, const float
     return hip_status(dcn::launch_deform_roi_pool(a, stream));
 }
 
+dcn_status dcn_mfma_probe(float *sink, int blocks, int iters, hipStream_t stream) {
+    if (blocks <= 0 || iters < 0) return DCN_ERR_PARAM;
+    if (!sink) return DCN_ERR_NULL;
+    if (!aligned(sink, 4)) return DCN_ERR_ALIGN;
+    return hip_status(dcn::launch_mfma_probe(sink, blocks, iters, stream));
+}
+
 }  // extern "C"

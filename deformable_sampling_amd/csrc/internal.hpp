@@ -206,4 +206,8 @@ struct RoiLaunch {
 };
 hipError_t launch_deform_roi_pool(const RoiLaunch &a, hipStream_t stream);
 
+// MFMA rate probe (probe.hip): blocks of 256 threads, iters rounds of four
+// 32x32x16 bf16 MFMAs per wave; sink gets blocks*256 floats.
+hipError_t launch_mfma_probe(float *sink, int blocks, int iters, hipStream_t stream);
+
 }  // namespace dcn

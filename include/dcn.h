@@ -451,6 +451,16 @@ dcn_status deform_agg_backward_path(const void *feat, const int32_t *spatial_sha
                                     int cams, int scales, int G, int Cg, int softmax,
                                     dcn_dtype dtype, unsigned path, hipStream_t stream);
 
+/*
+ * Measurement probe, not part of any operation: `blocks` blocks of 256 threads each run
+ * `iters` rounds of four dense bf16 MFMAs (v_mfma_f32_32x32x16_bf16, 32768 flops each)
+ * per wavefront on register operands, with no memory traffic, and write one float per
+ * thread to sink [blocks*256] (device, fp32). Timed by the caller, it gives the
+ * sustained MFMA rate the DCNv2 contraction is compared with beside the published peak:
+ * flops = blocks * 4 waves * iters * 4 * 32768.
+ */
+dcn_status dcn_mfma_probe(float *sink, int blocks, int iters, hipStream_t stream);
+
 /* hipError_t of this thread's last DCN_ERR_HIP (0 if none). */
 int dcn_last_hip_error(void);
 

@@ -64,6 +64,8 @@ def _load():
                                         ctypes.c_double, _dp]
         lib.oracle_threads.restype = ctypes.c_int
         lib.oracle_threads.argtypes = []
+        lib.oracle_set_threads.restype = None
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_softmax.restype = None
         lib.oracle_softmax.argtypes = [_dp, _i64, _dp]
         lib.oracle_dcn_core.restype = ctypes.c_int
@@ -116,6 +118,11 @@ def _idx(sel):
 def threads() -> int:
     """OpenMP threads the oracle's loops use."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Set the OpenMP thread count of the oracle's loops (for single-thread timings)."""
+    _load().oracle_set_threads(int(n))
 
 
 def out_size(n, k, s, p, d):

@@ -114,6 +114,16 @@ int oracle_threads(void)
 #endif
 }
 
+/* Set the thread count of the parallel loops (n >= 1; for single-thread timings). */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 static int64_t out_size(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d)
 {
     return (in + 2 * p - d * (k - 1) - 1) / s + 1;

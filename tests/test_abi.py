@@ -402,3 +402,11 @@ def test_v2_noalloc_sizes_and_validation(lib):
     assert call(out=A + 1) == ALIGN
     assert call(N=0) == OK
     assert lib.dcn_last_hip_error() == 0
+
+
+def test_mfma_probe_validation(lib):
+    assert lib.dcn_mfma_probe(A, 0, 10, None) == PARAM
+    assert lib.dcn_mfma_probe(A, 4, -1, None) == PARAM
+    assert lib.dcn_mfma_probe(None, 4, 10, None) == NULL
+    assert lib.dcn_mfma_probe(A + 2, 4, 10, None) == ALIGN
+    assert lib.dcn_last_hip_error() == 0

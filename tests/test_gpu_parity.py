@@ -81,6 +81,16 @@ CORE_SWEEP = [
     ("f32_offset_scale", dict(N=1, H=10, W=11, G=2, C=8, offset_std=3.0, dtype="f32"), {"offset_scale": 0.37}),
     ("f32_wide_c320", dict(N=1, H=5, W=6, G=1, C=320, dtype="f32"), {}),
     ("f16_many_groups", dict(N=1, H=8, W=8, G=32, C=8, dtype="f16"), {}),
+    # more tiles than compute units, several tile rows per column: the band kernel
+    # (persistent blocks carrying window rows from band to band), 20- and 16-wide tiles,
+    # partial last bands and columns, softmax, no mask, far offsets, offset_scale, fp32
+    ("f16_bands_tw20", dict(N=12, H=70, W=60, G=8, C=16, dtype="f16", oob_frac=0.05,
+                            offset_std=3.0), {}),
+    ("f16_bands_tw16_softmax", dict(N=10, H=50, W=45, G=8, C=16, mask="logits", dtype="f16"), {}),
+    ("f16_bands_far_nomask", dict(N=12, H=34, W=41, G=8, C=16, offset_std=6.0, mask=None,
+                                  dtype="f16"), {"offset_scale": 0.7}),
+    ("f32_bands_c8", dict(N=12, H=40, W=40, G=8, C=8, dtype="f32", offset_std=3.0,
+                          oob_frac=0.05), {}),
 ]
 
 
