@@ -136,29 +136,20 @@ __global__ __launch_bounds__(256) void v2_im2col_kernel(const uint16_t *__restri
 //
 // Deform-im2col fused into the GEMM (implicit GEMM): the columns never reach memory.
 // A block computes all kFBM output channels of kFBN output pixels. The K loop runs
-// tap-major in steps of 64 channels of one tap (Cin_pad % 64 == 0). Per step:
-//  - A (weight rows, [kFBM][64]) comes from wp in memory, loaded two steps ahead into
-//    registers and written to one of two LDS buffers;
-//  - B ([kFBN pixels][64 channels]) is computed: each thread owns one (pixel, 8-channel
-//    chunk), gathers its four corners two steps ahead, and in the step before use forms
-//    m * bilinear in fp32 exactly as the deform-im2col stage does, rounds it to the
-//    input dtype and writes one 16-byte chunk of the B buffer;
-//  - 8 waves (4 along channels x 2 along pixels, 64 x 32 each) run the MFMAs.
-// Both operands sit in LDS as [row][8 chunks] with chunk cc stored at cc ^ ((row >> 1) & 7).
+// tap-major in steps of 64 channels of one tap (Cin_pad % 64 == 0); per step the
+// weight tile A ([kFBM][64]) and the column tile B ([kFBN pixels][64 channels], formed
+// as m * bilinear in fp32 exactly as the deform-im2col stage forms it, rounded to the
+// input type) sit in one of two LDS buffers as [row][8 chunks], chunk cc stored at
+// cc ^ ((row >> 1) & 7) (the 16 lanes of a fragment read hit 16 different 16-byte bank
+// groups).
 
 #ifndef DCN_V2_FUSED
 #define DCN_V2_FUSED 1
 #endif
 constexpr int kFBM = 256;                    // output channels per block
 constexpr int kFBN = 64;                     // output pixels per block
-constexpr int kFThreads = 512;               // one B chunk per thread per step
 constexpr int kFAChunks = kFBM * kBK / 8;    // 2048 16-byte chunks of A per step
 constexpr int kFBChunks = kFBN * kBK / 8;    // 512 of B
-constexpr int kFAPer = kFAChunks / kFThreads;  // A chunks per thread (4)
-#ifndef DCN_V2_FUSED_STAGES
-#define DCN_V2_FUSED_STAGES 2
-#endif
-constexpr int kFStages = DCN_V2_FUSED_STAGES;  // register stages of loads in flight
 
 struct FusedParams {
     int N, H, W, Ho, Wo, kw, sh, sw, ph, pw, dh, dw;
@@ -170,13 +161,33 @@ struct FusedParams {
     unsigned xt_bytes;  // all of xt
 };
 
+// --------------------------------------------------- fused, specialised waves --
+//
+// The same implicit GEMM with the waves of a block split by role, so that the column
+// arithmetic of one step runs on the VALUs while the MFMAs of the previous step run on
+// the matrix cores of the same SIMDs. A block (kFBM output channels x kFBN pixels) has
+// four MMA waves, one per SIMD, each owning 64 channels x 64 pixels (2 x 2 tiles of
+// 32 x 32, 16 MFMAs per K step), and eight producer waves, two per SIMD: per K step
+// they load the next weight tile into registers and gather the next column tile's
+// corners (DCN_V2_WS_STAGES steps ahead), form m * bilinear in fp32 as the deform-im2col stage
+// does, round it to the input type and write both tiles into the other LDS buffer.
+// One barrier per step hands the buffers over.
+constexpr int kWSConsumers = 4;                           // MMA waves
+constexpr int kWSProducers = 8;                           // producer waves
+constexpr int kWSThreads = 64 * (kWSConsumers + kWSProducers);
+constexpr int kWSPThreads = 64 * kWSProducers;            // 512: one B chunk each per step
+constexpr int kWSAPer = kFAChunks / kWSPThreads;          // A chunks per producer thread (4)
+#ifndef DCN_V2_WS_STAGES
+#define DCN_V2_WS_STAGES 2
+#endif
+
 template <class E>
-__global__ __launch_bounds__(kFThreads) void v2_fused_kernel(const uint16_t *__restrict__ xt,
-                                                             const float *__restrict__ offset,
-                                                             const float *__restrict__ mask,
-                                                             const uint16_t *__restrict__ wp,
-                                                             uint16_t *__restrict__ out,
-                                                             const FusedParams p) {
+__global__ __launch_bounds__(kWSThreads) void v2_ws_kernel(const uint16_t *__restrict__ xt,
+                                                           const float *__restrict__ offset,
+                                                           const float *__restrict__ mask,
+                                                           const uint16_t *__restrict__ wp,
+                                                           uint16_t *__restrict__ out,
+                                                           const FusedParams p) {
     __shared__ uint4 sA[2][kFAChunks];
     __shared__ uint4 sB[2][kFBChunks];
     extern __shared__ float smem[];  // offsets [kFBN][dg][K][2], then masks [kFBN][dg][K]
@@ -190,11 +201,11 @@ __global__ __launch_bounds__(kFThreads) void v2_fused_kernel(const uint16_t *__r
     const int m0 = mt * kFBM;
     const long long n0 = (long long)nt * kFBN;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const long long HWo = p.HWo;
 
-    // offsets and masks of this block's pixels (pixel-fastest: coalesced NCHW rows)
-    for (int i = tid; i < kFBN * per_pix * 2; i += kFThreads) {
+    for (int i = tid; i < kFBN * per_pix * 2; i += kWSThreads) {
         const int pl = i % kFBN, c = i / kFBN;
         const long long pg = n0 + pl;
         float v = 0.0f;
@@ -204,7 +215,7 @@ __global__ __launch_bounds__(kFThreads) void v2_fused_kernel(const uint16_t *__r
         }
         s_off[pl * per_pix * 2 + c] = v;
     }
-    for (int i = tid; i < kFBN * per_pix; i += kFThreads) {
+    for (int i = tid; i < kFBN * per_pix; i += kWSThreads) {
         const int pl = i % kFBN, c = i / kFBN;
         const long long pg = n0 + pl;
         float v = 1.0f;
@@ -215,8 +226,8 @@ __global__ __launch_bounds__(kFThreads) void v2_fused_kernel(const uint16_t *__r
         s_m[pl * per_pix + c] = v;
     }
     __syncthreads();
-    if (p.softmax) {  // softmax over K per (pixel, deformable group)
-        for (int i = tid; i < kFBN * p.dg; i += kFThreads) {
+    if (p.softmax) {
+        for (int i = tid; i < kFBN * p.dg; i += kWSThreads) {
             float *ml = s_m + i * K;
             float mx = -INFINITY;
             for (int k = 0; k < K; ++k) mx = fmaxf(mx, ml[k]);
@@ -225,187 +236,164 @@ __global__ __launch_bounds__(kFThreads) void v2_fused_kernel(const uint16_t *__r
             const float inv = 1.0f / sum;
             for (int k = 0; k < K; ++k) ml[k] = expf(ml[k] - mx) * inv;
         }
-        __syncthreads();
     }
-
-    // this thread's B item: pixel row br, chunk bc (channels cb*64 + bc*8 .. +8)
-    const int br = tid >> 3, bc = tid & 7;
-    const long long pg = n0 + br;
-    const bool pvalid = pg < p.P;
-    const long long pgc = pvalid ? pg : 0;
-    const int n = (int)(pgc / HWo);
-    const int rr = (int)(pgc - (long long)n * HWo);
-    const int ho = rr / p.Wo, wo = rr - (rr / p.Wo) * p.Wo;
-    // one resource over all of xt (wave-uniform); the image is part of the lane offset
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xt, p.xt_bytes);
-    const int img_off = n * p.H * p.W * p.Cin_pad;  // elements
-    const unsigned wp_bytes = (unsigned)((size_t)(p.Mp - m0) * p.Rp * 2);  // rows m0 .. Mp-1
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(wp + (size_t)m0 * p.Rp, wp_bytes);
-    const int bdst = br * 8 + (bc ^ ((br >> 1) & 7));
-
-    // A chunk i of this thread: LDS position c = i*512 + tid, row c >> 3, logical
-    // chunk (c & 7) ^ ((row >> 1) & 7); rows past Mp read past the buffer's end (zeros)
-    int aoff[kFAPer];
-#pragma unroll
-    for (int i = 0; i < kFAPer; ++i) {
-        const int c = i * kFThreads + tid;
-        const int row = c >> 3, cc = (c & 7) ^ ((row >> 1) & 7);
-        aoff[i] = (m0 + row < p.Mp) ? (row * p.Rp + cc * 8) * 2 : (int)wp_bytes;
-    }
-
-    // corner byte offsets (this thread's channels folded in) and weights of one tap
-    struct TapB {
-        int o[4];
-        float w[4];
-    };
-    // Corners and weights of tap (i, j) for this thread's channels in 64-channel block cb
-    // (the block's byte offset cb*128 is added by the loads' scalar offset).
-    auto tap_of = [&](int k, int i, int j, int cb, TapB &t) __attribute__((always_inline)) {
-        const int grp = p.dg == 1 ? 0 : min((cb * 64 + bc * 8) / p.cpg, p.dg - 1);
-        const float *so = s_off + ((br * p.dg + grp) * K + k) * 2;
-        int y0, x0;
-        float fy, fx;
-        split_coord(ho * p.sh - p.ph + i * p.dh, so[1], y0, fy);
-        split_coord(wo * p.sw - p.pw + j * p.dw, so[0], x0, fx);
-        const float mk = pvalid ? s_m[(br * p.dg + grp) * K + k] : 0.0f;
-        const Tap tp = make_tap(y0, x0, fy, fx, mk, p.H, p.W, p.Cin_pad);
-        const int cl = img_off + bc * 8;
-        t.o[0] = (cl + tp.o00) * 2; t.o[1] = (cl + tp.o01) * 2;
-        t.o[2] = (cl + tp.o10) * 2; t.o[3] = (cl + tp.o11) * 2;
-        t.w[0] = tp.w00; t.w[1] = tp.w01; t.w[2] = tp.w10; t.w[3] = tp.w11;
-    };
-    struct Stage {
-        uint4 a[kFAPer];
-        uint4 g[4];
-        float w[4];
-    };
+    __syncthreads();
     const int NS = K * p.CB;
-    // Loads run in step order 0, 1, ..., NS-1 (then NS-1 again): counters track the next
-    // step's tap (k = i*kw + j) and 64-channel block cb, and the tap's corners and
-    // weights are recomputed only when the tap changes (every step when dg > 1, where a
-    // lane's group can change with the block).
-    int ld_n = 0, ld_s = 0, ld_k = 0, ld_i = 0, ld_j = 0, ld_cb = 0;
-    TapB tb;
-    auto load = [&](Stage &st) __attribute__((always_inline)) {
-        const int soff = ld_s * kBK * 2;  // this step's 64 columns of wp
+
+    if (wave >= kWSConsumers) {
+        // ------------------------------------------------------------ producers --
+        const int ptid = tid - 64 * kWSConsumers;
+        const int br = ptid >> 3, bc = ptid & 7;
+        const long long pg = n0 + br;
+        const bool pvalid = pg < p.P;
+        const long long pgc = pvalid ? pg : 0;
+        const int n = (int)(pgc / HWo);
+        const int rr = (int)(pgc - (long long)n * HWo);
+        const int ho = rr / p.Wo, wo = rr - (rr / p.Wo) * p.Wo;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(xt, p.xt_bytes);
+        const int img_off = n * p.H * p.W * p.Cin_pad;
+        const unsigned wp_bytes = (unsigned)((size_t)(p.Mp - m0) * p.Rp * 2);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(wp + (size_t)m0 * p.Rp, wp_bytes);
+        const int bdst = br * 8 + (bc ^ ((br >> 1) & 7));
+        int aoff[kWSAPer];
 #pragma unroll
-        for (int i = 0; i < kFAPer; ++i) st.a[i] = buffer_load<uint4>(ra, aoff[i], soff);
-        if (p.dg > 1 || ld_cb == 0) tap_of(ld_k, ld_i, ld_j, ld_cb, tb);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            st.g[c] = buffer_load<uint4>(rx, tb.o[c], ld_cb * kBK * 2);
-            st.w[c] = tb.w[c];
+        for (int i = 0; i < kWSAPer; ++i) {
+            const int c = i * kWSPThreads + ptid;
+            const int row = c >> 3, cc = (c & 7) ^ ((row >> 1) & 7);
+            aoff[i] = (m0 + row < p.Mp) ? (row * p.Rp + cc * 8) * 2 : (int)wp_bytes;
         }
-        if (ld_n < NS - 1) {  // after the last step, further loads repeat it (unused)
-            ++ld_n;
-            ++ld_s;
-            if (++ld_cb == p.CB) {
-                ld_cb = 0;
-                ++ld_k;
-                if (++ld_j == p.kw) {
-                    ld_j = 0;
-                    ++ld_i;
+        struct Stage {
+            uint4 a[kWSAPer];
+            uint4 g[4];
+            float w[4];
+        };
+        int ld_n = 0, ld_s = 0, ld_k = 0, ld_i = 0, ld_j = 0, ld_cb = 0;
+        int to[4];
+        float tw[4];
+        auto load = [&](Stage &st) __attribute__((always_inline)) {
+            const int soff = ld_s * kBK * 2;
+#pragma unroll
+            for (int i = 0; i < kWSAPer; ++i) st.a[i] = buffer_load<uint4>(ra, aoff[i], soff);
+            if (p.dg > 1 || ld_cb == 0) {
+                const int grp = p.dg == 1 ? 0 : min((ld_cb * 64 + bc * 8) / p.cpg, p.dg - 1);
+                const float *so = s_off + ((br * p.dg + grp) * K + ld_k) * 2;
+                int y0, x0;
+                float fy, fx;
+                split_coord(ho * p.sh - p.ph + ld_i * p.dh, so[1], y0, fy);
+                split_coord(wo * p.sw - p.pw + ld_j * p.dw, so[0], x0, fx);
+                const float mk = pvalid ? s_m[(br * p.dg + grp) * K + ld_k] : 0.0f;
+                const Tap tp = make_tap(y0, x0, fy, fx, mk, p.H, p.W, p.Cin_pad);
+                const int cl = img_off + bc * 8;
+                to[0] = (cl + tp.o00) * 2; to[1] = (cl + tp.o01) * 2;
+                to[2] = (cl + tp.o10) * 2; to[3] = (cl + tp.o11) * 2;
+                tw[0] = tp.w00; tw[1] = tp.w01; tw[2] = tp.w10; tw[3] = tp.w11;
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                st.g[c] = buffer_load<uint4>(rx, to[c], ld_cb * kBK * 2);
+                st.w[c] = tw[c];
+            }
+            if (ld_n < NS - 1) {
+                ++ld_n;
+                ++ld_s;
+                if (++ld_cb == p.CB) {
+                    ld_cb = 0;
+                    ++ld_k;
+                    if (++ld_j == p.kw) {
+                        ld_j = 0;
+                        ++ld_i;
+                    }
                 }
             }
+        };
+        auto fill = [&](const Stage &st, int buf) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < kWSAPer; ++i) sA[buf][i * kWSPThreads + ptid] = st.a[i];
+            float acc[kVec];
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) acc[e] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float f[kVec];
+                load_f32<E, kVec>(reinterpret_cast<const typename E::bits *>(&st.g[c]), f);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) acc[e] = fmaf(st.w[c], f[e], acc[e]);
+            }
+            typename E::bits b[kVec];
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) b[e] = from_f32(E{}, acc[e]);
+            uint4 v;
+            __builtin_memcpy(&v, b, 16);
+            sB[buf][bdst] = v;
+        };
+        constexpr int NST = DCN_V2_WS_STAGES;
+        Stage st[NST];
+#pragma unroll
+        for (int i = 0; i < NST; ++i) load(st[i]);
+        fill(st[0], 0);
+        __syncthreads();  // step 0's tiles are in buffer 0
+        for (int s = 0; s < NS; s += NST) {
+#pragma unroll
+            for (int u = 0; u < NST; ++u) {
+                if (s + u >= NS) break;
+                // buffer (s+u)&1 is being read by the MMA waves; fill the other
+                load(st[u]);  // step min(s + u + NST, NS - 1)
+                if (s + u + 1 < NS) fill(st[(u + 1) % NST], (s + u + 1) & 1);
+                __syncthreads();
+            }
         }
-    };
-    auto fill = [&](const Stage &st, int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < kFAPer; ++i) sA[buf][i * kFThreads + tid] = st.a[i];
-        // m * bilinear of 8 channels in fp32, in the deform-im2col stage's order
-        float acc[kVec];
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) acc[e] = 0.0f;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            float f[kVec];
-            load_f32<E, kVec>(reinterpret_cast<const typename E::bits *>(&st.g[c]), f);
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) acc[e] = fmaf(st.w[c], f[e], acc[e]);
-        }
-        typename E::bits b[kVec];
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) b[e] = from_f32(E{}, acc[e]);
-        uint4 v;
-        __builtin_memcpy(&v, b, 16);
-        sB[buf][bdst] = v;
-    };
+        return;
+    }
 
-    f32x16_t acc[2];
+    // ---------------------------------------------------------------- MMA waves --
+    f32x16_t acc[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[a][r] = 0.0f;
-    const int wm = wave & 3, wn = wave >> 2;  // 4 x 2 waves, 64 channels x 32 pixels each
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
     const int frow = lane & 31, fhalf = lane >> 5;
-    // All 12 fragments of the step are read first; the empty asm takes them as in/out
-    // operands, so the MFMAs (which use its outputs) start after a single wait instead of
-    // each waiting for its own reads.
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
-    auto mma = [&](int buf) __attribute__((always_inline)) {
-        const v4u *sa = reinterpret_cast<const v4u *>(sA[buf]);
-        const v4u *sb = reinterpret_cast<const v4u *>(sB[buf]);
-        v4u fa[4][2], fb[4];
+    __syncthreads();  // step 0's tiles
+    for (int s = 0; s < NS; ++s) {
+        const v4u *sa = reinterpret_cast<const v4u *>(sA[s & 1]);
+        const v4u *sb = reinterpret_cast<const v4u *>(sB[s & 1]);
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
             const int cc = 2 * ks + fhalf;
-            const int rb = wn * 32 + frow;
-            fb[ks] = sb[rb * 8 + (cc ^ ((rb >> 1) & 7))];
+            v4u fa[2], fb[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const int ra_ = wm * 64 + t * 32 + frow;
-                fa[ks][t] = sa[ra_ * 8 + (cc ^ ((ra_ >> 1) & 7))];
+                const int ra_ = wave * 64 + t * 32 + frow;
+                fa[t] = sa[ra_ * 8 + (cc ^ ((ra_ >> 1) & 7))];
+                const int rb = t * 32 + frow;
+                fb[t] = sb[rb * 8 + (cc ^ ((rb >> 1) & 7))];
             }
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = mfma32<E>(__builtin_bit_cast(uint4, fa[a]), __builtin_bit_cast(uint4, fb[b]),
+                                          acc[a][b]);
         }
-        asm volatile("" : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fa[1][0]), "+v"(fa[1][1]),
-                          "+v"(fa[2][0]), "+v"(fa[2][1]), "+v"(fa[3][0]), "+v"(fa[3][1]),
-                          "+v"(fb[0]), "+v"(fb[1]), "+v"(fb[2]), "+v"(fb[3]));
-#pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks)
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-                acc[t] = mfma32<E>(__builtin_bit_cast(uint4, fa[ks][t]),
-                                   __builtin_bit_cast(uint4, fb[ks]), acc[t]);
-    };
-
-    // Step s: LDS buffers s & 1 hold step s; the NST register stages hold the next NST
-    // steps. Load step s + NST into the stage step s used, run step s's MFMAs, then fill
-    // the other buffers with step s + 1. Loads past the last step repeat it: no branches
-    // around loads, so the compiler's wait counts stay exact.
-    constexpr int NST = kFStages;
-    Stage st[NST];
-#pragma unroll
-    for (int i = 0; i < NST; ++i) load(st[i]);
-    fill(st[0], 0);
-    auto step = [&](int s, Stage &mine, Stage &next) __attribute__((always_inline)) {
         __syncthreads();
-        load(mine);  // step min(s + NST, NS - 1)
-        mma(s & 1);
-        if (s + 1 < NS) fill(next, (s + 1) & 1);
-    };
-    for (int s = 0; s < NS; s += NST) {
-        step(s, st[0], st[1 % NST]);
-        if (s + 1 >= NS) break;
-        step(s + 1, st[1 % NST], st[2 % NST]);
-        if constexpr (NST == 3) {
-            if (s + 2 >= NS) break;
-            step(s + 2, st[2], st[0]);
-        }
     }
-
     // epilogue: D[i][j] of a 32x32 tile sits in lane j + 32*((i/4)%2), register
     // 4*(i/8) + i%4; row i is an output channel, column j an output pixel
-    const long long po = n0 + wn * 32 + (lane & 31);
-    if (po < p.P) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const long long po = n0 + b * 32 + (lane & 31);
+        if (po >= p.P) continue;
         const long long nimg = po / HWo;
         const int hw = (int)(po - nimg * HWo);
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int co = m0 + wm * 64 + a * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int co = m0 + wave * 64 + a * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 if (co < p.Cout)
-                    out[((size_t)nimg * p.Cout + co) * HWo + hw] = from_f32(E{}, acc[a][r]);
+                    out[((size_t)nimg * p.Cout + co) * HWo + hw] = from_f32(E{}, acc[a][b][r]);
             }
         }
     }
@@ -427,8 +415,13 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     pp.tiles_c = (pl.Cin_pad + 63) / 64;
     pp.tiles_hw = (pp.HW + 63) / 64;
     pp.n_tr_blocks = a.N * pp.tiles_c * pp.tiles_hw;
-    const long long wchunks = (long long)pl.Mp * (pl.Rp / kVec);
-    const int nwb = a.weight ? (int)((wchunks + 255) / 256) : 0;  // no weight: columns only
+    // register transposes where the pixel rows are whole 16-byte vectors: one wave per
+    // 64 channels x 64 pixels, four waves per block
+    pp.reg = pp.vec;
+    pp.cgroups = (pl.Cin_pad + 63) / 64;
+    pp.hgroups = (pp.HW + 63) / 64;
+    if (pp.reg) pp.n_tr_blocks = (a.N * pp.cgroups * pp.hgroups + 3) / 4;
+    const int nwb = a.weight ? pl.Mp : 0;  // one block per weight row; no weight: columns only
     hipLaunchKernelGGL(v2_prep_kernel, dim3(pp.n_tr_blocks + nwb), dim3(256), 0, stream,
                        static_cast<const uint16_t *>(a.x), static_cast<const uint16_t *>(a.weight),
                        xt, wp, pp);
@@ -448,7 +441,7 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
         fp.Mtiles = (pl.Mp + kFBM - 1) / kFBM;
         fp.nblocks = (int)(fp.Mtiles * ((pl.P + kFBN - 1) / kFBN));
         fp.xt_bytes = (unsigned)((size_t)a.N * a.H * a.W * pl.Cin_pad * 2);
-        hipLaunchKernelGGL(v2_fused_kernel<E>, dim3(fp.nblocks), dim3(kFThreads), fused_lds, stream, xt,
+        hipLaunchKernelGGL(v2_ws_kernel<E>, dim3(fp.nblocks), dim3(kWSThreads), fused_lds, stream, xt,
                            a.offset, a.mask, wp, static_cast<uint16_t *>(a.out), fp);
         return hipGetLastError();
     }

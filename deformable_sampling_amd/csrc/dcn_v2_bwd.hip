@@ -483,6 +483,7 @@ hipError_t launch_e(const V2BwdLaunch &a, hipStream_t stream) {
         pp.N = a.N; pp.Cin = C; pp.HW = hw; pp.Cin_pad = Cpad;
         pp.vec = (hw % kVec == 0) && ((uintptr_t)src % 16 == 0);
         pp.Mp = 0; pp.Rp = kVec;  // no weight blocks
+        pp.reg = 0;
         pp.tiles_c = (Cpad + 63) / 64;
         pp.tiles_hw = (hw + 63) / 64;
         pp.n_tr_blocks = a.N * pp.tiles_c * pp.tiles_hw;

@@ -17,8 +17,10 @@ long long round_up(long long v, long long m) { return (v + m - 1) / m * m; }
 struct PrepParams {
     int N, Cin, HW, Cin_pad;
     int vec;  // 16-byte transpose path: HW % 8 == 0 and x 16-byte aligned
+    int reg;  // register transpose (implies vec): blocks of 4 waves, each wave 64 x 64
+    int cgroups, hgroups;  // register transpose: 64-channel and 64-pixel groups per image
     int Cout, K, Mp, Rp;
-    int n_tr_blocks;  // blocks doing the transpose; the rest permute the weight
+    int n_tr_blocks;  // blocks doing the transpose; the rest (Mp of them) permute the weight
     int tiles_c, tiles_hw;
 };
 
@@ -29,6 +31,38 @@ __global__ __launch_bounds__(256) void v2_prep_kernel(const uint16_t *__restrict
                                                       uint16_t *__restrict__ wp, PrepParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // [channel][pixel], 144-byte rows
     const int b = blockIdx.x;
+    if (b < p.n_tr_blocks && p.reg) {
+        // 8 x 8 transposes in registers: lane (cl, hl) of a wave loads the 8 channel rows
+        // cb*8..+7 over the 8 pixels hb*8..+7 (16 bytes each; the wave's 8 lanes of one
+        // row read 128 contiguous bytes), swaps 16-bit halves with byte permutes, and
+        // stores 8 pixels of 8 channels (8 lanes write 128 contiguous bytes of a pixel).
+        const int wave = b * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+        const int hg = wave % p.hgroups, cg = (wave / p.hgroups) % p.cgroups;
+        const int n = wave / (p.hgroups * p.cgroups);
+        if (n >= p.N) return;  // no barrier in this path
+        const int cb = cg * 8 + (lane & 7), hb = hg * 8 + (lane >> 3);
+        if (cb * 8 >= p.Cin_pad || hb * 8 >= p.HW) return;
+        const uint16_t *xn = x + (size_t)n * p.Cin * p.HW + (size_t)hb * 8;
+        uint4 r[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = cb * 8 + i;
+            r[i] = c < p.Cin ? *reinterpret_cast<const uint4 *>(xn + (size_t)c * p.HW) : make_uint4(0, 0, 0, 0);
+        }
+        uint16_t *dst = xt + ((size_t)n * p.HW + (size_t)hb * 8) * p.Cin_pad + cb * 8;
+        auto dw = [](const uint4 &v, int d) { return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w; };
+#pragma unroll
+        for (int px = 0; px < 8; ++px) {
+            // pixel px sits in dword px/2 of every row, low half for even px
+            const unsigned sel = (px & 1) ? 0x07060302u : 0x05040100u;
+            unsigned o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = __builtin_amdgcn_perm(dw(r[2 * q + 1], px >> 1), dw(r[2 * q], px >> 1), sel);
+            *reinterpret_cast<uint4 *>(dst + (size_t)px * p.Cin_pad) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        return;
+    }
     if (b < p.n_tr_blocks) {
         const int tc = b % p.tiles_c;
         const int th = (b / p.tiles_c) % p.tiles_hw;
@@ -75,22 +109,42 @@ __global__ __launch_bounds__(256) void v2_prep_kernel(const uint16_t *__restrict
         }
         return;
     }
-    // weight: wp[co][k*Cin_pad + ci] = w[co][ci][k]; 8 consecutive r per thread
-    const long long t = (long long)(b - p.n_tr_blocks) * 256 + threadIdx.x;
-    const int rv = p.Rp / kVec;
-    if (t >= (long long)p.Mp * rv) return;
-    const int co = (int)(t / rv);
-    const int r0 = (int)(t % rv) * kVec;
-    // Cin_pad is a multiple of kVec: the 8 values share their tap k
-    const int k = r0 / p.Cin_pad, ci0 = r0 - k * p.Cin_pad;
-    const uint16_t *wk = w + ((size_t)co * p.Cin + ci0) * p.K + k;
-    const bool row = co < p.Cout && k < p.K;
-    uint16_t v[kVec];
+    // weight: wp[co][k*Cin_pad + ci] = w[co][ci][k], one row co per block. Rows of up
+    // to 4608 elements are first copied into LDS with coalesced 16-byte loads (the
+    // permutation then reads LDS at stride K), longer ones are read from memory directly;
+    // each thread writes 8 consecutive r as one 16-byte store.
+    const int co = b - p.n_tr_blocks;
+    if (co >= p.Mp) return;
+    const int rowlen = p.Cin * p.K;
+    const bool real = co < p.Cout;
+    const uint16_t *wr = w + (size_t)(real ? co : 0) * rowlen;
+    uint16_t *row = &tile[0][0];
+    const bool staged = real && rowlen <= 64 * 72;
+    if (staged) {
+        const bool v16 = rowlen % kVec == 0 && ((uintptr_t)wr % 16) == 0;
+        if (v16) {
+            for (int i = threadIdx.x; i < rowlen / kVec; i += 256)
+                reinterpret_cast<uint4 *>(row)[i] = reinterpret_cast<const uint4 *>(wr)[i];
+        } else {
+            for (int i = threadIdx.x; i < rowlen; i += 256) row[i] = wr[i];
+        }
+    }
+    __syncthreads();
+    for (int r0 = threadIdx.x * kVec; r0 < p.Rp; r0 += 256 * kVec) {
+        // Cin_pad is a multiple of kVec: the 8 values share their tap k
+        const int k = r0 / p.Cin_pad, ci0 = r0 - k * p.Cin_pad;
+        uint16_t v[kVec];
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) v[i] = (row && ci0 + i < p.Cin) ? wk[(size_t)i * p.K] : (uint16_t)0;
-    uint4 o;
-    __builtin_memcpy(&o, v, 16);
-    *reinterpret_cast<uint4 *>(wp + (size_t)co * p.Rp + r0) = o;
+        for (int i = 0; i < kVec; ++i) {
+            const int ci = ci0 + i;
+            const bool in = real && k < p.K && ci < p.Cin;
+            const int e = in ? ci * p.K + k : 0;
+            v[i] = in ? (staged ? row[e] : wr[e]) : (uint16_t)0;
+        }
+        uint4 o;
+        __builtin_memcpy(&o, v, 16);
+        *reinterpret_cast<uint4 *>(wp + (size_t)co * p.Rp + r0) = o;
+    }
 }
 
 // ------------------------------------------------------------------- gemm --
