@@ -137,18 +137,16 @@ __global__ __launch_bounds__(256) void v2_im2col_kernel(const uint16_t *__restri
 // Deform-im2col fused into the GEMM (implicit GEMM): the columns never reach memory.
 // A block computes all kFBM output channels of kFBN output pixels. The K loop runs
 // tap-major in steps of 64 channels of one tap (Cin_pad % 64 == 0); per step the
-// weight tile A ([kFBM][64]) and the column tile B ([kFBN pixels][64 channels], formed
-// as m * bilinear in fp32 exactly as the deform-im2col stage forms it, rounded to the
-// input type) sit in one of two LDS buffers as [row][8 chunks], chunk cc stored at
-// cc ^ ((row >> 1) & 7) (the 16 lanes of a fragment read hit 16 different 16-byte bank
-// groups).
+// column tile B ([kFBN pixels][64 channels], formed as m * bilinear in fp32 exactly as
+// the deform-im2col stage forms it, rounded to the input type) sits in one of two LDS
+// buffers as [pixel][8 chunks], chunk cc stored at cc ^ ((pixel >> 1) & 7) (the 16
+// lanes of a fragment read hit 16 different 16-byte bank groups).
 
 #ifndef DCN_V2_FUSED
 #define DCN_V2_FUSED 1
 #endif
 constexpr int kFBM = 256;                    // output channels per block
 constexpr int kFBN = 64;                     // output pixels per block
-constexpr int kFAChunks = kFBM * kBK / 8;    // 2048 16-byte chunks of A per step
 constexpr int kFBChunks = kFBN * kBK / 8;    // 512 of B
 
 struct FusedParams {
@@ -167,19 +165,32 @@ struct FusedParams {
 // arithmetic of one step runs on the VALUs while the MFMAs of the previous step run on
 // the matrix cores of the same SIMDs. A block (kFBM output channels x kFBN pixels) has
 // four MMA waves, one per SIMD, each owning 64 channels x 64 pixels (2 x 2 tiles of
-// 32 x 32, 16 MFMAs per K step), and eight producer waves, two per SIMD: per K step
-// they load the next weight tile into registers and gather the next column tile's
-// corners (DCN_V2_WS_STAGES steps ahead), form m * bilinear in fp32 as the deform-im2col stage
-// does, round it to the input type and write both tiles into the other LDS buffer.
-// One barrier per step hands the buffers over.
+// 32 x 32, 16 MFMAs per K step), and eight producer waves, two per SIMD.
+//   - The MMA waves read their weight fragments straight from memory (L2: every block
+//     reads the same permuted weight) into registers, one K step ahead, in the
+//     operand layout of the MFMA: the weight never passes through LDS.
+//   - Per K step the producers gather the column tile's corners DCN_V2_WS_STAGES steps
+//     ahead, form m * bilinear in fp32 as the deform-im2col stage does, round it to
+//     the input type and write it into one of two LDS buffers.
+// One barrier per step hands the column buffers over. The barrier carries no memory
+// fence: LDS writes are complete (lgkmcnt(0)) before it, and the weight loads still in
+// flight are waited for only where their registers are used.
 constexpr int kWSConsumers = 4;                           // MMA waves
 constexpr int kWSProducers = 8;                           // producer waves
 constexpr int kWSThreads = 64 * (kWSConsumers + kWSProducers);
 constexpr int kWSPThreads = 64 * kWSProducers;            // 512: one B chunk each per step
-constexpr int kWSAPer = kFAChunks / kWSPThreads;          // A chunks per producer thread (4)
+static_assert(kWSPThreads == kFBChunks, "one column chunk per producer thread and step");
 #ifndef DCN_V2_WS_STAGES
 #define DCN_V2_WS_STAGES 2
 #endif
+
+// Barrier after this wave's LDS accesses have completed; global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 template <class E>
 __global__ __launch_bounds__(kWSThreads) void v2_ws_kernel(const uint16_t *__restrict__ xt,
@@ -188,7 +199,6 @@ __global__ __launch_bounds__(kWSThreads) void v2_ws_kernel(const uint16_t *__res
                                                            const uint16_t *__restrict__ wp,
                                                            uint16_t *__restrict__ out,
                                                            const FusedParams p) {
-    __shared__ uint4 sA[2][kFAChunks];
     __shared__ uint4 sB[2][kFBChunks];
     extern __shared__ float smem[];  // offsets [kFBN][dg][K][2], then masks [kFBN][dg][K]
     const int K = p.K;
@@ -252,28 +262,15 @@ __global__ __launch_bounds__(kWSThreads) void v2_ws_kernel(const uint16_t *__res
         const int ho = rr / p.Wo, wo = rr - (rr / p.Wo) * p.Wo;
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(xt, p.xt_bytes);
         const int img_off = n * p.H * p.W * p.Cin_pad;
-        const unsigned wp_bytes = (unsigned)((size_t)(p.Mp - m0) * p.Rp * 2);
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(wp + (size_t)m0 * p.Rp, wp_bytes);
         const int bdst = br * 8 + (bc ^ ((br >> 1) & 7));
-        int aoff[kWSAPer];
-#pragma unroll
-        for (int i = 0; i < kWSAPer; ++i) {
-            const int c = i * kWSPThreads + ptid;
-            const int row = c >> 3, cc = (c & 7) ^ ((row >> 1) & 7);
-            aoff[i] = (m0 + row < p.Mp) ? (row * p.Rp + cc * 8) * 2 : (int)wp_bytes;
-        }
         struct Stage {
-            uint4 a[kWSAPer];
             uint4 g[4];
             float w[4];
         };
-        int ld_n = 0, ld_s = 0, ld_k = 0, ld_i = 0, ld_j = 0, ld_cb = 0;
+        int ld_n = 0, ld_k = 0, ld_i = 0, ld_j = 0, ld_cb = 0;
         int to[4];
         float tw[4];
         auto load = [&](Stage &st) __attribute__((always_inline)) {
-            const int soff = ld_s * kBK * 2;
-#pragma unroll
-            for (int i = 0; i < kWSAPer; ++i) st.a[i] = buffer_load<uint4>(ra, aoff[i], soff);
             if (p.dg > 1 || ld_cb == 0) {
                 const int grp = p.dg == 1 ? 0 : min((ld_cb * 64 + bc * 8) / p.cpg, p.dg - 1);
                 const float *so = s_off + ((br * p.dg + grp) * K + ld_k) * 2;
@@ -295,7 +292,6 @@ __global__ __launch_bounds__(kWSThreads) void v2_ws_kernel(const uint16_t *__res
             }
             if (ld_n < NS - 1) {
                 ++ld_n;
-                ++ld_s;
                 if (++ld_cb == p.CB) {
                     ld_cb = 0;
                     ++ld_k;
@@ -307,8 +303,6 @@ __global__ __launch_bounds__(kWSThreads) void v2_ws_kernel(const uint16_t *__res
             }
         };
         auto fill = [&](const Stage &st, int buf) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < kWSAPer; ++i) sA[buf][i * kWSPThreads + ptid] = st.a[i];
             float acc[kVec];
 #pragma unroll
             for (int e = 0; e < kVec; ++e) acc[e] = 0.0f;
@@ -331,7 +325,7 @@ __global__ __launch_bounds__(kWSThreads) void v2_ws_kernel(const uint16_t *__res
 #pragma unroll
         for (int i = 0; i < NST; ++i) load(st[i]);
         fill(st[0], 0);
-        __syncthreads();  // step 0's tiles are in buffer 0
+        lds_barrier();  // step 0's column tile is in buffer 0
         for (int s = 0; s < NS; s += NST) {
 #pragma unroll
             for (int u = 0; u < NST; ++u) {
@@ -339,13 +333,33 @@ __global__ __launch_bounds__(kWSThreads) void v2_ws_kernel(const uint16_t *__res
                 // buffer (s+u)&1 is being read by the MMA waves; fill the other
                 load(st[u]);  // step min(s + u + NST, NS - 1)
                 if (s + u + 1 < NS) fill(st[(u + 1) % NST], (s + u + 1) & 1);
-                __syncthreads();
+                lds_barrier();
             }
         }
         return;
     }
 
     // ---------------------------------------------------------------- MMA waves --
+    // Weight fragment of tile t, K sub-step ks of step s: lane l holds row
+    // m0 + wave*64 + t*32 + (l & 31), elements [s*64 + ks*16 + (l >> 5)*8, +8), which the
+    // prep stored (fragment order) as 1 KB per (32-row block, s, ks) with lane l's 16
+    // bytes at 16 l: each load is one contiguous 1 KB. Rows past Mp read zeros.
+    const int frow = lane & 31, fhalf = lane >> 5;
+    const unsigned wp_bytes = (unsigned)((size_t)(p.Mp - m0) * p.Rp * 2);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(wp + (size_t)m0 * p.Rp, wp_bytes);
+    int aoff[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) aoff[t] = (wave * 2 + t) * p.Rp * 64 + lane * 16;
+    // two register sets of fragments, used in turn: the loads of step s+1 are issued
+    // as step s begins (past the last step a set reloads the last step's fragments:
+    // unconditional loads keep the compiler's count of loads in flight exact)
+    uint4 fa[2][2][4];  // [set][tile][ks]
+    auto load_a = [&](uint4 (&f)[2][4], int s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) f[t][ks] = buffer_load<uint4>(ra, aoff[t], (s * 4 + ks) * 1024);
+    };
     f32x16_t acc[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -353,20 +367,15 @@ __global__ __launch_bounds__(kWSThreads) void v2_ws_kernel(const uint16_t *__res
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-    const int frow = lane & 31, fhalf = lane >> 5;
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
-    __syncthreads();  // step 0's tiles
-    for (int s = 0; s < NS; ++s) {
-        const v4u *sa = reinterpret_cast<const v4u *>(sA[s & 1]);
+    auto mma = [&](const uint4 (&f)[2][4], int s) __attribute__((always_inline)) {
         const v4u *sb = reinterpret_cast<const v4u *>(sB[s & 1]);
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
             const int cc = 2 * ks + fhalf;
-            v4u fa[2], fb[2];
+            v4u fb[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const int ra_ = wave * 64 + t * 32 + frow;
-                fa[t] = sa[ra_ * 8 + (cc ^ ((ra_ >> 1) & 7))];
                 const int rb = t * 32 + frow;
                 fb[t] = sb[rb * 8 + (cc ^ ((rb >> 1) & 7))];
             }
@@ -374,10 +383,27 @@ __global__ __launch_bounds__(kWSThreads) void v2_ws_kernel(const uint16_t *__res
             for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
-                    acc[a][b] = mfma32<E>(__builtin_bit_cast(uint4, fa[a]), __builtin_bit_cast(uint4, fb[b]),
-                                          acc[a][b]);
+                    acc[a][b] = mfma32<E>(f[a][ks], __builtin_bit_cast(uint4, fb[b]), acc[a][b]);
         }
-        __syncthreads();
+    };
+    load_a(fa[0], 0);
+    lds_barrier();  // step 0's column tile
+    int s = 0;
+    // (the empty asm statements keep the loads ahead of the step's LDS reads, so the
+    // two sets stay distinct)
+    for (; s + 1 < NS; s += 2) {
+        load_a(fa[1], s + 1);
+        asm volatile("" ::: "memory");
+        mma(fa[0], s);
+        lds_barrier();
+        load_a(fa[0], s + 2 < NS ? s + 2 : s + 1);
+        asm volatile("" ::: "memory");
+        mma(fa[1], s + 1);
+        lds_barrier();
+    }
+    if (s < NS) {  // odd step count: the last step's fragments are in set 0
+        mma(fa[0], s);
+        lds_barrier();
     }
     // epilogue: D[i][j] of a 32x32 tile sits in lane j + 32*((i/4)%2), register
     // 4*(i/8) + i%4; row i is an output channel, column j an output pixel
@@ -421,6 +447,8 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     pp.cgroups = (pl.Cin_pad + 63) / 64;
     pp.hgroups = (pp.HW + 63) / 64;
     if (pp.reg) pp.n_tr_blocks = (a.N * pp.cgroups * pp.hgroups + 3) / 4;
+    const bool fused = v2_fused_applies(pl, a.dg, a.weight != nullptr);
+    pp.frag = fused ? 1 : 0;  // the fused kernel reads the weight in MFMA fragment order
     const int nwb = a.weight ? pl.Mp : 0;  // one block per weight row; no weight: columns only
     hipLaunchKernelGGL(v2_prep_kernel, dim3(pp.n_tr_blocks + nwb), dim3(256), 0, stream,
                        static_cast<const uint16_t *>(a.x), static_cast<const uint16_t *>(a.weight),
@@ -429,7 +457,7 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     if (err != hipSuccess) return err;
 
     const size_t fused_lds = (size_t)kFBN * a.dg * pl.K * 3 * sizeof(float);
-    if (v2_fused_applies(pl, a.dg, a.weight != nullptr)) {  // 2+3. deform-im2col fused into the GEMM
+    if (fused) {  // 2+3. deform-im2col fused into the GEMM
         FusedParams fp;
         fp.N = a.N; fp.H = a.H; fp.W = a.W; fp.Ho = pl.Ho; fp.Wo = pl.Wo; fp.kw = a.kw;
         fp.sh = a.sh; fp.sw = a.sw; fp.ph = a.ph; fp.pw = a.pw; fp.dh = a.dh; fp.dw = a.dw;

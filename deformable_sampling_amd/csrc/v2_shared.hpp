@@ -20,6 +20,7 @@ struct PrepParams {
     int reg;  // register transpose (implies vec): blocks of 4 waves, each wave 64 x 64
     int cgroups, hgroups;  // register transpose: 64-channel and 64-pixel groups per image
     int Cout, K, Mp, Rp;
+    int frag;         // weight in MFMA fragment order (see below) instead of rows [Mp][Rp]
     int n_tr_blocks;  // blocks doing the transpose; the rest (Mp of them) permute the weight
     int tiles_c, tiles_hw;
 };
@@ -112,7 +113,11 @@ __global__ __launch_bounds__(256) void v2_prep_kernel(const uint16_t *__restrict
     // weight: wp[co][k*Cin_pad + ci] = w[co][ci][k], one row co per block. Rows of up
     // to 4608 elements are first copied into LDS with coalesced 16-byte loads (the
     // permutation then reads LDS at stride K), longer ones are read from memory directly;
-    // each thread writes 8 consecutive r as one 16-byte store.
+    // each thread writes 8 consecutive r as one 16-byte store. With frag set, the eight
+    // values (co, r0..r0+7), r0 = 64 s + 16 ks + 8 h, go to 16-byte slot
+    // (((co/32 * Rp/64 + s) * 4 + ks) * 2 + h) * 32 + co%32: the operand of one
+    // 32x32x16 MFMA (32 rows x 16 K values) is then 1 KB of consecutive memory, lane
+    // l's 16 bytes at 16 l.
     const int co = b - p.n_tr_blocks;
     if (co >= p.Mp) return;
     const int rowlen = p.Cin * p.K;
@@ -143,7 +148,13 @@ __global__ __launch_bounds__(256) void v2_prep_kernel(const uint16_t *__restrict
         }
         uint4 o;
         __builtin_memcpy(&o, v, 16);
-        *reinterpret_cast<uint4 *>(wp + (size_t)co * p.Rp + r0) = o;
+        size_t dst = (size_t)co * p.Rp + r0;
+        if (p.frag) {
+            const int c8 = r0 / kVec;  // s = c8 / 8, ks = (c8 / 2) % 4, h = c8 % 2
+            dst = (((((size_t)(co / 32) * (p.Rp / 64) + c8 / 8) * 4 + (c8 / 2) % 4) * 2 + c8 % 2) * 32 + co % 32) *
+                  kVec;
+        }
+        *reinterpret_cast<uint4 *>(wp + dst) = o;
     }
 }
 
