@@ -216,6 +216,12 @@ V2_SWEEP = [
     ("fused_k1x3", dict(N=1, Cin=64, H=9, W=10, Cout=8, kh=1, kw=3, pad=(0, 1), dtype="bf16")),
     ("fused_softmax_mask_none", dict(N=2, Cin=64, H=10, W=11, Cout=24, dg=2, mask=None,
                                      dtype="bf16"), dict(softmax=True)),
+    # Cin of 128 and 256: two and four 64-channel K steps per tap, with two groups of
+    # 128 channels, a 1x3 window (an odd number of steps) and the softmax
+    ("fused_wide_dg2", dict(N=1, Cin=256, H=7, W=9, Cout=32, dg=2, dtype="bf16")),
+    ("fused_wide_f16_k1x3", dict(N=1, Cin=128, H=6, W=10, Cout=48, kh=1, kw=3, pad=(0, 1),
+                                 dtype="f16")),
+    ("fused_wide_softmax", dict(N=2, Cin=128, H=9, W=8, Cout=72, mask="logits", dtype="bf16")),
 ]
 V2_SWEEP = [s if len(s) == 3 else s + ({},) for s in V2_SWEEP]
 
