@@ -281,7 +281,10 @@ def bench_core_bwd(dsa, torch, timer, name, iters, warmup):
                 frac=nbytes / kern / 1e9 / HBM_PEAK_GBS)
 
 
-def bench_v2(dsa, torch, timer, iters, warmup, flush=None):
+def bench_v2(dsa, torch, timer, iters, warmup, flush=None, prepacked=False):
+    """dcn_v2_forward on the 8x256x40x40 bf16 layer (prepacked: dcn_v2_forward_prepacked
+    with the weight packed once before the timed calls, as an inference layer whose
+    weight does not change would run)."""
     import workloads as wl
     name = "dcnv2_bf16_n8_c256_40x40"
     c = wl.make(name)
@@ -296,18 +299,32 @@ def bench_v2(dsa, torch, timer, iters, warmup, flush=None):
     args = (x.data_ptr(), off.data_ptr(), m.data_ptr(), w.data_ptr(), out.data_ptr(), ws.data_ptr(),
             need, N, Cin, H, W, Cout, 3, 3, 1, 1, 1, 1, 1, 1, 1, 0, 2, stream)
 
-    def call():
-        st = lib.dcn_v2_forward(*args)
-        if st:
-            raise RuntimeError("dcn_v2_forward status %d" % st)
+    if prepacked:
+        packed = dsa.dcn_v2_pack_weight(w)
+        pargs = (x.data_ptr(), off.data_ptr(), m.data_ptr(), packed.data_ptr(), packed.numel(),
+                 out.data_ptr(), ws.data_ptr(), need, N, Cin, H, W, Cout, 3, 3, 1, 1, 1, 1, 1, 1, 1, 0, 2,
+                 stream)
+
+        def call():
+            st = lib.dcn_v2_forward_prepacked(*pargs)
+            if st:
+                raise RuntimeError("dcn_v2_forward_prepacked status %d" % st)
+    else:
+        def call():
+            st = lib.dcn_v2_forward(*args)
+            if st:
+                raise RuntimeError("dcn_v2_forward status %d" % st)
     wall, kern = timer.run(call, iters, warmup)
     P = N * c["Ho"] * c["Wo"]
     flops = 2.0 * Cout * Cin * 9 * P
     nbytes = x.numel() * 2 + off.numel() * 4 + m.numel() * 4 + w.numel() * 2 + out.numel() * 2
-    r = dict(workload=name, taps=P * 9, channel_taps=P * 9 * Cin, algo_bytes=nbytes,
+    r = dict(workload=name + (" prepacked weight" if prepacked else ""), taps=P * 9,
+             channel_taps=P * 9 * Cin, algo_bytes=nbytes,
              flops=flops, wall_s=wall, kernel_s=kern, tflops=flops / kern / 1e12,
              mfma_frac=flops / kern / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-             note="two launches: layout prep, deform-im2col fused into the MFMA GEMM")
+             note=("two launches: x to channels-last, deform-im2col fused into the MFMA GEMM "
+                   "(weight packed once, outside the timed calls)" if prepacked else
+                   "two launches: layout prep (x and weight), deform-im2col fused into the MFMA GEMM"))
     if flush is not None:
         r.update(cold_fields(timer, call, flush, nbytes))
         r["cold_tflops"] = flops / (r["cold_kernel_us"] * 1e-6) / 1e12
@@ -540,7 +557,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["core", "all", "bwd", "aggbwd", "v2bwd", "c1", "c2", "v2",
+    ap.add_argument("--only", choices=["core", "all", "bwd", "aggbwd", "v2bwd", "c1", "c2", "v2", "v2p",
                                        "agg", "packed", "roi", "mfma"], default="all")
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
@@ -566,8 +583,8 @@ def main():
         r, _ = bench_core(dsa, torch, timer, nm, args.steps, args.warmup)
         log("%s: %.2f us/launch" % (nm, r["kernel_s"] * 1e6))
         return
-    if args.only == "v2":
-        r = bench_v2(dsa, torch, timer, args.steps, args.warmup)
+    if args.only in ("v2", "v2p"):
+        r = bench_v2(dsa, torch, timer, args.steps, args.warmup, prepacked=args.only == "v2p")
         log("dcnv2: %.2f us/call, %.0f TFLOP/s" % (r["kernel_s"] * 1e6, r["tflops"]))
         return
     if args.only == "agg":
@@ -623,9 +640,10 @@ def main():
         log("packed offset+mask done")
         extra.append(bench_core_bwd(dsa, torch, timer, HEADLINE, 100, 10))
         log("core backward done")
-        r = bench_v2(dsa, torch, timer, 100, 10, flush=flush)
-        r["mfma_frac_of_probe"] = r["tflops"] / ceilings["mfma_bf16_tflops"]
-        extra.append(r)
+        for pre in (False, True):
+            r = bench_v2(dsa, torch, timer, 100, 10, flush=flush, prepacked=pre)
+            r["mfma_frac_of_probe"] = r["tflops"] / ceilings["mfma_bf16_tflops"]
+            extra.append(r)
         log("dcnv2 done")
         extra.append(bench_v2_bwd(dsa, torch, timer, 50, 5))
         log("dcnv2 backward done")

@@ -38,6 +38,7 @@ EXPORTS = ("dcn_core_forward", "dcn_core_forward_packed", "dcn_core_backward_wor
            "dcn_core_backward_workspace_bytes_path", "dcn_core_backward_path",
            "deform_agg_backward_workspace_bytes_path", "deform_agg_backward_path",
            "dcn_v2_noalloc_bytes", "dcn_v2_forward_noalloc",
+           "dcn_v2_packed_weight_bytes", "dcn_v2_pack_weight", "dcn_v2_forward_prepacked",
            "dcn_mfma_probe", "dcn_status_string", "dcn_last_hip_error")
 
 
@@ -103,6 +104,12 @@ def load(path: str | None = None):
     lib.dcn_v2_noalloc_bytes.argtypes = [i] * 15
     lib.dcn_v2_forward_noalloc.restype = i
     lib.dcn_v2_forward_noalloc.argtypes = [vp] * 5 + [i] * 15 + [i, vp]
+    lib.dcn_v2_packed_weight_bytes.restype = _c.c_size_t
+    lib.dcn_v2_packed_weight_bytes.argtypes = [i] * 4
+    lib.dcn_v2_pack_weight.restype = i
+    lib.dcn_v2_pack_weight.argtypes = [vp, vp, _c.c_size_t] + [i] * 4 + [i, vp]
+    lib.dcn_v2_forward_prepacked.restype = i
+    lib.dcn_v2_forward_prepacked.argtypes = [vp, vp, vp, vp, _c.c_size_t, vp, vp, _c.c_size_t] + [i] * 15 + [i, vp]
     lib.dcn_mfma_probe.restype = i
     lib.dcn_mfma_probe.argtypes = [vp, i, i, vp]
     lib.deform_roi_pool_forward.restype = i
@@ -336,6 +343,61 @@ def dcn_v2_forward(x, offset, mask, weight, out=None, workspace=None, *, stride=
     _call("dcn_v2_forward", _ptr(x), _ptr(offset), _ptr(mask), _ptr(weight), _ptr(out),
           _ptr(workspace), workspace.numel() * workspace.element_size(), N, Cin, H, W, Cout, kh, kw,
           sh, sw, ph, pw, dh, dw, dg, int(bool(softmax)), _DTYPE_ID[x.dtype], _stream(stream))
+    return out
+
+
+def dcn_v2_packed_weight_bytes(Cout, Cin, kernel=(3, 3)):
+    """Bytes of the packed weight of a DCNv2 layer (0 if the sizes are invalid)."""
+    kh, kw = _pair(kernel)
+    return int(load().dcn_v2_packed_weight_bytes(Cout, Cin, kh, kw))
+
+
+def dcn_v2_pack_weight(weight, packed=None, stream=None):
+    """Permute weight [Cout,Cin,kh,kw] (bf16/fp16) once into the order the fused DCNv2
+    kernel reads; returns the packed buffer (uint8 device tensor) for
+    dcn_v2_forward_prepacked."""
+    _check(weight, "weight")
+    Cout, Cin, kh, kw = weight.shape
+    need = dcn_v2_packed_weight_bytes(Cout, Cin, (kh, kw))
+    if packed is None:
+        packed = torch.empty(max(need, 1), dtype=torch.uint8, device=weight.device)
+    _check(packed, "packed")
+    _call("dcn_v2_pack_weight", _ptr(weight), _ptr(packed), packed.numel() * packed.element_size(),
+          Cout, Cin, kh, kw, _DTYPE_ID[weight.dtype], _stream(stream))
+    return packed
+
+
+def dcn_v2_forward_prepacked(x, offset, mask, packed_weight, Cout, out=None, workspace=None, *,
+                             kernel=(3, 3), stride=1, pad=1, dilation=1, deform_groups=None,
+                             softmax=False, stream=None):
+    """dcn_v2_forward with a weight packed by dcn_v2_pack_weight (for Cout output channels
+    and the given kernel size). Returns out [N,Cout,Ho,Wo]."""
+    kh, kw = _pair(kernel)
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    dh, dw = _pair(dilation)
+    _check(x, "x")
+    _check(packed_weight, "packed_weight")
+    _check(offset, "offset", torch.float32)
+    _check(mask, "mask", torch.float32, allow_none=True)
+    N, Cin, H, W = x.shape
+    K = kh * kw
+    dg = deform_groups if deform_groups is not None else offset.shape[1] // (2 * K)
+    Ho, Wo = out_size(H, kh, sh, ph, dh), out_size(W, kw, sw, pw, dw)
+    if tuple(offset.shape) != (N, dg * K * 2, Ho, Wo):
+        raise ValueError("offset must be [N, dg*K*2, Ho, Wo]")
+    if mask is not None and tuple(mask.shape) != (N, dg * K, Ho, Wo):
+        raise ValueError("mask must be [N, dg*K, Ho, Wo]")
+    if out is None:
+        out = torch.empty((N, Cout, Ho, Wo), dtype=x.dtype, device=x.device)
+    _check(out, "out", x.dtype)
+    need = dcn_v2_workspace_bytes(N, Cin, H, W, Cout, (kh, kw), (sh, sw), (ph, pw), (dh, dw), x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _call("dcn_v2_forward_prepacked", _ptr(x), _ptr(offset), _ptr(mask), _ptr(packed_weight),
+          packed_weight.numel() * packed_weight.element_size(), _ptr(out), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), N, Cin, H, W, Cout, kh, kw, sh, sw, ph, pw,
+          dh, dw, dg, int(bool(softmax)), _DTYPE_ID[x.dtype], _stream(stream))
     return out
 
 

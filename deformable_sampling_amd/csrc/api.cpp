@@ -301,6 +301,7 @@ static dcn_status v2_check(const void *x, const float *offset, const float *mask
         out = nullptr;
     }
     a.x = x; a.offset = offset; a.mask = mask; a.weight = weight; a.out = out;
+    a.packed_weight = nullptr;
     a.workspace = nullptr;
     a.N = N; a.Cin = Cin; a.H = H; a.W = W; a.Cout = Cout; a.kh = kh; a.kw = kw;
     a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w; a.dh = dil_h; a.dw = dil_w;
@@ -336,6 +337,52 @@ dcn_status dcn_v2_forward(const void *x, const float *offset, const float *mask,
     return v2_call(x, offset, mask, weight, out, workspace, workspace_bytes, N, Cin, H, W, Cout, kh,
                    kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, deform_groups, softmax,
                    dtype, stream, false);
+}
+
+// The weight dimensions of a DCNv2 layer (Cin_pad, K, Rp, Mp) as plan_dcn_v2 sets them:
+// the plan of a one-pixel layer with the same weight.
+static bool v2_weight_plan(int Cout, int Cin, int kh, int kw, dcn::V2Plan &plan) {
+    if (Cout <= 0 || Cin <= 0 || kh <= 0 || kw <= 0 || kh * kw > 64) return false;
+    return dcn::plan_dcn_v2(1, Cin, kh, kw, Cout, kh, kw, 1, 1, 0, 0, 1, 1, DCN_BF16, plan);
+}
+
+size_t dcn_v2_packed_weight_bytes(int Cout, int Cin, int kh, int kw) {
+    dcn::V2Plan plan;
+    if (!v2_weight_plan(Cout, Cin, kh, kw, plan)) return 0;
+    return (size_t)plan.Mp * plan.Rp * 2;
+}
+
+dcn_status dcn_v2_pack_weight(const void *weight, void *packed, size_t packed_bytes, int Cout, int Cin,
+                              int kh, int kw, dcn_dtype dtype, hipStream_t stream) {
+    if (!valid_dtype(dtype) || dtype == DCN_F32) return DCN_ERR_DTYPE;
+    dcn::V2Plan plan;
+    if (!v2_weight_plan(Cout, Cin, kh, kw, plan)) return DCN_ERR_SHAPE;
+    if ((long long)plan.Mp * plan.Rp * 2 >= (1LL << 31)) return DCN_ERR_SHAPE;
+    if (!weight || !packed) return DCN_ERR_NULL;
+    if (!aligned(weight, 2) || !aligned(packed, 16)) return DCN_ERR_ALIGN;
+    if (packed_bytes < (size_t)plan.Mp * plan.Rp * 2) return DCN_ERR_WORKSPACE;
+    return hip_status(dcn::launch_dcn_v2_pack_weight(weight, packed, Cout, Cin, plan, stream));
+}
+
+dcn_status dcn_v2_forward_prepacked(const void *x, const float *offset, const float *mask,
+                                    const void *packed_weight, size_t packed_bytes, void *out,
+                                    void *workspace, size_t workspace_bytes, int N, int Cin, int H,
+                                    int W, int Cout, int kh, int kw, int stride_h, int stride_w,
+                                    int pad_h, int pad_w, int dil_h, int dil_w, int deform_groups,
+                                    int softmax, dcn_dtype dtype, hipStream_t stream) {
+    dcn::V2Launch a;
+    const dcn_status st = v2_check(x, offset, mask, packed_weight, out, N, Cin, H, W, Cout, kh, kw,
+                                   stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, deform_groups,
+                                   softmax, dtype, false, a);
+    if (st != DCN_OK || N == 0) return st;
+    if (!dcn::v2_fused_applies(a.plan, deform_groups, true)) return DCN_ERR_PARAM;
+    if (!aligned(packed_weight, 16)) return DCN_ERR_ALIGN;
+    if (packed_bytes < (size_t)a.plan.Mp * a.plan.Rp * 2) return DCN_ERR_WORKSPACE;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < a.plan.total)
+        return DCN_ERR_WORKSPACE;
+    a.packed_weight = packed_weight;
+    a.workspace = workspace;
+    return hip_status(dcn::launch_dcn_v2(a, stream));
 }
 
 dcn_status dcn_v2_im2col(const void *x, const float *offset, const float *mask, void *workspace,

@@ -430,6 +430,8 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     const V2Plan &pl = a.plan;
     char *ws = static_cast<char *>(a.workspace);
     uint16_t *xt = reinterpret_cast<uint16_t *>(ws + pl.off_xt);
+    // the fused kernel reads a pre-packed weight where the caller passes one
+    const uint16_t *wp_in = static_cast<const uint16_t *>(a.packed_weight);
     uint16_t *wp = reinterpret_cast<uint16_t *>(ws + pl.off_wp);
     uint16_t *col = reinterpret_cast<uint16_t *>(ws + pl.off_col);
 
@@ -449,7 +451,8 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     if (pp.reg) pp.n_tr_blocks = (a.N * pp.cgroups * pp.hgroups + 3) / 4;
     const bool fused = v2_fused_applies(pl, a.dg, a.weight != nullptr);
     pp.frag = fused ? 1 : 0;  // the fused kernel reads the weight in MFMA fragment order
-    const int nwb = a.weight ? pl.Mp : 0;  // one block per weight row; no weight: columns only
+    // one block per weight row; no weight (columns only) or a packed one: none
+    const int nwb = (a.weight && !wp_in) ? pl.Mp : 0;
     hipLaunchKernelGGL(v2_prep_kernel, dim3(pp.n_tr_blocks + nwb), dim3(256), 0, stream,
                        static_cast<const uint16_t *>(a.x), static_cast<const uint16_t *>(a.weight),
                        xt, wp, pp);
@@ -470,7 +473,7 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
         fp.nblocks = (int)(fp.Mtiles * ((pl.P + kFBN - 1) / kFBN));
         fp.xt_bytes = (unsigned)((size_t)a.N * a.H * a.W * pl.Cin_pad * 2);
         hipLaunchKernelGGL(v2_ws_kernel<E>, dim3(fp.nblocks), dim3(kWSThreads), fused_lds, stream, xt,
-                           a.offset, a.mask, wp, static_cast<uint16_t *>(a.out), fp);
+                           a.offset, a.mask, wp_in ? wp_in : wp, static_cast<uint16_t *>(a.out), fp);
         return hipGetLastError();
     }
 
@@ -548,6 +551,19 @@ bool plan_dcn_v2(int N, int Cin, int H, int W, int Cout, int kh, int kw, int sh,
 bool v2_fused_applies(const V2Plan &pl, int dg, bool has_weight) {
     // the block's offsets and masks ([kFBN][dg][K] x 3 floats) fit its 64 KB of dynamic LDS
     return has_weight && pl.fused && (size_t)kFBN * dg * pl.K * 3 * sizeof(float) <= 64 * 1024;
+}
+
+hipError_t launch_dcn_v2_pack_weight(const void *weight, void *packed, int Cout, int Cin, const V2Plan &pl,
+                                     hipStream_t stream) {
+    PrepParams pp = {};
+    pp.Cin = Cin; pp.Cin_pad = pl.Cin_pad;
+    pp.Cout = Cout; pp.K = pl.K; pp.Mp = pl.Mp; pp.Rp = pl.Rp;
+    pp.frag = 1;
+    pp.n_tr_blocks = 0;  // weight rows only
+    hipLaunchKernelGGL(v2_prep_kernel, dim3(pl.Mp), dim3(256), 0, stream, (const uint16_t *)nullptr,
+                       static_cast<const uint16_t *>(weight), (uint16_t *)nullptr, static_cast<uint16_t *>(packed),
+                       pp);
+    return hipGetLastError();
 }
 
 hipError_t launch_dcn_v2(const V2Launch &a, hipStream_t stream) {

@@ -111,6 +111,7 @@ struct V2Launch {
     const float *offset;
     const float *mask;  // may be NULL
     const void *weight;
+    const void *packed_weight;  // non-NULL: the weight already in the fused kernel's order
     void *out;
     void *workspace;
     int N, Cin, H, W, Cout, kh, kw, sh, sw, ph, pw, dh, dw, dg, softmax;
@@ -118,6 +119,10 @@ struct V2Launch {
     V2Plan plan;
 };
 hipError_t launch_dcn_v2(const V2Launch &a, hipStream_t stream);
+// The weight [Cout, Cin, kh, kw] permuted into the fused kernel's order (plan: Mp, Rp,
+// Cin_pad, K from plan_dcn_v2) at `packed`.
+hipError_t launch_dcn_v2_pack_weight(const void *weight, void *packed, int Cout, int Cin, const V2Plan &plan,
+                                     hipStream_t stream);
 
 // DCNv2 backward (dcn_v2_bwd.hip). Workspace regions (byte offsets, 256-aligned):
 // xt [N,H,W,Cin_pad], wT [Rr][CoK], gcl [Pp][CoK], goT [CoM][Pp], colT [Rr][Pp] (dtype);

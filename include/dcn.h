@@ -10,6 +10,8 @@
  *                       and an MFMA GEMM (fused, or in two stages through the workspace).
  *   dcn_v2_im2col       the deform-im2col stage alone: columns into the workspace.
  *   dcn_v2_forward_noalloc  dcn_v2_forward with a static in-library workspace.
+ *   dcn_v2_pack_weight, dcn_v2_forward_prepacked  the weight permuted once into the
+ *                       fused kernel's order, and the forward that reads it.
  *   dcn_v2_backward     gradients of DCNv2 w.r.t. x, offsets, masks and the weight.
  *   deform_agg_forward  Sparse4D-style multi-camera, multi-scale aggregation.
  *   deform_agg_backward gradients of the aggregation w.r.t. features, locations, weights.
@@ -178,10 +180,11 @@ dcn_status dcn_core_backward(const void *x, const float *offset, const float *ma
  * Workspace bytes dcn_v2_forward and dcn_v2_im2col need for these sizes (0 if they
  * are invalid). Layout (256-byte aligned regions, in this order): x transposed to
  * channels-last [N][H][W][Cin_pad], the weight permuted to [Cout_pad][Rp] (entry
- * k*Cin_pad + ci, tap-major) and the deform-im2col columns [P_pad][Rp], one row per
- * output pixel p = (n*Ho + ho)*Wo + wo with column k*Cin_pad + ci. Cin_pad = Cin
- * rounded up to 8, Rp = K*Cin_pad rounded up to 64, Cout_pad = Cout rounded up to
- * 128, P_pad = N*Ho*Wo rounded up to 128; padding entries are zero.
+ * k*Cin_pad + ci, tap-major; in the packed order of dcn_v2_pack_weight when the columns
+ * are formed on chip) and the deform-im2col columns [P_pad][Rp], one row per output
+ * pixel p = (n*Ho + ho)*Wo + wo with column k*Cin_pad + ci. Cin_pad = Cin rounded up
+ * to 8, Rp = K*Cin_pad rounded up to 64, Cout_pad = Cout rounded up to 128, P_pad =
+ * N*Ho*Wo rounded up to 128; padding entries are zero.
  */
 size_t dcn_v2_workspace_bytes(int N, int Cin, int H, int W, int Cout, int kh, int kw,
                               int stride_h, int stride_w, int pad_h, int pad_w,
@@ -250,6 +253,39 @@ dcn_status dcn_v2_forward_noalloc(const void *x, const float *offset, const floa
                                   int Cout, int kh, int kw, int stride_h, int stride_w,
                                   int pad_h, int pad_w, int dil_h, int dil_w, int deform_groups,
                                   int softmax, dcn_dtype dtype, hipStream_t stream);
+
+/*
+ * The weight of dcn_v2_forward permuted once, for layers whose weight does not change
+ * between calls (inference): dcn_v2_forward_prepacked then skips that step of every
+ * call. Only for layers that form their columns on chip (Cin a multiple of 64; see
+ * dcn_v2_forward).
+ *
+ *   dcn_v2_packed_weight_bytes(Cout, Cin, kh, kw)  bytes of the packed weight
+ *       (Cout_pad * Rp * 2, as in dcn_v2_workspace_bytes), 0 if the sizes are invalid.
+ *   dcn_v2_pack_weight: weight [Cout, Cin, kh, kw] (dtype DCN_F16 or DCN_BF16) ->
+ *       packed, a caller-owned device buffer of packed_bytes >= that size, 16-byte
+ *       aligned (DCN_ERR_WORKSPACE if smaller, DCN_ERR_ALIGN if not aligned). Layout:
+ *       the value weight[co, ci, k] has K index r = k*Cin_pad + ci; the eight values of
+ *       (co, r0..r0+7), r0 = 16 q + 8 h, sit at 16-byte slot
+ *       ((co/32 * Rp/16 + q) * 2 + h) * 32 + co%32, so the operand of one 32x32x16 MFMA
+ *       (32 output channels x 16 K values) is 1 KB of consecutive memory. Padding
+ *       entries are zero.
+ *   dcn_v2_forward_prepacked: dcn_v2_forward with packed_weight/packed_bytes (made by
+ *       dcn_v2_pack_weight for the same Cout, Cin, kh, kw and dtype) in place of
+ *       weight; same other arguments, validation and errors, plus DCN_ERR_PARAM when
+ *       the layer does not form its columns on chip and DCN_ERR_WORKSPACE when
+ *       packed_bytes is too small. Results are bit-identical to dcn_v2_forward. The
+ *       workspace's weight region is not used.
+ */
+size_t dcn_v2_packed_weight_bytes(int Cout, int Cin, int kh, int kw);
+dcn_status dcn_v2_pack_weight(const void *weight, void *packed, size_t packed_bytes, int Cout, int Cin,
+                              int kh, int kw, dcn_dtype dtype, hipStream_t stream);
+dcn_status dcn_v2_forward_prepacked(const void *x, const float *offset, const float *mask,
+                                    const void *packed_weight, size_t packed_bytes, void *out,
+                                    void *workspace, size_t workspace_bytes, int N, int Cin, int H,
+                                    int W, int Cout, int kh, int kw, int stride_h, int stride_w,
+                                    int pad_h, int pad_w, int dil_h, int dil_w, int deform_groups,
+                                    int softmax, dcn_dtype dtype, hipStream_t stream);
 
 /*
  * Workspace bytes dcn_v2_backward needs (0 if the sizes are invalid). Regions, each

@@ -404,6 +404,51 @@ def test_v2_noalloc_sizes_and_validation(lib):
     assert lib.dcn_last_hip_error() == 0
 
 
+def test_v2_packed_weight_sizes_and_validation(lib):
+    """dcn_v2_pack_weight / dcn_v2_forward_prepacked: packed size (Cout rounded up to
+    128 rows of Rp = K*Cin_pad rounded up to 64 values), and every rejected call's
+    status before any HIP call; the prepacked forward only takes layers that form their
+    columns on chip (Cin a multiple of 64)."""
+    assert lib.dcn_v2_packed_weight_bytes(256, 256, 3, 3) == 256 * 2304 * 2
+    assert lib.dcn_v2_packed_weight_bytes(24, 16, 3, 3) == 128 * 192 * 2
+    assert lib.dcn_v2_packed_weight_bytes(300, 128, 3, 3) == 384 * 1152 * 2
+    assert lib.dcn_v2_packed_weight_bytes(0, 16, 3, 3) == 0
+    assert lib.dcn_v2_packed_weight_bytes(8, 16, 9, 9) == 0  # K > 64
+    need = lib.dcn_v2_packed_weight_bytes(8, 64, 3, 3)
+
+    def pack(w=A, p=A, nbytes=need, Cout=8, Cin=64, kh=3, kw=3, dtype=2):
+        return lib.dcn_v2_pack_weight(w, p, nbytes, Cout, Cin, kh, kw, dtype, None)
+    assert pack(dtype=0) == DTYPE
+    assert pack(dtype=5) == DTYPE
+    assert pack(Cout=0) == SHAPE
+    assert pack(kh=0) == SHAPE
+    assert pack(w=None) == NULL
+    assert pack(p=None) == NULL
+    assert pack(w=A + 1) == ALIGN
+    assert pack(p=A + 8) == ALIGN
+    assert pack(nbytes=need - 1) == WORKSPACE
+
+    ws = lib.dcn_v2_workspace_bytes(1, 64, 8, 8, 8, 3, 3, 1, 1, 1, 1, 1, 1, 2)
+
+    def fwd(N=1, Cin=64, Cout=8, x=A, off=A, m=A, pw=A, pbytes=need, out=A, w=A, wbytes=ws, dg=1,
+            dtype=2):
+        return lib.dcn_v2_forward_prepacked(x, off, m, pw, pbytes, out, w, wbytes, N, Cin, 8, 8, Cout,
+                                            3, 3, 1, 1, 1, 1, 1, 1, dg, 0, dtype, None)
+    assert fwd(dtype=0) == DTYPE
+    assert fwd(Cin=0) == SHAPE
+    assert fwd(dg=3) == PARAM
+    assert fwd(Cin=16, pbytes=lib.dcn_v2_packed_weight_bytes(8, 16, 3, 3)) == PARAM  # two-stage layer
+    assert fwd(x=None) == NULL
+    assert fwd(pw=None) == NULL
+    assert fwd(out=A + 1) == ALIGN
+    assert fwd(pw=A + 8) == ALIGN
+    assert fwd(pbytes=need - 1) == WORKSPACE
+    assert fwd(wbytes=ws - 1) == WORKSPACE
+    assert fwd(w=None) == WORKSPACE
+    assert fwd(N=0) == OK
+    assert lib.dcn_last_hip_error() == 0
+
+
 def test_mfma_probe_validation(lib):
     assert lib.dcn_mfma_probe(A, 0, 10, None) == PARAM
     assert lib.dcn_mfma_probe(A, 4, -1, None) == PARAM
