@@ -8,7 +8,8 @@ nor the GPU path can lean on it for a result.
 Draws come from NumPy ``Generator(PCG64(seed))`` in float64, in a fixed order
 (features, offsets/locations, masks/logits, out-of-bounds selection, weights),
 and are then rounded once (round-to-nearest-even) to the tensor's dtype by torch.
-Everything returned is a CPU torch tensor.
+Everything returned is a CPU torch tensor, except from the ``*_device`` functions,
+whose multi-GB inputs are drawn on the GPU by torch's seeded generator.
 
 Named workloads (see ``WORKLOADS``) mirror the shapes and value distributions of
 the ops' typical uses: a DCNv4 block on a 32x32 map, a DCNv3 stage on 56x56
@@ -198,6 +199,64 @@ def agg_case(*, B, shapes, A, pts, G, Cg, dtype="f32", weights="logits", seed=0,
         feat=_t(feat, dtype), spatial_shape=ss, scale_start=st, loc=_t(loc, "f32"),
         weights=_t(w, "f32"), B=B, P_total=P_total, A=A, pts=pts, cams=cams, scales=scales,
         G=G, Cg=Cg, dtype=dtype, softmax=(weights == "logits"))
+
+
+# ------------------------------------------------------ device-side draws --
+#
+# For inputs of several GB (the tests at the 2-GiB buffer limits) the draws are made
+# on the GPU with torch's seeded generator (Philox) instead: NumPy would need minutes
+# and tens of GB of host memory. The tests copy the windows the oracle needs back to
+# the host, so both sides still see the same values.
+
+def _dgen(seed, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def core_case_device(*, N, H, W, G, C, dtype="f16", offset_range=4.0, seed=0, device="cuda"):
+    """Core inputs drawn on `device`: x ~ N(0,1) in dtype [N,H,W,G*C]; offsets
+    ~ U(-offset_range, offset_range) fp32 [N,H,W,G,9,2] (3x3 window, stride 1, pad 1);
+    masks ~ U(0,1) fp32 [N,H,W,G,9]."""
+    g = _dgen(seed, device)
+    x = torch.randn((N, H, W, G * C), generator=g, device=device, dtype=torch.float32).to(DTYPES[dtype])
+    off = torch.rand((N, H, W, G, 9, 2), generator=g, device=device) * (2 * offset_range) - offset_range
+    m = torch.rand((N, H, W, G, 9), generator=g, device=device)
+    return dict(x=x, offset=off, mask=m, N=N, H=H, W=W, G=G, C=C, dtype=dtype)
+
+
+def v2_case_device(*, N, Cin, H, W, Cout, dtype="bf16", offset_range=4.0, w_std=0.02, seed=0,
+                   device="cuda"):
+    """DCNv2 inputs drawn on `device` (3x3 window, stride 1, pad 1, one deformable
+    group): x ~ N(0,1) [N,Cin,H,W]; offsets ~ U(-r, r) [N,18,H,W]; masks ~ U(0,1)
+    [N,9,H,W]; weight ~ N(0, w_std^2) [Cout,Cin,3,3]."""
+    g = _dgen(seed, device)
+    x = torch.randn((N, Cin, H, W), generator=g, device=device, dtype=torch.float32).to(DTYPES[dtype])
+    off = torch.rand((N, 18, H, W), generator=g, device=device) * (2 * offset_range) - offset_range
+    m = torch.rand((N, 9, H, W), generator=g, device=device)
+    w = (torch.randn((Cout, Cin, 3, 3), generator=g, device=device) * w_std).to(DTYPES[dtype])
+    return dict(x=x, offset=off, mask=m, weight=w, N=N, Cin=Cin, H=H, W=W, Cout=Cout, dtype=dtype)
+
+
+def agg_case_device(*, B, shapes, A, pts, G, Cg, seed=0, device="cuda"):
+    """Aggregation inputs drawn on `device`, fp32: feat ~ N(0,1) [B,P_total,G*Cg] with
+    maps flattened camera-major; loc ~ U(0,1) [B,A,pts,cams,2]; weight logits ~ N(0,1)
+    [B,A,pts,cams,scales,G] (for the op's softmax). spatial_shape and scale_start are
+    host int32 arrays."""
+    cams, scales = len(shapes), len(shapes[0])
+    ss = np.array(shapes, dtype=np.int32).reshape(cams, scales, 2)
+    st = np.zeros((cams, scales), np.int32)
+    pos = 0
+    for c in range(cams):
+        for s in range(scales):
+            st[c, s] = pos
+            pos += int(ss[c, s, 0]) * int(ss[c, s, 1])
+    g = _dgen(seed, device)
+    feat = torch.randn((B, pos, G * Cg), generator=g, device=device)
+    loc = torch.rand((B, A, pts, cams, 2), generator=g, device=device)
+    w = torch.randn((B, A, pts, cams, scales, G), generator=g, device=device)
+    return dict(feat=feat, spatial_shape=ss, scale_start=st, loc=loc, weights=w, B=B, P_total=pos,
+                A=A, pts=pts, cams=cams, scales=scales, G=G, Cg=Cg, dtype="f32", softmax=True)
 
 
 # Named workloads: the five shapes the ops are exercised and measured on.
