@@ -557,8 +557,14 @@ hipError_t launch_e(const V2BwdLaunch &a, hipStream_t stream) {
         gp.Ntiles = pl.Rr / kBN;
         gp.nblocks = gp.Mtiles * gp.Ntiles;
         gp.ldc = pl.R; gp.Mstore = (int)pl.P; gp.Nstore = pl.R;
-        hipLaunchKernelGGL((v2_gemm_kernel<E, 1>), dim3(gp.nblocks), dim3(kGemmThreads), 0, stream,
-                           gcl, wT, gcol, gp);
+        // a reduction over Cout only: with a few K tiles per block, the two-slot ring
+        // lets two blocks share a CU, so one block's fp32 stores overlap the other's MFMAs
+        if (gp.nk <= 8)
+            hipLaunchKernelGGL((v2_gemm_kernel<E, 1, 2>), dim3(gp.nblocks), dim3(kGemmThreads), 0, stream,
+                               gcl, wT, gcol, gp);
+        else
+            hipLaunchKernelGGL((v2_gemm_kernel<E, 1>), dim3(gp.nblocks), dim3(kGemmThreads), 0, stream,
+                               gcl, wT, gcol, gp);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     // 6-8. buckets

@@ -196,7 +196,7 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 #define V2_WAIT_VMCNT(n) \
     __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
 
-constexpr int kStages = 4;                          // K tiles in flight (LDS ring)
+constexpr int kStages = 4;                          // K tiles in flight (LDS ring), at most
 constexpr int kTileChunks = kBM * kBK / 8;          // 16-byte chunks per operand tile (1024)
 // Waves per GEMM block: 8 (2 x 4, 64 x 32 each: two per SIMD, so one wave's LDS
 // waits overlap the other's MFMAs) or 4 (2 x 2, 64 x 64 each).
@@ -229,6 +229,9 @@ template <int S> __device__ __forceinline__ uint4 *ring_b() {
     else return s_gB3;
 }
 static_assert(kStages == 4, "the ring has four named slots");
+// A kernel instance with NS = 2 uses slots 0 and 1 only, so it holds 64 KB of LDS and
+// two blocks share a CU: for short reductions (a few K tiles), where a block's loads
+// and stores then overlap the other block's MFMAs.
 
 // Copy a 128 x 64 operand tile (rows row0.., reduction k0..k0+63) into an LDS ring slot:
 // wave w, copy i moves LDS chunks (i*W + w)*64 + lane, i.e. row c >> 3, position c & 7.
@@ -244,23 +247,24 @@ __device__ __forceinline__ void gemm_dma(uint4 *slot, const uint16_t *g, int ld,
     }
 }
 
-// One K step from ring slot S: wait until its tile has landed, barrier, refill the slot
-// the previous step used with tile kt + kStages - 1, then 4 x (2 x kTB) MFMAs.
-template <class E, int S>
+// One K step from ring slot S of an NS-slot ring: wait until its tile has landed,
+// barrier, refill the slot the previous step used with tile kt + NS - 1, then
+// 4 x (2 x kTB) MFMAs.
+template <class E, int S, int NS>
 __device__ __forceinline__ void gemm_step(int kt, int nk, const uint16_t *ga, const uint16_t *gb, int lda,
                                           int ldb, f32x16_t (&acc)[2][kTB], int wm, int wn, int frow,
                                           int fhalf) {
     if (kt >= nk) return;
-    // this wave's copies issued after tile kt: min(nk-1-kt, kStages-2) tiles x 2 operands
-    const int after = (nk - 1 - kt) < (kStages - 2) ? (nk - 1 - kt) : (kStages - 2);
+    // this wave's copies issued after tile kt: min(nk-1-kt, NS-2) tiles x 2 operands
+    const int after = (nk - 1 - kt) < (NS - 2) ? (nk - 1 - kt) : (NS - 2);
     if (after >= 2) V2_WAIT_VMCNT(2 * 2 * kDmaPerWave);
     else if (after == 1) V2_WAIT_VMCNT(1 * 2 * kDmaPerWave);
     else V2_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();  // all waves: tile kt in LDS, tile kt-1 consumed
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    const int nx = kt + kStages - 1;
+    const int nx = kt + NS - 1;
     if (nx < nk) {
-        constexpr int R = (S + kStages - 1) % kStages;
+        constexpr int R = (S + NS - 1) % NS;
         gemm_dma(ring_a<R>(), ga, lda, nx * kBK);
         gemm_dma(ring_b<R>(), gb, ldb, nx * kBK);
     }
@@ -291,7 +295,7 @@ __device__ __forceinline__ void gemm_step(int kt, int nk, const uint16_t *ga, co
 // 64 x kWaveN = 2 x kTB v_mfma_f32_32x32x16 tiles with fp32 accumulators. The K loop
 // runs over a kStages-deep ring of LDS tiles filled by direct global->LDS copies, so
 // HBM/L2 latency overlaps the MFMA work of the previous stages.
-template <class E, int MODE>
+template <class E, int MODE, int NS = kStages>
 __global__ __launch_bounds__(kGemmThreads) void v2_gemm_kernel(const uint16_t *__restrict__ A,
                                                       const uint16_t *__restrict__ B,
                                                       void *__restrict__ out, GemmParams p) {
@@ -315,17 +319,22 @@ __global__ __launch_bounds__(kGemmThreads) void v2_gemm_kernel(const uint16_t *_
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-    // prologue: tiles 0 .. kStages-2 in flight
+    static_assert(NS == 2 || NS == 4, "ring of two or four slots");
+    // prologue: tiles 0 .. NS-2 in flight
     if (0 < nk) { gemm_dma(ring_a<0>(), ga, p.lda, 0); gemm_dma(ring_b<0>(), gb, p.ldb, 0); }
-    if (1 < nk) { gemm_dma(ring_a<1>(), ga, p.lda, kBK); gemm_dma(ring_b<1>(), gb, p.ldb, kBK); }
-    if (2 < nk) { gemm_dma(ring_a<2>(), ga, p.lda, 2 * kBK); gemm_dma(ring_b<2>(), gb, p.ldb, 2 * kBK); }
+    if constexpr (NS == 4) {
+        if (1 < nk) { gemm_dma(ring_a<1>(), ga, p.lda, kBK); gemm_dma(ring_b<1>(), gb, p.ldb, kBK); }
+        if (2 < nk) { gemm_dma(ring_a<2>(), ga, p.lda, 2 * kBK); gemm_dma(ring_b<2>(), gb, p.ldb, 2 * kBK); }
+    }
     // fragment of lane l in a 16-deep k step ks: row (l % 32), logical chunk 2*ks + l/32
     const int frow = lane & 31, fhalf = lane >> 5;
-    for (int kt = 0; kt < nk; kt += kStages) {
-        gemm_step<E, 0>(kt + 0, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
-        gemm_step<E, 1>(kt + 1, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
-        gemm_step<E, 2>(kt + 2, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
-        gemm_step<E, 3>(kt + 3, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
+    for (int kt = 0; kt < nk; kt += NS) {
+        gemm_step<E, 0, NS>(kt + 0, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
+        gemm_step<E, 1, NS>(kt + 1, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
+        if constexpr (NS == 4) {
+            gemm_step<E, 2, NS>(kt + 2, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
+            gemm_step<E, 3, NS>(kt + 3, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
+        }
     }
 
     // epilogue: D[i][j] of a 32x32 tile sits in lane j + 32*((i/4)%2), register
