@@ -507,8 +507,13 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     gp.Mtiles = pl.Mp / kBM;
     gp.Ntiles = (int)(pl.Pp / kBN);
     gp.nblocks = gp.Mtiles * gp.Ntiles;
-    hipLaunchKernelGGL((v2_gemm_kernel<E, 0>), dim3(gp.nblocks), dim3(kGemmThreads), 0, stream, wp, col,
-                       a.out, gp);
+    // short reductions (few K tiles): the two-slot ring, two blocks per CU
+    if (gp.nk <= 8)
+        hipLaunchKernelGGL((v2_gemm_kernel<E, 0, 2>), dim3(gp.nblocks), dim3(kGemmThreads), 0, stream, wp, col,
+                           a.out, gp);
+    else
+        hipLaunchKernelGGL((v2_gemm_kernel<E, 0>), dim3(gp.nblocks), dim3(kGemmThreads), 0, stream, wp, col,
+                           a.out, gp);
     return hipGetLastError();
 }
 
