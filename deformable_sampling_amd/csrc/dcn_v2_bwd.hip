@@ -15,12 +15,13 @@
 //     destination sums its bucket's gcol rows into registers and stores once.
 // Launches (caller's stream, no host synchronisation):
 //   1. x -> xt [N,H,W,Cin_pad] and grad_out -> gcl [Pp][CoK] (the shared transpose),
-//      goT [CoM][Pp] (grad_out with the batch folded into the pixel axis), wT [Rr][CoK]
+//      then one launch for goT [CoM][Pp] (grad_out with the batch folded into the pixel
+//      axis), wT [Rr][CoK] and clearing the bucket counters
 //   2. colT [Rr][Pp]: the forward's columns, rounded to the dtype, transposed
 //   3. gcol = gcl x wT^T (fp32)   4. grad_weight partials = goT x colT^T   5. their sum
-//   6. clear the bucket counters  7. count  8. scan
-//   9. sample pass: grad_offset, grad_mask and the bucket entries
-//  10. destination gather into gx_cl [N,H,W,Cin_pad] fp32  11. transpose to grad_x.
+//   6. count  7. scan
+//   8. sample pass: grad_offset, grad_mask and the bucket entries
+//   9. destination gather into gx_cl [N,H,W,Cin_pad] fp32  10. transpose to grad_x.
 #include "dcn_common.hpp"
 #include "internal.hpp"
 
@@ -98,11 +99,12 @@ __device__ __forceinline__ void v2b_softmax_stats(const float *__restrict__ mask
 
 // goT[co][p] = grad_out[n][co][hw] for p = n*HWo + hw; zero for co >= Cout or p >= P.
 // VEC: 8 consecutive pixels per thread (HWo and P multiples of 8, 16-byte aligned rows).
+// Block bi of the job.
 template <bool VEC>
-__global__ __launch_bounds__(kB) void v2b_rows_kernel(const uint16_t *__restrict__ gout,
-                                                      uint16_t *__restrict__ goT, int Cout, int HWo,
-                                                      long long P, long long Pp, long long total) {
-    const long long t = (long long)blockIdx.x * kB + threadIdx.x;
+__device__ __forceinline__ void v2b_rows_block(int bi, const uint16_t *__restrict__ gout,
+                                               uint16_t *__restrict__ goT, int Cout, int HWo, long long P,
+                                               long long Pp, long long total) {
+    const long long t = (long long)bi * kB + threadIdx.x;
     if constexpr (VEC) {
         if (t * 8 >= total) return;
         const long long e = t * 8;
@@ -126,14 +128,42 @@ __global__ __launch_bounds__(kB) void v2b_rows_kernel(const uint16_t *__restrict
 }
 
 // wT[r][co] = weight[co][ci][k] for r = k*Cin_pad + ci; zero for padding entries.
-__global__ __launch_bounds__(kB) void v2b_wt_kernel(const uint16_t *__restrict__ w,
-                                                    uint16_t *__restrict__ wT, int Cout, int Cin,
-                                                    int K, int Cin_pad, int CoK, long long total) {
-    const long long t = (long long)blockIdx.x * kB + threadIdx.x;
+__device__ __forceinline__ void v2b_wt_block(int bi, const uint16_t *__restrict__ w, uint16_t *__restrict__ wT,
+                                             int Cout, int Cin, int K, int Cin_pad, int CoK, long long total) {
+    const long long t = (long long)bi * kB + threadIdx.x;
     if (t >= total) return;
     const int r = (int)(t / CoK), co = (int)(t - (long long)r * CoK);
     const int k = r / Cin_pad, ci = r - k * Cin_pad;
     wT[t] = (co < Cout && k < K && ci < Cin) ? w[((size_t)co * Cin + ci) * K + k] : (uint16_t)0;
+}
+
+// The backward's small layout jobs in one launch (a launch costs a few microseconds even
+// when it does little): blocks [0, e_wt) transpose the weight, [e_wt, e_rows) lay
+// grad_out out pixel-major, [e_rows, e_zero) clear the bucket counters.
+struct V2bLayout {
+    const uint16_t *gout, *w;
+    uint16_t *wT, *goT;
+    int Cout, Cin, K, Cin_pad, CoK, HWo, rows_vec;
+    long long P, Pp, nwt, nrows;
+    int *cnt;
+    long long nzero;
+    int e_wt, e_rows, e_zero;
+};
+
+__global__ __launch_bounds__(kB) void v2b_layout_kernel(const V2bLayout L) {
+    const int b = (int)blockIdx.x;
+    if (b < L.e_wt) {
+        v2b_wt_block(b, L.w, L.wT, L.Cout, L.Cin, L.K, L.Cin_pad, L.CoK, L.nwt);
+    } else if (b < L.e_rows) {
+        if (L.rows_vec)
+            v2b_rows_block<true>(b - L.e_wt, L.gout, L.goT, L.Cout, L.HWo, L.P, L.Pp, L.nrows);
+        else
+            v2b_rows_block<false>(b - L.e_wt, L.gout, L.goT, L.Cout, L.HWo, L.P, L.Pp, L.nrows);
+    } else {
+        const int nb = L.e_zero - L.e_rows;
+        for (long long i = (long long)(b - L.e_rows) * kB + threadIdx.x; i < L.nzero; i += (long long)nb * kB)
+            L.cnt[i] = 0;
+    }
 }
 
 // ---------------------------------------------------------------- columns --
@@ -214,11 +244,6 @@ __global__ __launch_bounds__(kB) void v2b_wsum_kernel(const float *__restrict__ 
 }
 
 // ---------------------------------------------------------------- buckets --
-
-__global__ __launch_bounds__(kB) void v2b_zero_kernel(int *__restrict__ p, long long n) {
-    for (long long i = (long long)blockIdx.x * kB + threadIdx.x; i < n; i += (long long)gridDim.x * kB)
-        p[i] = 0;
-}
 
 // One thread per sample (p, g, k): count the corners that receive a grad_x entry
 // (inside the image, weight non-zero) in their destination's bucket.
@@ -478,45 +503,72 @@ hipError_t launch_e(const V2BwdLaunch &a, hipStream_t stream) {
     const bool want_x = a.grad_x != nullptr;
     const bool want_s = want_x || a.grad_offset || a.grad_mask;
     hipError_t err;
-    auto transpose = [&](const void *src, uint16_t *dst, int C, int Cpad, int hw) {
+    // parameters of one channels-last transpose (register transposes where the pixel rows
+    // are whole 16-byte vectors, else through the LDS tile); its block count in n_tr_blocks
+    auto transpose_params = [&](const void *src, int C, int Cpad, int hw) {
         PrepParams pp = {};
         pp.N = a.N; pp.Cin = C; pp.HW = hw; pp.Cin_pad = Cpad;
         pp.vec = (hw % kVec == 0) && ((uintptr_t)src % 16 == 0);
         pp.Mp = 0; pp.Rp = kVec;  // no weight blocks
-        pp.reg = 0;
         pp.tiles_c = (Cpad + 63) / 64;
         pp.tiles_hw = (hw + 63) / 64;
-        pp.n_tr_blocks = a.N * pp.tiles_c * pp.tiles_hw;
-        hipLaunchKernelGGL(v2_prep_kernel, dim3(pp.n_tr_blocks), dim3(256), 0, stream,
-                           static_cast<const uint16_t *>(src), (const uint16_t *)nullptr, dst,
-                           (uint16_t *)nullptr, pp);
-        return hipGetLastError();
+        pp.cgroups = pp.tiles_c;
+        pp.hgroups = pp.tiles_hw;
+        pp.reg = pp.vec;
+        pp.n_tr_blocks = pp.reg ? (a.N * pp.cgroups * pp.hgroups + 3) / 4 : a.N * pp.tiles_c * pp.tiles_hw;
+        return pp;
     };
     V2bGeo q;
     q.N = a.N; q.H = a.H; q.W = a.W; q.Ho = pl.Ho; q.Wo = pl.Wo; q.kh = a.kh; q.kw = a.kw;
     q.sh = a.sh; q.sw = a.sw; q.ph = a.ph; q.pw = a.pw; q.dh = a.dh; q.dw = a.dw; q.dg = a.dg;
     q.K = pl.K; q.P = pl.P; q.has_mask = a.mask != nullptr; q.softmax = a.softmax ? 1 : 0;
 
-    // 1. layouts
-    if ((err = transpose(a.x, xt, a.Cin, pl.Cin_pad, HW)) != hipSuccess) return err;
-    if (want_s) {
-        if ((err = transpose(a.grad_out, gcl, a.Cout, pl.CoK, HWo)) != hipSuccess) return err;
-        const long long nwt = (long long)pl.Rr * pl.CoK;
-        hipLaunchKernelGGL(v2b_wt_kernel, dim3((unsigned)((nwt + kB - 1) / kB)), dim3(kB), 0, stream,
-                           static_cast<const uint16_t *>(a.weight), wT, a.Cout, a.Cin, pl.K,
-                           pl.Cin_pad, pl.CoK, nwt);
+    // 1. layouts: x and grad_out to channels-last (the forward's prep kernel), then the
+    // weight transposed, grad_out pixel-major and the bucket counters cleared in one launch
+    {
+        const PrepParams tx = transpose_params(a.x, a.Cin, pl.Cin_pad, HW);
+        hipLaunchKernelGGL(v2_prep_kernel, dim3(tx.n_tr_blocks), dim3(256), 0, stream,
+                           static_cast<const uint16_t *>(a.x), (const uint16_t *)nullptr, xt,
+                           (uint16_t *)nullptr, tx);
         if ((err = hipGetLastError()) != hipSuccess) return err;
+        if (want_s) {
+            const PrepParams tg = transpose_params(a.grad_out, a.Cout, pl.CoK, HWo);
+            hipLaunchKernelGGL(v2_prep_kernel, dim3(tg.n_tr_blocks), dim3(256), 0, stream,
+                               static_cast<const uint16_t *>(a.grad_out), (const uint16_t *)nullptr, gcl,
+                               (uint16_t *)nullptr, tg);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+        V2bLayout L = {};
+        L.gout = static_cast<const uint16_t *>(a.grad_out);
+        L.w = static_cast<const uint16_t *>(a.weight);
+        L.wT = wT; L.goT = goT;
+        L.Cout = a.Cout; L.Cin = a.Cin; L.K = pl.K; L.Cin_pad = pl.Cin_pad; L.CoK = pl.CoK; L.HWo = HWo;
+        L.P = pl.P; L.Pp = pl.Pp;
+        L.cnt = cnt;
+        int nb = 0;
+        if (want_s) {
+            L.nwt = (long long)pl.Rr * pl.CoK;
+            nb += (int)((L.nwt + kB - 1) / kB);
+        }
+        L.e_wt = nb;
+        if (want_w) {
+            L.nrows = (long long)pl.CoM * pl.Pp;
+            L.rows_vec = HWo % 8 == 0 && (uintptr_t)a.grad_out % 16 == 0;  // then P % 8 == 0 too
+            nb += (int)(((L.rows_vec ? L.nrows / 8 : L.nrows) + kB - 1) / kB);
+        }
+        L.e_rows = nb;
+        if (want_x) {
+            L.nzero = 2LL * pl.D;
+            const long long nz = (L.nzero + kB - 1) / kB;
+            nb += (int)(nz < 1024 ? nz : 1024);
+        }
+        L.e_zero = nb;
+        if (nb > 0) {
+            hipLaunchKernelGGL(v2b_layout_kernel, dim3(nb), dim3(kB), 0, stream, L);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
     }
     if (want_w) {
-        const long long nrows = (long long)pl.CoM * pl.Pp;
-        const uint16_t *gsrc = static_cast<const uint16_t *>(a.grad_out);
-        if (HWo % 8 == 0 && (uintptr_t)gsrc % 16 == 0)  // then P % 8 == 0 too
-            hipLaunchKernelGGL((v2b_rows_kernel<true>), dim3((unsigned)((nrows / 8 + kB - 1) / kB)), dim3(kB),
-                               0, stream, gsrc, goT, a.Cout, HWo, pl.P, pl.Pp, nrows);
-        else
-            hipLaunchKernelGGL((v2b_rows_kernel<false>), dim3((unsigned)((nrows + kB - 1) / kB)), dim3(kB),
-                               0, stream, gsrc, goT, a.Cout, HWo, pl.P, pl.Pp, nrows);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
         // 2. transposed columns
         V2bColParams cp;
         cp.q = q;
@@ -567,18 +619,16 @@ hipError_t launch_e(const V2BwdLaunch &a, hipStream_t stream) {
                                gcl, wT, gcol, gp);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    // 6-8. buckets
+    // 6-7. buckets
     const long long nsamp = pl.P * a.dg * pl.K;
-    if (want_x) {
-        hipLaunchKernelGGL(v2b_zero_kernel, dim3(1024), dim3(kB), 0, stream, cnt, 2 * pl.D);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (want_x) {  // (the counters were cleared with the layouts)
         hipLaunchKernelGGL(v2b_count_kernel, dim3((unsigned)((nsamp + kB - 1) / kB)), dim3(kB), 0,
                            stream, a.offset, cnt, q);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL(v2b_scan_kernel, dim3(1), dim3(1024), 0, stream, cnt, starts, pl.D);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    // 9. sample pass
+    // 8. sample pass
     {
         V2bSampleParams sp;
         sp.q = q;
@@ -601,7 +651,7 @@ hipError_t launch_e(const V2BwdLaunch &a, hipStream_t stream) {
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (!want_x) return hipSuccess;
-    // 10. destination gather, 11. NCHW grad_x
+    // 9. destination gather, 10. NCHW grad_x
     {
         V2bGatherParams gq;
         gq.dg = a.dg; gq.cpg = a.Cin / a.dg; gq.Cin_pad = pl.Cin_pad; gq.K = pl.K; gq.R = pl.R;
