@@ -216,6 +216,30 @@ __device__ __forceinline__ void lds_copy16(unsigned lds_wave_base, const void *s
         : "memory", "m0");
 }
 
+// The same copy through a buffer resource (buffer_load_dwordx4 ... lds): lane l reads
+// bytes [voff + soff, +16) of the resource, which reads as zeros where that range
+// passes the resource's end (a chunk outside the image costs no memory traffic). The
+// resource is given as its four descriptor words (gfx9 layout, as make_rsrc builds).
+typedef int rsrc_words_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ rsrc_words_t rsrc_words(const void *base, unsigned bytes) {
+    const unsigned long long a = (unsigned long long)(size_t)base;
+    rsrc_words_t r;
+    r.x = (int)(unsigned)a;
+    r.y = (int)((unsigned)(a >> 32) & 0xffffu);
+    r.z = (int)bytes;
+    r.w = 0x00020000;
+    return r;
+}
+__device__ __forceinline__ void lds_copy16_buf(unsigned lds_wave_base, rsrc_words_t rsrc, int voff, int soff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_wave_base)), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory", "m0");
+}
+
 // LDS byte address of a pointer into __shared__ memory.
 template <class T>
 __device__ __forceinline__ unsigned lds_addr(const T *p) {

@@ -157,6 +157,7 @@ struct FusedParams {
     int has_mask, softmax;
     int Mtiles, nblocks;
     unsigned xt_bytes;  // all of xt
+    int tiles_x, tiles_y;  // 8x8 pixel tiles per image row / column (staged-region kernel)
 };
 
 // --------------------------------------------------- fused, specialised waves --
@@ -425,6 +426,285 @@ __global__ __launch_bounds__(kWSThreads) void v2_ws_kernel(const uint16_t *__res
     }
 }
 
+// ------------------------------------------------- fused, staged region --
+//
+// The two-role kernel for 3x3 windows at stride 1 and dilation 1 with one deformable
+// group. A block takes an 8 x 8 tile of output pixels and all kFBM output channels;
+// the K loop runs channel-block-major: for 64-channel block c the nine taps in turn,
+// step t = 9c + k reading weight rows k*Cin_pad + 64c .. +63 (the two-stage GEMM
+// visits its K tiles in the same order for these layers, so both paths sum alike).
+// Per channel block the producers copy the tile's receptive region of xt into LDS
+// (kRW x kRW pixels x 64 channels: the tile's 3x3 bases +-kRHalo px and one more
+// for the bilinear corner) with direct global->LDS copies, one channel block ahead
+// in a second region buffer; a step's column corners are then four 16-byte LDS
+// reads instead of four loads through the vector memory path. Taps whose corners
+// leave the region (offsets beyond about +-6 px) read xt directly. A producer lane
+// keeps its pixel's nine tap records (region cell, four weights) in registers for
+// the whole K loop.
+constexpr int kRT = 8;                                  // tile edge: kRT * kRT = kFBN pixels
+constexpr int kRHalo = 6;
+constexpr int kRW = kRT + 2 + 2 * kRHalo;               // 22: region edge in pixels
+constexpr int kRChunks = kRW * kRW * 8;                 // 16-byte chunks per region
+constexpr int kRCopies = (kRChunks + kWSPThreads - 1) / kWSPThreads;
+static_assert(kRT * kRT == kFBN, "one pixel tile per block");
+constexpr int kRK = 9;                                  // taps of the 3x3 window
+
+template <class E>
+__global__ __launch_bounds__(kWSThreads) void v2_wsr_kernel(const uint16_t *__restrict__ xt,
+                                                            const float *__restrict__ offset,
+                                                            const float *__restrict__ mask,
+                                                            const uint16_t *__restrict__ wp,
+                                                            uint16_t *__restrict__ out,
+                                                            const FusedParams p) {
+    __shared__ uint4 sR[2][kRChunks];    // region buffers, [pixel row][pixel][8 chunks]
+    __shared__ uint4 sB[2][kFBChunks];   // column tiles, as in v2_ws_kernel
+    __shared__ float s_off[kFBN * kRK * 2];
+    __shared__ float s_m[kFBN * kRK];
+
+    const int blk = xcd_remap((int)blockIdx.x, p.nblocks);
+    const int mt = blk % p.Mtiles, tile = blk / p.Mtiles;
+    const int tpi = p.tiles_x * p.tiles_y;
+    const int n = tile / tpi, trest = tile - n * tpi;
+    const int ty0 = (trest / p.tiles_x) * kRT, tx0 = (trest - (trest / p.tiles_x) * p.tiles_x) * kRT;
+    const int m0 = mt * kFBM;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int HWo = p.HWo;
+    const int ry0 = ty0 - p.ph - kRHalo, rx0 = tx0 - p.pw - kRHalo;
+    const int CBn = p.CB;
+    const int NS = kRK * CBn;
+
+    // region of channel block c into buffer b (producer waves only): copy j of a lane
+    // moves region chunk i = j * 512 + (producer thread); chunks outside the image get
+    // an offset past the end of the resource over xt and read as zeros
+    const rsrc_words_t rxw = rsrc_words(xt, p.xt_bytes);
+    auto stage = [&](int c, int b) __attribute__((always_inline)) {
+        const int pwv = wave - kWSConsumers;
+#pragma unroll
+        for (int j = 0; j < kRCopies; ++j) {
+            const int i0 = j * kWSPThreads + pwv * 64;
+            if (i0 < kRChunks) {
+                const int i = i0 + lane;
+                const int q = i >> 3, cc = i & 7;
+                const int ry = q / kRW, rx = q - ry * kRW;
+                const int yy = ry0 + ry, xx = rx0 + rx;
+                const bool ok = (unsigned)yy < (unsigned)p.H && (unsigned)xx < (unsigned)p.W;
+                const int voff = ok ? ((n * p.H + yy) * p.W + xx) * p.Cin_pad * 2 + cc * 16 : (int)p.xt_bytes;
+                if (i < kRChunks) lds_copy16_buf(lds_addr(&sR[b][i0]), rxw, voff, c * kBK * 2);
+            }
+        }
+    };
+
+    if (wave >= kWSConsumers) stage(0, 0);
+    // offsets and masks of the tile's pixels: pixel pl = 8 py + px
+    for (int i = tid; i < kFBN * kRK * 2; i += kWSThreads) {
+        const int pl = i % kFBN, c = i / kFBN;
+        const int ho = ty0 + (pl >> 3), wo = tx0 + (pl & 7);
+        float v = 0.0f;
+        if (ho < p.Ho && wo < p.Wo) v = offset[((size_t)n * kRK * 2 + c) * HWo + ho * p.Wo + wo];
+        s_off[pl * kRK * 2 + c] = v;
+    }
+    for (int i = tid; i < kFBN * kRK; i += kWSThreads) {
+        const int pl = i % kFBN, c = i / kFBN;
+        const int ho = ty0 + (pl >> 3), wo = tx0 + (pl & 7);
+        float v = 1.0f;
+        if (p.has_mask && ho < p.Ho && wo < p.Wo) v = mask[((size_t)n * kRK + c) * HWo + ho * p.Wo + wo];
+        s_m[pl * kRK + c] = v;
+    }
+    V2_WAIT_VMCNT(0);  // region 0 has landed (this wave's copies)
+    __syncthreads();
+    if (p.softmax) {
+        for (int i = tid; i < kFBN; i += kWSThreads) {
+            float *ml = s_m + i * kRK;
+            float mx = -INFINITY;
+            for (int k = 0; k < kRK; ++k) mx = fmaxf(mx, ml[k]);
+            float sum = 0.0f;
+            for (int k = 0; k < kRK; ++k) sum += expf(ml[k] - mx);
+            const float inv = 1.0f / sum;
+            for (int k = 0; k < kRK; ++k) ml[k] = expf(ml[k] - mx) * inv;
+        }
+    }
+    __syncthreads();
+
+    if (wave >= kWSConsumers) {
+        // ------------------------------------------------------------ producers --
+        if (CBn > 1) stage(1, 1);
+        const int ptid = tid - 64 * kWSConsumers;
+        const int br = ptid >> 3, bc = ptid & 7;
+        const int ho = ty0 + (br >> 3), wo = tx0 + (br & 7);
+        const bool pvalid = ho < p.Ho && wo < p.Wo;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(xt, p.xt_bytes);
+        const int img_off = n * p.H * p.W * p.Cin_pad + bc * kVec;
+        const int bdst = br * 8 + (bc ^ ((br >> 1) & 7));
+        // tap records: region chunk of the (y0, x0) corner (this lane's 16 bytes), the
+        // four weights as the deform-im2col stage forms them; `far` marks taps that
+        // touch the image but leave the region
+        int cell[kRK];
+        float tw[kRK][4];
+        unsigned far = 0;
+#pragma unroll
+        for (int k = 0; k < kRK; ++k) {
+            const float *so = s_off + (br * kRK + k) * 2;
+            int y0, x0;
+            float fy, fx;
+            split_coord(ho - p.ph + k / 3, so[1], y0, fy);
+            split_coord(wo - p.pw + k % 3, so[0], x0, fx);
+            const float mk = pvalid ? s_m[br * kRK + k] : 0.0f;
+            const Tap tp = make_tap(y0, x0, fy, fx, mk, p.H, p.W, p.Cin_pad);
+            const int ly = y0 - ry0, lx = x0 - rx0;
+            const bool inreg = (unsigned)ly <= (unsigned)(kRW - 2) && (unsigned)lx <= (unsigned)(kRW - 2);
+            const bool touch = (unsigned)(y0 + 1) <= (unsigned)p.H && (unsigned)(x0 + 1) <= (unsigned)p.W;
+            far |= (pvalid && !inreg && touch) ? (1u << k) : 0u;
+            cell[k] = inreg ? (ly * kRW + lx) * 8 + bc : bc;
+            tw[k][0] = tp.w00; tw[k][1] = tp.w01; tw[k][2] = tp.w10; tw[k][3] = tp.w11;
+        }
+        // corners of step (c, k): LDS, or xt for a far tap
+        auto load = [&](uint4 (&g)[4], int k, int c) __attribute__((always_inline)) {
+            if (far & (1u << k)) {
+                const float *so = s_off + (br * kRK + k) * 2;
+                int y0, x0;
+                float fy, fx;
+                split_coord(ho - p.ph + k / 3, so[1], y0, fy);
+                split_coord(wo - p.pw + k % 3, so[0], x0, fx);
+                const Tap tp = make_tap(y0, x0, fy, fx, 1.0f, p.H, p.W, p.Cin_pad);
+                g[0] = buffer_load<uint4>(rx, (img_off + tp.o00) * 2, c * kBK * 2);
+                g[1] = buffer_load<uint4>(rx, (img_off + tp.o01) * 2, c * kBK * 2);
+                g[2] = buffer_load<uint4>(rx, (img_off + tp.o10) * 2, c * kBK * 2);
+                g[3] = buffer_load<uint4>(rx, (img_off + tp.o11) * 2, c * kBK * 2);
+            } else {
+                const uint4 *q = &sR[c & 1][cell[k]];
+                g[0] = q[0];
+                g[1] = q[8];
+                g[2] = q[kRW * 8];
+                g[3] = q[kRW * 8 + 8];
+            }
+        };
+        auto fill = [&](const uint4 (&g)[4], int k, int buf) __attribute__((always_inline)) {
+            float acc[kVec];
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) acc[e] = 0.0f;
+#pragma unroll
+            for (int cn = 0; cn < 4; ++cn) {
+                float f[kVec];
+                load_f32<E, kVec>(reinterpret_cast<const typename E::bits *>(&g[cn]), f);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) acc[e] = fmaf(tw[k][cn], f[e], acc[e]);
+            }
+            typename E::bits b[kVec];
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) b[e] = from_f32(E{}, acc[e]);
+            uint4 v;
+            __builtin_memcpy(&v, b, 16);
+            sB[buf][bdst] = v;
+        };
+        // three stage registers used in turn (step t's corners in st[t % 3], loaded two
+        // steps ahead; 9 steps per channel block keep t % 3 = k % 3)
+        uint4 st[3][4];
+        load(st[0], 0, 0);
+        load(st[1], 1, 0);
+        fill(st[0], 0, 0);
+        lds_barrier();  // step 0's column tile is in buffer 0
+        for (int c = 0; c < CBn; ++c) {
+#pragma unroll
+            for (int k = 0; k < kRK; ++k) {
+                const int t = c * kRK + k;
+                if (k == 7 && c + 2 < CBn) stage(c + 2, c & 1);  // region c read for the last time
+                if (t + 2 < NS) load(st[(k + 2) % 3], (k + 2) % kRK, c + (k + 2) / kRK);
+                if (t + 1 < NS) fill(st[(k + 1) % 3], (k + 1) % kRK, (t + 1) & 1);
+                if (k == 6 && c + 1 < CBn) V2_WAIT_VMCNT(0);  // region c+1, read from the next step on
+                lds_barrier();
+            }
+        }
+        return;
+    }
+
+    // ---------------------------------------------------------------- MMA waves --
+    // As in v2_ws_kernel; step t = 9c + k takes the weight fragments of K block
+    // k * CB + c.
+    const int frow = lane & 31, fhalf = lane >> 5;
+    const unsigned wp_bytes = (unsigned)((size_t)(p.Mp - m0) * p.Rp * 2);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(wp + (size_t)m0 * p.Rp, wp_bytes);
+    int aoff[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) aoff[t] = (wave * 2 + t) * p.Rp * 64 + lane * 16;
+    uint4 fa[2][2][4];  // [set][tile][ks]
+    auto load_a = [&](uint4 (&f)[2][4], int t) __attribute__((always_inline)) {
+        const int sw = (t % kRK) * CBn + t / kRK;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) f[u][ks] = buffer_load<uint4>(ra, aoff[u], (sw * 4 + ks) * 1024);
+    };
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    auto mma = [&](const uint4 (&f)[2][4], int t) __attribute__((always_inline)) {
+        const v4u *sb = reinterpret_cast<const v4u *>(sB[t & 1]);
+#pragma unroll
+        for (int ks = 0; ks < kBK / 16; ++ks) {
+            const int cc = 2 * ks + fhalf;
+            v4u fb[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int rb = u * 32 + frow;
+                fb[u] = sb[rb * 8 + (cc ^ ((rb >> 1) & 7))];
+            }
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = mfma32<E>(f[a][ks], __builtin_bit_cast(uint4, fb[b]), acc[a][b]);
+        }
+    };
+    load_a(fa[0], 0);
+    lds_barrier();  // step 0's column tile
+    int t = 0;
+    for (; t + 1 < NS; t += 2) {
+        load_a(fa[1], t + 1);
+        asm volatile("" ::: "memory");
+        mma(fa[0], t);
+        lds_barrier();
+        load_a(fa[0], t + 2 < NS ? t + 2 : t + 1);
+        asm volatile("" ::: "memory");
+        mma(fa[1], t + 1);
+        lds_barrier();
+    }
+    if (t < NS) {  // odd step count: the last step's fragments are in set 0
+        mma(fa[0], t);
+        lds_barrier();
+    }
+    // epilogue: column j of a 32x32 tile is tile pixel b*32 + j = 8 py + px
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int pl = b * 32 + (lane & 31);
+        const int ho = ty0 + (pl >> 3), wo = tx0 + (pl & 7);
+        if (ho >= p.Ho || wo >= p.Wo) continue;
+        const int hw = ho * p.Wo + wo;
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int co = m0 + wave * 64 + a * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                if (co < p.Cout)
+                    out[((size_t)n * p.Cout + co) * HWo + hw] = from_f32(E{}, acc[a][b][r]);
+            }
+        }
+    }
+}
+
+// Layers taken by v2_wsr_kernel when fused; their two-stage GEMM visits the K tiles in
+// the same channel-block-major order.
+bool v2_region_order(const V2Launch &a) {
+    return a.kh == 3 && a.kw == 3 && a.sh == 1 && a.sw == 1 && a.dh == 1 && a.dw == 1 && a.dg == 1 &&
+           a.plan.Cin_pad % kBK == 0;
+}
+
 template <class E>
 hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     const V2Plan &pl = a.plan;
@@ -472,8 +752,17 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
         fp.Mtiles = (pl.Mp + kFBM - 1) / kFBM;
         fp.nblocks = (int)(fp.Mtiles * ((pl.P + kFBN - 1) / kFBN));
         fp.xt_bytes = (unsigned)((size_t)a.N * a.H * a.W * pl.Cin_pad * 2);
-        hipLaunchKernelGGL(v2_ws_kernel<E>, dim3(fp.nblocks), dim3(kWSThreads), fused_lds, stream, xt,
-                           a.offset, a.mask, wp_in ? wp_in : wp, static_cast<uint16_t *>(a.out), fp);
+        const uint16_t *wf = wp_in ? wp_in : wp;
+        if (v2_region_order(a)) {
+            fp.tiles_x = (pl.Wo + kRT - 1) / kRT;
+            fp.tiles_y = (pl.Ho + kRT - 1) / kRT;
+            fp.nblocks = fp.Mtiles * a.N * fp.tiles_x * fp.tiles_y;
+            hipLaunchKernelGGL(v2_wsr_kernel<E>, dim3(fp.nblocks), dim3(kWSThreads), 0, stream, xt, a.offset,
+                               a.mask, wf, static_cast<uint16_t *>(a.out), fp);
+        } else {
+            hipLaunchKernelGGL(v2_ws_kernel<E>, dim3(fp.nblocks), dim3(kWSThreads), fused_lds, stream, xt,
+                               a.offset, a.mask, wf, static_cast<uint16_t *>(a.out), fp);
+        }
         return hipGetLastError();
     }
 
@@ -507,6 +796,10 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     gp.Mtiles = pl.Mp / kBM;
     gp.Ntiles = (int)(pl.Pp / kBN);
     gp.nblocks = gp.Mtiles * gp.Ntiles;
+    if (v2_region_order(a)) {
+        gp.perm_taps = pl.K;
+        gp.perm_cb = pl.Cin_pad / kBK;
+    }
     // short reductions (few K tiles): the two-slot ring, two blocks per CU
     if (gp.nk <= 8)
         hipLaunchKernelGGL((v2_gemm_kernel<E, 0, 2>), dim3(gp.nblocks), dim3(kGemmThreads), 0, stream, wp, col,

@@ -187,7 +187,14 @@ struct GemmParams {
     long long P;
     int ldc, Mstore, Nstore;
     long long split_stride;
+    // K tile order: natural (perm_taps 0), or channel-block-major over taps: step kt
+    // takes tile (kt % perm_taps) * perm_cb + kt / perm_taps (perm_taps * perm_cb tiles)
+    int perm_taps, perm_cb;
 };
+
+__device__ __forceinline__ int gemm_ktile(const GemmParams &p, int kt) {
+    return p.perm_taps ? (kt % p.perm_taps) * p.perm_cb + kt / p.perm_taps : kt;
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -251,9 +258,9 @@ __device__ __forceinline__ void gemm_dma(uint4 *slot, const uint16_t *g, int ld,
 // barrier, refill the slot the previous step used with tile kt + NS - 1, then
 // 4 x (2 x kTB) MFMAs.
 template <class E, int S, int NS>
-__device__ __forceinline__ void gemm_step(int kt, int nk, const uint16_t *ga, const uint16_t *gb, int lda,
-                                          int ldb, f32x16_t (&acc)[2][kTB], int wm, int wn, int frow,
-                                          int fhalf) {
+__device__ __forceinline__ void gemm_step(int kt, int nk, const uint16_t *ga, const uint16_t *gb,
+                                          const GemmParams &p, f32x16_t (&acc)[2][kTB], int wm, int wn,
+                                          int frow, int fhalf) {
     if (kt >= nk) return;
     // this wave's copies issued after tile kt: min(nk-1-kt, NS-2) tiles x 2 operands
     const int after = (nk - 1 - kt) < (NS - 2) ? (nk - 1 - kt) : (NS - 2);
@@ -265,8 +272,9 @@ __device__ __forceinline__ void gemm_step(int kt, int nk, const uint16_t *ga, co
     const int nx = kt + NS - 1;
     if (nx < nk) {
         constexpr int R = (S + NS - 1) % NS;
-        gemm_dma(ring_a<R>(), ga, lda, nx * kBK);
-        gemm_dma(ring_b<R>(), gb, ldb, nx * kBK);
+        const int k0 = gemm_ktile(p, nx) * kBK;
+        gemm_dma(ring_a<R>(), ga, p.lda, k0);
+        gemm_dma(ring_b<R>(), gb, p.ldb, k0);
     }
     const uint4 *sa = ring_a<S>();
     const uint4 *sb = ring_b<S>();
@@ -321,19 +329,31 @@ __global__ __launch_bounds__(kGemmThreads) void v2_gemm_kernel(const uint16_t *_
 
     static_assert(NS == 2 || NS == 4, "ring of two or four slots");
     // prologue: tiles 0 .. NS-2 in flight
-    if (0 < nk) { gemm_dma(ring_a<0>(), ga, p.lda, 0); gemm_dma(ring_b<0>(), gb, p.ldb, 0); }
+    if (0 < nk) {
+        const int k0 = gemm_ktile(p, 0) * kBK;
+        gemm_dma(ring_a<0>(), ga, p.lda, k0);
+        gemm_dma(ring_b<0>(), gb, p.ldb, k0);
+    }
     if constexpr (NS == 4) {
-        if (1 < nk) { gemm_dma(ring_a<1>(), ga, p.lda, kBK); gemm_dma(ring_b<1>(), gb, p.ldb, kBK); }
-        if (2 < nk) { gemm_dma(ring_a<2>(), ga, p.lda, 2 * kBK); gemm_dma(ring_b<2>(), gb, p.ldb, 2 * kBK); }
+        if (1 < nk) {
+            const int k0 = gemm_ktile(p, 1) * kBK;
+            gemm_dma(ring_a<1>(), ga, p.lda, k0);
+            gemm_dma(ring_b<1>(), gb, p.ldb, k0);
+        }
+        if (2 < nk) {
+            const int k0 = gemm_ktile(p, 2) * kBK;
+            gemm_dma(ring_a<2>(), ga, p.lda, k0);
+            gemm_dma(ring_b<2>(), gb, p.ldb, k0);
+        }
     }
     // fragment of lane l in a 16-deep k step ks: row (l % 32), logical chunk 2*ks + l/32
     const int frow = lane & 31, fhalf = lane >> 5;
     for (int kt = 0; kt < nk; kt += NS) {
-        gemm_step<E, 0, NS>(kt + 0, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
-        gemm_step<E, 1, NS>(kt + 1, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
+        gemm_step<E, 0, NS>(kt + 0, nk, ga, gb, p, acc, wm, wn, frow, fhalf);
+        gemm_step<E, 1, NS>(kt + 1, nk, ga, gb, p, acc, wm, wn, frow, fhalf);
         if constexpr (NS == 4) {
-            gemm_step<E, 2, NS>(kt + 2, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
-            gemm_step<E, 3, NS>(kt + 3, nk, ga, gb, p.lda, p.ldb, acc, wm, wn, frow, fhalf);
+            gemm_step<E, 2, NS>(kt + 2, nk, ga, gb, p, acc, wm, wn, frow, fhalf);
+            gemm_step<E, 3, NS>(kt + 3, nk, ga, gb, p, acc, wm, wn, frow, fhalf);
         }
     }
 

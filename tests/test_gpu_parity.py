@@ -222,6 +222,18 @@ V2_SWEEP = [
     ("fused_wide_f16_k1x3", dict(N=1, Cin=128, H=6, W=10, Cout=48, kh=1, kw=3, pad=(0, 1),
                                  dtype="f16")),
     ("fused_wide_softmax", dict(N=2, Cin=128, H=9, W=8, Cout=72, mask="logits", dtype="bf16")),
+    # 3x3 at stride 1 and dilation 1 with one group: the staged-region kernel (8x8 pixel
+    # tiles, partial at the image edge; 1, 2, 3 and 5 channel blocks), other paddings, no
+    # mask, softmax without mask, and offsets wide enough that many taps leave the
+    # +-6-px region and are read from memory
+    ("region_pad0_mask_none", dict(N=1, Cin=64, H=13, W=17, Cout=40, pad=(0, 0), mask=None,
+                                   dtype="bf16")),
+    ("region_softmax_mask_none_f16", dict(N=2, Cin=128, H=9, W=12, Cout=24, mask=None, dtype="f16"),
+     dict(softmax=True)),
+    ("region_far_taps_pad21", dict(N=1, Cin=64, H=20, W=21, Cout=32, pad=(2, 1), offset_std=6.0,
+                                   dtype="bf16")),
+    ("region_cin192", dict(N=1, Cin=192, H=10, W=9, Cout=16, dtype="bf16")),
+    ("region_cin320_softmax", dict(N=1, Cin=320, H=6, W=7, Cout=8, mask="logits", dtype="f16")),
 ]
 V2_SWEEP = [s if len(s) == 3 else s + ({},) for s in V2_SWEEP]
 
