@@ -475,28 +475,27 @@ __global__ __launch_bounds__(kWSThreads) void v2_wsr_kernel(const uint16_t *__re
     const int CBn = p.CB;
     const int NS = kRK * CBn;
 
-    // region of channel block c into buffer b (producer waves only): copy j of a lane
-    // moves region chunk i = j * 512 + (producer thread); chunks outside the image get
-    // an offset past the end of the resource over xt and read as zeros
-    const rsrc_words_t rxw = rsrc_words(xt, p.xt_bytes);
-    auto stage = [&](int c, int b) __attribute__((always_inline)) {
-        const int pwv = wave - kWSConsumers;
-#pragma unroll
-        for (int j = 0; j < kRCopies; ++j) {
-            const int i0 = j * kWSPThreads + pwv * 64;
-            if (i0 < kRChunks) {
-                const int i = i0 + lane;
-                const int q = i >> 3, cc = i & 7;
-                const int ry = q / kRW, rx = q - ry * kRW;
-                const int yy = ry0 + ry, xx = rx0 + rx;
-                const bool ok = (unsigned)yy < (unsigned)p.H && (unsigned)xx < (unsigned)p.W;
-                const int voff = ok ? ((n * p.H + yy) * p.W + xx) * p.Cin_pad * 2 + cc * 16 : (int)p.xt_bytes;
-                if (i < kRChunks) lds_copy16_buf(lds_addr(&sR[b][i0]), rxw, voff, c * kBK * 2);
-            }
-        }
+    // Region chunk i = 8 * (region pixel) + (16-byte chunk): its byte offset in xt, or an
+    // offset past the end of the resource over xt (reads as zeros) outside the image
+    auto region_voff = [&](int i) __attribute__((always_inline)) {
+        const int q = i >> 3, cc = i & 7;
+        const int ry = q / kRW, rx = q - ry * kRW;
+        const int yy = ry0 + ry, xx = rx0 + rx;
+        const bool ok = (unsigned)yy < (unsigned)p.H && (unsigned)xx < (unsigned)p.W;
+        return ok ? ((n * p.H + yy) * p.W + xx) * p.Cin_pad * 2 + cc * 16 : (int)p.xt_bytes;
     };
-
-    if (wave >= kWSConsumers) stage(0, 0);
+    // Copy j (< kRCopies) of a producer lane moves region chunk j * 512 + (producer
+    // thread) of channel block c into buffer b.
+    const rsrc_words_t rxw = rsrc_words(xt, p.xt_bytes);
+    auto region_copy = [&](int j, int c, int b) __attribute__((always_inline)) {
+        const int i0 = j * kWSPThreads + (wave - kWSConsumers) * 64;
+        if (i0 < kRChunks && i0 + lane < kRChunks)
+            lds_copy16_buf(lds_addr(&sR[b][i0]), rxw, region_voff(i0 + lane), c * kBK * 2);
+    };
+    if (wave >= kWSConsumers) {  // region 0, waited for below
+#pragma unroll
+        for (int j = 0; j < kRCopies; ++j) region_copy(j, 0, 0);
+    }
     // offsets and masks of the tile's pixels: pixel pl = 8 py + px
     for (int i = tid; i < kFBN * kRK * 2; i += kWSThreads) {
         const int pl = i % kFBN, c = i / kFBN;
@@ -529,7 +528,6 @@ __global__ __launch_bounds__(kWSThreads) void v2_wsr_kernel(const uint16_t *__re
 
     if (wave >= kWSConsumers) {
         // ------------------------------------------------------------ producers --
-        if (CBn > 1) stage(1, 1);
         const int ptid = tid - 64 * kWSConsumers;
         const int br = ptid >> 3, bc = ptid & 7;
         const int ho = ty0 + (br >> 3), wo = tx0 + (br & 7);
@@ -598,8 +596,13 @@ __global__ __launch_bounds__(kWSThreads) void v2_wsr_kernel(const uint16_t *__re
             __builtin_memcpy(&v, b, 16);
             sB[buf][bdst] = v;
         };
-        // three stage registers used in turn (step t's corners in st[t % 3], loaded two
-        // steps ahead; 9 steps per channel block keep t % 3 = k % 3)
+        // Step t's corners sit in stage registers st[t % 3], loaded two steps ahead (9
+        // steps per channel block keep t % 3 = k % 3); its column tile goes to sB[t & 1].
+        // Region r sits in sR[r & 1]. Region c + 1 is copied during steps 0..5 of block c,
+        // into the buffer that region c - 1 left (last read in step 6 of block c - 1),
+        // one or two copies per step so that a wait for a far tap's corners finds the
+        // copies of earlier steps landed; all are waited for in step 6 (the loads from
+        // step 7 on read it).
         uint4 st[3][4];
         load(st[0], 0, 0);
         load(st[1], 1, 0);
@@ -609,10 +612,14 @@ __global__ __launch_bounds__(kWSThreads) void v2_wsr_kernel(const uint16_t *__re
 #pragma unroll
             for (int k = 0; k < kRK; ++k) {
                 const int t = c * kRK + k;
-                if (k == 7 && c + 2 < CBn) stage(c + 2, c & 1);  // region c read for the last time
                 if (t + 2 < NS) load(st[(k + 2) % 3], (k + 2) % kRK, c + (k + 2) / kRK);
                 if (t + 1 < NS) fill(st[(k + 1) % 3], (k + 1) % kRK, (t + 1) & 1);
-                if (k == 6 && c + 1 < CBn) V2_WAIT_VMCNT(0);  // region c+1, read from the next step on
+                if (c + 1 < CBn) {
+                    static_assert(kRCopies <= 12, "two copies per step at most");
+                    if (k < 6) region_copy(k, c + 1, (c + 1) & 1);
+                    if (k < kRCopies - 6) region_copy(k + 6, c + 1, (c + 1) & 1);
+                    if (k == 6) V2_WAIT_VMCNT(0);
+                }
                 lds_barrier();
             }
         }
