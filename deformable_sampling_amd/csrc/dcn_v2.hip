@@ -185,14 +185,6 @@ static_assert(kWSPThreads == kFBChunks, "one column chunk per producer thread an
 #define DCN_V2_WS_STAGES 2
 #endif
 
-// Barrier after this wave's LDS accesses have completed; global loads stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 template <class E>
 __global__ __launch_bounds__(kWSThreads) void v2_ws_kernel(const uint16_t *__restrict__ xt,
                                                            const float *__restrict__ offset,

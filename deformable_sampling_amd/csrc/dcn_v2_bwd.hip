@@ -99,11 +99,17 @@ __device__ __forceinline__ void v2b_softmax_stats(const float *__restrict__ mask
 
 // goT[co][p] = grad_out[n][co][hw] for p = n*HWo + hw; zero for co >= Cout or p >= P.
 // VEC: 8 consecutive pixels per thread (HWo and P multiples of 8, 16-byte aligned rows).
-// Block bi of the job.
+// FRAG: in MFMA fragment order instead of rows, value (co, p) at element
+// (((co/32 * Pp/16 + p/16) * 2 + (p/8) % 2) * 32 + co % 32) * 8 + p % 8 (the fused
+// weight-gradient kernel's operand). Block bi of the job.
+__device__ __forceinline__ long long got_index(long long co, long long pp, long long Pp, bool frag) {
+    if (!frag) return co * Pp + pp;
+    return ((((co >> 5) * (Pp >> 4) + (pp >> 4)) * 2 + ((pp >> 3) & 1)) * 32 + (co & 31)) * 8 + (pp & 7);
+}
 template <bool VEC>
 __device__ __forceinline__ void v2b_rows_block(int bi, const uint16_t *__restrict__ gout,
                                                uint16_t *__restrict__ goT, int Cout, int HWo, long long P,
-                                               long long Pp, long long total) {
+                                               long long Pp, long long total, bool frag) {
     const long long t = (long long)bi * kB + threadIdx.x;
     if constexpr (VEC) {
         if (t * 8 >= total) return;
@@ -114,7 +120,7 @@ __device__ __forceinline__ void v2b_rows_block(int bi, const uint16_t *__restric
             const long long n = pp / HWo, hw = pp - n * HWo;
             v = *reinterpret_cast<const uint4 *>(gout + ((size_t)n * Cout + co) * HWo + hw);
         }
-        *reinterpret_cast<uint4 *>(goT + e) = v;
+        *reinterpret_cast<uint4 *>(goT + got_index(co, pp, Pp, frag)) = v;
     } else {
         if (t >= total) return;
         const long long co = t / Pp, pp = t - co * Pp;
@@ -123,7 +129,7 @@ __device__ __forceinline__ void v2b_rows_block(int bi, const uint16_t *__restric
             const long long n = pp / HWo, hw = pp - n * HWo;
             v = gout[((size_t)n * Cout + co) * HWo + hw];
         }
-        goT[t] = v;
+        goT[got_index(co, pp, Pp, frag)] = v;
     }
 }
 
@@ -143,7 +149,7 @@ __device__ __forceinline__ void v2b_wt_block(int bi, const uint16_t *__restrict_
 struct V2bLayout {
     const uint16_t *gout, *w;
     uint16_t *wT, *goT;
-    int Cout, Cin, K, Cin_pad, CoK, HWo, rows_vec;
+    int Cout, Cin, K, Cin_pad, CoK, HWo, rows_vec, rows_frag;
     long long P, Pp, nwt, nrows;
     int *cnt;
     long long nzero;
@@ -156,9 +162,9 @@ __global__ __launch_bounds__(kB) void v2b_layout_kernel(const V2bLayout L) {
         v2b_wt_block(b, L.w, L.wT, L.Cout, L.Cin, L.K, L.Cin_pad, L.CoK, L.nwt);
     } else if (b < L.e_rows) {
         if (L.rows_vec)
-            v2b_rows_block<true>(b - L.e_wt, L.gout, L.goT, L.Cout, L.HWo, L.P, L.Pp, L.nrows);
+            v2b_rows_block<true>(b - L.e_wt, L.gout, L.goT, L.Cout, L.HWo, L.P, L.Pp, L.nrows, L.rows_frag);
         else
-            v2b_rows_block<false>(b - L.e_wt, L.gout, L.goT, L.Cout, L.HWo, L.P, L.Pp, L.nrows);
+            v2b_rows_block<false>(b - L.e_wt, L.gout, L.goT, L.Cout, L.HWo, L.P, L.Pp, L.nrows, L.rows_frag);
     } else {
         const int nb = L.e_zero - L.e_rows;
         for (long long i = (long long)(b - L.e_rows) * kB + threadIdx.x; i < L.nzero; i += (long long)nb * kB)
@@ -482,6 +488,236 @@ __global__ __launch_bounds__(kB) void v2b_out_kernel(const float *__restrict__ g
 
 // ----------------------------------------------------------------- launch --
 
+// ------------------------------------------------------ fused weight gradient --
+//
+// grad_weight partials without the transposed columns in memory (Cin % 64 == 0): the
+// GEMM grad_weight[co][r] = sum_p grad_out[p][co] * col[p][r] with the column tile
+// formed on chip, in the two-role structure of the forward's fused kernel. A block
+// takes 256 output channels x 64 columns r (one tap k, channel block cb) over the
+// pixel range of its split, in steps of 64 pixels. Producer waves form the step's
+// column tile (m * bilinear in fp32 as the forward forms it, rounded to the dtype)
+// and write it transposed into LDS, pixels contiguous per column r: row rr holds 64
+// pixels, 16-byte chunk cc at position cc ^ ((rr >> 3) + rr) & 7, so that both the
+// producers' 2-byte writes (8 rows rr = 8 bc + e at once) and the MMA waves' 16-byte
+// fragment reads (16 consecutive rows at once) fall on distinct banks. MMA waves read
+// grad_out (goT in MFMA fragment order: the 8 values (co, 16q + 8h .. +7) at 16-byte
+// slot ((co/32 * Pp/16 + q) * 2 + h) * 32 + co % 32) straight from memory one step
+// ahead, like the forward's weight. Partials go to wpart[split][co][r] for the fixed-
+// order sum of v2b_wsum_kernel. The block's pixels' tap data (the two offsets and the
+// modulation of tap k in the block's group, the grid base of the tap and the image)
+// are staged in LDS before the K loop, so a producer's step starts from LDS instead of
+// two dependent global loads; a block takes at most kWgMaxSteps steps (the plan raises
+// the number of splits accordingly), and one deformable group per 64-channel block.
+constexpr int kWgMaxSteps = 32;
+constexpr int kWgMma = 4;                          // MMA waves: 64 grad_out channels each
+constexpr int kWgProd = 8;                         // producer waves: 64 pixels x 8 chunks
+constexpr int kWgThreads = 64 * (kWgMma + kWgProd);
+
+struct V2bWgParams {
+    V2bGeo q;
+    int Cin_pad, cpg, CBn, R, Cout;
+    int steps, nsteps;  // 64-pixel steps per split and in all (Pp / 64)
+    int Mt, nblocks;    // 256-channel blocks of grad_out; blocks
+    long long Pp;
+    unsigned xt_bytes, got_bytes;
+};
+
+__device__ __forceinline__ int wg_swz(int rr) { return ((rr >> 3) + rr) & 7; }
+
+// whether the weight gradient of a layer takes v2b_wgrad_kernel
+__host__ __device__ inline bool v2b_wgrad_fused(int N, int H, int W, int Cin, int Cin_pad, int dg, int CoM,
+                                                long long Pp) {
+    const int Mt = (CoM + 255) / 256;
+    return Cin_pad % kBK == 0 && (dg == 1 || (Cin / dg) % kBK == 0) &&
+           (size_t)N * H * W * Cin_pad * 2 < (1ull << 31) && (size_t)Mt * 256 * Pp * 2 < (1ull << 31);
+}
+
+template <class E>
+__global__ __launch_bounds__(kWgThreads) void v2b_wgrad_kernel(const uint16_t *__restrict__ xt,
+                                                               const float *__restrict__ offset,
+                                                               const float *__restrict__ mask,
+                                                               const uint16_t *__restrict__ gotf,
+                                                               float *__restrict__ wpart,
+                                                               const V2bWgParams p) {
+    __shared__ uint4 sB[2][512];  // [64 columns r][8 chunks of 8 pixels], swizzled
+    // per pixel of the block: offsets (y, x) and modulation of tap k; grid base (y, x)
+    // of the tap and the image's first element in xt
+    __shared__ float4 s_tf[kWgMaxSteps * 64];
+    __shared__ int4 s_ti[kWgMaxSteps * 64];
+    const V2bGeo &q = p.q;
+    const int nrb = q.K * p.CBn;
+    const int blk = xcd_remap((int)blockIdx.x, p.nblocks);
+    // the blocks of one split are consecutive: one XCD shares the split's grad_out in L2
+    const int sp = blk / (nrb * p.Mt), rest = blk - sp * (nrb * p.Mt);
+    const int mt = rest / nrb, rb = rest - mt * nrb;
+    const int k = rb / p.CBn, cb = rb - k * p.CBn;
+    const int s0 = sp * p.steps;
+    const int NS = min(p.steps, p.nsteps - s0);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int HWo = q.Ho * q.Wo;
+    const int g = min(cb * kBK / p.cpg, q.dg - 1);  // the block's deformable group
+    {
+        const int i = k / q.kw, j = k - i * q.kw;
+        for (int t = tid; t < NS * 64; t += kWgThreads) {
+            const long long pg = (long long)s0 * 64 + t;
+            float4 f = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            int4 iv = make_int4(0, 0, 0, 0);
+            if (pg < q.P) {
+                const int n = (int)(pg / HWo), r = (int)(pg - (long long)n * HWo);
+                float mx, inv;
+                v2b_softmax_stats(mask, q, n, r, g, mx, inv);
+                const float *op = offset + ((size_t)(n * q.dg + g) * q.K + k) * 2 * HWo + r;
+                const int ho = r / q.Wo, wo = r - ho * q.Wo;
+                f = make_float4(op[HWo], op[0], v2b_mod(mask, q, n, r, g, k, mx, inv), 0.0f);
+                iv = make_int4(ho * q.sh - q.ph + i * q.dh, wo * q.sw - q.pw + j * q.dw, n * q.H * q.W * p.Cin_pad, 0);
+            }
+            s_tf[t] = f;
+            s_ti[t] = iv;
+        }
+        __syncthreads();
+    }
+
+    if (wave >= kWgMma) {
+        // ------------------------------------------------------------ producers --
+        if (NS <= 0) return;  // an empty split: the MMA waves store zeros, no barriers
+        const int ptid = tid - 64 * kWgMma;
+        const int br = ptid >> 3, bc = ptid & 7;
+        const int c0 = cb * kBK + bc * kVec;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(xt, p.xt_bytes);
+        struct Stage {
+            uint4 v[4];
+            float w[4];
+        };
+        // corners of step s (pixel (s0 + s) * 64 + br), loaded unconditionally (pixels
+        // past P read offset 0 with weight 0) so the count of loads in flight is exact
+        auto load = [&](Stage &st, int s) __attribute__((always_inline)) {
+            // pixels past P were staged with modulation 0: weight 0, corners in the image
+            const float4 f = s_tf[s * 64 + br];
+            const int4 iv = s_ti[s * 64 + br];
+            int y0, x0;
+            float fy, fx;
+            split_coord(iv.x, f.x, y0, fy);
+            split_coord(iv.y, f.y, x0, fx);
+            const Tap t = make_tap(y0, x0, fy, fx, f.z, q.H, q.W, p.Cin_pad);
+            const int base = iv.z + c0;
+            st.v[0] = buffer_load<uint4>(rx, (base + t.o00) * 2, 0);
+            st.v[1] = buffer_load<uint4>(rx, (base + t.o01) * 2, 0);
+            st.v[2] = buffer_load<uint4>(rx, (base + t.o10) * 2, 0);
+            st.v[3] = buffer_load<uint4>(rx, (base + t.o11) * 2, 0);
+            st.w[0] = t.w00; st.w[1] = t.w01; st.w[2] = t.w10; st.w[3] = t.w11;
+        };
+        auto fill = [&](const Stage &st, int buf) __attribute__((always_inline)) {
+            float acc[kVec];
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) acc[e] = 0.0f;
+#pragma unroll
+            for (int cn = 0; cn < 4; ++cn) {
+                float f[kVec];
+                load_f32<E, kVec>(reinterpret_cast<const typename E::bits *>(&st.v[cn]), f);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) acc[e] = fmaf(st.w[cn], f[e], acc[e]);
+            }
+            uint16_t *t16 = reinterpret_cast<uint16_t *>(sB[buf]);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                const int rr = bc * kVec + e;
+                t16[rr * 64 + (((br >> 3) ^ wg_swz(rr)) << 3) + (br & 7)] = (uint16_t)from_f32(E{}, acc[e]);
+            }
+        };
+        Stage st[2];
+        load(st[0], 0);
+        load(st[1], NS > 1 ? 1 : 0);
+        fill(st[0], 0);
+        lds_barrier();  // step 0's column tile is in buffer 0
+        for (int s = 0; s < NS; s += 2) {
+            // buffer s & 1 is read by the MMA waves; fill the other
+            load(st[0], s + 2 < NS ? s + 2 : NS - 1);
+            if (s + 1 < NS) fill(st[1], 1);
+            lds_barrier();
+            if (s + 1 < NS) {
+                load(st[1], s + 3 < NS ? s + 3 : NS - 1);
+                if (s + 2 < NS) fill(st[0], 0);
+                lds_barrier();
+            }
+        }
+        return;
+    }
+
+    // ---------------------------------------------------------------- MMA waves --
+    const int frow = lane & 31, fhalf = lane >> 5;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(gotf, p.got_bytes);
+    int aoff[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        aoff[t] = (int)((long long)(mt * 8 + wave * 2 + t) * p.Pp * 64) + lane * 16;  // 1 KB per (32 rows, 16 pixels)
+    uint4 fa[2][2][4];  // [set][tile][ks]
+    auto load_a = [&](uint4 (&f)[2][4], int s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) f[t][ks] = buffer_load<uint4>(ra, aoff[t], ((s0 + s) * 4 + ks) * 1024);
+    };
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+    auto mma = [&](const uint4 (&f)[2][4], int s) __attribute__((always_inline)) {
+        const uint4 *sb = sB[s & 1];
+#pragma unroll
+        for (int ks = 0; ks < kBK / 16; ++ks) {
+            const int cc = 2 * ks + fhalf;
+            uint4 fb[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int rr = u * 32 + frow;
+                fb[u] = sb[rr * 8 + (cc ^ wg_swz(rr))];
+            }
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) acc[a][b] = mfma32<E>(f[a][ks], fb[b], acc[a][b]);
+        }
+    };
+    if (NS > 0) {
+        load_a(fa[0], 0);
+        lds_barrier();  // step 0's column tile
+        int s = 0;
+        for (; s + 1 < NS; s += 2) {
+            load_a(fa[1], s + 1);
+            asm volatile("" ::: "memory");
+            mma(fa[0], s);
+            lds_barrier();
+            load_a(fa[0], s + 2 < NS ? s + 2 : s + 1);
+            asm volatile("" ::: "memory");
+            mma(fa[1], s + 1);
+            lds_barrier();
+        }
+        if (s < NS) {  // odd step count: the last step's fragments are in set 0
+            mma(fa[0], s);
+            lds_barrier();
+        }
+    }
+    // D[i][j] of a 32x32 tile: lane j + 32*((i/4)%2), register 4*(i/8) + i%4; row i a
+    // grad_out channel co, column j a column r
+    float *o = wpart + (size_t)sp * p.Cout * p.R;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int rcol = k * p.Cin_pad + cb * kBK + b * 32 + (lane & 31);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int co = mt * 256 + wave * 64 + a * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                if (co < p.Cout) o[(size_t)co * p.R + rcol] = acc[a][b][r];
+            }
+        }
+    }
+}
+
 template <class E>
 hipError_t launch_e(const V2BwdLaunch &a, hipStream_t stream) {
     const V2BwdPlan &pl = a.plan;
@@ -518,6 +754,11 @@ hipError_t launch_e(const V2BwdLaunch &a, hipStream_t stream) {
         pp.n_tr_blocks = pp.reg ? (a.N * pp.cgroups * pp.hgroups + 3) / 4 : a.N * pp.tiles_c * pp.tiles_hw;
         return pp;
     };
+    // the weight gradient with the columns formed on chip: 64-channel column blocks within
+    // a tap, and 32-bit byte offsets into xt and the fragment-order goT
+    const int Mt = (pl.CoM + 255) / 256;
+    const bool wg_fused = v2b_wgrad_fused(a.N, a.H, a.W, a.Cin, pl.Cin_pad, a.dg, pl.CoM, pl.Pp) &&
+                          (pl.Pp / kBK + pl.splits - 1) / pl.splits <= kWgMaxSteps;  // as the plan arranges
     V2bGeo q;
     q.N = a.N; q.H = a.H; q.W = a.W; q.Ho = pl.Ho; q.Wo = pl.Wo; q.kh = a.kh; q.kw = a.kw;
     q.sh = a.sh; q.sw = a.sw; q.ph = a.ph; q.pw = a.pw; q.dh = a.dh; q.dw = a.dw; q.dg = a.dg;
@@ -554,6 +795,7 @@ hipError_t launch_e(const V2BwdLaunch &a, hipStream_t stream) {
         if (want_w) {
             L.nrows = (long long)pl.CoM * pl.Pp;
             L.rows_vec = HWo % 8 == 0 && (uintptr_t)a.grad_out % 16 == 0;  // then P % 8 == 0 too
+            L.rows_frag = wg_fused ? 1 : 0;
             nb += (int)(((L.rows_vec ? L.nrows / 8 : L.nrows) + kB - 1) / kB);
         }
         L.e_rows = nb;
@@ -568,7 +810,30 @@ hipError_t launch_e(const V2BwdLaunch &a, hipStream_t stream) {
             if ((err = hipGetLastError()) != hipSuccess) return err;
         }
     }
-    if (want_w) {
+    if (want_w && wg_fused) {
+        // 2-4. weight-gradient partials with the columns formed on chip, 5. their sum
+        V2bWgParams wg;
+        wg.q = q;
+        wg.Cin_pad = pl.Cin_pad;
+        wg.cpg = a.Cin / a.dg;
+        wg.CBn = pl.Cin_pad / kBK;
+        wg.R = pl.R;
+        wg.Cout = a.Cout;
+        wg.nsteps = (int)(pl.Pp / kBK);
+        wg.steps = (wg.nsteps + pl.splits - 1) / pl.splits;  // the plan's splits, all non-empty
+        wg.Mt = Mt;
+        wg.nblocks = pl.splits * Mt * pl.K * wg.CBn;
+        wg.Pp = pl.Pp;
+        wg.xt_bytes = (unsigned)((size_t)a.N * a.H * a.W * pl.Cin_pad * 2);
+        wg.got_bytes = (unsigned)((size_t)pl.CoM * pl.Pp * 2);
+        hipLaunchKernelGGL(v2b_wgrad_kernel<E>, dim3(wg.nblocks), dim3(kWgThreads), 0, stream, xt, a.offset,
+                           a.mask, goT, wpart, wg);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        const long long nw = (long long)a.Cout * pl.R;
+        hipLaunchKernelGGL(v2b_wsum_kernel, dim3((unsigned)((nw + kB - 1) / kB)), dim3(kB), 0, stream,
+                           wpart, a.grad_weight, a.Cout, a.Cin, pl.K, pl.Cin_pad, pl.R, pl.splits);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    } else if (want_w) {
         // 2. transposed columns
         V2bColParams cp;
         cp.q = q;
@@ -695,6 +960,11 @@ bool plan_dcn_v2_bwd(int N, int Cin, int H, int W, int Cout, int kh, int kw, int
     const long long tiles = (long long)(pl.CoM / kBM) * (pl.Rr / kBN);
     const long long nk = pl.Pp / kBK;
     long long splits = tiles >= 256 ? 1 : 256 / tiles;
+    // the fused weight-gradient kernel takes at most kWgMaxSteps 64-pixel steps per split
+    if (v2b_wgrad_fused(N, H, W, Cin, pl.Cin_pad, dg, pl.CoM, pl.Pp)) {
+        const long long need = (nk + kWgMaxSteps - 1) / kWgMaxSteps;
+        if (splits < need) splits = need;
+    }
     if (splits > nk) splits = nk;
     if (splits < 1) splits = 1;
     const long long per = (nk + splits - 1) / splits;

@@ -203,6 +203,14 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 #define V2_WAIT_VMCNT(n) \
     __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
 
+// Barrier after this wave's LDS accesses have completed; global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 constexpr int kStages = 4;                          // K tiles in flight (LDS ring), at most
 constexpr int kTileChunks = kBM * kBK / 8;          // 16-byte chunks per operand tile (1024)
 // Waves per GEMM block: 8 (2 x 4, 64 x 32 each: two per SIMD, so one wave's LDS

@@ -76,6 +76,12 @@ SWEEP = [
     ("bf16_far_offsets", dict(N=1, Cin=16, H=10, W=11, Cout=16, offset_std=12.0, dtype="bf16")),
     ("bf16_c320_many_pixels", dict(N=2, Cin=320, H=13, W=17, Cout=72, dtype="bf16")),
     ("bf16_1x1_image", dict(N=3, Cin=8, H=1, W=1, Cout=8, dtype="bf16")),
+    # Cin a multiple of 64: the weight gradient with the columns formed on chip (several
+    # pixel splits, grad_out channels past one 256-row block, tiny pixel counts, softmax)
+    ("bf16_c64_stride2", dict(N=2, Cin=64, H=11, W=13, Cout=40, stride=(2, 2), dtype="bf16")),
+    ("f16_c128_softmax", dict(N=1, Cin=128, H=7, W=9, Cout=24, mask="logits", dtype="f16")),
+    ("bf16_c64_cout300", dict(N=1, Cin=64, H=6, W=7, Cout=300, dtype="bf16")),
+    ("bf16_c64_1x1_image", dict(N=3, Cin=64, H=1, W=1, Cout=8, dtype="bf16")),
 ]
 
 
