@@ -449,7 +449,7 @@ __global__ __launch_bounds__(kWSThreads) void v2_wsr_kernel(const uint16_t *__re
                                                             uint16_t *__restrict__ out,
                                                             const FusedParams p) {
     __shared__ uint4 sR[2][kRChunks];    // region buffers, [pixel row][pixel][8 chunks]
-    __shared__ uint4 sB[2][kFBChunks];   // column tiles, as in v2_ws_kernel
+    __shared__ uint4 sB[4][kFBChunks];   // column tiles (layout as in v2_ws_kernel), step t in t % 4
     __shared__ float s_off[kFBN * kRK * 2];
     __shared__ float s_m[kFBN * kRK];
 
@@ -595,26 +595,32 @@ __global__ __launch_bounds__(kWSThreads) void v2_wsr_kernel(const uint16_t *__re
         // one or two copies per step so that a wait for a far tap's corners finds the
         // copies of earlier steps landed; all are waited for in step 6 (the loads from
         // step 7 on read it).
+        // One barrier per two steps: between barriers j and j + 1 the MMA waves take
+        // tiles 2j and 2j + 1 and the producers fill tiles 2j + 2 and 2j + 3 (four
+        // column-tile buffers, tile t in sB[t % 4]); barrier j follows step 2j + 1's
+        // fill, so the K loop of NS steps has 1 + ceil(NS / 2) barriers in each role.
         uint4 st[3][4];
         load(st[0], 0, 0);
         load(st[1], 1, 0);
-        fill(st[0], 0, 0);
-        lds_barrier();  // step 0's column tile is in buffer 0
         for (int c = 0; c < CBn; ++c) {
 #pragma unroll
             for (int k = 0; k < kRK; ++k) {
-                const int t = c * kRK + k;
-                if (t + 2 < NS) load(st[(k + 2) % 3], (k + 2) % kRK, c + (k + 2) / kRK);
-                if (t + 1 < NS) fill(st[(k + 1) % 3], (k + 1) % kRK, (t + 1) & 1);
+                const int u = c * kRK + k;
+                if (u + 2 < NS) load(st[(k + 2) % 3], (k + 2) % kRK, c + (k + 2) / kRK);
+                fill(st[k % 3], k, u & 3);
                 if (c + 1 < CBn) {
                     static_assert(kRCopies <= 12, "two copies per step at most");
                     if (k < 6) region_copy(k, c + 1, (c + 1) & 1);
                     if (k < kRCopies - 6) region_copy(k + 6, c + 1, (c + 1) & 1);
-                    if (k == 6) V2_WAIT_VMCNT(0);
+                    // region c + 1 is first read by step 7's loads: wait before the last
+                    // barrier ahead of them (after step 5 or 6, whichever is odd)
+                    if ((k == 5 || k == 6) && (u & 1)) V2_WAIT_VMCNT(0);
                 }
-                lds_barrier();
+                if (u & 1) lds_barrier();
             }
         }
+        lds_barrier();  // the MMA waves' last pair
+        if (NS & 1) lds_barrier();
         return;
     }
 
@@ -644,7 +650,7 @@ __global__ __launch_bounds__(kWSThreads) void v2_wsr_kernel(const uint16_t *__re
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
     auto mma = [&](const uint4 (&f)[2][4], int t) __attribute__((always_inline)) {
-        const v4u *sb = reinterpret_cast<const v4u *>(sB[t & 1]);
+        const v4u *sb = reinterpret_cast<const v4u *>(sB[t & 3]);
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
             const int cc = 2 * ks + fhalf;
@@ -662,13 +668,12 @@ __global__ __launch_bounds__(kWSThreads) void v2_wsr_kernel(const uint16_t *__re
         }
     };
     load_a(fa[0], 0);
-    lds_barrier();  // step 0's column tile
+    lds_barrier();  // tiles 0 and 1
     int t = 0;
     for (; t + 1 < NS; t += 2) {
         load_a(fa[1], t + 1);
         asm volatile("" ::: "memory");
         mma(fa[0], t);
-        lds_barrier();
         load_a(fa[0], t + 2 < NS ? t + 2 : t + 1);
         asm volatile("" ::: "memory");
         mma(fa[1], t + 1);
