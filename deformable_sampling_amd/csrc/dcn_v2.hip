@@ -720,7 +720,7 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     uint16_t *col = reinterpret_cast<uint16_t *>(ws + pl.off_col);
 
     // 1. prep
-    PrepParams pp;
+    PrepParams pp = {};
     pp.N = a.N; pp.Cin = a.Cin; pp.HW = a.H * a.W; pp.Cin_pad = pl.Cin_pad;
     pp.vec = (pp.HW % kVec == 0) && ((uintptr_t)a.x % 16 == 0);
     pp.Cout = a.Cout; pp.K = pl.K; pp.Mp = pl.Mp; pp.Rp = pl.Rp;
@@ -737,6 +737,7 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     pp.frag = fused ? 1 : 0;  // the fused kernel reads the weight in MFMA fragment order
     // one block per weight row; no weight (columns only) or a packed one: none
     const int nwb = (a.weight && !wp_in) ? pl.Mp : 0;
+    pp.w_first = nwb > 0 ? 1 : 0;
     hipLaunchKernelGGL(v2_prep_kernel, dim3(pp.n_tr_blocks + nwb), dim3(256), 0, stream,
                        static_cast<const uint16_t *>(a.x), static_cast<const uint16_t *>(a.weight),
                        xt, wp, pp);

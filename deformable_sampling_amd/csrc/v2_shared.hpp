@@ -22,6 +22,8 @@ struct PrepParams {
     int Cout, K, Mp, Rp;
     int frag;         // weight in MFMA fragment order (see below) instead of rows [Mp][Rp]
     int n_tr_blocks;  // blocks doing the transpose; the rest (Mp of them) permute the weight
+    int w_first;      // launch order: the weight rows' blocks first (their load -> LDS ->
+                      // permute chain is the longer one), then the transpose blocks
     int tiles_c, tiles_hw;
 };
 
@@ -31,7 +33,8 @@ __global__ __launch_bounds__(256) void v2_prep_kernel(const uint16_t *__restrict
                                                       uint16_t *__restrict__ xt,
                                                       uint16_t *__restrict__ wp, PrepParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // [channel][pixel], 144-byte rows
-    const int b = blockIdx.x;
+    int b = blockIdx.x;
+    if (p.w_first) b = b < p.Mp ? p.n_tr_blocks + b : b - p.Mp;
     if (b < p.n_tr_blocks && p.reg) {
         // 8 x 8 transposes in registers: lane (cl, hl) of a wave loads the 8 channel rows
         // cb*8..+7 over the 8 pixels hb*8..+7 (16 bytes each; the wave's 8 lanes of one
