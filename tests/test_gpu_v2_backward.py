@@ -82,6 +82,7 @@ SWEEP = [
     ("f16_c128_softmax", dict(N=1, Cin=128, H=7, W=9, Cout=24, mask="logits", dtype="f16")),
     ("bf16_c64_cout300", dict(N=1, Cin=64, H=6, W=7, Cout=300, dtype="bf16")),
     ("bf16_c64_1x1_image", dict(N=3, Cin=64, H=1, W=1, Cout=8, dtype="bf16")),
+    ("bf16_c128_dg2", dict(N=1, Cin=128, H=8, W=9, Cout=32, dg=2, dtype="bf16")),  # 64 channels per group
 ]
 
 
