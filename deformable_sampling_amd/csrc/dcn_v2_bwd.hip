@@ -21,7 +21,7 @@
 //   3. gcol = gcl x wT^T (fp32)   4. grad_weight partials = goT x colT^T   5. their sum
 //   6. count  7. scan
 //   8. sample pass: grad_offset, grad_mask and the bucket entries
-//   9. destination gather into gx_cl [N,H,W,Cin_pad] fp32  10. transpose to grad_x.
+//   9. destination gather, summed in fp32 and written to NCHW grad_x in the dtype.
 #include "dcn_common.hpp"
 #include "internal.hpp"
 
@@ -423,66 +423,59 @@ __global__ __launch_bounds__(kB) void v2b_sample_kernel(
 // ----------------------------------------------------- destination gather --
 
 struct V2bGatherParams {
-    int dg, cpg, Cin_pad, K, R, CT;
-    long long nitems;
+    int dg, cpg, Cin, Cin_pad, K, R, CT, HW, htiles;
     int nblocks;
 };
 
-// One wavefront per (image pixel, 256-channel tile), 4 channels per lane: sum the
-// bucket's entries coef * gcol[sample's pixel][tap, c..c+3] and store the fp32 sums
-// once (channels-last). With several deformable groups each lane walks the bucket of
-// its channels' group.
-__global__ __launch_bounds__(kB) void v2b_gather_kernel(const float *__restrict__ gcol,
-                                                        const int *__restrict__ starts,
-                                                        const int *__restrict__ cnt,
-                                                        const uint2 *__restrict__ entries,
-                                                        float *__restrict__ gx_cl, V2bGatherParams q) {
+// grad_x in the dtype, NCHW, straight from the buckets. A block takes 16 consecutive
+// pixels of one image and one 256-channel tile: wavefront w sums pixel w's bucket,
+// 4 channels per lane (entries coef * gcol[sample's pixel][tap, c..c+3]; with several
+// deformable groups each lane walks the bucket of its channels' group), the sums meet
+// transposed in LDS, and each channel's 16 pixels leave as one 32-byte run.
+constexpr int kGxPix = 16;
+__global__ __launch_bounds__(64 * kGxPix) void v2b_gather_kernel(const float *__restrict__ gcol,
+                                                                 const int *__restrict__ starts,
+                                                                 const int *__restrict__ cnt,
+                                                                 const uint2 *__restrict__ entries,
+                                                                 uint16_t *__restrict__ gx, int dtype_bf16,
+                                                                 V2bGatherParams q) {
+    __shared__ float tile[256][kGxPix + 1];
     const int blk = xcd_remap((int)blockIdx.x, q.nblocks);
-    const long long item = (long long)blk * 4 + (threadIdx.x >> 6);
-    if (item >= q.nitems) return;  // no barrier in this kernel
-    const int lane = threadIdx.x & 63;
-    const long long pix = item / q.CT;
-    const int ct = (int)(item - pix * q.CT);
+    const int ct = blk % q.CT, rest = blk / q.CT;
+    const int ht = rest % q.htiles, n = rest / q.htiles;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int hw = ht * kGxPix + w;
     const int c = ct * 256 + lane * 4;
-    if (c >= q.Cin_pad) return;
-    const int g = q.dg == 1 ? 0 : c / q.cpg;
-    const long long d = pix * q.dg + g;
-    const int b = starts[d], e = b + cnt[d];
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (hw < q.HW && c < q.Cin_pad) {
+        const int g = q.dg == 1 ? 0 : c / q.cpg;
+        const long long d = ((long long)n * q.HW + hw) * q.dg + g;
+        const int b = starts[d], e = b + cnt[d];
 #pragma unroll 4
-    for (int i = b; i < e; ++i) {
-        const uint2 en = entries[i];
-        const unsigned smp = en.x;
-        const float w = __uint_as_float(en.y);
-        const unsigned pp = smp / (unsigned)q.K, k = smp - pp * (unsigned)q.K;
-        const float4 v = *reinterpret_cast<const float4 *>(gcol + (size_t)pp * q.R + k * q.Cin_pad + c);
-        acc.x = fmaf(w, v.x, acc.x);
-        acc.y = fmaf(w, v.y, acc.y);
-        acc.z = fmaf(w, v.z, acc.z);
-        acc.w = fmaf(w, v.w, acc.w);
+        for (int i = b; i < e; ++i) {
+            const uint2 en = entries[i];
+            const unsigned smp = en.x;
+            const float wt = __uint_as_float(en.y);
+            const unsigned pp = smp / (unsigned)q.K, k = smp - pp * (unsigned)q.K;
+            const float4 v = *reinterpret_cast<const float4 *>(gcol + (size_t)pp * q.R + k * q.Cin_pad + c);
+            acc.x = fmaf(wt, v.x, acc.x);
+            acc.y = fmaf(wt, v.y, acc.y);
+            acc.z = fmaf(wt, v.z, acc.z);
+            acc.w = fmaf(wt, v.w, acc.w);
+        }
     }
-    *reinterpret_cast<float4 *>(gx_cl + (size_t)pix * q.Cin_pad + c) = acc;
-}
-
-// grad_x[n][c][hw] = gx_cl[n][hw][c] in the dtype, through a 64 x 64 LDS tile.
-template <class E>
-__global__ __launch_bounds__(kB) void v2b_out_kernel(const float *__restrict__ gx_cl,
-                                                     typename E::bits *__restrict__ gx, int Cin,
-                                                     int Cin_pad, int HW, int ctiles, int htiles) {
-    __shared__ float tile[64][65];
-    const int b = blockIdx.x;
-    const int ct = b % ctiles, ht = (b / ctiles) % htiles, n = b / (ctiles * htiles);
-    const int c0 = ct * 64, h0 = ht * 64;
-    for (int it = threadIdx.x; it < 4096; it += kB) {
-        const int px = it >> 6, c = it & 63;
-        float v = 0.0f;
-        if (h0 + px < HW && c0 + c < Cin_pad) v = gx_cl[((size_t)n * HW + h0 + px) * Cin_pad + c0 + c];
-        tile[c][px] = v;
-    }
+    tile[lane * 4 + 0][w] = acc.x;
+    tile[lane * 4 + 1][w] = acc.y;
+    tile[lane * 4 + 2][w] = acc.z;
+    tile[lane * 4 + 3][w] = acc.w;
     __syncthreads();
-    for (int it = threadIdx.x; it < 4096; it += kB) {
-        const int c = it >> 6, px = it & 63;
-        if (h0 + px < HW && c0 + c < Cin) gx[((size_t)n * Cin + c0 + c) * HW + h0 + px] = from_f32(E{}, tile[c][px]);
+    for (int it = threadIdx.x; it < 256 * kGxPix; it += 64 * kGxPix) {
+        const int cl = it / kGxPix, px = it % kGxPix;
+        const int cc = ct * 256 + cl, h = ht * kGxPix + px;
+        if (cc < q.Cin && h < q.HW) {
+            const float v = tile[cl][px];
+            gx[((size_t)n * q.Cin + cc) * q.HW + h] = dtype_bf16 ? from_f32(EBF16{}, v) : from_f32(EF16{}, v);
+        }
     }
 }
 
@@ -733,7 +726,6 @@ hipError_t launch_e(const V2BwdLaunch &a, hipStream_t stream) {
     int *fill = cnt + pl.D;
     int *starts = reinterpret_cast<int *>(ws + pl.off_starts);
     uint2 *entries = reinterpret_cast<uint2 *>(ws + pl.off_entries);
-    float *gx_cl = reinterpret_cast<float *>(ws + pl.off_gxcl);
     const int HW = a.H * a.W, HWo = pl.Ho * pl.Wo;
     const bool want_w = a.grad_weight != nullptr;
     const bool want_x = a.grad_x != nullptr;
@@ -916,20 +908,17 @@ hipError_t launch_e(const V2BwdLaunch &a, hipStream_t stream) {
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (!want_x) return hipSuccess;
-    // 9. destination gather, 10. NCHW grad_x
+    // 9. destination gather into NCHW grad_x
     {
         V2bGatherParams gq;
-        gq.dg = a.dg; gq.cpg = a.Cin / a.dg; gq.Cin_pad = pl.Cin_pad; gq.K = pl.K; gq.R = pl.R;
+        gq.dg = a.dg; gq.cpg = a.Cin / a.dg; gq.Cin = a.Cin; gq.Cin_pad = pl.Cin_pad; gq.K = pl.K;
+        gq.R = pl.R;
         gq.CT = (pl.Cin_pad + 255) / 256;
-        gq.nitems = (long long)a.N * HW * gq.CT;
-        gq.nblocks = (int)((gq.nitems + 3) / 4);
-        hipLaunchKernelGGL(v2b_gather_kernel, dim3(gq.nblocks), dim3(kB), 0, stream, gcol, starts, cnt,
-                           entries, gx_cl, gq);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-        const int ctiles = (a.Cin + 63) / 64, htiles = (HW + 63) / 64;
-        hipLaunchKernelGGL(v2b_out_kernel<E>, dim3(a.N * ctiles * htiles), dim3(kB), 0, stream, gx_cl,
-                           static_cast<typename E::bits *>(a.grad_x), a.Cin, pl.Cin_pad, HW, ctiles,
-                           htiles);
+        gq.HW = HW;
+        gq.htiles = (HW + kGxPix - 1) / kGxPix;
+        gq.nblocks = a.N * gq.htiles * gq.CT;
+        hipLaunchKernelGGL(v2b_gather_kernel, dim3(gq.nblocks), dim3(64 * kGxPix), 0, stream, gcol, starts, cnt,
+                           entries, static_cast<uint16_t *>(a.grad_x), E::id == DCN_BF16 ? 1 : 0, gq);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     return hipSuccess;
@@ -986,7 +975,6 @@ bool plan_dcn_v2_bwd(int N, int Cin, int H, int W, int Cout, int kh, int kw, int
     pl.off_cnt = take((size_t)pl.D * 2 * 4);  // counts, then fill cursors
     pl.off_starts = take((size_t)pl.D * 4);
     pl.off_entries = take((size_t)nent * 8);
-    pl.off_gxcl = take((size_t)N * H * W * pl.Cin_pad * 4);
     pl.total = off;
     pl.entries = nent;
     return true;

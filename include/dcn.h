@@ -292,7 +292,7 @@ dcn_status dcn_v2_forward_prepacked(const void *x, const float *offset, const fl
  * 256-byte aligned: x channels-last, the weight transposed, grad_out channels-last
  * and pixel-major, the forward's columns transposed (dtype); the column gradient
  * [N*Ho*Wo][K*Cin_pad] and split partial sums of the weight gradient (fp32); bucket
- * counters and entries of the grad_x gather; an fp32 channels-last grad_x.
+ * counters and entries of the grad_x gather.
  */
 size_t dcn_v2_backward_workspace_bytes(int N, int Cin, int H, int W, int Cout, int kh, int kw,
                                        int stride_h, int stride_w, int pad_h, int pad_w,
