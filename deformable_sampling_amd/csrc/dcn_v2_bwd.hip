@@ -114,7 +114,12 @@ __device__ __forceinline__ void v2b_rows_block(int bi, const uint16_t *__restric
     if constexpr (VEC) {
         if (t * 8 >= total) return;
         const long long e = t * 8;
-        const long long co = e / Pp, pp = e - co * Pp;
+        long long co = e / Pp, pp = e - co * Pp;
+        if (frag) {  // thread t fills 16-byte slot t: consecutive threads write consecutive bytes
+            const long long blk = t >> 6;  // (32-row block, 16-pixel group)
+            co = (blk / (Pp >> 4)) * 32 + (t & 31);
+            pp = (blk % (Pp >> 4)) * 16 + ((t >> 5) & 1) * 8;
+        }
         uint4 v = make_uint4(0, 0, 0, 0);
         if (co < Cout && pp < P) {
             const long long n = pp / HWo, hw = pp - n * HWo;
