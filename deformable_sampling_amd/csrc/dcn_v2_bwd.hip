@@ -238,11 +238,57 @@ __global__ __launch_bounds__(kB) void v2b_colT_kernel(const uint16_t *__restrict
     }
 }
 
-// grad_weight[co][ci][k] = sum over splits of part[s][co][k*Cin_pad + ci]: threads run
-// over (co, r) so the partial rows are read contiguously; the writes are strided by K.
-__global__ __launch_bounds__(kB) void v2b_wsum_kernel(const float *__restrict__ part,
-                                                      float *__restrict__ gw, int Cout, int Cin,
-                                                      int K, int Cin_pad, int R, int splits) {
+// grad_weight[co][ci][k] = sum over splits of part[s][co][k*Cin_pad + ci], the splits
+// added in order from zero. One block per output channel: thread t reads the 16-byte
+// vectors r = 4t..4t+3 of every split (up to eight splits' loads in flight before the
+// adds), the row meets in LDS in [k][ci] order (rows padded by one word) and leaves
+// as one contiguous [ci][k] run. Needs (Cin_pad + 1) * K floats of LDS (kWsumLds).
+constexpr int kWsumThreads = 1024;
+constexpr int kWsumLds = 16384;  // floats
+__global__ __launch_bounds__(kWsumThreads) void v2b_wsum_kernel(const float *__restrict__ part,
+                                                                float *__restrict__ gw, int Cout, int Cin,
+                                                                int K, int Cin_pad, int R, int splits) {
+    __shared__ float s_row[kWsumLds];
+    const int co = (int)blockIdx.x;
+    const size_t stride = (size_t)Cout * R;
+    const float *src = part + (size_t)co * R;
+    const int CP = Cin_pad + 1;
+    for (int q = threadIdx.x; q * 4 < R; q += kWsumThreads) {
+        float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int i0 = 0; i0 < splits; i0 += 8) {
+            float4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (i0 + u < splits) v[u] = *reinterpret_cast<const float4 *>(src + (i0 + u) * stride + 4 * q);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (i0 + u < splits) {
+                    s.x += v[u].x;
+                    s.y += v[u].y;
+                    s.z += v[u].z;
+                    s.w += v[u].w;
+                }
+        }
+        const int r = 4 * q, k = r / Cin_pad, ci = r - k * Cin_pad;  // Cin_pad % 8 == 0: one tap
+        float *d = s_row + k * CP + ci;
+        d[0] = s.x;
+        d[1] = s.y;
+        d[2] = s.z;
+        d[3] = s.w;
+    }
+    __syncthreads();
+    float *dst = gw + (size_t)co * Cin * K;
+    for (int o = threadIdx.x; o < Cin * K; o += kWsumThreads) {
+        const int ci = o / K, k = o - ci * K;
+        dst[o] = s_row[k * CP + ci];
+    }
+}
+
+// The same sum for rows too long for that LDS row: one thread per (co, r), writes
+// strided by K.
+__global__ __launch_bounds__(kB) void v2b_wsum_long_kernel(const float *__restrict__ part,
+                                                           float *__restrict__ gw, int Cout, int Cin,
+                                                           int K, int Cin_pad, int R, int splits) {
     const long long t = (long long)blockIdx.x * kB + threadIdx.x;
     if (t >= (long long)Cout * R) return;
     const int co = (int)(t / R), r = (int)(t - (long long)co * R);
@@ -254,30 +300,85 @@ __global__ __launch_bounds__(kB) void v2b_wsum_kernel(const float *__restrict__ 
     gw[((size_t)co * Cin + ci) * K + k] = s;
 }
 
+hipError_t launch_wsum(const float *wpart, float *gw, int Cout, int Cin, int K, int Cin_pad, int R,
+                       int splits, hipStream_t stream) {
+    if ((long long)(Cin_pad + 1) * K <= kWsumLds) {
+        hipLaunchKernelGGL(v2b_wsum_kernel, dim3((unsigned)Cout), dim3(kWsumThreads), 0, stream, wpart, gw,
+                           Cout, Cin, K, Cin_pad, R, splits);
+    } else {
+        const long long nw = (long long)Cout * R;
+        hipLaunchKernelGGL(v2b_wsum_long_kernel, dim3((unsigned)((nw + kB - 1) / kB)), dim3(kB), 0, stream,
+                           wpart, gw, Cout, Cin, K, Cin_pad, R, splits);
+    }
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- buckets --
 
-// One thread per sample (p, g, k): count the corners that receive a grad_x entry
-// (inside the image, weight non-zero) in their destination's bucket.
+// One thread per sample, samples in the offsets' own order (n, g, k, output pixel), so
+// a wavefront reads 64 consecutive offsets of one tap. A corner that receives a grad_x
+// entry (inside the image, weight non-zero) counts in its destination's bucket; the
+// block first counts in an LDS window of kCntWin consecutive counters around its first
+// sample's rows (one global atomic per touched counter afterwards), destinations outside
+// it go straight to global atomics.
+constexpr int kCntWin = 4096;
 __global__ __launch_bounds__(kB) void v2b_count_kernel(const float *__restrict__ offset,
                                                        int *__restrict__ cnt, V2bGeo q) {
-    const long long t = (long long)blockIdx.x * kB + threadIdx.x;
-    if (t >= q.P * q.dg * q.K) return;
-    const int k = (int)(t % q.K);
-    const long long pg = t / q.K;
-    const int g = (int)(pg % q.dg);
-    const long long p = pg / q.dg;
+    __shared__ int s_win[kCntWin];
     const int HWo = q.Ho * q.Wo;
-    const int n = (int)(p / HWo), r = (int)(p - (long long)n * HWo);
-    const V2bTap tp = v2b_tap(offset, q, n, r, g, k);
-    const size_t base = ((size_t)n * q.H + tp.y0) * q.W + tp.x0;
-    if (tp.w00 != 0.0f) atomicAdd(&cnt[base * q.dg + g], 1);
-    if (tp.w01 != 0.0f) atomicAdd(&cnt[(base + 1) * q.dg + g], 1);
-    if (tp.w10 != 0.0f) atomicAdd(&cnt[(base + q.W) * q.dg + g], 1);
-    if (tp.w11 != 0.0f) atomicAdd(&cnt[(base + q.W + 1) * q.dg + g], 1);
+    const long long total = q.P * q.dg * q.K;
+    const long long t0 = (long long)blockIdx.x * kB;
+    const long long rowc = (long long)q.W * q.dg;  // counters per image row
+    long long lo;
+    {
+        const int r = (int)(t0 % HWo);
+        const long long nk = t0 / HWo;
+        const int k = (int)(nk % q.K);
+        const int n = (int)(nk / q.K / q.dg);
+        const int ho = r / q.Wo, wo = r - ho * q.Wo;
+        const int y = ho * q.sh - q.ph + (k / q.kw) * q.dh;
+        const long long rows = kCntWin / rowc;
+        if (rows >= 2) {
+            const long long span = (kB + q.Wo - 1) / q.Wo * q.sh + 1;  // base rows the block covers
+            const long long margin = rows > span ? (rows - span) / 2 : 0;
+            lo = ((long long)n * q.H + y - margin) * rowc;
+        } else {
+            const int x = wo * q.sw - q.pw + (k % q.kw) * q.dw;
+            lo = (((long long)n * q.H + y) * q.W + x) * q.dg - kCntWin / 4;
+        }
+    }
+    for (int i = threadIdx.x; i < kCntWin; i += kB) s_win[i] = 0;
+    __syncthreads();
+    const long long t = t0 + threadIdx.x;
+    if (t < total) {
+        const int r = (int)(t % HWo);
+        const long long nk = t / HWo;
+        const int k = (int)(nk % q.K);
+        const long long ng = nk / q.K;
+        const int g = (int)(ng % q.dg), n = (int)(ng / q.dg);
+        const V2bTap tp = v2b_tap(offset, q, n, r, g, k);
+        const long long d00 = (((long long)n * q.H + tp.y0) * q.W + tp.x0) * q.dg + g;
+        auto add = [&](long long d) {
+            const long long w = d - lo;
+            if ((unsigned long long)w < (unsigned long long)kCntWin) atomicAdd(&s_win[w], 1);
+            else atomicAdd(&cnt[d], 1);
+        };
+        if (tp.w00 != 0.0f) add(d00);
+        if (tp.w01 != 0.0f) add(d00 + q.dg);
+        if (tp.w10 != 0.0f) add(d00 + rowc);
+        if (tp.w11 != 0.0f) add(d00 + rowc + q.dg);
+    }
+    __syncthreads();
+    // only counters of real destinations (0 <= lo + i < D) can be non-zero
+    for (int i = threadIdx.x; i < kCntWin; i += kB) {
+        const int c = s_win[i];
+        if (c) atomicAdd(&cnt[lo + i], c);
+    }
 }
 
 // Exclusive prefix sum of cnt[0..D) into starts, one block of 1024 threads walking
-// chunks of 4096 (4 consecutive values per thread) with a running carry.
+// chunks of 16384 (16 consecutive values per thread, loaded as four 16-byte vectors
+// where the chunk is whole; cnt and starts 16-byte aligned) with a running carry.
 __global__ __launch_bounds__(1024) void v2b_scan_kernel(const int *__restrict__ cnt,
                                                         int *__restrict__ starts, long long D) {
     __shared__ int s_wave[16];
@@ -285,12 +386,25 @@ __global__ __launch_bounds__(1024) void v2b_scan_kernel(const int *__restrict__ 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) s_carry = 0;
     __syncthreads();
-    for (long long c0 = 0; c0 < D; c0 += 4096) {
-        const long long b = c0 + 4LL * tid;
-        int v[4];
+    for (long long c0 = 0; c0 < D; c0 += 16384) {
+        const long long b = c0 + 16LL * tid;
+        int v[16];
+        if (b + 16 <= D) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = (b + i < D) ? cnt[b + i] : 0;
-        const int mine = v[0] + v[1] + v[2] + v[3];
+            for (int i = 0; i < 4; ++i) {
+                const int4 u = *reinterpret_cast<const int4 *>(cnt + b + 4 * i);
+                v[4 * i] = u.x;
+                v[4 * i + 1] = u.y;
+                v[4 * i + 2] = u.z;
+                v[4 * i + 3] = u.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = (b + i < D) ? cnt[b + i] : 0;
+        }
+        int mine = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mine += v[i];
         int incl = mine;  // inclusive scan over the wave
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -303,10 +417,21 @@ __global__ __launch_bounds__(1024) void v2b_scan_kernel(const int *__restrict__ 
         for (int w = 0; w < wave; ++w) wbase += s_wave[w];
         const int carry = s_carry;
         int run = carry + wbase + incl - mine;
+        int o[16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (b + i < D) starts[b + i] = run;
+        for (int i = 0; i < 16; ++i) {
+            o[i] = run;
             run += v[i];
+        }
+        if (b + 16 <= D) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<int4 *>(starts + b + 4 * i) =
+                    make_int4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (b + i < D) starts[b + i] = o[i];
         }
         __syncthreads();  // every thread has read s_wave and s_carry
         if (tid == 1023) s_carry = carry + wbase + incl;
@@ -826,10 +951,9 @@ hipError_t launch_e(const V2BwdLaunch &a, hipStream_t stream) {
         hipLaunchKernelGGL(v2b_wgrad_kernel<E>, dim3(wg.nblocks), dim3(kWgThreads), 0, stream, xt, a.offset,
                            a.mask, goT, wpart, wg);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        const long long nw = (long long)a.Cout * pl.R;
-        hipLaunchKernelGGL(v2b_wsum_kernel, dim3((unsigned)((nw + kB - 1) / kB)), dim3(kB), 0, stream,
-                           wpart, a.grad_weight, a.Cout, a.Cin, pl.K, pl.Cin_pad, pl.R, pl.splits);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if ((err = launch_wsum(wpart, a.grad_weight, a.Cout, a.Cin, pl.K, pl.Cin_pad, pl.R, pl.splits,
+                               stream)) != hipSuccess)
+            return err;
     } else if (want_w) {
         // 2. transposed columns
         V2bColParams cp;
@@ -855,10 +979,9 @@ hipError_t launch_e(const V2BwdLaunch &a, hipStream_t stream) {
         hipLaunchKernelGGL((v2_gemm_kernel<E, 1>), dim3(gp.nblocks), dim3(kGemmThreads), 0, stream,
                            goT, colT, wpart, gp);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        const long long nw = (long long)a.Cout * pl.R;
-        hipLaunchKernelGGL(v2b_wsum_kernel, dim3((unsigned)((nw + kB - 1) / kB)), dim3(kB), 0, stream,
-                           wpart, a.grad_weight, a.Cout, a.Cin, pl.K, pl.Cin_pad, pl.R, pl.splits);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if ((err = launch_wsum(wpart, a.grad_weight, a.Cout, a.Cin, pl.K, pl.Cin_pad, pl.R, pl.splits,
+                               stream)) != hipSuccess)
+            return err;
     }
     if (!want_s) return hipSuccess;
 
