@@ -98,12 +98,16 @@ __device__ __forceinline__ LaneAt lane_at(const TileAt &a, const TileParams &p) 
 }
 
 // Corner/fraction split of base + t as split_coord does, with the fraction taken by
-// v_fract_f32 (t - floor(t), held below 1) and the corner by a floor-convert. The
-// offsets reaching here are already scaled by offset_scale (see scale_offsets).
+// v_fract_f32 (t - floor(t), held below 1) and the corner by v_cvt_flr_i32_f32 (one
+// instruction for floor and convert, exact for the clamped |t| <= 2^24; the compiler
+// emits a floor and a convert). The offsets reaching here are already scaled by
+// offset_scale (see scale_offsets).
 __device__ __forceinline__ void split_coord_fast(int base, float t, int &c0, float &f) {
     t = __builtin_amdgcn_fmed3f(t, -16777216.0f, 16777216.0f);
     f = __builtin_amdgcn_fractf(t);
-    c0 = base + (int)floorf(t);
+    int fl;
+    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(fl) : "v"(t));
+    c0 = base + fl;
 }
 
 // fl32(offset_scale * d) for every offset, once per pair (skipped when the scale is 1,

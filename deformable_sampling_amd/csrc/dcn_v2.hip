@@ -649,22 +649,30 @@ __global__ __launch_bounds__(kWSThreads) void v2_wsr_kernel(const uint16_t *__re
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    // The column fragments of K slice ks + 1 are read before the MFMAs of slice ks (the
+    // scheduling barrier keeps the compiler from sinking the reads behind them), so an
+    // LDS read's latency overlaps four MFMAs instead of stalling the next one.
     auto mma = [&](const uint4 (&f)[2][4], int t) __attribute__((always_inline)) {
         const v4u *sb = reinterpret_cast<const v4u *>(sB[t & 3]);
-#pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
+        v4u fb[2][2];
+        auto rd = [&](v4u (&d)[2], int ks) __attribute__((always_inline)) {
             const int cc = 2 * ks + fhalf;
-            v4u fb[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int rb = u * 32 + frow;
-                fb[u] = sb[rb * 8 + (cc ^ ((rb >> 1) & 7))];
+                d[u] = sb[rb * 8 + (cc ^ ((rb >> 1) & 7))];
             }
+        };
+        rd(fb[0], 0);
+#pragma unroll
+        for (int ks = 0; ks < kBK / 16; ++ks) {
+            if (ks + 1 < kBK / 16) rd(fb[(ks + 1) & 1], ks + 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
-                    acc[a][b] = mfma32<E>(f[a][ks], __builtin_bit_cast(uint4, fb[b]), acc[a][b]);
+                    acc[a][b] = mfma32<E>(f[a][ks], __builtin_bit_cast(uint4, fb[ks & 1][b]), acc[a][b]);
         }
     };
     load_a(fa[0], 0);
