@@ -20,7 +20,11 @@
 // With 8 groups each XCD serves one group, and as its wavefronts advance through the
 // cameras roughly together, its L2 holds one camera's maps of one group at a time
 // (about 2 MB for 6 cameras x 4 scales of 64x176..8x22, 32 fp32 channels) instead of
-// that group's slice of every map.
+// that group's slice of every map. Where a camera's taps fit one 64-tap chunk, the
+// camera-phased kernel (deform_agg_cam_kernel) goes further: a persistent grid in
+// which each wavefront holds up to four units and visits camera c of all of them
+// before camera c + 1, so that every unit of an XCD's range passes through a camera
+// while its maps are in L2, not only the units resident at one time.
 #include "dcn_common.hpp"
 #include "internal.hpp"
 
@@ -441,6 +445,251 @@ void deform_agg_pipe_kernel(const typename E::bits *__restrict__ feat,
     if (z == 0) store_f32<E, V>(out + (size_t)ba * GC + g * p.Cg + s * V, acc);
 }
 
+// ------------------------------------------------------ camera-phased --
+//
+// The pipelined kernel with the units of an XCD processed camera by camera. In the
+// kernel above a wavefront takes one unit from start to end, so the 256 wavefronts an
+// XCD holds at a time pass through the cameras together, but the ~3.5 rounds of
+// units that follow each fetch every camera's maps of their group into L2 again:
+// about 3.5 x 6 x 1.9 MB of fills per group, where one camera's maps of one group
+// (1.9 MB for 64x176..8x22 and 32 fp32 channels) fit the 4 MB L2. Here the grid is
+// persistent (two blocks per CU, all resident): the units of a round are split into
+// eight XCD ranges, wavefront j of an XCD owns units j, j + W, j + 2W, ... (up to MU,
+// W = wavefronts per XCD), and a wavefront visits camera 0 of each of its units,
+// then camera 1, and so on. A camera's maps are then fetched about once per round
+// for all units of the XCD. A chunk is one unit's taps of one camera (scales x
+// points <= 64); the softmax keeps a running maximum, a sum and a rescale factor per
+// unit, as above. Records, gathers and the one-batch-ahead pipeline are those of the
+// kernel above.
+template <class E, int S, int U, int MU>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DCN_AGG_WAVES_PER_EU)))
+void deform_agg_cam_kernel(const typename E::bits *__restrict__ feat,
+                           const float *__restrict__ loc, const float *__restrict__ weights,
+                           typename E::bits *__restrict__ out, const AggParams p) {
+    constexpr int elt = (int)sizeof(typename E::bits);
+    constexpr int V = 16 / elt;
+    constexpr int Z = 64 / S;    // slices per wavefront
+    constexpr int NB = S / U;    // batches per slice per 64-record chunk
+    static_assert(S * Z == 64 && NB * U == S && NB % 2 == 0, "pipeline shape");
+    using R = uint4;
+
+    __shared__ int s_h[kAggMaxMaps], s_w[kAggMaxMaps], s_start[kAggMaxMaps];
+    __shared__ TapRec s_rec[kWaves][2][64];
+
+    const int nmaps = p.cams * p.scales;
+    for (int i = threadIdx.x; i < nmaps; i += kThreads) {
+        s_h[i] = p.maps.H[i];
+        s_w[i] = p.maps.W[i];
+        s_start[i] = p.maps.start[i];
+    }
+    __syncthreads();
+
+    // block b runs on XCD b % 8 (the dispatcher's round robin); p.nblocks is a
+    // multiple of 8
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int xcd = (int)blockIdx.x % 8;
+    const int wpx = (p.nblocks / 8) * kWaves;  // wavefronts per XCD
+    const int j = ((int)blockIdx.x / 8) * kWaves + wv;
+    const int lane = threadIdx.x & 63;
+    const int z = lane / S, s = lane % S;
+    const int sp = p.scales * p.pts;  // taps of one camera (<= 64)
+    const int GC = p.G * p.Cg;
+    const int lane_off = s * 16;
+    const int per_round = 8 * wpx * MU;
+    const int nch = p.cams * MU;
+
+    for (int r0 = 0; r0 < p.nunits; r0 += per_round) {
+        const int nr = min(per_round, p.nunits - r0);
+        const int q = (nr + 7) / 8;
+        const int u_beg = r0 + xcd * q, u_end = min(r0 + (xcd + 1) * q, r0 + nr);
+        if (u_beg + j >= u_end) continue;  // no unit for this wavefront in this round
+
+        bool ok[MU];
+        int ba_k[MU], g_k[MU];
+        const float *wrow[MU];
+        const float *lrow[MU];
+        __amdgpu_buffer_rsrc_t rs[MU];
+#pragma unroll
+        for (int k = 0; k < MU; ++k) {
+            const int unit = u_beg + j + k * wpx;
+            ok[k] = unit < u_end;
+            const int uu = ok[k] ? unit : u_beg + j;
+            const int g = uu / p.BA, ba = uu - g * p.BA;  // group-major
+            const int b = ba / p.A;
+            ba_k[k] = ba;
+            g_k[k] = g;
+            wrow[k] = weights + (size_t)ba * (sp * p.cams) * p.G + g;
+            lrow[k] = loc + (size_t)ba * p.pts * p.cams * 2;
+            const typename E::bits *fb = feat + (size_t)b * p.P_total * GC + g * p.Cg;
+            rs[k] = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)fb, (short)0, (int)((unsigned)((size_t)p.P_total * GC - g * p.Cg) * elt), 0x00020000);
+        }
+
+        float m_run[MU], esum[MU], fk[MU];
+        float acc[MU][V];
+#pragma unroll
+        for (int k = 0; k < MU; ++k) {
+            m_run[k] = -INFINITY;
+            esum[k] = 0.0f;
+            fk[k] = 1.0f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[k][i] = 0.0f;
+        }
+
+        // lane l < sp describes tap (cam, scale l / pts, point l % pts) of its unit
+        float w_nx = 0.0f;
+        float2 uv_nx = make_float2(0.0f, 0.0f);
+        auto fetch = [&](int cam, int k) __attribute__((always_inline)) {
+            if (ok[k] && lane < sp) {
+                const int sc = lane / p.pts, pt = lane - sc * p.pts;
+                w_nx = wrow[k][(size_t)((pt * p.cams + cam) * p.scales + sc) * p.G];
+                uv_nx = *reinterpret_cast<const float2 *>(lrow[k] + 2 * (pt * p.cams + cam));
+            }
+        };
+        // records of chunk (cam, k) into buf; then the inputs of chunk (cam2, k2)
+        auto build = [&](int cam, int k, TapRec *buf, int cam2, int k2) __attribute__((always_inline)) {
+            const bool valid = ok[k] && lane < sp;
+            float w = w_nx;
+            const float2 uv = uv_nx;
+            if (cam2 < p.cams) fetch(cam2, k2);  // in flight until the next build
+            if (p.softmax) {
+                const float l = valid ? w : -INFINITY;
+                const float m_new = fmaxf(m_run[k], wave_max(l));
+                fk[k] = m_new == -INFINITY ? 1.0f : expf(m_run[k] - m_new);
+                esum[k] *= fk[k];
+                m_run[k] = m_new;
+                w = l == -INFINITY ? 0.0f : expf(l - m_new);
+                esum[k] += w;
+            }
+            TapRec r;
+            if (valid) {
+                const int cs = cam * p.scales + lane / p.pts;
+                const int Hs = s_h[cs], Ws = s_w[cs];
+                // one fp32 rounding of u*W, then the half-pixel shift
+                const float xf = __fsub_rn(mul_rn(uv.x, (float)Ws), 0.5f);
+                const float yf = __fsub_rn(mul_rn(uv.y, (float)Hs), 0.5f);
+                int x0, y0;
+                float fx, fy;
+                split_coord(0, xf, x0, fx);
+                split_coord(0, yf, y0, fy);
+                const Tap tp = make_tap(y0, x0, fy, fx, w, Hs, Ws, GC);
+                const int base = s_start[cs] * GC;
+                r.o00 = (base + tp.o00) * elt; r.o01 = (base + tp.o01) * elt;
+                r.o10 = (base + tp.o10) * elt; r.o11 = (base + tp.o11) * elt;
+                r.w00 = tp.w00; r.w01 = tp.w01; r.w10 = tp.w10; r.w11 = tp.w11;
+            } else {  // padding record: weight 0, no loads (see issue)
+                r.o00 = r.o01 = r.o10 = r.o11 = 0;
+                r.w00 = r.w01 = r.w10 = r.w11 = 0.0f;
+            }
+            buf[lane] = r;  // this wavefront's own records: LDS keeps a wave's accesses in order
+        };
+
+        struct Batch {
+            R d[U][4];
+            float w[U][4];
+        };
+        // batch bb of the chunk in buffer cb for unit k: records (bb*U + u)*Z + z; the
+        // corners of padding records (index >= the chunk's tap count) are not loaded
+        auto issue = [&](int k, int cb, int bb, Batch &B) __attribute__((always_inline)) {
+            const TapRec *rc = s_rec[wv][cb];
+            const int nval = ok[k] ? sp : 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int ri = (bb * U + u) * Z + z;
+                const TapRec q = rc[ri];
+                B.w[u][0] = q.w00; B.w[u][1] = q.w01; B.w[u][2] = q.w10; B.w[u][3] = q.w11;
+                if (ri < nval) {
+                    B.d[u][0] = buffer_load<R>(rs[k], q.o00 + lane_off);
+                    B.d[u][1] = buffer_load<R>(rs[k], q.o01 + lane_off);
+                    B.d[u][2] = buffer_load<R>(rs[k], q.o10 + lane_off);
+                    B.d[u][3] = buffer_load<R>(rs[k], q.o11 + lane_off);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) B.d[u][c] = make_uint4(0, 0, 0, 0);
+                }
+            }
+        };
+        auto consume = [&](const Batch &B, float (&ac)[V]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    float f[V];
+                    load_f32<E, V>(reinterpret_cast<const typename E::bits *>(&B.d[u][c]), f);
+#pragma unroll
+                    for (int i = 0; i < V; ++i) ac[i] = fmaf(B.w[u][c], f[i], ac[i]);
+                }
+            // the batch's multiply-adds complete here (see the kernel above)
+#pragma unroll
+            for (int i = 0; i < V; ++i) asm volatile("" : "+v"(ac[i]));
+        };
+
+        // chunk n = cam * MU + k sits in record buffer n & 1 = k & 1 (MU even)
+        static_assert(MU % 2 == 0, "record buffer of a chunk from its unit index");
+        fetch(0, 0);
+        build(0, 0, s_rec[wv][0], 0, 1);
+        Batch A, B2;
+        issue(0, 0, 0, A);
+        for (int cam = 0; cam < p.cams; ++cam) {
+#pragma unroll
+            for (int k = 0; k < MU; ++k) {
+                const int n = cam * MU + k;
+                const bool more = n + 1 < nch;
+                const int k1 = (k + 1) % MU, cam1 = cam + (k + 1) / MU;
+                const int k2 = (k + 2) % MU, cam2 = cam + (k + 2) / MU;
+                if (p.softmax)  // chunk n's records are relative to its unit's maximum as of chunk n
+#pragma unroll
+                    for (int i = 0; i < V; ++i) acc[k][i] *= fk[k];
+                if (more) build(cam1, k1, s_rec[wv][k1 & 1], cam2, k2);
+#pragma unroll
+                for (int bb = 0; bb < NB; bb += 2) {  // A holds batch bb, B2 takes bb + 1
+                    issue(k, k & 1, bb + 1, B2);
+                    consume(A, acc[k]);
+                    if (bb + 2 < NB) issue(k, k & 1, bb + 2, A);
+                    else if (more) issue(k1, k1 & 1, 0, A);
+                    consume(B2, acc[k]);
+                }
+            }
+        }
+
+#pragma unroll
+        for (int k = 0; k < MU; ++k) {
+            // combine the Z slices (lanes s, s+S, s+2S, ...)
+#pragma unroll
+            for (int o = S; o < 64; o <<= 1)
+#pragma unroll
+                for (int i = 0; i < V; ++i) acc[k][i] += __shfl_xor(acc[k][i], o, 64);
+            if (p.softmax) {
+                const float inv = 1.0f / wave_sum(esum[k]);
+#pragma unroll
+                for (int i = 0; i < V; ++i) acc[k][i] *= inv;
+            }
+            if (ok[k] && z == 0) store_f32<E, V>(out + (size_t)ba_k[k] * GC + g_k[k] * p.Cg + s * V, acc[k]);
+        }
+    }
+}
+
+// Blocks of the persistent grid: two per CU of the current device (rounded up to a
+// multiple of the 8 XCDs), looked up once per device.
+#ifndef DCN_AGG_CAM_BPC
+#define DCN_AGG_CAM_BPC 2
+#endif
+#ifndef DCN_AGG_CAM_MU
+#define DCN_AGG_CAM_MU 4
+#endif
+int persistent_blocks() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cache[dev] == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 1)
+            cu = 256;
+        cache[dev] = (DCN_AGG_CAM_BPC * cu + 7) / 8 * 8;
+    }
+    return cache[dev];
+}
+
 template <class E, int V>
 hipError_t launch_v(const AggLaunch &a, AggParams &p, hipStream_t stream) {
     using Bt = typename E::bits;
@@ -484,6 +733,22 @@ hipError_t launch_e(const AggLaunch &a, hipStream_t stream) {
             return hipGetLastError();
         };
         constexpr int U = DCN_AGG_PIPE_U;
+        if (p.scales * p.pts <= 64 && (p.nchunk == 8 || p.nchunk == 16 || (p.nchunk == 4 && U <= 2))) {
+            // camera-phased persistent grid: two blocks per CU, a multiple of 8
+            p.nblocks = persistent_blocks();
+            constexpr int MU = DCN_AGG_CAM_MU;
+            // dynamic LDS that leaves room for DCN_AGG_CAM_BPC blocks per CU and no more
+            constexpr size_t res = 163840 / DCN_AGG_CAM_BPC - (sizeof(TapRec) * kWaves * 2 * 64 + 3 * 4 * kAggMaxMaps) - 1024;
+            auto cam = [&](auto kern) {
+                hipLaunchKernelGGL(kern, dim3(p.nblocks), dim3(kThreads), res, stream,
+                                   static_cast<const Bt *>(a.feat), a.loc, a.weights,
+                                   static_cast<Bt *>(a.out), p);
+                return hipGetLastError();
+            };
+            if (p.nchunk == 8) return cam(deform_agg_cam_kernel<E, 8, U, MU>);
+            if (p.nchunk == 16) return cam(deform_agg_cam_kernel<E, 16, U, MU>);
+            return cam(deform_agg_cam_kernel<E, 4, (U < 2 ? U : 2), MU>);
+        }
         if (p.nchunk == 8) return pipe(deform_agg_pipe_kernel<E, 8, U>);
         if (p.nchunk == 16) return pipe(deform_agg_pipe_kernel<E, 16, U>);
         if (p.nchunk == 4 && U <= 2) return pipe(deform_agg_pipe_kernel<E, 4, (U < 2 ? U : 2)>);

@@ -299,7 +299,8 @@ AGG_SWEEP = [
                              loc_lo=-0.3, loc_hi=1.3)),
     ("f16_small", dict(B=1, shapes=[[(9, 13), (5, 7)]] * 2, A=33, pts=3, G=2, Cg=16, dtype="f16")),
     ("bf16_small", dict(B=1, shapes=[[(9, 13), (5, 7)]] * 2, A=33, pts=3, G=2, Cg=16, dtype="bf16")),
-    # group channels of 64/128/256 bytes: the pipelined path with 4/8/16 lanes per slice;
+    # group channels of 64/128/256 bytes: the pipelined paths with 4/8/16 lanes per slice
+    # (camera-phased where a camera's taps, scales x points, fit one 64-tap chunk);
     # T = pts*cams*scales below one 64-tap chunk, just over one, and several with a tail
     ("f32_cg16_s4_t12", dict(B=2, shapes=[[(9, 13), (5, 7)], [(6, 10), (3, 5)]], A=37, pts=3,
                              G=2, Cg=16)),
@@ -314,6 +315,14 @@ AGG_SWEEP = [
                               dtype="bf16")),
     ("bf16_cg128_s16_t24", dict(B=1, shapes=[[(7, 9), (4, 5), (2, 3)]] * 2, A=7, pts=4, G=1,
                                 Cg=128, dtype="bf16")),
+    # the camera-phased grid over more units than one round (9003 units: a full round of
+    # four units per wavefront, then 811 split unevenly over the eight XCD ranges)
+    ("f32_cg32_s8_rounds", dict(B=1, shapes=[[(6, 8), (3, 4)]] * 2, A=3001, pts=2, G=3, Cg=32)),
+    # 80 taps per camera (scales x points > 64): the unit-at-a-time pipelined kernel
+    ("f32_cg32_s8_sp80", dict(B=1, shapes=[[(6, 9), (3, 5), (2, 3), (1, 2)]] * 2, A=9, pts=20,
+                              G=2, Cg=32)),
+    ("bf16_cg64_s8_sp72", dict(B=2, shapes=[[(9, 13), (5, 7), (3, 4)]] * 3, A=5, pts=24, G=2,
+                               Cg=64, dtype="bf16")),
 ]
 
 
