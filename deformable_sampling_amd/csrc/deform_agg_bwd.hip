@@ -45,8 +45,8 @@
 // the bucket, four entries at a time in four 16-lane groups, and stores the row once
 // in its dtype. No float atomics; the summation order within a bucket follows the
 // fill order, so grad_feat's last bits may vary between runs, while grad_loc and
-// grad_weights are deterministic. Past the bucket limits (or with
-// DCN_AGG_BWD_ATOMIC=1) the feature gradient is accumulated with fp32 atomic adds
+// grad_weights are deterministic. Past the bucket limits (or with the DCN_BWD_ATOMIC
+// path of deform_agg_backward_path) the feature gradient is accumulated with fp32 atomic adds
 // after each batch of records (half a wavefront per corner, 32 contiguous channels
 // per half, G from LDS) into grad_feat (fp32) or a workspace accumulator rounded
 // once at the end.
