@@ -331,6 +331,41 @@ def bench_v2(dsa, torch, timer, iters, warmup, flush=None, prepacked=False):
     return r
 
 
+def bench_v2_im2col(dsa, torch, timer, iters, warmup, flush=None):
+    """dcn_v2_im2col on the 8x256x40x40 bf16 layer: the deform-im2col stage alone (x to
+    channels-last, then the K-contiguous bf16 columns [P][K*Cin] into the workspace),
+    against the HBM roofline of x, offsets and masks read once and the columns written
+    once."""
+    import workloads as wl
+    name = "dcnv2_bf16_n8_c256_40x40"
+    c = wl.make(name)
+    dev = lambda t: None if t is None else t.to("cuda").contiguous()
+    x, off, m = dev(c["x"]), dev(c["offset"]), dev(c["mask"])
+    N, Cin, H, W, Cout = c["N"], c["Cin"], c["H"], c["W"], c["Cout"]
+    need = dsa.dcn_v2_workspace_bytes(N, Cin, H, W, Cout, dtype=torch.bfloat16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    lib = dsa.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    args = (x.data_ptr(), off.data_ptr(), m.data_ptr(), ws.data_ptr(), need, N, Cin, H, W, Cout,
+            3, 3, 1, 1, 1, 1, 1, 1, 1, 0, 2, stream)
+
+    def call():
+        st = lib.dcn_v2_im2col(*args)
+        if st:
+            raise RuntimeError("dcn_v2_im2col status %d" % st)
+    wall, kern = timer.run(call, iters, warmup)
+    P = N * c["Ho"] * c["Wo"]
+    cols = P * 9 * Cin * 2
+    nbytes = x.numel() * 2 + off.numel() * 4 + m.numel() * 4 + cols
+    r = dict(workload=name + " deform-im2col", taps=P * 9, channel_taps=P * 9 * Cin, algo_bytes=nbytes,
+             wall_s=wall, kernel_s=kern, taps_per_s=P * 9 / kern, gbs=nbytes / kern / 1e9,
+             frac=nbytes / kern / 1e9 / HBM_PEAK_GBS,
+             note="two launches: x to channels-last, then the column kernel")
+    if flush is not None:
+        r.update(cold_fields(timer, call, flush, nbytes))
+    return r
+
+
 def bench_v2_bwd(dsa, torch, timer, iters, warmup):
     """dcn_v2_backward (grad x, offsets, masks, weight) on the 8x256x40x40 bf16 layer:
     the whole call (layouts, transposed columns, two MFMA GEMMs, bucket count/scan,
@@ -558,7 +593,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["core", "all", "bwd", "aggbwd", "v2bwd", "c1", "c2", "v2", "v2p",
-                                       "agg", "packed", "roi", "mfma"], default="all")
+                                       "agg", "packed", "roi", "mfma", "v2col"], default="all")
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -582,6 +617,10 @@ def main():
         nm = {"c1": "dcnv4_f32_n1_32x32_g4c16", "c2": "dcnv3_f32_n8_56x56_g4c16_softmax"}[args.only]
         r, _ = bench_core(dsa, torch, timer, nm, args.steps, args.warmup)
         log("%s: %.2f us/launch" % (nm, r["kernel_s"] * 1e6))
+        return
+    if args.only == "v2col":
+        r = bench_v2_im2col(dsa, torch, timer, args.steps, args.warmup)
+        log("dcnv2 deform-im2col: %.2f us/call, %.0f GB/s" % (r["kernel_s"] * 1e6, r["gbs"]))
         return
     if args.only in ("v2", "v2p"):
         r = bench_v2(dsa, torch, timer, args.steps, args.warmup, prepacked=args.only == "v2p")
@@ -644,6 +683,7 @@ def main():
             r = bench_v2(dsa, torch, timer, 100, 10, flush=flush, prepacked=pre)
             r["mfma_frac_of_probe"] = r["tflops"] / ceilings["mfma_bf16_tflops"]
             extra.append(r)
+        extra.append(bench_v2_im2col(dsa, torch, timer, 100, 10, flush=flush))
         log("dcnv2 done")
         extra.append(bench_v2_bwd(dsa, torch, timer, 50, 5))
         log("dcnv2 backward done")

@@ -32,7 +32,15 @@ struct ColParams {
     int S, Q, nchunk;  // lanes per (pixel, tap) item, items per wave, chunks per item
     int TP;            // pixels per block
     int nblocks;
+    unsigned magic_k, magic_kw;  // ceil(2^20 / K), ceil(2^20 / kw): exact quotients below 2^12
 };
+
+// floor(a / d) for 0 <= a < 2^12 and 1 <= d < 2^6 from m = ceil(2^20 / d): a * m / 2^20
+// exceeds a / d by less than a / 2^20 < 2^-8 < 1 / d, so the floor is exact, and
+// a * m < 2^12 * 2^20 fits 32 bits.
+__device__ __forceinline__ int div_small(int a, unsigned m) { return (int)(((unsigned)a * m) >> 20); }
+
+constexpr int kColMaxTP = 64;  // pixels per im2col block, at most
 
 template <class E>
 __global__ __launch_bounds__(256) void v2_im2col_kernel(const uint16_t *__restrict__ xt,
@@ -43,9 +51,26 @@ __global__ __launch_bounds__(256) void v2_im2col_kernel(const uint16_t *__restri
     const int K = p.K;
     float *s_off = smem;                          // [TP][dg][K][2]
     float *s_m = smem + p.TP * p.dg * K * 2;      // [TP][dg][K]
+    __shared__ int s_pix[3][kColMaxTP];  // image, output row, output column of the block's pixels
     const int blk = xcd_remap((int)blockIdx.x, p.nblocks);
     const long long p0 = (long long)blk * p.TP;
     const long long HWo = (long long)p.Ho * p.Wo;
+
+    // 0. the block's pixels split into (image, row, column) once (64-bit divisions)
+    if ((int)threadIdx.x < p.TP) {
+        const long long pg = p0 + threadIdx.x;
+        int n = 0, ho = 0, wo = 0;
+        if (pg < p.P) {
+            const long long r = pg % HWo;
+            n = (int)(pg / HWo);
+            ho = (int)(r / p.Wo);
+            wo = (int)(r - (long long)ho * p.Wo);
+        }
+        s_pix[0][threadIdx.x] = n;
+        s_pix[1][threadIdx.x] = ho;
+        s_pix[2][threadIdx.x] = wo;
+    }
+    __syncthreads();
 
     // 1. stage offsets / masks of this block's pixels (pixel-fastest: coalesced NCHW rows)
     const int per_pix = p.dg * K;
@@ -54,8 +79,8 @@ __global__ __launch_bounds__(256) void v2_im2col_kernel(const uint16_t *__restri
         const long long pg = p0 + pl;
         float v = 0.0f;
         if (pg < p.P) {
-            const long long n = pg / HWo, r = pg % HWo;
-            v = offset[((size_t)n * per_pix * 2 + c) * HWo + r];
+            const size_t r = (size_t)s_pix[1][pl] * p.Wo + s_pix[2][pl];
+            v = offset[((size_t)s_pix[0][pl] * per_pix * 2 + c) * HWo + r];
         }
         s_off[pl * per_pix * 2 + c] = v;
     }
@@ -64,8 +89,8 @@ __global__ __launch_bounds__(256) void v2_im2col_kernel(const uint16_t *__restri
         const long long pg = p0 + pl;
         float v = 1.0f;
         if (p.has_mask && pg < p.P) {
-            const long long n = pg / HWo, r = pg % HWo;
-            v = mask[((size_t)n * per_pix + c) * HWo + r];
+            const size_t r = (size_t)s_pix[1][pl] * p.Wo + s_pix[2][pl];
+            v = mask[((size_t)s_pix[0][pl] * per_pix + c) * HWo + r];
         }
         s_m[pl * per_pix + c] = v;
     }
@@ -88,7 +113,63 @@ __global__ __launch_bounds__(256) void v2_im2col_kernel(const uint16_t *__restri
     const int q = lane / p.S, s = lane - q * p.S;
     const int nitems = p.TP * K;
     const int per_pass = 4 * p.Q;
-    if (q < p.Q) {
+    if (q < p.Q && p.nchunk <= p.S && nitems < 4096 && K < 64) {
+        // one 16-byte chunk per lane and item: items are taken kB passes at a time, the
+        // corners of all kB loaded before any is summed, so that a wave has kB items'
+        // gathers in flight instead of one
+        constexpr int kB = 3;
+        const int ch = s, ci0 = ch * kVec;
+        const bool lane_on = ch < p.nchunk;
+        const int g = min(ci0 / p.cpg, p.dg - 1);
+        for (int it0 = wave * p.Q + q; it0 < nitems; it0 += per_pass * kB) {
+            uint4 cr[kB][4];
+            Tap tb[kB];
+            uint16_t *crow[kB];
+            bool live[kB];
+#pragma unroll
+            for (int b = 0; b < kB; ++b) {
+                const int it = it0 + b * per_pass;
+                live[b] = it < nitems;
+                const int pl = live[b] ? div_small(it, p.magic_k) : 0, k = live[b] ? it - pl * K : 0;
+                const long long pg = p0 + pl;
+                crow[b] = col + (size_t)pg * p.Rp + (size_t)k * p.Cin_pad + ci0;
+                const bool real = live[b] && pg < p.P && lane_on;
+                const int n = s_pix[0][pl], ho = s_pix[1][pl], wo = s_pix[2][pl];
+                const int i = div_small(k, p.magic_kw), j = k - i * p.kw;
+                const float *so = s_off + ((pl * p.dg + g) * K + k) * 2;
+                int y0, x0;
+                float fy, fx;
+                split_coord(ho * p.sh - p.ph + i * p.dh, so[1], y0, fy);
+                split_coord(wo * p.sw - p.pw + j * p.dw, so[0], x0, fx);
+                tb[b] = make_tap(y0, x0, fy, fx, real ? s_m[(pl * p.dg + g) * K + k] : 0.0f, p.H, p.W,
+                                 p.Cin_pad);
+                const uint16_t *img = xt + (size_t)n * p.H * p.W * p.Cin_pad + ci0;
+                cr[b][0] = *reinterpret_cast<const uint4 *>(img + tb[b].o00);
+                cr[b][1] = *reinterpret_cast<const uint4 *>(img + tb[b].o01);
+                cr[b][2] = *reinterpret_cast<const uint4 *>(img + tb[b].o10);
+                cr[b][3] = *reinterpret_cast<const uint4 *>(img + tb[b].o11);
+            }
+#pragma unroll
+            for (int b = 0; b < kB; ++b) {
+                if (!live[b] || !lane_on) continue;
+                float va[kVec], vb[kVec], vc[kVec], ve[kVec];
+                unpack<E, kVec>(cr[b][0], va);
+                unpack<E, kVec>(cr[b][1], vb);
+                unpack<E, kVec>(cr[b][2], vc);
+                unpack<E, kVec>(cr[b][3], ve);
+                float acc[kVec];
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) {
+                    acc[e] = 0.0f;
+                    acc[e] = fmaf(tb[b].w00, va[e], acc[e]);
+                    acc[e] = fmaf(tb[b].w01, vb[e], acc[e]);
+                    acc[e] = fmaf(tb[b].w10, vc[e], acc[e]);
+                    acc[e] = fmaf(tb[b].w11, ve[e], acc[e]);
+                }
+                store_f32<E, kVec>(crow[b], acc);  // rows past P get zeros (weight 0)
+            }
+        }
+    } else if (q < p.Q) {
         for (int it = wave * p.Q + q; it < nitems; it += per_pass) {
             const int pl = it / K, k = it - pl * K;
             const long long pg = p0 + pl;
@@ -98,9 +179,7 @@ __global__ __launch_bounds__(256) void v2_im2col_kernel(const uint16_t *__restri
                     *reinterpret_cast<uint4 *>(crow + ch * kVec) = make_uint4(0, 0, 0, 0);
                 continue;
             }
-            const int n = (int)(pg / HWo);
-            const int r = (int)(pg % HWo);
-            const int ho = r / p.Wo, wo = r % p.Wo;
+            const int n = s_pix[0][pl], ho = s_pix[1][pl], wo = s_pix[2][pl];
             const int i = k / p.kw, j = k - i * p.kw;
             const uint16_t *img = xt + (size_t)n * p.H * p.W * p.Cin_pad;
             for (int ch = s; ch < p.nchunk; ch += p.S) {
@@ -792,7 +871,10 @@ hipError_t launch_e(const V2Launch &a, hipStream_t stream) {
     cp.S = cp.nchunk < 64 ? cp.nchunk : 64;
     cp.Q = 64 / cp.S;
     cp.TP = 8;  // 4 waves x 2 items x 9 passes: many small blocks hide gather latency
+    static_assert(8 <= kColMaxTP, "im2col block pixels");
     cp.nblocks = (int)((pl.Pp + cp.TP - 1) / cp.TP);
+    cp.magic_k = (unsigned)(((1u << 20) + pl.K - 1) / pl.K);
+    cp.magic_kw = (unsigned)(((1u << 20) + a.kw - 1) / a.kw);
     const size_t lds = (size_t)cp.TP * a.dg * pl.K * 3 * sizeof(float);
     hipLaunchKernelGGL(v2_im2col_kernel<E>, dim3(cp.nblocks), dim3(256), lds, stream, xt,
                        a.offset, a.mask, col, cp);
