@@ -9,11 +9,12 @@ the timed region.
 Printed (one JSON line): bilinear taps/s (whole job), ms per step, the roofline
 object of the core kernel (algorithmic bytes per launch / HIP-event launch time vs
 8 TB/s), the CPU oracle's rate on a bounded sample, and side measurements of the
-other ops (DCNv4/DCNv3 small maps, the core backward, DCNv2 im2col + MFMA GEMM,
-aggregation forward and backward, deformable RoI pooling).
+other ops (DCNv4/DCNv3 small maps, the core backward, DCNv2 im2col + MFMA GEMM and
+the deform-im2col stage alone, aggregation forward and backward, deformable RoI
+pooling).
 
   python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--only core|c1|c2|packed|bwd|v2|v2bwd|agg|aggbwd|roi|mfma]
+                  [--only core|c1|c2|packed|bwd|v2|v2p|v2col|v2bwd|agg|aggbwd|roi|mfma]
   python bench.py --calib-copy     # plain copy of known size, for counter scaling
 """
 from __future__ import annotations
