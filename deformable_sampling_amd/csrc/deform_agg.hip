@@ -57,6 +57,22 @@ __device__ __forceinline__ float wave_max(float v) {
     for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
     return v;
 }
+// The same maximum without LDS permutes (every lane active): row_shr DPP steps leave
+// each 16-lane row's maximum in the row's last lane (lanes without a source keep -inf),
+// and four lane reads combine the rows.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    const int ninf = __float_as_int(-INFINITY);
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x111, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x112, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x114, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x118, 0xf, 0xf, false)));
+    const int b = __float_as_int(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 15));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 31));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 47));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 63));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
 __device__ __forceinline__ float wave_sum(float v) {
     for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
     return v;
@@ -554,7 +570,7 @@ void deform_agg_cam_kernel(const typename E::bits *__restrict__ feat,
             if (cam2 < p.cams) fetch(cam2, k2);  // in flight until the next build
             if (p.softmax) {
                 const float l = valid ? w : -INFINITY;
-                const float m_new = fmaxf(m_run[k], wave_max(l));
+                const float m_new = fmaxf(m_run[k], wave_max_dpp(l));
                 fk[k] = m_new == -INFINITY ? 1.0f : expf(m_run[k] - m_new);
                 esum[k] *= fk[k];
                 m_run[k] = m_new;
