@@ -189,12 +189,35 @@ __device__ __forceinline__ void softmax_k(float (&m)[K], int s) {
         e[j] = k < K ? expf(mk - mx) : 0.0f;
         sum += e[j];
     }
+    if constexpr (S == 1) {
+        const float inv = 1.0f / sum;
 #pragma unroll
-    for (int o = 1; o < S; o <<= 1) sum += __shfl_xor(sum, o, 64);
-    const float inv = 1.0f / sum;
-    const int seg = (threadIdx.x & 63) - s;  // first lane of this pair's segment
+        for (int k = 0; k < K; ++k) m[k] = e[k] * inv;
+    } else if constexpr (S == 2) {
+        // the pair's two lanes are neighbours: a DPP swap (quad_perm 1,0,3,2) instead of
+        // LDS permutes
+        auto swap = [](float v) {
+            return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xb1, 0xf, 0xf, false));
+        };
+        sum += swap(sum);
+        const float inv = 1.0f / sum;
 #pragma unroll
-    for (int k = 0; k < K; ++k) m[k] = __shfl(e[k / S], seg + k % S, 64) * inv;
+        for (int j = 0; j < J; ++j) {
+            const float o = swap(e[j]);  // the other lane's exponential of point 2j + (1 - s)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int k = 2 * j + t;
+                if (k < K) m[k] = (t == s ? e[j] : o) * inv;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int o = 1; o < S; o <<= 1) sum += __shfl_xor(sum, o, 64);
+        const float inv = 1.0f / sum;
+        const int seg = (threadIdx.x & 63) - s;  // first lane of this pair's segment
+#pragma unroll
+        for (int k = 0; k < K; ++k) m[k] = __shfl(e[k / S], seg + k % S, 64) * inv;
+    }
 }
 
 // The taps of one lane in two steps. make_taps turns the pair's offsets and masks into
