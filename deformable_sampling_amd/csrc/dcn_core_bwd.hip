@@ -154,6 +154,19 @@ constexpr int kBinMaxSamples = 2344;
 #include "core_bwd_bins.hpp"
 static_assert(kBinTile == kTile, "bins and destination tiles share their edge");
 
+// Inclusive prefix sum over a full wavefront (every lane active) without LDS permutes:
+// row_shr DPP steps within 16-lane rows, then row_bcast steps carry each row's total
+// into the rows above it.
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned v) {
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);  // row_shr:1
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);  // row_shr:2
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);  // row_shr:4
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);  // row_shr:8
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
 // 1. Samples per home bin. A block takes the 256 pairs of one output tile of one
 // group (tiled order) and its samples tap-fastest; it counts them per bin in LDS
 // and adds one count per distinct bin to the global counters.
@@ -292,10 +305,7 @@ __global__ __launch_bounds__(1024) void bwd_scan_kernel(const unsigned *__restri
             sum += a[k].x + a[k].y + a[k].z + a[k].w;
         }
         unsigned incl = sum;
-        for (int o = 1; o < 64; o <<= 1) {
-            const unsigned w = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += w;
-        }
+        incl = wave_incl_scan(incl);
         if (lane == 63) s_wave[wave] = incl;
         __syncthreads();
         unsigned run = carry + incl - sum;
@@ -753,10 +763,7 @@ __global__ __launch_bounds__(1024) void bwd_gather_kernel(const uint4 *__restric
                     sum += v[i];
                 }
                 unsigned incl = sum;
-                for (int o = 1; o < 64; o <<= 1) {
-                    const unsigned w = __shfl_up(incl, o, 64);
-                    if (tid >= o) incl += w;
-                }
+                incl = wave_incl_scan(incl);
                 unsigned run = incl - sum;
 #pragma unroll
                 for (int i = 0; i < kPer; ++i) {
@@ -1018,10 +1025,7 @@ __global__ __launch_bounds__(256 * NCH) void bwd_gather_staged_kernel(
                 sum += v[i];
             }
             unsigned incl = sum;
-            for (int o = 1; o < 64; o <<= 1) {
-                const unsigned w = __shfl_up(incl, o, 64);
-                if (tid >= o) incl += w;
-            }
+            incl = wave_incl_scan(incl);
             unsigned run = incl - sum;
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
